@@ -1,0 +1,268 @@
+"""Pins for the oracle's routing, permutation, MoE layer and dense linear.
+
+The MoE layer and the dense linear are checked against a pure-Python brute
+force written from the definitions on tiny shapes: every weight is decoded
+from its nibble and scale bits with exact rationals, contractions are exact
+(fractions.Fraction), only silu/exp are float64.  Routing is checked against
+a full sort, permutation against explicit loops.
+"""
+
+import math
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.moe import ACT_BF16, ACT_FP8_E4M3
+
+# ----------------------------------------------------------------- brute force
+
+
+def _bf_e2m1(code):
+    s = -1 if code & 8 else 1
+    e, m = (code >> 1) & 3, code & 1
+    mag = Fraction(m, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+    return s * mag
+
+
+def _bf_weight(blocks, scales, n, kk):
+    byte = int(blocks[n, kk // 32, (kk % 32) // 2])
+    code = (byte >> 4) if kk % 2 else (byte & 15)
+    return _bf_e2m1(code) * Fraction(2) ** (int(scales[n, kk // 32]) - 127)
+
+
+def _bf_bf16(bits):
+    return Fraction(struct.unpack(">f", struct.pack(">I", int(bits) << 16))[0])
+
+
+def _bf_rn_f32(fr):
+    if fr == 0:
+        return Fraction(0)
+    s = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = 0
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    n = a / ulp
+    fl = math.floor(n)
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return s * fl * ulp
+
+
+def _bf_e4m3_values():
+    vals = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            v = Fraction(m, 512) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+            vals.append((v, m))
+    return vals
+
+
+E4M3_VALS = _bf_e4m3_values()
+
+
+def _bf_fp8_round(q):
+    """Nearest E4M3 value (ties to even mantissa), saturating; returns Fraction."""
+    a = abs(q)
+    best = None
+    for v, m in E4M3_VALS:
+        d = abs(a - v)
+        if best is None or d < best[0] or (d == best[0] and m % 2 == 0 and best[2] % 2 == 1):
+            best = (d, v, m)
+    return best[1] if q >= 0 else -best[1]
+
+
+def _bf_quant(values):
+    """Per-tensor FP8: returns list of dequantized Fractions."""
+    amax = max(abs(v) for v in values)
+    s = Fraction(1) if amax == 0 else _bf_rn_f32(amax / 448)
+    return [_bf_fp8_round(_bf_rn_f32(v / s)) * s for v in values]
+
+
+def _silu(z):
+    return z / (1.0 + math.exp(-z))
+
+
+def _bf_moe(x_bits, logits, L, k, act_mode):
+    T, H = x_bits.shape
+    E = L["w13_blocks"].shape[0]
+    I = L["w2_blocks"].shape[2] * 32
+    x = [[_bf_bf16(x_bits[t, i]) for i in range(H)] for t in range(T)]
+    if act_mode == ACT_FP8_E4M3:
+        flat = _bf_quant([v for row in x for v in row])
+        x = [flat[t * H:(t + 1) * H] for t in range(T)]
+    routes = []
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+        z = [math.exp(float(logits[t, e]) - float(logits[t, order[0]])) for e in order]
+        routes.append([(e, zi / sum(z)) for e, zi in zip(order, z)])
+    hs = {}
+    for t in range(T):
+        for j, (e, _) in enumerate(routes[t]):
+            g = []
+            for n in range(2 * I):
+                acc = sum(_bf_weight(L["w13_blocks"][e], L["w13_scales"][e], n, kk) * x[t][kk]
+                          for kk in range(H))
+                g.append(acc + _bf_bf16(L["w13_bias"][e, n]))
+            hs[t, j] = [_silu(float(g[i])) * float(g[I + i]) for i in range(I)]
+    if act_mode == ACT_FP8_E4M3:
+        keys = sorted(hs)
+        flat = _bf_quant([_bf_rn_f32(Fraction(v)) for key in keys for v in hs[key]])
+        hs = {key: flat[i * I:(i + 1) * I] for i, key in enumerate(keys)}
+    else:
+        hs = {key: [Fraction(v) for v in val] for key, val in hs.items()}
+    out = np.zeros((T, H))
+    for t in range(T):
+        for j, (e, w) in enumerate(routes[t]):
+            for n in range(H):
+                acc = sum(_bf_weight(L["w2_blocks"][e], L["w2_scales"][e], n, kk) * hs[t, j][kk]
+                          for kk in range(I))
+                out[t, n] += w * float(acc + _bf_bf16(L["w2_bias"][e, n]))
+    return out
+
+
+def _tiny(E=4, H=64, I=64, T=3, seed=9):
+    L = synth.layer(seed=seed, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(seed + 1, T, E=E, H=H)
+    return L, logits, x
+
+
+# --------------------------------------------------------------------- routing
+
+
+def test_route_topk_matches_full_sort_with_ties():
+    rng = np.random.default_rng(4)
+    logits = rng.integers(-3, 4, size=(64, 16)).astype(np.float32)   # many ties
+    logits[0, :] = 0.0
+    logits[1, ::2] = -0.0                                            # -0 ties +0
+    ids, w = oracle.route_topk(logits, 4)
+    for t in range(64):
+        want = sorted(range(16), key=lambda e: (-float(logits[t, e]), e))[:4]
+        assert list(ids[t]) == want
+    assert list(ids[0]) == [0, 1, 2, 3]
+    assert np.allclose(w[0], 0.25)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+
+
+def test_route_weights_equal_renormalised_full_softmax():
+    rng = np.random.default_rng(8)
+    logits = rng.normal(size=(20, 128)).astype(np.float32)
+    ids, w = oracle.route_topk(logits, 4)
+    l64 = logits.astype(np.float64)
+    p = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    assert np.allclose(w, sel / sel.sum(axis=1, keepdims=True), rtol=1e-13)
+    assert np.all(np.diff(np.take_along_axis(logits, ids.astype(np.int64), axis=1), axis=1) <= 0)
+    ids1, w1 = oracle.route_topk(logits, 1)
+    assert np.array_equal(ids1[:, 0], np.argmax(logits, axis=1)) and np.all(w1 == 1.0)
+    with pytest.raises(ValueError):
+        oracle.route_topk(np.array([[np.nan, 1.0]], dtype=np.float32), 1)
+
+
+def test_permute_matches_loops():
+    rng = np.random.default_rng(12)
+    T, k, E = 37, 4, 16
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, sp, inv = oracle.permute(ids, E)
+    want = []
+    for e in range(E):
+        want += [t * k + j for t in range(T) for j in range(k) if ids[t, j] == e]
+        assert counts[e] == sum(1 for v in ids.ravel() if v == e)
+    assert list(sp) == want
+    assert offsets[0] == 0 and offsets[-1] == T * k
+    assert np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(sp[inv], np.arange(T * k))
+
+
+# -------------------------------------------------------------- moe and linear
+
+
+@pytest.mark.parametrize("act_mode", [ACT_BF16, ACT_FP8_E4M3])
+def test_moe_forward_matches_exact_brute_force(act_mode):
+    L, logits, x = _tiny()
+    res = oracle.moe_forward(x, logits, **L, k=2, act_mode=act_mode)
+    bf = _bf_moe(x, logits, L, 2, act_mode)
+    scale = np.sqrt(np.mean(bf ** 2))
+    assert np.max(np.abs(res["out"] - bf)) <= 1e-12 * scale * 64
+
+
+def test_swiglu_takes_silu_of_the_gate_half():
+    # gate rows come first in the fused gate_up output; silu is applied to them only
+    g = np.zeros(4)
+    g[:2] = [1.0, -2.0]
+    g[2:] = [3.0, 0.5]
+    h = oracle.swiglu(g, 2)
+    assert np.allclose(h, [_silu(1.0) * 3.0, _silu(-2.0) * 0.5], rtol=1e-15)
+    assert not np.allclose(h, [_silu(3.0) * 1.0, _silu(0.5) * -2.0])
+
+
+def test_moe_identical_experts_equal_single_expert():
+    E, H, I, T = 6, 64, 96, 5
+    L1 = synth.layer(seed=21, E=1, H=H, I=I)
+    LE = {key: np.repeat(v, E, axis=0) for key, v in L1.items()}
+    logits, x = synth.moe_inputs(22, T, E=E, H=H)
+    outE = oracle.moe_forward(x, logits, **LE, k=4)["out"]
+    out1 = oracle.moe_forward(x, np.zeros((T, 1), np.float32), **L1, k=1)["out"]
+    assert np.allclose(outE, out1, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_e1_k1_reduces_to_dense_linear():
+    H, I, T = 64, 64, 4
+    L = synth.layer(seed=31, E=1, H=H, I=I)
+    _, x = synth.moe_inputs(32, T, E=1, H=H)
+    out = oracle.moe_forward(x, np.zeros((T, 1), np.float32), **L, k=1)["out"]
+    g = oracle.linear(x, L["w13_blocks"][0], L["w13_scales"][0], L["w13_bias"][0])
+    h = oracle.swiglu(g, I)
+    W2 = oracle.dequant(L["w2_blocks"][0], L["w2_scales"][0])
+    want = h @ W2.T + oracle.bf16_bits_to_f64(L["w2_bias"][0])
+    assert np.allclose(out, want, rtol=1e-13, atol=1e-13)
+
+
+def test_moe_token_permutation_equivariance():
+    L, logits, x = _tiny(T=6)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    a = oracle.moe_forward(x, logits, **L, k=2)["out"]
+    b = oracle.moe_forward(x[perm], logits[perm], **L, k=2)["out"]
+    assert np.allclose(a[perm], b, rtol=1e-13, atol=1e-13)
+
+
+def test_linear_matches_exact_brute_force():
+    N, K, M = 24, 96, 3
+    D = synth.dense(41, N, K)
+    x = synth.dense_x(42, M, K)
+    got = oracle.linear(x, D["w_blocks"], D["w_scales"], D["bias"])
+    for m in range(M):
+        for n in range(N):
+            acc = sum(_bf_weight(D["w_blocks"], D["w_scales"], n, kk) * _bf_bf16(x[m, kk])
+                      for kk in range(K))
+            want = float(acc + _bf_bf16(D["bias"][n]))
+            assert abs(got[m, n] - want) <= 1e-13 * max(1.0, abs(want))
+    rows = np.array([5, 0, 23])
+    assert np.array_equal(oracle.linear_rows(x, D["w_blocks"], D["w_scales"], D["bias"], rows),
+                          got[:, rows])
+
+
+def test_one_bf16_rounding_fits_the_tolerance_but_two_do_not():
+    """Error budget behind the 'one rounding at the end' design: rounding a
+    Gaussian output to bf16 once costs about 1.7e-3 relative Frobenius error,
+    under the 2e-3 bar; an extra bf16 rounding of an intermediate does not fit."""
+    rng = np.random.default_rng(1)
+    ref = rng.normal(size=200000)
+    r1 = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+    e1 = np.linalg.norm(r1 - ref) / np.linalg.norm(ref)
+    assert 1.4e-3 < e1 < 2e-3
+    noise = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((ref + 1e-3).astype(np.float32)))
+    e2 = np.linalg.norm((noise - 1e-3) - ref) / np.linalg.norm(ref)
+    both = np.sqrt(e1 ** 2 + e2 ** 2)
+    assert both > 2e-3
