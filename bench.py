@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Throughput of the MXFP4 MoE layer on one MI355X, with roofline context.
+
+A step is one pass of the hot path over one batch: router top-k, then the MoE
+layer (permutation, [FP8 quantisation of x], gate_up GEMM + SwiGLU, [FP8
+quantisation of h], down GEMM, weighted combine), all through the C ABI.
+Weights, logits and activations are resident in HBM before timing starts.
+Before every timed step a 1 GiB buffer is overwritten so the step reads its
+weights from HBM and not from the 256 MB last-level cache; each step is
+bracketed by events on the launch stream and the flush is outside them.
+
+The headline line is the 32-token decode batch (hidden 2880, 128 experts,
+top-4, bf16 activations).  The same run also measures the 4-token decode,
+the FP8 prefill workloads (2048 tokens; 8192 tokens with hot experts) and the
+dense MXFP4 projections (qkv_proj, o_proj, lm_head at 1 and 4 tokens), and
+times the float64 CPU oracle on a bounded sample for the cpu_baseline field.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--primary-only]
+                       [--no-cpu-baseline] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer GB/s & % HBM roofline (decode 4–32 tok); MXFP4 TFLOP/s (prefill)"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0        # dense MFMA, FP8 (the FP8 x FP4 instruction's operand rate)
+MXFP4_PEAK_TFLOPS = 10100.0     # dense MFMA, FP4 / FP6
+PRIMARY = "moe_decode_t32"
+FLUSH_BYTES = 1 << 30
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def expert_bytes(H, I):
+    """Bytes of one expert's gate_up and down weights (blocks + scales + bf16 bias)."""
+    gate_up = 2 * I * (H // 32) * 17 + 2 * I * 2
+    down = H * (I // 32) * 17 + H * 2
+    return gate_up, down
+
+
+def moe_accounting(ids, T, H, I, act):
+    """Algorithmic bytes and flops of one layer pass and of its gate_up kernel."""
+    touched = len(np.unique(ids))
+    pairs = ids.size
+    gu, dn = expert_bytes(H, I)
+    E = 128
+    layer_bytes = touched * (gu + dn) + T * H * 2 + T * E * 4 + T * H * 2
+    h_bytes = pairs * I * 4                     # bf16 hi+lo or fp32 h written
+    xin = T * H * (1 if act else 2)             # bf16 x or fp8 codes read
+    gemm1_bytes = touched * gu + xin + h_bytes
+    gemm1_flops = 2.0 * pairs * 2 * I * H
+    flops = 2.0 * pairs * (2 * I * H + H * I)
+    return dict(touched=touched, pairs=pairs, layer_bytes=layer_bytes, gemm1_bytes=gemm1_bytes,
+                gemm1_flops=gemm1_flops, flops=flops)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mxfp4_block_scaled_top_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(n.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class Runner:
+    def __init__(self, torch, mx):
+        self.torch = torch
+        self.mx = mx
+        self.flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def dev(self, a):
+        torch = self.torch
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    def time_steps(self, step, steps, warmup, flush=True, stage_events=False):
+        """Per-step event times (ms); optional per-stage times (ms) via the ABI events."""
+        torch, mx = self.torch, self.mx
+        for _ in range(warmup):
+            if flush:
+                self.flush.fill_(1.0)
+            step(None)
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        evs = None
+        if stage_events:
+            evs = [[mx.mxfp4_event_create() for _ in range(mx.NUM_STAGES)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if flush:
+                self.flush.fill_(float(i))
+            starts[i].record()
+            step(evs[i] if evs else None)
+            ends[i].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+        stages = None
+        if evs:
+            stages = {}
+            for a in range(mx.NUM_STAGES - 1):
+                d = [mx.mxfp4_event_elapsed_ms(ev[a], ev[a + 1]) for ev in evs]
+                stages[mx.STAGES[a + 1]] = float(np.mean(d))
+            for ev in evs:
+                for e in ev:
+                    mx.mxfp4_event_destroy(e)
+        return ms, stages, wall
+
+
+def moe_setup(run, Ld, name, synth):
+    torch, mx = run.torch, run.mx
+    wl = synth.workload(name)
+    T, H = wl["x"].shape
+    I = synth.H_GPT_OSS
+    E, k, act = synth.E_GPT_OSS, synth.TOPK_GPT_OSS, wl["act_mode"]
+    logits = run.dev(wl["logits"])
+    x = run.dev(wl["x"])
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.mxfp4_moe_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device="cuda")
+
+    def step(events):
+        mx.mxfp4_route_topk(logits, k, ids, w)
+        mx.mxfp4_moe_forward(x, ids, w, Ld["w13_blocks"], Ld["w13_scales"], Ld["w13_bias"],
+                             Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"], act, out=out,
+                             workspace=ws, events=events)
+
+    step(None)
+    torch.cuda.synchronize()
+    acct = moe_accounting(ids.cpu().numpy(), T, H, I, act)
+    return step, acct, wl
+
+
+def measure_moe(run, Ld, name, synth, steps, warmup):
+    step, acct, wl = moe_setup(run, Ld, name, synth)
+    ms, stages, wall = run.time_steps(step, steps, warmup, flush=True, stage_events=True)
+    ms_plain, _, _ = run.time_steps(step, steps, warmup, flush=True, stage_events=False)
+    warm, _, _ = run.time_steps(step, max(steps // 2, 3), 1, flush=False)
+    mean = float(np.mean(ms_plain))
+    g1 = stages["gemm1"]
+    act = wl["act_mode"]
+    res = dict(
+        tokens=wl["T"], act="fp8_e4m3" if act else "bf16", touched_experts=acct["touched"],
+        ms_per_step=mean, ms_p10=float(np.percentile(ms_plain, 10)),
+        ms_p50=float(np.median(ms_plain)), ms_p90=float(np.percentile(ms_plain, 90)),
+        layer_GBps=acct["layer_bytes"] / mean / 1e6,
+        layer_TFLOPs=acct["flops"] / mean / 1e9,
+        layer_hbm_frac=acct["layer_bytes"] / mean / 1e6 / HBM_PEAK_GBS,
+        warm_ms_per_step=float(np.mean(warm)),
+        stage_ms=stages, gemm1_ms=g1,
+        gemm1_GBps=acct["gemm1_bytes"] / g1 / 1e6,
+        gemm1_TFLOPs=acct["gemm1_flops"] / g1 / 1e9,
+        algorithmic_bytes=acct["layer_bytes"], gemm1_bytes=acct["gemm1_bytes"],
+        flops=acct["flops"], wall_s=wall)
+    return res
+
+
+def measure_dense(run, synth, steps, warmup):
+    mx = run.mx
+    out = {}
+    for name, (N, K) in synth.DENSE_SHAPES.items():
+        D = synth.dense(synth.DENSE_SEEDS[name], N, K)
+        wb, wsc, b = run.dev(D["w_blocks"]), run.dev(D["w_scales"]), run.dev(D["bias"])
+        for M in (1, 4):
+            x = run.dev(synth.dense_x(synth.DENSE_X_SEED, M, K))
+            y = run.torch.empty((M, N), dtype=run.torch.bfloat16, device="cuda")
+
+            def step(_ev, x=x, y=y, wb=wb, wsc=wsc, b=b):
+                mx.mxfp4_linear(x, wb, wsc, b, out=y)
+
+            ms, _, _ = run.time_steps(step, steps, warmup, flush=True)
+            nbytes = N * (K // 32) * 17 + 2 * N + M * K * 2 + M * N * 2
+            mean = float(np.mean(ms))
+            out["%s_m%d" % (name, M)] = dict(N=N, K=K, M=M, ms=mean, GBps=nbytes / mean / 1e6,
+                                             hbm_frac=nbytes / mean / 1e6 / HBM_PEAK_GBS,
+                                             TFLOPs=2.0 * M * N * K / mean / 1e9, bytes=nbytes)
+        del wb, wsc, b
+    return out
+
+
+def cpu_baseline(synth, budget_tokens=4):
+    """The float64 oracle on the first tokens of the headline batch, on host cores."""
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    L = synth.layer()
+    wl = synth.workload(PRIMARY)
+    x, logits = wl["x"][:budget_tokens], wl["logits"][:budget_tokens]
+    t0 = time.perf_counter()
+    res = oracle.moe_forward(x, logits, **L, k=synth.TOPK_GPT_OSS, act_mode=wl["act_mode"])
+    dt = time.perf_counter() - t0
+    acct = moe_accounting(res["ids"], budget_tokens, synth.H_GPT_OSS, synth.H_GPT_OSS, 0)
+    return dict(value=acct["layer_bytes"] / dt / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample="first %d of the %d tokens of the decode batch (%d experts touched), "
+                       "float64 numpy, %.1f s" % (budget_tokens, wl["T"], acct["touched"], dt))
+
+
+def pmc_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = d.get(kernel)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=PRIMARY)
+    ap.add_argument("--primary-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (requested %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mxfp4_block_scaled_top_amd as mx
+    import synth
+
+    mx.lib()
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    run = Runner(torch, mx)
+    L = synth.layer()
+    Ld = {k: run.dev(v) for k, v in L.items()}
+    del L
+    print("bench: layer resident (%.2f GB)" % (sum(t.numel() * t.element_size() for t in Ld.values()) / 1e9),
+          file=sys.stderr, flush=True)
+
+    prim = measure_moe(run, Ld, args.workload, synth, args.steps, args.warmup)
+    print("bench: %s %.1f us/step" % (args.workload, prim["ms_per_step"] * 1e3), file=sys.stderr, flush=True)
+    others = {}
+    if not args.primary_only:
+        for name in synth.MOE_WORKLOADS:
+            if name == args.workload:
+                continue
+            others[name] = measure_moe(run, Ld, name, synth, max(args.steps // 2, 5), 2)
+            print("bench: %s %.1f us/step" % (name, others[name]["ms_per_step"] * 1e3),
+                  file=sys.stderr, flush=True)
+        del Ld
+        torch.cuda.empty_cache()
+        others["dense"] = measure_dense(run, synth, max(args.steps // 2, 5), 2)
+        print("bench: dense set done", file=sys.stderr, flush=True)
+
+    fp8 = prim["act"] != "bf16"
+    kname = "gemm_fp8_kernel<true>" if fp8 else "gemv_bf16_kernel<0>"
+    if fp8 and prim["tokens"] >= 4096:
+        roof = dict(bound="mfma", achieved=prim["gemm1_TFLOPs"], peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=prim["gemm1_TFLOPs"] / FP8_PEAK_TFLOPS)
+    else:
+        roof = dict(bound="hbm", achieved=prim["gemm1_GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=prim["gemm1_GBps"] / HBM_PEAK_GBS)
+    roof["kernel"] = kname
+    roof["traffic"] = pmc_traffic(kname)
+    line = {
+        "metric": METRIC,
+        "value": prim["layer_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": prim["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": prim["tokens"], "experts": 128, "topk": 4,
+                   "hidden": 2880, "intermediate": 2880, "weights": "mxfp4", "act": prim["act"],
+                   "parallelism": "none (1 GPU)"},
+        "hbm_frac": prim["layer_hbm_frac"],
+        "roofline": roof,
+        "detail": prim,
+        "workloads": others,
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * mxfp4_moe.h - C ABI of the MI355X (gfx950) MXFP4 block-scaled MoE layer and
+ * dense projections.
+ *
+ * What is computed (source pages):
+ *   - Weights are MXFP4 as the gpt-oss page describes them in "MXFP4 Tensor
+ *     Structure": *_blocks uint8 [E, N, K/32, 16] hold two E2M1 codes per
+ *     byte (32 elements per 16-byte block), *_scales uint8 [E, N, K/32] one
+ *     E8M0 power-of-two scale per block with bias 127, *_bias bfloat16.  An
+ *     element's value is E2M1(code) * 2^(scale - 127) ("Conversion
+ *     Methodology", step 1).  Element 2i of a block sits in the low nibble of
+ *     byte i, element 2i+1 in its high nibble.
+ *   - The MoE layer of gpt-oss-120b ("GPT-OSS-120B Architecture": 128
+ *     experts, 4 active per token, hidden 2880) run as an FP8 x FP4 grouped
+ *     GEMM (spark-vllm page, "What's Included") or, for small token counts,
+ *     with bf16 activations; dense MXFP4 qkv_proj, o_proj and lm_head
+ *     (spark-vllm page, full MXFP4 stack; gptoss-spark page, "What produced
+ *     it, ranked").
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are DEVICE pointers owned by the caller, row-major
+ *     and contiguous.  bfloat16 is passed as uint16_t bit patterns.  `stream`
+ *     is a hipStream_t (NULL = the default stream).
+ *   - Calls are asynchronous: they validate, enqueue kernels on `stream` and
+ *     return.  Faults inside kernels surface at the caller's next
+ *     synchronisation of the stream.
+ *   - Validation is complete before anything is enqueued: on any non-zero
+ *     return nothing has been launched and no output has been written.
+ *   - The library allocates no device memory; scratch comes from the caller's
+ *     `workspace`, sized with mxfp4_moe_workspace_size().
+ *   - No C++ exception crosses this boundary.  Functions are thread-safe; the
+ *     only state is a per-device cache of the architecture check and a
+ *     thread-local error message.
+ *   - Only gfx950 devices are accepted (MXFP4_E_DEVICE otherwise).
+ */
+#ifndef MXFP4_MOE_H
+#define MXFP4_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXFP4_ABI_VERSION 1
+
+/* Status codes.  0 is success; every failure leaves outputs untouched. */
+enum {
+  MXFP4_OK = 0,
+  MXFP4_E_NULL = 1,      /* a required pointer is NULL */
+  MXFP4_E_SHAPE = 2,     /* bad size: K/H/I not a positive multiple of 32, k > E, ... */
+  MXFP4_E_ALIGN = 3,     /* a pointer is not aligned as documented */
+  MXFP4_E_MODE = 4,      /* unknown enum value (never silently ignored) */
+  MXFP4_E_WORKSPACE = 5, /* workspace NULL or smaller than required */
+  MXFP4_E_DEVICE = 6,    /* no HIP device, or the current device is not gfx950 */
+  MXFP4_E_HIP = 7        /* a HIP runtime call or kernel launch failed */
+};
+
+/* Activation precision of the MoE contraction. */
+enum {
+  MXFP4_ACT_BF16 = 0,         /* x used as given (bf16), fp32 accumulation */
+  MXFP4_ACT_FP8_E4M3 = 1      /* x and the SwiGLU output h each quantised to
+                                 OCP FP8 E4M3 with one per-tensor fp32 scale
+                                 amax/448; FP8 x FP4 block-scaled MFMA */
+};
+
+/* Stage boundaries at which mxfp4_moe_forward can record caller events. */
+enum {
+  MXFP4_STAGE_BEGIN = 0,      /* before the first kernel */
+  MXFP4_STAGE_PERMUTE = 1,    /* after the token-by-expert permutation */
+  MXFP4_STAGE_QUANT_X = 2,    /* after FP8 quantisation of x (FP8 mode) */
+  MXFP4_STAGE_GEMM1 = 3,      /* after gate_up GEMM + SwiGLU */
+  MXFP4_STAGE_QUANT_H = 4,    /* after FP8 quantisation of h (FP8 mode) */
+  MXFP4_STAGE_GEMM2 = 5,      /* after the down GEMM */
+  MXFP4_STAGE_COMBINE = 6,    /* after the weighted combine (end) */
+  MXFP4_NUM_STAGES = 7
+};
+
+/* Optional per-call options for mxfp4_moe_forward (pass NULL for none). */
+typedef struct {
+  /* events[i], if non-NULL, is a hipEvent_t recorded on `stream` at stage
+     boundary i (0 <= i < MXFP4_NUM_STAGES).  Used for per-kernel timing. */
+  void* events[MXFP4_NUM_STAGES];
+} mxfp4_moe_opts;
+
+/* Byte offsets of the intermediate results inside the MoE workspace, for
+   inspection by tests and profilers (all offsets are 256-byte aligned). */
+typedef struct {
+  uint64_t total_bytes;
+  uint64_t status;          /* int32[16]: [0] error flags (bit 0: an expert id was
+                               outside [0,E) and its pair was skipped),
+                               [1] amax(x) fp32 bits, [2] amax(h) fp32 bits,
+                               [3] x scale fp32 bits, [4] h scale fp32 bits,
+                               [5] number of row tiles */
+  uint64_t expert_offsets;  /* int32 [E+1]: sorted rows of expert e are
+                               [offsets[e], offsets[e+1]) */
+  uint64_t sorted_pairs;    /* int32 [T*k]: pair index p = t*k + j per sorted row,
+                               ascending p within an expert */
+  uint64_t inv_pairs;       /* int32 [T*k]: sorted row of pair p */
+  uint64_t chunk_counts;    /* int32 scratch of the permutation */
+  uint64_t chunk_ranks;     /* int32 scratch of the permutation */
+  uint64_t tiles;           /* int32 [2 * max_tiles]: (expert, first sorted row) */
+  uint64_t x_codes;         /* uint8 [T, H] E4M3 codes of x (FP8 mode) */
+  uint64_t h;               /* BF16 mode: bf16 hi [T*k, I] then bf16 lo [T*k, I]
+                               with h = hi + lo; FP8 mode: fp32 [T*k, I];
+                               rows in sorted order */
+  uint64_t h_codes;         /* uint8 [T*k, I] E4M3 codes of h (FP8 mode) */
+  uint64_t y;               /* fp32 [T*k, H] per-pair expert outputs, sorted rows */
+} mxfp4_moe_workspace_layout;
+
+/* Library ABI version (MXFP4_ABI_VERSION of the build). */
+int mxfp4_abi_version(void);
+
+/* Static text for a status code. */
+const char* mxfp4_status_string(int status);
+
+/* Detail text of the last failing call on this thread ("" if none). */
+const char* mxfp4_last_error(void);
+
+/*
+ * Router top-k (gpt-oss page, "GPT-OSS-120B Architecture": 4 of 128 experts
+ * per token).  For each token t: ids are the k experts with the largest fp32
+ * logit, in descending logit order, equal logits going to the lower index
+ * (-0 equals +0); weights are the softmax over the k chosen logits, in fp32.
+ *   logits        fp32 [T, E]           input (NaN logits are not supported)
+ *   topk_ids      int32 [T, k]          output
+ *   topk_weights  fp32 [T, k]           output
+ * Limits: 1 <= E <= 512, 1 <= k <= min(E, 16), T >= 0 (T == 0 is a no-op).
+ * Alignment: 4 bytes for every pointer.
+ */
+int mxfp4_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                     int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* Workspace bytes mxfp4_moe_forward needs for these sizes (written to *bytes). */
+int mxfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                             int32_t act_mode, size_t* bytes);
+
+/* Offsets of the intermediates inside that workspace (see the struct). */
+int mxfp4_moe_workspace_layout_query(int64_t T, int64_t H, int64_t I, int32_t E,
+                                     int32_t k, int32_t act_mode,
+                                     mxfp4_moe_workspace_layout* layout);
+
+/*
+ * One MoE layer (gpt-oss page, "GPT-OSS-120B Architecture" and "MXFP4 Tensor
+ * Structure"; spark-vllm page, FP8 x FP4 grouped GEMM).  For each token t and
+ * slot j, with e = topk_ids[t, j]:
+ *     g      = W13[e] a_t + b13[e]                 (2I values)
+ *     h      = silu(g[0:I]) * g[I:2I],  silu(z) = z / (1 + exp(-z))
+ *     y[t,j] = W2[e] h' + b2[e]                    (H values)
+ *     out[t] = sum_j topk_weights[t, j] * y[t, j]  (fp32, j ascending, then one
+ *                                                   round-to-nearest-even to bf16)
+ * where a_t = x_t and h' = h in MXFP4_ACT_BF16 mode; in MXFP4_ACT_FP8_E4M3
+ * mode a_t and h' are the E4M3-dequantised values with per-tensor scales
+ * s = fp32(amax/448) computed over all of x, and over all T*k*I values of h,
+ * codes = E4M3 round-to-nearest-even, saturating, of the correctly rounded
+ * fp32 quotient v / s.  W13 rows [0, I) are the gate rows, [I, 2I) the up rows.
+ *
+ *   x            bf16 [T, H]                 16-byte aligned
+ *   topk_ids     int32 [T, k]                values in [0, E); a pair with an
+ *                                            id outside is skipped (contributes
+ *                                            0) and status bit 0 is set
+ *   topk_weights fp32 [T, k]
+ *   w13_blocks   uint8 [E, 2I, H/32, 16]     16-byte aligned
+ *   w13_scales   uint8 [E, 2I, H/32]
+ *   w13_bias     bf16 [E, 2I] or NULL (zero bias)
+ *   w2_blocks    uint8 [E, H, I/32, 16]      16-byte aligned
+ *   w2_scales    uint8 [E, H, I/32]
+ *   w2_bias      bf16 [E, H] or NULL
+ *   act_mode     MXFP4_ACT_BF16 or MXFP4_ACT_FP8_E4M3
+ *   out          bf16 [T, H]                 16-byte aligned, must not alias
+ *                                            any input or the workspace
+ *   workspace    >= mxfp4_moe_workspace_size() bytes, 256-byte aligned
+ *   opts         NULL or per-call options (stage events)
+ * Limits: H, I positive multiples of 32 (<= 65536); 1 <= E <= 512;
+ * 1 <= k <= min(E, 16); 0 <= T <= 2^22 (T == 0 is a no-op).  In MXFP4_ACT_BF16 mode, E8M0 scale bytes must
+ * lie in [2, 252] (the weight is formed exactly in bf16 before the MFMA); the
+ * FP8 mode accepts every byte except 255.
+ */
+int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E,
+                      int32_t k, const int32_t* topk_ids, const float* topk_weights,
+                      const uint8_t* w13_blocks, const uint8_t* w13_scales,
+                      const uint16_t* w13_bias, const uint8_t* w2_blocks,
+                      const uint8_t* w2_scales, const uint16_t* w2_bias,
+                      int32_t act_mode, uint16_t* out, void* workspace,
+                      size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream);
+
+/*
+ * Dense MXFP4 projection out = x W^T + b (spark-vllm page, MXFP4 qkv/o/lm_head;
+ * gptoss-spark page: qkv_proj, o_proj and the 201k-row lm_head in MXFP4), bf16
+ * activations, fp32 accumulation, one round-to-nearest-even to bf16.
+ *   x         bf16 [M, K]          16-byte aligned
+ *   w_blocks  uint8 [N, K/32, 16]  16-byte aligned
+ *   w_scales  uint8 [N, K/32]      E8M0 bytes in [2, 252]
+ *   bias      bf16 [N] or NULL
+ *   out       bf16 [M, N]          16-byte aligned, must not alias the inputs
+ * Limits: K a positive multiple of 32, N a positive multiple of 16,
+ * 0 <= M <= 2^20 (M == 0 is a no-op).
+ */
+int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                 const uint8_t* w_blocks, const uint8_t* w_scales, const uint16_t* bias,
+                 uint16_t* out, void* stream);
+
+/*
+ * Per-tensor FP8 E4M3 quantiser, exactly the codec the FP8 MoE mode applies to
+ * x and h, exported for bit-exact tests:
+ *   amax = max |v|; s = fp32(amax / 448) (1 if amax == 0);
+ *   code = E4M3 round-to-nearest-even, saturating to +-448, of fp32(v / s).
+ *   in        fp32 [n] (in_dtype 0) or bf16 [n] (in_dtype 1), 16-byte aligned
+ *   codes     uint8 [n] output
+ *   scale     fp32 [1] output s
+ *   amax      fp32 [1] output amax (also used as the accumulator)
+ * n >= 0 (n == 0 writes s = 1, amax = 0).  NaN inputs are not supported.
+ */
+int mxfp4_quant_fp8_e4m3(const void* in, int32_t in_dtype, int64_t n, uint8_t* codes,
+                         float* scale, float* amax, void* stream);
+
+/* Thin hipEvent helpers so callers can time stages without their own HIP
+   bindings: create (timing enabled), destroy, and elapsed milliseconds between
+   two recorded events (synchronises on `end`). */
+int mxfp4_event_create(void** event);
+int mxfp4_event_destroy(void* event);
+int mxfp4_event_elapsed_ms(void* start, void* end, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_MOE_H */

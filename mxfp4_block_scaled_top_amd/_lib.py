@@ -1,0 +1,247 @@
+"""ctypes binding of libmxfp4moe.so (include/mxfp4_moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the shared library.  PyTorch provides device memory and the stream.  There is
+no fallback: if the library is missing the first call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxfp4moe.so")
+
+ACT_BF16 = 0
+ACT_FP8_E4M3 = 1
+NUM_STAGES = 7
+STAGES = ("begin", "permute", "quant_x", "gemm1", "quant_h", "gemm2", "combine")
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "total_bytes", "status", "expert_offsets", "sorted_pairs", "inv_pairs",
+        "chunk_counts", "chunk_ranks", "tiles", "x_codes", "h", "h_codes", "y")]
+
+
+class MoeOpts(ctypes.Structure):
+    _fields_ = [("events", _c_void_p * NUM_STAGES)]
+
+
+class Mxfp4Error(RuntimeError):
+    def __init__(self, func, status, detail):
+        super().__init__("%s failed with status %d: %s" % (func, status, detail))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmxfp4moe.so is not built (run __graft_entry__.build()): %s" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        L.mxfp4_abi_version.restype = ctypes.c_int
+        L.mxfp4_status_string.restype = ctypes.c_char_p
+        L.mxfp4_status_string.argtypes = [ctypes.c_int]
+        L.mxfp4_last_error.restype = ctypes.c_char_p
+        L.mxfp4_route_topk.argtypes = [_c_void_p, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]
+        L.mxfp4_moe_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32,
+                                               ctypes.POINTER(ctypes.c_size_t)]
+        L.mxfp4_moe_workspace_layout_query.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32,
+                                                       ctypes.POINTER(WorkspaceLayout)]
+        L.mxfp4_moe_forward.argtypes = [
+            _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
+            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+            _i32, _c_void_p, _c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeOpts), _c_void_p]
+        L.mxfp4_linear.argtypes = [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p, _c_void_p]
+        L.mxfp4_quant_fp8_e4m3.argtypes = [_c_void_p, _i32, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                           _c_void_p]
+        L.mxfp4_event_create.argtypes = [ctypes.POINTER(_c_void_p)]
+        L.mxfp4_event_destroy.argtypes = [_c_void_p]
+        L.mxfp4_event_elapsed_ms.argtypes = [_c_void_p, _c_void_p, ctypes.POINTER(ctypes.c_float)]
+        for name in ("mxfp4_route_topk", "mxfp4_moe_workspace_size", "mxfp4_moe_workspace_layout_query",
+                     "mxfp4_moe_forward", "mxfp4_linear", "mxfp4_quant_fp8_e4m3", "mxfp4_event_create",
+                     "mxfp4_event_destroy", "mxfp4_event_elapsed_ms"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(func, status):
+    if status != 0:
+        raise Mxfp4Error(func, status, lib().mxfp4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims" % (name, ndim))
+
+
+def mxfp4_abi_version():
+    return lib().mxfp4_abi_version()
+
+
+def mxfp4_route_topk(logits, k, topk_ids=None, topk_weights=None, stream=None):
+    """Top-k expert ids (int32 [T,k]) and softmax-of-k weights (fp32 [T,k])."""
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    _need(topk_weights, "topk_weights", torch.float32, 2)
+    if tuple(topk_ids.shape) != (T, k) or tuple(topk_weights.shape) != (T, k):
+        raise ValueError("topk outputs must be [T, k]")
+    _check("mxfp4_route_topk", lib().mxfp4_route_topk(
+        _ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_weights), _stream(stream)))
+    return topk_ids, topk_weights
+
+
+def mxfp4_moe_workspace_size(T, H, I, E, k, act_mode):
+    n = ctypes.c_size_t(0)
+    _check("mxfp4_moe_workspace_size",
+           lib().mxfp4_moe_workspace_size(T, H, I, E, k, act_mode, ctypes.byref(n)))
+    return n.value
+
+
+def mxfp4_moe_workspace_layout_query(T, H, I, E, k, act_mode):
+    L = WorkspaceLayout()
+    _check("mxfp4_moe_workspace_layout_query",
+           lib().mxfp4_moe_workspace_layout_query(T, H, I, E, k, act_mode, ctypes.byref(L)))
+    return {name: getattr(L, name) for name, _ in WorkspaceLayout._fields_}
+
+
+def mxfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bias,
+                      w2_blocks, w2_scales, w2_bias, act_mode, out=None, workspace=None,
+                      events=None, stream=None):
+    """One MoE layer; returns out (bf16 [T, H]).  `workspace` is a uint8 device
+    tensor of at least mxfp4_moe_workspace_size() bytes (allocated here if None);
+    `events` is an optional list of NUM_STAGES event handles (or None entries)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    _need(topk_weights, "topk_weights", torch.float32, 2)
+    _need(w13_blocks, "w13_blocks", torch.uint8, 4)
+    _need(w13_scales, "w13_scales", torch.uint8, 3)
+    _need(w2_blocks, "w2_blocks", torch.uint8, 4)
+    _need(w2_scales, "w2_scales", torch.uint8, 3)
+    if w13_bias is not None:
+        _need(w13_bias, "w13_bias", torch.bfloat16, 2)
+    if w2_bias is not None:
+        _need(w2_bias, "w2_bias", torch.bfloat16, 2)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E, twoI = w13_blocks.shape[0], w13_blocks.shape[1]
+    I = twoI // 2
+    if (tuple(w13_blocks.shape) != (E, 2 * I, H // 32, 16) or tuple(w13_scales.shape) != (E, 2 * I, H // 32)
+            or tuple(w2_blocks.shape) != (E, H, I // 32, 16) or tuple(w2_scales.shape) != (E, H, I // 32)
+            or tuple(topk_ids.shape) != (T, k) or tuple(topk_weights.shape) != (T, k)
+            or (w13_bias is not None and tuple(w13_bias.shape) != (E, 2 * I))
+            or (w2_bias is not None and tuple(w2_bias.shape) != (E, H))):
+        raise ValueError("inconsistent MoE tensor shapes")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if workspace is None:
+        workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, act_mode), 1),
+                                dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    opts = None
+    if events is not None:
+        opts = MoeOpts()
+        for i, ev in enumerate(events):
+            opts.events[i] = ev
+    _check("mxfp4_moe_forward", lib().mxfp4_moe_forward(
+        _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
+        _ptr(w13_blocks), _ptr(w13_scales), _ptr(w13_bias),
+        _ptr(w2_blocks), _ptr(w2_scales), _ptr(w2_bias), act_mode, _ptr(out),
+        _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts is not None else None,
+        _stream(stream)))
+    return out
+
+
+def mxfp4_linear(x, w_blocks, w_scales, bias=None, out=None, stream=None):
+    """Dense MXFP4 projection out = x W^T + b, bf16 [M, N]."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_blocks, "w_blocks", torch.uint8, 3)
+    _need(w_scales, "w_scales", torch.uint8, 2)
+    M, K = x.shape
+    N = w_blocks.shape[0]
+    if tuple(w_blocks.shape) != (N, K // 32, 16) or tuple(w_scales.shape) != (N, K // 32):
+        raise ValueError("w_blocks/w_scales shape does not match x")
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must be [N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2)
+    _check("mxfp4_linear", lib().mxfp4_linear(
+        _ptr(x), M, N, K, _ptr(w_blocks), _ptr(w_scales), _ptr(bias), _ptr(out), _stream(stream)))
+    return out
+
+
+def mxfp4_quant_fp8_e4m3(inp, codes=None, scale=None, amax=None, stream=None):
+    """Per-tensor E4M3 codes (uint8, same shape), scale and amax (fp32 [1])."""
+    if inp.dtype == torch.float32:
+        dt = 0
+    elif inp.dtype == torch.bfloat16:
+        dt = 1
+    else:
+        raise TypeError("inp must be float32 or bfloat16")
+    _need(inp, "inp", inp.dtype)
+    if codes is None:
+        codes = torch.empty(inp.shape, dtype=torch.uint8, device=inp.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=inp.device)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=inp.device)
+    _need(codes, "codes", torch.uint8)
+    _check("mxfp4_quant_fp8_e4m3", lib().mxfp4_quant_fp8_e4m3(
+        _ptr(inp), dt, inp.numel(), _ptr(codes), _ptr(scale), _ptr(amax), _stream(stream)))
+    return codes, scale, amax
+
+
+def mxfp4_event_create():
+    ev = ctypes.c_void_p()
+    _check("mxfp4_event_create", lib().mxfp4_event_create(ctypes.byref(ev)))
+    return ev.value
+
+
+def mxfp4_event_destroy(ev):
+    _check("mxfp4_event_destroy", lib().mxfp4_event_destroy(ctypes.c_void_p(ev)))
+
+
+def mxfp4_event_elapsed_ms(start, end):
+    ms = ctypes.c_float()
+    _check("mxfp4_event_elapsed_ms",
+           lib().mxfp4_event_elapsed_ms(ctypes.c_void_p(start), ctypes.c_void_p(end), ctypes.byref(ms)))
+    return ms.value

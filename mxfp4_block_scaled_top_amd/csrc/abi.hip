@@ -1,0 +1,315 @@
+// C ABI of the MXFP4 MoE library: argument validation, workspace plan and
+// launch sequencing.  Declarations and the contract are in
+// include/mxfp4_moe.h.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mxfp4_moe.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MXFP4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Cached per-device architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch[64];
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MXFP4_E_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MXFP4_E_DEVICE, "device index %d out of range", dev);
+  int state = g_arch[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(MXFP4_E_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(state, std::memory_order_relaxed);
+    if (state == 2) return fail(MXFP4_E_DEVICE, "device %d is %s, only gfx950 is supported", dev, prop.gcnArchName);
+  }
+  if (state != 1) return fail(MXFP4_E_DEVICE, "device %d is not gfx950", dev);
+  return MXFP4_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int moe_shape_check(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mode) {
+  if (act_mode != MXFP4_ACT_BF16 && act_mode != MXFP4_ACT_FP8_E4M3)
+    return fail(MXFP4_E_MODE, "unknown act_mode %d", act_mode);
+  if (T < 0 || T > (1 << 22)) return fail(MXFP4_E_SHAPE, "T=%lld outside [0, 2^22]", (long long)T);
+  if (H <= 0 || H % 32 || H > (1 << 16)) return fail(MXFP4_E_SHAPE, "H=%lld must be a positive multiple of 32 (<= 65536)", (long long)H);
+  if (I <= 0 || I % 32 || I > (1 << 16)) return fail(MXFP4_E_SHAPE, "I=%lld must be a positive multiple of 32 (<= 65536)", (long long)I);
+  if (E < 1 || E > 512) return fail(MXFP4_E_SHAPE, "E=%d outside [1, 512]", E);
+  if (k < 1 || k > 16 || k > E) return fail(MXFP4_E_SHAPE, "k=%d outside [1, min(E, 16)]", k);
+  const int64_t npairs = T * k;
+  const int bm = act_mode == MXFP4_ACT_BF16 ? mx::kDecodeBM : mx::kPrefillBM;
+  if (mx::max_tiles(npairs, E, bm) > 65535) return fail(MXFP4_E_SHAPE, "T*k=%lld gives too many row tiles", (long long)npairs);
+  return MXFP4_OK;
+}
+
+void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mode,
+          mxfp4_moe_workspace_layout* L) {
+  const int64_t np = T * k;
+  const int64_t nchunks = (np + 1023) / 1024;
+  const int bm = act_mode == MXFP4_ACT_BF16 ? mx::kDecodeBM : mx::kPrefillBM;
+  size_t o = 0;
+  memset(L, 0, sizeof(*L));
+  L->status = o; o = up(o + mx::kStWords * 4);
+  L->expert_offsets = o; o = up(o + (size_t)(E + 1) * 4);
+  L->sorted_pairs = o; o = up(o + (size_t)np * 4);
+  L->inv_pairs = o; o = up(o + (size_t)np * 4);
+  L->chunk_counts = o; o = up(o + (size_t)nchunks * E * 4);
+  L->chunk_ranks = o; o = up(o + (size_t)np * 4);
+  L->tiles = o; o = up(o + (size_t)mx::max_tiles(np, E, bm) * 2 * 4);
+  if (act_mode == MXFP4_ACT_FP8_E4M3) {
+    L->x_codes = o; o = up(o + (size_t)T * H);
+    L->h = o; o = up(o + (size_t)np * I * 4);
+    L->h_codes = o; o = up(o + (size_t)np * I);
+  } else {
+    L->x_codes = o;
+    L->h = o; o = up(o + (size_t)np * I * 2 * 2);
+    L->h_codes = o;
+  }
+  L->y = o; o = up(o + (size_t)np * H * 4);
+  L->total_bytes = o;
+}
+
+mx::WsPtrs ws_ptrs(void* base, const mxfp4_moe_workspace_layout& L) {
+  uint8_t* b = static_cast<uint8_t*>(base);
+  mx::WsPtrs w;
+  w.status = reinterpret_cast<int*>(b + L.status);
+  w.offsets = reinterpret_cast<int*>(b + L.expert_offsets);
+  w.sorted_pairs = reinterpret_cast<int*>(b + L.sorted_pairs);
+  w.inv = reinterpret_cast<int*>(b + L.inv_pairs);
+  w.chunk_counts = reinterpret_cast<int*>(b + L.chunk_counts);
+  w.chunk_ranks = reinterpret_cast<int*>(b + L.chunk_ranks);
+  w.tiles = reinterpret_cast<int*>(b + L.tiles);
+  w.x_codes = b + L.x_codes;
+  w.h = b + L.h;
+  w.h_codes = b + L.h_codes;
+  w.y = reinterpret_cast<float*>(b + L.y);
+  return w;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MXFP4_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp4_abi_version(void) { return MXFP4_ABI_VERSION; }
+
+const char* mxfp4_status_string(int status) {
+  switch (status) {
+    case MXFP4_OK: return "ok";
+    case MXFP4_E_NULL: return "null pointer";
+    case MXFP4_E_SHAPE: return "bad shape";
+    case MXFP4_E_ALIGN: return "misaligned pointer";
+    case MXFP4_E_MODE: return "unknown mode";
+    case MXFP4_E_WORKSPACE: return "workspace too small";
+    case MXFP4_E_DEVICE: return "unsupported or missing device";
+    case MXFP4_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mxfp4_last_error(void) { return g_err; }
+
+int mxfp4_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                     float* topk_weights, void* stream) {
+  if (T < 0 || T > (1 << 24)) return fail(MXFP4_E_SHAPE, "T=%lld outside [0, 2^24]", (long long)T);
+  if (E < 1 || E > 512) return fail(MXFP4_E_SHAPE, "E=%d outside [1, 512]", E);
+  if (k < 1 || k > 16 || k > E) return fail(MXFP4_E_SHAPE, "k=%d outside [1, min(E, 16)]", k);
+  if (T == 0) return ok();
+  if (!logits || !topk_ids || !topk_weights) return fail(MXFP4_E_NULL, "route_topk: null pointer");
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+    return fail(MXFP4_E_ALIGN, "route_topk: pointers must be 4-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = mx::launch_route_topk(logits, (int)T, E, k, topk_ids, topk_weights,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "route_topk launch");
+  return ok();
+}
+
+int mxfp4_moe_workspace_layout_query(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                                     int32_t act_mode, mxfp4_moe_workspace_layout* layout) {
+  if (!layout) return fail(MXFP4_E_NULL, "layout is null");
+  int rc = moe_shape_check(T, H, I, E, k, act_mode);
+  if (rc) return rc;
+  plan(T, H, I, E, k, act_mode, layout);
+  return ok();
+}
+
+int mxfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                             int32_t act_mode, size_t* bytes) {
+  if (!bytes) return fail(MXFP4_E_NULL, "bytes is null");
+  mxfp4_moe_workspace_layout L;
+  int rc = mxfp4_moe_workspace_layout_query(T, H, I, E, k, act_mode, &L);
+  if (rc) return rc;
+  *bytes = L.total_bytes;
+  return ok();
+}
+
+int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                      const int32_t* topk_ids, const float* topk_weights,
+                      const uint8_t* w13_blocks, const uint8_t* w13_scales,
+                      const uint16_t* w13_bias, const uint8_t* w2_blocks,
+                      const uint8_t* w2_scales, const uint16_t* w2_bias, int32_t act_mode,
+                      uint16_t* out, void* workspace, size_t workspace_bytes,
+                      const mxfp4_moe_opts* opts, void* stream) {
+  int rc = moe_shape_check(T, H, I, E, k, act_mode);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if (!x || !topk_ids || !topk_weights || !w13_blocks || !w13_scales || !w2_blocks ||
+      !w2_scales || !out)
+    return fail(MXFP4_E_NULL, "moe_forward: null pointer");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w13_blocks, 16) ||
+      !aligned(w2_blocks, 16) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+      (w13_bias && !aligned(w13_bias, 2)) || (w2_bias && !aligned(w2_bias, 2)))
+    return fail(MXFP4_E_ALIGN, "moe_forward: x/out/blocks need 16-byte, ids/weights 4-byte alignment");
+  mxfp4_moe_workspace_layout L;
+  plan(T, H, I, E, k, act_mode, &L);
+  if (!workspace) return fail(MXFP4_E_WORKSPACE, "workspace is null");
+  if (!aligned(workspace, 256)) return fail(MXFP4_E_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total_bytes)
+    return fail(MXFP4_E_WORKSPACE, "workspace %zu bytes < required %llu", workspace_bytes,
+                (unsigned long long)L.total_bytes);
+  rc = check_device();
+  if (rc) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mx::WsPtrs ws = ws_ptrs(workspace, L);
+  const mx::MoeShape sh{(int)T, (int)H, (int)I, E, k};
+  const mx::MoeWeights w{w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias};
+  const bool fp8 = act_mode == MXFP4_ACT_FP8_E4M3;
+  const int bm = fp8 ? mx::kPrefillBM : mx::kDecodeBM;
+  const int64_t npairs = T * k;
+  const int64_t bound = mx::max_tiles(npairs, E, bm);
+
+  auto mark = [&](int stage) -> hipError_t {
+    if (opts && opts->events[stage])
+      return hipEventRecord(static_cast<hipEvent_t>(opts->events[stage]), s);
+    return hipSuccess;
+  };
+  hipError_t e;
+#define MX_STEP(call, what)                      \
+  do {                                           \
+    e = (call);                                  \
+    if (e != hipSuccess) return hip_fail(e, what); \
+  } while (0)
+
+  MX_STEP(mark(MXFP4_STAGE_BEGIN), "event record");
+  MX_STEP(mx::launch_permute(topk_ids, (int)npairs, E, bm, ws, s), "permute launch");
+  MX_STEP(mark(MXFP4_STAGE_PERMUTE), "event record");
+  if (fp8) {
+    MX_STEP(mx::launch_quant_fp8(x, true, T * H, ws.x_codes,
+                                 reinterpret_cast<uint32_t*>(ws.status + mx::kStAmaxX),
+                                 reinterpret_cast<float*>(ws.status + mx::kStScaleX), s),
+            "quant x launch");
+  }
+  MX_STEP(mark(MXFP4_STAGE_QUANT_X), "event record");
+  if (fp8) MX_STEP(mx::launch_moe_gateup_fp8(sh, w, ws, bound, s), "gate_up launch");
+  else MX_STEP(mx::launch_moe_gateup_bf16(x, sh, w, ws, bound, s), "gate_up launch");
+  MX_STEP(mark(MXFP4_STAGE_GEMM1), "event record");
+  if (fp8) {
+    MX_STEP(mx::launch_encode_fp8(ws.h, false, npairs * I, ws.h_codes,
+                                  reinterpret_cast<const uint32_t*>(ws.status + mx::kStAmaxH),
+                                  reinterpret_cast<float*>(ws.status + mx::kStScaleH), s),
+            "quant h launch");
+  }
+  MX_STEP(mark(MXFP4_STAGE_QUANT_H), "event record");
+  if (fp8) MX_STEP(mx::launch_moe_down_fp8(sh, w, ws, bound, s), "down launch");
+  else MX_STEP(mx::launch_moe_down_bf16(sh, w, ws, bound, s), "down launch");
+  MX_STEP(mark(MXFP4_STAGE_GEMM2), "event record");
+  MX_STEP(mx::launch_combine(sh, topk_weights, ws, out, s), "combine launch");
+  MX_STEP(mark(MXFP4_STAGE_COMBINE), "event record");
+#undef MX_STEP
+  return ok();
+}
+
+int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_blocks,
+                 const uint8_t* w_scales, const uint16_t* bias, uint16_t* out, void* stream) {
+  if (M < 0 || M > (1 << 20)) return fail(MXFP4_E_SHAPE, "M=%lld outside [0, 2^20]", (long long)M);
+  if (N <= 0 || N % 16 || N > (1LL << 26)) return fail(MXFP4_E_SHAPE, "N=%lld must be a positive multiple of 16", (long long)N);
+  if (K <= 0 || K % 32 || K > (1 << 20)) return fail(MXFP4_E_SHAPE, "K=%lld must be a positive multiple of 32", (long long)K);
+  if (M == 0) return ok();
+  if (!x || !w_blocks || !w_scales || !out) return fail(MXFP4_E_NULL, "linear: null pointer");
+  if (!aligned(x, 16) || !aligned(w_blocks, 16) || !aligned(out, 16) || (bias && !aligned(bias, 2)))
+    return fail(MXFP4_E_ALIGN, "linear: x, w_blocks and out need 16-byte alignment");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = mx::launch_linear_bf16(x, (int)M, (int)N, (int)K, w_blocks, w_scales, bias, out,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  return ok();
+}
+
+int mxfp4_quant_fp8_e4m3(const void* in, int32_t in_dtype, int64_t n, uint8_t* codes, float* scale,
+                         float* amax, void* stream) {
+  if (in_dtype != 0 && in_dtype != 1) return fail(MXFP4_E_MODE, "unknown in_dtype %d", in_dtype);
+  if (n < 0 || n > (1LL << 40)) return fail(MXFP4_E_SHAPE, "n=%lld out of range", (long long)n);
+  if (!scale || !amax) return fail(MXFP4_E_NULL, "quant: scale/amax null");
+  if (n > 0 && (!in || !codes)) return fail(MXFP4_E_NULL, "quant: null pointer");
+  if (!aligned(in, 16) || !aligned(codes, 16) || !aligned(scale, 4) || !aligned(amax, 4))
+    return fail(MXFP4_E_ALIGN, "quant: in/codes need 16-byte alignment");
+  int rc = check_device();
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mx::launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 0u, 1, s);
+  if (e != hipSuccess) return hip_fail(e, "quant init");
+  e = mx::launch_quant_fp8(in, in_dtype == 1, n, codes, reinterpret_cast<uint32_t*>(amax), scale, s);
+  if (e != hipSuccess) return hip_fail(e, "quant launch");
+  return ok();
+}
+
+int mxfp4_event_create(void** event) {
+  if (!event) return fail(MXFP4_E_NULL, "event is null");
+  hipEvent_t ev;
+  hipError_t e = hipEventCreate(&ev);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  *event = ev;
+  return ok();
+}
+
+int mxfp4_event_destroy(void* event) {
+  if (!event) return fail(MXFP4_E_NULL, "event is null");
+  hipError_t e = hipEventDestroy(static_cast<hipEvent_t>(event));
+  if (e != hipSuccess) return hip_fail(e, "hipEventDestroy");
+  return ok();
+}
+
+int mxfp4_event_elapsed_ms(void* start, void* end, float* ms) {
+  if (!start || !end || !ms) return fail(MXFP4_E_NULL, "event/ms is null");
+  hipError_t e = hipEventSynchronize(static_cast<hipEvent_t>(end));
+  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  e = hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(end));
+  if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Device helpers shared by the gfx950 kernels of the MXFP4 MoE library.
+//
+// Formats (gpt-oss page, "MXFP4 Tensor Structure"): E2M1 nibbles, two per
+// byte with the even element in the low nibble, 32 elements per 16-byte
+// block, one E8M0 scale byte 2^(s-127) per block.  Activations in the FP8
+// path use the OCP E4M3 encoding (bias 7, largest finite 448).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kBlockElems = 32;   // elements per MX block
+constexpr int kBlockBytes = 16;   // bytes per MX block of E2M1 nibbles
+
+// Indices of the int32 status words at the head of the MoE workspace.
+enum StatusWord {
+  kStFlags = 0,      // bit 0: a top-k id outside [0, E) was skipped
+  kStAmaxX = 1,      // fp32 bits of max|x| (FP8 mode)
+  kStAmaxH = 2,      // fp32 bits of max|h| (FP8 mode)
+  kStScaleX = 3,     // fp32 bits of the x scale
+  kStScaleH = 4,     // fp32 bits of the h scale
+  kStNumTiles = 5,   // number of (expert, row-tile) entries in the tile list
+  kStWords = 16
+};
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// E8M0 byte s -> 2^(s-127) as fp32, exact for s in [1, 254].
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s << 23);
+}
+
+// OCP E4M3 code of an fp32 value q: round to nearest, ties to even mantissa,
+// saturating to +-448, sign of zero kept.  q must not be NaN.
+__device__ __forceinline__ uint32_t e4m3_encode(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;          // |q| >= 448
+  if (a >= 0x3c800000u) {                               // |q| >= 2^-6: normal
+    // keep 3 mantissa bits: round the fp32 pattern at bit 20, ties to even
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    const uint32_t e = (r >> 23) - 120u;                // 127 - 7
+    const uint32_t m = (r >> 20) & 7u;
+    return sign | (e << 3) | m;
+  }
+  // subnormal: multiples of 2^-9; |q| * 512 is exact, rintf ties to even
+  const float n = rintf(__uint_as_float(a) * 512.0f);
+  return sign | (uint32_t)n;
+}
+
+// silu(z) = z / (1 + exp(-z)); exp overflow gives -0 for very negative z.
+__device__ __forceinline__ float silu(float z) {
+  return __fdividef(z, 1.0f + __expf(-z));
+}
+
+// Four E2M1 nibbles pairs (one dword = 8 elements) -> 8 bf16 scaled by `scale`
+// (a power of two), element order preserved (low nibble first).
+__device__ __forceinline__ v8bf fp4x8_to_bf16(uint32_t w, float scale) {
+  v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  v8bf r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 v) {
+  return __builtin_bit_cast(v8bf, v);
+}
+
+// Wave64 reductions (deterministic xor trees).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace mx

@@ -1,0 +1,82 @@
+// Host-side launch wrappers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mx {
+
+constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to here
+constexpr int kDecodeBM = 16;                // sorted rows per tile, bf16 path
+constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 path
+
+// Typed pointers into the caller's MoE workspace.
+struct WsPtrs {
+  int* status;
+  int* offsets;
+  int* sorted_pairs;
+  int* inv;
+  int* chunk_counts;
+  int* chunk_ranks;
+  int* tiles;
+  uint8_t* x_codes;
+  void* h;          // bf16 hi|lo (BF16 mode) or fp32 (FP8 mode)
+  uint8_t* h_codes;
+  float* y;
+};
+
+// Upper bound of the number of (expert, row-tile) entries.
+inline int64_t max_tiles(int64_t npairs, int64_t E, int BM) {
+  const int64_t busy = npairs < E ? npairs : E;
+  return npairs / BM + busy + 1;
+}
+
+struct MoeShape {
+  int T, H, I, E, k;
+};
+
+struct MoeWeights {
+  const uint8_t* w13_blocks;
+  const uint8_t* w13_scales;
+  const uint16_t* w13_bias;
+  const uint8_t* w2_blocks;
+  const uint8_t* w2_scales;
+  const uint16_t* w2_bias;
+};
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* ids, float* w,
+                             hipStream_t s);
+hipError_t launch_permute(const int* ids, int npairs, int E, int BM, const WsPtrs& ws,
+                          hipStream_t s);
+
+// FP8 quantisation of n values (fp32 or bf16 input); amax accumulates into
+// *amax_bits (must be zero beforehand), the scale is written to *scale_out.
+hipError_t launch_quant_fp8(const void* in, bool in_bf16, int64_t n, uint8_t* codes,
+                            uint32_t* amax_bits, float* scale_out, hipStream_t s);
+hipError_t launch_amax(const void* in, bool in_bf16, int64_t n, uint32_t* amax_bits,
+                       hipStream_t s);
+hipError_t launch_encode_fp8(const void* in, bool in_bf16, int64_t n, uint8_t* codes,
+                             const uint32_t* amax_bits, float* scale_out, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t s);
+
+// bf16-activation path (MFMA bf16 with weights expanded from FP4 in registers).
+hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const MoeWeights& w,
+                                  const WsPtrs& ws, int64_t ntile_bound, hipStream_t s);
+hipError_t launch_moe_down_bf16(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
+                                int64_t ntile_bound, hipStream_t s);
+hipError_t launch_linear_bf16(const uint16_t* x, int M, int N, int K, const uint8_t* wb,
+                              const uint8_t* ws, const uint16_t* bias, uint16_t* out,
+                              hipStream_t s);
+
+// FP8 x FP4 block-scaled MFMA path.
+hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
+                                 int64_t ntile_bound, hipStream_t s);
+hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
+                               int64_t ntile_bound, hipStream_t s);
+
+// out[t] = sum_j w[t,j] * y[inv[t*k+j]]  -> bf16
+hipError_t launch_combine(const MoeShape& sh, const float* topk_weights, const WsPtrs& ws,
+                          uint16_t* out, hipStream_t s);
+
+}  // namespace mx

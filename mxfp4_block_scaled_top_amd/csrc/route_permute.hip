@@ -1,0 +1,310 @@
+// Router top-k and the token-by-expert permutation (histogram, scan, stable
+// scatter) that regroups the T*k (token, slot) pairs by expert.
+//
+// gpt-oss page, "GPT-OSS-120B Architecture": each token is routed to 4 of
+// 128 experts.  gptoss-spark page, "What produced it, ranked": a MoE support
+// kernel that aligns tokens to experts was one of the measured wins; this is
+// the gfx950 version of that step.  Everything here is integer work except
+// the fp32 softmax of the k chosen logits.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mx {
+
+// ---------------------------------------------------------------- top-k ----
+// One wave per token; lane l holds logits l, l+64, ... (PER_LANE of them).
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int T, int E, int k,
+                                                         int* __restrict__ ids,
+                                                         float* __restrict__ weights) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  float v[PER_LANE];
+  bool avail[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    const int idx = lane + 64 * i;
+    avail[i] = idx < E;
+    v[i] = avail[i] ? row[idx] : 0.0f;
+  }
+  float my_val = 0.0f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    // best (largest value, then smallest index) among this lane's free entries
+    float bv = 0.0f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      const int idx = lane + 64 * i;
+      if (avail[i] && (bi == 0x7fffffff || v[i] > bv)) { bv = v[i]; bi = idx; }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      const bool take = oi != 0x7fffffff &&
+                        (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
+      if (take) { bv = ov; bi = oi; }
+    }
+    // the owner marks its entry as taken
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i)
+      if (lane + 64 * i == bi) avail[i] = false;
+    if (lane == j) { my_val = bv; my_id = bi; }
+  }
+  // softmax over the k chosen logits (lane 0 holds the largest)
+  const float vmax = __shfl(my_val, 0, 64);
+  const float z = lane < k ? expf(my_val - vmax) : 0.0f;
+  const float s = wave_sum(z);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = my_id;
+    weights[(size_t)t * k + lane] = z / s;
+  }
+}
+
+// ---------------------------------------------------------- permutation ----
+constexpr int kChunk = 1024;          // pairs ranked together by one block
+constexpr int kChunkWaves = kChunk / 64;
+
+// Exclusive scan of one int per thread over a 1024-thread block.
+// `tmp` holds kChunkWaves ints of LDS.  Returns the exclusive prefix; *total
+// receives the block sum.
+__device__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kChunkWaves ? tmp[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(wi, off, 64);
+      if (lane >= off) wi += o;
+    }
+    if (lane < kChunkWaves) tmp[lane] = wi - w;    // exclusive wave offsets
+    if (lane == kChunkWaves - 1) tmp[kChunkWaves] = wi;
+  }
+  __syncthreads();
+  const int res = tmp[wave] + incl - v;
+  *total = tmp[kChunkWaves];
+  __syncthreads();
+  return res;
+}
+
+// Lanes of this wave holding the same expert id e (valid lanes only).
+__device__ __forceinline__ uint64_t match_lanes(int e, bool valid, int id_bits) {
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < id_bits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    same &= bit ? bb : ~bb;
+  }
+  return valid ? same : 0ull;
+}
+
+// Within-chunk stable ranks.  Each of the 1024 threads holds pair base+tid
+// with expert e (valid only if in range).  wcnt is [kChunkWaves][E] LDS.
+// Returns the rank of the pair among the chunk's pairs of the same expert
+// (ascending pair index); afterwards wcnt[w][e] holds wave w's count of e.
+__device__ int chunk_rank(int e, bool valid, int E, int id_bits, int* wcnt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kChunkWaves * E; i += kChunk) wcnt[i] = 0;
+  __syncthreads();
+  const uint64_t same = match_lanes(e, valid, id_bits);
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const int rank_in_wave = __popcll(same & below);
+  const bool leader = valid && (same & below) == 0;
+  if (leader) wcnt[wave * E + e] = __popcll(same);
+  __syncthreads();
+  int pre = 0;
+  if (valid)
+    for (int w = 0; w < wave; ++w) pre += wcnt[w * E + e];
+  return pre + rank_in_wave;
+}
+
+__device__ __forceinline__ bool id_ok(int e, int E) { return e >= 0 && e < E; }
+
+// Tile list: expert e with n_e sorted rows contributes ceil(n_e / BM) entries
+// (e, offsets[e] + i*BM).  Called by a whole 1024-thread block with cnt and
+// off valid in LDS (E <= 1024).
+__device__ void write_tiles(const int* cnt, const int* off, int E, int BM, int* scan_tmp,
+                            int* tiles, int* status) {
+  const int e = threadIdx.x;
+  const int nt = (e < E) ? (cnt[e] + BM - 1) / BM : 0;
+  int total;
+  const int first = block_exclusive_scan(nt, scan_tmp, &total);
+  for (int i = 0; i < nt; ++i) {
+    tiles[2 * (first + i)] = e;
+    tiles[2 * (first + i) + 1] = off[e] + i * BM;
+  }
+  if (threadIdx.x == 0) status[kStNumTiles] = total;
+}
+
+// Single-block permutation for small pair counts (decode): counts, offsets,
+// stable scatter and tile list in one launch.  LDS: cnt[E], off[E], run[E],
+// wcnt[16*E] ints (dynamic) + static scan scratch.
+__global__ __launch_bounds__(1024) void permute_fused_kernel(
+    const int* __restrict__ ids, int npairs, int E, int id_bits, int BM,
+    int* __restrict__ status, int* __restrict__ offsets, int* __restrict__ sorted_pairs,
+    int* __restrict__ inv, int* __restrict__ tiles) {
+  extern __shared__ int lds[];
+  __shared__ int scan_tmp[kChunkWaves + 1];
+  int* cnt = lds;
+  int* off = lds + E;
+  int* run = lds + 2 * E;
+  int* wcnt = lds + 3 * E;
+  const int tid = threadIdx.x;
+  if (tid < kStWords && tid != kStNumTiles) status[tid] = 0;
+  for (int e = tid; e < E; e += kChunk) cnt[e] = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int p = tid; p < npairs; p += kChunk) {
+    const int e = ids[p];
+    if (id_ok(e, E)) atomicAdd(&cnt[e], 1); else bad = true;
+  }
+  __syncthreads();
+  int total;
+  const int ex = block_exclusive_scan(tid < E ? cnt[tid] : 0, scan_tmp, &total);
+  if (tid < E) { off[tid] = ex; run[tid] = ex; offsets[tid] = ex; }
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  for (int base = 0; base < npairs; base += kChunk) {
+    const int p = base + tid;
+    const int e = p < npairs ? ids[p] : -1;
+    const bool valid = p < npairs && id_ok(e, E);
+    const int r = chunk_rank(e, valid, E, id_bits, wcnt);
+    if (valid) {
+      const int pos = run[e] + r;
+      sorted_pairs[pos] = p;
+      inv[p] = pos;
+    } else if (p < npairs) {
+      inv[p] = -1;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kChunk) {
+      int c = 0;
+      for (int w = 0; w < kChunkWaves; ++w) c += wcnt[w * E + ee];
+      run[ee] += c;
+    }
+    __syncthreads();
+  }
+  if (bad) atomicOr(&status[kStFlags], 1);
+  write_tiles(cnt, off, E, BM, scan_tmp, tiles, status);
+}
+
+// Multi-block path, phase 1: per-chunk ranks and per-chunk expert counts.
+__global__ __launch_bounds__(1024) void permute_count_kernel(
+    const int* __restrict__ ids, int npairs, int E, int id_bits, int* __restrict__ status,
+    int* __restrict__ chunk_counts, int* __restrict__ chunk_ranks) {
+  extern __shared__ int wcnt[];
+  const int c = blockIdx.x;
+  const int p = c * kChunk + threadIdx.x;
+  const int e = p < npairs ? ids[p] : -1;
+  const bool valid = p < npairs && id_ok(e, E);
+  if (p < npairs && !valid) atomicOr(&status[kStFlags], 1);
+  const int r = chunk_rank(e, valid, E, id_bits, wcnt);
+  if (p < npairs) chunk_ranks[p] = valid ? r : -1;
+  for (int ee = threadIdx.x; ee < E; ee += kChunk) {
+    int s = 0;
+    for (int w = 0; w < kChunkWaves; ++w) s += wcnt[w * E + ee];
+    chunk_counts[(size_t)c * E + ee] = s;
+  }
+}
+
+// Phase 2 (one block): per-expert totals, offsets, per-chunk bases, tiles.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(
+    int nchunks, int E, int BM, int* __restrict__ status, int* __restrict__ offsets,
+    int* __restrict__ chunk_counts, int* __restrict__ tiles) {
+  __shared__ int cnt[1024];
+  __shared__ int off[1024];
+  __shared__ int scan_tmp[kChunkWaves + 1];
+  const int e = threadIdx.x;
+  int running = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = chunk_counts[(size_t)c * E + e];
+      chunk_counts[(size_t)c * E + e] = running;
+      running += v;
+    }
+    cnt[e] = running;
+  }
+  int total;
+  const int ex = block_exclusive_scan(e < E ? running : 0, scan_tmp, &total);
+  if (e < E) {
+    off[e] = ex;
+    offsets[e] = ex;
+    for (int c = 0; c < nchunks; ++c) chunk_counts[(size_t)c * E + e] += ex;
+  }
+  if (e == 0) offsets[E] = total;
+  __syncthreads();
+  write_tiles(cnt, off, E, BM, scan_tmp, tiles, status);
+}
+
+// Phase 3: scatter each pair to its sorted row.
+__global__ __launch_bounds__(1024) void permute_scatter_kernel(
+    const int* __restrict__ ids, int npairs, int E, const int* __restrict__ chunk_counts,
+    const int* __restrict__ chunk_ranks, int* __restrict__ sorted_pairs, int* __restrict__ inv) {
+  const int c = blockIdx.x;
+  const int p = c * kChunk + threadIdx.x;
+  if (p >= npairs) return;
+  const int e = ids[p];
+  const int r = chunk_ranks[p];
+  if (!id_ok(e, E) || r < 0) { inv[p] = -1; return; }
+  const int pos = chunk_counts[(size_t)c * E + e] + r;
+  sorted_pairs[pos] = p;
+  inv[p] = pos;
+}
+
+// Clears the status words (multi-block path; the fused kernel does it itself).
+__global__ void clear_status_kernel(int* status) {
+  if (threadIdx.x < kStWords) status[threadIdx.x] = 0;
+}
+
+// ------------------------------------------------------------- launchers ----
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* ids, float* w,
+                             hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64) route_topk_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 128) route_topk_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 256) route_topk_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else route_topk_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+static int id_bits_for(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+hipError_t launch_permute(const int* ids, int npairs, int E, int BM, const WsPtrs& ws,
+                          hipStream_t s) {
+  const int bits = id_bits_for(E);
+  if (npairs <= kFusedPermuteMaxPairs) {
+    const size_t lds = (size_t)(3 + kChunkWaves) * E * sizeof(int);
+    permute_fused_kernel<<<1, kChunk, lds, s>>>(ids, npairs, E, bits, BM, ws.status,
+                                                 ws.offsets, ws.sorted_pairs, ws.inv, ws.tiles);
+    return hipGetLastError();
+  }
+  const int nchunks = (npairs + kChunk - 1) / kChunk;
+  clear_status_kernel<<<1, 64, 0, s>>>(ws.status);
+  permute_count_kernel<<<nchunks, kChunk, (size_t)kChunkWaves * E * sizeof(int), s>>>(
+      ids, npairs, E, bits, ws.status, ws.chunk_counts, ws.chunk_ranks);
+  permute_scan_kernel<<<1, kChunk, 0, s>>>(nchunks, E, BM, ws.status, ws.offsets,
+                                           ws.chunk_counts, ws.tiles);
+  permute_scatter_kernel<<<nchunks, kChunk, 0, s>>>(ids, npairs, E, ws.chunk_counts,
+                                                    ws.chunk_ranks, ws.sorted_pairs, ws.inv);
+  return hipGetLastError();
+}
+
+}  // namespace mx

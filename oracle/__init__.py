@@ -27,13 +27,14 @@ Pins (see tests/test_oracle_*.py):
 from . import fp8, moe, mxfp4  # noqa: F401
 from .fp8 import e4m3_decode, e4m3_encode, quant_per_tensor  # noqa: F401
 from .moe import (ACT_BF16, ACT_FP8_E4M3, linear, linear_rows,  # noqa: F401
-                  moe_forward, permute, route_topk, swiglu)
+                  moe_forward, moe_forward_routed, permute, route_topk,
+                  swiglu)
 from .mxfp4 import (E2M1_TABLE, bf16_bits_to_f64, dequant,  # noqa: F401
                     e2m1_value, e8m0_scale, pack_nibbles, unpack_nibbles)
 
 __all__ = [
     "fp8", "moe", "mxfp4", "e4m3_decode", "e4m3_encode", "quant_per_tensor",
-    "ACT_BF16", "ACT_FP8_E4M3", "linear", "linear_rows", "moe_forward", "permute", "route_topk", "swiglu", "E2M1_TABLE",
+    "ACT_BF16", "ACT_FP8_E4M3", "linear", "linear_rows", "moe_forward", "moe_forward_routed", "permute", "route_topk", "swiglu", "E2M1_TABLE",
     "bf16_bits_to_f64", "dequant", "e2m1_value", "e8m0_scale",
     "pack_nibbles", "unpack_nibbles",
 ]

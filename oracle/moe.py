@@ -88,7 +88,7 @@ def _bias(bias_bits, shape):
 
 def moe_forward(x_bits, logits, w13_blocks, w13_scales, w13_bias,
                 w2_blocks, w2_scales, w2_bias, k=4, act_mode=ACT_BF16):
-    """One MoE layer.  Returns a dict of float64 results and intermediates.
+    """One MoE layer from router logits: route_topk, then moe_forward_routed.
 
     x_bits   uint16 [T, H]   bfloat16 activations
     logits   float32 [T, E]  router logits
@@ -99,14 +99,32 @@ def moe_forward(x_bits, logits, w13_blocks, w13_scales, w13_bias,
     act_mode ACT_BF16 (activations used as given) or ACT_FP8_E4M3
              (x and h each quantized with one per-tensor scale)
     """
+    ids, w = route_topk(logits, k)
+    res = moe_forward_routed(x_bits, ids, w, w13_blocks, w13_scales, w13_bias,
+                             w2_blocks, w2_scales, w2_bias, act_mode)
+    res.update(ids=ids, weights=w)
+    return res
+
+
+def moe_forward_routed(x_bits, ids, w, w13_blocks, w13_scales, w13_bias,
+                       w2_blocks, w2_scales, w2_bias, act_mode=ACT_BF16):
+    """One MoE layer for given routing: ids int [T, k], weights [T, k].
+
+    A pair whose id lies outside [0, E) contributes nothing to its token (the
+    HIP boundary skips such pairs); in FP8 mode it also takes no part in the
+    scale of h.  Returns a dict of float64 results and intermediates.
+    """
     x = bf16_bits_to_f64(x_bits)
     T, H = x.shape
     E = w13_blocks.shape[0]
     I = w2_blocks.shape[2] * 32
     if w13_blocks.shape[1] != 2 * I or w13_blocks.shape[2] * 32 != H:
         raise ValueError("inconsistent weight shapes")
-    ids, w = route_topk(logits, k)
-    res = {"ids": ids, "weights": w}
+    ids = np.asarray(ids, dtype=np.int64)
+    w = np.asarray(w, dtype=np.float64)
+    k = ids.shape[1]
+    valid = (ids >= 0) & (ids < E)
+    res = {}
 
     if act_mode == ACT_FP8_E4M3:
         xc, sx, _ = quant_per_tensor(x)
@@ -120,7 +138,7 @@ def moe_forward(x_bits, logits, w13_blocks, w13_scales, w13_bias,
     b1 = _bias(w13_bias, (E, 2 * I))
     b2 = _bias(w2_bias, (E, H))
     h = np.zeros((T, k, I))
-    experts = np.unique(ids)
+    experts = np.unique(ids[valid])
     for e in experts:
         t, j = np.nonzero(ids == e)
         W1 = dequant(w13_blocks[e], w13_scales[e])           # [2I, H]
@@ -130,8 +148,9 @@ def moe_forward(x_bits, logits, w13_blocks, w13_scales, w13_bias,
 
     if act_mode == ACT_FP8_E4M3:
         h32 = h.astype(np.float32).astype(np.float64)
-        hc, sh, _ = quant_per_tensor(h32)
-        hq = e4m3_decode(hc) * sh
+        hc, sh, _ = quant_per_tensor(h32[valid])
+        hq = np.zeros_like(h32)
+        hq[valid] = e4m3_decode(hc) * sh
         res.update(h32=h32, h_codes=hc, h_scale=sh)
     else:
         hq = h
@@ -142,7 +161,7 @@ def moe_forward(x_bits, logits, w13_blocks, w13_scales, w13_bias,
         W2 = dequant(w2_blocks[e], w2_scales[e])             # [H, I]
         y[t, j] = hq[t, j] @ W2.T + b2[e]
     res["y"] = y
-    res["out"] = np.einsum("tk,tkh->th", w, y)
+    res["out"] = np.einsum("tk,tkh->th", np.where(valid, w, 0.0), y)
     return res
 
 

@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching a device (runs without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4_moe.h")
+
+E_NULL, E_SHAPE, E_ALIGN, E_MODE, E_WORKSPACE, E_DEVICE = 1, 2, 3, 4, 5, 6
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mxfp4_block_scaled_top_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmxfp4moe.so is not built; run __graft_entry__.build()")
+    return _lib.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for must in ("mxfp4_route_topk", "mxfp4_moe_forward", "mxfp4_linear",
+                 "mxfp4_quant_fp8_e4m3", "mxfp4_moe_workspace_size"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.mxfp4_abi_version() == 1
+    assert L.mxfp4_status_string(0) == b"ok"
+    assert L.mxfp4_status_string(E_WORKSPACE) == b"workspace too small"
+    assert L.mxfp4_status_string(99) == b"unknown status"
+
+
+def _size(L, T, H, I, E, k, mode):
+    n = ctypes.c_size_t(0)
+    rc = L.mxfp4_moe_workspace_size(T, H, I, E, k, mode, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_validation(L):
+    rc, n = _size(L, 32, 2880, 2880, 128, 4, 0)
+    assert rc == 0 and n > 32 * 4 * 2880 * 4
+    rc8, n8 = _size(L, 2048, 2880, 2880, 128, 4, 1)
+    assert rc8 == 0 and n8 > n
+    assert _size(L, 4, 2880, 2880, 128, 4, 2)[0] == E_MODE          # unknown act_mode
+    assert _size(L, 4, 2880 + 16, 2880, 128, 4, 0)[0] == E_SHAPE    # H % 32
+    assert _size(L, 4, 2880, 0, 128, 4, 0)[0] == E_SHAPE
+    assert _size(L, 4, 2880, 2880, 128, 0, 0)[0] == E_SHAPE         # k < 1
+    assert _size(L, 4, 2880, 2880, 3, 4, 0)[0] == E_SHAPE           # k > E
+    assert _size(L, 4, 2880, 2880, 513, 4, 0)[0] == E_SHAPE
+    assert _size(L, -1, 2880, 2880, 128, 4, 0)[0] == E_SHAPE
+    assert L.mxfp4_moe_workspace_size(4, 2880, 2880, 128, 4, 0, None) == E_NULL
+    assert b"act_mode" in L.mxfp4_last_error() or L.mxfp4_last_error() != b""
+
+
+def test_layout_offsets_are_ordered_and_aligned(L):
+    from mxfp4_block_scaled_top_amd._lib import WorkspaceLayout
+    lay = WorkspaceLayout()
+    assert L.mxfp4_moe_workspace_layout_query(8192, 2880, 2880, 128, 4, 1, ctypes.byref(lay)) == 0
+    offs = [lay.status, lay.expert_offsets, lay.sorted_pairs, lay.inv_pairs, lay.chunk_counts,
+            lay.chunk_ranks, lay.tiles, lay.x_codes, lay.h, lay.h_codes, lay.y]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and lay.total_bytes > lay.y
+    assert lay.y - lay.h >= 8192 * 4 * 2880 * 5          # fp32 h + u8 codes
+
+
+def _fake(n=1):
+    return ctypes.c_void_p(0x1000 * n)     # never dereferenced: validation fails first
+
+
+def test_moe_forward_rejects_bad_arguments_without_touching_memory(L):
+    a = dict(x=_fake(1), T=4, H=2880, I=2880, E=128, k=4, ids=_fake(2), w=_fake(3), b13=_fake(4),
+             s13=_fake(5), bias13=None, b2=_fake(6), s2=_fake(7), bias2=None, mode=0, out=_fake(8),
+             ws=_fake(9), wsb=1 << 40, opts=None, stream=None)
+
+    def call(**kw):
+        d = dict(a, **kw)
+        return L.mxfp4_moe_forward(d["x"], d["T"], d["H"], d["I"], d["E"], d["k"], d["ids"], d["w"],
+                                   d["b13"], d["s13"], d["bias13"], d["b2"], d["s2"], d["bias2"],
+                                   d["mode"], d["out"], d["ws"], d["wsb"], d["opts"], d["stream"])
+    assert call(mode=7) == E_MODE
+    assert call(H=100) == E_SHAPE
+    assert call(k=17) == E_SHAPE
+    assert call(x=None) == E_NULL
+    assert call(out=None) == E_NULL
+    assert call(x=ctypes.c_void_p(0x1008)) == E_ALIGN
+    assert call(ws=ctypes.c_void_p(0x1010)) == E_ALIGN
+    assert call(ws=None) == E_WORKSPACE
+    assert call(wsb=100) == E_WORKSPACE
+    assert call(T=0) == 0                       # empty batch: a no-op
+
+
+def test_linear_and_quant_and_route_validation(L):
+    assert L.mxfp4_linear(_fake(), 1, 100, 2880, _fake(), _fake(), None, _fake(), None) == E_SHAPE
+    assert L.mxfp4_linear(_fake(), 1, 128, 2881, _fake(), _fake(), None, _fake(), None) == E_SHAPE
+    assert L.mxfp4_linear(None, 1, 128, 2880, _fake(), _fake(), None, _fake(), None) == E_NULL
+    assert L.mxfp4_linear(_fake(), 0, 128, 2880, _fake(), _fake(), None, _fake(), None) == 0
+    assert L.mxfp4_quant_fp8_e4m3(_fake(), 5, 10, _fake(), _fake(), _fake(), None) == E_MODE
+    assert L.mxfp4_quant_fp8_e4m3(_fake(), 0, 10, _fake(), None, _fake(), None) == E_NULL
+    assert L.mxfp4_route_topk(_fake(), 4, 128, 0, _fake(), _fake(), None) == E_SHAPE
+    assert L.mxfp4_route_topk(_fake(), 4, 600, 4, _fake(), _fake(), None) == E_SHAPE
+    assert L.mxfp4_route_topk(None, 4, 128, 4, _fake(), _fake(), None) == E_NULL
+    assert L.mxfp4_route_topk(None, 0, 128, 4, None, None, None) == 0
+
+
+def test_valid_call_without_a_gpu_reports_no_device(L):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert L.mxfp4_route_topk(_fake(), 4, 128, 4, _fake(), _fake(), None) == E_DEVICE
+    assert L.mxfp4_last_error() != b""

@@ -1,0 +1,371 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bars: top-k ids, permutation and FP8 codes bit-exact; layer outputs within
+relative Frobenius error 2e-3 and max |error| 2e-2 * rms(reference).
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import (assert_close, assert_close_rounded, bf16_bits_to_f64, bf16_dev_to_f64,
+                     errors, no_constant_rows, to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def mx():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import mxfp4_block_scaled_top_amd as m
+    m.lib()
+    return m
+
+
+def _layer_dev(L):
+    return {k: to_dev(v, torch) for k, v in L.items()}
+
+
+def _run_moe(mx, Ld, x_bits, ids, w, act_mode, want_ws=False):
+    T = x_bits.shape[0]
+    E, twoI = Ld["w13_blocks"].shape[:2]
+    H = x_bits.shape[1]
+    k = ids.shape[1]
+    ws_bytes = mx.mxfp4_moe_workspace_size(T, H, twoI // 2, E, k, act_mode)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = mx.mxfp4_moe_forward(to_dev(x_bits, torch), to_dev(ids.astype(np.int32), torch),
+                               to_dev(w.astype(np.float32), torch), Ld["w13_blocks"],
+                               Ld["w13_scales"], Ld["w13_bias"], Ld["w2_blocks"],
+                               Ld["w2_scales"], Ld["w2_bias"], act_mode, workspace=ws)
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out)
+    if not want_ws:
+        return got
+    lay = mx.mxfp4_moe_workspace_layout_query(T, H, twoI // 2, E, k, act_mode)
+    return got, ws, lay
+
+
+def _ws_view(ws, lay, key, dtype, count):
+    nbytes = np.dtype(dtype).itemsize * count
+    return ws[lay[key]:lay[key] + nbytes].cpu().numpy().view(dtype)
+
+
+def _status(ws, lay):
+    return _ws_view(ws, lay, "status", np.int32, 16)
+
+
+def _f32(bits):
+    return float(np.array([bits], dtype=np.int32).view(np.float32)[0])
+
+
+# ---------------------------------------------------------------- routing ----
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 128, 4), (7, 128, 4), (300, 128, 4), (33, 64, 1),
+                                   (65, 200, 8), (17, 512, 16), (5, 3, 3)])
+def test_route_topk_bit_exact(mx, T, E, k):
+    rng = np.random.default_rng(T * 1000 + E)
+    logits = rng.normal(size=(T, E)).astype(np.float32)
+    ids, w = mx.mxfp4_route_topk(to_dev(logits, torch), k)
+    ref_ids, ref_w = oracle.route_topk(logits, k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7)
+
+
+def test_route_topk_ties_and_signed_zero(mx):
+    rng = np.random.default_rng(3)
+    logits = rng.integers(-2, 3, size=(257, 128)).astype(np.float32)
+    logits[0] = 0.0
+    logits[1, ::3] = -0.0
+    logits[2] = -np.inf
+    logits[2, 77] = 1.0
+    ids, w = mx.mxfp4_route_topk(to_dev(logits, torch), 4)
+    ref_ids, ref_w = oracle.route_topk(logits, 4)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("name", list(synth.MOE_WORKLOADS))
+def test_route_topk_workloads(mx, name):
+    wl = synth.workload(name)
+    ids, w = mx.mxfp4_route_topk(to_dev(wl["logits"], torch), synth.TOPK_GPT_OSS)
+    ref_ids, ref_w = oracle.route_topk(wl["logits"], synth.TOPK_GPT_OSS)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------- fp8 codec ----
+
+
+@pytest.mark.parametrize("top", [-100, -10, 0, 3, 20, 100])
+def test_quant_fp8_exhaustive_bf16(mx, top):
+    bits = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        v = (bits << 16).view(np.float32)
+    keep = np.isfinite(v) & (np.abs(v) < np.float32(2.0 ** top))
+    vb = (bits[keep]).astype(np.uint16)
+    codes, scale, amax = mx.mxfp4_quant_fp8_e4m3(to_dev(vb, torch))
+    rc, rs, ra = oracle.quant_per_tensor(bf16_bits_to_f64(vb))
+    assert float(amax.item()) == ra
+    assert float(scale.item()) == rs
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("n", [0, 1, 17, 4096, 1000003])
+def test_quant_fp8_fp32_ragged(mx, n):
+    rng = np.random.default_rng(n)
+    v = (rng.standard_cauchy(n) * 3).astype(np.float32)
+    codes, scale, amax = mx.mxfp4_quant_fp8_e4m3(to_dev(v, torch))
+    rc, rs, ra = oracle.quant_per_tensor(v.astype(np.float64))
+    assert float(amax.item()) == ra and float(scale.item()) == rs
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+# -------------------------------------------------------------- permutation ----
+
+
+@pytest.mark.parametrize("T,E,k,hot", [(25, 16, 4, 0), (1024, 16, 4, 0), (1025, 16, 4, 3),
+                                       (5000, 64, 4, 5), (333, 16, 1, 0)])
+def test_permutation_bit_exact(mx, T, E, k, hot):
+    H = I = 64
+    L = synth.layer(seed=5, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(6, T, E=E, H=H, hot=hot)
+    ids, w = oracle.route_topk(logits, k)
+    for act in (synth.ACT_BF16, synth.ACT_FP8_E4M3):
+        got, ws, lay = _run_moe(mx, _layer_dev(L), x, ids, w, act, want_ws=True)
+        counts, offsets, sp, inv = oracle.permute(ids, E)
+        np_ = T * k
+        assert np.array_equal(_ws_view(ws, lay, "expert_offsets", np.int32, E + 1), offsets)
+        assert np.array_equal(_ws_view(ws, lay, "sorted_pairs", np.int32, np_), sp)
+        assert np.array_equal(_ws_view(ws, lay, "inv_pairs", np.int32, np_), inv)
+        bm = 16 if act == synth.ACT_BF16 else 128
+        assert _status(ws, lay)[5] == int(np.sum((counts + bm - 1) // bm))
+        assert _status(ws, lay)[0] == 0
+
+
+# ------------------------------------------------------------ small layers ----
+
+SMALL = [  # E, H, I, T, k   (H/32 and I/32 give every K tail modulo 4)
+    (8, 288, 320, 1, 4),
+    (8, 288, 320, 5, 4),
+    (8, 288, 320, 37, 4),
+    (16, 96, 128, 300, 4),
+    (4, 224, 64, 70, 2),
+    (1, 64, 96, 9, 1),
+]
+
+
+@pytest.mark.parametrize("E,H,I,T,k", SMALL)
+@pytest.mark.parametrize("act", [synth.ACT_BF16, synth.ACT_FP8_E4M3])
+def test_moe_small_layers(mx, E, H, I, T, k, act):
+    L = synth.layer(seed=E * 7 + H, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(T + 11, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    got, ws, lay = _run_moe(mx, _layer_dev(L), x, ids, w, act, want_ws=True)
+    ref = oracle.moe_forward_routed(x, ids, w, **L, act_mode=act)
+    assert_close_rounded(got, ref["out"], "E%d H%d I%d T%d act%d" % (E, H, I, T, act))
+    np_ = T * k
+    st = _status(ws, lay)
+    inv = _ws_view(ws, lay, "inv_pairs", np.int32, np_)
+    if act == synth.ACT_FP8_E4M3:
+        assert np.array_equal(_ws_view(ws, lay, "x_codes", np.uint8, T * H).reshape(T, H), ref["x_codes"])
+        assert _f32(st[3]) == ref["x_scale"]
+        h_gpu = _ws_view(ws, lay, "h", np.float32, np_ * I).reshape(np_, I)
+        hc_gpu = _ws_view(ws, lay, "h_codes", np.uint8, np_ * I).reshape(np_, I)
+        # the GPU's codes of h are the oracle codec applied to the GPU's own fp32 h
+        rc, rs, ra = oracle.quant_per_tensor(h_gpu.astype(np.float64))
+        assert _f32(st[2]) == ra and _f32(st[4]) == rs
+        assert np.array_equal(hc_gpu, rc)
+        # and h itself matches the oracle's h (sorted rows back to (t, j))
+        h_ref = ref["h"].reshape(np_, I)
+        rf, _, _ = errors(h_gpu[inv], h_ref)
+        assert rf < 1e-4
+    else:
+        hh = _ws_view(ws, lay, "h", np.uint16, 2 * np_ * I)
+        h_gpu = bf16_bits_to_f64(hh[:np_ * I]) + bf16_bits_to_f64(hh[np_ * I:])
+        rf, _, _ = errors(h_gpu.reshape(np_, I)[inv], ref["h"].reshape(np_, I))
+        assert rf < 1e-5
+        # bf16 outputs are the oracle rounded once, up to rare one-ulp flips
+        ref_bits = synth.f32_to_bf16_bits(ref["out"].astype(np.float32))
+        assert np.mean(got != bf16_bits_to_f64(ref_bits)) < 0.02
+
+
+def test_moe_edge_cases(mx):
+    E, H, I, T, k = 8, 64, 96, 40, 4
+    L = synth.layer(seed=77, E=E, H=H, I=I)
+    Ld = _layer_dev(L)
+    logits, x = synth.moe_inputs(78, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    for act in (synth.ACT_BF16, synth.ACT_FP8_E4M3):
+        # every token on the same four experts (one expert spans several tiles)
+        ids_hot = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+        got = _run_moe(mx, Ld, x, ids_hot, w, act)
+        assert_close_rounded(got, oracle.moe_forward_routed(x, ids_hot, w, **L, act_mode=act)["out"], "hot")
+        # duplicated expert inside a token, and ids out of range (skipped, flagged)
+        ids_bad = ids.copy()
+        ids_bad[0, 1] = ids_bad[0, 0]
+        ids_bad[3, 2] = -1
+        ids_bad[5, 0] = E + 5
+        got, ws, lay = _run_moe(mx, Ld, x, ids_bad, w, act, want_ws=True)
+        assert _status(ws, lay)[0] & 1
+        assert_close_rounded(got, oracle.moe_forward_routed(x, ids_bad, w, **L, act_mode=act)["out"], "bad ids")
+        # all-zero activations: outputs come from the biases alone
+        x0 = np.zeros_like(x)
+        got = _run_moe(mx, Ld, x0, ids, w, act)
+        assert_close_rounded(got, oracle.moe_forward_routed(x0, ids, w, **L, act_mode=act)["out"], "zero x")
+        # no bias
+        Lnb = dict(L, w13_bias=None, w2_bias=None)
+        Ldnb = dict(Ld, w13_bias=None, w2_bias=None)
+        got = _run_moe(mx, Ldnb, x, ids, w, act)
+        assert_close_rounded(got, oracle.moe_forward_routed(x, ids, w, **Lnb, act_mode=act)["out"], "no bias")
+
+
+def test_moe_wide_scales(mx):
+    E, H, I, T, k = 4, 128, 64, 16, 2
+    rng = np.random.default_rng(91)
+    L = synth.layer(seed=90, E=E, H=H, I=I)
+    L["w13_scales"] = rng.integers(100, 155, size=L["w13_scales"].shape, dtype=np.uint8)
+    L["w2_scales"] = rng.integers(100, 155, size=L["w2_scales"].shape, dtype=np.uint8)
+    logits, x = synth.moe_inputs(92, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    for act in (synth.ACT_BF16, synth.ACT_FP8_E4M3):
+        got = _run_moe(mx, _layer_dev(L), x, ids, w, act)
+        assert_close_rounded(got, oracle.moe_forward_routed(x, ids, w, **L, act_mode=act)["out"], "scales")
+
+
+def test_moe_zero_tokens_is_noop(mx):
+    L = synth.layer(seed=1, E=4, H=64, I=64)
+    Ld = _layer_dev(L)
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.zeros((0, 2), dtype=torch.float32, device="cuda")
+    out = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    mx.mxfp4_moe_forward(x, ids, w, Ld["w13_blocks"], Ld["w13_scales"], Ld["w13_bias"],
+                         Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"], 0, out=out,
+                         workspace=torch.zeros(256, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_moe_deterministic(mx):
+    E, H, I, T, k = 16, 96, 128, 300, 4
+    L = synth.layer(seed=3, E=E, H=H, I=I)
+    Ld = _layer_dev(L)
+    logits, x = synth.moe_inputs(4, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    for act in (synth.ACT_BF16, synth.ACT_FP8_E4M3):
+        a = _run_moe(mx, Ld, x, ids, w, act)
+        b = _run_moe(mx, Ld, x, ids, w, act)
+        assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ dense ----
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 32), (4, 48, 96), (17, 1040, 288), (33, 64, 4096),
+                                   (3, 5120, 2880), (1, 2880, 4096)])
+def test_linear_small_and_projection_shapes(mx, M, N, K):
+    D = synth.dense(M * 31 + N, N, K)
+    x = synth.dense_x(M + K, M, K)
+    out = mx.mxfp4_linear(to_dev(x, torch), to_dev(D["w_blocks"], torch), to_dev(D["w_scales"], torch),
+                          to_dev(D["bias"], torch))
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out)
+    ref = oracle.linear(x, D["w_blocks"], D["w_scales"], D["bias"])
+    assert_close_rounded(got, ref, "linear %dx%dx%d" % (M, N, K))
+    no_constant_rows(got)
+
+
+@pytest.mark.parametrize("name", ["qkv_proj", "o_proj", "lm_head"])
+@pytest.mark.parametrize("M", [1, 4])
+def test_linear_dense_set_full_size(mx, name, M):
+    N, K = synth.DENSE_SHAPES[name]
+    D = synth.dense(synth.DENSE_SEEDS[name], N, K)
+    x = synth.dense_x(synth.DENSE_X_SEED, M, K)
+    out = mx.mxfp4_linear(to_dev(x, torch), to_dev(D["w_blocks"], torch), to_dev(D["w_scales"], torch),
+                          to_dev(D["bias"], torch))
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out)
+    if N > 8192:   # lm_head: sampled rows, including both ends
+        rng = np.random.default_rng(5)
+        rows = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N),
+                                         rng.choice(N, 2048, replace=False)]))
+        ref = oracle.linear_rows(x, D["w_blocks"], D["w_scales"], D["bias"], rows)
+        got_s = got[:, rows]
+    else:
+        ref = oracle.linear(x, D["w_blocks"], D["w_scales"], D["bias"])
+        got_s = got
+    assert_close(got_s, ref, name)
+    no_constant_rows(got)
+
+
+def test_linear_no_bias_zero_rows(mx):
+    D = synth.dense(8, 64, 64)
+    x = synth.dense_x(9, 5, 64)
+    out = mx.mxfp4_linear(to_dev(x, torch), to_dev(D["w_blocks"], torch), to_dev(D["w_scales"], torch))
+    torch.cuda.synchronize()
+    assert_close_rounded(bf16_dev_to_f64(out), oracle.linear(x, D["w_blocks"], D["w_scales"]), "no bias")
+    empty = mx.mxfp4_linear(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"),
+                            to_dev(D["w_blocks"], torch), to_dev(D["w_scales"], torch))
+    assert empty.shape == (0, 64)
+
+
+# ------------------------------------------------- full-size MoE workloads ----
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    L = synth.layer()
+    return L, _layer_dev(L)
+
+
+@pytest.mark.parametrize("name", list(synth.MOE_WORKLOADS))
+def test_moe_full_size_workloads(mx, full_layer, name):
+    path = os.path.join(GOLDEN, "%s.npz" % name)
+    gold = np.load(path)
+    L, Ld = full_layer
+    wl = synth.workload(name)
+    act = wl["act_mode"]
+    ids_d, w_d = mx.mxfp4_route_topk(to_dev(wl["logits"], torch), synth.TOPK_GPT_OSS)
+    ref_ids, _ = oracle.route_topk(wl["logits"], synth.TOPK_GPT_OSS)
+    assert np.array_equal(ids_d.cpu().numpy(), ref_ids)
+    T, H = wl["x"].shape
+    I = synth.H_GPT_OSS
+    E = synth.E_GPT_OSS
+    k = synth.TOPK_GPT_OSS
+    ws_bytes = mx.mxfp4_moe_workspace_size(T, H, I, E, k, act)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = mx.mxfp4_moe_forward(to_dev(wl["x"], torch), ids_d, w_d, Ld["w13_blocks"], Ld["w13_scales"],
+                               Ld["w13_bias"], Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"], act,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out)
+    tokens = gold["tokens"]
+    assert_close(got[tokens], gold["out"].astype(np.float64), name)
+    no_constant_rows(got)
+    lay = mx.mxfp4_moe_workspace_layout_query(T, H, I, E, k, act)
+    st = _status(ws, lay)
+    assert st[0] == 0
+    if act == synth.ACT_FP8_E4M3:
+        xc_ref, sx, _ = oracle.quant_per_tensor(oracle.bf16_bits_to_f64(wl["x"]))
+        assert _f32(st[3]) == sx == float(gold["x_scale"])
+        assert np.array_equal(_ws_view(ws, lay, "x_codes", np.uint8, T * H).reshape(T, H), xc_ref)
+        # h: amax/scale from the GPU's own fp32 h, codes on a sample of rows
+        np_ = T * k
+        h_t = ws[lay["h"]:lay["h"] + np_ * I * 4].view(torch.float32).view(np_, I)
+        amax = float(h_t.abs().max().item())
+        assert _f32(st[2]) == amax
+        assert _f32(st[4]) == oracle.fp8.f32_scale(amax)
+        assert abs(amax - float(gold["h_amax"])) <= 1e-4 * float(gold["h_amax"])
+        rows = np.random.default_rng(1).choice(np_, 512, replace=False)
+        h_rows = h_t[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+        sh = _f32(st[4])
+        rc = oracle.e4m3_encode((h_rows / sh).astype(np.float32).astype(np.float64))
+        hc = ws[lay["h_codes"]:lay["h_codes"] + np_ * I].view(np_, I)[torch.from_numpy(rows).cuda()]
+        assert np.array_equal(hc.cpu().numpy(), rc)
