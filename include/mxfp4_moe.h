@@ -162,10 +162,10 @@ int mxfp4_moe_workspace_layout_query(int64_t T, int64_t H, int64_t I, int32_t E,
  *                                            0) and status bit 0 is set
  *   topk_weights fp32 [T, k]
  *   w13_blocks   uint8 [E, 2I, H/32, 16]     16-byte aligned
- *   w13_scales   uint8 [E, 2I, H/32]
+ *   w13_scales   uint8 [E, 2I, H/32]      4-byte aligned
  *   w13_bias     bf16 [E, 2I] or NULL (zero bias)
  *   w2_blocks    uint8 [E, H, I/32, 16]      16-byte aligned
- *   w2_scales    uint8 [E, H, I/32]
+ *   w2_scales    uint8 [E, H, I/32]       4-byte aligned
  *   w2_bias      bf16 [E, H] or NULL
  *   act_mode     MXFP4_ACT_BF16 or MXFP4_ACT_FP8_E4M3
  *   out          bf16 [T, H]                 16-byte aligned, must not alias
@@ -191,7 +191,7 @@ int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
  * activations, fp32 accumulation, one round-to-nearest-even to bf16.
  *   x         bf16 [M, K]          16-byte aligned
  *   w_blocks  uint8 [N, K/32, 16]  16-byte aligned
- *   w_scales  uint8 [N, K/32]      E8M0 bytes in [2, 252]
+ *   w_scales  uint8 [N, K/32]      4-byte aligned; E8M0 bytes in [2, 252]
  *   bias      bf16 [N] or NULL
  *   out       bf16 [M, N]          16-byte aligned, must not alias the inputs
  * Limits: K a positive multiple of 32, N a positive multiple of 16,

@@ -190,8 +190,9 @@ int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
     return fail(MXFP4_E_NULL, "moe_forward: null pointer");
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w13_blocks, 16) ||
       !aligned(w2_blocks, 16) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+      !aligned(w13_scales, 4) || !aligned(w2_scales, 4) ||
       (w13_bias && !aligned(w13_bias, 2)) || (w2_bias && !aligned(w2_bias, 2)))
-    return fail(MXFP4_E_ALIGN, "moe_forward: x/out/blocks need 16-byte, ids/weights 4-byte alignment");
+    return fail(MXFP4_E_ALIGN, "moe_forward: x/out/blocks need 16-byte, ids/weights/scales 4-byte alignment");
   mxfp4_moe_workspace_layout L;
   plan(T, H, I, E, k, act_mode, &L);
   if (!workspace) return fail(MXFP4_E_WORKSPACE, "workspace is null");
@@ -259,8 +260,9 @@ int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8
   if (K <= 0 || K % 32 || K > (1 << 20)) return fail(MXFP4_E_SHAPE, "K=%lld must be a positive multiple of 32", (long long)K);
   if (M == 0) return ok();
   if (!x || !w_blocks || !w_scales || !out) return fail(MXFP4_E_NULL, "linear: null pointer");
-  if (!aligned(x, 16) || !aligned(w_blocks, 16) || !aligned(out, 16) || (bias && !aligned(bias, 2)))
-    return fail(MXFP4_E_ALIGN, "linear: x, w_blocks and out need 16-byte alignment");
+  if (!aligned(x, 16) || !aligned(w_blocks, 16) || !aligned(out, 16) || !aligned(w_scales, 4) ||
+      (bias && !aligned(bias, 2)))
+    return fail(MXFP4_E_ALIGN, "linear: x, w_blocks and out need 16-byte, w_scales 4-byte alignment");
   int rc = check_device();
   if (rc) return rc;
   hipError_t e = mx::launch_linear_bf16(x, (int)M, (int)N, (int)K, w_blocks, w_scales, bias, out,

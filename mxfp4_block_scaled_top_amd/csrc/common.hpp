@@ -88,6 +88,19 @@ __device__ __forceinline__ v8bf as_v8bf(uint4 v) {
   return __builtin_bit_cast(v8bf, v);
 }
 
+// Streaming (nontemporal) loads for data read exactly once per call, such as
+// the weights: on gfx950 they keep the read stream from thrashing the caches
+// (measured: 6.3 TB/s for a plain 2 GiB read, against 5.0-5.4 TB/s with
+// ordinary loads).
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const uint8_t* p) {
+  const v4u_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_stream1(const uint8_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // Wave64 reductions (deterministic xor trees).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -3,13 +3,19 @@
 // lm_head at a few tokens).
 //
 // These are HBM-bound weight streams (gpt-oss page, "MXFP4 Tensor
-// Structure" for the layout; forum page, 59 tok/s "close to" the bandwidth
-// ceiling: decode is a bandwidth problem).  Design for gfx950:
-//   * each wave owns 16 weight rows (gate_up: 16 gate + the matching 16 up
-//     rows) and streams them with 16-byte loads, one MX block per lane per
-//     K-group of four blocks;
+// Structure" for the layout; forum page: decode runs close to the bandwidth
+// ceiling).  Design for gfx950:
+//   * a wave owns 16 weight rows (gate_up: 16 gate + the matching 16 up rows)
+//     and streams them with 16-byte loads, one MX block per lane per K-group
+//     of four blocks;
+//   * loads run DEPTH groups ahead through a statically indexed register
+//     ring, so a wave keeps several KB in flight and only waits for the group
+//     it is about to multiply;
+//   * when a launch has few row tiles (qkv/o projections, a handful of
+//     routed tokens) the K range of a row tile is split across KSPLIT waves
+//     of the block and the partial sums are added in LDS in a fixed order;
 //   * the E2M1 nibbles are expanded in registers with the scaled FP4->bf16
-//     convert (the E8M0 block scale folded in, exact for scale bytes 2..252)
+//     convert (the E8M0 block scale folded in; exact for scale bytes 2..252)
 //     and fed to v_mfma_f32_16x16x32_bf16 with the routed tokens as the 16
 //     columns; a K-group is four MFMAs, each taking 8 elements of the lane's
 //     own block, so the K order inside an MFMA is permuted identically for
@@ -24,6 +30,7 @@
 namespace mx {
 
 enum GemvMode { kGateUp = 0, kDown = 1, kDense = 2 };
+constexpr int kDepth = 3;   // K-groups in flight per wave
 
 struct GemvArgs {
   const uint8_t* wb;        // blocks [E, R, nb, 16]
@@ -34,6 +41,7 @@ struct GemvArgs {
   int nb;                   // K / 32
   const uint16_t* act;      // gate_up: x [T, K]; dense: x [M, K]; down: h hi [rows, K]
   const uint16_t* act_lo;   // down: h lo [rows, K]
+  uint32_t act_bytes;       // bytes of act (and of act_lo); < 2^31
   const int* sorted_pairs;
   int topk;
   const int* tiles;
@@ -45,12 +53,24 @@ struct GemvArgs {
   float* y;                 // down
 };
 
+// One K-group's operands for one lane.
 template <int MODE>
+struct Group {
+  uint4 w0, w1;        // 16 B of the lane's block: main/gate row, up row
+  uint32_t s0, s1;     // their E8M0 scales
+  uint4 b[4];          // 32 activations (bf16) of the lane's column
+  uint4 bl[4];         // down: the lo halves
+};
+
+template <int MODE, int KSPLIT>
 __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvArgs a) {
-  const int wave = threadIdx.x >> 6;
+  constexpr int kTilesPerBlock = 4 / KSPLIT;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;   // weight row inside the 16-row group / token column
   const int g = lane >> 4;   // which of the K-group's four blocks this lane loads
+  const int kpart = wave % KSPLIT;
+  const int rt = wave / KSPLIT;
 
   int e, row_begin, row_end;
   if (MODE == kDense) {
@@ -63,105 +83,127 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvArgs a) {
     row_begin = a.tiles[2 * blockIdx.y + 1];
     row_end = min(row_begin + kDecodeBM, a.offsets[e + 1]);
   }
-  const int n0 = (blockIdx.x * 4 + wave) * 16;
-  if (n0 >= a.nout) return;
+  const int n0 = (blockIdx.x * kTilesPerBlock + rt) * 16;
+  const bool tile_ok = n0 < a.nout;   // uniform per wave; no early return (LDS reduction below)
 
   // activation row feeding MFMA column r
   const int row = row_begin + r;
   const bool col_ok = row < row_end;
+  const int arow = col_ok ? row : row_begin;   // inactive columns read a valid row
   const uint16_t* act0 = a.act;
   const uint16_t* act1 = a.act_lo;
-  if (col_ok) {
-    if (MODE == kGateUp) {
-      const int t = a.sorted_pairs[row] / a.topk;
-      act0 += (size_t)t * a.nb * kBlockElems;
-    } else {
-      act0 += (size_t)row * a.nb * kBlockElems;
-      if (MODE == kDown) act1 += (size_t)row * a.nb * kBlockElems;
-    }
+  if (MODE == kGateUp) {
+    const int t = a.sorted_pairs[arow] / a.topk;
+    act0 += (size_t)t * a.nb * kBlockElems;
+  } else {
+    act0 += (size_t)arow * a.nb * kBlockElems;
+    if (MODE == kDown) act1 += (size_t)arow * a.nb * kBlockElems;
   }
 
-  const size_t wrow0 = (size_t)e * a.rows_per_expert + n0 + r;
+  const size_t wrow0 = (size_t)e * a.rows_per_expert + (tile_ok ? n0 + r : 0);
   const size_t wrow1 = wrow0 + a.nout;  // matching up row (gate_up only)
   const uint8_t* wb0 = a.wb + wrow0 * a.nb * kBlockBytes;
   const uint8_t* ws0 = a.ws + wrow0 * a.nb;
   const uint8_t* wb1 = a.wb + wrow1 * a.nb * kBlockBytes;
   const uint8_t* ws1 = a.ws + wrow1 * a.nb;
 
+  // this wave's share of the K-groups
+  const int ngroups = (a.nb + 3) >> 2;
+  const int g_begin = tile_ok ? (kpart * ngroups) / KSPLIT : 0;
+  const int g_end = tile_ok ? ((kpart + 1) * ngroups) / KSPLIT : 0;
+
+  // Loads are issued unconditionally so the outstanding-load count is the
+  // same on every path: a block past the end of K reads the last block with
+  // its scale forced to 0 (the expanded weights are then 0), and a column
+  // past the tile's rows reads a valid row whose results are discarded.
+  auto load = [&](int grp, Group<MODE>& G) {
+    const int j = grp * 4 + g;
+    const int jc = j < a.nb ? j : a.nb - 1;
+    G.w0 = ld_stream16(wb0 + (size_t)jc * kBlockBytes);
+    G.s0 = ld_stream1(ws0 + jc);
+    if (MODE == kGateUp) {
+      G.w1 = ld_stream16(wb1 + (size_t)jc * kBlockBytes);
+      G.s1 = ld_stream1(ws1 + jc);
+    }
+    const uint4* p = reinterpret_cast<const uint4*>(act0 + (size_t)jc * kBlockElems);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) G.b[q] = p[q];
+    if (MODE == kDown) {
+      const uint4* pl = reinterpret_cast<const uint4*>(act1 + (size_t)jc * kBlockElems);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) G.bl[q] = pl[q];
+    }
+  };
+
   v4f acc0 = {0.f, 0.f, 0.f, 0.f};
   v4f acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int ngroups = (a.nb + 3) >> 2;
-
-  // software pipeline: group grp+1 is loaded while grp is computed
-  uint4 w0n = {0, 0, 0, 0}, w1n = {0, 0, 0, 0};
-  uint32_t s0n = 0, s1n = 0;
-  uint4 bn[4], bln[4];
-  auto load_group = [&](int grp, uint4& w0, uint4& w1, uint32_t& s0, uint32_t& s1, uint4* b,
-                        uint4* bl) {
-    const int j = grp * 4 + g;
-    const bool jok = j < a.nb;
-    w0 = make_uint4(0, 0, 0, 0);
-    w1 = make_uint4(0, 0, 0, 0);
-    s0 = 0;
-    s1 = 0;
-    if (jok) {
-      w0 = *reinterpret_cast<const uint4*>(wb0 + (size_t)j * kBlockBytes);
-      s0 = ws0[j];
-      if (MODE == kGateUp) {
-        w1 = *reinterpret_cast<const uint4*>(wb1 + (size_t)j * kBlockBytes);
-        s1 = ws1[j];
-      }
-    }
+  auto compute = [&](int grp, const Group<MODE>& G) {
+    const bool jok = grp * 4 + g < a.nb;     // tail blocks: scale 0 zeroes the weights
+    const float f0 = jok ? e8m0_to_f32(G.s0) : 0.0f;
+    const uint32_t wv0[4] = {G.w0.x, G.w0.y, G.w0.z, G.w0.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      b[q] = make_uint4(0, 0, 0, 0);
-      if (MODE == kDown) bl[q] = make_uint4(0, 0, 0, 0);
+      const v8bf A0 = fp4x8_to_bf16(wv0[q], f0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, as_v8bf(G.b[q]), acc0, 0, 0, 0);
+      if (MODE == kDown)
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, as_v8bf(G.bl[q]), acc0, 0, 0, 0);
     }
-    if (jok && col_ok) {
-      const uint4* p = reinterpret_cast<const uint4*>(act0 + (size_t)j * kBlockElems);
+    if (MODE == kGateUp) {
+      const float f1 = jok ? e8m0_to_f32(G.s1) : 0.0f;
+      const uint32_t wv1[4] = {G.w1.x, G.w1.y, G.w1.z, G.w1.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[q] = p[q];
-      if (MODE == kDown) {
-        const uint4* pl = reinterpret_cast<const uint4*>(act1 + (size_t)j * kBlockElems);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bl[q] = pl[q];
+      for (int q = 0; q < 4; ++q) {
+        const v8bf A1 = fp4x8_to_bf16(wv1[q], f1);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, as_v8bf(G.b[q]), acc1, 0, 0, 0);
       }
     }
   };
 
-  load_group(0, w0n, w1n, s0n, s1n, bn, bln);
-  for (int grp = 0; grp < ngroups; ++grp) {
-    const uint4 w0 = w0n, w1 = w1n;
-    const uint32_t s0 = s0n, s1 = s1n;
-    uint4 b[4], bl[4];
+  // prefetch ring: group grp lives in ring[(grp - g_begin) % kDepth].  The
+  // steady-state loop refills after every multiply with no condition, so the
+  // compiler can keep kDepth groups outstanding; the tail drains the ring.
+  Group<MODE> ring[kDepth];
+  if (g_end - g_begin >= kDepth) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      b[q] = bn[q];
-      if (MODE == kDown) bl[q] = bln[q];
-    }
-    if (grp + 1 < ngroups) load_group(grp + 1, w0n, w1n, s0n, s1n, bn, bln);
-
-    const float f0 = e8m0_to_f32(s0);
-    const uint32_t wv0[4] = {w0.x, w0.y, w0.z, w0.w};
+    for (int u = 0; u < kDepth; ++u) load(g_begin + u, ring[u]);
+    int grp = g_begin;
+    for (; grp + 2 * kDepth <= g_end; grp += kDepth) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const v8bf A0 = fp4x8_to_bf16(wv0[q], f0);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, as_v8bf(b[q]), acc0, 0, 0, 0);
-      if (MODE == kDown)
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, as_v8bf(bl[q]), acc0, 0, 0, 0);
-    }
-    if (MODE == kGateUp) {
-      const float f1 = e8m0_to_f32(s1);
-      const uint32_t wv1[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const v8bf A1 = fp4x8_to_bf16(wv1[q], f1);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, as_v8bf(b[q]), acc1, 0, 0, 0);
+      for (int u = 0; u < kDepth; ++u) {
+        compute(grp + u, ring[u]);
+        load(grp + u + kDepth, ring[u]);
       }
+    }
+    // kDepth <= g_end - grp < 2 * kDepth groups remain, kDepth of them loaded
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      compute(grp + u, ring[u]);
+      if (grp + u + kDepth < g_end) load(grp + u + kDepth, ring[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u)
+      if (grp + kDepth + u < g_end) compute(grp + kDepth + u, ring[u]);
+  } else {
+    for (int grp = g_begin; grp < g_end; ++grp) {
+      load(grp, ring[0]);
+      compute(grp, ring[0]);
     }
   }
 
-  if (!col_ok) return;
+  if (KSPLIT > 1) {
+    // fixed-order reduction of the K parts of each row tile
+    __shared__ v4f part[4][2][64];
+    part[wave][0][lane] = acc0;
+    part[wave][1][lane] = acc1;
+    __syncthreads();
+    if (kpart != 0) return;
+    for (int kp = 1; kp < KSPLIT; ++kp) {
+      acc0 += part[wave + kp][0][lane];
+      acc1 += part[wave + kp][1][lane];
+    }
+  }
+  if (!col_ok || !tile_ok) return;
+
   // lane holds output rows n0 + 4g + jj (jj = 0..3) of token column r
   const int nbase = n0 + 4 * g;
   const uint16_t* bias_e = a.bias ? a.bias + (size_t)e * a.rows_per_expert : nullptr;
@@ -204,8 +246,242 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvArgs a) {
   }
 }
 
-static dim3 gemv_grid(int nout, int64_t ytiles) {
-  return dim3((unsigned)((nout + 63) / 64), (unsigned)ytiles);
+// ---------------------------------------------------------------------------
+// Streaming variant (decode-sized MoE GEMMs, lm_head).
+//   * A wave owns one weight tile whose bytes are contiguous in HBM: 16 rows
+//     (down, dense), or 8 gate rows plus the matching 8 up rows (gate_up; each
+//     8-row run is a whole number of 128-byte lines).  It copies the tile and
+//     its E8M0 scales by DMA (global -> LDS, 1 KB / 256 B per instruction,
+//     nontemporal) into its own LDS slice -- measured 6.7 TB/s for this
+//     pattern, against 3.7 TB/s for 16 rows x 64 B per register load -- and
+//     then reads it back in MFMA layout.  Many short-lived waves (6 per CU)
+//     keep ~140 KB of DMA in flight per CU, which loaded HBM latency needs.
+//   * Activations come through a range-checked buffer descriptor: MFMA
+//     columns past the tile's tokens get an out-of-range offset and read zeros
+//     without touching memory.
+//   * gate_up: one 16-row MFMA holds 8 gate rows (0-7) and their 8 up rows
+//     (8-15); the up result moves to the gate lane (lane ^ 32) for SwiGLU.
+constexpr int kStreamWaves = 2;                 // waves (tiles) per block
+constexpr int kStreamMaxWaveLds = 32 * 1024;    // LDS per wave (<= 64 KB per block)
+
+__host__ __device__ constexpr int chunks_of(int64_t bytes, int chunk) {
+  return (int)((bytes + chunk - 1) / chunk);
+}
+
+struct StreamPlan {
+  int wave;         // LDS bytes per wave: weights A | weights B | scales A | scales B
+  int wa, sa, sb;   // offsets of weights B, scales A, scales B
+};
+
+static StreamPlan stream_plan(int mode, int nb) {
+  StreamPlan p{};
+  const int64_t rb = (int64_t)nb * kBlockBytes;
+  const int rows = mode == kGateUp ? 8 : 16;
+  const int wchunk = chunks_of(rows * rb, 1024) * 1024;
+  const int schunk = chunks_of((int64_t)rows * nb, 256) * 256;
+  const bool pair = mode == kGateUp;
+  p.wa = wchunk;
+  p.sa = pair ? 2 * wchunk : wchunk;
+  p.sb = p.sa + schunk;
+  p.wave = pair ? p.sb + schunk : p.sa + schunk;
+  return p;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs a, StreamPlan P) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  constexpr bool kPair = MODE == kGateUp;
+  constexpr int kRowsA = kPair ? 8 : 16;
+
+  int e, row_begin, row_end;
+  if (MODE == kDense) {
+    e = 0;
+    row_begin = blockIdx.y * kDecodeBM;
+    row_end = min(row_begin + kDecodeBM, a.M);
+  } else {
+    if ((int)blockIdx.y >= a.status[kStNumTiles]) return;
+    e = a.tiles[2 * blockIdx.y];
+    row_begin = a.tiles[2 * blockIdx.y + 1];
+    row_end = min(row_begin + kDecodeBM, a.offsets[e + 1]);
+  }
+  const int n0 = (blockIdx.x * kStreamWaves + wave) * kRowsA;
+  if (n0 >= a.nout) return;   // no block-level synchronisation below
+
+  // activation row feeding MFMA column r; columns past the tile read zeros
+  const int row = row_begin + r;
+  const bool col_ok = row < row_end;
+  int arow = row;
+  if (MODE == kGateUp && col_ok) arow = a.sorted_pairs[row] / a.topk;
+  const uint32_t xbase = col_ok ? (uint32_t)arow * (uint32_t)(a.nb * kBlockElems * 2) : 0x80000000u;
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, (int)a.act_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(MODE == kDown ? a.act_lo : a.act), (short)0,
+                                        (int)a.act_bytes, 0x00020000);
+
+  // weights and scales: DMA into this wave's LDS slice
+  const int rb = a.nb * kBlockBytes;
+  uint8_t* sl = smem + wave * P.wave;
+  {
+    const int64_t region = (int64_t)kRowsA * rb;
+    const uint8_t* ga = a.wb + ((size_t)e * a.rows_per_expert + n0) * rb;
+    const uint8_t* gb = ga + (size_t)a.nout * rb;
+    const int nch = chunks_of(region, 1024);
+    for (int c = 0; c < nch; ++c) {   // tail lanes re-read the run's last 16 B into slack
+      const int64_t off = min((int64_t)c * 1024 + lane * 16, region - 16);
+      __builtin_amdgcn_global_load_lds(ga + off, sl + c * 1024, 16, 0, 2);
+      if (kPair) __builtin_amdgcn_global_load_lds(gb + off, sl + P.wa + c * 1024, 16, 0, 2);
+    }
+    const int64_t sreg = (int64_t)kRowsA * a.nb;   // every scale run is 4-byte aligned
+    const uint8_t* sga = a.ws + ((size_t)e * a.rows_per_expert + n0) * a.nb;
+    const uint8_t* sgb = sga + (size_t)a.nout * a.nb;
+    const int nsc = chunks_of(sreg, 256);
+    for (int c = 0; c < nsc; ++c) {
+      const int64_t off = min((int64_t)c * 256 + lane * 4, sreg - 4);
+      __builtin_amdgcn_global_load_lds(sga + off, sl + P.sa + c * 256, 4, 0, 2);
+      if (kPair) __builtin_amdgcn_global_load_lds(sgb + off, sl + P.sb + c * 256, 4, 0, 2);
+    }
+  }
+  const int wr = kPair ? (r & 7) : r;
+  const bool upper = kPair && r >= 8;
+  const uint8_t* lrow = sl + (upper ? P.wa : 0) + wr * rb;
+  const uint8_t* lsc = sl + (upper ? P.sb : P.sa) + wr * a.nb;
+
+  // activations run kXDepth groups ahead through a static ring
+  const int ngroups = (a.nb + 3) >> 2;
+  constexpr int kXDepth = MODE == kDown ? 3 : 4;
+  struct XGroup {
+    uint4 b[4];
+    uint4 bl[4];
+  };
+  auto fetch = [&](int grp, XGroup& X) {
+    const int j = grp * 4 + g;
+    const int jc = j < a.nb ? j : a.nb - 1;
+    const uint32_t off = xbase + (uint32_t)jc * (kBlockElems * 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * q, 0, 0);
+      X.b[q] = make_uint4(v.x, v.y, v.z, v.w);
+      if (MODE == kDown) {
+        const v4u_t vl = __builtin_amdgcn_raw_buffer_load_b128(lrs, off + 16 * q, 0, 0);
+        X.bl[q] = make_uint4(vl.x, vl.y, vl.z, vl.w);
+      }
+    }
+  };
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int grp, const XGroup& X) {
+    const int j = grp * 4 + g;
+    const bool jok = j < a.nb;
+    const int jc = jok ? j : a.nb - 1;
+    const uint4 w = *reinterpret_cast<const uint4*>(lrow + jc * kBlockBytes);
+    const float f = jok ? e8m0_to_f32(lsc[jc]) : 0.0f;   // tail blocks contribute 0
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v8bf A = fp4x8_to_bf16(wv[q], f);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(X.b[q]), acc, 0, 0, 0);
+      if (MODE == kDown) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(X.bl[q]), acc, 0, 0, 0);
+    }
+  };
+
+  XGroup ring[kXDepth];
+#pragma unroll
+  for (int u = 0; u < kXDepth; ++u)
+    if (u < ngroups) fetch(u, ring[u]);
+  __builtin_amdgcn_s_waitcnt(0);   // the wave's LDS tile (and the first groups) have landed
+  int grp = 0;
+  for (; grp + 2 * kXDepth <= ngroups; grp += kXDepth) {
+#pragma unroll
+    for (int u = 0; u < kXDepth; ++u) {
+      compute(grp + u, ring[u]);
+      fetch(grp + u + kXDepth, ring[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kXDepth; ++u) {
+    if (grp + u < ngroups) {
+      compute(grp + u, ring[u]);
+      if (grp + u + kXDepth < ngroups) fetch(grp + u + kXDepth, ring[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kXDepth; ++u)
+    if (grp + kXDepth + u < ngroups) compute(grp + kXDepth + u, ring[u]);
+
+  // lane (column r, group g) holds rows 4g + jj of column r
+  const uint16_t* bias_e = a.bias ? a.bias + (size_t)e * a.rows_per_expert : nullptr;
+  if (MODE == kGateUp) {
+    float upv[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) upv[jj] = __shfl_xor(acc[jj], 32, 64);
+    if (g >= 2 || !col_ok) return;
+    const int nbase = n0 + 4 * g;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float gate = acc[jj], up = upv[jj];
+      if (bias_e) {
+        gate += bf16_bits_to_f32(bias_e[nbase + jj]);
+        up += bf16_bits_to_f32(bias_e[a.nout + nbase + jj]);
+      }
+      const float h = silu(gate) * up;
+      hi[jj] = f32_to_bf16_bits(h);
+      lo[jj] = f32_to_bf16_bits(h - bf16_bits_to_f32(hi[jj]));
+    }
+    const size_t o = (size_t)row * a.nout + nbase;
+    *reinterpret_cast<uint2*>(a.out_hi + o) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+    *reinterpret_cast<uint2*>(a.out_lo + o) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+  } else {
+    if (!col_ok) return;
+    const int nbase = n0 + 4 * g;
+    float v[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      v[jj] = acc[jj];
+      if (bias_e) v[jj] += bf16_bits_to_f32(bias_e[nbase + jj]);
+    }
+    if (MODE == kDown) {
+      *reinterpret_cast<float4*>(a.y + (size_t)row * a.nout + nbase) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      const uint32_t o0 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+      const uint32_t o1 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+      *reinterpret_cast<uint2*>(a.out_hi + (size_t)row * a.nout + nbase) = make_uint2(o0, o1);
+    }
+  }
+}
+
+template <int MODE>
+static hipError_t launch_stream(const GemvArgs& a, int nout, int64_t ytiles, const StreamPlan& P,
+                                hipStream_t s) {
+  const int rows = MODE == kGateUp ? 8 : 16;
+  const int tiles = nout / rows;
+  const dim3 grid((unsigned)((tiles + kStreamWaves - 1) / kStreamWaves), (unsigned)ytiles);
+  gemv_stream_kernel<MODE><<<grid, 64 * kStreamWaves, kStreamWaves * P.wave, s>>>(a, P);
+  return hipGetLastError();
+}
+
+// Row tiles of 16 rows; KSPLIT waves per row tile, 4 waves per block.
+template <int MODE>
+static hipError_t launch_gemv(const GemvArgs& a, int nout, int64_t ytiles, int ksplit, hipStream_t s) {
+  const int per_block = 4 / ksplit;
+  const dim3 grid((unsigned)((nout / 16 + per_block - 1) / per_block), (unsigned)ytiles);
+  switch (ksplit) {
+    case 1: gemv_bf16_kernel<MODE, 1><<<grid, 256, 0, s>>>(a); break;
+    case 2: gemv_bf16_kernel<MODE, 2><<<grid, 256, 0, s>>>(a); break;
+    default: gemv_bf16_kernel<MODE, 4><<<grid, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+// Split K when the launch would have fewer than ~8 waves per CU otherwise.
+static int pick_ksplit(int64_t row_tiles) {
+  if (row_tiles >= 2048) return 1;
+  if (row_tiles >= 1024) return 2;
+  return 4;
 }
 
 hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const MoeWeights& w,
@@ -218,6 +494,8 @@ hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const M
   a.nout = sh.I;
   a.nb = sh.H / kBlockElems;
   a.act = x;
+  const size_t xbytes = (size_t)sh.T * sh.H * 2;
+  a.act_bytes = (uint32_t)(xbytes < (1u << 31) ? xbytes : 0);
   a.sorted_pairs = ws.sorted_pairs;
   a.topk = sh.k;
   a.tiles = ws.tiles;
@@ -226,8 +504,12 @@ hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const M
   uint16_t* h = static_cast<uint16_t*>(ws.h);
   a.out_hi = h;
   a.out_lo = h + (size_t)sh.T * sh.k * sh.I;
-  gemv_bf16_kernel<kGateUp><<<gemv_grid(sh.I, ntile_bound), 256, 0, s>>>(a);
-  return hipGetLastError();
+  // expected busy row tiles: one m-tile per routed pair at most
+  const int64_t pairs = (int64_t)sh.T * sh.k;
+  const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.I / 16);
+  const StreamPlan P = stream_plan(kGateUp, a.nb);
+  if (a.act_bytes && P.wave <= kStreamMaxWaveLds) return launch_stream<kGateUp>(a, sh.I, ntile_bound, P, s);
+  return launch_gemv<kGateUp>(a, sh.I, ntile_bound, pick_ksplit(busy), s);
 }
 
 hipError_t launch_moe_down_bf16(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
@@ -242,12 +524,17 @@ hipError_t launch_moe_down_bf16(const MoeShape& sh, const MoeWeights& w, const W
   const uint16_t* h = static_cast<const uint16_t*>(ws.h);
   a.act = h;
   a.act_lo = h + (size_t)sh.T * sh.k * sh.I;
+  const size_t hbytes = (size_t)sh.T * sh.k * sh.I * 2;
+  a.act_bytes = (uint32_t)(hbytes < (1u << 31) ? hbytes : 0);
   a.tiles = ws.tiles;
   a.offsets = ws.offsets;
   a.status = ws.status;
   a.y = ws.y;
-  gemv_bf16_kernel<kDown><<<gemv_grid(sh.H, ntile_bound), 256, 0, s>>>(a);
-  return hipGetLastError();
+  const int64_t pairs = (int64_t)sh.T * sh.k;
+  const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.H / 16);
+  const StreamPlan P = stream_plan(kDown, a.nb);
+  if (a.act_bytes && P.wave <= kStreamMaxWaveLds) return launch_stream<kDown>(a, sh.H, ntile_bound, P, s);
+  return launch_gemv<kDown>(a, sh.H, ntile_bound, pick_ksplit(busy), s);
 }
 
 hipError_t launch_linear_bf16(const uint16_t* x, int M, int N, int K, const uint8_t* wb,
@@ -261,10 +548,16 @@ hipError_t launch_linear_bf16(const uint16_t* x, int M, int N, int K, const uint
   a.nout = N;
   a.nb = K / kBlockElems;
   a.act = x;
+  const size_t xbytes = (size_t)M * K * 2;
+  a.act_bytes = (uint32_t)(xbytes < (1u << 31) ? xbytes : 0);
   a.M = M;
   a.out_hi = out;
-  gemv_bf16_kernel<kDense><<<gemv_grid(N, (M + 15) / 16), 256, 0, s>>>(a);
-  return hipGetLastError();
+  const int64_t mt = (M + 15) / 16;
+  const int64_t row_tiles = (int64_t)(N / 16) * mt;
+  const StreamPlan P = stream_plan(kDense, a.nb);
+  if (a.act_bytes && P.wave <= kStreamMaxWaveLds && row_tiles >= 2048)
+    return launch_stream<kDense>(a, N, (M + kDecodeBM - 1) / kDecodeBM, P, s);
+  return launch_gemv<kDense>(a, N, mt, pick_ksplit(row_tiles), s);
 }
 
 }  // namespace mx

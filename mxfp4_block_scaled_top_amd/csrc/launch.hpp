@@ -8,7 +8,7 @@
 namespace mx {
 
 constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to here
-constexpr int kDecodeBM = 16;                // sorted rows per tile, bf16 path
+constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
 constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 path
 
 // Typed pointers into the caller's MoE workspace.

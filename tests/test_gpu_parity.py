@@ -11,8 +11,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import (assert_close, assert_close_rounded, bf16_bits_to_f64, bf16_dev_to_f64,
-                     errors, no_constant_rows, to_dev)
+from helpers import (assert_close, assert_close_rounded, assert_close_slack, bf16_bits_to_f64,
+                     bf16_dev_to_f64, errors, no_constant_rows, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -145,7 +145,7 @@ def test_permutation_bit_exact(mx, T, E, k, hot):
         assert np.array_equal(_ws_view(ws, lay, "expert_offsets", np.int32, E + 1), offsets)
         assert np.array_equal(_ws_view(ws, lay, "sorted_pairs", np.int32, np_), sp)
         assert np.array_equal(_ws_view(ws, lay, "inv_pairs", np.int32, np_), inv)
-        bm = 16 if act == synth.ACT_BF16 else 128
+        bm = 4 if act == synth.ACT_BF16 else 128
         assert _status(ws, lay)[5] == int(np.sum((counts + bm - 1) // bm))
         assert _status(ws, lay)[0] == 0
 
@@ -347,7 +347,13 @@ def test_moe_full_size_workloads(mx, full_layer, name):
     torch.cuda.synchronize()
     got = bf16_dev_to_f64(out)
     tokens = gold["tokens"]
-    assert_close(got[tokens], gold["out"].astype(np.float64), name)
+    ref = gold["out"].astype(np.float64)
+    if act == synth.ACT_FP8_E4M3:
+        # outputs are unique except where an h code sits within the stated h
+        # error of a rounding boundary; the golden slack bounds that freedom
+        assert_close_slack(got[tokens], ref, gold["slack"], name)
+    else:
+        assert_close(got[tokens], ref, name)
     no_constant_rows(got)
     lay = mx.mxfp4_moe_workspace_layout_query(T, H, I, E, k, act)
     st = _status(ws, lay)
@@ -356,16 +362,23 @@ def test_moe_full_size_workloads(mx, full_layer, name):
         xc_ref, sx, _ = oracle.quant_per_tensor(oracle.bf16_bits_to_f64(wl["x"]))
         assert _f32(st[3]) == sx == float(gold["x_scale"])
         assert np.array_equal(_ws_view(ws, lay, "x_codes", np.uint8, T * H).reshape(T, H), xc_ref)
-        # h: amax/scale from the GPU's own fp32 h, codes on a sample of rows
         np_ = T * k
+        inv = _ws_view(ws, lay, "inv_pairs", np.int32, np_)
         h_t = ws[lay["h"]:lay["h"] + np_ * I * 4].view(torch.float32).view(np_, I)
+        # h within the error the slack assumes, on the sampled pairs
+        rel, absu = float(gold["h_rel_err"]), float(gold["h_abs_err"])
+        rows = torch.from_numpy(inv[gold["h_pairs"]].astype(np.int64)).cuda()
+        h_gpu = h_t[rows].cpu().numpy().astype(np.float64)
+        h_ref = gold["h_ref"].astype(np.float64)
+        assert np.all(np.abs(h_gpu - h_ref) <= rel * np.abs(h_ref) + absu * float(gold["h_scale"]))
+        # amax and scale from the GPU's own fp32 h, codes on a sample of rows
         amax = float(h_t.abs().max().item())
         assert _f32(st[2]) == amax
         assert _f32(st[4]) == oracle.fp8.f32_scale(amax)
-        assert abs(amax - float(gold["h_amax"])) <= 1e-4 * float(gold["h_amax"])
-        rows = np.random.default_rng(1).choice(np_, 512, replace=False)
-        h_rows = h_t[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+        assert abs(amax - float(gold["h_amax"])) <= rel * float(gold["h_amax"])
+        srows = np.random.default_rng(1).choice(np_, 512, replace=False)
+        h_rows = h_t[torch.from_numpy(srows).cuda()].cpu().numpy().astype(np.float64)
         sh = _f32(st[4])
         rc = oracle.e4m3_encode((h_rows / sh).astype(np.float32).astype(np.float64))
-        hc = ws[lay["h_codes"]:lay["h_codes"] + np_ * I].view(np_, I)[torch.from_numpy(rows).cuda()]
+        hc = ws[lay["h_codes"]:lay["h_codes"] + np_ * I].view(np_, I)[torch.from_numpy(srows).cuda()]
         assert np.array_equal(hc.cpu().numpy(), rc)
