@@ -236,6 +236,9 @@ def main():
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--primary-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy (3 times), the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requested %d)" % args.gpus,
@@ -247,8 +250,17 @@ def main():
     import mxfp4_block_scaled_top_amd as mx
     import synth
 
-    mx.lib()
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    if args.pmc_calibrate:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 512 << 20, "bytes_written": 512 << 20,
+                          "launches": 3}))
+        return
+    mx.lib()
     run = Runner(torch, mx)
     L = synth.layer()
     Ld = {k: run.dev(v) for k, v in L.items()}
@@ -272,7 +284,7 @@ def main():
         print("bench: dense set done", file=sys.stderr, flush=True)
 
     fp8 = prim["act"] != "bf16"
-    kname = "gemm_fp8_kernel<true>" if fp8 else "gemv_bf16_kernel<0>"
+    kname = "gemm_fp8_kernel<true, true>" if fp8 else "gemv_stream_kernel<0>"
     if fp8 and prim["tokens"] >= 4096:
         roof = dict(bound="mfma", achieved=prim["gemm1_TFLOPs"], peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=prim["gemm1_TFLOPs"] / FP8_PEAK_TFLOPS)
