@@ -193,8 +193,9 @@ def measure_dense(run, synth, steps, warmup):
     return out
 
 
-def cpu_baseline(synth, budget_tokens=4):
-    """The float64 oracle on the first tokens of the headline batch, on host cores."""
+def cpu_baseline(synth, budget_tokens=32):
+    """The float64 oracle on the first `budget_tokens` tokens of the headline batch (all 32 by
+    default: about 80 experts, several seconds), on host cores."""
     import oracle
     try:
         import threadpoolctl

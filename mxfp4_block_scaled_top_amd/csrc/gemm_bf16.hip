@@ -256,13 +256,24 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvArgs a) {
 //     pattern, against 3.7 TB/s for 16 rows x 64 B per register load -- and
 //     then reads it back in MFMA layout.  Many short-lived waves (6 per CU)
 //     keep ~140 KB of DMA in flight per CU, which loaded HBM latency needs.
-//   * Activations come through a range-checked buffer descriptor: MFMA
-//     columns past the tile's tokens get an out-of-range offset and read zeros
-//     without touching memory.
+//   * The tile's (at most 4) activation rows are loaded once, up front, in a
+//     compact layout: register set j holds in lane t + 4q + 16g the 8
+//     activations [128j + 32g + 8q, +8) of tile column t, so one 16-byte load
+//     per lane brings 256 contiguous bytes of each column (a quarter of the
+//     load instructions of an MFMA-layout load, whose lanes past column 3 would
+//     idle).  An MFMA step q takes its B operand from set j rotated by 4q lanes
+//     inside each 16-lane row (DPP), which puts column t's values in lane
+//     t + 16g.  Lanes of columns 4..15 then hold other columns' values; their
+//     MFMA outputs are never stored.  Columns past the tile's rows and blocks
+//     past K read through a range-checked buffer descriptor with an
+//     out-of-range offset, which returns zeros without touching memory.
 //   * gate_up: one 16-row MFMA holds 8 gate rows (0-7) and their 8 up rows
 //     (8-15); the up result moves to the gate lane (lane ^ 32) for SwiGLU.
 constexpr int kStreamWaves = 2;                 // waves (tiles) per block
 constexpr int kStreamMaxWaveLds = 32 * 1024;    // LDS per wave (<= 64 KB per block)
+constexpr int kStreamMaxGroups = 24;            // K <= 3072 on this path
+constexpr int kStreamCols = 4;                  // activation rows per tile
+static_assert(kStreamCols == kDecodeBM, "a decode tile feeds one stream tile");
 
 __host__ __device__ constexpr int chunks_of(int64_t bytes, int chunk) {
   return (int)((bytes + chunk - 1) / chunk);
@@ -287,6 +298,22 @@ static StreamPlan stream_plan(int mode, int nb) {
   return p;
 }
 
+static bool stream_fits(int mode, int nb, uint32_t act_bytes) {
+  return act_bytes != 0 && (nb + 3) / 4 <= kStreamMaxGroups &&
+         stream_plan(mode, nb).wave <= kStreamMaxWaveLds;
+}
+
+// Lane i of each 16-lane row takes lane (i + 4q) mod 16 of the same row.
+template <int Q>
+__device__ __forceinline__ uint4 row_rotate4(uint4 v) {
+  if (Q == 0) return v;
+  constexpr int ctrl = 0x120 + 16 - 4 * Q;   // DPP row_ror:(16 - 4Q)
+  return make_uint4((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, ctrl, 0xf, 0xf, true),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, ctrl, 0xf, 0xf, true),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, ctrl, 0xf, 0xf, true),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctrl, 0xf, 0xf, true));
+}
+
 template <int MODE>
 __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs a, StreamPlan P) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -300,28 +327,16 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs
   int e, row_begin, row_end;
   if (MODE == kDense) {
     e = 0;
-    row_begin = blockIdx.y * kDecodeBM;
-    row_end = min(row_begin + kDecodeBM, a.M);
+    row_begin = blockIdx.y * kStreamCols;
+    row_end = min(row_begin + kStreamCols, a.M);
   } else {
     if ((int)blockIdx.y >= a.status[kStNumTiles]) return;
     e = a.tiles[2 * blockIdx.y];
     row_begin = a.tiles[2 * blockIdx.y + 1];
-    row_end = min(row_begin + kDecodeBM, a.offsets[e + 1]);
+    row_end = min(row_begin + kStreamCols, a.offsets[e + 1]);
   }
   const int n0 = (blockIdx.x * kStreamWaves + wave) * kRowsA;
   if (n0 >= a.nout) return;   // no block-level synchronisation below
-
-  // activation row feeding MFMA column r; columns past the tile read zeros
-  const int row = row_begin + r;
-  const bool col_ok = row < row_end;
-  int arow = row;
-  if (MODE == kGateUp && col_ok) arow = a.sorted_pairs[row] / a.topk;
-  const uint32_t xbase = col_ok ? (uint32_t)arow * (uint32_t)(a.nb * kBlockElems * 2) : 0x80000000u;
-  const __amdgpu_buffer_rsrc_t xrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, (int)a.act_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t lrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(MODE == kDown ? a.act_lo : a.act), (short)0,
-                                        (int)a.act_bytes, 0x00020000);
 
   // weights and scales: DMA into this wave's LDS slice
   const int rb = a.nb * kBlockBytes;
@@ -346,73 +361,72 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs
       if (kPair) __builtin_amdgcn_global_load_lds(sgb + off, sl + P.sb + c * 256, 4, 0, 2);
     }
   }
+
+  // compact activation load (layout above): this lane reads column xt, chunk xq
+  const int ngroups = (a.nb + 3) >> 2;
+  const int xt = lane & 3;
+  const int xq = (lane >> 2) & 3;
+  const int xrow = row_begin + xt;
+  const bool xt_ok = xrow < row_end;
+  int arow = xrow;
+  if (MODE == kGateUp && xt_ok) arow = a.sorted_pairs[xrow] / a.topk;
+  const uint32_t rowb = (uint32_t)(a.nb * kBlockElems * 2);
+  const uint32_t xoff = (uint32_t)arow * rowb + (uint32_t)(32 * g + 8 * xq) * 2;
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, (int)a.act_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(MODE == kDown ? a.act_lo : a.act), (short)0,
+                                        (int)a.act_bytes, 0x00020000);
+  uint4 xa[kStreamMaxGroups];
+  uint4 xl[MODE == kDown ? kStreamMaxGroups : 1];
+#pragma unroll
+  for (int j = 0; j < kStreamMaxGroups; ++j) {
+    if (j < ngroups) {
+      const bool ok = xt_ok && 4 * j + g < a.nb;
+      const uint32_t off = ok ? xoff + 256u * j : 0x80000000u;
+      const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+      xa[j] = make_uint4(v.x, v.y, v.z, v.w);
+      if (MODE == kDown) {
+        const v4u_t vl = __builtin_amdgcn_raw_buffer_load_b128(lrs, off, 0, 0);
+        xl[j] = make_uint4(vl.x, vl.y, vl.z, vl.w);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // the wave's LDS tile and its activations have landed
+
   const int wr = kPair ? (r & 7) : r;
   const bool upper = kPair && r >= 8;
   const uint8_t* lrow = sl + (upper ? P.wa : 0) + wr * rb;
   const uint8_t* lsc = sl + (upper ? P.sb : P.sa) + wr * a.nb;
 
-  // activations run kXDepth groups ahead through a static ring
-  const int ngroups = (a.nb + 3) >> 2;
-  constexpr int kXDepth = MODE == kDown ? 3 : 4;
-  struct XGroup {
-    uint4 b[4];
-    uint4 bl[4];
+  // K order inside group j: lane group g takes block 4j + g, MFMA step q its
+  // elements 8q..8q+7 -- the same permutation for weights and activations.
+  v4f acc0 = {0.f, 0.f, 0.f, 0.f};
+  v4f acc1 = {0.f, 0.f, 0.f, 0.f};
+  auto step = [&](v4f& acc, const v8bf& A, const uint4& b, const uint4& bl) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(b), acc, 0, 0, 0);
+    if (MODE == kDown) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(bl), acc, 0, 0, 0);
   };
-  auto fetch = [&](int grp, XGroup& X) {
-    const int j = grp * 4 + g;
-    const int jc = j < a.nb ? j : a.nb - 1;
-    const uint32_t off = xbase + (uint32_t)jc * (kBlockElems * 2);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * q, 0, 0);
-      X.b[q] = make_uint4(v.x, v.y, v.z, v.w);
-      if (MODE == kDown) {
-        const v4u_t vl = __builtin_amdgcn_raw_buffer_load_b128(lrs, off + 16 * q, 0, 0);
-        X.bl[q] = make_uint4(vl.x, vl.y, vl.z, vl.w);
-      }
-    }
-  };
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int grp, const XGroup& X) {
-    const int j = grp * 4 + g;
-    const bool jok = j < a.nb;
-    const int jc = jok ? j : a.nb - 1;
-    const uint4 w = *reinterpret_cast<const uint4*>(lrow + jc * kBlockBytes);
-    const float f = jok ? e8m0_to_f32(lsc[jc]) : 0.0f;   // tail blocks contribute 0
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const v8bf A = fp4x8_to_bf16(wv[q], f);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(X.b[q]), acc, 0, 0, 0);
-      if (MODE == kDown) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(X.bl[q]), acc, 0, 0, 0);
-    }
-  };
-
-  XGroup ring[kXDepth];
-#pragma unroll
-  for (int u = 0; u < kXDepth; ++u)
-    if (u < ngroups) fetch(u, ring[u]);
-  __builtin_amdgcn_s_waitcnt(0);   // the wave's LDS tile (and the first groups) have landed
-  int grp = 0;
-  for (; grp + 2 * kXDepth <= ngroups; grp += kXDepth) {
-#pragma unroll
-    for (int u = 0; u < kXDepth; ++u) {
-      compute(grp + u, ring[u]);
-      fetch(grp + u + kXDepth, ring[u]);
+  for (int j = 0; j < kStreamMaxGroups; ++j) {
+    if (j < ngroups) {
+      const int blk = 4 * j + g;
+      const bool jok = blk < a.nb;
+      const int jc = jok ? blk : a.nb - 1;
+      const uint4 w = *reinterpret_cast<const uint4*>(lrow + jc * kBlockBytes);
+      const float f = jok ? e8m0_to_f32(lsc[jc]) : 0.0f;   // tail blocks contribute 0
+      const uint4 lo = MODE == kDown ? xl[j] : xa[j];
+      step(acc0, fp4x8_to_bf16(w.x, f), xa[j], lo);
+      step(acc1, fp4x8_to_bf16(w.y, f), row_rotate4<1>(xa[j]), row_rotate4<1>(lo));
+      step(acc0, fp4x8_to_bf16(w.z, f), row_rotate4<2>(xa[j]), row_rotate4<2>(lo));
+      step(acc1, fp4x8_to_bf16(w.w, f), row_rotate4<3>(xa[j]), row_rotate4<3>(lo));
     }
   }
-#pragma unroll
-  for (int u = 0; u < kXDepth; ++u) {
-    if (grp + u < ngroups) {
-      compute(grp + u, ring[u]);
-      if (grp + u + kXDepth < ngroups) fetch(grp + u + kXDepth, ring[u]);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kXDepth; ++u)
-    if (grp + kXDepth + u < ngroups) compute(grp + kXDepth + u, ring[u]);
+  const v4f acc = acc0 + acc1;
 
   // lane (column r, group g) holds rows 4g + jj of column r
+  const int row = row_begin + r;
+  const bool col_ok = r < kStreamCols && row < row_end;
   const uint16_t* bias_e = a.bias ? a.bias + (size_t)e * a.rows_per_expert : nullptr;
   if (MODE == kGateUp) {
     float upv[4];
@@ -508,7 +522,7 @@ hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const M
   const int64_t pairs = (int64_t)sh.T * sh.k;
   const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.I / 16);
   const StreamPlan P = stream_plan(kGateUp, a.nb);
-  if (a.act_bytes && P.wave <= kStreamMaxWaveLds) return launch_stream<kGateUp>(a, sh.I, ntile_bound, P, s);
+  if (stream_fits(kGateUp, a.nb, a.act_bytes)) return launch_stream<kGateUp>(a, sh.I, ntile_bound, P, s);
   return launch_gemv<kGateUp>(a, sh.I, ntile_bound, pick_ksplit(busy), s);
 }
 
@@ -533,7 +547,7 @@ hipError_t launch_moe_down_bf16(const MoeShape& sh, const MoeWeights& w, const W
   const int64_t pairs = (int64_t)sh.T * sh.k;
   const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.H / 16);
   const StreamPlan P = stream_plan(kDown, a.nb);
-  if (a.act_bytes && P.wave <= kStreamMaxWaveLds) return launch_stream<kDown>(a, sh.H, ntile_bound, P, s);
+  if (stream_fits(kDown, a.nb, a.act_bytes)) return launch_stream<kDown>(a, sh.H, ntile_bound, P, s);
   return launch_gemv<kDown>(a, sh.H, ntile_bound, pick_ksplit(busy), s);
 }
 
@@ -555,8 +569,8 @@ hipError_t launch_linear_bf16(const uint16_t* x, int M, int N, int K, const uint
   const int64_t mt = (M + 15) / 16;
   const int64_t row_tiles = (int64_t)(N / 16) * mt;
   const StreamPlan P = stream_plan(kDense, a.nb);
-  if (a.act_bytes && P.wave <= kStreamMaxWaveLds && row_tiles >= 2048)
-    return launch_stream<kDense>(a, N, (M + kDecodeBM - 1) / kDecodeBM, P, s);
+  if (stream_fits(kDense, a.nb, a.act_bytes) && row_tiles >= 2048)
+    return launch_stream<kDense>(a, N, (M + kStreamCols - 1) / kStreamCols, P, s);
   return launch_gemv<kDense>(a, N, mt, pick_ksplit(row_tiles), s);
 }
 
