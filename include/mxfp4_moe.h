@@ -100,7 +100,8 @@ typedef struct {
   uint64_t inv_pairs;       /* int32 [T*k]: sorted row of pair p */
   uint64_t chunk_counts;    /* int32 scratch of the permutation */
   uint64_t chunk_ranks;     /* int32 scratch of the permutation */
-  uint64_t tiles;           /* int32 [2 * max_tiles]: (expert, first sorted row) */
+  uint64_t tiles;           /* int32 [4 * max_tiles]: (expert, first sorted row, end row, 0);
+                               entries past the tile count have expert -1 */
   uint64_t x_codes;         /* uint8 [T, H] E4M3 codes of x (FP8 mode) */
   uint64_t h;               /* BF16 mode: bf16 hi [T*k, I] then bf16 lo [T*k, I]
                                with h = hi + lo; FP8 mode: fp32 [T*k, I];
@@ -163,10 +164,10 @@ int mxfp4_moe_workspace_layout_query(int64_t T, int64_t H, int64_t I, int32_t E,
  *   topk_weights fp32 [T, k]
  *   w13_blocks   uint8 [E, 2I, H/32, 16]     16-byte aligned
  *   w13_scales   uint8 [E, 2I, H/32]      4-byte aligned
- *   w13_bias     bf16 [E, 2I] or NULL (zero bias)
+ *   w13_bias     bf16 [E, 2I] or NULL (zero bias), 8-byte aligned
  *   w2_blocks    uint8 [E, H, I/32, 16]      16-byte aligned
  *   w2_scales    uint8 [E, H, I/32]       4-byte aligned
- *   w2_bias      bf16 [E, H] or NULL
+ *   w2_bias      bf16 [E, H] or NULL, 8-byte aligned
  *   act_mode     MXFP4_ACT_BF16 or MXFP4_ACT_FP8_E4M3
  *   out          bf16 [T, H]                 16-byte aligned, must not alias
  *                                            any input or the workspace
@@ -192,7 +193,7 @@ int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
  *   x         bf16 [M, K]          16-byte aligned
  *   w_blocks  uint8 [N, K/32, 16]  16-byte aligned
  *   w_scales  uint8 [N, K/32]      4-byte aligned; E8M0 bytes in [2, 252]
- *   bias      bf16 [N] or NULL
+ *   bias      bf16 [N] or NULL, 8-byte aligned
  *   out       bf16 [M, N]          16-byte aligned, must not alias the inputs
  * Limits: K a positive multiple of 32, N a positive multiple of 16,
  * 0 <= M <= 2^20 (M == 0 is a no-op).

@@ -82,7 +82,7 @@ void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mod
   L->inv_pairs = o; o = up(o + (size_t)np * 4);
   L->chunk_counts = o; o = up(o + (size_t)nchunks * E * 4);
   L->chunk_ranks = o; o = up(o + (size_t)np * 4);
-  L->tiles = o; o = up(o + (size_t)mx::max_tiles(np, E, bm) * 2 * 4);
+  L->tiles = o; o = up(o + (size_t)mx::max_tiles(np, E, bm) * mx::kTileInts * 4);
   if (act_mode == MXFP4_ACT_FP8_E4M3) {
     L->x_codes = o; o = up(o + (size_t)T * H);
     L->h = o; o = up(o + (size_t)np * I * 4);
@@ -191,8 +191,8 @@ int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w13_blocks, 16) ||
       !aligned(w2_blocks, 16) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
       !aligned(w13_scales, 4) || !aligned(w2_scales, 4) ||
-      (w13_bias && !aligned(w13_bias, 2)) || (w2_bias && !aligned(w2_bias, 2)))
-    return fail(MXFP4_E_ALIGN, "moe_forward: x/out/blocks need 16-byte, ids/weights/scales 4-byte alignment");
+      (w13_bias && !aligned(w13_bias, 8)) || (w2_bias && !aligned(w2_bias, 8)))
+    return fail(MXFP4_E_ALIGN, "moe_forward: x/out/blocks need 16-byte, biases 8-byte, ids/weights/scales 4-byte alignment");
   mxfp4_moe_workspace_layout L;
   plan(T, H, I, E, k, act_mode, &L);
   if (!workspace) return fail(MXFP4_E_WORKSPACE, "workspace is null");
@@ -225,7 +225,7 @@ int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
   } while (0)
 
   MX_STEP(mark(MXFP4_STAGE_BEGIN), "event record");
-  MX_STEP(mx::launch_permute(topk_ids, (int)npairs, E, bm, ws, s), "permute launch");
+  MX_STEP(mx::launch_permute(topk_ids, (int)npairs, E, bm, (int)bound, ws, s), "permute launch");
   MX_STEP(mark(MXFP4_STAGE_PERMUTE), "event record");
   if (fp8) {
     MX_STEP(mx::launch_quant_fp8(x, true, T * H, ws.x_codes,
@@ -261,8 +261,8 @@ int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8
   if (M == 0) return ok();
   if (!x || !w_blocks || !w_scales || !out) return fail(MXFP4_E_NULL, "linear: null pointer");
   if (!aligned(x, 16) || !aligned(w_blocks, 16) || !aligned(out, 16) || !aligned(w_scales, 4) ||
-      (bias && !aligned(bias, 2)))
-    return fail(MXFP4_E_ALIGN, "linear: x, w_blocks and out need 16-byte, w_scales 4-byte alignment");
+      (bias && !aligned(bias, 8)))
+    return fail(MXFP4_E_ALIGN, "linear: x, w_blocks and out need 16-byte, bias 8-byte, w_scales 4-byte alignment");
   int rc = check_device();
   if (rc) return rc;
   hipError_t e = mx::launch_linear_bf16(x, (int)M, (int)N, (int)K, w_blocks, w_scales, bias, out,

@@ -78,10 +78,11 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvArgs a) {
     row_begin = blockIdx.y * 16;
     row_end = min(row_begin + 16, a.M);
   } else {
-    if ((int)blockIdx.y >= a.status[kStNumTiles]) return;
-    e = a.tiles[2 * blockIdx.y];
-    row_begin = a.tiles[2 * blockIdx.y + 1];
-    row_end = min(row_begin + kDecodeBM, a.offsets[e + 1]);
+    const int4 tile = *reinterpret_cast<const int4*>(a.tiles + kTileInts * blockIdx.y);
+    if (tile.x < 0) return;
+    e = tile.x;
+    row_begin = tile.y;
+    row_end = tile.z;
   }
   const int n0 = (blockIdx.x * kTilesPerBlock + rt) * 16;
   const bool tile_ok = n0 < a.nout;   // uniform per wave; no early return (LDS reduction below)
@@ -330,15 +331,25 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs
     row_begin = blockIdx.y * kStreamCols;
     row_end = min(row_begin + kStreamCols, a.M);
   } else {
-    if ((int)blockIdx.y >= a.status[kStNumTiles]) return;
-    e = a.tiles[2 * blockIdx.y];
-    row_begin = a.tiles[2 * blockIdx.y + 1];
-    row_end = min(row_begin + kStreamCols, a.offsets[e + 1]);
+    const int4 tile = *reinterpret_cast<const int4*>(a.tiles + kTileInts * blockIdx.y);
+    if (tile.x < 0) return;
+    e = tile.x;
+    row_begin = tile.y;
+    row_end = tile.z;
   }
   const int n0 = (blockIdx.x * kStreamWaves + wave) * kRowsA;
   if (n0 >= a.nout) return;   // no block-level synchronisation below
+  const int ncols = row_end - row_begin;   // 1..kStreamCols
 
-  // weights and scales: DMA into this wave's LDS slice
+  // Everything the wave reads is requested before its first wait: the pair
+  // ids of its tile columns (scalar loads, so the vector wait below does not
+  // cover them), the weight DMA, the activation rows and the bias.
+  int pair[kStreamCols];
+  if (MODE == kGateUp) {
+#pragma unroll
+    for (int c = 0; c < kStreamCols; ++c)
+      pair[c] = a.sorted_pairs[__builtin_amdgcn_readfirstlane(row_begin + min(c, ncols - 1))];
+  }
   const int rb = a.nb * kBlockBytes;
   uint8_t* sl = smem + wave * P.wave;
   {
@@ -366,10 +377,14 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs
   const int ngroups = (a.nb + 3) >> 2;
   const int xt = lane & 3;
   const int xq = (lane >> 2) & 3;
-  const int xrow = row_begin + xt;
-  const bool xt_ok = xrow < row_end;
-  int arow = xrow;
-  if (MODE == kGateUp && xt_ok) arow = a.sorted_pairs[xrow] / a.topk;
+  int arow = row_begin + min(xt, ncols - 1);
+  if (MODE == kGateUp) {   // token of the lane's tile column
+    int p = pair[0];
+#pragma unroll
+    for (int c = 1; c < kStreamCols; ++c) p = xt == c ? pair[c] : p;
+    arow = p / a.topk;
+  }
+  const bool xt_ok = xt < ncols;
   const uint32_t rowb = (uint32_t)(a.nb * kBlockElems * 2);
   const uint32_t xoff = (uint32_t)arow * rowb + (uint32_t)(32 * g + 8 * xq) * 2;
   const __amdgpu_buffer_rsrc_t xrs =
@@ -392,7 +407,16 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);   // the wave's LDS tile and its activations have landed
+  // bias of the output rows this lane stores (rows n0 + 4g .. +3; gate_up: the
+  // gate lanes g < 2 also need the matching up rows)
+  const int nbase = n0 + 4 * (kPair ? (g & 1) : g);
+  uint2 bias_a = make_uint2(0, 0), bias_b = make_uint2(0, 0);
+  if (a.bias) {
+    const uint16_t* be = a.bias + (size_t)e * a.rows_per_expert + nbase;
+    bias_a = *reinterpret_cast<const uint2*>(be);
+    if (kPair) bias_b = *reinterpret_cast<const uint2*>(be + a.nout);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // the wave's LDS tile, activations and bias have landed
 
   const int wr = kPair ? (r & 7) : r;
   const bool upper = kPair && r >= 8;
@@ -407,14 +431,22 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(b), acc, 0, 0, 0);
     if (MODE == kDown) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(bl), acc, 0, 0, 0);
   };
+  // the LDS reads of group j + 1 are issued before group j's multiplies
+  auto lds_group = [&](int j, uint4& w, uint32_t& sc) {
+    const int blk = 4 * j + g;
+    const int jc = blk < a.nb ? blk : a.nb - 1;
+    w = *reinterpret_cast<const uint4*>(lrow + jc * kBlockBytes);
+    sc = lsc[jc];
+  };
+  uint4 wn;
+  uint32_t sn;
+  lds_group(0, wn, sn);
 #pragma unroll
   for (int j = 0; j < kStreamMaxGroups; ++j) {
     if (j < ngroups) {
-      const int blk = 4 * j + g;
-      const bool jok = blk < a.nb;
-      const int jc = jok ? blk : a.nb - 1;
-      const uint4 w = *reinterpret_cast<const uint4*>(lrow + jc * kBlockBytes);
-      const float f = jok ? e8m0_to_f32(lsc[jc]) : 0.0f;   // tail blocks contribute 0
+      const uint4 w = wn;
+      const float f = 4 * j + g < a.nb ? e8m0_to_f32(sn) : 0.0f;   // tail blocks contribute 0
+      if (j + 1 < ngroups) lds_group(j + 1, wn, sn);
       const uint4 lo = MODE == kDown ? xl[j] : xa[j];
       step(acc0, fp4x8_to_bf16(w.x, f), xa[j], lo);
       step(acc1, fp4x8_to_bf16(w.y, f), row_rotate4<1>(xa[j]), row_rotate4<1>(lo));
@@ -426,22 +458,20 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs
 
   // lane (column r, group g) holds rows 4g + jj of column r
   const int row = row_begin + r;
-  const bool col_ok = r < kStreamCols && row < row_end;
-  const uint16_t* bias_e = a.bias ? a.bias + (size_t)e * a.rows_per_expert : nullptr;
+  const bool col_ok = r < ncols;
+  const float bia[4] = {bf16_bits_to_f32(bias_a.x & 0xffffu), bf16_bits_to_f32(bias_a.x >> 16),
+                        bf16_bits_to_f32(bias_a.y & 0xffffu), bf16_bits_to_f32(bias_a.y >> 16)};
   if (MODE == kGateUp) {
     float upv[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) upv[jj] = __shfl_xor(acc[jj], 32, 64);
     if (g >= 2 || !col_ok) return;
-    const int nbase = n0 + 4 * g;
+    const float bib[4] = {bf16_bits_to_f32(bias_b.x & 0xffffu), bf16_bits_to_f32(bias_b.x >> 16),
+                          bf16_bits_to_f32(bias_b.y & 0xffffu), bf16_bits_to_f32(bias_b.y >> 16)};
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      float gate = acc[jj], up = upv[jj];
-      if (bias_e) {
-        gate += bf16_bits_to_f32(bias_e[nbase + jj]);
-        up += bf16_bits_to_f32(bias_e[a.nout + nbase + jj]);
-      }
+      const float gate = acc[jj] + bia[jj], up = upv[jj] + bib[jj];
       const float h = silu(gate) * up;
       hi[jj] = f32_to_bf16_bits(h);
       lo[jj] = f32_to_bf16_bits(h - bf16_bits_to_f32(hi[jj]));
@@ -451,13 +481,9 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs
     *reinterpret_cast<uint2*>(a.out_lo + o) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
   } else {
     if (!col_ok) return;
-    const int nbase = n0 + 4 * g;
     float v[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      v[jj] = acc[jj];
-      if (bias_e) v[jj] += bf16_bits_to_f32(bias_e[nbase + jj]);
-    }
+    for (int jj = 0; jj < 4; ++jj) v[jj] = acc[jj] + bia[jj];
     if (MODE == kDown) {
       *reinterpret_cast<float4*>(a.y + (size_t)row * a.nout + nbase) = make_float4(v[0], v[1], v[2], v[3]);
     } else {

@@ -79,10 +79,11 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 // expanded operands, else the block-scaled FP4 x FP8 MFMA.
 template <bool GATEUP, bool EXACT>
 __global__ __launch_bounds__(256, 2) void gemm_fp8_kernel(Fp8Args a) {
-  if ((int)blockIdx.y >= a.status[kStNumTiles]) return;
-  const int e = a.tiles[2 * blockIdx.y];
-  const int row_begin = a.tiles[2 * blockIdx.y + 1];
-  const int row_end = min(row_begin + kBM, a.offsets[e + 1]);
+  const int4 tile = *reinterpret_cast<const int4*>(a.tiles + kTileInts * blockIdx.y);
+  if (tile.x < 0) return;
+  const int e = tile.x;
+  const int row_begin = tile.y;
+  const int row_end = tile.z;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;

@@ -10,6 +10,9 @@ namespace mx {
 constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to here
 constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
 constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 path
+// A row tile is 4 ints: expert, first sorted row, end row (exclusive), 0.
+// Entries past the number of tiles (up to max_tiles) hold expert -1.
+constexpr int kTileInts = 4;
 
 // Typed pointers into the caller's MoE workspace.
 struct WsPtrs {
@@ -47,8 +50,8 @@ struct MoeWeights {
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* ids, float* w,
                              hipStream_t s);
-hipError_t launch_permute(const int* ids, int npairs, int E, int BM, const WsPtrs& ws,
-                          hipStream_t s);
+hipError_t launch_permute(const int* ids, int npairs, int E, int BM, int tile_bound,
+                          const WsPtrs& ws, hipStream_t s);
 
 // FP8 quantisation of n values (fp32 or bf16 input); amax accumulates into
 // *amax_bits (must be zero beforehand), the scale is written to *scale_out.

@@ -135,18 +135,23 @@ __device__ int chunk_rank(int e, bool valid, int E, int id_bits, int* wcnt) {
 __device__ __forceinline__ bool id_ok(int e, int E) { return e >= 0 && e < E; }
 
 // Tile list: expert e with n_e sorted rows contributes ceil(n_e / BM) entries
-// (e, offsets[e] + i*BM).  Called by a whole 1024-thread block with cnt and
-// off valid in LDS (E <= 1024).
-__device__ void write_tiles(const int* cnt, const int* off, int E, int BM, int* scan_tmp,
-                            int* tiles, int* status) {
+// (e, offsets[e] + i*BM, min(offsets[e] + (i+1)*BM, offsets[e] + n_e), 0);
+// entries from the tile count up to `bound` get expert -1, so a GEMM block
+// learns everything about its tile from one 16-byte read.  Called by a whole
+// 1024-thread block with cnt and off valid in LDS (E <= 1024).
+__device__ void write_tiles(const int* cnt, const int* off, int E, int BM, int bound,
+                            int* scan_tmp, int* tiles, int* status) {
   const int e = threadIdx.x;
   const int nt = (e < E) ? (cnt[e] + BM - 1) / BM : 0;
   int total;
   const int first = block_exclusive_scan(nt, scan_tmp, &total);
   for (int i = 0; i < nt; ++i) {
-    tiles[2 * (first + i)] = e;
-    tiles[2 * (first + i) + 1] = off[e] + i * BM;
+    const int b = off[e] + i * BM;
+    const int end = off[e] + cnt[e];
+    *reinterpret_cast<int4*>(tiles + kTileInts * (first + i)) = make_int4(e, b, min(b + BM, end), 0);
   }
+  for (int t = total + (int)threadIdx.x; t < bound; t += (int)blockDim.x)
+    *reinterpret_cast<int4*>(tiles + kTileInts * t) = make_int4(-1, 0, 0, 0);
   if (threadIdx.x == 0) status[kStNumTiles] = total;
 }
 
@@ -154,7 +159,7 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int BM, int* 
 // stable scatter and tile list in one launch.  LDS: cnt[E], off[E], run[E],
 // wcnt[16*E] ints (dynamic) + static scan scratch.
 __global__ __launch_bounds__(1024) void permute_fused_kernel(
-    const int* __restrict__ ids, int npairs, int E, int id_bits, int BM,
+    const int* __restrict__ ids, int npairs, int E, int id_bits, int BM, int bound,
     int* __restrict__ status, int* __restrict__ offsets, int* __restrict__ sorted_pairs,
     int* __restrict__ inv, int* __restrict__ tiles) {
   extern __shared__ int lds[];
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
     __syncthreads();
   }
   if (bad) atomicOr(&status[kStFlags], 1);
-  write_tiles(cnt, off, E, BM, scan_tmp, tiles, status);
+  write_tiles(cnt, off, E, BM, bound, scan_tmp, tiles, status);
 }
 
 // Multi-block path, phase 1: per-chunk ranks and per-chunk expert counts.
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(
 
 // Phase 2 (one block): per-expert totals, offsets, per-chunk bases, tiles.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
-    int nchunks, int E, int BM, int* __restrict__ status, int* __restrict__ offsets,
+    int nchunks, int E, int BM, int bound, int* __restrict__ status, int* __restrict__ offsets,
     int* __restrict__ chunk_counts, int* __restrict__ tiles) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   }
   if (e == 0) offsets[E] = total;
   __syncthreads();
-  write_tiles(cnt, off, E, BM, scan_tmp, tiles, status);
+  write_tiles(cnt, off, E, BM, bound, scan_tmp, tiles, status);
 }
 
 // Phase 3: scatter each pair to its sorted row.
@@ -287,12 +292,12 @@ static int id_bits_for(int E) {
   return b;
 }
 
-hipError_t launch_permute(const int* ids, int npairs, int E, int BM, const WsPtrs& ws,
-                          hipStream_t s) {
+hipError_t launch_permute(const int* ids, int npairs, int E, int BM, int tile_bound,
+                          const WsPtrs& ws, hipStream_t s) {
   const int bits = id_bits_for(E);
   if (npairs <= kFusedPermuteMaxPairs) {
     const size_t lds = (size_t)(3 + kChunkWaves) * E * sizeof(int);
-    permute_fused_kernel<<<1, kChunk, lds, s>>>(ids, npairs, E, bits, BM, ws.status,
+    permute_fused_kernel<<<1, kChunk, lds, s>>>(ids, npairs, E, bits, BM, tile_bound, ws.status,
                                                  ws.offsets, ws.sorted_pairs, ws.inv, ws.tiles);
     return hipGetLastError();
   }
@@ -300,7 +305,7 @@ hipError_t launch_permute(const int* ids, int npairs, int E, int BM, const WsPtr
   clear_status_kernel<<<1, 64, 0, s>>>(ws.status);
   permute_count_kernel<<<nchunks, kChunk, (size_t)kChunkWaves * E * sizeof(int), s>>>(
       ids, npairs, E, bits, ws.status, ws.chunk_counts, ws.chunk_ranks);
-  permute_scan_kernel<<<1, kChunk, 0, s>>>(nchunks, E, BM, ws.status, ws.offsets,
+  permute_scan_kernel<<<1, kChunk, 0, s>>>(nchunks, E, BM, tile_bound, ws.status, ws.offsets,
                                            ws.chunk_counts, ws.tiles);
   permute_scatter_kernel<<<nchunks, kChunk, 0, s>>>(ids, npairs, E, ws.chunk_counts,
                                                     ws.chunk_ranks, ws.sorted_pairs, ws.inv);

@@ -100,6 +100,8 @@ def test_moe_forward_rejects_bad_arguments_without_touching_memory(L):
     assert call(out=None) == E_NULL
     assert call(x=ctypes.c_void_p(0x1008)) == E_ALIGN
     assert call(ws=ctypes.c_void_p(0x1010)) == E_ALIGN
+    assert call(bias13=ctypes.c_void_p(0x1002)) == E_ALIGN   # biases are read 4 rows at a time
+    assert call(bias2=ctypes.c_void_p(0x1004)) == E_ALIGN
     assert call(ws=None) == E_WORKSPACE
     assert call(wsb=100) == E_WORKSPACE
     assert call(T=0) == 0                       # empty batch: a no-op
@@ -110,6 +112,8 @@ def test_linear_and_quant_and_route_validation(L):
     assert L.mxfp4_linear(_fake(), 1, 128, 2881, _fake(), _fake(), None, _fake(), None) == E_SHAPE
     assert L.mxfp4_linear(None, 1, 128, 2880, _fake(), _fake(), None, _fake(), None) == E_NULL
     assert L.mxfp4_linear(_fake(), 0, 128, 2880, _fake(), _fake(), None, _fake(), None) == 0
+    assert L.mxfp4_linear(_fake(), 1, 128, 2880, _fake(), _fake(), ctypes.c_void_p(0x1002), _fake(),
+                          None) == E_ALIGN
     assert L.mxfp4_quant_fp8_e4m3(_fake(), 5, 10, _fake(), _fake(), _fake(), None) == E_MODE
     assert L.mxfp4_quant_fp8_e4m3(_fake(), 0, 10, _fake(), None, _fake(), None) == E_NULL
     assert L.mxfp4_route_topk(_fake(), 4, 128, 0, _fake(), _fake(), None) == E_SHAPE
