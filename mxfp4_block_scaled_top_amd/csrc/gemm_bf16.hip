@@ -24,6 +24,8 @@
 //     the epilogue.  The SwiGLU output is kept as two bf16 halves hi + lo so
 //     that the down projection runs on bf16 MFMAs without a second rounding
 //     of h (hi = bf16(h), lo = bf16(h - hi)).
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -248,60 +250,78 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming variant (decode-sized MoE GEMMs, lm_head).
-//   * A wave owns one weight tile whose bytes are contiguous in HBM: 16 rows
-//     (down, dense), or 8 gate rows plus the matching 8 up rows (gate_up; each
-//     8-row run is a whole number of 128-byte lines).  It copies the tile and
-//     its E8M0 scales by DMA (global -> LDS, 1 KB / 256 B per instruction,
-//     nontemporal) into its own LDS slice -- measured 6.7 TB/s for this
-//     pattern, against 3.7 TB/s for 16 rows x 64 B per register load -- and
-//     then reads it back in MFMA layout.  Many short-lived waves (6 per CU)
-//     keep ~140 KB of DMA in flight per CU, which loaded HBM latency needs.
-//   * The tile's (at most 4) activation rows are loaded once, up front, in a
-//     compact layout: register set j holds in lane t + 4q + 16g the 8
-//     activations [128j + 32g + 8q, +8) of tile column t, so one 16-byte load
-//     per lane brings 256 contiguous bytes of each column (a quarter of the
-//     load instructions of an MFMA-layout load, whose lanes past column 3 would
-//     idle).  An MFMA step q takes its B operand from set j rotated by 4q lanes
-//     inside each 16-lane row (DPP), which puts column t's values in lane
-//     t + 16g.  Lanes of columns 4..15 then hold other columns' values; their
-//     MFMA outputs are never stored.  Columns past the tile's rows and blocks
-//     past K read through a range-checked buffer descriptor with an
-//     out-of-range offset, which returns zeros without touching memory.
-//   * gate_up: one 16-row MFMA holds 8 gate rows (0-7) and their 8 up rows
-//     (8-15); the up result moves to the gate lane (lane ^ 32) for SwiGLU.
-constexpr int kStreamWaves = 2;                 // waves (tiles) per block
-constexpr int kStreamMaxWaveLds = 32 * 1024;    // LDS per wave (<= 64 KB per block)
-constexpr int kStreamMaxGroups = 24;            // K <= 3072 on this path
-constexpr int kStreamCols = 4;                  // activation rows per tile
-static_assert(kStreamCols == kDecodeBM, "a decode tile feeds one stream tile");
+// Persistent streaming variant (decode-sized MoE GEMMs, lm_head).
+//   * A unit is one m-tile (at most 4 activation rows: routed pairs of one
+//     expert, or dense rows) times 16 weight rows (down, dense) or 8 gate rows
+//     plus the matching 8 up rows (gate_up).  The grid is a fixed number of
+//     blocks that walk contiguous ranges of units, so consecutive units share
+//     their m-tile and the activations stay in registers.
+//   * The two waves of a block split K: wave h takes K-groups [HG*h, HG*h + HG)
+//     of every unit (HG a compile-time count; groups past K are zero).  Each wave copies its half of the unit's weight rows and the
+//     rows' E8M0 scales by DMA (global -> LDS, 1 KB / 256 B per instruction,
+//     nontemporal; measured 6.7 TB/s for this pattern, against 3.7 TB/s for
+//     16 rows x 64 B per register load) into its LDS slot, copies the slot
+//     into registers, and at once starts the DMA of its next unit into the
+//     slot, so the slot stays in flight while the unit is multiplied.  The
+//     slot keeps a row stride of an odd number of 16-byte chunks (one padding
+//     chunk per row when needed), which makes the 16 rows' 16-byte reads
+//     bank-conflict free.
+//   * Activations use the compact layout: register set j holds in lane
+//     t + 4q + 16g the 8 activations [128j + 32g + 8q, +8) of m-tile column t,
+//     one 16-byte load per lane bringing 256 contiguous bytes of each column.
+//     MFMA step q rotates the set by 4q lanes inside each 16-lane row (DPP),
+//     which puts column t's values in lane t + 16g; lanes of columns 4..15 then
+//     hold other columns' values and their MFMA outputs are never stored.
+//     Columns past the m-tile's rows and blocks past K read through a
+//     range-checked buffer descriptor with an out-of-range offset, which
+//     returns zeros without touching memory.
+//   * Wave 1 hands its partial sums to wave 0 through LDS (fixed order, two
+//     buffers so one barrier per unit suffices); wave 0 adds bias, applies
+//     SwiGLU (gate_up: one 16-row MFMA holds 8 gate rows and their 8 up rows,
+//     the up result moves to the gate lane, lane ^ 32) and stores.
+constexpr int kPersistWaves = 2;       // waves per block (K halves)
+constexpr int kHalfGroups = 12;        // largest HG: K <= 3072 on this path
+constexpr int kUnitRows = 16;          // weight rows per unit
+constexpr int kCols = 4;               // activation rows per unit
+constexpr int kMaxDma = 13;            // 1 KB DMA instructions per wave and unit
+static_assert(kCols == kDecodeBM, "a decode row tile is one m-tile");
+static_assert(kUnitRows * ((4 * kHalfGroups) | 1) <= 64 * kMaxDma, "slot holds a padded half");
 
 __host__ __device__ constexpr int chunks_of(int64_t bytes, int chunk) {
   return (int)((bytes + chunk - 1) / chunk);
 }
 
-struct StreamPlan {
-  int wave;         // LDS bytes per wave: weights A | weights B | scales A | scales B
-  int wa, sa, sb;   // offsets of weights B, scales A, scales B
+struct PersistPlan {
+  int run_rows;      // rows per contiguous weight run (8 for gate_up, else 16)
+  int sc_run;        // LDS bytes per scale run
+  int slot;          // LDS bytes per wave: weights (kMaxDma KB) | scale runs
+  int row_tiles;     // units per m-tile
 };
 
-static StreamPlan stream_plan(int mode, int nb) {
-  StreamPlan p{};
-  const int64_t rb = (int64_t)nb * kBlockBytes;
-  const int rows = mode == kGateUp ? 8 : 16;
-  const int wchunk = chunks_of(rows * rb, 1024) * 1024;
-  const int schunk = chunks_of((int64_t)rows * nb, 256) * 256;
-  const bool pair = mode == kGateUp;
-  p.wa = wchunk;
-  p.sa = pair ? 2 * wchunk : wchunk;
-  p.sb = p.sa + schunk;
-  p.wave = pair ? p.sb + schunk : p.sa + schunk;
+static PersistPlan persist_plan(int mode, int nb, int nout) {
+  PersistPlan p{};
+  p.run_rows = mode == kGateUp ? 8 : 16;
+  p.sc_run = chunks_of((int64_t)p.run_rows * nb, 256) * 256;
+  p.slot = kMaxDma * 1024 + (kUnitRows / p.run_rows) * p.sc_run;
+  p.row_tiles = nout / p.run_rows;
   return p;
 }
 
-static bool stream_fits(int mode, int nb, uint32_t act_bytes) {
-  return act_bytes != 0 && (nb + 3) / 4 <= kStreamMaxGroups &&
-         stream_plan(mode, nb).wave <= kStreamMaxWaveLds;
+static int persist_lds(const PersistPlan& p) {
+  return kPersistWaves * p.slot + 2 * 64 * (int)sizeof(v4f);
+}
+
+// K-groups per wave for nb blocks (0: K outside this path)
+static int persist_half_groups(int nb) {
+  const int ng = (nb + 3) / 4;
+  if (ng < 2 || ng > 2 * kHalfGroups) return 0;
+  for (int hg : {1, 2, 3, 6, 12})
+    if (2 * hg >= ng) return hg;
+  return 0;
+}
+
+static bool persist_fits(int nb, uint32_t act_bytes) {
+  return act_bytes != 0 && persist_half_groups(nb) != 0;
 }
 
 // Lane i of each 16-lane row takes lane (i + 4q) mod 16 of the same row.
@@ -315,193 +335,283 @@ __device__ __forceinline__ uint4 row_rotate4(uint4 v) {
                     (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctrl, 0xf, 0xf, true));
 }
 
-template <int MODE>
-__global__ __launch_bounds__(64 * kStreamWaves) void gemv_stream_kernel(GemvArgs a, StreamPlan P) {
+template <int MODE, int HG>
+__global__ __launch_bounds__(64 * kPersistWaves) void gemv_persist_kernel(
+    GemvArgs a, PersistPlan P, const int* __restrict__ tiles, const int* __restrict__ sorted_pairs,
+    const int* __restrict__ status) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr bool kPair = MODE == kGateUp;
+  const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
-  constexpr bool kPair = MODE == kGateUp;
-  constexpr int kRowsA = kPair ? 8 : 16;
 
-  int e, row_begin, row_end;
-  if (MODE == kDense) {
-    e = 0;
-    row_begin = blockIdx.y * kStreamCols;
-    row_end = min(row_begin + kStreamCols, a.M);
-  } else {
-    const int4 tile = *reinterpret_cast<const int4*>(a.tiles + kTileInts * blockIdx.y);
-    if (tile.x < 0) return;
-    e = tile.x;
-    row_begin = tile.y;
-    row_end = tile.z;
-  }
-  const int n0 = (blockIdx.x * kStreamWaves + wave) * kRowsA;
-  if (n0 >= a.nout) return;   // no block-level synchronisation below
-  const int ncols = row_end - row_begin;   // 1..kStreamCols
+  // this block's units
+  const int64_t mtiles = MODE == kDense ? (a.M + kCols - 1) / kCols : status[kStNumTiles];
+  const int64_t U = mtiles * P.row_tiles;
+  const int64_t u_begin = U * blockIdx.x / gridDim.x;
+  const int64_t u_end = U * (blockIdx.x + 1) / gridDim.x;
+  if (u_begin >= u_end) return;   // the same for both waves: no barrier is skipped by one
 
-  // Everything the wave reads is requested before its first wait: the pair
-  // ids of its tile columns (scalar loads, so the vector wait below does not
-  // cover them), the weight DMA, the activation rows and the bias.
-  int pair[kStreamCols];
-  if (MODE == kGateUp) {
+  // this wave's K range: groups [gl, gl + HG), blocks [blk0, blk0 + nbw); the
+  // launcher picks HG with HG < ceil(nb / 4) <= 2 HG, so 1 <= nbw <= 4 HG
+  const int gl = kh * HG;
+  const int blk0 = 4 * gl;
+  const int nbw = min(4 * HG, a.nb - blk0);
+  const int cps = nbw | 1;                  // LDS row stride in 16-byte chunks (odd)
+  const int64_t rb = (int64_t)a.nb * kBlockBytes;
+  uint8_t* slot = smem + kh * P.slot;
+  const uint8_t* slot_sc = slot + kMaxDma * 1024;
+  v4f* red = reinterpret_cast<v4f*>(smem + kPersistWaves * P.slot);
+
+  // DMA sources relative to the unit's first row, fixed for every unit:
+  // chunk q = 64c + lane of the wave's 16 x cps chunks (the padding chunk of a
+  // row and the tail of the last instruction re-read a valid chunk)
+  uint32_t doff[kMaxDma];
+  const int nq = kUnitRows * cps;
+  const int ndma = (nq + 63) >> 6;
 #pragma unroll
-    for (int c = 0; c < kStreamCols; ++c)
-      pair[c] = a.sorted_pairs[__builtin_amdgcn_readfirstlane(row_begin + min(c, ncols - 1))];
+  for (int c = 0; c < kMaxDma; ++c) {
+    const int q = min(64 * c + lane, nq - 1);
+    const int row = q / cps;
+    const int col = min(q - row * cps, nbw - 1);
+    const int run = row / P.run_rows;
+    const int rr = row - run * P.run_rows;
+    doff[c] = (uint32_t)(run * (int64_t)a.nout * rb + rr * rb + (int64_t)(blk0 + col) * kBlockBytes);
   }
-  const int rb = a.nb * kBlockBytes;
-  uint8_t* sl = smem + wave * P.wave;
-  {
-    const int64_t region = (int64_t)kRowsA * rb;
-    const uint8_t* ga = a.wb + ((size_t)e * a.rows_per_expert + n0) * rb;
-    const uint8_t* gb = ga + (size_t)a.nout * rb;
-    const int nch = chunks_of(region, 1024);
-    for (int c = 0; c < nch; ++c) {   // tail lanes re-read the run's last 16 B into slack
-      const int64_t off = min((int64_t)c * 1024 + lane * 16, region - 16);
-      __builtin_amdgcn_global_load_lds(ga + off, sl + c * 1024, 16, 0, 2);
-      if (kPair) __builtin_amdgcn_global_load_lds(gb + off, sl + P.wa + c * 1024, 16, 0, 2);
-    }
-    const int64_t sreg = (int64_t)kRowsA * a.nb;   // every scale run is 4-byte aligned
-    const uint8_t* sga = a.ws + ((size_t)e * a.rows_per_expert + n0) * a.nb;
-    const uint8_t* sgb = sga + (size_t)a.nout * a.nb;
-    const int nsc = chunks_of(sreg, 256);
-    for (int c = 0; c < nsc; ++c) {
-      const int64_t off = min((int64_t)c * 256 + lane * 4, sreg - 4);
-      __builtin_amdgcn_global_load_lds(sga + off, sl + P.sa + c * 256, 4, 0, 2);
-      if (kPair) __builtin_amdgcn_global_load_lds(sgb + off, sl + P.sb + c * 256, 4, 0, 2);
-    }
-  }
+  const int64_t sreg = (int64_t)P.run_rows * a.nb;   // scale bytes per run (4-byte aligned runs)
+  const int nsc = chunks_of(sreg, 256);
 
-  // compact activation load (layout above): this lane reads column xt, chunk xq
-  const int ngroups = (a.nb + 3) >> 2;
+  auto issue_dma = [&](int e, int n0) {
+    const size_t first = (size_t)e * a.rows_per_expert + n0;
+    const uint8_t* gw = a.wb + first * rb;
+    for (int c = 0; c < ndma; ++c)
+      __builtin_amdgcn_global_load_lds(gw + doff[c], slot + c * 1024, 16, 0, 2);
+    const uint8_t* gs = a.ws + first * a.nb;
+    for (int run = 0; run < kUnitRows / P.run_rows; ++run) {
+      const uint8_t* gsr = gs + (size_t)run * a.nout * a.nb;
+      for (int c = 0; c < nsc; ++c) {
+        const int64_t off = min((int64_t)c * 256 + lane * 4, sreg - 4);
+        __builtin_amdgcn_global_load_lds(gsr + off, (uint8_t*)slot_sc + run * P.sc_run + c * 256, 4, 0, 2);
+      }
+    }
+  };
+
+  // m-tile of a unit: expert, first sorted row, end row
+  auto tile_of = [&](int64_t m, int& e, int& rbeg, int& rend) {
+    if (MODE == kDense) {
+      e = 0;
+      rbeg = (int)m * kCols;
+      rend = min(rbeg + kCols, a.M);
+    } else {
+      const int4 t = *reinterpret_cast<const int4*>(tiles + kTileInts * m);
+      e = t.x;
+      rbeg = t.y;
+      rend = t.z;
+    }
+  };
+
+  // activations of an m-tile (compact layout), this wave's groups only
   const int xt = lane & 3;
   const int xq = (lane >> 2) & 3;
-  int arow = row_begin + min(xt, ncols - 1);
-  if (MODE == kGateUp) {   // token of the lane's tile column
-    int p = pair[0];
-#pragma unroll
-    for (int c = 1; c < kStreamCols; ++c) p = xt == c ? pair[c] : p;
-    arow = p / a.topk;
-  }
-  const bool xt_ok = xt < ncols;
   const uint32_t rowb = (uint32_t)(a.nb * kBlockElems * 2);
-  const uint32_t xoff = (uint32_t)arow * rowb + (uint32_t)(32 * g + 8 * xq) * 2;
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, (int)a.act_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t lrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(MODE == kDown ? a.act_lo : a.act), (short)0,
                                         (int)a.act_bytes, 0x00020000);
-  uint4 xa[kStreamMaxGroups];
-  uint4 xl[MODE == kDown ? kStreamMaxGroups : 1];
+  uint4 xa[HG];
+  uint4 xl[MODE == kDown ? HG : 1];
+  auto load_x = [&](int rbeg, int rend) {
+    const int ncols = rend - rbeg;
+    int arow = rbeg + min(xt, ncols - 1);
+    if (MODE == kGateUp) {   // token of the lane's column
+      int p = sorted_pairs[rbeg];
 #pragma unroll
-  for (int j = 0; j < kStreamMaxGroups; ++j) {
-    if (j < ngroups) {
+      for (int c = 1; c < kCols; ++c) {
+        const int pc = sorted_pairs[rbeg + min(c, ncols - 1)];
+        p = xt == c ? pc : p;
+      }
+      arow = p / a.topk;
+    }
+    const bool xt_ok = xt < ncols;
+    const uint32_t xoff = (uint32_t)arow * rowb + (uint32_t)(32 * g + 8 * xq) * 2;
+#pragma unroll
+    for (int jj = 0; jj < HG; ++jj) {
+      const int j = gl + jj;
       const bool ok = xt_ok && 4 * j + g < a.nb;
       const uint32_t off = ok ? xoff + 256u * j : 0x80000000u;
       const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
-      xa[j] = make_uint4(v.x, v.y, v.z, v.w);
+      xa[jj] = make_uint4(v.x, v.y, v.z, v.w);
       if (MODE == kDown) {
         const v4u_t vl = __builtin_amdgcn_raw_buffer_load_b128(lrs, off, 0, 0);
-        xl[j] = make_uint4(vl.x, vl.y, vl.z, vl.w);
+        xl[jj] = make_uint4(vl.x, vl.y, vl.z, vl.w);
       }
     }
-  }
-  // bias of the output rows this lane stores (rows n0 + 4g .. +3; gate_up: the
+  };
+
+  // bias of the rows wave 0's lane stores (rows n0 + 4g .. +3; gate_up: the
   // gate lanes g < 2 also need the matching up rows)
-  const int nbase = n0 + 4 * (kPair ? (g & 1) : g);
   uint2 bias_a = make_uint2(0, 0), bias_b = make_uint2(0, 0);
-  if (a.bias) {
-    const uint16_t* be = a.bias + (size_t)e * a.rows_per_expert + nbase;
-    bias_a = *reinterpret_cast<const uint2*>(be);
-    if (kPair) bias_b = *reinterpret_cast<const uint2*>(be + a.nout);
-  }
-  __builtin_amdgcn_s_waitcnt(0);   // the wave's LDS tile, activations and bias have landed
+  auto load_bias = [&](int e, int n0) {
+    if (kh == 0 && a.bias) {
+      const uint16_t* be = a.bias + (size_t)e * a.rows_per_expert + n0 + 4 * (kPair ? (g & 1) : g);
+      bias_a = *reinterpret_cast<const uint2*>(be);
+      if (kPair) bias_b = *reinterpret_cast<const uint2*>(be + a.nout);
+    }
+  };
 
-  const int wr = kPair ? (r & 7) : r;
-  const bool upper = kPair && r >= 8;
-  const uint8_t* lrow = sl + (upper ? P.wa : 0) + wr * rb;
-  const uint8_t* lsc = sl + (upper ? P.sb : P.sa) + wr * a.nb;
+  // staging reads of this wave's half unit: lane (r, g), group jj -> block
+  // 4jj + g of row r
+  const int srun = r / P.run_rows;
+  const uint8_t* wrow = slot + r * cps * kBlockBytes;
+  const uint8_t* srow = slot_sc + srun * P.sc_run + (r - srun * P.run_rows) * a.nb + blk0;
 
-  // K order inside group j: lane group g takes block 4j + g, MFMA step q its
-  // elements 8q..8q+7 -- the same permutation for weights and activations.
-  v4f acc0 = {0.f, 0.f, 0.f, 0.f};
-  v4f acc1 = {0.f, 0.f, 0.f, 0.f};
   auto step = [&](v4f& acc, const v8bf& A, const uint4& b, const uint4& bl) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(b), acc, 0, 0, 0);
     if (MODE == kDown) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(bl), acc, 0, 0, 0);
   };
-  // the LDS reads of group j + 1 are issued before group j's multiplies
-  auto lds_group = [&](int j, uint4& w, uint32_t& sc) {
-    const int blk = 4 * j + g;
-    const int jc = blk < a.nb ? blk : a.nb - 1;
-    w = *reinterpret_cast<const uint4*>(lrow + jc * kBlockBytes);
-    sc = lsc[jc];
-  };
-  uint4 wn;
-  uint32_t sn;
-  lds_group(0, wn, sn);
-#pragma unroll
-  for (int j = 0; j < kStreamMaxGroups; ++j) {
-    if (j < ngroups) {
-      const uint4 w = wn;
-      const float f = 4 * j + g < a.nb ? e8m0_to_f32(sn) : 0.0f;   // tail blocks contribute 0
-      if (j + 1 < ngroups) lds_group(j + 1, wn, sn);
-      const uint4 lo = MODE == kDown ? xl[j] : xa[j];
-      step(acc0, fp4x8_to_bf16(w.x, f), xa[j], lo);
-      step(acc1, fp4x8_to_bf16(w.y, f), row_rotate4<1>(xa[j]), row_rotate4<1>(lo));
-      step(acc0, fp4x8_to_bf16(w.z, f), row_rotate4<2>(xa[j]), row_rotate4<2>(lo));
-      step(acc1, fp4x8_to_bf16(w.w, f), row_rotate4<3>(xa[j]), row_rotate4<3>(lo));
-    }
-  }
-  const v4f acc = acc0 + acc1;
 
-  // lane (column r, group g) holds rows 4g + jj of column r
-  const int row = row_begin + r;
-  const bool col_ok = r < ncols;
-  const float bia[4] = {bf16_bits_to_f32(bias_a.x & 0xffffu), bf16_bits_to_f32(bias_a.x >> 16),
-                        bf16_bits_to_f32(bias_a.y & 0xffffu), bf16_bits_to_f32(bias_a.y >> 16)};
-  if (MODE == kGateUp) {
-    float upv[4];
+  int64_t u = u_begin;
+  int64_t m = u / P.row_tiles;
+  int e, rbeg, rend;
+  tile_of(m, e, rbeg, rend);
+  int n0 = (int)(u - m * P.row_tiles) * P.run_rows;
+  issue_dma(e, n0);
+  load_x(rbeg, rend);
+  load_bias(e, n0);
+  int buf = 0;
+  for (;;) {
+    __builtin_amdgcn_s_waitcnt(0);   // DMA of unit u, activations, bias (and earlier stores)
+    uint4 wreg[HG];
+    uint32_t sreg8[HG];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) upv[jj] = __shfl_xor(acc[jj], 32, 64);
-    if (g >= 2 || !col_ok) return;
-    const float bib[4] = {bf16_bits_to_f32(bias_b.x & 0xffffu), bf16_bits_to_f32(bias_b.x >> 16),
-                          bf16_bits_to_f32(bias_b.y & 0xffffu), bf16_bits_to_f32(bias_b.y >> 16)};
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float gate = acc[jj] + bia[jj], up = upv[jj] + bib[jj];
-      const float h = silu(gate) * up;
-      hi[jj] = f32_to_bf16_bits(h);
-      lo[jj] = f32_to_bf16_bits(h - bf16_bits_to_f32(hi[jj]));
+    for (int jj = 0; jj < HG; ++jj) {
+      const int lbc = min(4 * jj + g, nbw - 1);
+      wreg[jj] = *reinterpret_cast<const uint4*>(wrow + lbc * kBlockBytes);
+      sreg8[jj] = srow[lbc];
     }
-    const size_t o = (size_t)row * a.nout + nbase;
-    *reinterpret_cast<uint2*>(a.out_hi + o) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-    *reinterpret_cast<uint2*>(a.out_lo + o) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
-  } else {
-    if (!col_ok) return;
-    float v[4];
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the slot has been read
+
+    // next unit: start its DMA before multiplying this one
+    const int64_t un = u + 1;
+    const bool more = un < u_end;
+    const int64_t mn = un / P.row_tiles;
+    int en = e, rbn = rbeg, ren = rend;
+    if (more && mn != m) tile_of(mn, en, rbn, ren);
+    const int n0n = (int)(un - mn * P.row_tiles) * P.run_rows;
+    if (more) issue_dma(en, n0n);
+
+    v4f acc0 = {0.f, 0.f, 0.f, 0.f};
+    v4f acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) v[jj] = acc[jj] + bia[jj];
-    if (MODE == kDown) {
-      *reinterpret_cast<float4*>(a.y + (size_t)row * a.nout + nbase) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-      const uint32_t o0 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-      const uint32_t o1 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-      *reinterpret_cast<uint2*>(a.out_hi + (size_t)row * a.nout + nbase) = make_uint2(o0, o1);
+    for (int jj = 0; jj < HG; ++jj) {
+      const uint4 w = wreg[jj];
+      // blocks past K (scale byte forced to 0, i.e. a factor 0) contribute 0
+      const float f = e8m0_to_f32(4 * jj + g < nbw ? sreg8[jj] : 0u);
+      const uint4 lo = MODE == kDown ? xl[jj] : xa[jj];
+      step(acc0, fp4x8_to_bf16(w.x, f), xa[jj], lo);
+      step(acc1, fp4x8_to_bf16(w.y, f), row_rotate4<1>(xa[jj]), row_rotate4<1>(lo));
+      step(acc0, fp4x8_to_bf16(w.z, f), row_rotate4<2>(xa[jj]), row_rotate4<2>(lo));
+      step(acc1, fp4x8_to_bf16(w.w, f), row_rotate4<3>(xa[jj]), row_rotate4<3>(lo));
     }
+    v4f acc = acc0 + acc1;
+    if (kh == 1) red[buf * 64 + lane] = acc;
+    // wave 1's partial sums are in LDS; the DMA of the next unit stays in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kh == 0) {
+      acc += red[buf * 64 + lane];
+      // lane (column r, group g) holds rows 4g + jj of column r
+      const int row = rbeg + r;
+      const bool col_ok = r < rend - rbeg;
+      const int nbase = n0 + 4 * (kPair ? (g & 1) : g);
+      const float bia[4] = {bf16_bits_to_f32(bias_a.x & 0xffffu), bf16_bits_to_f32(bias_a.x >> 16),
+                            bf16_bits_to_f32(bias_a.y & 0xffffu), bf16_bits_to_f32(bias_a.y >> 16)};
+      if (MODE == kGateUp) {
+        float upv[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) upv[jj] = __shfl_xor(acc[jj], 32, 64);
+        if (g < 2 && col_ok) {
+          const float bib[4] = {bf16_bits_to_f32(bias_b.x & 0xffffu), bf16_bits_to_f32(bias_b.x >> 16),
+                                bf16_bits_to_f32(bias_b.y & 0xffffu), bf16_bits_to_f32(bias_b.y >> 16)};
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float gate = acc[jj] + bia[jj], up = upv[jj] + bib[jj];
+            const float h = silu(gate) * up;
+            hi[jj] = f32_to_bf16_bits(h);
+            lo[jj] = f32_to_bf16_bits(h - bf16_bits_to_f32(hi[jj]));
+          }
+          const size_t o = (size_t)row * a.nout + nbase;
+          *reinterpret_cast<uint2*>(a.out_hi + o) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+          *reinterpret_cast<uint2*>(a.out_lo + o) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+        }
+      } else if (col_ok) {
+        float v[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = acc[jj] + bia[jj];
+        if (MODE == kDown) {
+          *reinterpret_cast<float4*>(a.y + (size_t)row * a.nout + nbase) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          const uint32_t o0 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+          const uint32_t o1 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+          *reinterpret_cast<uint2*>(a.out_hi + (size_t)row * a.nout + nbase) = make_uint2(o0, o1);
+        }
+      }
+    }
+    buf ^= 1;
+    if (!more) break;
+    if (mn != m) load_x(rbn, ren);
+    load_bias(en, n0n);
+    u = un;
+    m = mn;
+    e = en;
+    rbeg = rbn;
+    rend = ren;
+    n0 = n0n;
   }
 }
 
-template <int MODE>
-static hipError_t launch_stream(const GemvArgs& a, int nout, int64_t ytiles, const StreamPlan& P,
-                                hipStream_t s) {
-  const int rows = MODE == kGateUp ? 8 : 16;
-  const int tiles = nout / rows;
-  const dim3 grid((unsigned)((tiles + kStreamWaves - 1) / kStreamWaves), (unsigned)ytiles);
-  gemv_stream_kernel<MODE><<<grid, 64 * kStreamWaves, kStreamWaves * P.wave, s>>>(a, P);
+// Blocks of the persistent kernel: as many as are resident at once on the
+// device (compute units x resident blocks per unit, queried per kernel).
+template <int MODE, int HG>
+static hipError_t launch_persist_hg(const GemvArgs& a, const PersistPlan& P, const int* tiles,
+                                    const int* sorted_pairs, const int* status, hipStream_t s) {
+  // (device + 1) << 48 | lds << 24 | blocks, cached per kernel; threads may race
+  // to fill it, but every writer stores the same value
+  static std::atomic<uint64_t> cache{0};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const int lds = persist_lds(P);
+  const uint64_t key = ((uint64_t)(dev + 1) << 48) | ((uint64_t)lds << 24);
+  uint64_t c = cache.load(std::memory_order_relaxed);
+  if ((c & ~0xffffffull) != key) {
+    int cus = 0, per_cu = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_persist_kernel<MODE, HG>,
+                                                       64 * kPersistWaves, lds);
+    if (err != hipSuccess) return err;
+    c = key | (uint64_t)(cus * (per_cu > 0 ? per_cu : 1));
+    cache.store(c, std::memory_order_relaxed);
+  }
+  const unsigned blocks = (unsigned)(c & 0xffffff);
+  gemv_persist_kernel<MODE, HG><<<blocks, 64 * kPersistWaves, lds, s>>>(a, P, tiles, sorted_pairs, status);
   return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_persist(const GemvArgs& a, const PersistPlan& P, const int* tiles,
+                                 const int* sorted_pairs, const int* status, hipStream_t s) {
+  switch (persist_half_groups(a.nb)) {
+    case 1: return launch_persist_hg<MODE, 1>(a, P, tiles, sorted_pairs, status, s);
+    case 2: return launch_persist_hg<MODE, 2>(a, P, tiles, sorted_pairs, status, s);
+    case 3: return launch_persist_hg<MODE, 3>(a, P, tiles, sorted_pairs, status, s);
+    case 6: return launch_persist_hg<MODE, 6>(a, P, tiles, sorted_pairs, status, s);
+    case 12: return launch_persist_hg<MODE, 12>(a, P, tiles, sorted_pairs, status, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // Row tiles of 16 rows; KSPLIT waves per row tile, 4 waves per block.
@@ -547,8 +657,9 @@ hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const M
   // expected busy row tiles: one m-tile per routed pair at most
   const int64_t pairs = (int64_t)sh.T * sh.k;
   const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.I / 16);
-  const StreamPlan P = stream_plan(kGateUp, a.nb);
-  if (stream_fits(kGateUp, a.nb, a.act_bytes)) return launch_stream<kGateUp>(a, sh.I, ntile_bound, P, s);
+  if (persist_fits(a.nb, a.act_bytes))
+    return launch_persist<kGateUp>(a, persist_plan(kGateUp, a.nb, sh.I), ws.tiles, ws.sorted_pairs,
+                                   ws.status, s);
   return launch_gemv<kGateUp>(a, sh.I, ntile_bound, pick_ksplit(busy), s);
 }
 
@@ -572,8 +683,9 @@ hipError_t launch_moe_down_bf16(const MoeShape& sh, const MoeWeights& w, const W
   a.y = ws.y;
   const int64_t pairs = (int64_t)sh.T * sh.k;
   const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.H / 16);
-  const StreamPlan P = stream_plan(kDown, a.nb);
-  if (stream_fits(kDown, a.nb, a.act_bytes)) return launch_stream<kDown>(a, sh.H, ntile_bound, P, s);
+  if (persist_fits(a.nb, a.act_bytes))
+    return launch_persist<kDown>(a, persist_plan(kDown, a.nb, sh.H), ws.tiles, ws.sorted_pairs,
+                                 ws.status, s);
   return launch_gemv<kDown>(a, sh.H, ntile_bound, pick_ksplit(busy), s);
 }
 
@@ -594,9 +706,8 @@ hipError_t launch_linear_bf16(const uint16_t* x, int M, int N, int K, const uint
   a.out_hi = out;
   const int64_t mt = (M + 15) / 16;
   const int64_t row_tiles = (int64_t)(N / 16) * mt;
-  const StreamPlan P = stream_plan(kDense, a.nb);
-  if (stream_fits(kDense, a.nb, a.act_bytes) && row_tiles >= 2048)
-    return launch_stream<kDense>(a, N, (M + kStreamCols - 1) / kStreamCols, P, s);
+  if (persist_fits(a.nb, a.act_bytes) && row_tiles >= 2048)
+    return launch_persist<kDense>(a, persist_plan(kDense, a.nb, N), nullptr, nullptr, nullptr, s);
   return launch_gemv<kDense>(a, N, mt, pick_ksplit(row_tiles), s);
 }
 
