@@ -253,19 +253,22 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvArgs a) {
 // Persistent streaming variant (decode-sized MoE GEMMs, lm_head).
 //   * A unit is one m-tile (at most 4 activation rows: routed pairs of one
 //     expert, or dense rows) times 16 weight rows (down, dense) or 8 gate rows
-//     plus the matching 8 up rows (gate_up).  The grid is a fixed number of
-//     blocks that walk contiguous ranges of units, so consecutive units share
-//     their m-tile and the activations stay in registers.
-//   * The two waves of a block split K: wave h takes K-groups [HG*h, HG*h + HG)
-//     of every unit (HG a compile-time count; groups past K are zero).  Each wave copies its half of the unit's weight rows and the
-//     rows' E8M0 scales by DMA (global -> LDS, 1 KB / 256 B per instruction,
-//     nontemporal; measured 6.7 TB/s for this pattern, against 3.7 TB/s for
-//     16 rows x 64 B per register load) into its LDS slot, copies the slot
-//     into registers, and at once starts the DMA of its next unit into the
-//     slot, so the slot stays in flight while the unit is multiplied.  The
-//     slot keeps a row stride of an odd number of 16-byte chunks (one padding
-//     chunk per row when needed), which makes the 16 rows' 16-byte reads
-//     bank-conflict free.
+//     plus the matching 8 up rows (gate_up).  The grid is the number of blocks
+//     resident at once; each block walks a contiguous range of units, so
+//     consecutive units share their m-tile and the activations stay in
+//     registers.
+//   * Loading: wave w of the block's two waves copies the unit's weight rows
+//     8w..8w+7 (one contiguous run of whole 128-byte lines: no line is shared
+//     with another wave or unit) and their E8M0 scales by DMA (global -> LDS,
+//     1 KB / 256 B per instruction, nontemporal; measured 6.7 TB/s for this
+//     pattern, against 3.7 TB/s for 16 rows x 64 B per register load) into the
+//     block's LDS buffer.  As soon as both waves have copied the buffer into
+//     registers, the DMA of the next unit is issued, so the buffer stays in
+//     flight while the unit is multiplied -- the bytes in flight per CU, which
+//     loaded HBM latency calls for, are the LDS the resident blocks hold (six
+//     blocks of 27 KB per CU).
+//   * Multiplying: the waves split K: wave h takes K-groups [HG*h, HG*h + HG)
+//     of all 16 rows (HG a compile-time count; groups past K are zero).
 //   * Activations use the compact layout: register set j holds in lane
 //     t + 4q + 16g the 8 activations [128j + 32g + 8q, +8) of m-tile column t,
 //     one 16-byte load per lane bringing 256 contiguous bytes of each column.
@@ -275,53 +278,47 @@ __global__ __launch_bounds__(256) void gemv_bf16_kernel(GemvArgs a) {
 //     Columns past the m-tile's rows and blocks past K read through a
 //     range-checked buffer descriptor with an out-of-range offset, which
 //     returns zeros without touching memory.
-//   * Wave 1 hands its partial sums to wave 0 through LDS (fixed order, two
-//     buffers so one barrier per unit suffices); wave 0 adds bias, applies
-//     SwiGLU (gate_up: one 16-row MFMA holds 8 gate rows and their 8 up rows,
-//     the up result moves to the gate lane, lane ^ 32) and stores.
-constexpr int kPersistWaves = 2;       // waves per block (K halves)
-constexpr int kHalfGroups = 12;        // largest HG: K <= 3072 on this path
+//   * Wave 1 hands its partial sums to wave 0 through LDS; wave 0 adds them,
+//     adds bias, applies SwiGLU (gate_up: one 16-row MFMA holds 8 gate rows and
+//     their 8 up rows, the up result moves to the gate lane, lane ^ 32) and
+//     stores.  Three barriers per unit: data landed, buffer read, partial sums
+//     written.
 constexpr int kUnitRows = 16;          // weight rows per unit
+constexpr int kRunRows = 8;            // rows per wave's DMA run
 constexpr int kCols = 4;               // activation rows per unit
-constexpr int kMaxDma = 13;            // 1 KB DMA instructions per wave and unit
+constexpr int kMaxHG = 12;             // K-groups per wave: K <= 3072 on this path
+constexpr int kRunDma = 12;            // 1 KB weight DMA instructions per run (8 x 1536 B max)
+constexpr int kRunScDma = 3;           // 256 B scale DMA instructions per run (8 x 96 B max)
+// (a run's region also covers reads of blocks up to 95 of its last row:
+// 7 * 1536 + 96 * 16 <= 12 KB and 7 * 96 + 96 <= 768)
+constexpr int kRunBytes = kRunDma * 1024 + kRunScDma * 256;   // LDS per run
+constexpr int kBufBytes = 2 * kRunBytes;                       // LDS per unit buffer
+constexpr int kPersistLds = kBufBytes + 64 * 16;               // buffer + partial sums
 static_assert(kCols == kDecodeBM, "a decode row tile is one m-tile");
-static_assert(kUnitRows * ((4 * kHalfGroups) | 1) <= 64 * kMaxDma, "slot holds a padded half");
-
-__host__ __device__ constexpr int chunks_of(int64_t bytes, int chunk) {
-  return (int)((bytes + chunk - 1) / chunk);
-}
 
 struct PersistPlan {
-  int run_rows;      // rows per contiguous weight run (8 for gate_up, else 16)
-  int sc_run;        // LDS bytes per scale run
-  int slot;          // LDS bytes per wave: weights (kMaxDma KB) | scale runs
+  int run_rows;      // rows per contiguous weight run of a unit: 8
   int row_tiles;     // units per m-tile
 };
 
-static PersistPlan persist_plan(int mode, int nb, int nout) {
+static PersistPlan persist_plan(int mode, int nout) {
   PersistPlan p{};
-  p.run_rows = mode == kGateUp ? 8 : 16;
-  p.sc_run = chunks_of((int64_t)p.run_rows * nb, 256) * 256;
-  p.slot = kMaxDma * 1024 + (kUnitRows / p.run_rows) * p.sc_run;
-  p.row_tiles = nout / p.run_rows;
+  p.run_rows = kRunRows;
+  p.row_tiles = nout / (mode == kGateUp ? kRunRows : kUnitRows);
   return p;
 }
 
-static int persist_lds(const PersistPlan& p) {
-  return kPersistWaves * p.slot + 2 * 64 * (int)sizeof(v4f);
-}
-
 // K-groups per wave for nb blocks (0: K outside this path)
-static int persist_half_groups(int nb) {
+static int persist_hg(int nb) {
   const int ng = (nb + 3) / 4;
-  if (ng < 2 || ng > 2 * kHalfGroups) return 0;
+  if (ng < 2 || ng > 2 * kMaxHG) return 0;
   for (int hg : {1, 2, 3, 6, 12})
     if (2 * hg >= ng) return hg;
   return 0;
 }
 
 static bool persist_fits(int nb, uint32_t act_bytes) {
-  return act_bytes != 0 && persist_half_groups(nb) != 0;
+  return act_bytes != 0 && persist_hg(nb) != 0;
 }
 
 // Lane i of each 16-lane row takes lane (i + 4q) mod 16 of the same row.
@@ -336,7 +333,7 @@ __device__ __forceinline__ uint4 row_rotate4(uint4 v) {
 }
 
 template <int MODE, int HG>
-__global__ __launch_bounds__(64 * kPersistWaves) void gemv_persist_kernel(
+__global__ __launch_bounds__(128) void gemv_persist_kernel(
     GemvArgs a, PersistPlan P, const int* __restrict__ tiles, const int* __restrict__ sorted_pairs,
     const int* __restrict__ status) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -353,47 +350,28 @@ __global__ __launch_bounds__(64 * kPersistWaves) void gemv_persist_kernel(
   const int64_t u_end = U * (blockIdx.x + 1) / gridDim.x;
   if (u_begin >= u_end) return;   // the same for both waves: no barrier is skipped by one
 
-  // this wave's K range: groups [gl, gl + HG), blocks [blk0, blk0 + nbw); the
-  // launcher picks HG with HG < ceil(nb / 4) <= 2 HG, so 1 <= nbw <= 4 HG
-  const int gl = kh * HG;
-  const int blk0 = 4 * gl;
-  const int nbw = min(4 * HG, a.nb - blk0);
-  const int cps = nbw | 1;                  // LDS row stride in 16-byte chunks (odd)
   const int64_t rb = (int64_t)a.nb * kBlockBytes;
-  uint8_t* slot = smem + kh * P.slot;
-  const uint8_t* slot_sc = slot + kMaxDma * 1024;
-  v4f* red = reinterpret_cast<v4f*>(smem + kPersistWaves * P.slot);
+  v4f* red = reinterpret_cast<v4f*>(smem + kBufBytes);
 
-  // DMA sources relative to the unit's first row, fixed for every unit:
-  // chunk q = 64c + lane of the wave's 16 x cps chunks (the padding chunk of a
-  // row and the tail of the last instruction re-read a valid chunk)
-  uint32_t doff[kMaxDma];
-  const int nq = kUnitRows * cps;
-  const int ndma = (nq + 63) >> 6;
-#pragma unroll
-  for (int c = 0; c < kMaxDma; ++c) {
-    const int q = min(64 * c + lane, nq - 1);
-    const int row = q / cps;
-    const int col = min(q - row * cps, nbw - 1);
-    const int run = row / P.run_rows;
-    const int rr = row - run * P.run_rows;
-    doff[c] = (uint32_t)(run * (int64_t)a.nout * rb + rr * rb + (int64_t)(blk0 + col) * kBlockBytes);
-  }
-  const int64_t sreg = (int64_t)P.run_rows * a.nb;   // scale bytes per run (4-byte aligned runs)
-  const int nsc = chunks_of(sreg, 256);
-
+  // DMA of this wave's run (rows 8kh..8kh+7 of a unit) into buffer `buf`; the
+  // tail lanes of the last instruction re-read the run's last 16 bytes
+  const int64_t wrun = kRunRows * rb;                 // weight bytes of the run
+  const int64_t srun = (int64_t)kRunRows * a.nb;      // scale bytes (4-byte aligned run)
   auto issue_dma = [&](int e, int n0) {
-    const size_t first = (size_t)e * a.rows_per_expert + n0;
-    const uint8_t* gw = a.wb + first * rb;
-    for (int c = 0; c < ndma; ++c)
-      __builtin_amdgcn_global_load_lds(gw + doff[c], slot + c * 1024, 16, 0, 2);
-    const uint8_t* gs = a.ws + first * a.nb;
-    for (int run = 0; run < kUnitRows / P.run_rows; ++run) {
-      const uint8_t* gsr = gs + (size_t)run * a.nout * a.nb;
-      for (int c = 0; c < nsc; ++c) {
-        const int64_t off = min((int64_t)c * 256 + lane * 4, sreg - 4);
-        __builtin_amdgcn_global_load_lds(gsr + off, (uint8_t*)slot_sc + run * P.sc_run + c * 256, 4, 0, 2);
-      }
+    // first row of the run: gate_up wave 1 takes the matching up rows
+    const size_t row0 = (size_t)e * a.rows_per_expert + n0 + (kPair ? (size_t)kh * a.nout : (size_t)kh * kRunRows);
+    const uint8_t* gw = a.wb + row0 * rb;
+    const uint8_t* gs = a.ws + row0 * a.nb;
+    uint8_t* dst = smem + kh * kRunBytes;
+#pragma unroll
+    for (int c = 0; c < kRunDma; ++c) {
+      const int64_t off = min((int64_t)c * 1024 + lane * 16, wrun - 16);
+      __builtin_amdgcn_global_load_lds(gw + off, dst + c * 1024, 16, 0, 2);
+    }
+#pragma unroll
+    for (int c = 0; c < kRunScDma; ++c) {
+      const int64_t off = min((int64_t)c * 256 + lane * 4, srun - 4);
+      __builtin_amdgcn_global_load_lds(gs + off, dst + kRunDma * 1024 + c * 256, 4, 0, 2);
     }
   };
 
@@ -410,8 +388,14 @@ __global__ __launch_bounds__(64 * kPersistWaves) void gemv_persist_kernel(
       rend = t.z;
     }
   };
+  auto unit_of = [&](int64_t u, int& e, int& rbeg, int& rend, int& n0) {
+    const int64_t m = u / P.row_tiles;
+    tile_of(m, e, rbeg, rend);
+    n0 = (int)(u - m * P.row_tiles) * (kPair ? kRunRows : kUnitRows);
+  };
 
   // activations of an m-tile (compact layout), this wave's groups only
+  const int gl = kh * HG;
   const int xt = lane & 3;
   const int xq = (lane >> 2) & 3;
   const uint32_t rowb = (uint32_t)(a.nb * kBlockElems * 2);
@@ -461,11 +445,11 @@ __global__ __launch_bounds__(64 * kPersistWaves) void gemv_persist_kernel(
     }
   };
 
-  // staging reads of this wave's half unit: lane (r, g), group jj -> block
-  // 4jj + g of row r
-  const int srun = r / P.run_rows;
-  const uint8_t* wrow = slot + r * cps * kBlockBytes;
-  const uint8_t* srow = slot_sc + srun * P.sc_run + (r - srun * P.run_rows) * a.nb + blk0;
+  // staging reads: lane (r, g), group jj -> block 4(gl + jj) + g of unit row r
+  // (run r / 8, row r % 8 of the run)
+  const int lrun = r / kRunRows, lrr = r % kRunRows;
+  const int wrow_off = lrun * kRunBytes + lrr * (int)rb;
+  const int srow_off = lrun * kRunBytes + kRunDma * 1024 + lrr * a.nb;
 
   auto step = [&](v4f& acc, const v8bf& A, const uint4& b, const uint4& bl) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(b), acc, 0, 0, 0);
@@ -473,42 +457,45 @@ __global__ __launch_bounds__(64 * kPersistWaves) void gemv_persist_kernel(
   };
 
   int64_t u = u_begin;
-  int64_t m = u / P.row_tiles;
-  int e, rbeg, rend;
-  tile_of(m, e, rbeg, rend);
-  int n0 = (int)(u - m * P.row_tiles) * P.run_rows;
+  int e, rbeg, rend, n0;
+  unit_of(u, e, rbeg, rend, n0);
   issue_dma(e, n0);
   load_x(rbeg, rend);
   load_bias(e, n0);
-  int buf = 0;
   for (;;) {
-    __builtin_amdgcn_s_waitcnt(0);   // DMA of unit u, activations, bias (and earlier stores)
+    __builtin_amdgcn_s_waitcnt(0);            // this wave's run of unit u, activations, bias
+    asm volatile("s_barrier" ::: "memory");   // both runs of unit u have landed
+    // blocks past K (up to 8 HG - 1 < 96) read bytes inside the run's region
+    // (finite FP4 codes or stale scales); their scale is forced to 0 below
     uint4 wreg[HG];
-    uint32_t sreg8[HG];
+    uint32_t spk[(HG + 3) / 4];   // scale bytes of groups jj, packed four per register
+    const uint8_t* wsrc = smem + wrow_off + (4 * gl + g) * kBlockBytes;
+    const uint8_t* ssrc = smem + srow_off + 4 * gl + g;
 #pragma unroll
-    for (int jj = 0; jj < HG; ++jj) {
-      const int lbc = min(4 * jj + g, nbw - 1);
-      wreg[jj] = *reinterpret_cast<const uint4*>(wrow + lbc * kBlockBytes);
-      sreg8[jj] = srow[lbc];
+    for (int jj = 0; jj < HG; ++jj) wreg[jj] = *reinterpret_cast<const uint4*>(wsrc + jj * 4 * kBlockBytes);
+#pragma unroll
+    for (int k4 = 0; k4 < (HG + 3) / 4; ++k4) {
+      uint32_t p = 0;
+#pragma unroll
+      for (int i = 0; i < 4 && 4 * k4 + i < HG; ++i) p |= (uint32_t)ssrc[4 * (4 * k4 + i)] << (8 * i);
+      spk[k4] = p;
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the slot has been read
-
-    // next unit: start its DMA before multiplying this one
-    const int64_t un = u + 1;
-    const bool more = un < u_end;
-    const int64_t mn = un / P.row_tiles;
-    int en = e, rbn = rbeg, ren = rend;
-    if (more && mn != m) tile_of(mn, en, rbn, ren);
-    const int n0n = (int)(un - mn * P.row_tiles) * P.run_rows;
-    if (more) issue_dma(en, n0n);
-
+    // both waves have read the buffer: the next unit's DMA may overwrite it
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool more = u + 1 < u_end;
+    int e1 = e, rbeg1 = rbeg, rend1 = rend, n01 = n0;
+    if (more) {
+      unit_of(u + 1, e1, rbeg1, rend1, n01);
+      issue_dma(e1, n01);
+    }
     v4f acc0 = {0.f, 0.f, 0.f, 0.f};
     v4f acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jj = 0; jj < HG; ++jj) {
       const uint4 w = wreg[jj];
       // blocks past K (scale byte forced to 0, i.e. a factor 0) contribute 0
-      const float f = e8m0_to_f32(4 * jj + g < nbw ? sreg8[jj] : 0u);
+      const uint32_t sc = (spk[jj / 4] >> (8 * (jj % 4))) & 0xffu;
+      const float f = e8m0_to_f32(4 * (gl + jj) + g < a.nb ? sc : 0u);
       const uint4 lo = MODE == kDown ? xl[jj] : xa[jj];
       step(acc0, fp4x8_to_bf16(w.x, f), xa[jj], lo);
       step(acc1, fp4x8_to_bf16(w.y, f), row_rotate4<1>(xa[jj]), row_rotate4<1>(lo));
@@ -516,11 +503,11 @@ __global__ __launch_bounds__(64 * kPersistWaves) void gemv_persist_kernel(
       step(acc1, fp4x8_to_bf16(w.w, f), row_rotate4<3>(xa[jj]), row_rotate4<3>(lo));
     }
     v4f acc = acc0 + acc1;
-    if (kh == 1) red[buf * 64 + lane] = acc;
-    // wave 1's partial sums are in LDS; the DMA of the next unit stays in flight
+    if (kh == 1) red[lane] = acc;
+    // wave 1's partial sums are in LDS; the next unit's DMA stays in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kh == 0) {
-      acc += red[buf * 64 + lane];
+      acc += red[lane];
       // lane (column r, group g) holds rows 4g + jj of column r
       const int row = rbeg + r;
       const bool col_ok = r < rend - rbeg;
@@ -559,16 +546,11 @@ __global__ __launch_bounds__(64 * kPersistWaves) void gemv_persist_kernel(
         }
       }
     }
-    buf ^= 1;
     if (!more) break;
-    if (mn != m) load_x(rbn, ren);
-    load_bias(en, n0n);
-    u = un;
-    m = mn;
-    e = en;
-    rbeg = rbn;
-    rend = ren;
-    n0 = n0n;
+    if (rbeg1 != rbeg || rend1 != rend) load_x(rbeg1, rend1);
+    load_bias(e1, n01);
+    ++u;
+    e = e1; rbeg = rbeg1; rend = rend1; n0 = n01;
   }
 }
 
@@ -577,34 +559,33 @@ __global__ __launch_bounds__(64 * kPersistWaves) void gemv_persist_kernel(
 template <int MODE, int HG>
 static hipError_t launch_persist_hg(const GemvArgs& a, const PersistPlan& P, const int* tiles,
                                     const int* sorted_pairs, const int* status, hipStream_t s) {
-  // (device + 1) << 48 | lds << 24 | blocks, cached per kernel; threads may race
-  // to fill it, but every writer stores the same value
+  // (device + 1) << 32 | blocks, cached per kernel; threads may race to fill
+  // it, but every writer stores the same value
   static std::atomic<uint64_t> cache{0};
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  const int lds = persist_lds(P);
-  const uint64_t key = ((uint64_t)(dev + 1) << 48) | ((uint64_t)lds << 24);
+  const uint64_t key = (uint64_t)(dev + 1) << 32;
   uint64_t c = cache.load(std::memory_order_relaxed);
-  if ((c & ~0xffffffull) != key) {
+  if ((c >> 32) != (key >> 32)) {
     int cus = 0, per_cu = 0;
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_persist_kernel<MODE, HG>,
-                                                       64 * kPersistWaves, lds);
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_persist_kernel<MODE, HG>, 128,
+                                                       kPersistLds);
     if (err != hipSuccess) return err;
     c = key | (uint64_t)(cus * (per_cu > 0 ? per_cu : 1));
     cache.store(c, std::memory_order_relaxed);
   }
-  const unsigned blocks = (unsigned)(c & 0xffffff);
-  gemv_persist_kernel<MODE, HG><<<blocks, 64 * kPersistWaves, lds, s>>>(a, P, tiles, sorted_pairs, status);
+  const unsigned blocks = (unsigned)(c & 0xffffffffu);
+  gemv_persist_kernel<MODE, HG><<<blocks, 128, kPersistLds, s>>>(a, P, tiles, sorted_pairs, status);
   return hipGetLastError();
 }
 
 template <int MODE>
 static hipError_t launch_persist(const GemvArgs& a, const PersistPlan& P, const int* tiles,
                                  const int* sorted_pairs, const int* status, hipStream_t s) {
-  switch (persist_half_groups(a.nb)) {
+  switch (persist_hg(a.nb)) {
     case 1: return launch_persist_hg<MODE, 1>(a, P, tiles, sorted_pairs, status, s);
     case 2: return launch_persist_hg<MODE, 2>(a, P, tiles, sorted_pairs, status, s);
     case 3: return launch_persist_hg<MODE, 3>(a, P, tiles, sorted_pairs, status, s);
@@ -658,7 +639,7 @@ hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const M
   const int64_t pairs = (int64_t)sh.T * sh.k;
   const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.I / 16);
   if (persist_fits(a.nb, a.act_bytes))
-    return launch_persist<kGateUp>(a, persist_plan(kGateUp, a.nb, sh.I), ws.tiles, ws.sorted_pairs,
+    return launch_persist<kGateUp>(a, persist_plan(kGateUp, sh.I), ws.tiles, ws.sorted_pairs,
                                    ws.status, s);
   return launch_gemv<kGateUp>(a, sh.I, ntile_bound, pick_ksplit(busy), s);
 }
@@ -684,7 +665,7 @@ hipError_t launch_moe_down_bf16(const MoeShape& sh, const MoeWeights& w, const W
   const int64_t pairs = (int64_t)sh.T * sh.k;
   const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.H / 16);
   if (persist_fits(a.nb, a.act_bytes))
-    return launch_persist<kDown>(a, persist_plan(kDown, a.nb, sh.H), ws.tiles, ws.sorted_pairs,
+    return launch_persist<kDown>(a, persist_plan(kDown, sh.H), ws.tiles, ws.sorted_pairs,
                                  ws.status, s);
   return launch_gemv<kDown>(a, sh.H, ntile_bound, pick_ksplit(busy), s);
 }
@@ -707,7 +688,7 @@ hipError_t launch_linear_bf16(const uint16_t* x, int M, int N, int K, const uint
   const int64_t mt = (M + 15) / 16;
   const int64_t row_tiles = (int64_t)(N / 16) * mt;
   if (persist_fits(a.nb, a.act_bytes) && row_tiles >= 2048)
-    return launch_persist<kDense>(a, persist_plan(kDense, a.nb, N), nullptr, nullptr, nullptr, s);
+    return launch_persist<kDense>(a, persist_plan(kDense, N), nullptr, nullptr, nullptr, s);
   return launch_gemv<kDense>(a, N, mt, pick_ksplit(row_tiles), s);
 }
 
