@@ -357,6 +357,8 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
   // tail lanes of the last instruction re-read the run's last 16 bytes
   const int64_t wrun = kRunRows * rb;                 // weight bytes of the run
   const int64_t srun = (int64_t)kRunRows * a.nb;      // scale bytes (4-byte aligned run)
+  const uint32_t wlast = (uint32_t)(wrun - 16), slast = (uint32_t)(srun - 4);
+  const uint32_t lane16 = 16u * lane, lane4 = 4u * lane;
   auto issue_dma = [&](int e, int n0) {
     // first row of the run: gate_up wave 1 takes the matching up rows
     const size_t row0 = (size_t)e * a.rows_per_expert + n0 + (kPair ? (size_t)kh * a.nout : (size_t)kh * kRunRows);
@@ -365,12 +367,12 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     uint8_t* dst = smem + kh * kRunBytes;
 #pragma unroll
     for (int c = 0; c < kRunDma; ++c) {
-      const int64_t off = min((int64_t)c * 1024 + lane * 16, wrun - 16);
+      const uint32_t off = min((uint32_t)(c * 1024) + lane16, wlast);
       __builtin_amdgcn_global_load_lds(gw + off, dst + c * 1024, 16, 0, 2);
     }
 #pragma unroll
     for (int c = 0; c < kRunScDma; ++c) {
-      const int64_t off = min((int64_t)c * 256 + lane * 4, srun - 4);
+      const uint32_t off = min((uint32_t)(c * 256) + lane4, slast);
       __builtin_amdgcn_global_load_lds(gs + off, dst + kRunDma * 1024 + c * 256, 4, 0, 2);
     }
   };
@@ -388,11 +390,7 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
       rend = t.z;
     }
   };
-  auto unit_of = [&](int64_t u, int& e, int& rbeg, int& rend, int& n0) {
-    const int64_t m = u / P.row_tiles;
-    tile_of(m, e, rbeg, rend);
-    n0 = (int)(u - m * P.row_tiles) * (kPair ? kRunRows : kUnitRows);
-  };
+  constexpr int kUnitStep = kPair ? kRunRows : kUnitRows;   // first rows of consecutive units
 
   // activations of an m-tile (compact layout), this wave's groups only
   const int gl = kh * HG;
@@ -456,9 +454,13 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     if (MODE == kDown) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(bl), acc, 0, 0, 0);
   };
 
+  // unit u = m-tile m, row tile nt (stepped without dividing)
   int64_t u = u_begin;
-  int e, rbeg, rend, n0;
-  unit_of(u, e, rbeg, rend, n0);
+  int64_t m = u_begin / P.row_tiles;
+  int nt = (int)(u_begin - m * P.row_tiles);
+  int e, rbeg, rend;
+  tile_of(m, e, rbeg, rend);
+  int n0 = nt * kUnitStep;
   issue_dma(e, n0);
   load_x(rbeg, rend);
   load_bias(e, n0);
@@ -483,9 +485,11 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     // both waves have read the buffer: the next unit's DMA may overwrite it
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const bool more = u + 1 < u_end;
-    int e1 = e, rbeg1 = rbeg, rend1 = rend, n01 = n0;
+    const bool next_tile = nt + 1 == P.row_tiles;
+    int e1 = e, rbeg1 = rbeg, rend1 = rend;
+    const int n01 = next_tile ? 0 : n0 + kUnitStep;
     if (more) {
-      unit_of(u + 1, e1, rbeg1, rend1, n01);
+      if (next_tile) tile_of(m + 1, e1, rbeg1, rend1);
       issue_dma(e1, n01);
     }
     v4f acc0 = {0.f, 0.f, 0.f, 0.f};
@@ -550,6 +554,12 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     if (rbeg1 != rbeg || rend1 != rend) load_x(rbeg1, rend1);
     load_bias(e1, n01);
     ++u;
+    if (next_tile) {
+      ++m;
+      nt = 0;
+    } else {
+      ++nt;
+    }
     e = e1; rbeg = rbeg1; rend = rend1; n0 = n01;
   }
 }
