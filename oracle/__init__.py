@@ -18,23 +18,27 @@ Pins (see tests/test_oracle_*.py):
     gpt-oss page prints, nibble round trips, exact powers of two;
   * fp8 e4m3: exhaustive nearest-code search over all bf16 inputs;
   * route_topk: brute-force full sort;
+  * quantize_mxfp4: hand-derived rounding cases (tests/golden), exact round
+    trips of representable blocks, the scale rule's closed form, the error
+    bound of round-to-nearest;
   * moe_forward / linear: exact rational (fractions.Fraction) brute force on
     tiny shapes, reductions E=1/k=1 to the dense linear, identical experts.
   Values at the full layer shapes are "parity unpinned" by the pages: they
   print no output of any layer; only the functions above are pinned.
 """
 
-from . import fp8, moe, mxfp4  # noqa: F401
+from . import fp8, moe, mxfp4, quant  # noqa: F401
 from .fp8 import e4m3_decode, e4m3_encode, quant_per_tensor  # noqa: F401
 from .moe import (ACT_BF16, ACT_FP8_E4M3, linear, linear_rows,  # noqa: F401
                   moe_forward, moe_forward_routed, permute, route_topk,
                   swiglu)
 from .mxfp4 import (E2M1_TABLE, bf16_bits_to_f64, dequant,  # noqa: F401
                     e2m1_value, e8m0_scale, pack_nibbles, unpack_nibbles)
+from .quant import quantize_mxfp4  # noqa: F401
 
 __all__ = [
     "fp8", "moe", "mxfp4", "e4m3_decode", "e4m3_encode", "quant_per_tensor",
     "ACT_BF16", "ACT_FP8_E4M3", "linear", "linear_rows", "moe_forward", "moe_forward_routed", "permute", "route_topk", "swiglu", "E2M1_TABLE",
     "bf16_bits_to_f64", "dequant", "e2m1_value", "e8m0_scale",
-    "pack_nibbles", "unpack_nibbles",
+    "pack_nibbles", "unpack_nibbles", "quant", "quantize_mxfp4",
 ]
