@@ -193,6 +193,26 @@ def measure_dense(run, synth, steps, warmup):
     return out
 
 
+def measure_quantizer(run, synth, steps, warmup):
+    """BF16 -> MXFP4 quantisation of the lm_head weight (201,088 x 2880): a stream
+    of N*K*2 bytes in and N*K*17/32 bytes out."""
+    mx = run.mx
+    N, K = synth.DENSE_SHAPES["lm_head"]
+    w = run.dev(synth.dense_bf16_weights(50, N, K))
+    blocks = run.torch.empty((N, K // 32, 16), dtype=run.torch.uint8, device="cuda")
+    scales = run.torch.empty((N, K // 32), dtype=run.torch.uint8, device="cuda")
+
+    def step(_ev):
+        mx.mxfp4_quantize_weights(w, blocks, scales)
+
+    ms, _, _ = run.time_steps(step, steps, warmup, flush=True)
+    nbytes = N * K * 2 + N * (K // 32) * 17
+    mean = float(np.mean(ms))
+    del w, blocks, scales
+    return dict(N=N, K=K, ms=mean, GBps=nbytes / mean / 1e6, hbm_frac=nbytes / mean / 1e6 / HBM_PEAK_GBS,
+                bytes=nbytes)
+
+
 def cpu_baseline(synth, budget_tokens=32):
     """The float64 oracle on the first `budget_tokens` tokens of the headline batch (all 32 by
     default: about 80 experts, several seconds), on host cores."""
@@ -283,6 +303,8 @@ def main():
         torch.cuda.empty_cache()
         others["dense"] = measure_dense(run, synth, max(args.steps // 2, 5), 2)
         print("bench: dense set done", file=sys.stderr, flush=True)
+        others["quantize_lm_head"] = measure_quantizer(run, synth, max(args.steps // 3, 5), 2)
+        print("bench: quantiser %.1f us" % (others["quantize_lm_head"]["ms"] * 1e3), file=sys.stderr, flush=True)
 
     fp8 = prim["act"] != "bf16"
     kname = "gemm_fp8_kernel<true, true>" if fp8 else "gemv_stream_kernel<0>"

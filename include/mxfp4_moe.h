@@ -216,6 +216,25 @@ int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K,
 int mxfp4_quant_fp8_e4m3(const void* in, int32_t in_dtype, int64_t n, uint8_t* codes,
                          float* scale, float* amax, void* stream);
 
+/*
+ * BF16 -> MXFP4 weight quantiser, for dense weights kept in bf16 (gpt-oss
+ * page, "MXFP4 Tensor Structure": attention projections and the LM head are
+ * stored bf16; spark-vllm page: MXFP4 for qkv/o/lm_head).  The steps follow
+ * the gpt-oss page's "Conversion Methodology" (per-block amax, scale, E2M1
+ * rounding, packing) with 32-element blocks and the OCP MX scale rule:
+ *   X = floor(log2(max |v| of the block)) - 2, clamped to [-125, 125];
+ *   scale byte = X + 127 (so 2..252, what mxfp4_linear takes);
+ *   code = E2M1 value nearest to |v| / 2^X, ties to the even mantissa,
+ *          saturating at 6, with the sign bit of v;
+ *   nibbles packed as mxfp4_linear reads them (element 2i low, 2i+1 high).
+ *   w       bf16 [N, K], 16-byte aligned; finite values (NaN/Inf unsupported)
+ *   blocks  uint8 [N, K/32, 16] output, 16-byte aligned
+ *   scales  uint8 [N, K/32] output
+ * Limits: K a positive multiple of 32, 0 <= N, N * K < 2^40 (N == 0 is a no-op).
+ */
+int mxfp4_quantize_weights(const uint16_t* w, int64_t N, int64_t K, uint8_t* blocks,
+                           uint8_t* scales, void* stream);
+
 /* Thin hipEvent helpers so callers can time stages without their own HIP
    bindings: create (timing enabled), destroy, and elapsed milliseconds between
    two recorded events (synchronises on `end`). */

@@ -66,11 +66,13 @@ def lib():
                                    _c_void_p, _c_void_p]
         L.mxfp4_quant_fp8_e4m3.argtypes = [_c_void_p, _i32, _i64, _c_void_p, _c_void_p, _c_void_p,
                                            _c_void_p]
+        L.mxfp4_quantize_weights.argtypes = [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]
         L.mxfp4_event_create.argtypes = [ctypes.POINTER(_c_void_p)]
         L.mxfp4_event_destroy.argtypes = [_c_void_p]
         L.mxfp4_event_elapsed_ms.argtypes = [_c_void_p, _c_void_p, ctypes.POINTER(ctypes.c_float)]
         for name in ("mxfp4_route_topk", "mxfp4_moe_workspace_size", "mxfp4_moe_workspace_layout_query",
-                     "mxfp4_moe_forward", "mxfp4_linear", "mxfp4_quant_fp8_e4m3", "mxfp4_event_create",
+                     "mxfp4_moe_forward", "mxfp4_linear", "mxfp4_quant_fp8_e4m3",
+                     "mxfp4_quantize_weights", "mxfp4_event_create",
                      "mxfp4_event_destroy", "mxfp4_event_elapsed_ms"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -228,6 +230,25 @@ def mxfp4_quant_fp8_e4m3(inp, codes=None, scale=None, amax=None, stream=None):
     _check("mxfp4_quant_fp8_e4m3", lib().mxfp4_quant_fp8_e4m3(
         _ptr(inp), dt, inp.numel(), _ptr(codes), _ptr(scale), _ptr(amax), _stream(stream)))
     return codes, scale, amax
+
+
+def mxfp4_quantize_weights(w, blocks=None, scales=None, stream=None):
+    """bf16 weights [N, K] -> MXFP4 blocks uint8 [N, K/32, 16] and E8M0 scales [N, K/32]."""
+    _need(w, "w", torch.bfloat16, 2)
+    N, K = w.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    if blocks is None:
+        blocks = torch.empty((N, K // 32, 16), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    _need(blocks, "blocks", torch.uint8, 3)
+    _need(scales, "scales", torch.uint8, 2)
+    if tuple(blocks.shape) != (N, K // 32, 16) or tuple(scales.shape) != (N, K // 32):
+        raise ValueError("blocks/scales shape does not match w")
+    _check("mxfp4_quantize_weights", lib().mxfp4_quantize_weights(
+        _ptr(w), N, K, _ptr(blocks), _ptr(scales), _stream(stream)))
+    return blocks, scales
 
 
 def mxfp4_event_create():

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmxfp4moe.so")
-SOURCES = ["route_permute.hip", "quant_combine.hip", "gemm_bf16.hip", "gemm_fp8.hip", "abi.hip"]
+SOURCES = ["route_permute.hip", "quant_combine.hip", "quant_mxfp4.hip", "gemm_bf16.hip", "gemm_fp8.hip",
+           "abi.hip"]
 ARCH = "gfx950"
 # No fast-math: the FP8 quantiser relies on correctly rounded fp32 division.
 # Packed fp32 VALU ops are switched off for the device code.

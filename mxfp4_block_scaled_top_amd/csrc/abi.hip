@@ -289,6 +289,21 @@ int mxfp4_quant_fp8_e4m3(const void* in, int32_t in_dtype, int64_t n, uint8_t* c
   return ok();
 }
 
+int mxfp4_quantize_weights(const uint16_t* w, int64_t N, int64_t K, uint8_t* blocks,
+                           uint8_t* scales, void* stream) {
+  if (K <= 0 || K % 32) return fail(MXFP4_E_SHAPE, "K=%lld must be a positive multiple of 32", (long long)K);
+  if (N < 0 || (N > 0 && N > (1LL << 40) / K)) return fail(MXFP4_E_SHAPE, "N=%lld out of range", (long long)N);
+  if (N == 0) return ok();
+  if (!w || !blocks || !scales) return fail(MXFP4_E_NULL, "quantize_weights: null pointer");
+  if (!aligned(w, 16) || !aligned(blocks, 16))
+    return fail(MXFP4_E_ALIGN, "quantize_weights: w and blocks need 16-byte alignment");
+  int rc = check_device();
+  if (rc) return rc;
+  const hipError_t e = mx::launch_quant_mxfp4(w, N * (K / 32), blocks, scales, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize_weights launch");
+  return ok();
+}
+
 int mxfp4_event_create(void** event) {
   if (!event) return fail(MXFP4_E_NULL, "event is null");
   hipEvent_t ev;

@@ -78,6 +78,10 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
 hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
                                int64_t ntile_bound, hipStream_t s);
 
+// bf16 [nblocks * 32] -> MXFP4 blocks [nblocks, 16] + E8M0 scales [nblocks]
+hipError_t launch_quant_mxfp4(const uint16_t* w, int64_t nblocks, uint8_t* blocks, uint8_t* scales,
+                              hipStream_t s);
+
 // out[t] = sum_j w[t,j] * y[inv[t*k+j]]  -> bf16
 hipError_t launch_combine(const MoeShape& sh, const float* topk_weights, const WsPtrs& ws,
                           uint16_t* out, hipStream_t s);

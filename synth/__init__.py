@@ -106,6 +106,23 @@ def dense(seed, N, K):
     return dict(w_blocks=blocks, w_scales=scales, bias=bias)
 
 
+def dense_bf16_weights(seed, N, K):
+    """bf16 bits [N, K] of a dense weight before MXFP4 quantisation: N(0, 0.02)
+    with row scales spread over 2^-4 .. 2^4 and about one outlier (x 50) per
+    1024 elements, the shape a trained projection's weights take.  Generated
+    in row chunks (float32) so the 201k-row lm_head fits in a few GB."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((N, K), dtype=np.uint16)
+    for r0 in range(0, N, 8192):
+        r1 = min(N, r0 + 8192)
+        scale = np.ldexp(np.float32(0.02), rng.integers(-4, 5, size=(r1 - r0, 1))).astype(np.float32)
+        w = rng.standard_normal(size=(r1 - r0, K), dtype=np.float32) * scale
+        spike = rng.random(size=(r1 - r0, K), dtype=np.float32) < np.float32(1.0 / 1024)
+        w = np.where(spike, w * np.float32(50.0), w)
+        out[r0:r1] = f32_to_bf16_bits(w)
+    return out
+
+
 def dense_x(seed, M, K):
     rng = np.random.default_rng(seed)
     return f32_to_bf16_bits(rng.normal(0.0, 1.0, size=(M, K)).astype(np.float32))

@@ -120,6 +120,11 @@ def test_linear_and_quant_and_route_validation(L):
     assert L.mxfp4_route_topk(_fake(), 4, 600, 4, _fake(), _fake(), None) == E_SHAPE
     assert L.mxfp4_route_topk(None, 4, 128, 4, _fake(), _fake(), None) == E_NULL
     assert L.mxfp4_route_topk(None, 0, 128, 4, None, None, None) == 0
+    assert L.mxfp4_quantize_weights(_fake(), 4, 33, _fake(), _fake(), None) == E_SHAPE
+    assert L.mxfp4_quantize_weights(_fake(), -1, 32, _fake(), _fake(), None) == E_SHAPE
+    assert L.mxfp4_quantize_weights(None, 4, 32, _fake(), _fake(), None) == E_NULL
+    assert L.mxfp4_quantize_weights(ctypes.c_void_p(0x1008), 4, 32, _fake(), _fake(), None) == E_ALIGN
+    assert L.mxfp4_quantize_weights(None, 0, 32, None, None, None) == 0
 
 
 def test_valid_call_without_a_gpu_reports_no_device(L):

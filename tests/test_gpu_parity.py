@@ -390,3 +390,69 @@ def test_moe_full_size_workloads(mx, full_layer, name):
         rc = oracle.e4m3_encode((h_rows / sh).astype(np.float32).astype(np.float64))
         hc = ws[lay["h_codes"]:lay["h_codes"] + np_ * I].view(np_, I)[torch.from_numpy(srows).cuda()]
         assert np.array_equal(hc.cpu().numpy(), rc)
+
+
+# ------------------------------------------------------ weight quantiser ----
+
+
+def _quant_ref(w_bits):
+    return oracle.quantize_mxfp4(bf16_bits_to_f64(w_bits))
+
+
+def _quant_gpu(mx, w_bits):
+    b, s = mx.mxfp4_quantize_weights(to_dev(w_bits, torch))
+    torch.cuda.synchronize()
+    return b.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 320), (64, 2880), (5, 4096)])
+def test_quantize_weights_bit_exact(mx, N, K):
+    w = synth.dense_bf16_weights(40 + N, N, K)
+    b, s = _quant_gpu(mx, w)
+    rb, rs = _quant_ref(w)
+    assert np.array_equal(s, rs)
+    assert np.array_equal(b, rb)
+
+
+def test_quantize_weights_ties_signs_and_extremes(mx):
+    # rows: exact rounding ties under scale 2^0 (block max 6), zeros and -0,
+    # bf16 subnormals, the largest finite bf16, and values just past ties
+    rows = []
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]
+    rows.append((ties + [-t for t in ties]) * 2)
+    rows.append([0.0] * 16 + [-0.0] * 16)
+    rows.append([2.0 ** -133 * (i + 1) for i in range(32)])
+    rows.append([3.3895e38 * (1 - 2 * (i % 2)) for i in range(32)])
+    rows.append([(t + 2.0 ** -6) for t in ties] * 4)
+    rows.append([7.99, 7.0, -6.5] + [0.0] * 29)
+    w = synth.f32_to_bf16_bits(np.array(rows, dtype=np.float32))
+    b, s = _quant_gpu(mx, w)
+    rb, rs = _quant_ref(w)
+    assert np.array_equal(s, rs)
+    assert np.array_equal(b, rb)
+
+
+def test_quantize_weights_full_lm_head_sampled(mx):
+    # the 201,088 x 2880 lm_head quantised at once; rows sampled for the oracle
+    N, K = synth.DENSE_SHAPES["lm_head"]
+    w = synth.dense_bf16_weights(50, N, K)
+    b, s = _quant_gpu(mx, w)
+    rows = np.random.default_rng(51).choice(N, 512, replace=False)
+    rows = np.concatenate([rows, [0, N - 1]])
+    rb, rs = _quant_ref(w[rows])
+    assert np.array_equal(s[rows], rs)
+    assert np.array_equal(b[rows], rb)
+
+
+def test_quantized_weights_feed_the_linear(mx):
+    # quantise on the GPU, run the dense projection on the result, compare with
+    # the oracle's linear on the oracle's quantisation of the same weights
+    N, K, M = 1040, 2880, 4
+    w = synth.dense_bf16_weights(52, N, K)
+    b, s = mx.mxfp4_quantize_weights(to_dev(w, torch))
+    x = synth.dense_x(53, M, K)
+    out = mx.mxfp4_linear(to_dev(x, torch), b, s)
+    torch.cuda.synchronize()
+    rb, rs = _quant_ref(w)
+    ref = oracle.linear(x, rb, rs, None)
+    assert_close_rounded(bf16_dev_to_f64(out), ref, "quantise -> linear")
