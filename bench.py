@@ -135,10 +135,10 @@ def moe_setup(run, Ld, name, synth):
     ws = torch.empty(mx.mxfp4_moe_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device="cuda")
 
     def step(events):
-        mx.mxfp4_route_topk(logits, k, ids, w)
-        mx.mxfp4_moe_forward(x, ids, w, Ld["w13_blocks"], Ld["w13_scales"], Ld["w13_bias"],
-                             Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"], act, out=out,
-                             workspace=ws, events=events)
+        # router + layer in one library call (its "permute" stage covers routing too)
+        mx.mxfp4_moe_layer(x, logits, k, Ld["w13_blocks"], Ld["w13_scales"], Ld["w13_bias"],
+                           Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"], act, out=out,
+                           topk_ids=ids, topk_weights=w, workspace=ws, events=events)
 
     step(None)
     torch.cuda.synchronize()

@@ -187,6 +187,21 @@ int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
                       size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream);
 
 /*
+ * The router and the layer in one call: mxfp4_route_topk on `logits` (fp32
+ * [T, E], 4-byte aligned) writing topk_ids / topk_weights (outputs here, same
+ * layout and values as mxfp4_route_topk), then mxfp4_moe_forward on them, on
+ * one stream in one call.  Every other
+ * argument, limit and error is that of mxfp4_moe_forward; the result is
+ * bitwise the same as the two calls in sequence.
+ */
+int mxfp4_moe_layer(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t I,
+                    int32_t E, int32_t k, int32_t* topk_ids, float* topk_weights,
+                    const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                    const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                    int32_t act_mode, uint16_t* out, void* workspace, size_t workspace_bytes,
+                    const mxfp4_moe_opts* opts, void* stream);
+
+/*
  * Dense MXFP4 projection out = x W^T + b (spark-vllm page, MXFP4 qkv/o/lm_head;
  * gptoss-spark page: qkv_proj, o_proj and the 201k-row lm_head in MXFP4), bf16
  * activations, fp32 accumulation, one round-to-nearest-even to bf16.

@@ -62,6 +62,10 @@ def lib():
             _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
             _i32, _c_void_p, _c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeOpts), _c_void_p]
+        L.mxfp4_moe_layer.argtypes = [
+            _c_void_p, _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
+            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+            _i32, _c_void_p, _c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeOpts), _c_void_p]
         L.mxfp4_linear.argtypes = [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p, _c_void_p]
         L.mxfp4_quant_fp8_e4m3.argtypes = [_c_void_p, _i32, _i64, _c_void_p, _c_void_p, _c_void_p,
@@ -71,7 +75,7 @@ def lib():
         L.mxfp4_event_destroy.argtypes = [_c_void_p]
         L.mxfp4_event_elapsed_ms.argtypes = [_c_void_p, _c_void_p, ctypes.POINTER(ctypes.c_float)]
         for name in ("mxfp4_route_topk", "mxfp4_moe_workspace_size", "mxfp4_moe_workspace_layout_query",
-                     "mxfp4_moe_forward", "mxfp4_linear", "mxfp4_quant_fp8_e4m3",
+                     "mxfp4_moe_forward", "mxfp4_moe_layer", "mxfp4_linear", "mxfp4_quant_fp8_e4m3",
                      "mxfp4_quantize_weights", "mxfp4_event_create",
                      "mxfp4_event_destroy", "mxfp4_event_elapsed_ms"):
             getattr(L, name).restype = ctypes.c_int
@@ -188,6 +192,57 @@ def mxfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bia
         _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts is not None else None,
         _stream(stream)))
     return out
+
+
+def mxfp4_moe_layer(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias,
+                    act_mode, out=None, topk_ids=None, topk_weights=None, workspace=None, events=None,
+                    stream=None):
+    """Router + MoE layer in one call; returns (out, topk_ids, topk_weights)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(logits, "logits", torch.float32, 2)
+    T, H = x.shape
+    E = logits.shape[1]
+    if logits.shape[0] != T or w13_blocks.shape[0] != E:
+        raise ValueError("logits must be [T, E]")
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    _need(topk_weights, "topk_weights", torch.float32, 2)
+    for t, name, nd in ((w13_blocks, "w13_blocks", 4), (w13_scales, "w13_scales", 3),
+                        (w2_blocks, "w2_blocks", 4), (w2_scales, "w2_scales", 3)):
+        _need(t, name, torch.uint8, nd)
+    I = w13_blocks.shape[1] // 2
+    if (tuple(w13_blocks.shape) != (E, 2 * I, H // 32, 16) or tuple(w13_scales.shape) != (E, 2 * I, H // 32)
+            or tuple(w2_blocks.shape) != (E, H, I // 32, 16) or tuple(w2_scales.shape) != (E, H, I // 32)
+            or tuple(topk_ids.shape) != (T, k) or tuple(topk_weights.shape) != (T, k)
+            or (w13_bias is not None and tuple(w13_bias.shape) != (E, 2 * I))
+            or (w2_bias is not None and tuple(w2_bias.shape) != (E, H))):
+        raise ValueError("inconsistent MoE tensor shapes")
+    if w13_bias is not None:
+        _need(w13_bias, "w13_bias", torch.bfloat16, 2)
+    if w2_bias is not None:
+        _need(w2_bias, "w2_bias", torch.bfloat16, 2)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if workspace is None:
+        workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, act_mode), 1),
+                                dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    opts = None
+    if events is not None:
+        opts = MoeOpts()
+        for i, ev in enumerate(events):
+            opts.events[i] = ev
+    _check("mxfp4_moe_layer", lib().mxfp4_moe_layer(
+        _ptr(x), _ptr(logits), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
+        _ptr(w13_blocks), _ptr(w13_scales), _ptr(w13_bias),
+        _ptr(w2_blocks), _ptr(w2_scales), _ptr(w2_bias), act_mode, _ptr(out),
+        _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts is not None else None,
+        _stream(stream)))
+    return out, topk_ids, topk_weights
 
 
 def mxfp4_linear(x, w_blocks, w_scales, bias=None, out=None, stream=None):

@@ -175,24 +175,28 @@ int mxfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E, int32_t
   return ok();
 }
 
-int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
-                      const int32_t* topk_ids, const float* topk_weights,
-                      const uint8_t* w13_blocks, const uint8_t* w13_scales,
-                      const uint16_t* w13_bias, const uint8_t* w2_blocks,
-                      const uint8_t* w2_scales, const uint16_t* w2_bias, int32_t act_mode,
-                      uint16_t* out, void* workspace, size_t workspace_bytes,
-                      const mxfp4_moe_opts* opts, void* stream) {
+namespace {
+
+// The layer after validation of the shared arguments.  With `logits`, the
+// router runs first (writing topk_ids / topk_weights); otherwise they are
+// inputs.
+int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t I, int32_t E,
+            int32_t k, int32_t* topk_ids, float* topk_weights, const uint8_t* w13_blocks,
+            const uint8_t* w13_scales, const uint16_t* w13_bias, const uint8_t* w2_blocks,
+            const uint8_t* w2_scales, const uint16_t* w2_bias, int32_t act_mode, uint16_t* out,
+            void* workspace, size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream,
+            const char* fn) {
   int rc = moe_shape_check(T, H, I, E, k, act_mode);
   if (rc) return rc;
   if (T == 0) return ok();
   if (!x || !topk_ids || !topk_weights || !w13_blocks || !w13_scales || !w2_blocks ||
       !w2_scales || !out)
-    return fail(MXFP4_E_NULL, "moe_forward: null pointer");
+    return fail(MXFP4_E_NULL, "%s: null pointer", fn);
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w13_blocks, 16) ||
       !aligned(w2_blocks, 16) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
-      !aligned(w13_scales, 4) || !aligned(w2_scales, 4) ||
+      !aligned(w13_scales, 4) || !aligned(w2_scales, 4) || (logits && !aligned(logits, 4)) ||
       (w13_bias && !aligned(w13_bias, 8)) || (w2_bias && !aligned(w2_bias, 8)))
-    return fail(MXFP4_E_ALIGN, "moe_forward: x/out/blocks need 16-byte, biases 8-byte, ids/weights/scales 4-byte alignment");
+    return fail(MXFP4_E_ALIGN, "%s: x/out/blocks need 16-byte, biases 8-byte, logits/ids/weights/scales 4-byte alignment", fn);
   mxfp4_moe_workspace_layout L;
   plan(T, H, I, E, k, act_mode, &L);
   if (!workspace) return fail(MXFP4_E_WORKSPACE, "workspace is null");
@@ -225,6 +229,7 @@ int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
   } while (0)
 
   MX_STEP(mark(MXFP4_STAGE_BEGIN), "event record");
+  if (logits) MX_STEP(mx::launch_route_topk(logits, (int)T, E, k, topk_ids, topk_weights, s), "route launch");
   MX_STEP(mx::launch_permute(topk_ids, (int)npairs, E, bm, (int)bound, ws, s), "permute launch");
   MX_STEP(mark(MXFP4_STAGE_PERMUTE), "event record");
   if (fp8) {
@@ -251,6 +256,33 @@ int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
   MX_STEP(mark(MXFP4_STAGE_COMBINE), "event record");
 #undef MX_STEP
   return ok();
+}
+
+}  // namespace
+
+int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                      const int32_t* topk_ids, const float* topk_weights,
+                      const uint8_t* w13_blocks, const uint8_t* w13_scales,
+                      const uint16_t* w13_bias, const uint8_t* w2_blocks,
+                      const uint8_t* w2_scales, const uint16_t* w2_bias, int32_t act_mode,
+                      uint16_t* out, void* workspace, size_t workspace_bytes,
+                      const mxfp4_moe_opts* opts, void* stream) {
+  return moe_run(x, nullptr, T, H, I, E, k, const_cast<int32_t*>(topk_ids),
+                 const_cast<float*>(topk_weights), w13_blocks, w13_scales, w13_bias, w2_blocks,
+                 w2_scales, w2_bias, act_mode, out, workspace, workspace_bytes, opts, stream,
+                 "moe_forward");
+}
+
+int mxfp4_moe_layer(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t I,
+                    int32_t E, int32_t k, int32_t* topk_ids, float* topk_weights,
+                    const uint8_t* w13_blocks, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                    const uint8_t* w2_blocks, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                    int32_t act_mode, uint16_t* out, void* workspace, size_t workspace_bytes,
+                    const mxfp4_moe_opts* opts, void* stream) {
+  if (T > 0 && !logits) return fail(MXFP4_E_NULL, "moe_layer: logits is null");
+  return moe_run(x, logits, T, H, I, E, k, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bias,
+                 w2_blocks, w2_scales, w2_bias, act_mode, out, workspace, workspace_bytes, opts,
+                 stream, "moe_layer");
 }
 
 int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_blocks,

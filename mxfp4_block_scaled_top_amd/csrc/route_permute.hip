@@ -12,17 +12,12 @@
 namespace mx {
 
 // ---------------------------------------------------------------- top-k ----
-// One wave per token; lane l holds logits l, l+64, ... (PER_LANE of them).
+// One wave routes one token; lane l holds logits l, l+64, ... (PER_LANE of
+// them).  Lanes j < k end with the j-th choice (id, softmax weight over the k
+// chosen logits).
 template <int PER_LANE>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
-                                                         int T, int E, int k,
-                                                         int* __restrict__ ids,
-                                                         float* __restrict__ weights) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
+                                            int& out_id, float& out_w) {
   float v[PER_LANE];
   bool avail[PER_LANE];
 #pragma unroll
@@ -60,9 +55,25 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const float vmax = __shfl(my_val, 0, 64);
   const float z = lane < k ? expf(my_val - vmax) : 0.0f;
   const float s = wave_sum(z);
+  out_id = my_id;
+  out_w = z / s;
+}
+
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int T, int E, int k,
+                                                         int* __restrict__ ids,
+                                                         float* __restrict__ weights) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  int id;
+  float w;
+  route_token<PER_LANE>(logits + (size_t)t * E, E, k, lane, id, w);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    weights[(size_t)t * k + lane] = z / s;
+    ids[(size_t)t * k + lane] = id;
+    weights[(size_t)t * k + lane] = w;
   }
 }
 
@@ -156,14 +167,12 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int BM, int b
 }
 
 // Single-block permutation for small pair counts (decode): counts, offsets,
-// stable scatter and tile list in one launch.  LDS: cnt[E], off[E], run[E],
-// wcnt[16*E] ints (dynamic) + static scan scratch.
-__global__ __launch_bounds__(1024) void permute_fused_kernel(
-    const int* __restrict__ ids, int npairs, int E, int id_bits, int BM, int bound,
-    int* __restrict__ status, int* __restrict__ offsets, int* __restrict__ sorted_pairs,
-    int* __restrict__ inv, int* __restrict__ tiles) {
-  extern __shared__ int lds[];
-  __shared__ int scan_tmp[kChunkWaves + 1];
+// stable scatter and tile list, run by a whole 1024-thread block.  `ids` may
+// live in global memory or LDS.  lds: cnt[E], off[E], run[E], wcnt[16*E] ints.
+__device__ void permute_block(const int* ids, int npairs, int E, int id_bits, int BM, int bound,
+                              int* __restrict__ status, int* __restrict__ offsets,
+                              int* __restrict__ sorted_pairs, int* __restrict__ inv,
+                              int* __restrict__ tiles, int* lds, int* scan_tmp) {
   int* cnt = lds;
   int* off = lds + E;
   int* run = lds + 2 * E;
@@ -205,6 +214,16 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
   }
   if (bad) atomicOr(&status[kStFlags], 1);
   write_tiles(cnt, off, E, BM, bound, scan_tmp, tiles, status);
+}
+
+__global__ __launch_bounds__(1024) void permute_fused_kernel(
+    const int* __restrict__ ids, int npairs, int E, int id_bits, int BM, int bound,
+    int* __restrict__ status, int* __restrict__ offsets, int* __restrict__ sorted_pairs,
+    int* __restrict__ inv, int* __restrict__ tiles) {
+  extern __shared__ int lds[];
+  __shared__ int scan_tmp[kChunkWaves + 1];
+  permute_block(ids, npairs, E, id_bits, BM, bound, status, offsets, sorted_pairs, inv, tiles, lds,
+                scan_tmp);
 }
 
 // Multi-block path, phase 1: per-chunk ranks and per-chunk expert counts.

@@ -105,6 +105,13 @@ def test_moe_forward_rejects_bad_arguments_without_touching_memory(L):
     assert call(ws=None) == E_WORKSPACE
     assert call(wsb=100) == E_WORKSPACE
     assert call(T=0) == 0                       # empty batch: a no-op
+    # the router + layer call: same checks, plus the logits
+    assert L.mxfp4_moe_layer(_fake(1), None, 4, 2880, 2880, 128, 4, _fake(2), _fake(3), _fake(4), _fake(5),
+                             None, _fake(6), _fake(7), None, 0, _fake(8), _fake(9), 1 << 40, None,
+                             None) == E_NULL
+    assert L.mxfp4_moe_layer(_fake(1), _fake(10), 4, 2880, 2880, 128, 4, _fake(2), _fake(3), _fake(4),
+                             _fake(5), None, _fake(6), _fake(7), None, 9, _fake(8), _fake(9), 1 << 40,
+                             None, None) == E_MODE
 
 
 def test_linear_and_quant_and_route_validation(L):

@@ -456,3 +456,46 @@ def test_quantized_weights_feed_the_linear(mx):
     rb, rs = _quant_ref(w)
     ref = oracle.linear(x, rb, rs, None)
     assert_close_rounded(bf16_dev_to_f64(out), ref, "quantise -> linear")
+
+
+# ------------------------------------------------- router + layer in one call ----
+
+
+@pytest.mark.parametrize("E,H,I,T,k,act", [(8, 288, 320, 37, 4, synth.ACT_BF16),
+                                           (8, 288, 320, 37, 4, synth.ACT_FP8_E4M3),
+                                           (128, 256, 128, 1025, 4, synth.ACT_BF16),
+                                           (128, 256, 128, 64, 4, synth.ACT_BF16),
+                                           (128, 256, 128, 65, 4, synth.ACT_BF16),
+                                           (512, 64, 64, 64, 4, synth.ACT_BF16),
+                                           (16, 96, 128, 300, 2, synth.ACT_FP8_E4M3)])
+def test_moe_layer_equals_route_then_forward(mx, E, H, I, T, k, act):
+    L = synth.layer(seed=E + H, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(T + 3, T, E=E, H=H)
+    Ld = _layer_dev(L)
+    lg, xd = to_dev(logits, torch), to_dev(x, torch)
+    ids, w = mx.mxfp4_route_topk(lg, k)
+    out_a = mx.mxfp4_moe_forward(xd, ids, w, Ld["w13_blocks"], Ld["w13_scales"], Ld["w13_bias"],
+                                 Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"], act)
+    out_b, ids_b, w_b = mx.mxfp4_moe_layer(xd, lg, k, Ld["w13_blocks"], Ld["w13_scales"], Ld["w13_bias"],
+                                           Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"], act)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_b) and torch.equal(w, w_b)
+    assert torch.equal(out_a, out_b)
+    rid, rw = oracle.route_topk(logits, k)
+    assert np.array_equal(ids_b.cpu().numpy(), rid)
+
+
+def test_moe_layer_decode_workload_against_golden(mx, full_layer):
+    name = "moe_decode_t32"
+    wl = synth.workload(name)
+    g = np.load(os.path.join(GOLDEN, "%s.npz" % name))
+    lg, xd = to_dev(wl["logits"], torch), to_dev(wl["x"], torch)
+    Ld = full_layer[1]
+    out, ids, _ = mx.mxfp4_moe_layer(xd, lg, synth.TOPK_GPT_OSS, Ld["w13_blocks"], Ld["w13_scales"],
+                                     Ld["w13_bias"], Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"],
+                                     wl["act_mode"])
+    torch.cuda.synchronize()
+    rid, _ = oracle.route_topk(wl["logits"], synth.TOPK_GPT_OSS)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    got = bf16_dev_to_f64(out)[g["tokens"]]
+    assert_close(got, g["out"].astype(np.float64), name + " via moe_layer")
