@@ -63,10 +63,12 @@ def moe_accounting(ids, T, H, I, act):
                 gemm1_flops=gemm1_flops, flops=flops)
 
 
-def source_digest():
+def source_digest(files):
+    """Digest of the named files under csrc/ (a kernel's source and the headers it
+    includes): counter readings taken on other sources are not reported."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mxfp4_block_scaled_top_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
+    for n in sorted(files):
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + f.read())
     return h.hexdigest()[:16]
@@ -244,7 +246,12 @@ def pmc_traffic(kernel):
     except (OSError, ValueError):
         return None
     ent = d.get(kernel)
-    if not ent or ent.get("source_digest") != source_digest():
+    if not ent or not ent.get("sources"):
+        return None
+    try:
+        if ent.get("source_digest") != source_digest(ent["sources"]):
+            return None
+    except OSError:
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -307,7 +314,7 @@ def main():
         print("bench: quantiser %.1f us" % (others["quantize_lm_head"]["ms"] * 1e3), file=sys.stderr, flush=True)
 
     fp8 = prim["act"] != "bf16"
-    kname = "gemm_fp8_kernel<true, true>" if fp8 else "gemv_stream_kernel<0>"
+    kname = "gemm_fp8_kernel<true, true>" if fp8 else "gemv_persist_kernel<0, 12>"
     if fp8 and prim["tokens"] >= 4096:
         roof = dict(bound="mfma", achieved=prim["gemm1_TFLOPs"], peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=prim["gemm1_TFLOPs"] / FP8_PEAK_TFLOPS)
@@ -336,7 +343,7 @@ def main():
         "roofline": roof,
         "detail": prim,
         "workloads": others,
-        "source_digest": source_digest(),
+        "source_digest": source_digest(os.listdir(os.path.join(ROOT, "mxfp4_block_scaled_top_amd", "csrc"))),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(synth)
