@@ -102,7 +102,9 @@ typedef struct {
   uint64_t chunk_ranks;     /* int32 scratch of the permutation */
   uint64_t tiles;           /* int32 [4 * max_tiles]: (expert, first sorted row, end row, 0);
                                entries past the tile count have expert -1 */
-  uint64_t x_codes;         /* uint8 [T, H] E4M3 codes of x (FP8 mode) */
+  uint64_t x_codes;         /* uint8 [T*k, H] E4M3 codes of x in sorted row order:
+                               row r holds token sorted_pairs[r] / k (FP8 mode;
+                               rows past expert_offsets[E] unused) */
   uint64_t h;               /* BF16 mode: bf16 hi [T*k, I] then bf16 lo [T*k, I]
                                with h = hi + lo; FP8 mode: fp32 [T*k, I];
                                rows in sorted order */

@@ -84,7 +84,7 @@ void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mod
   L->chunk_ranks = o; o = up(o + (size_t)np * 4);
   L->tiles = o; o = up(o + (size_t)mx::max_tiles(np, E, bm) * mx::kTileInts * 4);
   if (act_mode == MXFP4_ACT_FP8_E4M3) {
-    L->x_codes = o; o = up(o + (size_t)T * H);
+    L->x_codes = o; o = up(o + (size_t)np * H);
     L->h = o; o = up(o + (size_t)np * I * 4);
     L->h_codes = o; o = up(o + (size_t)np * I);
   } else {
@@ -233,10 +233,10 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   MX_STEP(mx::launch_permute(topk_ids, (int)npairs, E, bm, (int)bound, ws, s), "permute launch");
   MX_STEP(mark(MXFP4_STAGE_PERMUTE), "event record");
   if (fp8) {
-    MX_STEP(mx::launch_quant_fp8(x, true, T * H, ws.x_codes,
-                                 reinterpret_cast<uint32_t*>(ws.status + mx::kStAmaxX),
-                                 reinterpret_cast<float*>(ws.status + mx::kStScaleX), s),
-            "quant x launch");
+    // per-tensor scale over all of x, codes written in expert-sorted row order
+    MX_STEP(mx::launch_amax(x, true, T * H, reinterpret_cast<uint32_t*>(ws.status + mx::kStAmaxX), s),
+            "amax x launch");
+    MX_STEP(mx::launch_encode_sorted_rows(x, sh, ws, s), "quant x launch");
   }
   MX_STEP(mark(MXFP4_STAGE_QUANT_X), "event record");
   if (fp8) MX_STEP(mx::launch_moe_gateup_fp8(sh, w, ws, bound, s), "gate_up launch");

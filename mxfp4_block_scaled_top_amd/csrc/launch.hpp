@@ -9,7 +9,7 @@ namespace mx {
 
 constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to here
 constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
-constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 path
+constexpr int kPrefillBM = 64;               // sorted rows per tile, FP8 path
 // A row tile is 4 ints: expert, first sorted row, end row (exclusive), 0.
 // Entries past the number of tiles (up to max_tiles) hold expert -1.
 constexpr int kTileInts = 4;
@@ -61,6 +61,10 @@ hipError_t launch_amax(const void* in, bool in_bf16, int64_t n, uint32_t* amax_b
                        hipStream_t s);
 hipError_t launch_encode_fp8(const void* in, bool in_bf16, int64_t n, uint8_t* codes,
                              const uint32_t* amax_bits, float* scale_out, hipStream_t s);
+// x codes in expert-sorted row order ([T*k, H], rows up to offsets[E]),
+// scale from status[kStAmaxX] into status[kStScaleX].
+hipError_t launch_encode_sorted_rows(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
+                                     hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t s);
 
 // bf16-activation path (MFMA bf16 with weights expanded from FP4 in registers).

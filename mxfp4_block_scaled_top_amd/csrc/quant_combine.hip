@@ -92,6 +92,36 @@ __global__ __launch_bounds__(256) void encode_kernel(const void* __restrict__ in
       codes[i] = (uint8_t)e4m3_encode(load1<BF16>(in, i) / s);
 }
 
+// Codes of the activation rows in expert-sorted order (the layout both
+// prefill GEMMs read): sorted row r holds the codes of token
+// sorted_pairs[r] / k.  Rows past the number of routed pairs (offsets[E]) are
+// not written.  16 elements per thread.
+__global__ __launch_bounds__(256) void encode_sorted_rows_kernel(
+    const uint16_t* __restrict__ x, int H, int k, const int* __restrict__ sorted_pairs,
+    const int* __restrict__ offsets, int E, uint8_t* __restrict__ codes,
+    const uint32_t* __restrict__ amax_bits, float* __restrict__ scale_out) {
+  const float s = scale_from_amax(*amax_bits);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
+  const int per_row = H / 16;
+  const int64_t n = (int64_t)offsets[E] * per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t r = i / per_row;
+    const int c = (int)(i - r * per_row) * 16;
+    const int64_t t = sorted_pairs[r] / k;
+    float v[16];
+    load8<true>(x, t * H + c, v);
+    load8<true>(x, t * H + c + 8, v + 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[q] = e4m3_encode(v[4 * q] / s) | (e4m3_encode(v[4 * q + 1] / s) << 8) |
+             (e4m3_encode(v[4 * q + 2] / s) << 16) | (e4m3_encode(v[4 * q + 3] / s) << 24);
+    }
+    *reinterpret_cast<uint4*>(codes + r * H + c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -122,6 +152,17 @@ hipError_t launch_encode_fp8(const void* in, bool in_bf16, int64_t n, uint8_t* c
   const int grid = grid_for(n / 16);
   if (in_bf16) encode_kernel<true><<<grid, 256, 0, s>>>(in, n, codes, amax_bits, scale_out);
   else encode_kernel<false><<<grid, 256, 0, s>>>(in, n, codes, amax_bits, scale_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_sorted_rows(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
+                                    hipStream_t s) {
+  const int64_t npairs = (int64_t)sh.T * sh.k;
+  const int grid = grid_for(npairs * (sh.H / 16));
+  encode_sorted_rows_kernel<<<grid, 256, 0, s>>>(
+      x, sh.H, sh.k, ws.sorted_pairs, ws.offsets, sh.E, ws.x_codes,
+      reinterpret_cast<const uint32_t*>(ws.status + kStAmaxX),
+      reinterpret_cast<float*>(ws.status + kStScaleX));
   return hipGetLastError();
 }
 

@@ -77,6 +77,7 @@ def test_layout_offsets_are_ordered_and_aligned(L):
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs) and lay.total_bytes > lay.y
     assert lay.y - lay.h >= 8192 * 4 * 2880 * 5          # fp32 h + u8 codes
+    assert lay.h - lay.x_codes >= 8192 * 4 * 2880        # x codes per routed pair (sorted rows)
 
 
 def _fake(n=1):
