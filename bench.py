@@ -314,7 +314,7 @@ def main():
         print("bench: quantiser %.1f us" % (others["quantize_lm_head"]["ms"] * 1e3), file=sys.stderr, flush=True)
 
     fp8 = prim["act"] != "bf16"
-    kname = "gemm_fp8_kernel<true, true>" if fp8 else "gemv_persist_kernel<0, 12>"
+    kname = "prefill_gemm_kernel<true, 128>" if fp8 else "gemv_persist_kernel<0, 12>"
     if fp8 and prim["tokens"] >= 4096:
         roof = dict(bound="mfma", achieved=prim["gemm1_TFLOPs"], peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=prim["gemm1_TFLOPs"] / FP8_PEAK_TFLOPS)

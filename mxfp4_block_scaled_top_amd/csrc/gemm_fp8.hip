@@ -25,30 +25,31 @@
 //     permutation builds) times one n-tile of 256 weight rows (gate_up: 128
 //     gate rows and the matching 128 up rows).  Block b takes units b, b + G,
 //     b + 2G, ...; a unit is nsteps K steps of 128.
-//   * Four loader waves copy every K step's activations (BM x 128 B of E4M3
-//     codes, rows in expert-sorted order), weights (256 x 64 B of E2M1) and
-//     E8M0 scales from global memory into one slot of an LDS ring by DMA
-//     (global -> LDS), and run STAGES-1 steps ahead of the compute waves.
-//     The DMA issue rate is a per-wave limit (measured: about 12.5 GB/s per
-//     wave whether the data comes from L2 or HBM, scaling with the number of
-//     issuing waves), so the copies are spread over four waves.
-//     Each loader issues the same number of DMA instructions every step, so
-//     it waits for exactly the slot the next step needs with an explicit
-//     vector-memory count.  The loaders read the tile list through the scalar
-//     cache, so no other vector-memory operation enters those counts.
-//   * The compute waves issue no vector-memory loads in the K loop, so the
-//     counter wait the compiler places before LDS reads that may alias a DMA
-//     never stalls them.
+//   * Every K step's activations (BM x 128 B of E4M3 codes, rows in
+//     expert-sorted order), weights (256 x 64 B of E2M1) and E8M0 scales are
+//     copied from global memory into one slot of an LDS ring by DMA (global ->
+//     LDS), STAGES-1 steps ahead of their use.  All waves of the block share
+//     the copies: the DMA issue rate is a per-wave limit (measured: about
+//     12.5 GB/s per wave whether the data comes from L2 or HBM, scaling with
+//     the number of issuing waves).  Each wave issues the same number of DMA
+//     instructions every step, so before the step's barrier it waits for
+//     exactly its part of the slot that step needs, with an explicit
+//     vector-memory count.
+//   * The compute reads of the ring are inline-assembly LDS loads with their
+//     own lgkmcnt wait.  The compiler does not track which ring slot a DMA
+//     writes and would otherwise wait for every DMA in flight before any LDS
+//     read, which serialises the ring.  Tile-list entries and biases come
+//     through the scalar cache, so no other load enters the vector-memory
+//     counts.
 //   * One barrier per K step: after it the slot of step t has landed and the
-//     slot of step t-1 is free; the loaders then refill it with step
-//     t+STAGES-1.
-//   * BM/16 compute waves, each 64 sorted rows x 64 weight rows (4 x 4 MFMA
-//     tiles of 16 x 16).
+//     slot of step t-1 is free to be refilled with step t+STAGES-1.
+//   * BM/16 waves (two per SIMD at BM = 128), each 64 sorted rows x 64 weight
+//     rows (4 x 4 MFMA tiles of 16 x 16).
 //   * LDS layouts are XOR-swizzled at 16-byte granularity, chosen through
 //     each lane's DMA source address, so that the MFMA-layout reads of a
 //     group of 8 lanes hit distinct banks.
 //   * K tails: chunks past K are loaded from a valid address and the weight
-//     operand of MX blocks past K is forced to zero in the compute waves.
+//     operand of MX blocks past K is forced to zero.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -61,21 +62,20 @@ constexpr int kScTile = kBN * 8;       // two aligned scale dwords per weight ro
 
 template <int BM>
 struct Ring {
-  static constexpr int kCompute = BM / 16;              // compute waves
-  static constexpr int kLoaders = 4;                    // DMA issue rate is per wave
-  static constexpr int kThreads = 64 * (kCompute + kLoaders);
-  static constexpr int kStages = BM == 128 ? 4 : 5;
+  static constexpr int kWaves = BM / 16;                // each 64 sorted rows x 64 weight rows
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kStages = BM == 128 ? 4 : 6;
   static constexpr int kAct = BM * kBK;                 // activation bytes per slot
   static constexpr int kW = kAct;                       // offsets inside a slot
   static constexpr int kSc = kAct + kWTile;
   static constexpr int kSlot = kSc + kScTile;
-  static constexpr int kActDma = BM / 8 / kLoaders;     // 1 KB activation DMAs per loader per step
-  static constexpr int kWDma = 16 / kLoaders;           // 1 KB weight DMAs per loader per step
-  static constexpr int kScDma = 8 / kLoaders;           // 256 B scale DMAs per loader per step
-  static constexpr int kDma = kActDma + kWDma + kScDma; // DMA instructions per loader per step
-  static_assert(kActDma * kLoaders * 8 == BM, "activation rows split over the loaders");
-  static_assert(3 * kDma <= 63, "vector-memory count range");
-  static_assert(kStages - 2 <= 3, "waits cover up to three steps ahead");
+  static constexpr int kActDma = BM / 8 / kWaves;       // 1 KB activation DMAs per wave per step
+  static constexpr int kWDma = 16 / kWaves;             // 1 KB weight DMAs per wave per step
+  static constexpr int kScDma = 8 / kWaves;             // 256 B scale DMAs per wave per step
+  static constexpr int kDma = kActDma + kWDma + kScDma; // DMA instructions per wave per step
+  static_assert(kActDma * kWaves * 8 == BM && kScDma >= 1, "copies split over the waves");
+  static_assert((kStages - 2) * kDma <= 63, "vector-memory count range");
+  static_assert(kStages - 2 <= 4, "waits cover up to four steps ahead");
   static_assert(kStages * kSlot <= 160 * 1024, "LDS");
 };
 
@@ -139,159 +139,220 @@ __device__ __forceinline__ int weight_row(int lr, int nt, int nout) {
   return min(nt * kBN + lr, nout - 1);
 }
 
-template <bool GATEUP, int BM>
-__device__ __forceinline__ void prefill_loader(const PrefillArgs& a, const int* __restrict__ tiles,
-                                               uint8_t* smem, int l, int lane, int total, int u0,
-                                               int G) {
-  using C = Ring<BM>;
-  constexpr int NL = C::kLoaders;
-  // Per-lane parts fixed for the whole kernel.  Activation DMA i of loader l
-  // fills slot rows 8j..8j+7 (j = NL*i + l): lane -> row 8j + lane/8, 16-byte
-  // slot lane%8, which holds logical chunk (lane%8) ^ (row%8).
-  const int a_row = lane >> 3;
-  const int a_chunk = (lane & 7) ^ a_row;
-  // Weight DMA i fills rows 16j..16j+15: lane -> row 16j + lane/4, slot
-  // lane%4, which holds MX block (lane%4) ^ ((row/2)%4).
-  const int w_row = lane >> 2;
-  const int w_blk = (lane & 3) ^ ((lane >> 3) & 3);
-  // Scale DMA i fills rows 32j..32j+31: lane -> row 32j + lane/2, aligned
-  // dword lane%2 of the 8 bytes that hold the row's four scales of the step.
-  const int s_row = lane >> 1;
-  const int s_dw = lane & 1;
-  const int my_units = total / a.nsteps;
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
 
+// bf16 numbers 4g .. 4g+3 of the 16 at p (wave-uniform, 4-byte aligned), for
+// the lane's g (0..3), as two dwords: one scalar load, then a select chain
+// on g
+__device__ __forceinline__ uint2 bias_quad(const uint16_t* p, int g) {
+  v8i_t v;
+  asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  const uint32_t lo = (uint32_t)(g == 0 ? v[0] : g == 1 ? v[2] : g == 2 ? v[4] : v[6]);
+  const uint32_t hi = (uint32_t)(g == 0 ? v[1] : g == 1 ? v[3] : g == 2 ? v[5] : v[7]);
+  return make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ float bf16_of(uint2 q, int jj) {
+  const uint32_t w = jj < 2 ? q.x : q.y;
+  return bf16_bits_to_f32(jj & 1 ? w >> 16 : w & 0xffffu);
+}
+
+// A wave's share of the copies of every K step (global -> LDS DMA).
+// Activation DMA i fills slot rows 8j..8j+7 (j = NW*i + wave): lane -> row
+// 8j + lane/8, 16-byte slot lane%8, which holds logical chunk
+// (lane%8) ^ (row%8).  Weight DMA i fills rows 16j..16j+15: lane -> row
+// 16j + lane/4, slot lane%4, which holds MX block (lane%4) ^ ((row/2)%4).
+// Scale DMA i fills rows 32j..32j+31: lane -> row 32j + lane/2, aligned dword
+// lane%2 of the 8 bytes that hold the row's four scales of the step.
+template <bool GATEUP, int BM>
+struct PrefillCopier {
+  using C = Ring<BM>;
+  static constexpr int NW = C::kWaves;
+  const int* tiles;
+  uint8_t* smem;
+  int wave, u0, G, my_units;
+  int a_chunk, a_row, w_row, w_blk, s_row, s_dw;
   const uint8_t* aptr[C::kActDma];
   const uint8_t* wptr[C::kWDma];
   int64_t sofs[C::kScDma];
+  int k, step, slot;    // next copy: local unit, step, ring slot
 
-  auto setup = [&](int u) __attribute__((always_inline)) {
+  __device__ __forceinline__ void init(const PrefillArgs& a, const int* t, uint8_t* sm, int w, int lane, int first,
+                                       int grid, int units) {
+    tiles = t; smem = sm; wave = w; u0 = first; G = grid; my_units = units;
+    a_row = lane >> 3;
+    a_chunk = (lane & 7) ^ a_row;
+    w_row = lane >> 2;
+    w_blk = (lane & 3) ^ ((lane >> 3) & 3);
+    s_row = lane >> 1;
+    s_dw = lane & 1;
+    k = 0; step = 0; slot = 0;
+    setup(a, u0);
+  }
+
+  __device__ __forceinline__ void setup(const PrefillArgs& a, int u) {
     const int tile = u / a.NT;
     const int nt = u - tile * a.NT;
     const int3 te = tile_entry(tiles + kTileInts * tile);
 #pragma unroll
     for (int i = 0; i < C::kActDma; ++i) {
-      int row = te.y + 8 * (NL * i + l) + a_row;
+      int row = te.y + 8 * (NW * i + wave) + a_row;
       row = row < te.z ? row : te.y;
       aptr[i] = a.act + (int64_t)row * a.K;
     }
     const int64_t ebase = (int64_t)te.x * a.R;
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
-      const int wr = weight_row<GATEUP>(16 * (NL * i + l) + w_row, nt, a.nout);
+      const int wr = weight_row<GATEUP>(16 * (NW * i + wave) + w_row, nt, a.nout);
       wptr[i] = a.wb + (ebase + wr) * a.nb * kBlockBytes;
     }
 #pragma unroll
     for (int i = 0; i < C::kScDma; ++i) {
-      const int wr = weight_row<GATEUP>(32 * (NL * i + l) + s_row, nt, a.nout);
+      const int wr = weight_row<GATEUP>(32 * (NW * i + wave) + s_row, nt, a.nout);
       sofs[i] = (ebase + wr) * a.nb;
     }
-  };
+  }
 
-  int k = 0, step = 0, slot = 0;   // local unit index, step and ring slot of the next issue
-  auto issue = [&]() __attribute__((always_inline)) {
+  // copies of the next step into its slot, then advance
+  __device__ __forceinline__ void issue(const PrefillArgs& a) {
     uint8_t* dst = smem + slot * C::kSlot;
     const bool tail = step == a.nsteps - 1;
     const int kb = step * kBK;
 #pragma unroll
     for (int i = 0; i < C::kActDma; ++i) {
       const int off = kb + 16 * a_chunk;           // past K: the row's first 16 bytes
-      __builtin_amdgcn_global_load_lds(aptr[i] + (!tail || off < a.K ? off : 0), dst + 1024 * (NL * i + l),
+      __builtin_amdgcn_global_load_lds(aptr[i] + (!tail || off < a.K ? off : 0), dst + 1024 * (NW * i + wave),
                                        16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
       const int blk = 4 * step + w_blk;            // past K: the row's first block
       __builtin_amdgcn_global_load_lds(wptr[i] + (!tail || blk < a.nb ? blk * kBlockBytes : 0),
-                                       dst + C::kW + 1024 * (NL * i + l), 16, 0, 0);
+                                       dst + C::kW + 1024 * (NW * i + wave), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::kScDma; ++i) {
       int64_t q = ((sofs[i] + 4 * step) & ~(int64_t)3) + 4 * s_dw;
       q = q < a.sc_total - 4 ? q : a.sc_total - 4;
-      __builtin_amdgcn_global_load_lds(a.ws + q, dst + C::kSc + 256 * (NL * i + l), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.ws + q, dst + C::kSc + 256 * (NW * i + wave), 4, 0, 0);
     }
     slot = slot + 1 == C::kStages ? 0 : slot + 1;
     if (++step == a.nsteps) {
       step = 0;
-      if (++k < my_units) setup(u0 + k * G);
+      if (++k < my_units) setup(a, u0 + k * G);
     }
-  };
+  }
+};
 
-  setup(u0);
-  const int pro = total < C::kStages - 1 ? total : C::kStages - 1;
-  for (int p = 0; p < pro; ++p) issue();
-  for (int t = 0; t < total; ++t) {
-    // steps issued beyond t: min(STAGES - 2, total - 1 - t); wait for the rest
-    int ahead = total - 1 - t;
-    ahead = ahead < C::kStages - 2 ? ahead : C::kStages - 2;
-    if (ahead >= 3) wait_vm<3 * C::kDma>();
-    else if (ahead == 2) wait_vm<2 * C::kDma>();
-    else if (ahead == 1) wait_vm<C::kDma>();
-    else wait_vm<0>();
-    asm volatile("s_barrier" ::: "memory");
-    if (t + C::kStages - 1 < total) issue();
+// One K step's operands of a wave from its LDS slot: 8 activation reads
+// (two chunks of 4 token-row groups, 2 KB apart), 4 weight reads and 4 scale
+// bytes (gate_up: weight groups at LDS rows +0, +16, +128, +144; down: +0,
+// +16, +32, +48), issued and waited for in one assembly block so that no
+// compiler-generated code sees the registers while the loads are in flight.
+#define MX_RD_ACT                                                                    \
+  "ds_read_b128 %0, %16\n\tds_read_b128 %4, %17\n\t"                               \
+  "ds_read_b128 %1, %16 offset:2048\n\tds_read_b128 %5, %17 offset:2048\n\t"       \
+  "ds_read_b128 %2, %16 offset:4096\n\tds_read_b128 %6, %17 offset:4096\n\t"       \
+  "ds_read_b128 %3, %16 offset:6144\n\tds_read_b128 %7, %17 offset:6144\n\t"
+#define MX_RD_OUTS                                                                   \
+  "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(xb0), "=&v"(xb1), "=&v"(xb2), "=&v"(xb3), \
+      "=&v"(wq0), "=&v"(wq1), "=&v"(wq2), "=&v"(wq3), "=&v"(sb0), "=&v"(sb1), "=&v"(sb2), "=&v"(sb3)
+template <bool GATEUP>
+__device__ __forceinline__ void lds_step_reads(uint32_t aa0, uint32_t aa1, uint32_t ww, uint32_t ss,
+                                               v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3,
+                                               v4u_t& xb0, v4u_t& xb1, v4u_t& xb2, v4u_t& xb3,
+                                               v4u_t& wq0, v4u_t& wq1, v4u_t& wq2, v4u_t& wq3,
+                                               uint32_t& sb0, uint32_t& sb1, uint32_t& sb2, uint32_t& sb3) {
+  if (GATEUP) {
+    asm volatile(MX_RD_ACT
+                 "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
+                 "ds_read_b128 %10, %18 offset:8192\n\tds_read_b128 %11, %18 offset:9216\n\t"
+                 "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:128\n\t"
+                 "ds_read_u8 %14, %19 offset:1024\n\tds_read_u8 %15, %19 offset:1152\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_RD_OUTS
+                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
+  } else {
+    asm volatile(MX_RD_ACT
+                 "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
+                 "ds_read_b128 %10, %18 offset:2048\n\tds_read_b128 %11, %18 offset:3072\n\t"
+                 "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:128\n\t"
+                 "ds_read_u8 %14, %19 offset:256\n\tds_read_u8 %15, %19 offset:384\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_RD_OUTS
+                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
   }
 }
+#undef MX_RD_ACT
+#undef MX_RD_OUTS
 
 template <bool GATEUP, int BM>
 __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(PrefillArgs a,
                                                                           const int* __restrict__ tiles,
                                                                           int* status) {
   using C = Ring<BM>;
+  constexpr int NW = C::kWaves;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kSlot];
   const int num_units = status[kStNumTiles] * a.NT;
   const float sx = __uint_as_float((uint32_t)status[a.scale_word]);
   const int G = gridDim.x;
   const int u0 = blockIdx.x;
   if (u0 >= num_units) return;
-  const int total = ((num_units - 1 - u0) / G + 1) * a.nsteps;
+  const int my_units = (num_units - 1 - u0) / G + 1;
+  const int total = my_units * a.nsteps;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (wave >= C::kCompute) {
-    prefill_loader<GATEUP, BM>(a, tiles, smem, wave - C::kCompute, lane, total, u0, G);
-    return;
-  }
 
+  PrefillCopier<GATEUP, BM> cp;
+  cp.init(a, tiles, smem, wave, lane, u0, G, my_units);
+
+  // ---------------- compute: 64 sorted rows x 64 weight rows ----------------
   const int wm = wave >> 2, wn = wave & 3;
   const int r = lane & 15, g = lane >> 4;
-  // LDS weight rows of this lane in the wave's four 16-row groups (gate_up:
-  // groups 0, 1 gate rows, 2, 3 the matching up rows)
-  int lrow[4];
-#pragma unroll
-  for (int rg = 0; rg < 4; ++rg)
-    lrow[rg] = (GATEUP ? (rg >> 1) * (kBN / 2) + 32 * wn + 16 * (rg & 1) : 64 * wn + 16 * rg) + r;
-  const int wslot = g ^ ((r >> 1) & 3);    // slot of MX block g in these rows
+  // LDS weight row of this lane in the wave's first 16-row group; the others
+  // follow at fixed offsets (gate_up: groups 0, 1 gate rows, 2, 3 the
+  // matching up rows)
+  const int lrow0 = (GATEUP ? 32 * wn : 64 * wn) + r;
+  const int wslot = g ^ ((r >> 1) & 3);             // slot of MX block g in these rows
   // activation chunks: the bf16 path takes K [32g, 32g+32) = chunks 2g, 2g+1,
   // the block-scaled path chunks g and 4+g; the row's swizzle is row%8 = r%8
   const int c0 = (GATEUP ? 2 * g : g) ^ (r & 7);
   const int c1 = (GATEUP ? 2 * g + 1 : 4 + g) ^ (r & 7);
+  // byte of this lane's row in its 8 scale bytes: the row's first scale
+  // byte is at (e*R + row)*nb, and e*R and the weight-row offsets of the four
+  // groups are multiples of 4, so the phase is that of r*nb
+  const int sphase = (r * a.nb) & 3;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t a0 = lds0 + (64 * wm + r) * kBK + 16 * c0;
+  const uint32_t a1 = lds0 + (64 * wm + r) * kBK + 16 * c1;
+  const uint32_t w0 = lds0 + C::kW + lrow0 * 64 + 16 * wslot;
+  const uint32_t s0 = lds0 + C::kSc + lrow0 * 8 + sphase + g;
 
-  int unit = u0, step = 0, slot = 0;
+  int cstep = 0, cslot = 0, ck = 0;
   int e = 0, rb = 0, re = 0, nt = 0;
-  int sphase[4];
   // bias of the lane's four output rows of each epilogue group, as bf16
-  // pairs; loaded when a unit starts so that its epilogue does not wait on
-  // memory (gate_up: gate and up rows of groups 0 and 1; down: groups 0..3)
+  // pairs (gate_up: gate and up rows of groups 0 and 1; down: groups 0..3)
   uint2 bq[4];
-  auto setup = [&](int u) __attribute__((always_inline)) {
+  auto comp_setup = [&](int u) __attribute__((always_inline)) {
     const int tile = u / a.NT;
     nt = u - tile * a.NT;
-    const int4 te = *reinterpret_cast<const int4*>(tiles + kTileInts * tile);
+    const int3 te = tile_entry(tiles + kTileInts * tile);
     e = te.x; rb = te.y; re = te.z;
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int wr = weight_row<GATEUP>(lrow[rg], nt, a.nout);
-      sphase[rg] = (int)((((int64_t)e * a.R + wr) * a.nb) & 3);
-    }
+    // through the scalar cache, 16 rows at a time (a group past nout is
+    // never stored and not loaded)
     const uint16_t* bias_e = a.bias + (size_t)e * a.R;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n0 = GATEUP ? nt * (kBN / 2) + 32 * wn + 16 * (j >> 1) : nt * kBN + 64 * wn + 16 * j;
-      const int off = (GATEUP && (j & 1) ? a.nout : 0) + n0 + 4 * g;
-      bq[j] = a.bias && n0 < a.nout ? *reinterpret_cast<const uint2*>(bias_e + off) : make_uint2(0, 0);
+      const int off = (GATEUP && (j & 1) ? a.nout : 0) + n0;
+      bq[j] = a.bias && n0 < a.nout ? bias_quad(bias_e + off, g) : make_uint2(0u, 0u);
     }
   };
-  setup(unit);
+
+  comp_setup(u0);
+  const int pro = total < C::kStages - 1 ? total : C::kStages - 1;
+  for (int p = 0; p < pro; ++p) cp.issue(a);
 
   v4f acc[4][4];
 #pragma unroll
@@ -300,25 +361,33 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
     for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = {0.f, 0.f, 0.f, 0.f};
 
   for (int t = 0; t < total; ++t) {
-    // slot of step t landed; everyone is done with step t-1's slot
+    // this wave's copies of step t have landed (steps issued beyond t:
+    // min(STAGES - 2, total - 1 - t)); after the barrier everybody's have,
+    // and everybody is done reading step t-1's slot
+    int ahead = total - 1 - t;
+    ahead = ahead < C::kStages - 2 ? ahead : C::kStages - 2;
+    if (ahead >= 4) wait_vm<4 * C::kDma>();
+    else if (ahead == 3) wait_vm<3 * C::kDma>();
+    else if (ahead == 2) wait_vm<2 * C::kDma>();
+    else if (ahead == 1) wait_vm<C::kDma>();
+    else wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const uint8_t* base = smem + slot * C::kSlot;
-    const bool valid = 4 * step + g < a.nb;    // this lane's MX block lies inside K
-    uint4 wq[4];
-    uint32_t sb[4];
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      wq[rg] = *reinterpret_cast<const uint4*>(base + C::kW + lrow[rg] * 64 + 16 * wslot);
-      sb[rg] = base[C::kSc + lrow[rg] * 8 + sphase[rg] + g];
-    }
+
+    // refill the slot freed by the barrier
+    if (t + C::kStages - 1 < total) cp.issue(a);
+    // step t's operands
+    const uint32_t so = (uint32_t)(cslot * C::kSlot);
+    const uint32_t aa0 = a0 + so, aa1 = a1 + so, ww = w0 + so, ss = s0 + so;
+    v4u_t xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3;
+    uint32_t sb0, sb1, sb2, sb3;
+    lds_step_reads<GATEUP>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3,
+                           sb0, sb1, sb2, sb3);
+    const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
+    const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
+    const v4u_t wq[4] = {wq0, wq1, wq2, wq3};
+    const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
+    const bool valid = 4 * cstep + g < a.nb;        // this lane's MX block lies inside K
     if (GATEUP) {
-      uint4 xa[4], xb[4];
-#pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
-        const uint8_t* p = base + (64 * wm + 16 * tg + r) * kBK;
-        xa[tg] = *reinterpret_cast<const uint4*>(p + 16 * c0);
-        xb[tg] = *reinterpret_cast<const uint4*>(p + 16 * c1);
-      }
       // lane group g holds K [32g, 32g+32) of the step (its own MX block);
       // MFMA q takes elements 8q..8q+7 of it, in the same order for both
       // operands
@@ -327,41 +396,35 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
         v8bf B[4];
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-          const uint4 c = q < 2 ? xa[tg] : xb[tg];
+          const v4u_t c = q < 2 ? xa[tg] : xb[tg];
           B[tg] = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
         }
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
-          const uint32_t wv = q == 0 ? wq[rg].x : q == 1 ? wq[rg].y : q == 2 ? wq[rg].z : wq[rg].w;
-          const v8bf A = fp4x8_to_bf16(wv, f);
+          const v8bf A = fp4x8_to_bf16(wq[rg][q], f);
 #pragma unroll
           for (int tg = 0; tg < 4; ++tg)
             acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[tg], acc[rg][tg], 0, 0, 0);
         }
       }
     } else {
-      typedef int v4i_t __attribute__((ext_vector_type(4)));
       v8i B[4];
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
-        const uint8_t* p = base + (64 * wm + 16 * tg + r) * kBK;
-        const v4i_t lo = *reinterpret_cast<const v4i_t*>(p + 16 * c0);
-        const v4i_t hi = *reinterpret_cast<const v4i_t*>(p + 16 * c1);
-        B[tg] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      for (int tg = 0; tg < 4; ++tg)
+        B[tg] = __builtin_bit_cast(v8i, __builtin_shufflevector(xa[tg], xb[tg], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const v8i A = valid ? v8i{(int)wq[rg].x, (int)wq[rg].y, (int)wq[rg].z, (int)wq[rg].w, 0, 0, 0, 0}
-                            : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
+        const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg)
           acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 0, 0,
                                                                          (int)sb[rg], 0, 127);
       }
     }
-    slot = slot + 1 == C::kStages ? 0 : slot + 1;
-    if (++step < a.nsteps) continue;
+    cslot = cslot + 1 == C::kStages ? 0 : cslot + 1;
+    if (++cstep < a.nsteps) continue;
 
     // ---- epilogue of the unit: the lane holds rows 4g + jj of each 16-row
     // weight group and sorted row r of each 16-row token group
@@ -378,10 +441,8 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
           float hv[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const uint2 bg = bq[2 * half], bu = bq[2 * half + 1];
-            const uint32_t wg = jj < 2 ? bg.x : bg.y, wu = jj < 2 ? bu.x : bu.y;
-            const float gate = acc[half][tg][jj] * sx + bf16_bits_to_f32(jj & 1 ? wg >> 16 : wg & 0xffffu);
-            const float up = acc[half + 2][tg][jj] * sx + bf16_bits_to_f32(jj & 1 ? wu >> 16 : wu & 0xffffu);
+            const float gate = acc[half][tg][jj] * sx + bf16_of(bq[2 * half], jj);
+            const float up = acc[half + 2][tg][jj] * sx + bf16_of(bq[2 * half + 1], jj);
             hv[jj] = silu_accurate(gate) * up;
             amax = fmaxf(amax, fabsf(hv[jj]));
           }
@@ -402,10 +463,7 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
           if (row >= re) continue;
           float v[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t wb = jj < 2 ? bq[rg].x : bq[rg].y;
-            v[jj] = acc[rg][tg][jj] * sx + bf16_bits_to_f32(jj & 1 ? wb >> 16 : wb & 0xffffu);
-          }
+          for (int jj = 0; jj < 4; ++jj) v[jj] = acc[rg][tg][jj] * sx + bf16_of(bq[rg], jj);
           *reinterpret_cast<float4*>(a.out + (size_t)row * a.nout + n0 + 4 * g) =
               make_float4(v[0], v[1], v[2], v[3]);
         }
@@ -415,9 +473,8 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
     for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
       for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = {0.f, 0.f, 0.f, 0.f};
-    step = 0;
-    unit += G;
-    if (t + 1 < total) setup(unit);
+    cstep = 0;
+    if (++ck < my_units) comp_setup(u0 + ck * G);
   }
 }
 

@@ -9,7 +9,7 @@ namespace mx {
 
 constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to here
 constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
-constexpr int kPrefillBM = 64;               // sorted rows per tile, FP8 path
+constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 path
 // A row tile is 4 ints: expert, first sorted row, end row (exclusive), 0.
 // Entries past the number of tiles (up to max_tiles) hold expert -1.
 constexpr int kTileInts = 4;

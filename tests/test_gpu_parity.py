@@ -145,7 +145,7 @@ def test_permutation_bit_exact(mx, T, E, k, hot):
         assert np.array_equal(_ws_view(ws, lay, "expert_offsets", np.int32, E + 1), offsets)
         assert np.array_equal(_ws_view(ws, lay, "sorted_pairs", np.int32, np_), sp)
         assert np.array_equal(_ws_view(ws, lay, "inv_pairs", np.int32, np_), inv)
-        bm = 4 if act == synth.ACT_BF16 else 64
+        bm = 4 if act == synth.ACT_BF16 else 128
         assert _status(ws, lay)[5] == int(np.sum((counts + bm - 1) // bm))
         assert _status(ws, lay)[0] == 0
         # row-tile list: (expert, first row, end row, 0) per BM rows of each expert in
