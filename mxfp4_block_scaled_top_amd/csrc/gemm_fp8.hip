@@ -359,6 +359,7 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
   for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = {0.f, 0.f, 0.f, 0.f};
+  float amax = 0.0f;     // gate_up: max |h| of the lane's outputs
 
   for (int t = 0; t < total; ++t) {
     // this wave's copies of step t have landed (steps issued beyond t:
@@ -429,7 +430,6 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
     // ---- epilogue of the unit: the lane holds rows 4g + jj of each 16-row
     // weight group and sorted row r of each 16-row token group
     if (GATEUP) {
-      float amax = 0.0f;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int i0 = nt * (kBN / 2) + 32 * wn + 16 * half;
@@ -450,8 +450,6 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
               make_float4(hv[0], hv[1], hv[2], hv[3]);
         }
       }
-      amax = wave_max(amax);
-      if (lane == 0) atomicMax(reinterpret_cast<uint32_t*>(&status[kStAmaxH]), __float_as_uint(amax));
     } else {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
@@ -475,6 +473,11 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
       for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = {0.f, 0.f, 0.f, 0.f};
     cstep = 0;
     if (++ck < my_units) comp_setup(u0 + ck * G);
+  }
+  if (GATEUP) {
+    // max |h| over all of this wave's units: one atomic per wave
+    amax = wave_max(amax);
+    if (lane == 0) atomicMax(reinterpret_cast<uint32_t*>(&status[kStAmaxH]), __float_as_uint(amax));
   }
 }
 

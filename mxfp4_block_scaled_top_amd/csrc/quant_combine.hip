@@ -93,22 +93,17 @@ __global__ __launch_bounds__(256) void encode_kernel(const void* __restrict__ in
 }
 
 // Codes of the activation rows in expert-sorted order (the layout both
-// prefill GEMMs read): sorted row r holds the codes of token
-// sorted_pairs[r] / k.  Rows past the number of routed pairs (offsets[E]) are
-// not written.  16 elements per thread.
+// prefill GEMMs read): sorted row inv[t*k + j] holds the codes of token t.
+// One block per token: each thread encodes 16 elements once and writes them
+// to the token's k sorted rows (pairs whose expert id was skipped have no
+// row, inv < 0).
 __global__ __launch_bounds__(256) void encode_sorted_rows_kernel(
-    const uint16_t* __restrict__ x, int H, int k, const int* __restrict__ sorted_pairs,
-    const int* __restrict__ offsets, int E, uint8_t* __restrict__ codes,
-    const uint32_t* __restrict__ amax_bits, float* __restrict__ scale_out) {
+    const uint16_t* __restrict__ x, int H, int k, const int* __restrict__ inv,
+    uint8_t* __restrict__ codes, const uint32_t* __restrict__ amax_bits, float* __restrict__ scale_out) {
   const float s = scale_from_amax(*amax_bits);
   if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
-  const int per_row = H / 16;
-  const int64_t n = (int64_t)offsets[E] * per_row;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const int64_t r = i / per_row;
-    const int c = (int)(i - r * per_row) * 16;
-    const int64_t t = sorted_pairs[r] / k;
+  const int64_t t = blockIdx.x;
+  for (int c = (int)threadIdx.x * 16; c < H; c += (int)blockDim.x * 16) {
     float v[16];
     load8<true>(x, t * H + c, v);
     load8<true>(x, t * H + c + 8, v + 8);
@@ -118,7 +113,11 @@ __global__ __launch_bounds__(256) void encode_sorted_rows_kernel(
       w[q] = e4m3_encode(v[4 * q] / s) | (e4m3_encode(v[4 * q + 1] / s) << 8) |
              (e4m3_encode(v[4 * q + 2] / s) << 16) | (e4m3_encode(v[4 * q + 3] / s) << 24);
     }
-    *reinterpret_cast<uint4*>(codes + r * H + c) = make_uint4(w[0], w[1], w[2], w[3]);
+    const uint4 o = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int j = 0; j < k; ++j) {
+      const int r = inv[t * k + j];
+      if (r >= 0) *reinterpret_cast<uint4*>(codes + (int64_t)r * H + c) = o;
+    }
   }
 }
 
@@ -141,7 +140,9 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t s) {
 
 hipError_t launch_amax(const void* in, bool in_bf16, int64_t n, uint32_t* amax_bits,
                        hipStream_t s) {
-  const int grid = grid_for(n / 8);
+  // few blocks: every block ends in an atomic on the same word
+  int grid = grid_for(n / 8);
+  if (grid > 512) grid = 512;
   if (in_bf16) amax_kernel<true><<<grid, 256, 0, s>>>(in, n, amax_bits);
   else amax_kernel<false><<<grid, 256, 0, s>>>(in, n, amax_bits);
   return hipGetLastError();
@@ -157,11 +158,9 @@ hipError_t launch_encode_fp8(const void* in, bool in_bf16, int64_t n, uint8_t* c
 
 hipError_t launch_encode_sorted_rows(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
                                     hipStream_t s) {
-  const int64_t npairs = (int64_t)sh.T * sh.k;
-  const int grid = grid_for(npairs * (sh.H / 16));
-  encode_sorted_rows_kernel<<<grid, 256, 0, s>>>(
-      x, sh.H, sh.k, ws.sorted_pairs, ws.offsets, sh.E, ws.x_codes,
-      reinterpret_cast<const uint32_t*>(ws.status + kStAmaxX),
+  if (sh.T <= 0) return hipSuccess;
+  encode_sorted_rows_kernel<<<sh.T, 256, 0, s>>>(
+      x, sh.H, sh.k, ws.inv, ws.x_codes, reinterpret_cast<const uint32_t*>(ws.status + kStAmaxX),
       reinterpret_cast<float*>(ws.status + kStScaleX));
   return hipGetLastError();
 }
