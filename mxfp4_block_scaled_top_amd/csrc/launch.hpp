@@ -8,6 +8,7 @@
 namespace mx {
 
 constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to here
+constexpr int kFusedRouteMaxTokens = 16;     // single-block route + permute up to here
 constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
 constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 path
 // A row tile is 4 ints: expert, first sorted row, end row (exclusive), 0.
@@ -52,6 +53,9 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* ids,
                              hipStream_t s);
 hipError_t launch_permute(const int* ids, int npairs, int E, int BM, int tile_bound,
                           const WsPtrs& ws, hipStream_t s);
+// route + permute in one single-block launch, for T*k <= kFusedPermuteMaxPairs
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* ids, float* w, int BM,
+                                int tile_bound, const WsPtrs& ws, hipStream_t s);
 
 // FP8 quantisation of n values (fp32 or bf16 input); amax accumulates into
 // *amax_bits (must be zero beforehand), the scale is written to *scale_out.

@@ -226,6 +226,37 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
                 scan_tmp);
 }
 
+// Router and permutation in one 1024-thread block (decode-sized batches:
+// T*k <= kFusedPermuteMaxPairs): the 16 waves route tokens wave, wave + 16,
+// ... into LDS (and the caller's id/weight outputs), then the block permutes
+// from LDS.  One launch instead of two.
+// lds: ids[npairs] ints, then the permutation's cnt/off/run/wcnt arrays.
+template <int PER_LANE>
+__global__ __launch_bounds__(1024) void route_permute_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int id_bits, int BM, int bound,
+    int* __restrict__ ids_out, float* __restrict__ w_out, int* __restrict__ status,
+    int* __restrict__ offsets, int* __restrict__ sorted_pairs, int* __restrict__ inv,
+    int* __restrict__ tiles) {
+  extern __shared__ int lds[];
+  __shared__ int scan_tmp[kChunkWaves + 1];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int npairs = T * k;
+  int* ids = lds;
+  for (int t = wave; t < T; t += kChunkWaves) {
+    int id;
+    float w;
+    route_token<PER_LANE>(logits + (size_t)t * E, E, k, lane, id, w);
+    if (lane < k) {
+      ids[t * k + lane] = id;
+      ids_out[(size_t)t * k + lane] = id;
+      w_out[(size_t)t * k + lane] = w;
+    }
+  }
+  __syncthreads();
+  permute_block(ids, npairs, E, id_bits, BM, bound, status, offsets, sorted_pairs, inv, tiles,
+                lds + ((npairs + 3) & ~3), scan_tmp);
+}
+
 // Multi-block path, phase 1: per-chunk ranks and per-chunk expert counts.
 __global__ __launch_bounds__(1024) void permute_count_kernel(
     const int* __restrict__ ids, int npairs, int E, int id_bits, int* __restrict__ status,
@@ -309,6 +340,26 @@ static int id_bits_for(int E) {
   int b = 0;
   while ((1 << b) < E) ++b;
   return b;
+}
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* ids, float* w, int BM,
+                                int tile_bound, const WsPtrs& ws, hipStream_t s) {
+  const int npairs = T * k;
+  const int bits = id_bits_for(E);
+  const size_t lds = ((size_t)((npairs + 3) & ~3) + (size_t)(3 + kChunkWaves) * E) * sizeof(int);
+  if (E <= 64)
+    route_permute_kernel<1><<<1, kChunk, lds, s>>>(logits, T, E, k, bits, BM, tile_bound, ids, w, ws.status,
+                                                    ws.offsets, ws.sorted_pairs, ws.inv, ws.tiles);
+  else if (E <= 128)
+    route_permute_kernel<2><<<1, kChunk, lds, s>>>(logits, T, E, k, bits, BM, tile_bound, ids, w, ws.status,
+                                                    ws.offsets, ws.sorted_pairs, ws.inv, ws.tiles);
+  else if (E <= 256)
+    route_permute_kernel<4><<<1, kChunk, lds, s>>>(logits, T, E, k, bits, BM, tile_bound, ids, w, ws.status,
+                                                    ws.offsets, ws.sorted_pairs, ws.inv, ws.tiles);
+  else
+    route_permute_kernel<8><<<1, kChunk, lds, s>>>(logits, T, E, k, bits, BM, tile_bound, ids, w, ws.status,
+                                                    ws.offsets, ws.sorted_pairs, ws.inv, ws.tiles);
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int* ids, int npairs, int E, int BM, int tile_bound,

@@ -473,7 +473,13 @@ def test_quantized_weights_feed_the_linear(mx):
                                            (128, 256, 128, 64, 4, synth.ACT_BF16),
                                            (128, 256, 128, 65, 4, synth.ACT_BF16),
                                            (512, 64, 64, 64, 4, synth.ACT_BF16),
-                                           (16, 96, 128, 300, 2, synth.ACT_FP8_E4M3)])
+                                           (16, 96, 128, 300, 2, synth.ACT_FP8_E4M3),
+                                           # up to 16 tokens route and permute in one launch
+                                           (128, 256, 128, 4, 4, synth.ACT_BF16),
+                                           (8, 288, 320, 16, 4, synth.ACT_FP8_E4M3),
+                                           (512, 64, 64, 1, 4, synth.ACT_BF16),
+                                           (48, 96, 128, 9, 2, synth.ACT_BF16),
+                                           (200, 64, 96, 13, 3, synth.ACT_BF16)])
 def test_moe_layer_equals_route_then_forward(mx, E, H, I, T, k, act):
     L = synth.layer(seed=E + H, E=E, H=H, I=I)
     logits, x = synth.moe_inputs(T + 3, T, E=E, H=H)
@@ -491,8 +497,8 @@ def test_moe_layer_equals_route_then_forward(mx, E, H, I, T, k, act):
     assert np.array_equal(ids_b.cpu().numpy(), rid)
 
 
-def test_moe_layer_decode_workload_against_golden(mx, full_layer):
-    name = "moe_decode_t32"
+@pytest.mark.parametrize("name", ["moe_decode_t4", "moe_decode_t32"])
+def test_moe_layer_decode_workload_against_golden(mx, full_layer, name):
     wl = synth.workload(name)
     g = np.load(os.path.join(GOLDEN, "%s.npz" % name))
     lg, xd = to_dev(wl["logits"], torch), to_dev(wl["x"], torch)
