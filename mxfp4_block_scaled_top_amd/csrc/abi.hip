@@ -229,9 +229,8 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   } while (0)
 
   MX_STEP(mark(MXFP4_STAGE_BEGIN), "event record");
-  // one launch for route + permute while one wave per token routes the whole
-  // batch in a single round (measured faster up to 16 tokens; at 32 tokens the
-  // two-kernel path is faster)
+  // one launch for route + permute while the block routes the whole batch in
+  // one round (a half wave per token)
   if (logits && T <= mx::kFusedRouteMaxTokens && npairs <= mx::kFusedPermuteMaxPairs) {
     MX_STEP(mx::launch_route_permute(logits, (int)T, E, k, topk_ids, topk_weights, bm, (int)bound, ws, s),
             "route+permute launch");

@@ -8,7 +8,7 @@
 namespace mx {
 
 constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to here
-constexpr int kFusedRouteMaxTokens = 16;     // single-block route + permute up to here
+constexpr int kFusedRouteMaxTokens = 32;     // single-block route + permute up to here
 constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
 constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 path
 // A row tile is 4 ints: expert, first sorted row, end row (exclusive), 0.

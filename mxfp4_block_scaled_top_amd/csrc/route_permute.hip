@@ -12,17 +12,17 @@
 namespace mx {
 
 // ---------------------------------------------------------------- top-k ----
-// One wave routes one token; lane l holds logits l, l+64, ... (PER_LANE of
-// them).  Lanes j < k end with the j-th choice (id, softmax weight over the k
-// chosen logits).
-template <int PER_LANE>
+// W lanes (a wave, or half a wave) route one token; lane l of the group
+// holds logits l, l+W, ... (PER_LANE of them).  Lanes j < k of the group end
+// with the j-th choice (id, softmax weight over the k chosen logits).
+template <int PER_LANE, int W = 64>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
                                             int& out_id, float& out_w) {
   float v[PER_LANE];
   bool avail[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
-    const int idx = lane + 64 * i;
+    const int idx = lane + W * i;
     avail[i] = idx < E;
     v[i] = avail[i] ? row[idx] : 0.0f;
   }
@@ -34,13 +34,13 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) {
-      const int idx = lane + 64 * i;
+      const int idx = lane + W * i;
       if (avail[i] && (bi == 0x7fffffff || v[i] > bv)) { bv = v[i]; bi = idx; }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
+    for (int off = W / 2; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, W);
+      const int oi = __shfl_xor(bi, off, W);
       const bool take = oi != 0x7fffffff &&
                         (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
       if (take) { bv = ov; bi = oi; }
@@ -48,13 +48,15 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     // the owner marks its entry as taken
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i)
-      if (lane + 64 * i == bi) avail[i] = false;
+      if (lane + W * i == bi) avail[i] = false;
     if (lane == j) { my_val = bv; my_id = bi; }
   }
-  // softmax over the k chosen logits (lane 0 holds the largest)
-  const float vmax = __shfl(my_val, 0, 64);
+  // softmax over the k chosen logits (lane 0 of the group holds the largest)
+  const float vmax = __shfl(my_val, 0, W);
   const float z = lane < k ? expf(my_val - vmax) : 0.0f;
-  const float s = wave_sum(z);
+  float s = z;
+#pragma unroll
+  for (int off = W / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, W);
   out_id = my_id;
   out_w = z / s;
 }
@@ -226,10 +228,10 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(
                 scan_tmp);
 }
 
-// Router and permutation in one 1024-thread block (decode-sized batches:
-// T*k <= kFusedPermuteMaxPairs): the 16 waves route tokens wave, wave + 16,
-// ... into LDS (and the caller's id/weight outputs), then the block permutes
-// from LDS.  One launch instead of two.
+// Router and permutation in one 1024-thread block (decode-sized batches):
+// each half wave routes one token (32 per round: tokens h, h + 32, ... for
+// half wave h) into LDS and the caller's id/weight outputs, then the block
+// permutes from LDS.  One launch instead of two.
 // lds: ids[npairs] ints, then the permutation's cnt/off/run/wcnt arrays.
 template <int PER_LANE>
 __global__ __launch_bounds__(1024) void route_permute_kernel(
@@ -242,14 +244,18 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int npairs = T * k;
   int* ids = lds;
-  for (int t = wave; t < T; t += kChunkWaves) {
+  const int hl = lane & 31;
+  for (int t = 2 * wave + (lane >> 5); t - (lane >> 5) < T; t += 2 * kChunkWaves) {
+    // both halves of a wave stay in the loop together (the shuffles are
+    // wave instructions); a half past T routes a clamped row and stores nothing
+    const int tt = t < T ? t : T - 1;
     int id;
     float w;
-    route_token<PER_LANE>(logits + (size_t)t * E, E, k, lane, id, w);
-    if (lane < k) {
-      ids[t * k + lane] = id;
-      ids_out[(size_t)t * k + lane] = id;
-      w_out[(size_t)t * k + lane] = w;
+    route_token<2 * PER_LANE, 32>(logits + (size_t)tt * E, E, k, hl, id, w);
+    if (t < T && hl < k) {
+      ids[t * k + hl] = id;
+      ids_out[(size_t)t * k + hl] = id;
+      w_out[(size_t)t * k + hl] = w;
     }
   }
   __syncthreads();
