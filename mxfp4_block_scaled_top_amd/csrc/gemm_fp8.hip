@@ -142,15 +142,20 @@ __device__ __forceinline__ int weight_row(int lr, int nt, int nout) {
 typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 
-// bf16 numbers 4g .. 4g+3 of the 16 at p (wave-uniform, 4-byte aligned), for
-// the lane's g (0..3), as two dwords: one scalar load, then a select chain
-// on g
-__device__ __forceinline__ uint2 bias_quad(const uint16_t* p, int g) {
-  v8i_t v;
-  asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+// bf16 numbers 4g .. 4g+3 of the 16 held in v, for the lane's g (0..3), as
+// two dwords picked by a select chain on g
+__device__ __forceinline__ uint2 bias_quad(const v8i_t& v, int g) {
   const uint32_t lo = (uint32_t)(g == 0 ? v[0] : g == 1 ? v[2] : g == 2 ? v[4] : v[6]);
   const uint32_t hi = (uint32_t)(g == 0 ? v[1] : g == 1 ? v[3] : g == 2 ? v[5] : v[7]);
   return make_uint2(lo, hi);
+}
+
+// 2 x 16 bf16 through the scalar cache in one round trip; p0, p1 wave-uniform
+// and 4-byte aligned
+__device__ __forceinline__ void sload_bias2(const uint16_t* p0, const uint16_t* p1, v8i_t& v0, v8i_t& v1) {
+  asm volatile("s_load_dwordx8 %0, %2, 0x0\n\ts_load_dwordx8 %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(v0), "=&s"(v1)
+               : "s"(p0), "s"(p1));
 }
 
 __device__ __forceinline__ float bf16_of(uint2 q, int jj) {
@@ -287,6 +292,41 @@ __device__ __forceinline__ void lds_step_reads(uint32_t aa0, uint32_t aa1, uint3
 #undef MX_RD_ACT
 #undef MX_RD_OUTS
 
+// gate_up variant in two phases: the 16 reads are issued in the order the
+// MFMAs consume them (scales, weights, then the activation chunks of MFMAs
+// 0-1, then those of MFMAs 2-3), and the caller waits for the first twelve
+// (lds_wait_first) before it starts and for the rest (lds_wait_rest) halfway.
+// The destination registers of pending reads are only named by these
+// assembly blocks until their wait.
+__device__ __forceinline__ void lds_step_issue_gateup(uint32_t aa0, uint32_t aa1, uint32_t ww, uint32_t ss,
+                                                      v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3,
+                                                      v4u_t& xb0, v4u_t& xb1, v4u_t& xb2, v4u_t& xb3,
+                                                      v4u_t& wq0, v4u_t& wq1, v4u_t& wq2, v4u_t& wq3,
+                                                      uint32_t& sb0, uint32_t& sb1, uint32_t& sb2, uint32_t& sb3) {
+  asm volatile("ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:128\n\t"
+               "ds_read_u8 %14, %19 offset:1024\n\tds_read_u8 %15, %19 offset:1152\n\t"
+               "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
+               "ds_read_b128 %10, %18 offset:8192\n\tds_read_b128 %11, %18 offset:9216\n\t"
+               "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:2048\n\t"
+               "ds_read_b128 %2, %16 offset:4096\n\tds_read_b128 %3, %16 offset:6144\n\t"
+               "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:2048\n\t"
+               "ds_read_b128 %6, %17 offset:4096\n\tds_read_b128 %7, %17 offset:6144"
+               : "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(xb0), "=&v"(xb1), "=&v"(xb2),
+                 "=&v"(xb3), "=&v"(wq0), "=&v"(wq1), "=&v"(wq2), "=&v"(wq3), "=&v"(sb0), "=&v"(sb1),
+                 "=&v"(sb2), "=&v"(sb3)
+               : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
+}
+__device__ __forceinline__ void lds_wait_first(v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3, v4u_t& wq0,
+                                               v4u_t& wq1, v4u_t& wq2, v4u_t& wq3, uint32_t& sb0,
+                                               uint32_t& sb1, uint32_t& sb2, uint32_t& sb3) {
+  asm volatile("s_waitcnt lgkmcnt(4)"
+               : "+v"(xa0), "+v"(xa1), "+v"(xa2), "+v"(xa3), "+v"(wq0), "+v"(wq1), "+v"(wq2), "+v"(wq3),
+                 "+v"(sb0), "+v"(sb1), "+v"(sb2), "+v"(sb3));
+}
+__device__ __forceinline__ void lds_wait_rest(v4u_t& xb0, v4u_t& xb1, v4u_t& xb2, v4u_t& xb3) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xb0), "+v"(xb1), "+v"(xb2), "+v"(xb3));
+}
+
 template <bool GATEUP, int BM>
 __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(PrefillArgs a,
                                                                           const int* __restrict__ tiles,
@@ -343,10 +383,24 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
     // never stored and not loaded)
     const uint16_t* bias_e = a.bias + (size_t)e * a.R;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n0 = GATEUP ? nt * (kBN / 2) + 32 * wn + 16 * (j >> 1) : nt * kBN + 64 * wn + 16 * j;
-      const int off = (GATEUP && (j & 1) ? a.nout : 0) + n0;
-      bq[j] = a.bias && n0 < a.nout ? bias_quad(bias_e + off, g) : make_uint2(0u, 0u);
+    for (int jp = 0; jp < 4; jp += 2) {
+      // groups jp and jp + 1 (16 rows each); a group past nout reads group jp's
+      // rows again and is zeroed (never stored)
+      int n0[2], off[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = jp + h;
+        n0[h] = GATEUP ? nt * (kBN / 2) + 32 * wn + 16 * (j >> 1) : nt * kBN + 64 * wn + 16 * j;
+        off[h] = (GATEUP && (j & 1) ? a.nout : 0) + n0[h];
+      }
+      if (a.bias && n0[0] < a.nout) {
+        v8i_t v0, v1;
+        sload_bias2(bias_e + off[0], bias_e + (n0[1] < a.nout ? off[1] : off[0]), v0, v1);
+        bq[jp] = bias_quad(v0, g);
+        bq[jp + 1] = n0[1] < a.nout ? bias_quad(v1, g) : make_uint2(0u, 0u);
+      } else {
+        bq[jp] = bq[jp + 1] = make_uint2(0u, 0u);
+      }
     }
   };
 
@@ -381,19 +435,26 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
     const uint32_t aa0 = a0 + so, aa1 = a1 + so, ww = w0 + so, ss = s0 + so;
     v4u_t xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3;
     uint32_t sb0, sb1, sb2, sb3;
-    lds_step_reads<GATEUP>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3,
-                           sb0, sb1, sb2, sb3);
+    if (GATEUP) {
+      lds_step_issue_gateup(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3, sb0,
+                            sb1, sb2, sb3);
+      lds_wait_first(xa0, xa1, xa2, xa3, wq0, wq1, wq2, wq3, sb0, sb1, sb2, sb3);
+    } else {
+      lds_step_reads<GATEUP>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3,
+                             sb0, sb1, sb2, sb3);
+    }
     const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
-    const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
     const v4u_t wq[4] = {wq0, wq1, wq2, wq3};
     const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
     const bool valid = 4 * cstep + g < a.nb;        // this lane's MX block lies inside K
     if (GATEUP) {
       // lane group g holds K [32g, 32g+32) of the step (its own MX block);
       // MFMA q takes elements 8q..8q+7 of it, in the same order for both
-      // operands
+      // operands; MFMAs 2-3 use the chunks read last
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
+        const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
         v8bf B[4];
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
@@ -410,6 +471,7 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
         }
       }
     } else {
+      const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
       v8i B[4];
 #pragma unroll
       for (int tg = 0; tg < 4; ++tg)
