@@ -107,18 +107,35 @@ def moe_forward(x_bits, logits, w13_blocks, w13_scales, w13_bias,
 
 
 def moe_forward_routed(x_bits, ids, w, w13_blocks, w13_scales, w13_bias,
-                       w2_blocks, w2_scales, w2_bias, act_mode=ACT_BF16):
+                       w2_blocks, w2_scales, w2_bias, act_mode=ACT_BF16, weight_format=None):
     """One MoE layer for given routing: ids int [T, k], weights [T, k].
 
     A pair whose id lies outside [0, E) contributes nothing to its token (the
     HIP boundary skips such pairs); in FP8 mode it also takes no part in the
     scale of h.  Returns a dict of float64 results and intermediates.
+
+    weight_format None is MXFP4 (blocks [.., K/32, 16], E8M0 scales);
+    ("nvfp4", g13, g2) is NVFP4 (blocks [.., K/16, 8], E4M3 scales, global
+    scales g13 of w13 and g2 of w2; gpt-oss page, "The MXFP4 -> NVFP4
+    Conversion").
     """
     x = bf16_bits_to_f64(x_bits)
     T, H = x.shape
     E = w13_blocks.shape[0]
-    I = w2_blocks.shape[2] * 32
-    if w13_blocks.shape[1] != 2 * I or w13_blocks.shape[2] * 32 != H:
+    if weight_format is None:
+        elems = 32
+        dq13 = lambda e: dequant(w13_blocks[e], w13_scales[e])    # noqa: E731
+        dq2 = lambda e: dequant(w2_blocks[e], w2_scales[e])       # noqa: E731
+    elif weight_format[0] == "nvfp4":
+        from .nvfp4 import dequant_nvfp4
+        elems = 16
+        g13, g2 = weight_format[1], weight_format[2]
+        dq13 = lambda e: dequant_nvfp4(w13_blocks[e], w13_scales[e], g13)   # noqa: E731
+        dq2 = lambda e: dequant_nvfp4(w2_blocks[e], w2_scales[e], g2)       # noqa: E731
+    else:
+        raise ValueError("unknown weight format")
+    I = w2_blocks.shape[2] * elems
+    if w13_blocks.shape[1] != 2 * I or w13_blocks.shape[2] * elems != H:
         raise ValueError("inconsistent weight shapes")
     ids = np.asarray(ids, dtype=np.int64)
     w = np.asarray(w, dtype=np.float64)
@@ -141,7 +158,7 @@ def moe_forward_routed(x_bits, ids, w, w13_blocks, w13_scales, w13_bias,
     experts = np.unique(ids[valid])
     for e in experts:
         t, j = np.nonzero(ids == e)
-        W1 = dequant(w13_blocks[e], w13_scales[e])           # [2I, H]
+        W1 = dq13(e)                                          # [2I, H]
         g = a[t] @ W1.T + b1[e]
         h[t, j] = swiglu(g, I)
     res["h"] = h
@@ -158,7 +175,7 @@ def moe_forward_routed(x_bits, ids, w, w13_blocks, w13_scales, w13_bias,
     y = np.zeros((T, k, H))
     for e in experts:
         t, j = np.nonzero(ids == e)
-        W2 = dequant(w2_blocks[e], w2_scales[e])             # [H, I]
+        W2 = dq2(e)                                           # [H, I]
         y[t, j] = hq[t, j] @ W2.T + b2[e]
     res["y"] = y
     res["out"] = np.einsum("tk,tkh->th", np.where(valid, w, 0.0), y)
