@@ -11,8 +11,9 @@ bracketed by events on the launch stream and the flush is outside them.
 
 The headline line is the 32-token decode batch (hidden 2880, 128 experts,
 top-4, bf16 activations).  The same run also measures the 4-token decode,
-the FP8 prefill workloads (2048 tokens; 8192 tokens with hot experts) and the
-dense MXFP4 projections (qkv_proj, o_proj, lm_head at 1 and 4 tokens), and
+the FP8 prefill workloads (2048 tokens; 8192 tokens with hot experts), both
+decode batches with NVFP4 expert weights, the dense MXFP4 projections
+(qkv_proj, o_proj, lm_head at 1 and 4 tokens) and the weight quantiser, and
 times the float64 CPU oracle on a bounded sample for the cpu_baseline field.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--primary-only]
@@ -172,6 +173,57 @@ def measure_moe(run, Ld, name, synth, steps, warmup):
     return res
 
 
+def nvfp4_expert_bytes(H, I):
+    """Bytes of one NVFP4 expert: 16-element blocks of 8 bytes plus one E4M3
+    scale byte each, bf16 bias."""
+    gate_up = 2 * I * (H // 16) * 9 + 2 * I * 2
+    down = H * (I // 16) * 9 + H * 2
+    return gate_up, down
+
+
+def measure_nvfp4(run, synth, steps, warmup):
+    """The decode batches with NVFP4 expert weights: router top-k and the NVFP4
+    MoE layer, bf16 activations."""
+    torch, mx = run.torch, run.mx
+    L = synth.nvfp4_layer()
+    Nd = {k: (run.dev(v) if isinstance(v, np.ndarray) else v) for k, v in L.items()}
+    del L
+    H = I = synth.H_GPT_OSS
+    E, k = synth.E_GPT_OSS, synth.TOPK_GPT_OSS
+    res = {}
+    for name in ("moe_decode_t4", "moe_decode_t32"):
+        wl = synth.workload(name)
+        T = wl["T"]
+        logits, x = run.dev(wl["logits"]), run.dev(wl["x"])
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mx.mxfp4_moe_workspace_size(T, H, I, E, k, synth.ACT_BF16), dtype=torch.uint8,
+                         device="cuda")
+
+        def step(events, logits=logits, x=x, ids=ids, w=w, out=out, ws=ws):
+            mx.mxfp4_route_topk(logits, k, topk_ids=ids, topk_weights=w)
+            mx.nvfp4_moe_forward(x, ids, w, Nd["w13_blocks"], Nd["w13_scales"], Nd["w13_global"],
+                                 Nd["w13_bias"], Nd["w2_blocks"], Nd["w2_scales"], Nd["w2_global"],
+                                 Nd["w2_bias"], out=out, workspace=ws, events=events)
+
+        step(None)
+        torch.cuda.synchronize()
+        touched = len(np.unique(ids.cpu().numpy()))
+        gu, dn = nvfp4_expert_bytes(H, I)
+        layer_bytes = touched * (gu + dn) + T * H * 2 + T * E * 4 + T * H * 2
+        gemm1_bytes = touched * gu + T * H * 2 + ids.numel() * I * 4
+        ms, stages, _ = run.time_steps(step, steps, warmup, flush=True, stage_events=True)
+        ms_plain, _, _ = run.time_steps(step, steps, warmup, flush=True)
+        mean = float(np.mean(ms_plain))
+        res[name.replace("moe_", "moe_nvfp4_")] = dict(
+            tokens=T, touched_experts=touched, ms_per_step=mean, layer_GBps=layer_bytes / mean / 1e6,
+            layer_hbm_frac=layer_bytes / mean / 1e6 / HBM_PEAK_GBS, stage_ms=stages,
+            gemm1_GBps=gemm1_bytes / stages["gemm1"] / 1e6, algorithmic_bytes=layer_bytes)
+    del Nd
+    return res
+
+
 def measure_dense(run, synth, steps, warmup):
     mx = run.mx
     out = {}
@@ -307,6 +359,11 @@ def main():
             print("bench: %s %.1f us/step" % (name, others[name]["ms_per_step"] * 1e3),
                   file=sys.stderr, flush=True)
         del Ld
+        torch.cuda.empty_cache()
+        others.update(measure_nvfp4(run, synth, max(args.steps // 2, 5), 2))
+        print("bench: nvfp4 decode %.1f / %.1f us (4 / 32 tokens)"
+              % (others["moe_nvfp4_decode_t4"]["ms_per_step"] * 1e3,
+                 others["moe_nvfp4_decode_t32"]["ms_per_step"] * 1e3), file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         others["dense"] = measure_dense(run, synth, max(args.steps // 2, 5), 2)
         print("bench: dense set done", file=sys.stderr, flush=True)

@@ -204,6 +204,34 @@ int mxfp4_moe_layer(const uint16_t* x, const float* logits, int64_t T, int64_t H
                     const mxfp4_moe_opts* opts, void* stream);
 
 /*
+ * The MoE layer of mxfp4_moe_forward with NVFP4 expert weights (gpt-oss page,
+ * "The MXFP4 -> NVFP4 Conversion": the same E2M1 element code, 16-element
+ * blocks, one E4M3 scale per block, one global scale per tensor), bf16
+ * activations only.  A weight is E2M1(code) * E4M3(block scale) * global.
+ *   w13_blocks   uint8 [E, 2I, H/16, 8]      16-byte aligned; element 2i of a
+ *                                            block in the low nibble of byte i
+ *   w13_scales   uint8 [E, 2I, H/16]         4-byte aligned; finite OCP E4M3
+ *                                            codes (not S.1111.111)
+ *   w13_global   fp32 global scale of w13 (finite)
+ *   w2_blocks    uint8 [E, H, I/16, 8]       16-byte aligned
+ *   w2_scales    uint8 [E, H, I/16]          4-byte aligned
+ *   w2_global    fp32 global scale of w2 (finite)
+ * Every other argument is that of mxfp4_moe_forward with act_mode
+ * MXFP4_ACT_BF16 (workspace: mxfp4_moe_workspace_size(..., MXFP4_ACT_BF16)).
+ * Each weight is formed exactly in bf16 (E2M1 x E4M3 has at most 6
+ * significant bits) and the global scale multiplies the fp32 sums before the
+ * bias.  Limits as mxfp4_moe_forward, and 160 <= H, I <= 3072 (five to 96
+ * 32-element chunks per weight row, the span of the persistent decode
+ * kernel) and T*k*max(H, I)*2 < 2^31; outside them MXFP4_E_SHAPE.
+ */
+int nvfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                      const int32_t* topk_ids, const float* topk_weights,
+                      const uint8_t* w13_blocks, const uint8_t* w13_scales, float w13_global,
+                      const uint16_t* w13_bias, const uint8_t* w2_blocks, const uint8_t* w2_scales,
+                      float w2_global, const uint16_t* w2_bias, uint16_t* out, void* workspace,
+                      size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream);
+
+/*
  * Dense MXFP4 projection out = x W^T + b (spark-vllm page, MXFP4 qkv/o/lm_head;
  * gptoss-spark page: qkv_proj, o_proj and the 201k-row lm_head in MXFP4), bf16
  * activations, fp32 accumulation, one round-to-nearest-even to bf16.

@@ -66,6 +66,10 @@ def lib():
             _c_void_p, _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
             _i32, _c_void_p, _c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeOpts), _c_void_p]
+        L.nvfp4_moe_forward.argtypes = [
+            _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
+            _c_void_p, _c_void_p, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, ctypes.c_float,
+            _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeOpts), _c_void_p]
         L.mxfp4_linear.argtypes = [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p, _c_void_p]
         L.mxfp4_quant_fp8_e4m3.argtypes = [_c_void_p, _i32, _i64, _c_void_p, _c_void_p, _c_void_p,
@@ -75,7 +79,8 @@ def lib():
         L.mxfp4_event_destroy.argtypes = [_c_void_p]
         L.mxfp4_event_elapsed_ms.argtypes = [_c_void_p, _c_void_p, ctypes.POINTER(ctypes.c_float)]
         for name in ("mxfp4_route_topk", "mxfp4_moe_workspace_size", "mxfp4_moe_workspace_layout_query",
-                     "mxfp4_moe_forward", "mxfp4_moe_layer", "mxfp4_linear", "mxfp4_quant_fp8_e4m3",
+                     "mxfp4_moe_forward", "mxfp4_moe_layer", "nvfp4_moe_forward", "mxfp4_linear",
+                     "mxfp4_quant_fp8_e4m3",
                      "mxfp4_quantize_weights", "mxfp4_event_create",
                      "mxfp4_event_destroy", "mxfp4_event_elapsed_ms"):
             getattr(L, name).restype = ctypes.c_int
@@ -189,6 +194,54 @@ def mxfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bia
         _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
         _ptr(w13_blocks), _ptr(w13_scales), _ptr(w13_bias),
         _ptr(w2_blocks), _ptr(w2_scales), _ptr(w2_bias), act_mode, _ptr(out),
+        _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts is not None else None,
+        _stream(stream)))
+    return out
+
+
+def nvfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_global, w13_bias,
+                      w2_blocks, w2_scales, w2_global, w2_bias, out=None, workspace=None, events=None,
+                      stream=None):
+    """MoE layer with NVFP4 expert weights (blocks [E, N, K/16, 8], E4M3 scales
+    [E, N, K/16], one fp32 global scale per tensor), bf16 activations; returns
+    out (bf16 [T, H])."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    _need(topk_weights, "topk_weights", torch.float32, 2)
+    _need(w13_blocks, "w13_blocks", torch.uint8, 4)
+    _need(w13_scales, "w13_scales", torch.uint8, 3)
+    _need(w2_blocks, "w2_blocks", torch.uint8, 4)
+    _need(w2_scales, "w2_scales", torch.uint8, 3)
+    if w13_bias is not None:
+        _need(w13_bias, "w13_bias", torch.bfloat16, 2)
+    if w2_bias is not None:
+        _need(w2_bias, "w2_bias", torch.bfloat16, 2)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E, twoI = w13_blocks.shape[0], w13_blocks.shape[1]
+    I = twoI // 2
+    if (tuple(w13_blocks.shape) != (E, 2 * I, H // 16, 8) or tuple(w13_scales.shape) != (E, 2 * I, H // 16)
+            or tuple(w2_blocks.shape) != (E, H, I // 16, 8) or tuple(w2_scales.shape) != (E, H, I // 16)
+            or tuple(topk_ids.shape) != (T, k) or tuple(topk_weights.shape) != (T, k)
+            or (w13_bias is not None and tuple(w13_bias.shape) != (E, 2 * I))
+            or (w2_bias is not None and tuple(w2_bias.shape) != (E, H))):
+        raise ValueError("inconsistent NVFP4 MoE tensor shapes")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if workspace is None:
+        workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, ACT_BF16), 1),
+                                dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    opts = None
+    if events is not None:
+        opts = MoeOpts()
+        for i, ev in enumerate(events):
+            opts.events[i] = ev
+    _check("nvfp4_moe_forward", lib().nvfp4_moe_forward(
+        _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
+        _ptr(w13_blocks), _ptr(w13_scales), float(w13_global), _ptr(w13_bias),
+        _ptr(w2_blocks), _ptr(w2_scales), float(w2_global), _ptr(w2_bias), _ptr(out),
         _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts is not None else None,
         _stream(stream)))
     return out

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -185,9 +186,19 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
             const uint8_t* w13_scales, const uint16_t* w13_bias, const uint8_t* w2_blocks,
             const uint8_t* w2_scales, const uint16_t* w2_bias, int32_t act_mode, uint16_t* out,
             void* workspace, size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream,
-            const char* fn) {
+            const char* fn, const float* nv_globals = nullptr) {
   int rc = moe_shape_check(T, H, I, E, k, act_mode);
   if (rc) return rc;
+  if (nv_globals) {
+    if (act_mode != MXFP4_ACT_BF16)
+      return fail(MXFP4_E_MODE, "%s: NVFP4 weights take bf16 activations only", fn);
+    if (H < 160 || I < 160 || H > 3072 || I > 3072)
+      return fail(MXFP4_E_SHAPE, "%s: NVFP4 weights need 160 <= H, I <= 3072", fn);
+    if (!std::isfinite(nv_globals[0]) || !std::isfinite(nv_globals[1]))
+      return fail(MXFP4_E_SHAPE, "%s: global scales must be finite", fn);
+    if ((int64_t)T * k * (I > H ? I : H) * 2 >= (1LL << 31))
+      return fail(MXFP4_E_SHAPE, "%s: NVFP4 path needs T*k*max(H, I)*2 < 2^31", fn);
+  }
   if (T == 0) return ok();
   if (!x || !topk_ids || !topk_weights || !w13_blocks || !w13_scales || !w2_blocks ||
       !w2_scales || !out)
@@ -210,7 +221,12 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mx::WsPtrs ws = ws_ptrs(workspace, L);
   const mx::MoeShape sh{(int)T, (int)H, (int)I, E, k};
-  const mx::MoeWeights w{w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias};
+  mx::MoeWeights w{w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias};
+  if (nv_globals) {
+    w.nvfp4 = true;
+    w.w13_global = nv_globals[0];
+    w.w2_global = nv_globals[1];
+  }
   const bool fp8 = act_mode == MXFP4_ACT_FP8_E4M3;
   const int bm = fp8 ? mx::kPrefillBM : mx::kDecodeBM;
   const int64_t npairs = T * k;
@@ -290,6 +306,19 @@ int mxfp4_moe_layer(const uint16_t* x, const float* logits, int64_t T, int64_t H
   return moe_run(x, logits, T, H, I, E, k, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bias,
                  w2_blocks, w2_scales, w2_bias, act_mode, out, workspace, workspace_bytes, opts,
                  stream, "moe_layer");
+}
+
+int nvfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                      const int32_t* topk_ids, const float* topk_weights,
+                      const uint8_t* w13_blocks, const uint8_t* w13_scales, float w13_global,
+                      const uint16_t* w13_bias, const uint8_t* w2_blocks, const uint8_t* w2_scales,
+                      float w2_global, const uint16_t* w2_bias, uint16_t* out, void* workspace,
+                      size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream) {
+  const float g[2] = {w13_global, w2_global};
+  return moe_run(x, nullptr, T, H, I, E, k, const_cast<int32_t*>(topk_ids),
+                 const_cast<float*>(topk_weights), w13_blocks, w13_scales, w13_bias, w2_blocks,
+                 w2_scales, w2_bias, MXFP4_ACT_BF16, out, workspace, workspace_bytes, opts, stream,
+                 "nvfp4_moe_forward", g);
 }
 
 int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_blocks,

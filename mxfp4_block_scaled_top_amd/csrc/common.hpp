@@ -16,6 +16,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kBlockElems = 32;   // elements per MX block
 constexpr int kBlockBytes = 16;   // bytes per MX block of E2M1 nibbles
@@ -45,6 +46,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 // E8M0 byte s -> 2^(s-127) as fp32, exact for s in [1, 254].
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(s << 23);
+}
+
+// OCP E4M3 code -> fp32 (exact; the NaN codes S.1111.111 are not expected
+// here and decode as +-480).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
 }
 
 // OCP E4M3 code of an fp32 value q: round to nearest, ties to even mantissa,

@@ -53,6 +53,7 @@ struct GemvArgs {
   uint16_t* out_hi;         // gate_up: h hi / dense: out bf16
   uint16_t* out_lo;         // gate_up: h lo
   float* y;                 // down
+  float gscale;             // NVFP4: the weight tensor's global scale (MXFP4: 1)
 };
 
 // One K-group's operands for one lane.
@@ -288,12 +289,36 @@ constexpr int kRunRows = 8;            // rows per wave's DMA run
 constexpr int kCols = 4;               // activation rows per unit
 constexpr int kMaxHG = 12;             // K-groups per wave: K <= 3072 on this path
 constexpr int kRunDma = 12;            // 1 KB weight DMA instructions per run (8 x 1536 B max)
-constexpr int kRunScDma = 3;           // 256 B scale DMA instructions per run (8 x 96 B max)
-// (a run's region also covers reads of blocks up to 95 of its last row:
-// 7 * 1536 + 96 * 16 <= 12 KB and 7 * 96 + 96 <= 768)
-constexpr int kRunBytes = kRunDma * 1024 + kRunScDma * 256;   // LDS per run
-constexpr int kBufBytes = 2 * kRunBytes;                       // LDS per unit buffer
-constexpr int kPersistLds = kBufBytes + 64 * 16;               // buffer + partial sums
+// 256 B scale DMA instructions per run: MXFP4 8 x 96 B max, NVFP4 (two
+// scales per 32 elements) 8 x 192 B max
+// Eight E2M1 nibbles (one dword) times a full fp32 factor, as bf16.  The
+// scaled FP4 conversions apply only the exponent field of their scale
+// operand, so an E4M3 block scale (four significant bits) cannot ride on
+// them: the nibbles are converted at unit scale, multiplied in fp32 and
+// rounded to bf16.  Every step is exact: an E2M1 value times an E4M3 value
+// has at most six significant bits and stays inside bf16's normal range.
+__device__ __forceinline__ v8bf fp4x8_times_bf16(uint32_t w, float f) {
+  const v2f p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const v2f p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const v2f p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const v2f p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  v8bf r;
+  r[0] = (__bf16)(p0[0] * f); r[1] = (__bf16)(p0[1] * f);
+  r[2] = (__bf16)(p1[0] * f); r[3] = (__bf16)(p1[1] * f);
+  r[4] = (__bf16)(p2[0] * f); r[5] = (__bf16)(p2[1] * f);
+  r[6] = (__bf16)(p3[0] * f); r[7] = (__bf16)(p3[1] * f);
+  return r;
+}
+
+template <bool NV> struct RunLayout {
+  static constexpr int kScDma = NV ? 6 : 3;
+  // (a run's region also covers reads of blocks up to 95 of its last row:
+  // 7 * 1536 + 96 * 16 <= 12 KB; scales 7 * 96 + 96 <= 768, NVFP4
+  // 7 * 192 + 192 <= 1536)
+  static constexpr int kRunBytes = kRunDma * 1024 + kScDma * 256;   // LDS per run
+  static constexpr int kBufBytes = 2 * kRunBytes;                  // LDS per unit buffer
+  static constexpr int kLds = kBufBytes + 64 * 16;                 // buffer + partial sums
+};
 static_assert(kCols == kDecodeBM, "a decode row tile is one m-tile");
 
 struct PersistPlan {
@@ -332,7 +357,9 @@ __device__ __forceinline__ uint4 row_rotate4(uint4 v) {
                     (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctrl, 0xf, 0xf, true));
 }
 
-template <int MODE, int HG>
+// NV: NVFP4 weights (16-element blocks with E4M3 scales: two scales per
+// 32-element chunk; the tensor's global scale is applied to the sums).
+template <int MODE, int HG, bool NV>
 __global__ __launch_bounds__(128) void gemv_persist_kernel(
     GemvArgs a, PersistPlan P, const int* __restrict__ tiles, const int* __restrict__ sorted_pairs,
     const int* __restrict__ status) {
@@ -351,19 +378,22 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
   if (u_begin >= u_end) return;   // the same for both waves: no barrier is skipped by one
 
   const int64_t rb = (int64_t)a.nb * kBlockBytes;
-  v4f* red = reinterpret_cast<v4f*>(smem + kBufBytes);
+  using RL = RunLayout<NV>;
+  constexpr int kRunBytes = RL::kRunBytes;
+  v4f* red = reinterpret_cast<v4f*>(smem + RL::kBufBytes);
+  const int nsr = NV ? 2 * a.nb : a.nb;               // scale bytes per weight row
 
   // DMA of this wave's run (rows 8kh..8kh+7 of a unit) into buffer `buf`; the
   // tail lanes of the last instruction re-read the run's last 16 bytes
   const int64_t wrun = kRunRows * rb;                 // weight bytes of the run
-  const int64_t srun = (int64_t)kRunRows * a.nb;      // scale bytes (4-byte aligned run)
+  const int64_t srun = (int64_t)kRunRows * nsr;       // scale bytes (4-byte aligned run)
   const uint32_t wlast = (uint32_t)(wrun - 16), slast = (uint32_t)(srun - 4);
   const uint32_t lane16 = 16u * lane, lane4 = 4u * lane;
   auto issue_dma = [&](int e, int n0) {
     // first row of the run: gate_up wave 1 takes the matching up rows
     const size_t row0 = (size_t)e * a.rows_per_expert + n0 + (kPair ? (size_t)kh * a.nout : (size_t)kh * kRunRows);
     const uint8_t* gw = a.wb + row0 * rb;
-    const uint8_t* gs = a.ws + row0 * a.nb;
+    const uint8_t* gs = a.ws + row0 * nsr;
     uint8_t* dst = smem + kh * kRunBytes;
 #pragma unroll
     for (int c = 0; c < kRunDma; ++c) {
@@ -371,7 +401,7 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
       __builtin_amdgcn_global_load_lds(gw + off, dst + c * 1024, 16, 0, 2);
     }
 #pragma unroll
-    for (int c = 0; c < kRunScDma; ++c) {
+    for (int c = 0; c < RL::kScDma; ++c) {
       const uint32_t off = min((uint32_t)(c * 256) + lane4, slast);
       __builtin_amdgcn_global_load_lds(gs + off, dst + kRunDma * 1024 + c * 256, 4, 0, 2);
     }
@@ -447,7 +477,7 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
   // (run r / 8, row r % 8 of the run)
   const int lrun = r / kRunRows, lrr = r % kRunRows;
   const int wrow_off = lrun * kRunBytes + lrr * (int)rb;
-  const int srow_off = lrun * kRunBytes + kRunDma * 1024 + lrr * a.nb;
+  const int srow_off = lrun * kRunBytes + kRunDma * 1024 + lrr * nsr;
 
   auto step = [&](v4f& acc, const v8bf& A, const uint4& b, const uint4& bl) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(b), acc, 0, 0, 0);
@@ -469,19 +499,33 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     asm volatile("s_barrier" ::: "memory");   // both runs of unit u have landed
     // blocks past K (up to 8 HG - 1 < 96) read bytes inside the run's region
     // (finite FP4 codes or stale scales); their scale is forced to 0 below
+    // scale bytes of groups jj: MXFP4 one per group, packed four per
+    // register; NVFP4 two per group (the chunk's two 16-element blocks),
+    // packed two groups per register
+    constexpr int kSpk = NV ? (HG + 1) / 2 : (HG + 3) / 4;
+    uint32_t spk[kSpk];
+    if (NV) {
+      const uint8_t* ssrc = smem + srow_off + 2 * (4 * gl + g);
+#pragma unroll
+      for (int k2 = 0; k2 < kSpk; ++k2) {
+        uint32_t p = *reinterpret_cast<const uint16_t*>(ssrc + 8 * (2 * k2));
+        if (2 * k2 + 1 < HG) p |= (uint32_t)*reinterpret_cast<const uint16_t*>(ssrc + 8 * (2 * k2 + 1)) << 16;
+        spk[k2] = p;
+      }
+    } else {
+      const uint8_t* ssrc = smem + srow_off + 4 * gl + g;
+#pragma unroll
+      for (int k4 = 0; k4 < kSpk; ++k4) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int i = 0; i < 4 && 4 * k4 + i < HG; ++i) p |= (uint32_t)ssrc[4 * (4 * k4 + i)] << (8 * i);
+        spk[k4] = p;
+      }
+    }
     uint4 wreg[HG];
-    uint32_t spk[(HG + 3) / 4];   // scale bytes of groups jj, packed four per register
     const uint8_t* wsrc = smem + wrow_off + (4 * gl + g) * kBlockBytes;
-    const uint8_t* ssrc = smem + srow_off + 4 * gl + g;
 #pragma unroll
     for (int jj = 0; jj < HG; ++jj) wreg[jj] = *reinterpret_cast<const uint4*>(wsrc + jj * 4 * kBlockBytes);
-#pragma unroll
-    for (int k4 = 0; k4 < (HG + 3) / 4; ++k4) {
-      uint32_t p = 0;
-#pragma unroll
-      for (int i = 0; i < 4 && 4 * k4 + i < HG; ++i) p |= (uint32_t)ssrc[4 * (4 * k4 + i)] << (8 * i);
-      spk[k4] = p;
-    }
     // both waves have read the buffer: the next unit's DMA may overwrite it
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const bool more = u + 1 < u_end;
@@ -497,14 +541,30 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
 #pragma unroll
     for (int jj = 0; jj < HG; ++jj) {
       const uint4 w = wreg[jj];
-      // blocks past K (scale byte forced to 0, i.e. a factor 0) contribute 0
-      const uint32_t sc = (spk[jj / 4] >> (8 * (jj % 4))) & 0xffu;
-      const float f = e8m0_to_f32(4 * (gl + jj) + g < a.nb ? sc : 0u);
+      // blocks past K (factor 0) contribute 0
+      const bool in_k = 4 * (gl + jj) + g < a.nb;
+      float f0, f1;   // factors of elements 0-15 and 16-31 of the lane's chunk
+      if (NV) {
+        // E4M3 block scales, applied whole (mantissa included) below
+        const uint32_t sw = (spk[jj / 2] >> (16 * (jj % 2))) & 0xffffu;
+        f0 = in_k ? e4m3_to_f32(sw & 0xffu) : 0.0f;
+        f1 = in_k ? e4m3_to_f32(sw >> 8) : 0.0f;
+      } else {
+        const uint32_t sc = (spk[jj / 4] >> (8 * (jj % 4))) & 0xffu;
+        f0 = f1 = e8m0_to_f32(in_k ? sc : 0u);
+      }
       const uint4 lo = MODE == kDown ? xl[jj] : xa[jj];
-      step(acc0, fp4x8_to_bf16(w.x, f), xa[jj], lo);
-      step(acc1, fp4x8_to_bf16(w.y, f), row_rotate4<1>(xa[jj]), row_rotate4<1>(lo));
-      step(acc0, fp4x8_to_bf16(w.z, f), row_rotate4<2>(xa[jj]), row_rotate4<2>(lo));
-      step(acc1, fp4x8_to_bf16(w.w, f), row_rotate4<3>(xa[jj]), row_rotate4<3>(lo));
+      if (NV) {
+        step(acc0, fp4x8_times_bf16(w.x, f0), xa[jj], lo);
+        step(acc1, fp4x8_times_bf16(w.y, f0), row_rotate4<1>(xa[jj]), row_rotate4<1>(lo));
+        step(acc0, fp4x8_times_bf16(w.z, f1), row_rotate4<2>(xa[jj]), row_rotate4<2>(lo));
+        step(acc1, fp4x8_times_bf16(w.w, f1), row_rotate4<3>(xa[jj]), row_rotate4<3>(lo));
+      } else {
+        step(acc0, fp4x8_to_bf16(w.x, f0), xa[jj], lo);
+        step(acc1, fp4x8_to_bf16(w.y, f0), row_rotate4<1>(xa[jj]), row_rotate4<1>(lo));
+        step(acc0, fp4x8_to_bf16(w.z, f1), row_rotate4<2>(xa[jj]), row_rotate4<2>(lo));
+        step(acc1, fp4x8_to_bf16(w.w, f1), row_rotate4<3>(xa[jj]), row_rotate4<3>(lo));
+      }
     }
     v4f acc = acc0 + acc1;
     if (kh == 1) red[lane] = acc;
@@ -512,6 +572,7 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kh == 0) {
       acc += red[lane];
+      if (NV) acc *= a.gscale;
       // lane (column r, group g) holds rows 4g + jj of column r
       const int row = rbeg + r;
       const bool col_ok = r < rend - rbeg;
@@ -566,9 +627,10 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
 
 // Blocks of the persistent kernel: as many as are resident at once on the
 // device (compute units x resident blocks per unit, queried per kernel).
-template <int MODE, int HG>
+template <int MODE, int HG, bool NV>
 static hipError_t launch_persist_hg(const GemvArgs& a, const PersistPlan& P, const int* tiles,
                                     const int* sorted_pairs, const int* status, hipStream_t s) {
+  constexpr int kPersistLds = RunLayout<NV>::kLds;
   // (device + 1) << 32 | blocks, cached per kernel; threads may race to fill
   // it, but every writer stores the same value
   static std::atomic<uint64_t> cache{0};
@@ -581,26 +643,26 @@ static hipError_t launch_persist_hg(const GemvArgs& a, const PersistPlan& P, con
     int cus = 0, per_cu = 0;
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_persist_kernel<MODE, HG>, 128,
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_persist_kernel<MODE, HG, NV>, 128,
                                                        kPersistLds);
     if (err != hipSuccess) return err;
     c = key | (uint64_t)(cus * (per_cu > 0 ? per_cu : 1));
     cache.store(c, std::memory_order_relaxed);
   }
   const unsigned blocks = (unsigned)(c & 0xffffffffu);
-  gemv_persist_kernel<MODE, HG><<<blocks, 128, kPersistLds, s>>>(a, P, tiles, sorted_pairs, status);
+  gemv_persist_kernel<MODE, HG, NV><<<blocks, 128, kPersistLds, s>>>(a, P, tiles, sorted_pairs, status);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool NV = false>
 static hipError_t launch_persist(const GemvArgs& a, const PersistPlan& P, const int* tiles,
                                  const int* sorted_pairs, const int* status, hipStream_t s) {
   switch (persist_hg(a.nb)) {
-    case 1: return launch_persist_hg<MODE, 1>(a, P, tiles, sorted_pairs, status, s);
-    case 2: return launch_persist_hg<MODE, 2>(a, P, tiles, sorted_pairs, status, s);
-    case 3: return launch_persist_hg<MODE, 3>(a, P, tiles, sorted_pairs, status, s);
-    case 6: return launch_persist_hg<MODE, 6>(a, P, tiles, sorted_pairs, status, s);
-    case 12: return launch_persist_hg<MODE, 12>(a, P, tiles, sorted_pairs, status, s);
+    case 1: return launch_persist_hg<MODE, 1, NV>(a, P, tiles, sorted_pairs, status, s);
+    case 2: return launch_persist_hg<MODE, 2, NV>(a, P, tiles, sorted_pairs, status, s);
+    case 3: return launch_persist_hg<MODE, 3, NV>(a, P, tiles, sorted_pairs, status, s);
+    case 6: return launch_persist_hg<MODE, 6, NV>(a, P, tiles, sorted_pairs, status, s);
+    case 12: return launch_persist_hg<MODE, 12, NV>(a, P, tiles, sorted_pairs, status, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -648,6 +710,14 @@ hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const M
   // expected busy row tiles: one m-tile per routed pair at most
   const int64_t pairs = (int64_t)sh.T * sh.k;
   const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.I / 16);
+  if (w.nvfp4) {
+    // NVFP4 runs on the persistent kernel only
+    if (!persist_fits(a.nb, a.act_bytes)) return hipErrorInvalidValue;
+    a.gscale = w.w13_global;
+    return launch_persist<kGateUp, true>(a, persist_plan(kGateUp, sh.I), ws.tiles, ws.sorted_pairs,
+                                         ws.status, s);
+  }
+  a.gscale = 1.0f;
   if (persist_fits(a.nb, a.act_bytes))
     return launch_persist<kGateUp>(a, persist_plan(kGateUp, sh.I), ws.tiles, ws.sorted_pairs,
                                    ws.status, s);
@@ -674,6 +744,13 @@ hipError_t launch_moe_down_bf16(const MoeShape& sh, const MoeWeights& w, const W
   a.y = ws.y;
   const int64_t pairs = (int64_t)sh.T * sh.k;
   const int64_t busy = (pairs < sh.E ? pairs : sh.E) * (sh.H / 16);
+  if (w.nvfp4) {
+    if (!persist_fits(a.nb, a.act_bytes)) return hipErrorInvalidValue;
+    a.gscale = w.w2_global;
+    return launch_persist<kDown, true>(a, persist_plan(kDown, sh.H), ws.tiles, ws.sorted_pairs,
+                                       ws.status, s);
+  }
+  a.gscale = 1.0f;
   if (persist_fits(a.nb, a.act_bytes))
     return launch_persist<kDown>(a, persist_plan(kDown, sh.H), ws.tiles, ws.sorted_pairs,
                                  ws.status, s);

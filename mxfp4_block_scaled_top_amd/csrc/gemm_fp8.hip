@@ -332,7 +332,6 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
                                                                           const int* __restrict__ tiles,
                                                                           int* status) {
   using C = Ring<BM>;
-  constexpr int NW = C::kWaves;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kSlot];
   const int num_units = status[kStNumTiles] * a.NT;
   const float sx = __uint_as_float((uint32_t)status[a.scale_word]);

@@ -47,6 +47,11 @@ struct MoeWeights {
   const uint8_t* w2_blocks;
   const uint8_t* w2_scales;
   const uint16_t* w2_bias;
+  // NVFP4 weights (16-element blocks, E4M3 scales [., ., K/16], one global
+  // scale per tensor); bf16-activation path only
+  bool nvfp4 = false;
+  float w13_global = 1.0f;
+  float w2_global = 1.0f;
 };
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* ids, float* w,

@@ -83,6 +83,31 @@ def layer(seed=LAYER_SEED, E=E_GPT_OSS, H=H_GPT_OSS, I=H_GPT_OSS):
                 w2_blocks=w2_blocks, w2_scales=w2_scales, w2_bias=w2_bias)
 
 
+NVFP4_LAYER_SEED = 2000
+
+
+def _nv_weights(rng, lead, N, K):
+    """NVFP4 blocks (uniform bytes: two uniform E2M1 codes), E4M3 block scales
+    (positive, exponent field 4..10 with any mantissa: 0.125 .. 15.0) and a
+    bf16 bias, for [lead.., N, K] weights."""
+    blocks = rng.integers(0, 256, lead + (N, K // 16, 8), dtype=np.uint8)
+    exp = rng.integers(4, 11, lead + (N, K // 16))
+    man = rng.integers(0, 8, lead + (N, K // 16))
+    scales = ((exp << 3) | man).astype(np.uint8)
+    bias = f32_to_bf16_bits(rng.normal(0.0, 0.02, lead + (N,)).astype(np.float32))
+    return blocks, scales, bias
+
+
+def nvfp4_layer(seed=NVFP4_LAYER_SEED, E=E_GPT_OSS, H=H_GPT_OSS, I=H_GPT_OSS):
+    """One MoE layer's NVFP4 weights (dict of numpy arrays and the two fp32
+    global scales, 2^-6 and 3 * 2^-8)."""
+    rng = np.random.default_rng(seed)
+    w13_blocks, w13_scales, w13_bias = _nv_weights(rng, (E,), 2 * I, H)
+    w2_blocks, w2_scales, w2_bias = _nv_weights(rng, (E,), H, I)
+    return dict(w13_blocks=w13_blocks, w13_scales=w13_scales, w13_global=2.0 ** -6, w13_bias=w13_bias,
+                w2_blocks=w2_blocks, w2_scales=w2_scales, w2_global=3.0 * 2.0 ** -8, w2_bias=w2_bias)
+
+
 def moe_inputs(seed, T, E=E_GPT_OSS, H=H_GPT_OSS, hot=0):
     """Router logits float32 [T, E] and x bf16 bits [T, H]."""
     rng = np.random.default_rng(seed)

@@ -141,3 +141,20 @@ def test_valid_call_without_a_gpu_reports_no_device(L):
         pytest.skip("a device is present")
     assert L.mxfp4_route_topk(_fake(), 4, 128, 4, _fake(), _fake(), None) == E_DEVICE
     assert L.mxfp4_last_error() != b""
+
+
+def test_nvfp4_moe_forward_rejects_bad_arguments_without_touching_memory(L):
+    f = L.nvfp4_moe_forward
+    fake = _fake
+    args = [fake(1), 4, 2880, 2880, 128, 4, fake(2), fake(3), fake(4), fake(5), ctypes.c_float(1.0), None,
+            fake(6), fake(7), ctypes.c_float(1.0), None, fake(8), fake(9), ctypes.c_size_t(1 << 30), None, None]
+    a = list(args); a[8] = None                       # null w13_blocks
+    assert f(*a) == E_NULL
+    a = list(args); a[2] = 4096; a[3] = 4096          # beyond the NVFP4 limit
+    assert f(*a) == E_SHAPE
+    a = list(args); a[2] = 128                        # below the NVFP4 limit
+    assert f(*a) == E_SHAPE
+    a = list(args); a[10] = ctypes.c_float(float("nan"))
+    assert f(*a) == E_SHAPE
+    a = list(args); a[2] = 2880 + 16                  # H % 32
+    assert f(*a) == E_SHAPE

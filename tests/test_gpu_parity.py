@@ -511,3 +511,102 @@ def test_moe_layer_decode_workload_against_golden(mx, full_layer, name):
     assert np.array_equal(ids.cpu().numpy(), rid)
     got = bf16_dev_to_f64(out)[g["tokens"]]
     assert_close(got, g["out"].astype(np.float64), name + " via moe_layer")
+
+
+# ------------------------------------------------------------ NVFP4 weights ----
+
+
+def _nv_dev(L):
+    return {k: (to_dev(v, torch) if isinstance(v, np.ndarray) else v) for k, v in L.items()}
+
+
+def _run_nv(mx, Ld, x_bits, ids, w):
+    out = mx.nvfp4_moe_forward(to_dev(x_bits, torch), to_dev(ids.astype(np.int32), torch),
+                               to_dev(w.astype(np.float32), torch), Ld["w13_blocks"], Ld["w13_scales"],
+                               Ld["w13_global"], Ld["w13_bias"], Ld["w2_blocks"], Ld["w2_scales"],
+                               Ld["w2_global"], Ld["w2_bias"])
+    torch.cuda.synchronize()
+    return out
+
+
+def _mx_as_nv(blocks, scales):
+    """MXFP4 weights as NVFP4 with the same values (power-of-two E4M3 scales)."""
+    nb = blocks.shape[-2]
+    e = scales.astype(np.int64) - 127
+    assert e.min() >= -9 and e.max() <= 8
+    # 2^-6 .. 2^8 are E4M3 normals (mantissa 0); 2^-9 .. 2^-7 are the
+    # subnormal codes 1, 2, 4 (m * 2^-9)
+    codes = np.where(e >= -6, (e + 7) << 3, 1 << np.clip(e + 9, 0, 2)).astype(np.uint8)
+    return (np.ascontiguousarray(blocks.reshape(blocks.shape[:-2] + (2 * nb, 8))),
+            np.ascontiguousarray(np.repeat(codes, 2, axis=-1)))
+
+
+# NVFP4 runs where 160 <= H, I <= 3072; H/32 and I/32 still give every K tail
+# modulo 4, and the largest case fills the kernel's twelve chunk groups
+NV_SMALL = [  # E, H, I, T, k
+    (8, 288, 320, 1, 4),
+    (8, 288, 320, 5, 4),
+    (8, 288, 320, 37, 4),
+    (16, 160, 256, 300, 4),
+    (4, 224, 192, 70, 2),
+    (1, 256, 160, 9, 1),
+    (2, 3072, 3072, 3, 2),
+]
+
+
+@pytest.mark.parametrize("E,H,I,T,k", [(8, 288, 320, 37, 4), (16, 160, 256, 300, 4), (4, 224, 192, 70, 2)])
+def test_nvfp4_equals_mxfp4_for_power_of_two_scales(mx, E, H, I, T, k):
+    # the same weight values in both formats give bitwise the same layer
+    L = synth.layer(seed=E * 5 + H, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(T + 1, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    ref = _run_moe(mx, _layer_dev(L), x, ids, w, synth.ACT_BF16)
+    n13, m13 = _mx_as_nv(L["w13_blocks"], L["w13_scales"])
+    n2, m2 = _mx_as_nv(L["w2_blocks"], L["w2_scales"])
+    Nd = _nv_dev(dict(w13_blocks=n13, w13_scales=m13, w13_global=1.0, w13_bias=L["w13_bias"],
+                      w2_blocks=n2, w2_scales=m2, w2_global=1.0, w2_bias=L["w2_bias"]))
+    got = bf16_dev_to_f64(_run_nv(mx, Nd, x, ids, w))
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("E,H,I,T,k", NV_SMALL)
+def test_nvfp4_small_layers(mx, E, H, I, T, k):
+    L = synth.nvfp4_layer(seed=E * 11 + H, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(T + 5, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    got = bf16_dev_to_f64(_run_nv(mx, _nv_dev(L), x, ids, w))
+    ref = oracle.moe_forward_routed(x, ids, w, L["w13_blocks"], L["w13_scales"], L["w13_bias"],
+                                    L["w2_blocks"], L["w2_scales"], L["w2_bias"],
+                                    weight_format=("nvfp4", L["w13_global"], L["w2_global"]))
+    assert_close_rounded(got, ref["out"], "nvfp4 E%d H%d I%d T%d" % (E, H, I, T))
+
+
+@pytest.mark.parametrize("T", [4, 32])
+def test_nvfp4_decode_full_size_sampled(mx, T):
+    # gpt-oss-120b MoE shape with NVFP4 weights; the oracle on 4 sampled tokens
+    L = synth.nvfp4_layer()
+    logits, x = synth.moe_inputs(40 + T, T)
+    ids, w = oracle.route_topk(logits, synth.TOPK_GPT_OSS)
+    got = bf16_dev_to_f64(_run_nv(mx, _nv_dev(L), x, ids, w))
+    no_constant_rows(got)
+    toks = np.random.default_rng(T).choice(T, min(T, 4), replace=False)
+    ref = oracle.moe_forward_routed(x[toks], ids[toks], w[toks], L["w13_blocks"], L["w13_scales"],
+                                    L["w13_bias"], L["w2_blocks"], L["w2_scales"], L["w2_bias"],
+                                    weight_format=("nvfp4", L["w13_global"], L["w2_global"]))
+    assert_close(got[toks], ref["out"], "nvfp4 decode T%d" % T)
+
+
+def test_nvfp4_rejects_small_shapes_and_bad_globals(mx):
+    L = synth.nvfp4_layer(seed=3, E=4, H=160, I=160)
+    Ld = _nv_dev(L)
+    logits, x = synth.moe_inputs(1, 4, E=4, H=160)
+    ids, w = oracle.route_topk(logits, 2)
+    bad = dict(L, w13_global=float("inf"))
+    with pytest.raises(mx.Mxfp4Error):
+        _run_nv(mx, _nv_dev(bad), x, ids, w)
+    S = synth.nvfp4_layer(seed=3, E=4, H=128, I=160)
+    _, xs = synth.moe_inputs(1, 4, E=4, H=128)
+    with pytest.raises(mx.Mxfp4Error):
+        _run_nv(mx, _nv_dev(S), xs, ids, w)
+    out = _run_nv(mx, Ld, x, ids, w)
+    assert out.shape == (4, 160)
