@@ -26,14 +26,17 @@ Pins (see tests/test_oracle_*.py):
     grid (8 mantissa steps per binade, range) against the gpt-oss page's
     MXFP4/NVFP4 property table;
   * moe_forward / linear: exact rational (fractions.Fraction) brute force on
-    tiny shapes, reductions E=1/k=1 to the dense linear, identical experts.
+    tiny shapes (all three activation modes; the MXFP4-activation brute force
+    has its own block quantiser), reductions E=1/k=1 to the dense linear,
+    identical experts, MXFP4-representable activations passing through the
+    MXFP4-activation mode unchanged.
   Values at the full layer shapes are "parity unpinned" by the pages: they
   print no output of any layer; only the functions above are pinned.
 """
 
 from . import fp8, moe, mxfp4, nvfp4, quant  # noqa: F401
 from .fp8 import e4m3_decode, e4m3_encode, quant_per_tensor  # noqa: F401
-from .moe import (ACT_BF16, ACT_FP8_E4M3, linear, linear_rows,  # noqa: F401
+from .moe import (ACT_BF16, ACT_FP8_E4M3, ACT_MXFP4, linear, linear_rows,  # noqa: F401
                   moe_forward, moe_forward_routed, permute, route_topk,
                   swiglu)
 from .mxfp4 import (E2M1_TABLE, bf16_bits_to_f64, dequant,  # noqa: F401
@@ -43,7 +46,7 @@ from .quant import quantize_mxfp4  # noqa: F401
 
 __all__ = [
     "fp8", "moe", "mxfp4", "e4m3_decode", "e4m3_encode", "quant_per_tensor",
-    "ACT_BF16", "ACT_FP8_E4M3", "linear", "linear_rows", "moe_forward", "moe_forward_routed", "permute", "route_topk", "swiglu", "E2M1_TABLE",
+    "ACT_BF16", "ACT_FP8_E4M3", "ACT_MXFP4", "linear", "linear_rows", "moe_forward", "moe_forward_routed", "permute", "route_topk", "swiglu", "E2M1_TABLE",
     "bf16_bits_to_f64", "dequant", "e2m1_value", "e8m0_scale",
     "pack_nibbles", "unpack_nibbles", "quant", "quantize_mxfp4", "nvfp4", "dequant_nvfp4",
     "unpack_nibbles16",

@@ -22,6 +22,11 @@ Readings where the pages are silent (listed in the design doc):
   * biases are added inside each expert, before the routing weight;
   * FP8 mode quantizes x, and h, each with its own single per-tensor scale
     over the whole call (h rounded to fp32 first);
+  * MXFP4-activation mode (the FP4 x FP4 block-scaled contraction the
+    spark-vllm page lists as future work, "Performance Optimizations")
+    quantizes each 32-element block of every row of x, and of every routed
+    row of h (rounded to fp32 first), with the same block rule as the weight
+    quantiser (oracle/quant.py);
   * out[t] = sum_k w[t,k] * y[t,k]; the oracle keeps it in float64.
 """
 
@@ -29,9 +34,11 @@ import numpy as np
 
 from .fp8 import e4m3_decode, quant_per_tensor
 from .mxfp4 import bf16_bits_to_f64, dequant
+from .quant import quantize_mxfp4
 
 ACT_BF16 = 0
 ACT_FP8_E4M3 = 1
+ACT_MXFP4 = 2
 
 
 def route_topk(logits, k):
@@ -96,8 +103,10 @@ def moe_forward(x_bits, logits, w13_blocks, w13_scales, w13_bias,
              bias bf16 bits [E, 2I] or None
     w2_*     down weights: blocks [E, H, I/32, 16], scales [E, H, I/32],
              bias bf16 bits [E, H] or None
-    act_mode ACT_BF16 (activations used as given) or ACT_FP8_E4M3
-             (x and h each quantized with one per-tensor scale)
+    act_mode ACT_BF16 (activations used as given), ACT_FP8_E4M3
+             (x and h each quantized with one per-tensor scale) or
+             ACT_MXFP4 (x and h quantized to MXFP4, one E8M0 scale per
+             32-element block of each row)
     """
     ids, w = route_topk(logits, k)
     res = moe_forward_routed(x_bits, ids, w, w13_blocks, w13_scales, w13_bias,
@@ -147,6 +156,10 @@ def moe_forward_routed(x_bits, ids, w, w13_blocks, w13_scales, w13_bias,
         xc, sx, _ = quant_per_tensor(x)
         a = e4m3_decode(xc) * sx
         res.update(x_codes=xc, x_scale=sx)
+    elif act_mode == ACT_MXFP4:
+        xb, xs = quantize_mxfp4(x)                           # per token row, 32-element blocks
+        a = dequant(xb, xs)
+        res.update(x_blocks=xb, x_scales=xs)
     elif act_mode == ACT_BF16:
         a = x
     else:
@@ -169,6 +182,12 @@ def moe_forward_routed(x_bits, ids, w, w13_blocks, w13_scales, w13_bias,
         hq = np.zeros_like(h32)
         hq[valid] = e4m3_decode(hc) * sh
         res.update(h32=h32, h_codes=hc, h_scale=sh)
+    elif act_mode == ACT_MXFP4:
+        h32 = h.astype(np.float32).astype(np.float64)
+        hb, hs = quantize_mxfp4(h32[valid])                  # [valid pairs, I/32, 16], [.., I/32]
+        hq = np.zeros_like(h32)
+        hq[valid] = dequant(hb, hs)
+        res.update(h32=h32, h_blocks=hb, h_scales=hs)
     else:
         hq = h
 

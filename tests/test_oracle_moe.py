@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import synth
-from oracle.moe import ACT_BF16, ACT_FP8_E4M3
+from oracle.moe import ACT_BF16, ACT_FP8_E4M3, ACT_MXFP4
 
 # ----------------------------------------------------------------- brute force
 
@@ -89,6 +89,42 @@ def _bf_quant(values):
     return [_bf_fp8_round(_bf_rn_f32(v / s)) * s for v in values]
 
 
+E2M1_MAGS = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+             Fraction(4), Fraction(6)]
+
+
+def _bf_floor_log2(a):
+    e = 0
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    return e
+
+
+def _bf_mx_quant(values):
+    """MXFP4 of one row (length a multiple of 32), block by block: shared
+    exponent floor(log2 amax) - 2 clamped to [-125, 125], each |v| / 2^X to the
+    nearest E2M1 magnitude (a tie to the even code, past 6 to 6), sign kept.
+    Returns the dequantized Fractions."""
+    out = []
+    for b0 in range(0, len(values), 32):
+        blk = values[b0:b0 + 32]
+        amax = max(abs(v) for v in blk)
+        X = -125 if amax == 0 else min(max(_bf_floor_log2(amax) - 2, -125), 125)
+        sc = Fraction(2) ** X
+        for v in blk:
+            q = abs(v) / sc
+            best = None
+            for c, m in enumerate(E2M1_MAGS):
+                d = abs(q - m)
+                if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+                    best = (d, c)
+            mag = E2M1_MAGS[best[1]] * sc
+            out.append(-mag if v < 0 else mag)
+    return out
+
+
 def _silu(z):
     return z / (1.0 + math.exp(-z))
 
@@ -101,6 +137,8 @@ def _bf_moe(x_bits, logits, L, k, act_mode):
     if act_mode == ACT_FP8_E4M3:
         flat = _bf_quant([v for row in x for v in row])
         x = [flat[t * H:(t + 1) * H] for t in range(T)]
+    elif act_mode == ACT_MXFP4:
+        x = [_bf_mx_quant(row) for row in x]
     routes = []
     for t in range(T):
         order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
@@ -119,6 +157,8 @@ def _bf_moe(x_bits, logits, L, k, act_mode):
         keys = sorted(hs)
         flat = _bf_quant([_bf_rn_f32(Fraction(v)) for key in keys for v in hs[key]])
         hs = {key: flat[i * I:(i + 1) * I] for i, key in enumerate(keys)}
+    elif act_mode == ACT_MXFP4:
+        hs = {key: _bf_mx_quant([_bf_rn_f32(Fraction(v)) for v in val]) for key, val in hs.items()}
     else:
         hs = {key: [Fraction(v) for v in val] for key, val in hs.items()}
     out = np.zeros((T, H))
@@ -188,13 +228,32 @@ def test_permute_matches_loops():
 # -------------------------------------------------------------- moe and linear
 
 
-@pytest.mark.parametrize("act_mode", [ACT_BF16, ACT_FP8_E4M3])
+@pytest.mark.parametrize("act_mode", [ACT_BF16, ACT_FP8_E4M3, ACT_MXFP4])
 def test_moe_forward_matches_exact_brute_force(act_mode):
     L, logits, x = _tiny()
     res = oracle.moe_forward(x, logits, **L, k=2, act_mode=act_mode)
     bf = _bf_moe(x, logits, L, 2, act_mode)
     scale = np.sqrt(np.mean(bf ** 2))
     assert np.max(np.abs(res["out"] - bf)) <= 1e-12 * scale * 64
+
+
+def test_mxfp4_activation_mode_passes_representable_x_unchanged():
+    # x made of MXFP4 values: quantising it again changes nothing, so the
+    # gate_up outputs (and h) equal those of the bf16 mode exactly; the
+    # down inputs do differ (h itself is not representable)
+    E, H, I, T = 4, 96, 64, 6
+    L = synth.layer(seed=41, E=E, H=H, I=I)
+    rng = np.random.default_rng(42)
+    xb = rng.integers(0, 256, size=(T, H // 32, 16), dtype=np.uint8)
+    xs = rng.integers(120, 131, size=(T, H // 32), dtype=np.uint8)
+    x = synth.f32_to_bf16_bits(oracle.dequant(xb, xs).astype(np.float32))
+    logits, _ = synth.moe_inputs(43, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, 2)
+    mx = oracle.moe_forward_routed(x, ids, w, **L, act_mode=ACT_MXFP4)
+    bf = oracle.moe_forward_routed(x, ids, w, **L, act_mode=ACT_BF16)
+    assert np.array_equal(mx["h"], bf["h"])
+    assert np.array_equal(oracle.dequant(mx["x_blocks"], mx["x_scales"]), oracle.bf16_bits_to_f64(x))
+    assert not np.array_equal(mx["out"], bf["out"])
 
 
 def test_swiglu_takes_silu_of_the_gate_half():
