@@ -37,6 +37,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0        # dense MFMA, FP8 (the FP8 x FP4 instruction's operand rate)
 MXFP4_PEAK_TFLOPS = 10100.0     # dense MFMA, FP4 / FP6
 PRIMARY = "moe_decode_t32"
+ACT_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "mxfp4"}
 FLUSH_BYTES = 1 << 30
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
@@ -56,7 +57,8 @@ def moe_accounting(ids, T, H, I, act):
     E = 128
     layer_bytes = touched * (gu + dn) + T * H * 2 + T * E * 4 + T * H * 2
     h_bytes = pairs * I * 4                     # bf16 hi+lo or fp32 h written
-    xin = T * H * (1 if act else 2)             # bf16 x or fp8 codes read
+    # bf16 x, E4M3 codes, or E2M1 codes + one scale byte per 32 read
+    xin = T * H * 2 if act == 0 else T * H if act == 1 else T * H * 17 // 32
     gemm1_bytes = touched * gu + xin + h_bytes
     gemm1_flops = 2.0 * pairs * 2 * I * H
     flops = 2.0 * pairs * (2 * I * H + H * I)
@@ -158,7 +160,7 @@ def measure_moe(run, Ld, name, synth, steps, warmup):
     g1 = stages["gemm1"]
     act = wl["act_mode"]
     res = dict(
-        tokens=wl["T"], act="fp8_e4m3" if act else "bf16", touched_experts=acct["touched"],
+        tokens=wl["T"], act=ACT_NAMES[act], touched_experts=acct["touched"],
         ms_per_step=mean, ms_p10=float(np.percentile(ms_plain, 10)),
         ms_p50=float(np.median(ms_plain)), ms_p90=float(np.percentile(ms_plain, 90)),
         layer_GBps=acct["layer_bytes"] / mean / 1e6,
@@ -371,10 +373,13 @@ def main():
         print("bench: quantiser %.1f us" % (others["quantize_lm_head"]["ms"] * 1e3), file=sys.stderr, flush=True)
 
     fp8 = prim["act"] != "bf16"
-    kname = "prefill_gemm_kernel<true, 128>" if fp8 else "gemv_persist_kernel<0, 12>"
+    fp4 = prim["act"] == "mxfp4"
+    kname = ("prefill_gemm_kernel<true, 128, true>" if fp4 else "prefill_gemm_kernel<true, 128, false>"
+             if fp8 else "gemv_persist_kernel<0, 12, false>")
     if fp8 and prim["tokens"] >= 4096:
-        roof = dict(bound="mfma", achieved=prim["gemm1_TFLOPs"], peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=prim["gemm1_TFLOPs"] / FP8_PEAK_TFLOPS)
+        peak = MXFP4_PEAK_TFLOPS if fp4 else FP8_PEAK_TFLOPS
+        roof = dict(bound="mfma", achieved=prim["gemm1_TFLOPs"], peak=peak, unit="TFLOP/s",
+                    frac=prim["gemm1_TFLOPs"] / peak)
     else:
         roof = dict(bound="hbm", achieved=prim["gemm1_GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=prim["gemm1_GBps"] / HBM_PEAK_GBS)
@@ -391,7 +396,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "dtype": prim["act"],
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": prim["tokens"], "experts": 128, "topk": 4,
                    "hidden": 2880, "intermediate": 2880, "weights": "mxfp4", "act": prim["act"],

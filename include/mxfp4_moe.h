@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 1
+#define MXFP4_ABI_VERSION 2
 
 /* Status codes.  0 is success; every failure leaves outputs untouched. */
 enum {
@@ -60,18 +60,24 @@ enum {
 /* Activation precision of the MoE contraction. */
 enum {
   MXFP4_ACT_BF16 = 0,         /* x used as given (bf16), fp32 accumulation */
-  MXFP4_ACT_FP8_E4M3 = 1      /* x and the SwiGLU output h each quantised to
+  MXFP4_ACT_FP8_E4M3 = 1,     /* x and the SwiGLU output h each quantised to
                                  OCP FP8 E4M3 with one per-tensor fp32 scale
                                  amax/448; FP8 x FP4 block-scaled MFMA */
+  MXFP4_ACT_MXFP4 = 2         /* x and h each quantised to MXFP4 (E2M1 codes,
+                                 one E8M0 scale per 32-element block of a
+                                 row); FP4 x FP4 block-scaled MFMA (the
+                                 native FP4 x FP4 contraction the spark-vllm
+                                 page lists under "Performance
+                                 Optimizations") */
 };
 
 /* Stage boundaries at which mxfp4_moe_forward can record caller events. */
 enum {
   MXFP4_STAGE_BEGIN = 0,      /* before the first kernel */
   MXFP4_STAGE_PERMUTE = 1,    /* after the token-by-expert permutation */
-  MXFP4_STAGE_QUANT_X = 2,    /* after FP8 quantisation of x (FP8 mode) */
+  MXFP4_STAGE_QUANT_X = 2,    /* after quantisation of x (FP8, MXFP4 activations) */
   MXFP4_STAGE_GEMM1 = 3,      /* after gate_up GEMM + SwiGLU */
-  MXFP4_STAGE_QUANT_H = 4,    /* after FP8 quantisation of h (FP8 mode) */
+  MXFP4_STAGE_QUANT_H = 4,    /* after quantisation of h (FP8, MXFP4 activations) */
   MXFP4_STAGE_GEMM2 = 5,      /* after the down GEMM */
   MXFP4_STAGE_COMBINE = 6,    /* after the weighted combine (end) */
   MXFP4_NUM_STAGES = 7
@@ -102,14 +108,25 @@ typedef struct {
   uint64_t chunk_ranks;     /* int32 scratch of the permutation */
   uint64_t tiles;           /* int32 [4 * max_tiles]: (expert, first sorted row, end row, 0);
                                entries past the tile count have expert -1 */
-  uint64_t x_codes;         /* uint8 [T*k, H] E4M3 codes of x in sorted row order:
-                               row r holds token sorted_pairs[r] / k (FP8 mode;
-                               rows past expert_offsets[E] unused) */
+  uint64_t x_codes;         /* FP8 mode: uint8 [T*k, H] E4M3 codes of x in sorted
+                               row order: row r holds token sorted_pairs[r] / k
+                               (rows past expert_offsets[E] unused);
+                               MXFP4-activation mode: uint8 [T*k, H/32, 16]
+                               E2M1 blocks of x in the same row order */
   uint64_t h;               /* BF16 mode: bf16 hi [T*k, I] then bf16 lo [T*k, I]
-                               with h = hi + lo; FP8 mode: fp32 [T*k, I];
-                               rows in sorted order */
-  uint64_t h_codes;         /* uint8 [T*k, I] E4M3 codes of h (FP8 mode) */
+                               with h = hi + lo; FP8 and MXFP4-activation modes:
+                               fp32 [T*k, I]; rows in sorted order */
+  uint64_t h_codes;         /* FP8 mode: uint8 [T*k, I] E4M3 codes of h;
+                               MXFP4-activation mode: uint8 [T*k, I/32, 16]
+                               E2M1 blocks of h */
   uint64_t y;               /* fp32 [T*k, H] per-pair expert outputs, sorted rows */
+  uint64_t x_scales;        /* MXFP4-activation mode: uint8 [T*k, 4*ceil(H/128)]
+                               E8M0 scales of the x blocks, rows padded to whole
+                               128-element steps (pad bytes hold 127); 0 in the
+                               other modes */
+  uint64_t h_scales;        /* MXFP4-activation mode: uint8 [T*k, 4*ceil(I/128)]
+                               E8M0 scales of the h blocks, padded likewise;
+                               0 in the other modes */
 } mxfp4_moe_workspace_layout;
 
 /* Library ABI version (MXFP4_ABI_VERSION of the build). */
@@ -157,7 +174,13 @@ int mxfp4_moe_workspace_layout_query(int64_t T, int64_t H, int64_t I, int32_t E,
  * mode a_t and h' are the E4M3-dequantised values with per-tensor scales
  * s = fp32(amax/448) computed over all of x, and over all T*k*I values of h,
  * codes = E4M3 round-to-nearest-even, saturating, of the correctly rounded
- * fp32 quotient v / s.  W13 rows [0, I) are the gate rows, [I, 2I) the up rows.
+ * fp32 quotient v / s.  In MXFP4_ACT_MXFP4 mode a_t and h' are the
+ * MXFP4-dequantised values, each 32-element block of a row of x (and of each
+ * pair's fp32 h) quantised on its own: shared exponent X = floor(log2 amax)
+ * - 2 clamped to [-125, 125], codes = the E2M1 value nearest to |v| / 2^X
+ * (ties to the even code, saturating at 6), sign kept (the rule of
+ * mxfp4_quantize_weights).  W13 rows [0, I) are the gate rows, [I, 2I) the up
+ * rows.
  *
  *   x            bf16 [T, H]                 16-byte aligned
  *   topk_ids     int32 [T, k]                values in [0, E); a pair with an
@@ -170,7 +193,7 @@ int mxfp4_moe_workspace_layout_query(int64_t T, int64_t H, int64_t I, int32_t E,
  *   w2_blocks    uint8 [E, H, I/32, 16]      16-byte aligned
  *   w2_scales    uint8 [E, H, I/32]       4-byte aligned
  *   w2_bias      bf16 [E, H] or NULL, 8-byte aligned
- *   act_mode     MXFP4_ACT_BF16 or MXFP4_ACT_FP8_E4M3
+ *   act_mode     MXFP4_ACT_BF16, MXFP4_ACT_FP8_E4M3 or MXFP4_ACT_MXFP4
  *   out          bf16 [T, H]                 16-byte aligned, must not alias
  *                                            any input or the workspace
  *   workspace    >= mxfp4_moe_workspace_size() bytes, 256-byte aligned
@@ -178,7 +201,7 @@ int mxfp4_moe_workspace_layout_query(int64_t T, int64_t H, int64_t I, int32_t E,
  * Limits: H, I positive multiples of 32 (<= 65536); 1 <= E <= 512;
  * 1 <= k <= min(E, 16); 0 <= T <= 2^22 (T == 0 is a no-op).  In MXFP4_ACT_BF16 mode, E8M0 scale bytes must
  * lie in [2, 252] (the weight is formed exactly in bf16 before the MFMA); the
- * FP8 mode accepts every byte except 255.
+ * FP8 and MXFP4-activation modes accept every byte except 255.
  */
 int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E,
                       int32_t k, const int32_t* topk_ids, const float* topk_weights,

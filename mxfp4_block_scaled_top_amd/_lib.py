@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(_PKG, "libmxfp4moe.so")
 
 ACT_BF16 = 0
 ACT_FP8_E4M3 = 1
+ACT_MXFP4 = 2
+ABI_VERSION = 2
 NUM_STAGES = 7
 STAGES = ("begin", "permute", "quant_x", "gemm1", "quant_h", "gemm2", "combine")
 
@@ -26,7 +28,8 @@ _i32 = ctypes.c_int32
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "total_bytes", "status", "expert_offsets", "sorted_pairs", "inv_pairs",
-        "chunk_counts", "chunk_ranks", "tiles", "x_codes", "h", "h_codes", "y")]
+        "chunk_counts", "chunk_ranks", "tiles", "x_codes", "h", "h_codes", "y", "x_scales",
+        "h_scales")]
 
 
 class MoeOpts(ctypes.Structure):
@@ -50,6 +53,9 @@ def lib():
             raise RuntimeError("libmxfp4moe.so is not built (run __graft_entry__.build()): %s" % LIB_PATH)
         L = ctypes.CDLL(LIB_PATH)
         L.mxfp4_abi_version.restype = ctypes.c_int
+        if L.mxfp4_abi_version() != ABI_VERSION:
+            raise RuntimeError("libmxfp4moe.so has ABI version %d, the binding expects %d (rebuild it)"
+                               % (L.mxfp4_abi_version(), ABI_VERSION))
         L.mxfp4_status_string.restype = ctypes.c_char_p
         L.mxfp4_status_string.argtypes = [ctypes.c_int]
         L.mxfp4_last_error.restype = ctypes.c_char_p

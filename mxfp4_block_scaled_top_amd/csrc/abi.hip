@@ -57,7 +57,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int moe_shape_check(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mode) {
-  if (act_mode != MXFP4_ACT_BF16 && act_mode != MXFP4_ACT_FP8_E4M3)
+  if (act_mode != MXFP4_ACT_BF16 && act_mode != MXFP4_ACT_FP8_E4M3 && act_mode != MXFP4_ACT_MXFP4)
     return fail(MXFP4_E_MODE, "unknown act_mode %d", act_mode);
   if (T < 0 || T > (1 << 22)) return fail(MXFP4_E_SHAPE, "T=%lld outside [0, 2^22]", (long long)T);
   if (H <= 0 || H % 32 || H > (1 << 16)) return fail(MXFP4_E_SHAPE, "H=%lld must be a positive multiple of 32 (<= 65536)", (long long)H);
@@ -88,6 +88,12 @@ void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mod
     L->x_codes = o; o = up(o + (size_t)np * H);
     L->h = o; o = up(o + (size_t)np * I * 4);
     L->h_codes = o; o = up(o + (size_t)np * I);
+  } else if (act_mode == MXFP4_ACT_MXFP4) {
+    L->x_codes = o; o = up(o + (size_t)np * H / 2);
+    L->x_scales = o; o = up(o + (size_t)np * mx::act_scale_stride((int)H));
+    L->h = o; o = up(o + (size_t)np * I * 4);
+    L->h_codes = o; o = up(o + (size_t)np * I / 2);
+    L->h_scales = o; o = up(o + (size_t)np * mx::act_scale_stride((int)I));
   } else {
     L->x_codes = o;
     L->h = o; o = up(o + (size_t)np * I * 2 * 2);
@@ -111,6 +117,8 @@ mx::WsPtrs ws_ptrs(void* base, const mxfp4_moe_workspace_layout& L) {
   w.h = b + L.h;
   w.h_codes = b + L.h_codes;
   w.y = reinterpret_cast<float*>(b + L.y);
+  w.x_scales = b + L.x_scales;
+  w.h_scales = b + L.h_scales;
   return w;
 }
 
@@ -228,7 +236,8 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
     w.w2_global = nv_globals[1];
   }
   const bool fp8 = act_mode == MXFP4_ACT_FP8_E4M3;
-  const int bm = fp8 ? mx::kPrefillBM : mx::kDecodeBM;
+  const bool a4 = act_mode == MXFP4_ACT_MXFP4;
+  const int bm = act_mode == MXFP4_ACT_BF16 ? mx::kDecodeBM : mx::kPrefillBM;
   const int64_t npairs = T * k;
   const int64_t bound = mx::max_tiles(npairs, E, bm);
 
@@ -260,9 +269,12 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
     MX_STEP(mx::launch_amax(x, true, T * H, reinterpret_cast<uint32_t*>(ws.status + mx::kStAmaxX), s),
             "amax x launch");
     MX_STEP(mx::launch_encode_sorted_rows(x, sh, ws, s), "quant x launch");
+  } else if (a4) {
+    MX_STEP(mx::launch_quant_x_mxfp4_sorted(x, sh, ws, s), "quant x launch");
   }
   MX_STEP(mark(MXFP4_STAGE_QUANT_X), "event record");
   if (fp8) MX_STEP(mx::launch_moe_gateup_fp8(sh, w, ws, bound, s), "gate_up launch");
+  else if (a4) MX_STEP(mx::launch_moe_gateup_fp4(sh, w, ws, s), "gate_up launch");
   else MX_STEP(mx::launch_moe_gateup_bf16(x, sh, w, ws, bound, s), "gate_up launch");
   MX_STEP(mark(MXFP4_STAGE_GEMM1), "event record");
   if (fp8) {
@@ -270,9 +282,12 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
                                   reinterpret_cast<const uint32_t*>(ws.status + mx::kStAmaxH),
                                   reinterpret_cast<float*>(ws.status + mx::kStScaleH), s),
             "quant h launch");
+  } else if (a4) {
+    MX_STEP(mx::launch_quant_h_mxfp4(sh, ws, s), "quant h launch");
   }
   MX_STEP(mark(MXFP4_STAGE_QUANT_H), "event record");
   if (fp8) MX_STEP(mx::launch_moe_down_fp8(sh, w, ws, bound, s), "down launch");
+  else if (a4) MX_STEP(mx::launch_moe_down_fp4(sh, w, ws, s), "down launch");
   else MX_STEP(mx::launch_moe_down_bf16(sh, w, ws, bound, s), "down launch");
   MX_STEP(mark(MXFP4_STAGE_GEMM2), "event record");
   MX_STEP(mx::launch_combine(sh, topk_weights, ws, out, s), "combine launch");

@@ -24,7 +24,9 @@
 //     tile (up to BM expert-sorted rows of one expert, from the tile list the
 //     permutation builds) times one n-tile of 256 weight rows (gate_up: 128
 //     gate rows and the matching 128 up rows).  Block b takes units b, b + G,
-//     b + 2G, ...; a unit is nsteps K steps of 128.
+//     b + 2G, ...; a unit is nsteps K steps of 128.  (Placing the n-tiles of
+//     one row tile on one XCD, to share its activations in that XCD's L2, made
+//     no measurable difference.)
 //   * Every K step's activations (BM x 128 B of E4M3 codes, rows in
 //     expert-sorted order), weights (256 x 64 B of E2M1) and E8M0 scales are
 //     copied from global memory into one slot of an LDS ring by DMA (global ->
@@ -60,23 +62,35 @@ constexpr int kBK = 128;               // K per step (four MX blocks)
 constexpr int kWTile = kBN * kBK / 2;  // E2M1 bytes per step
 constexpr int kScTile = kBN * 8;       // two aligned scale dwords per weight row
 
-template <int BM>
+// A4: MXFP4 activations (64 B of E2M1 codes per row per step, the geometry
+// of a weight row, plus one dword of four E8M0 scales per row); otherwise
+// E4M3 activations (128 B per row per step).
+template <int BM, bool A4 = false>
 struct Ring {
   static constexpr int kWaves = BM / 16;                // each 64 sorted rows x 64 weight rows
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kStages = BM == 128 ? 4 : 6;
-  static constexpr int kAct = BM * kBK;                 // activation bytes per slot
+  static constexpr int kStages = A4 ? 5 : BM == 128 ? 4 : 6;
+  static constexpr int kActRow = A4 ? kBK / 2 : kBK;    // activation bytes per row per step
+  static constexpr int kAct = BM * kActRow;             // activation bytes per slot
   static constexpr int kW = kAct;                       // offsets inside a slot
   static constexpr int kSc = kAct + kWTile;
-  static constexpr int kSlot = kSc + kScTile;
-  static constexpr int kActDma = BM / 8 / kWaves;       // 1 KB activation DMAs per wave per step
+  static constexpr int kASc = kSc + kScTile;            // A4: activation scales, 4 B per row
+  static constexpr int kSlot = kASc + (A4 ? BM * 4 : 0);
+  static constexpr int kActDma = BM * kActRow / 1024 / kWaves;  // 1 KB activation DMAs per wave per step
   static constexpr int kWDma = 16 / kWaves;             // 1 KB weight DMAs per wave per step
   static constexpr int kScDma = 8 / kWaves;             // 256 B scale DMAs per wave per step
-  static constexpr int kDma = kActDma + kWDma + kScDma; // DMA instructions per wave per step
-  static_assert(kActDma * kWaves * 8 == BM && kScDma >= 1, "copies split over the waves");
+  static constexpr int kAScDma = A4 ? 1 : 0;            // 256 B activation-scale DMAs per wave per step
+  static constexpr int kDma = kActDma + kWDma + kScDma + kAScDma;  // DMA instructions per wave per step
+  // A4: waves 0 and 1 copy the 128 rows' scale dwords; the other waves issue
+  // the same copy into this 256 B sink, so that every wave counts the same
+  // number of copies per step
+  static constexpr int kSink = kStages * kSlot;
+  static constexpr int kLds = kSink + (A4 ? 256 : 0);
+  static_assert(kActDma * kWaves * 1024 == BM * kActRow && kScDma >= 1, "copies split over the waves");
+  static_assert(!A4 || BM == 128, "two waves of 64 lanes copy the activation scales");
   static_assert((kStages - 2) * kDma <= 63, "vector-memory count range");
   static_assert(kStages - 2 <= 4, "waits cover up to four steps ahead");
-  static_assert(kStages * kSlot <= 160 * 1024, "LDS");
+  static_assert(kLds <= 160 * 1024, "LDS");
 };
 
 struct PrefillArgs {
@@ -90,8 +104,11 @@ struct PrefillArgs {
   int K;
   int NT;                  // n-tiles
   int nsteps;              // ceil(nb / 4)
-  const uint8_t* act;      // [sorted rows, K] E4M3 codes
-  int scale_word;          // status word holding the activation scale
+  const uint8_t* act;      // [sorted rows, K] E4M3 codes, or [sorted rows, K/32, 16] E2M1 blocks
+  int act_ld;              // activation bytes per row (K, or K/2 for E2M1)
+  const uint8_t* asc;      // E2M1 activations: E8M0 [sorted rows, nbp]
+  int nbp;                 // activation scale bytes per row (a multiple of 4)
+  int scale_word;          // status word holding the per-tensor activation scale (E4M3)
   float* out;              // h [rows, I] (gate_up) or y [rows, H] (down), fp32
 };
 
@@ -170,9 +187,14 @@ __device__ __forceinline__ float bf16_of(uint2 q, int jj) {
 // 16j + lane/4, slot lane%4, which holds MX block (lane%4) ^ ((row/2)%4).
 // Scale DMA i fills rows 32j..32j+31: lane -> row 32j + lane/2, aligned dword
 // lane%2 of the 8 bytes that hold the row's four scales of the step.
-template <bool GATEUP, int BM>
+//
+// A4 (E2M1 activations): activation DMA i fills slot rows 16j..16j+15 like a
+// weight DMA (lane -> row 16j + lane/4, slot lane%4 holding MX block
+// (lane%4) ^ ((row/2)%4)); the scale DMA of wave w < 2 fills the scale dwords
+// of rows 64w .. 64w+63 (one per lane), the other waves' go to the sink.
+template <bool GATEUP, int BM, bool A4 = false>
 struct PrefillCopier {
-  using C = Ring<BM>;
+  using C = Ring<BM, A4>;
   static constexpr int NW = C::kWaves;
   const int* tiles;
   uint8_t* smem;
@@ -181,13 +203,14 @@ struct PrefillCopier {
   const uint8_t* aptr[C::kActDma];
   const uint8_t* wptr[C::kWDma];
   int64_t sofs[C::kScDma];
+  const uint8_t* ascp;  // A4: this lane's activation-scale row
   int k, step, slot;    // next copy: local unit, step, ring slot
 
   __device__ __forceinline__ void init(const PrefillArgs& a, const int* t, uint8_t* sm, int w, int lane, int first,
                                        int grid, int units) {
     tiles = t; smem = sm; wave = w; u0 = first; G = grid; my_units = units;
-    a_row = lane >> 3;
-    a_chunk = (lane & 7) ^ a_row;
+    a_row = A4 ? lane >> 2 : lane >> 3;
+    a_chunk = A4 ? (lane & 3) ^ ((lane >> 3) & 3) : (lane & 7) ^ a_row;
     w_row = lane >> 2;
     w_blk = (lane & 3) ^ ((lane >> 3) & 3);
     s_row = lane >> 1;
@@ -202,9 +225,14 @@ struct PrefillCopier {
     const int3 te = tile_entry(tiles + kTileInts * tile);
 #pragma unroll
     for (int i = 0; i < C::kActDma; ++i) {
-      int row = te.y + 8 * (NW * i + wave) + a_row;
+      int row = te.y + (A4 ? 16 : 8) * (NW * i + wave) + a_row;
       row = row < te.z ? row : te.y;
-      aptr[i] = a.act + (int64_t)row * a.K;
+      aptr[i] = a.act + (int64_t)row * a.act_ld;
+    }
+    if (A4) {
+      int row = te.y + 64 * (wave & 1) + (int)(threadIdx.x & 63);
+      row = row < te.z ? row : te.y;
+      ascp = a.asc + (int64_t)row * a.nbp;
     }
     const int64_t ebase = (int64_t)te.x * a.R;
 #pragma unroll
@@ -226,9 +254,15 @@ struct PrefillCopier {
     const int kb = step * kBK;
 #pragma unroll
     for (int i = 0; i < C::kActDma; ++i) {
-      const int off = kb + 16 * a_chunk;           // past K: the row's first 16 bytes
-      __builtin_amdgcn_global_load_lds(aptr[i] + (!tail || off < a.K ? off : 0), dst + 1024 * (NW * i + wave),
-                                       16, 0, 0);
+      if (A4) {
+        const int blk = 4 * step + a_chunk;        // past K: the row's first block
+        __builtin_amdgcn_global_load_lds(aptr[i] + (!tail || blk < a.nb ? blk * kBlockBytes : 0),
+                                         dst + 1024 * (NW * i + wave), 16, 0, 0);
+      } else {
+        const int off = kb + 16 * a_chunk;         // past K: the row's first 16 bytes
+        __builtin_amdgcn_global_load_lds(aptr[i] + (!tail || off < a.K ? off : 0), dst + 1024 * (NW * i + wave),
+                                         16, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
@@ -242,6 +276,9 @@ struct PrefillCopier {
       q = q < a.sc_total - 4 ? q : a.sc_total - 4;
       __builtin_amdgcn_global_load_lds(a.ws + q, dst + C::kSc + 256 * (NW * i + wave), 4, 0, 0);
     }
+    if (A4)   // the step's four scales of the row: one aligned dword of the padded row
+      __builtin_amdgcn_global_load_lds(ascp + 4 * step, wave < 2 ? dst + C::kASc + 256 * wave : smem + C::kSink,
+                                       4, 0, 0);
     slot = slot + 1 == C::kStages ? 0 : slot + 1;
     if (++step == a.nsteps) {
       step = 0;
@@ -327,14 +364,57 @@ __device__ __forceinline__ void lds_wait_rest(v4u_t& xb0, v4u_t& xb1, v4u_t& xb2
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xb0), "+v"(xb1), "+v"(xb2), "+v"(xb3));
 }
 
-template <bool GATEUP, int BM>
-__global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(PrefillArgs a,
-                                                                          const int* __restrict__ tiles,
-                                                                          int* status) {
-  using C = Ring<BM>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kSlot];
+// A4 step reads: 4 activation blocks (token groups at LDS rows +0, +16, +32,
+// +48), the 4 weight blocks and weight scales as in lds_step_reads, and the
+// 4 activation scale bytes, in one assembly block with its own wait.
+template <bool GATEUP>
+__device__ __forceinline__ void lds_step_reads_a4(uint32_t aa, uint32_t ww, uint32_t ss, uint32_t as,
+                                                  v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3,
+                                                  v4u_t& wq0, v4u_t& wq1, v4u_t& wq2, v4u_t& wq3,
+                                                  uint32_t& sb0, uint32_t& sb1, uint32_t& sb2, uint32_t& sb3,
+                                                  uint32_t& ab0, uint32_t& ab1, uint32_t& ab2, uint32_t& ab3) {
+  if (GATEUP) {
+    asm volatile("ds_read_u8 %8, %18\n\tds_read_u8 %9, %18 offset:128\n\t"
+                 "ds_read_u8 %10, %18 offset:1024\n\tds_read_u8 %11, %18 offset:1152\n\t"
+                 "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
+                 "ds_read_u8 %14, %19 offset:128\n\tds_read_u8 %15, %19 offset:192\n\t"
+                 "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:1024\n\t"
+                 "ds_read_b128 %6, %17 offset:8192\n\tds_read_b128 %7, %17 offset:9216\n\t"
+                 "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:1024\n\t"
+                 "ds_read_b128 %2, %16 offset:2048\n\tds_read_b128 %3, %16 offset:3072\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(wq0), "=&v"(wq1), "=&v"(wq2),
+                   "=&v"(wq3), "=&v"(sb0), "=&v"(sb1), "=&v"(sb2), "=&v"(sb3), "=&v"(ab0), "=&v"(ab1),
+                   "=&v"(ab2), "=&v"(ab3)
+                 : "v"(aa), "v"(ww), "v"(ss), "v"(as));
+  } else {
+    asm volatile("ds_read_u8 %8, %18\n\tds_read_u8 %9, %18 offset:128\n\t"
+                 "ds_read_u8 %10, %18 offset:256\n\tds_read_u8 %11, %18 offset:384\n\t"
+                 "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
+                 "ds_read_u8 %14, %19 offset:128\n\tds_read_u8 %15, %19 offset:192\n\t"
+                 "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:1024\n\t"
+                 "ds_read_b128 %6, %17 offset:2048\n\tds_read_b128 %7, %17 offset:3072\n\t"
+                 "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:1024\n\t"
+                 "ds_read_b128 %2, %16 offset:2048\n\tds_read_b128 %3, %16 offset:3072\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(wq0), "=&v"(wq1), "=&v"(wq2),
+                   "=&v"(wq3), "=&v"(sb0), "=&v"(sb1), "=&v"(sb2), "=&v"(sb3), "=&v"(ab0), "=&v"(ab1),
+                   "=&v"(ab2), "=&v"(ab3)
+                 : "v"(aa), "v"(ww), "v"(ss), "v"(as));
+  }
+}
+
+// A4: E2M1 activations with E8M0 block scales; both operands of the
+// block-scaled MFMA are FP4 and carry their own scales, and the epilogue has
+// no per-tensor factor.
+template <bool GATEUP, int BM, bool A4 = false>
+__global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(PrefillArgs a,
+                                                                              const int* __restrict__ tiles,
+                                                                              int* status) {
+  using C = Ring<BM, A4>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
   const int num_units = status[kStNumTiles] * a.NT;
-  const float sx = __uint_as_float((uint32_t)status[a.scale_word]);
+  const float sx = A4 ? 1.0f : __uint_as_float((uint32_t)status[a.scale_word]);
   const int G = gridDim.x;
   const int u0 = blockIdx.x;
   if (u0 >= num_units) return;
@@ -343,7 +423,7 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
-  PrefillCopier<GATEUP, BM> cp;
+  PrefillCopier<GATEUP, BM, A4> cp;
   cp.init(a, tiles, smem, wave, lane, u0, G, my_units);
 
   // ---------------- compute: 64 sorted rows x 64 weight rows ----------------
@@ -367,6 +447,11 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
   const uint32_t a1 = lds0 + (64 * wm + r) * kBK + 16 * c1;
   const uint32_t w0 = lds0 + C::kW + lrow0 * 64 + 16 * wslot;
   const uint32_t s0 = lds0 + C::kSc + lrow0 * 8 + sphase + g;
+  // A4: activation block g of token row 64 wm + r sits in slot wslot (the
+  // rows' swizzle phase (row/2)%4 is that of r), its scale at byte g of the
+  // row's dword
+  const uint32_t ax0 = lds0 + (64 * wm + r) * 64 + 16 * wslot;
+  const uint32_t as0 = lds0 + C::kASc + (64 * wm + r) * 4 + g;
 
   int cstep = 0, cslot = 0, ck = 0;
   int e = 0, rb = 0, re = 0, nt = 0;
@@ -434,55 +519,85 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
     const uint32_t aa0 = a0 + so, aa1 = a1 + so, ww = w0 + so, ss = s0 + so;
     v4u_t xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3;
     uint32_t sb0, sb1, sb2, sb3;
-    if (GATEUP) {
-      lds_step_issue_gateup(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3, sb0,
-                            sb1, sb2, sb3);
-      lds_wait_first(xa0, xa1, xa2, xa3, wq0, wq1, wq2, wq3, sb0, sb1, sb2, sb3);
-    } else {
-      lds_step_reads<GATEUP>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3,
-                             sb0, sb1, sb2, sb3);
-    }
-    const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
-    const v4u_t wq[4] = {wq0, wq1, wq2, wq3};
-    const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
-    const bool valid = 4 * cstep + g < a.nb;        // this lane's MX block lies inside K
-    if (GATEUP) {
-      // lane group g holds K [32g, 32g+32) of the step (its own MX block);
-      // MFMA q takes elements 8q..8q+7 of it, in the same order for both
-      // operands; MFMAs 2-3 use the chunks read last
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
-        const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
-        v8bf B[4];
-#pragma unroll
-        for (int tg = 0; tg < 4; ++tg) {
-          const v4u_t c = q < 2 ? xa[tg] : xb[tg];
-          B[tg] = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
-        }
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
-          const v8bf A = fp4x8_to_bf16(wq[rg][q], f);
-#pragma unroll
-          for (int tg = 0; tg < 4; ++tg)
-            acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[tg], acc[rg][tg], 0, 0, 0);
-        }
-      }
-    } else {
-      const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
+    if constexpr (A4) {
+      uint32_t ab0, ab1, ab2, ab3;
+      lds_step_reads_a4<GATEUP>(ax0 + so, ww, ss, as0 + so, xa0, xa1, xa2, xa3, wq0, wq1, wq2, wq3, sb0, sb1,
+                                sb2, sb3, ab0, ab1, ab2, ab3);
+      const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
+      const v4u_t wq[4] = {wq0, wq1, wq2, wq3};
+      const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
+      const uint32_t ab[4] = {ab0, ab1, ab2, ab3};
+      // lane group g holds MX block g of the step in both operands; past K the
+      // weights are zero and both scales 2^0
+      const bool valid = 4 * cstep + g < a.nb;
       v8i B[4];
+      int bsc[4];
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg)
-        B[tg] = __builtin_bit_cast(v8i, __builtin_shufflevector(xa[tg], xb[tg], 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int tg = 0; tg < 4; ++tg) {
+        B[tg] = v8i{(int)xa[tg].x, (int)xa[tg].y, (int)xa[tg].z, (int)xa[tg].w, 0, 0, 0, 0};
+        bsc[tg] = valid ? (int)ab[tg] : 127;
+      }
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
         const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
+        const int asc = valid ? (int)sb[rg] : 127;
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg)
-          acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 0, 0,
-                                                                         (int)sb[rg], 0, 127);
+          acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 4, 0, asc, 0,
+                                                                         bsc[tg]);
+      }
+    } else {
+      if (GATEUP) {
+        lds_step_issue_gateup(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3, sb0,
+                              sb1, sb2, sb3);
+        lds_wait_first(xa0, xa1, xa2, xa3, wq0, wq1, wq2, wq3, sb0, sb1, sb2, sb3);
+      } else {
+        lds_step_reads<GATEUP>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3,
+                               sb0, sb1, sb2, sb3);
+      }
+      const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
+      const v4u_t wq[4] = {wq0, wq1, wq2, wq3};
+      const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
+      const bool valid = 4 * cstep + g < a.nb;        // this lane's MX block lies inside K
+      if (GATEUP) {
+        // lane group g holds K [32g, 32g+32) of the step (its own MX block);
+        // MFMA q takes elements 8q..8q+7 of it, in the same order for both
+        // operands; MFMAs 2-3 use the chunks read last
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
+          const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
+          v8bf B[4];
+#pragma unroll
+          for (int tg = 0; tg < 4; ++tg) {
+            const v4u_t c = q < 2 ? xa[tg] : xb[tg];
+            B[tg] = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
+          }
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
+            const v8bf A = fp4x8_to_bf16(wq[rg][q], f);
+#pragma unroll
+            for (int tg = 0; tg < 4; ++tg)
+              acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[tg], acc[rg][tg], 0, 0, 0);
+          }
+        }
+      } else {
+        const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
+        v8i B[4];
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg)
+          B[tg] = __builtin_bit_cast(v8i, __builtin_shufflevector(xa[tg], xb[tg], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
+          const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
+#pragma unroll
+          for (int tg = 0; tg < 4; ++tg)
+            acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 0, 0,
+                                                                           (int)sb[rg], 0, 127);
+        }
       }
     }
     cslot = cslot + 1 == C::kStages ? 0 : cslot + 1;
@@ -535,21 +650,22 @@ __global__ __launch_bounds__(Ring<BM>::kThreads) void prefill_gemm_kernel(Prefil
     cstep = 0;
     if (++ck < my_units) comp_setup(u0 + ck * G);
   }
-  if (GATEUP) {
+  if (GATEUP && !A4) {
     // max |h| over all of this wave's units: one atomic per wave
     amax = wave_max(amax);
     if (lane == 0) atomicMax(reinterpret_cast<uint32_t*>(&status[kStAmaxH]), __float_as_uint(amax));
   }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool A4 = false>
 static hipError_t launch_prefill(const PrefillArgs& a, const WsPtrs& ws, hipStream_t s) {
   // one block per compute unit: the LDS ring takes most of a unit's LDS
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  prefill_gemm_kernel<GATEUP, kPrefillBM><<<cus, Ring<kPrefillBM>::kThreads, 0, s>>>(a, ws.tiles, ws.status);
+  prefill_gemm_kernel<GATEUP, kPrefillBM, A4><<<cus, Ring<kPrefillBM, A4>::kThreads, 0, s>>>(a, ws.tiles,
+                                                                                            ws.status);
   return hipGetLastError();
 }
 
@@ -567,6 +683,7 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
   a.NT = (sh.I + kBN / 2 - 1) / (kBN / 2);
   a.nsteps = (a.nb + 3) / 4;
   a.act = ws.x_codes;
+  a.act_ld = sh.H;
   a.scale_word = kStScaleX;
   a.out = static_cast<float*>(ws.h);
   return launch_prefill<true>(a, ws, s);
@@ -586,9 +703,52 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
   a.NT = (sh.H + kBN - 1) / kBN;
   a.nsteps = (a.nb + 3) / 4;
   a.act = ws.h_codes;
+  a.act_ld = sh.I;
   a.scale_word = kStScaleH;
   a.out = ws.y;
   return launch_prefill<false>(a, ws, s);
+}
+
+hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, hipStream_t s) {
+  PrefillArgs a{};
+  a.wb = w.w13_blocks;
+  a.ws = w.w13_scales;
+  a.bias = w.w13_bias;
+  a.R = 2 * sh.I;
+  a.nout = sh.I;
+  a.nb = sh.H / kBlockElems;
+  a.K = sh.H;
+  a.sc_total = (int64_t)sh.E * a.R * a.nb;
+  a.NT = (sh.I + kBN / 2 - 1) / (kBN / 2);
+  a.nsteps = (a.nb + 3) / 4;
+  a.act = ws.x_codes;
+  a.act_ld = sh.H / 2;
+  a.asc = ws.x_scales;
+  a.nbp = act_scale_stride(sh.H);
+  a.scale_word = -1;
+  a.out = static_cast<float*>(ws.h);
+  return launch_prefill<true, true>(a, ws, s);
+}
+
+hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, hipStream_t s) {
+  PrefillArgs a{};
+  a.wb = w.w2_blocks;
+  a.ws = w.w2_scales;
+  a.bias = w.w2_bias;
+  a.R = sh.H;
+  a.nout = sh.H;
+  a.nb = sh.I / kBlockElems;
+  a.K = sh.I;
+  a.sc_total = (int64_t)sh.E * a.R * a.nb;
+  a.NT = (sh.H + kBN - 1) / kBN;
+  a.nsteps = (a.nb + 3) / 4;
+  a.act = ws.h_codes;
+  a.act_ld = sh.I / 2;
+  a.asc = ws.h_scales;
+  a.nbp = act_scale_stride(sh.I);
+  a.scale_word = -1;
+  a.out = ws.y;
+  return launch_prefill<false, true>(a, ws, s);
 }
 
 }  // namespace mx

@@ -10,7 +10,7 @@ namespace mx {
 constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to here
 constexpr int kFusedRouteMaxTokens = 32;     // single-block route + permute up to here
 constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
-constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 path
+constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 and FP4 x FP4 paths
 // A row tile is 4 ints: expert, first sorted row, end row (exclusive), 0.
 // Entries past the number of tiles (up to max_tiles) hold expert -1.
 constexpr int kTileInts = 4;
@@ -24,11 +24,17 @@ struct WsPtrs {
   int* chunk_counts;
   int* chunk_ranks;
   int* tiles;
-  uint8_t* x_codes;
-  void* h;          // bf16 hi|lo (BF16 mode) or fp32 (FP8 mode)
+  uint8_t* x_codes;  // FP8: E4M3 codes; MXFP4 activations: E2M1 blocks
+  void* h;           // bf16 hi|lo (BF16 mode) or fp32 (FP8 / MXFP4-activation modes)
   uint8_t* h_codes;
   float* y;
+  uint8_t* x_scales;  // MXFP4 activations: E8M0 [T*k, act_scale_stride(H)]
+  uint8_t* h_scales;  // MXFP4 activations: E8M0 [T*k, act_scale_stride(I)]
 };
+
+// E8M0 bytes per row of MXFP4 activations: the row's K/32 scales padded to
+// whole 128-element K steps, so each step's four are one aligned dword.
+inline int act_scale_stride(int K) { return 4 * ((K + 127) / 128); }
 
 // Upper bound of the number of (expert, row-tile) entries.
 inline int64_t max_tiles(int64_t npairs, int64_t E, int BM) {
@@ -90,6 +96,18 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
                                  int64_t ntile_bound, hipStream_t s);
 hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
                                int64_t ntile_bound, hipStream_t s);
+
+// MXFP4 activations: x in expert-sorted row order, and fp32 h (rows below
+// offsets[E]), each as E2M1 blocks + padded E8M0 scale rows.
+hipError_t launch_quant_x_mxfp4_sorted(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
+                                       hipStream_t s);
+hipError_t launch_quant_h_mxfp4(const MoeShape& sh, const WsPtrs& ws, hipStream_t s);
+
+// FP4 x FP4 block-scaled MFMA path (MXFP4 activations).
+hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
+                                 hipStream_t s);
+hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
+                               hipStream_t s);
 
 // bf16 [nblocks * 32] -> MXFP4 blocks [nblocks, 16] + E8M0 scales [nblocks]
 hipError_t launch_quant_mxfp4(const uint16_t* w, int64_t nblocks, uint8_t* blocks, uint8_t* scales,

@@ -68,6 +68,115 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 activations (FP4 x FP4 MoE mode): the same block rule on x (bf16) and
+// on the SwiGLU output h (fp32).  Scale rows are padded to whole 128-element
+// K steps (act_scale_stride) so that a step's four scales of a row are one
+// aligned dword; pad bytes hold 127 (2^0).
+
+// 32 finite fp32 values -> E2M1 nibbles (element 2i in the low nibble of
+// byte i) and the E8M0 byte.  For fp32, floor(log2 amax) is the exponent
+// field - 127 for a normal amax; zero and subnormal blocks land below the
+// clamp.  |v| * 2^-X is exact (a power-of-two scaling that stays below 8).
+__device__ __forceinline__ uint32_t mx_encode32(const float* v, uint4& out) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7fffffffu);
+  const int x = min(max((int)(amax >> 23) - 127 - 2, -125), 125);
+  const float inv = __uint_as_float((uint32_t)(127 - x) << 23);
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const uint32_t bits = __float_as_uint(v[e]);
+    const float q = __uint_as_float(bits & 0x7fffffffu) * inv;
+    packed[e >> 3] |= (e2m1_round_mag(q) | ((bits >> 31) << 3)) << (4 * (e & 7));
+  }
+  out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  return (uint32_t)(x + 127);
+}
+
+// One thread per (token, scale slot c < nbp): block c of the token's row
+// (c < H/32) or a pad byte, written to every sorted row the token's pairs
+// occupy (inv[t*k + j] >= 0).
+__global__ __launch_bounds__(256) void quant_x_mxfp4_sorted_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int k, int nbp, const int* __restrict__ inv,
+    uint8_t* __restrict__ xb, uint8_t* __restrict__ xs) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * nbp) return;
+  const int t = (int)(idx / nbp), c = (int)(idx - (int64_t)t * nbp);
+  const bool real = c < H / kBlockElems;
+  uint4 packed = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t sc = 127u;
+  if (real) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * H + c * kBlockElems);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 q = src[i];
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = bf16_bits_to_f32(w[j] & 0xffffu);
+        v[8 * i + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+      }
+    }
+    sc = mx_encode32(v, packed);
+  }
+  for (int j = 0; j < k; ++j) {
+    const int r = inv[(int64_t)t * k + j];
+    if (r < 0) continue;
+    if (real) *reinterpret_cast<uint4*>(xb + (int64_t)r * (H / 2) + c * kBlockBytes) = packed;
+    xs[(int64_t)r * nbp + c] = (uint8_t)sc;
+  }
+}
+
+// One thread per (sorted row r < offsets[E], scale slot c < nbp) of fp32 h.
+__global__ __launch_bounds__(256) void quant_h_mxfp4_kernel(const float* __restrict__ h, int64_t rows,
+                                                            int I, int nbp, const int* __restrict__ nvalid,
+                                                            uint8_t* __restrict__ hb,
+                                                            uint8_t* __restrict__ hs) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * nbp) return;
+  const int64_t r = idx / nbp;
+  const int c = (int)(idx - r * nbp);
+  if (r >= *nvalid) return;
+  uint32_t sc = 127u;
+  if (c < I / kBlockElems) {
+    const float4* src = reinterpret_cast<const float4*>(h + r * I + c * kBlockElems);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 q = src[i];
+      v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+    }
+    uint4 packed;
+    sc = mx_encode32(v, packed);
+    *reinterpret_cast<uint4*>(hb + r * (I / 2) + c * kBlockBytes) = packed;
+  }
+  hs[r * nbp + c] = (uint8_t)sc;
+}
+
+hipError_t launch_quant_x_mxfp4_sorted(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
+                                       hipStream_t s) {
+  const int nbp = act_scale_stride(sh.H);
+  const int64_t n = (int64_t)sh.T * nbp;
+  if (n <= 0) return hipSuccess;
+  quant_x_mxfp4_sorted_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, sh.T, sh.H, sh.k, nbp, ws.inv,
+                                                                          ws.x_codes, ws.x_scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_h_mxfp4(const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
+  const int nbp = act_scale_stride(sh.I);
+  const int64_t rows = (int64_t)sh.T * sh.k;
+  const int64_t n = rows * nbp;
+  if (n <= 0) return hipSuccess;
+  quant_h_mxfp4_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<const float*>(ws.h), rows, sh.I,
+                                                                   nbp, ws.offsets + sh.E, ws.h_codes,
+                                                                   ws.h_scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_mxfp4(const uint16_t* w, int64_t nblocks, uint8_t* blocks, uint8_t* scales,
                               hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;

@@ -42,11 +42,15 @@ DENSE_SHAPES = {                  # name -> (N, K)
 # MoE workloads: name -> (seed, tokens, act_mode, hot experts)
 ACT_BF16 = 0
 ACT_FP8_E4M3 = 1
+ACT_MXFP4 = 2
 MOE_WORKLOADS = {
     "moe_decode_t4": (0, 4, ACT_BF16, 0),
     "moe_decode_t32": (1, 32, ACT_BF16, 0),
     "moe_prefill_t2048_fp8": (2, 2048, ACT_FP8_E4M3, 0),
     "moe_prefill_t8192_fp8_skewed": (4, 8192, ACT_FP8_E4M3, 8),
+    # the same token batches with MXFP4 activations (FP4 x FP4)
+    "moe_prefill_t2048_fp4": (2, 2048, ACT_MXFP4, 0),
+    "moe_prefill_t8192_fp4_skewed": (4, 8192, ACT_MXFP4, 8),
 }
 HOT_BOOST = 2.0
 

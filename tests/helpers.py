@@ -98,6 +98,24 @@ def assert_close_slack(got, ref, slack, what=""):
     return rel_fro, dist.max() / max(rms, 1e-300)
 
 
+def assert_close_rounded_slack(got, ref, slack, what=""):
+    """assert_close_rounded with the per-output allowance of assert_close_slack:
+    the distance from the reference to each bf16 output's rounding interval,
+    less the slack, must meet the bounds."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(got).all(), "%s: non-finite output" % what
+    lo, hi = bf16_rounding_interval(got)
+    dist = np.maximum(np.maximum(lo - ref, ref - hi), 0.0)
+    dist = np.maximum(dist - np.asarray(slack, dtype=np.float64), 0.0)
+    rms = np.sqrt(np.mean(ref ** 2))
+    rel_fro = np.linalg.norm(dist) / max(np.linalg.norm(ref), 1e-300)
+    assert rel_fro <= REL_FRO_TOL, "%s: rel Frobenius beyond rounding and slack %.3e" % (what, rel_fro)
+    assert dist.max() <= MAX_ABS_TOL * rms, "%s: max abs beyond rounding and slack %.3e > %.1e * rms %.3e" % (
+        what, dist.max(), MAX_ABS_TOL, rms)
+    return rel_fro, dist.max() / max(rms, 1e-300)
+
+
 def no_constant_rows(out):
     """Broken FP4 kernels were reported to emit rows made of one repeated value
     (forum page, bug 1); a healthy layer output never does at these sizes."""

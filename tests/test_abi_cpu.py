@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 1
+    assert L.mxfp4_abi_version() == 2
     assert L.mxfp4_status_string(0) == b"ok"
     assert L.mxfp4_status_string(E_WORKSPACE) == b"workspace too small"
     assert L.mxfp4_status_string(99) == b"unknown status"
@@ -57,7 +57,9 @@ def test_workspace_size_validation(L):
     assert rc == 0 and n > 32 * 4 * 2880 * 4
     rc8, n8 = _size(L, 2048, 2880, 2880, 128, 4, 1)
     assert rc8 == 0 and n8 > n
-    assert _size(L, 4, 2880, 2880, 128, 4, 2)[0] == E_MODE          # unknown act_mode
+    rc4, n4 = _size(L, 2048, 2880, 2880, 128, 4, 2)                # MXFP4 activations
+    assert rc4 == 0 and n < n4 < n8
+    assert _size(L, 4, 2880, 2880, 128, 4, 3)[0] == E_MODE          # unknown act_mode
     assert _size(L, 4, 2880 + 16, 2880, 128, 4, 0)[0] == E_SHAPE    # H % 32
     assert _size(L, 4, 2880, 0, 128, 4, 0)[0] == E_SHAPE
     assert _size(L, 4, 2880, 2880, 128, 0, 0)[0] == E_SHAPE         # k < 1
@@ -78,6 +80,23 @@ def test_layout_offsets_are_ordered_and_aligned(L):
     assert offs == sorted(offs) and lay.total_bytes > lay.y
     assert lay.y - lay.h >= 8192 * 4 * 2880 * 5          # fp32 h + u8 codes
     assert lay.h - lay.x_codes >= 8192 * 4 * 2880        # x codes per routed pair (sorted rows)
+    assert lay.x_scales == 0 and lay.h_scales == 0
+
+
+def test_layout_of_mxfp4_activations(L):
+    from mxfp4_block_scaled_top_amd._lib import WorkspaceLayout
+    lay = WorkspaceLayout()
+    T, H, I = 2048, 2880, 2880
+    np_ = T * 4
+    assert L.mxfp4_moe_workspace_layout_query(T, H, I, 128, 4, 2, ctypes.byref(lay)) == 0
+    offs = [lay.x_codes, lay.x_scales, lay.h, lay.h_codes, lay.h_scales, lay.y]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert lay.x_scales - lay.x_codes >= np_ * H // 2    # E2M1 blocks per sorted row
+    assert lay.h - lay.x_scales >= np_ * 92              # 90 scales padded to 92 per row
+    assert lay.h_codes - lay.h >= np_ * I * 4            # fp32 h
+    assert lay.h_scales - lay.h_codes >= np_ * I // 2
+    assert lay.y - lay.h_scales >= np_ * 92
+    assert lay.total_bytes >= lay.y + np_ * H * 4
 
 
 def _fake(n=1):

@@ -11,8 +11,9 @@ import pytest
 
 import oracle
 import synth
-from helpers import (assert_close, assert_close_rounded, assert_close_slack, bf16_bits_to_f64,
-                     bf16_dev_to_f64, errors, no_constant_rows, to_dev)
+from golden.make_golden import mx_code_gap, output_slack
+from helpers import (assert_close, assert_close_rounded, assert_close_rounded_slack, assert_close_slack,
+                     bf16_bits_to_f64, bf16_dev_to_f64, errors, no_constant_rows, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -30,7 +31,7 @@ def mx():
 
 
 def _layer_dev(L):
-    return {k: to_dev(v, torch) for k, v in L.items()}
+    return {k: (None if v is None else to_dev(v, torch)) for k, v in L.items()}
 
 
 def _run_moe(mx, Ld, x_bits, ids, w, act_mode, want_ws=False):
@@ -360,7 +361,7 @@ def test_moe_full_size_workloads(mx, full_layer, name):
     got = bf16_dev_to_f64(out)
     tokens = gold["tokens"]
     ref = gold["out"].astype(np.float64)
-    if act == synth.ACT_FP8_E4M3:
+    if act in (synth.ACT_FP8_E4M3, synth.ACT_MXFP4):
         # outputs are unique except where an h code sits within the stated h
         # error of a rounding boundary; the golden slack bounds that freedom
         assert_close_slack(got[tokens], ref, gold["slack"], name)
@@ -396,6 +397,126 @@ def test_moe_full_size_workloads(mx, full_layer, name):
         rc = oracle.e4m3_encode((h_rows / sh).astype(np.float32).astype(np.float64))
         hc = ws[lay["h_codes"]:lay["h_codes"] + np_ * I].view(np_, I)[torch.from_numpy(srows).cuda()]
         assert np.array_equal(hc.cpu().numpy(), rc)
+    if act == synth.ACT_MXFP4:
+        np_ = T * k
+        sp = _ws_view(ws, lay, "sorted_pairs", np.int32, np_).astype(np.int64)
+        inv = _ws_view(ws, lay, "inv_pairs", np.int32, np_)
+        nbh, nbi = 4 * -(-H // 128), 4 * -(-I // 128)
+        # x codes of every sorted row (every pair is routed)
+        xb = _ws_view(ws, lay, "x_codes", np.uint8, np_ * H // 2).reshape(np_, H // 32, 16)
+        xs = _ws_view(ws, lay, "x_scales", np.uint8, np_ * nbh).reshape(np_, nbh)
+        rb, rs = oracle.quantize_mxfp4(oracle.bf16_bits_to_f64(wl["x"]))
+        assert np.array_equal(xs[:, :H // 32], rs[sp // k])
+        assert np.array_equal(xb, rb[sp // k])
+        del xb, rb
+        # h within the error the slack assumes, on the sampled pairs
+        h_t = ws[lay["h"]:lay["h"] + np_ * I * 4].view(torch.float32).view(np_, I)
+        rel, absu = float(gold["h_rel_err"]), float(gold["h_abs_err"])
+        rows = torch.from_numpy(inv[gold["h_pairs"]].astype(np.int64)).cuda()
+        h_gpu = h_t[rows].cpu().numpy().astype(np.float64)
+        h_ref = gold["h_ref"].astype(np.float64)
+        hb_ref = h_ref.reshape(len(h_ref), I // 32, 32)
+        bscale = np.ldexp(1.0, oracle.quant.block_exponent(np.abs(hb_ref).max(axis=-1)))[..., None]
+        bound = rel * np.abs(hb_ref) + absu * bscale
+        assert np.all(np.abs(h_gpu.reshape(hb_ref.shape) - hb_ref) <= bound)
+        # h codes on a sample of rows: the oracle quantiser of the kernel's own h
+        srows = torch.from_numpy(np.random.default_rng(1).choice(np_, 512, replace=False)).cuda()
+        h_rows = h_t[srows].cpu().numpy().astype(np.float64)
+        rhb, rhs = oracle.quantize_mxfp4(h_rows)
+        hb = ws[lay["h_codes"]:lay["h_codes"] + np_ * I // 2].view(np_, I // 32, 16)[srows]
+        hs = ws[lay["h_scales"]:lay["h_scales"] + np_ * nbi].view(np_, nbi)[srows]
+        assert np.array_equal(hs.cpu().numpy()[:, :I // 32], rhs)
+        assert np.array_equal(hb.cpu().numpy(), rhb)
+
+
+# ------------------------------------- MXFP4 activations (FP4 x FP4 MFMA) ----
+
+
+def _mx_act_check(mx, L, x, ids, w, what):
+    """The FP4 x FP4 layer against the oracle, step by step.
+
+    The x codes are unique and compared bit for bit.  h is compared with the
+    oracle's h.  The h codes are the oracle quantiser applied to the kernel's
+    own fp32 h, bit for bit: where an h value lies within the contraction's
+    rounding of a code boundary (or a block's amax of a power of two) both
+    codes are correct, and the kernel's h decides.  The output is then
+    compared with the oracle's down projection and combine of those codes.
+    Returns (relative error of h, relative error against the float64 layer)."""
+    E = L["w13_blocks"].shape[0]
+    T, H = x.shape
+    I = L["w2_blocks"].shape[2] * 32
+    k = ids.shape[1]
+    np_ = T * k
+    got, ws, lay = _run_moe(mx, _layer_dev(L), x, ids, w, synth.ACT_MXFP4, want_ws=True)
+    ref = oracle.moe_forward_routed(x, ids, w, **L, act_mode=synth.ACT_MXFP4)
+    sp = _ws_view(ws, lay, "sorted_pairs", np.int32, np_)
+    nrows = int(_ws_view(ws, lay, "expert_offsets", np.int32, E + 1)[E])
+    pairs = sp[:nrows].astype(np.int64)
+    nbh, nbi = 4 * -(-H // 128), 4 * -(-I // 128)
+    xb = _ws_view(ws, lay, "x_codes", np.uint8, np_ * H // 2).reshape(np_, H // 32, 16)[:nrows]
+    xs = _ws_view(ws, lay, "x_scales", np.uint8, np_ * nbh).reshape(np_, nbh)[:nrows]
+    assert np.array_equal(xb, ref["x_blocks"][pairs // k])
+    assert np.array_equal(xs[:, :H // 32], ref["x_scales"][pairs // k])
+    assert np.all(xs[:, H // 32:] == 127)
+    h_gpu = _ws_view(ws, lay, "h", np.float32, np_ * I).reshape(np_, I)[:nrows].astype(np.float64)
+    h_rel = errors(h_gpu, ref["h"].reshape(np_, I)[pairs])[0] if nrows else 0.0
+    assert h_rel < 1e-4, "%s: h rel Frobenius %.3e" % (what, h_rel)
+    hb = _ws_view(ws, lay, "h_codes", np.uint8, np_ * I // 2).reshape(np_, I // 32, 16)[:nrows]
+    hs = _ws_view(ws, lay, "h_scales", np.uint8, np_ * nbi).reshape(np_, nbi)[:nrows]
+    rb, rs = oracle.quantize_mxfp4(h_gpu)
+    assert np.array_equal(hs[:, :I // 32], rs)
+    assert np.all(hs[:, I // 32:] == 127)
+    assert np.array_equal(hb, rb)
+    # y = W2 h' + b2 of the kernel's h codes and the weighted combine, float64
+    hq = oracle.dequant(hb, hs[:, :I // 32])
+    e_of = ids.reshape(-1).astype(np.int64)[pairs]
+    y = np.zeros((np_, H))
+    for e in np.unique(e_of):
+        sel = np.nonzero(e_of == e)[0]
+        W2 = oracle.dequant(L["w2_blocks"][e], L["w2_scales"][e])
+        b2 = 0.0 if L["w2_bias"] is None else oracle.bf16_bits_to_f64(L["w2_bias"][e])
+        y[pairs[sel]] = hq[sel] @ W2.T + b2
+    wf = np.where((ids >= 0) & (ids < E), w, 0.0).reshape(-1)
+    out_ref = (wf[:, None] * y).reshape(T, k, H).sum(axis=1)
+    assert_close_rounded(got, out_ref, what)
+    # end to end against the float64 layer, with the allowance for h codes
+    # that are ambiguous within the stated h error
+    ids64 = np.where((ids >= 0) & (ids < E), ids, -1)
+    slack = output_slack(ref["h32"], ids64, w, L, np.arange(T), mx_code_gap)
+    assert_close_rounded_slack(got, ref["out"], slack, what + " end to end")
+    end = errors(got, ref["out"])[0]
+    print("%s: h rel %.3e, end-to-end rel %.3e, slack max %.3g" % (what, h_rel, end, slack.max()))
+    return h_rel, end
+
+
+@pytest.mark.parametrize("E,H,I,T,k", SMALL)
+def test_mxfp4_act_small_layers(mx, E, H, I, T, k):
+    L = synth.layer(seed=E * 13 + H, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(T + 17, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    _mx_act_check(mx, L, x, ids, w, "mxfp4-act E%d H%d I%d T%d" % (E, H, I, T))
+
+
+def test_mxfp4_act_edge_cases(mx):
+    E, H, I, T, k = 8, 64, 96, 40, 4
+    L = synth.layer(seed=79, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(80, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    # every token on the same four experts (one expert spans several tiles)
+    _mx_act_check(mx, L, x, np.tile(np.arange(k, dtype=np.int32), (T, 1)), w, "hot")
+    # duplicated expert inside a token, ids out of range (skipped)
+    ids_bad = ids.copy()
+    ids_bad[0, 1] = ids_bad[0, 0]
+    ids_bad[3, 2] = -1
+    ids_bad[5, 0] = E + 5
+    _mx_act_check(mx, L, x, ids_bad, w, "bad ids")
+    # all-zero activations (every block gets the smallest scale) and no bias
+    _mx_act_check(mx, L, np.zeros_like(x), ids, w, "zero x")
+    _mx_act_check(mx, dict(L, w13_bias=None, w2_bias=None), x, ids, w, "no bias")
+    # a wide spread of magnitudes inside the blocks of x
+    xw = synth.f32_to_bf16_bits(oracle.bf16_bits_to_f64(x) * np.exp2(np.random.default_rng(81).integers(
+        -20, 20, size=x.shape)))
+    _mx_act_check(mx, L, xw, ids, w, "wide x")
 
 
 # ------------------------------------------------------ weight quantiser ----
