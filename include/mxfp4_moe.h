@@ -75,12 +75,26 @@ enum {
 enum {
   MXFP4_STAGE_BEGIN = 0,      /* before the first kernel */
   MXFP4_STAGE_PERMUTE = 1,    /* after the token-by-expert permutation */
-  MXFP4_STAGE_QUANT_X = 2,    /* after quantisation of x (FP8, MXFP4 activations) */
+  MXFP4_STAGE_QUANT_X = 2,    /* after quantisation of x and the restaging of the
+                                 w13 scales (FP8, MXFP4 activations) */
   MXFP4_STAGE_GEMM1 = 3,      /* after gate_up GEMM + SwiGLU */
-  MXFP4_STAGE_QUANT_H = 4,    /* after quantisation of h (FP8, MXFP4 activations) */
+  MXFP4_STAGE_QUANT_H = 4,    /* after quantisation of h and the restaging of the
+                                 w2 scales (FP8, MXFP4 activations) */
   MXFP4_STAGE_GEMM2 = 5,      /* after the down GEMM */
   MXFP4_STAGE_COMBINE = 6,    /* after the weighted combine (end) */
   MXFP4_NUM_STAGES = 7
+};
+
+/* Bits of mxfp4_moe_opts.flags. */
+enum {
+  /* FP8 and MXFP4-activation modes: the workspace already holds the restaged
+     weight scales (w13_scale_stream, w2_scale_stream) of exactly these
+     w13_scales / w2_scales, written by an earlier call with the same weights,
+     shapes, act_mode and workspace, and not overwritten since; the restaging
+     is skipped.  For callers whose weights stay fixed (prepared once, as a
+     load-time step).  Ignored in BF16 mode.  If the promise does not hold the
+     result is undefined (but every access stays inside the workspace). */
+  MXFP4_OPT_SCALE_STREAMS_READY = 1
 };
 
 /* Optional per-call options for mxfp4_moe_forward (pass NULL for none). */
@@ -88,6 +102,7 @@ typedef struct {
   /* events[i], if non-NULL, is a hipEvent_t recorded on `stream` at stage
      boundary i (0 <= i < MXFP4_NUM_STAGES).  Used for per-kernel timing. */
   void* events[MXFP4_NUM_STAGES];
+  uint32_t flags;             /* MXFP4_OPT_* bits; 0 for none */
 } mxfp4_moe_opts;
 
 /* Byte offsets of the intermediate results inside the MoE workspace, for
@@ -120,13 +135,18 @@ typedef struct {
                                MXFP4-activation mode: uint8 [T*k, I/32, 16]
                                E2M1 blocks of h */
   uint64_t y;               /* fp32 [T*k, H] per-pair expert outputs, sorted rows */
-  uint64_t x_scales;        /* MXFP4-activation mode: uint8 [T*k, 4*ceil(H/128)]
-                               E8M0 scales of the x blocks, rows padded to whole
-                               128-element steps (pad bytes hold 127); 0 in the
+  uint64_t x_scales;        /* MXFP4-activation mode: uint8 [ceil(H/128), T*k, 4]
+                               E8M0 scales of the x blocks, step-major: block b
+                               of sorted row r at ((b/4)*T*k + r)*4 + b%4;
+                               bytes of blocks past H/32 hold 127; 0 in the
                                other modes */
-  uint64_t h_scales;        /* MXFP4-activation mode: uint8 [T*k, 4*ceil(I/128)]
-                               E8M0 scales of the h blocks, padded likewise;
-                               0 in the other modes */
+  uint64_t h_scales;        /* MXFP4-activation mode: uint8 [ceil(I/128), T*k, 4]
+                               E8M0 scales of the h blocks, likewise; 0 in the
+                               other modes */
+  uint64_t w13_scale_stream; /* FP8 and MXFP4-activation modes: the w13 E8M0
+                               scales restaged in the order the prefill GEMM
+                               copies them (internal layout); 0 in BF16 mode */
+  uint64_t w2_scale_stream; /* the same for w2 */
 } mxfp4_moe_workspace_layout;
 
 /* Library ABI version (MXFP4_ABI_VERSION of the build). */

@@ -29,11 +29,24 @@ class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "total_bytes", "status", "expert_offsets", "sorted_pairs", "inv_pairs",
         "chunk_counts", "chunk_ranks", "tiles", "x_codes", "h", "h_codes", "y", "x_scales",
-        "h_scales")]
+        "h_scales", "w13_scale_stream", "w2_scale_stream")]
+
+
+OPT_SCALE_STREAMS_READY = 1
 
 
 class MoeOpts(ctypes.Structure):
-    _fields_ = [("events", _c_void_p * NUM_STAGES)]
+    _fields_ = [("events", _c_void_p * NUM_STAGES), ("flags", ctypes.c_uint32)]
+
+
+def _opts(events, scale_streams_ready):
+    if events is None and not scale_streams_ready:
+        return None
+    opts = MoeOpts()
+    for i, ev in enumerate(events or ()):
+        opts.events[i] = ev
+    opts.flags = OPT_SCALE_STREAMS_READY if scale_streams_ready else 0
+    return opts
 
 
 class Mxfp4Error(RuntimeError):
@@ -159,10 +172,12 @@ def mxfp4_moe_workspace_layout_query(T, H, I, E, k, act_mode):
 
 def mxfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bias,
                       w2_blocks, w2_scales, w2_bias, act_mode, out=None, workspace=None,
-                      events=None, stream=None):
+                      events=None, stream=None, scale_streams_ready=False):
     """One MoE layer; returns out (bf16 [T, H]).  `workspace` is a uint8 device
     tensor of at least mxfp4_moe_workspace_size() bytes (allocated here if None);
-    `events` is an optional list of NUM_STAGES event handles (or None entries)."""
+    `events` is an optional list of NUM_STAGES event handles (or None entries);
+    `scale_streams_ready` sets MXFP4_OPT_SCALE_STREAMS_READY (the workspace
+    already holds these weights' restaged scales from an earlier call)."""
     _need(x, "x", torch.bfloat16, 2)
     _need(topk_ids, "topk_ids", torch.int32, 2)
     _need(topk_weights, "topk_weights", torch.float32, 2)
@@ -191,11 +206,7 @@ def mxfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bia
         workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, act_mode), 1),
                                 dtype=torch.uint8, device=x.device)
     _need(workspace, "workspace", torch.uint8, 1)
-    opts = None
-    if events is not None:
-        opts = MoeOpts()
-        for i, ev in enumerate(events):
-            opts.events[i] = ev
+    opts = _opts(events, scale_streams_ready)
     _check("mxfp4_moe_forward", lib().mxfp4_moe_forward(
         _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
         _ptr(w13_blocks), _ptr(w13_scales), _ptr(w13_bias),
@@ -239,11 +250,7 @@ def nvfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_glo
         workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, ACT_BF16), 1),
                                 dtype=torch.uint8, device=x.device)
     _need(workspace, "workspace", torch.uint8, 1)
-    opts = None
-    if events is not None:
-        opts = MoeOpts()
-        for i, ev in enumerate(events):
-            opts.events[i] = ev
+    opts = _opts(events, False)
     _check("nvfp4_moe_forward", lib().nvfp4_moe_forward(
         _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
         _ptr(w13_blocks), _ptr(w13_scales), float(w13_global), _ptr(w13_bias),
@@ -255,7 +262,7 @@ def nvfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_glo
 
 def mxfp4_moe_layer(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias,
                     act_mode, out=None, topk_ids=None, topk_weights=None, workspace=None, events=None,
-                    stream=None):
+                    stream=None, scale_streams_ready=False):
     """Router + MoE layer in one call; returns (out, topk_ids, topk_weights)."""
     _need(x, "x", torch.bfloat16, 2)
     _need(logits, "logits", torch.float32, 2)
@@ -290,11 +297,7 @@ def mxfp4_moe_layer(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w
         workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, act_mode), 1),
                                 dtype=torch.uint8, device=x.device)
     _need(workspace, "workspace", torch.uint8, 1)
-    opts = None
-    if events is not None:
-        opts = MoeOpts()
-        for i, ev in enumerate(events):
-            opts.events[i] = ev
+    opts = _opts(events, scale_streams_ready)
     _check("mxfp4_moe_layer", lib().mxfp4_moe_layer(
         _ptr(x), _ptr(logits), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
         _ptr(w13_blocks), _ptr(w13_scales), _ptr(w13_bias),

@@ -90,16 +90,20 @@ void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mod
     L->h_codes = o; o = up(o + (size_t)np * I);
   } else if (act_mode == MXFP4_ACT_MXFP4) {
     L->x_codes = o; o = up(o + (size_t)np * H / 2);
-    L->x_scales = o; o = up(o + (size_t)np * mx::act_scale_stride((int)H));
+    L->x_scales = o; o = up(o + (size_t)mx::act_scale_bytes(np, (int)H));
     L->h = o; o = up(o + (size_t)np * I * 4);
     L->h_codes = o; o = up(o + (size_t)np * I / 2);
-    L->h_scales = o; o = up(o + (size_t)np * mx::act_scale_stride((int)I));
+    L->h_scales = o; o = up(o + (size_t)mx::act_scale_bytes(np, (int)I));
   } else {
     L->x_codes = o;
     L->h = o; o = up(o + (size_t)np * I * 2 * 2);
     L->h_codes = o;
   }
   L->y = o; o = up(o + (size_t)np * H * 4);
+  if (act_mode != MXFP4_ACT_BF16) {
+    L->w13_scale_stream = o; o = up(o + (size_t)mx::scale_stream_bytes(E, mx::gateup_ntiles((int)I), (int)H));
+    L->w2_scale_stream = o; o = up(o + (size_t)mx::scale_stream_bytes(E, mx::down_ntiles((int)H), (int)I));
+  }
   L->total_bytes = o;
 }
 
@@ -119,6 +123,8 @@ mx::WsPtrs ws_ptrs(void* base, const mxfp4_moe_workspace_layout& L) {
   w.y = reinterpret_cast<float*>(b + L.y);
   w.x_scales = b + L.x_scales;
   w.h_scales = b + L.h_scales;
+  w.w13_stream = b + L.w13_scale_stream;
+  w.w2_stream = b + L.w2_scale_stream;
   return w;
 }
 
@@ -272,6 +278,8 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   } else if (a4) {
     MX_STEP(mx::launch_quant_x_mxfp4_sorted(x, sh, ws, s), "quant x launch");
   }
+  const bool restage = (fp8 || a4) && !(opts && (opts->flags & MXFP4_OPT_SCALE_STREAMS_READY));
+  if (restage) MX_STEP(mx::launch_scale_stream(sh, w, ws, true, s), "w13 scale stream launch");
   MX_STEP(mark(MXFP4_STAGE_QUANT_X), "event record");
   if (fp8) MX_STEP(mx::launch_moe_gateup_fp8(sh, w, ws, bound, s), "gate_up launch");
   else if (a4) MX_STEP(mx::launch_moe_gateup_fp4(sh, w, ws, s), "gate_up launch");
@@ -285,6 +293,7 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   } else if (a4) {
     MX_STEP(mx::launch_quant_h_mxfp4(sh, ws, s), "quant h launch");
   }
+  if (restage) MX_STEP(mx::launch_scale_stream(sh, w, ws, false, s), "w2 scale stream launch");
   MX_STEP(mark(MXFP4_STAGE_QUANT_H), "event record");
   if (fp8) MX_STEP(mx::launch_moe_down_fp8(sh, w, ws, bound, s), "down launch");
   else if (a4) MX_STEP(mx::launch_moe_down_fp4(sh, w, ws, s), "down launch");

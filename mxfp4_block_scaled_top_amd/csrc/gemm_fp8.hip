@@ -60,7 +60,7 @@ namespace mx {
 constexpr int kBN = 256;               // weight rows per unit
 constexpr int kBK = 128;               // K per step (four MX blocks)
 constexpr int kWTile = kBN * kBK / 2;  // E2M1 bytes per step
-constexpr int kScTile = kBN * 8;       // two aligned scale dwords per weight row
+constexpr int kScTile = kBN * 4;       // the step's four scale bytes of each weight row
 
 // A4: MXFP4 activations (64 B of E2M1 codes per row per step, the geometry
 // of a weight row, plus one dword of four E8M0 scales per row); otherwise
@@ -78,16 +78,12 @@ struct Ring {
   static constexpr int kSlot = kASc + (A4 ? BM * 4 : 0);
   static constexpr int kActDma = BM * kActRow / 1024 / kWaves;  // 1 KB activation DMAs per wave per step
   static constexpr int kWDma = 16 / kWaves;             // 1 KB weight DMAs per wave per step
-  static constexpr int kScDma = 8 / kWaves;             // 256 B scale DMAs per wave per step
-  static constexpr int kAScDma = A4 ? 1 : 0;            // 256 B activation-scale DMAs per wave per step
+  static constexpr int kScDma = 1;                      // the wave's 1/8 of the step's weight scales
+  static constexpr int kAScDma = A4 ? 1 : 0;            // the wave's 1/8 of the step's activation scales
   static constexpr int kDma = kActDma + kWDma + kScDma + kAScDma;  // DMA instructions per wave per step
-  // A4: waves 0 and 1 copy the 128 rows' scale dwords; the other waves issue
-  // the same copy into this 256 B sink, so that every wave counts the same
-  // number of copies per step
-  static constexpr int kSink = kStages * kSlot;
-  static constexpr int kLds = kSink + (A4 ? 256 : 0);
-  static_assert(kActDma * kWaves * 1024 == BM * kActRow && kScDma >= 1, "copies split over the waves");
-  static_assert(!A4 || BM == 128, "two waves of 64 lanes copy the activation scales");
+  static constexpr int kLds = kStages * kSlot;
+  static_assert(kActDma * kWaves * 1024 == BM * kActRow, "copies split over the waves");
+  static_assert(kWaves == 8 && (!A4 || BM == 128), "each wave copies 128 B of weight and 64 B of activation scales");
   static_assert((kStages - 2) * kDma <= 63, "vector-memory count range");
   static_assert(kStages - 2 <= 4, "waits cover up to four steps ahead");
   static_assert(kLds <= 160 * 1024, "LDS");
@@ -95,9 +91,8 @@ struct Ring {
 
 struct PrefillArgs {
   const uint8_t* wb;       // [E, R, nb, 16]
-  const uint8_t* ws;       // [E, R, nb]
+  const uint8_t* wsp;      // the weight scales restaged by launch_scale_stream
   const uint16_t* bias;    // [E, R] or null
-  int64_t sc_total;        // E * R * nb (scale bytes; a multiple of 4)
   int R;                   // rows per expert: 2I (gate_up) or H (down)
   int nout;                // I (gate_up) or H (down)
   int nb;                  // K / 32
@@ -106,8 +101,8 @@ struct PrefillArgs {
   int nsteps;              // ceil(nb / 4)
   const uint8_t* act;      // [sorted rows, K] E4M3 codes, or [sorted rows, K/32, 16] E2M1 blocks
   int act_ld;              // activation bytes per row (K, or K/2 for E2M1)
-  const uint8_t* asc;      // E2M1 activations: E8M0 [sorted rows, nbp]
-  int nbp;                 // activation scale bytes per row (a multiple of 4)
+  const uint8_t* asc;      // E2M1 activations: E8M0 [nsteps, sorted rows, 4] (step-major)
+  int64_t asc_step;        // bytes per step of asc (4 * sorted rows)
   int scale_word;          // status word holding the per-tensor activation scale (E4M3)
   float* out;              // h [rows, I] (gate_up) or y [rows, H] (down), fp32
 };
@@ -185,13 +180,17 @@ __device__ __forceinline__ float bf16_of(uint2 q, int jj) {
 // 8j + lane/8, 16-byte slot lane%8, which holds logical chunk
 // (lane%8) ^ (row%8).  Weight DMA i fills rows 16j..16j+15: lane -> row
 // 16j + lane/4, slot lane%4, which holds MX block (lane%4) ^ ((row/2)%4).
-// Scale DMA i fills rows 32j..32j+31: lane -> row 32j + lane/2, aligned dword
-// lane%2 of the 8 bytes that hold the row's four scales of the step.
+// The weight scales come from the restaged stream (launch_scale_stream),
+// where a unit's step is 1 KB: the four scale bytes of each of its 256 LDS
+// rows in row order.  Wave w copies bytes [128w, 128w + 128) with lanes 0-7,
+// one cache line per instruction (the checkpoint layout would need a
+// scattered 4-byte read per row: rows are K/32 bytes apart).
 //
 // A4 (E2M1 activations): activation DMA i fills slot rows 16j..16j+15 like a
 // weight DMA (lane -> row 16j + lane/4, slot lane%4 holding MX block
-// (lane%4) ^ ((row/2)%4)); the scale DMA of wave w < 2 fills the scale dwords
-// of rows 64w .. 64w+63 (one per lane), the other waves' go to the sink.
+// (lane%4) ^ ((row/2)%4)).  The activation scales are stored step-major, so a
+// step's scales of the tile's 128 rows are 512 contiguous bytes; wave w
+// copies rows 16w .. 16w+15 with lanes 0-3.
 template <bool GATEUP, int BM, bool A4 = false>
 struct PrefillCopier {
   using C = Ring<BM, A4>;
@@ -199,22 +198,21 @@ struct PrefillCopier {
   const int* tiles;
   uint8_t* smem;
   int wave, u0, G, my_units;
-  int a_chunk, a_row, w_row, w_blk, s_row, s_dw;
+  int lane, a_chunk, a_row, w_row, w_blk;
   const uint8_t* aptr[C::kActDma];
   const uint8_t* wptr[C::kWDma];
-  int64_t sofs[C::kScDma];
-  const uint8_t* ascp;  // A4: this lane's activation-scale row
+  const uint8_t* wsp;   // this lane's 16 bytes of the unit's first step in the scale stream
+  const uint8_t* ascp;  // A4: this lane's 16 bytes of the tile's scales at step 0
   int k, step, slot;    // next copy: local unit, step, ring slot
 
   __device__ __forceinline__ void init(const PrefillArgs& a, const int* t, uint8_t* sm, int w, int lane, int first,
                                        int grid, int units) {
     tiles = t; smem = sm; wave = w; u0 = first; G = grid; my_units = units;
+    this->lane = lane;
     a_row = A4 ? lane >> 2 : lane >> 3;
     a_chunk = A4 ? (lane & 3) ^ ((lane >> 3) & 3) : (lane & 7) ^ a_row;
     w_row = lane >> 2;
     w_blk = (lane & 3) ^ ((lane >> 3) & 3);
-    s_row = lane >> 1;
-    s_dw = lane & 1;
     k = 0; step = 0; slot = 0;
     setup(a, u0);
   }
@@ -229,22 +227,15 @@ struct PrefillCopier {
       row = row < te.z ? row : te.y;
       aptr[i] = a.act + (int64_t)row * a.act_ld;
     }
-    if (A4) {
-      int row = te.y + 64 * (wave & 1) + (int)(threadIdx.x & 63);
-      row = row < te.z ? row : te.y;
-      ascp = a.asc + (int64_t)row * a.nbp;
-    }
+    // rows past the tile end read other rows' scales (never stored)
+    if (A4) ascp = a.asc + (int64_t)te.y * 4 + 64 * wave + 16 * (lane & 3);
     const int64_t ebase = (int64_t)te.x * a.R;
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
       const int wr = weight_row<GATEUP>(16 * (NW * i + wave) + w_row, nt, a.nout);
       wptr[i] = a.wb + (ebase + wr) * a.nb * kBlockBytes;
     }
-#pragma unroll
-    for (int i = 0; i < C::kScDma; ++i) {
-      const int wr = weight_row<GATEUP>(32 * (NW * i + wave) + s_row, nt, a.nout);
-      sofs[i] = (ebase + wr) * a.nb;
-    }
+    wsp = a.wsp + ((int64_t)te.x * a.NT + nt) * a.nsteps * 1024 + 128 * wave + 16 * (lane & 7);
   }
 
   // copies of the next step into its slot, then advance
@@ -270,15 +261,9 @@ struct PrefillCopier {
       __builtin_amdgcn_global_load_lds(wptr[i] + (!tail || blk < a.nb ? blk * kBlockBytes : 0),
                                        dst + C::kW + 1024 * (NW * i + wave), 16, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < C::kScDma; ++i) {
-      int64_t q = ((sofs[i] + 4 * step) & ~(int64_t)3) + 4 * s_dw;
-      q = q < a.sc_total - 4 ? q : a.sc_total - 4;
-      __builtin_amdgcn_global_load_lds(a.ws + q, dst + C::kSc + 256 * (NW * i + wave), 4, 0, 0);
-    }
-    if (A4)   // the step's four scales of the row: one aligned dword of the padded row
-      __builtin_amdgcn_global_load_lds(ascp + 4 * step, wave < 2 ? dst + C::kASc + 256 * wave : smem + C::kSink,
-                                       4, 0, 0);
+    if (lane < 8) __builtin_amdgcn_global_load_lds(wsp + step * 1024, dst + C::kSc + 128 * wave, 16, 0, 0);
+    if (A4 && lane < 4)
+      __builtin_amdgcn_global_load_lds(ascp + step * a.asc_step, dst + C::kASc + 64 * wave, 16, 0, 0);
     slot = slot + 1 == C::kStages ? 0 : slot + 1;
     if (++step == a.nsteps) {
       step = 0;
@@ -310,8 +295,8 @@ __device__ __forceinline__ void lds_step_reads(uint32_t aa0, uint32_t aa1, uint3
     asm volatile(MX_RD_ACT
                  "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
                  "ds_read_b128 %10, %18 offset:8192\n\tds_read_b128 %11, %18 offset:9216\n\t"
-                 "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:128\n\t"
-                 "ds_read_u8 %14, %19 offset:1024\n\tds_read_u8 %15, %19 offset:1152\n\t"
+                 "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
+                 "ds_read_u8 %14, %19 offset:512\n\tds_read_u8 %15, %19 offset:576\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : MX_RD_OUTS
                  : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
@@ -319,8 +304,8 @@ __device__ __forceinline__ void lds_step_reads(uint32_t aa0, uint32_t aa1, uint3
     asm volatile(MX_RD_ACT
                  "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
                  "ds_read_b128 %10, %18 offset:2048\n\tds_read_b128 %11, %18 offset:3072\n\t"
-                 "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:128\n\t"
-                 "ds_read_u8 %14, %19 offset:256\n\tds_read_u8 %15, %19 offset:384\n\t"
+                 "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
+                 "ds_read_u8 %14, %19 offset:128\n\tds_read_u8 %15, %19 offset:192\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : MX_RD_OUTS
                  : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
@@ -340,8 +325,8 @@ __device__ __forceinline__ void lds_step_issue_gateup(uint32_t aa0, uint32_t aa1
                                                       v4u_t& xb0, v4u_t& xb1, v4u_t& xb2, v4u_t& xb3,
                                                       v4u_t& wq0, v4u_t& wq1, v4u_t& wq2, v4u_t& wq3,
                                                       uint32_t& sb0, uint32_t& sb1, uint32_t& sb2, uint32_t& sb3) {
-  asm volatile("ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:128\n\t"
-               "ds_read_u8 %14, %19 offset:1024\n\tds_read_u8 %15, %19 offset:1152\n\t"
+  asm volatile("ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
+               "ds_read_u8 %14, %19 offset:512\n\tds_read_u8 %15, %19 offset:576\n\t"
                "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
                "ds_read_b128 %10, %18 offset:8192\n\tds_read_b128 %11, %18 offset:9216\n\t"
                "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:2048\n\t"
@@ -374,8 +359,8 @@ __device__ __forceinline__ void lds_step_reads_a4(uint32_t aa, uint32_t ww, uint
                                                   uint32_t& sb0, uint32_t& sb1, uint32_t& sb2, uint32_t& sb3,
                                                   uint32_t& ab0, uint32_t& ab1, uint32_t& ab2, uint32_t& ab3) {
   if (GATEUP) {
-    asm volatile("ds_read_u8 %8, %18\n\tds_read_u8 %9, %18 offset:128\n\t"
-                 "ds_read_u8 %10, %18 offset:1024\n\tds_read_u8 %11, %18 offset:1152\n\t"
+    asm volatile("ds_read_u8 %8, %18\n\tds_read_u8 %9, %18 offset:64\n\t"
+                 "ds_read_u8 %10, %18 offset:512\n\tds_read_u8 %11, %18 offset:576\n\t"
                  "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
                  "ds_read_u8 %14, %19 offset:128\n\tds_read_u8 %15, %19 offset:192\n\t"
                  "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:1024\n\t"
@@ -388,8 +373,8 @@ __device__ __forceinline__ void lds_step_reads_a4(uint32_t aa, uint32_t ww, uint
                    "=&v"(ab2), "=&v"(ab3)
                  : "v"(aa), "v"(ww), "v"(ss), "v"(as));
   } else {
-    asm volatile("ds_read_u8 %8, %18\n\tds_read_u8 %9, %18 offset:128\n\t"
-                 "ds_read_u8 %10, %18 offset:256\n\tds_read_u8 %11, %18 offset:384\n\t"
+    asm volatile("ds_read_u8 %8, %18\n\tds_read_u8 %9, %18 offset:64\n\t"
+                 "ds_read_u8 %10, %18 offset:128\n\tds_read_u8 %11, %18 offset:192\n\t"
                  "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
                  "ds_read_u8 %14, %19 offset:128\n\tds_read_u8 %15, %19 offset:192\n\t"
                  "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:1024\n\t"
@@ -438,15 +423,11 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
   // the block-scaled path chunks g and 4+g; the row's swizzle is row%8 = r%8
   const int c0 = (GATEUP ? 2 * g : g) ^ (r & 7);
   const int c1 = (GATEUP ? 2 * g + 1 : 4 + g) ^ (r & 7);
-  // byte of this lane's row in its 8 scale bytes: the row's first scale
-  // byte is at (e*R + row)*nb, and e*R and the weight-row offsets of the four
-  // groups are multiples of 4, so the phase is that of r*nb
-  const int sphase = (r * a.nb) & 3;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const uint32_t a0 = lds0 + (64 * wm + r) * kBK + 16 * c0;
   const uint32_t a1 = lds0 + (64 * wm + r) * kBK + 16 * c1;
   const uint32_t w0 = lds0 + C::kW + lrow0 * 64 + 16 * wslot;
-  const uint32_t s0 = lds0 + C::kSc + lrow0 * 8 + sphase + g;
+  const uint32_t s0 = lds0 + C::kSc + lrow0 * 4 + g;   // scale of MX block g of the step
   // A4: activation block g of token row 64 wm + r sits in slot wslot (the
   // rows' swizzle phase (row/2)%4 is that of r), its scale at byte g of the
   // row's dword
@@ -657,6 +638,94 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
   }
 }
 
+// The weight scales of every unit in the order the copies take them: for
+// expert e, n-tile nt and K step s, 1 KB holding, for each of the unit's 256
+// LDS rows lr (weight_row), the scale bytes of MX blocks 4s .. 4s+3 (127,
+// i.e. 2^0, past K).  A block takes CPB chunks of 32 LDS rows of one unit:
+// the chunk's rows are read into LDS (one contiguous range unless rows are
+// clamped), then written out step by step.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void scale_stream_kernel(const uint8_t* __restrict__ ws, int R, int nout, int nb,
+                                                           int NT, int nsteps, int cpb, uint32_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t rows[];   // 32 * cpb x nb bytes, row-major
+  const int per_unit = 8 / cpb;
+  const int unit = blockIdx.x / per_unit;     // e * NT + nt
+  const int c0 = (blockIdx.x - unit * per_unit) * cpb;
+  const int e = unit / NT, nt = unit - e * NT;
+  const int t = threadIdx.x;
+  const int chunk_dw = 8 * nb;                // dwords of 32 rows
+  bool contiguous = true;
+  for (int c = 0; c < cpb; ++c) {
+    const int r0 = weight_row<GATEUP>(32 * (c0 + c), nt, nout);
+    contiguous = contiguous && weight_row<GATEUP>(32 * (c0 + c) + 31, nt, nout) == r0 + 31;
+  }
+  if (contiguous && cpb == 8 && chunk_dw <= 768) {
+    // each chunk is 32 consecutive rows: 32 * nb bytes at an offset that is a
+    // multiple of 32 from the 4-byte aligned scales; a chunk's base is
+    // wave-uniform and a thread loads dwords t, t + 256, t + 512 of it (an
+    // index past the chunk loads its last dword again, unused).  The loads are
+    // straight-line code, all issued before the first store to LDS (loads
+    // under branches get a full wait at each branch).
+    uint32_t v[8][3];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(
+          ws + ((int64_t)e * R + weight_row<GATEUP>(32 * (c0 + c), nt, nout)) * nb);
+#pragma unroll
+      for (int q = 0; q < 3; ++q) v[c][q] = src[min(t + 256 * q, chunk_dw - 1)];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        if (t + 256 * q < chunk_dw) reinterpret_cast<uint32_t*>(rows)[c * chunk_dw + t + 256 * q] = v[c][q];
+    }
+  } else {
+    // chunks with clamped rows (the last n-tile of a tensor), or K > 3072
+    for (int i = t; i < 32 * cpb * nb; i += blockDim.x) {
+      const int l = i / nb, b = i - l * nb;
+      rows[i] = ws[((int64_t)e * R + weight_row<GATEUP>(32 * c0 + l, nt, nout)) * nb + b];
+    }
+  }
+  __syncthreads();
+  // thread l writes LDS row l's word of every step (consecutive threads,
+  // consecutive words)
+  const int l = t;
+  if (l < 32 * cpb) {
+    const uint8_t* src = rows + l * nb;
+    uint32_t* dst = out + (int64_t)unit * nsteps * 256 + 32 * c0 + l;
+    for (int st = 0; st < nsteps; ++st) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = 4 * st + j;
+        word |= (uint32_t)(b < nb ? src[b] : 127u) << (8 * j);
+      }
+      dst[st * 256] = word;
+    }
+  }
+}
+
+hipError_t launch_scale_stream(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, bool gateup,
+                               hipStream_t s) {
+  const int R = gateup ? 2 * sh.I : sh.H, nout = gateup ? sh.I : sh.H;
+  const int K = gateup ? sh.H : sh.I, nb = K / kBlockElems;
+  const int NT = gateup ? (sh.I + kBN / 2 - 1) / (kBN / 2) : (sh.H + kBN - 1) / kBN;
+  const int nsteps = (nb + 3) / 4;
+  // chunks of 32 rows per block: a whole unit while its rows fit in 48 KB
+  int cpb = 8;
+  while (cpb > 1 && (size_t)32 * cpb * nb > 48 * 1024) cpb /= 2;
+  const unsigned grid = (unsigned)(sh.E * NT * (8 / cpb));
+  const size_t lds = (size_t)32 * cpb * nb;
+  if (gateup)
+    scale_stream_kernel<true><<<grid, 256, lds, s>>>(w.w13_scales, R, nout, nb, NT, nsteps, cpb,
+                                                     reinterpret_cast<uint32_t*>(ws.w13_stream));
+  else
+    scale_stream_kernel<false><<<grid, 256, lds, s>>>(w.w2_scales, R, nout, nb, NT, nsteps, cpb,
+                                                      reinterpret_cast<uint32_t*>(ws.w2_stream));
+  return hipGetLastError();
+}
+
 template <bool GATEUP, bool A4 = false>
 static hipError_t launch_prefill(const PrefillArgs& a, const WsPtrs& ws, hipStream_t s) {
   // one block per compute unit: the LDS ring takes most of a unit's LDS
@@ -673,13 +742,12 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
                                  int64_t /*ntile_bound*/, hipStream_t s) {
   PrefillArgs a{};
   a.wb = w.w13_blocks;
-  a.ws = w.w13_scales;
+  a.wsp = ws.w13_stream;
   a.bias = w.w13_bias;
   a.R = 2 * sh.I;
   a.nout = sh.I;
   a.nb = sh.H / kBlockElems;
   a.K = sh.H;
-  a.sc_total = (int64_t)sh.E * a.R * a.nb;
   a.NT = (sh.I + kBN / 2 - 1) / (kBN / 2);
   a.nsteps = (a.nb + 3) / 4;
   a.act = ws.x_codes;
@@ -693,13 +761,12 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
                                int64_t /*ntile_bound*/, hipStream_t s) {
   PrefillArgs a{};
   a.wb = w.w2_blocks;
-  a.ws = w.w2_scales;
+  a.wsp = ws.w2_stream;
   a.bias = w.w2_bias;
   a.R = sh.H;
   a.nout = sh.H;
   a.nb = sh.I / kBlockElems;
   a.K = sh.I;
-  a.sc_total = (int64_t)sh.E * a.R * a.nb;
   a.NT = (sh.H + kBN - 1) / kBN;
   a.nsteps = (a.nb + 3) / 4;
   a.act = ws.h_codes;
@@ -712,19 +779,18 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
 hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, hipStream_t s) {
   PrefillArgs a{};
   a.wb = w.w13_blocks;
-  a.ws = w.w13_scales;
+  a.wsp = ws.w13_stream;
   a.bias = w.w13_bias;
   a.R = 2 * sh.I;
   a.nout = sh.I;
   a.nb = sh.H / kBlockElems;
   a.K = sh.H;
-  a.sc_total = (int64_t)sh.E * a.R * a.nb;
   a.NT = (sh.I + kBN / 2 - 1) / (kBN / 2);
   a.nsteps = (a.nb + 3) / 4;
   a.act = ws.x_codes;
   a.act_ld = sh.H / 2;
   a.asc = ws.x_scales;
-  a.nbp = act_scale_stride(sh.H);
+  a.asc_step = (int64_t)4 * sh.T * sh.k;
   a.scale_word = -1;
   a.out = static_cast<float*>(ws.h);
   return launch_prefill<true, true>(a, ws, s);
@@ -733,19 +799,18 @@ hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const 
 hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, hipStream_t s) {
   PrefillArgs a{};
   a.wb = w.w2_blocks;
-  a.ws = w.w2_scales;
+  a.wsp = ws.w2_stream;
   a.bias = w.w2_bias;
   a.R = sh.H;
   a.nout = sh.H;
   a.nb = sh.I / kBlockElems;
   a.K = sh.I;
-  a.sc_total = (int64_t)sh.E * a.R * a.nb;
   a.NT = (sh.H + kBN - 1) / kBN;
   a.nsteps = (a.nb + 3) / 4;
   a.act = ws.h_codes;
   a.act_ld = sh.I / 2;
   a.asc = ws.h_scales;
-  a.nbp = act_scale_stride(sh.I);
+  a.asc_step = (int64_t)4 * sh.T * sh.k;
   a.scale_word = -1;
   a.out = ws.y;
   return launch_prefill<false, true>(a, ws, s);

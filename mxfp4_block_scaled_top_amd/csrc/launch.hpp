@@ -28,13 +28,21 @@ struct WsPtrs {
   void* h;           // bf16 hi|lo (BF16 mode) or fp32 (FP8 / MXFP4-activation modes)
   uint8_t* h_codes;
   float* y;
-  uint8_t* x_scales;  // MXFP4 activations: E8M0 [T*k, act_scale_stride(H)]
-  uint8_t* h_scales;  // MXFP4 activations: E8M0 [T*k, act_scale_stride(I)]
+  uint8_t* x_scales;  // MXFP4 activations: E8M0 [ceil(H/128), T*k, 4] (step-major)
+  uint8_t* h_scales;  // MXFP4 activations: E8M0 [ceil(I/128), T*k, 4]
+  uint8_t* w13_stream;  // prefill modes: w13 scales restaged by launch_scale_stream
+  uint8_t* w2_stream;   // prefill modes: w2 scales restaged
 };
 
-// E8M0 bytes per row of MXFP4 activations: the row's K/32 scales padded to
-// whole 128-element K steps, so each step's four are one aligned dword.
-inline int act_scale_stride(int K) { return 4 * ((K + 127) / 128); }
+// Bytes of MXFP4 activation scales for `rows` rows of K elements: per
+// 128-element K step, the four E8M0 bytes of every row (pad bytes 127), plus
+// 512 bytes so that a step's read of a partial last row tile stays inside.
+inline int64_t act_scale_bytes(int64_t rows, int K) { return (int64_t)((K + 127) / 128) * rows * 4 + 512; }
+
+// Bytes of a restaged weight-scale stream: 1 KB per (expert, n-tile, K step).
+inline int64_t scale_stream_bytes(int E, int nout_tiles, int K) { return (int64_t)E * nout_tiles * ((K + 127) / 128) * 1024; }
+inline int gateup_ntiles(int I) { return (I + 127) / 128; }
+inline int down_ntiles(int H) { return (H + 255) / 256; }
 
 // Upper bound of the number of (expert, row-tile) entries.
 inline int64_t max_tiles(int64_t npairs, int64_t E, int BM) {
@@ -102,6 +110,11 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
 hipError_t launch_quant_x_mxfp4_sorted(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
                                        hipStream_t s);
 hipError_t launch_quant_h_mxfp4(const MoeShape& sh, const WsPtrs& ws, hipStream_t s);
+
+// Restage one weight tensor's E8M0 scales (w13 when gateup, else w2) into
+// the order the prefill GEMM copies them.
+hipError_t launch_scale_stream(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, bool gateup,
+                               hipStream_t s);
 
 // FP4 x FP4 block-scaled MFMA path (MXFP4 activations).
 hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,

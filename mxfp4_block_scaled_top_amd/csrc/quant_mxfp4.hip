@@ -70,9 +70,10 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
 
 // ---------------------------------------------------------------------------
 // MXFP4 activations (FP4 x FP4 MoE mode): the same block rule on x (bf16) and
-// on the SwiGLU output h (fp32).  Scale rows are padded to whole 128-element
-// K steps (act_scale_stride) so that a step's four scales of a row are one
-// aligned dword; pad bytes hold 127 (2^0).
+// on the SwiGLU output h (fp32).  Scales are stored step-major: block b of
+// row r at ((b / 4) * rows + r) * 4 + b % 4, so one 128-element K step's
+// scales of consecutive rows are contiguous; blocks past K (up to the whole
+// step) hold 127 (2^0).
 
 // 32 finite fp32 values -> E2M1 nibbles (element 2i in the low nibble of
 // byte i) and the E8M0 byte.  For fp32, floor(log2 amax) is the exponent
@@ -95,12 +96,13 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, uint4& out) {
   return (uint32_t)(x + 127);
 }
 
-// One thread per (token, scale slot c < nbp): block c of the token's row
-// (c < H/32) or a pad byte, written to every sorted row the token's pairs
-// occupy (inv[t*k + j] >= 0).
+// One thread per (token, scale slot c < nbp = whole steps of blocks): block c
+// of the token's row (c < H/32) or a pad byte, written to every sorted row
+// the token's pairs occupy (inv[t*k + j] >= 0).
 __global__ __launch_bounds__(256) void quant_x_mxfp4_sorted_kernel(
     const uint16_t* __restrict__ x, int T, int H, int k, int nbp, const int* __restrict__ inv,
     uint8_t* __restrict__ xb, uint8_t* __restrict__ xs) {
+  const int64_t rows = (int64_t)T * k;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)T * nbp) return;
   const int t = (int)(idx / nbp), c = (int)(idx - (int64_t)t * nbp);
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(256) void quant_x_mxfp4_sorted_kernel(
     const int r = inv[(int64_t)t * k + j];
     if (r < 0) continue;
     if (real) *reinterpret_cast<uint4*>(xb + (int64_t)r * (H / 2) + c * kBlockBytes) = packed;
-    xs[(int64_t)r * nbp + c] = (uint8_t)sc;
+    xs[((c >> 2) * rows + r) * 4 + (c & 3)] = (uint8_t)sc;
   }
 }
 
@@ -153,12 +155,12 @@ __global__ __launch_bounds__(256) void quant_h_mxfp4_kernel(const float* __restr
     sc = mx_encode32(v, packed);
     *reinterpret_cast<uint4*>(hb + r * (I / 2) + c * kBlockBytes) = packed;
   }
-  hs[r * nbp + c] = (uint8_t)sc;
+  hs[((c >> 2) * rows + r) * 4 + (c & 3)] = (uint8_t)sc;
 }
 
 hipError_t launch_quant_x_mxfp4_sorted(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
                                        hipStream_t s) {
-  const int nbp = act_scale_stride(sh.H);
+  const int nbp = 4 * ((sh.H + 127) / 128);
   const int64_t n = (int64_t)sh.T * nbp;
   if (n <= 0) return hipSuccess;
   quant_x_mxfp4_sorted_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, sh.T, sh.H, sh.k, nbp, ws.inv,
@@ -167,7 +169,7 @@ hipError_t launch_quant_x_mxfp4_sorted(const uint16_t* x, const MoeShape& sh, co
 }
 
 hipError_t launch_quant_h_mxfp4(const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
-  const int nbp = act_scale_stride(sh.I);
+  const int nbp = 4 * ((sh.I + 127) / 128);
   const int64_t rows = (int64_t)sh.T * sh.k;
   const int64_t n = rows * nbp;
   if (n <= 0) return hipSuccess;

@@ -81,6 +81,10 @@ def test_layout_offsets_are_ordered_and_aligned(L):
     assert lay.y - lay.h >= 8192 * 4 * 2880 * 5          # fp32 h + u8 codes
     assert lay.h - lay.x_codes >= 8192 * 4 * 2880        # x codes per routed pair (sorted rows)
     assert lay.x_scales == 0 and lay.h_scales == 0
+    # restaged scale streams: 1 KB per (expert, n-tile, K step)
+    assert lay.y < lay.w13_scale_stream < lay.w2_scale_stream < lay.total_bytes
+    assert lay.w2_scale_stream - lay.w13_scale_stream >= 128 * 23 * 23 * 1024
+    assert lay.total_bytes - lay.w2_scale_stream >= 128 * 12 * 23 * 1024
 
 
 def test_layout_of_mxfp4_activations(L):
@@ -89,14 +93,16 @@ def test_layout_of_mxfp4_activations(L):
     T, H, I = 2048, 2880, 2880
     np_ = T * 4
     assert L.mxfp4_moe_workspace_layout_query(T, H, I, 128, 4, 2, ctypes.byref(lay)) == 0
-    offs = [lay.x_codes, lay.x_scales, lay.h, lay.h_codes, lay.h_scales, lay.y]
+    offs = [lay.x_codes, lay.x_scales, lay.h, lay.h_codes, lay.h_scales, lay.y, lay.w13_scale_stream,
+            lay.w2_scale_stream]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
     assert lay.x_scales - lay.x_codes >= np_ * H // 2    # E2M1 blocks per sorted row
-    assert lay.h - lay.x_scales >= np_ * 92              # 90 scales padded to 92 per row
+    assert lay.h - lay.x_scales >= 23 * np_ * 4 + 512    # 23 steps x 4 scales per row, + read slack
     assert lay.h_codes - lay.h >= np_ * I * 4            # fp32 h
     assert lay.h_scales - lay.h_codes >= np_ * I // 2
-    assert lay.y - lay.h_scales >= np_ * 92
-    assert lay.total_bytes >= lay.y + np_ * H * 4
+    assert lay.y - lay.h_scales >= 23 * np_ * 4 + 512
+    assert lay.w13_scale_stream - lay.y >= np_ * H * 4
+    assert lay.total_bytes - lay.w2_scale_stream >= 128 * 12 * 23 * 1024
 
 
 def _fake(n=1):

@@ -401,10 +401,9 @@ def test_moe_full_size_workloads(mx, full_layer, name):
         np_ = T * k
         sp = _ws_view(ws, lay, "sorted_pairs", np.int32, np_).astype(np.int64)
         inv = _ws_view(ws, lay, "inv_pairs", np.int32, np_)
-        nbh, nbi = 4 * -(-H // 128), 4 * -(-I // 128)
         # x codes of every sorted row (every pair is routed)
         xb = _ws_view(ws, lay, "x_codes", np.uint8, np_ * H // 2).reshape(np_, H // 32, 16)
-        xs = _ws_view(ws, lay, "x_scales", np.uint8, np_ * nbh).reshape(np_, nbh)
+        xs = _step_major(ws, lay, "x_scales", np_, H)
         rb, rs = oracle.quantize_mxfp4(oracle.bf16_bits_to_f64(wl["x"]))
         assert np.array_equal(xs[:, :H // 32], rs[sp // k])
         assert np.array_equal(xb, rb[sp // k])
@@ -424,12 +423,20 @@ def test_moe_full_size_workloads(mx, full_layer, name):
         h_rows = h_t[srows].cpu().numpy().astype(np.float64)
         rhb, rhs = oracle.quantize_mxfp4(h_rows)
         hb = ws[lay["h_codes"]:lay["h_codes"] + np_ * I // 2].view(np_, I // 32, 16)[srows]
-        hs = ws[lay["h_scales"]:lay["h_scales"] + np_ * nbi].view(np_, nbi)[srows]
-        assert np.array_equal(hs.cpu().numpy()[:, :I // 32], rhs)
+        hs = _step_major(ws, lay, "h_scales", np_, I)[srows.cpu().numpy()]
+        assert np.array_equal(hs[:, :I // 32], rhs)
         assert np.array_equal(hb.cpu().numpy(), rhb)
 
 
 # ------------------------------------- MXFP4 activations (FP4 x FP4 MFMA) ----
+
+
+def _step_major(ws, lay, key, rows, K):
+    """MXFP4 activation scales from the workspace's step-major layout
+    [ceil(K/128), rows, 4] as [rows, 4*ceil(K/128)] (blocks past K/32 are pad)."""
+    ns = -(-K // 128)
+    a = _ws_view(ws, lay, key, np.uint8, ns * rows * 4).reshape(ns, rows, 4)
+    return a.transpose(1, 0, 2).reshape(rows, ns * 4)
 
 
 def _mx_act_check(mx, L, x, ids, w, what):
@@ -452,9 +459,8 @@ def _mx_act_check(mx, L, x, ids, w, what):
     sp = _ws_view(ws, lay, "sorted_pairs", np.int32, np_)
     nrows = int(_ws_view(ws, lay, "expert_offsets", np.int32, E + 1)[E])
     pairs = sp[:nrows].astype(np.int64)
-    nbh, nbi = 4 * -(-H // 128), 4 * -(-I // 128)
     xb = _ws_view(ws, lay, "x_codes", np.uint8, np_ * H // 2).reshape(np_, H // 32, 16)[:nrows]
-    xs = _ws_view(ws, lay, "x_scales", np.uint8, np_ * nbh).reshape(np_, nbh)[:nrows]
+    xs = _step_major(ws, lay, "x_scales", np_, H)[:nrows]
     assert np.array_equal(xb, ref["x_blocks"][pairs // k])
     assert np.array_equal(xs[:, :H // 32], ref["x_scales"][pairs // k])
     assert np.all(xs[:, H // 32:] == 127)
@@ -462,7 +468,7 @@ def _mx_act_check(mx, L, x, ids, w, what):
     h_rel = errors(h_gpu, ref["h"].reshape(np_, I)[pairs])[0] if nrows else 0.0
     assert h_rel < 1e-4, "%s: h rel Frobenius %.3e" % (what, h_rel)
     hb = _ws_view(ws, lay, "h_codes", np.uint8, np_ * I // 2).reshape(np_, I // 32, 16)[:nrows]
-    hs = _ws_view(ws, lay, "h_scales", np.uint8, np_ * nbi).reshape(np_, nbi)[:nrows]
+    hs = _step_major(ws, lay, "h_scales", np_, I)[:nrows]
     rb, rs = oracle.quantize_mxfp4(h_gpu)
     assert np.array_equal(hs[:, :I // 32], rs)
     assert np.all(hs[:, I // 32:] == 127)
@@ -487,6 +493,65 @@ def _mx_act_check(mx, L, x, ids, w, what):
     end = errors(got, ref["out"])[0]
     print("%s: h rel %.3e, end-to-end rel %.3e, slack max %.3g" % (what, h_rel, end, slack.max()))
     return h_rel, end
+
+
+def _expected_stream(scales, nout, gateup):
+    """The restaged scale stream from its definition: for expert e, n-tile nt,
+    K step s and LDS row lr of the unit, the scales of blocks 4s .. 4s+3 of
+    the weight row the unit holds in that LDS row (127 past K)."""
+    E, R, nb = scales.shape
+    bn = 128 if gateup else 256
+    NT, ns = -(-nout // bn), -(-nb // 4)
+    lr = np.arange(256)
+    out = np.full((E, NT, ns, 256, 4), 127, dtype=np.uint8)
+    for nt in range(NT):
+        if gateup:
+            rows = np.where(lr < 128, 0, nout) + np.minimum(nt * 128 + (lr & 127), nout - 1)
+        else:
+            rows = np.minimum(nt * 256 + lr, nout - 1)
+        for s4 in range(ns):
+            for j in range(4):
+                b = 4 * s4 + j
+                if b < nb:
+                    out[:, nt, s4, :, j] = scales[:, rows, b]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("act", [synth.ACT_FP8_E4M3, synth.ACT_MXFP4])
+@pytest.mark.parametrize("E,H,I", [(8, 288, 320), (4, 224, 96), (2, 544, 384), (2, 1056, 1024), (3, 2880, 2880)])
+def test_prefill_scale_streams(mx, E, H, I, act):
+    L = synth.layer(seed=E + H + I, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(5, 20, E=E, H=H)
+    ids, w = oracle.route_topk(logits, 2)
+    _, ws, lay = _run_moe(mx, _layer_dev(L), x, ids, w, act, want_ws=True)
+    want13 = _expected_stream(L["w13_scales"], I, True)
+    want2 = _expected_stream(L["w2_scales"], H, False)
+    assert np.array_equal(_ws_view(ws, lay, "w13_scale_stream", np.uint8, want13.size), want13)
+    assert np.array_equal(_ws_view(ws, lay, "w2_scale_stream", np.uint8, want2.size), want2)
+
+
+@pytest.mark.parametrize("act", [synth.ACT_FP8_E4M3, synth.ACT_MXFP4])
+def test_scale_streams_ready_reuses_the_workspace(mx, act):
+    E, H, I, T, k = 8, 288, 320, 40, 4
+    L = synth.layer(seed=91, E=E, H=H, I=I)
+    Ld = _layer_dev(L)
+    logits, x = synth.moe_inputs(92, T, E=E, H=H)
+    xd, ld = to_dev(x, torch), to_dev(logits, torch)
+    ws = torch.zeros(mx.mxfp4_moe_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device="cuda")
+    lay = mx.mxfp4_moe_workspace_layout_query(T, H, I, E, k, act)
+
+    def run(ready):
+        out = mx.mxfp4_moe_layer(xd, ld, k, Ld["w13_blocks"], Ld["w13_scales"], Ld["w13_bias"], Ld["w2_blocks"],
+                                 Ld["w2_scales"], Ld["w2_bias"], act, workspace=ws, scale_streams_ready=ready)[0]
+        torch.cuda.synchronize()
+        return out.clone()
+
+    first = run(False)
+    assert torch.equal(run(True), first)           # the streams left by the first call
+    # the flag does skip the restaging: with the streams cleared the result changes
+    ws[lay["w13_scale_stream"]:lay["total_bytes"]] = 0
+    assert not torch.equal(run(True), first)
+    assert torch.equal(run(False), first)          # and a normal call restages them again
 
 
 @pytest.mark.parametrize("E,H,I,T,k", SMALL)
