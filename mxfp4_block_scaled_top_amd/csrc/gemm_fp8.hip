@@ -640,10 +640,15 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
 
 // The weight scales of every unit in the order the copies take them: for
 // expert e, n-tile nt and K step s, 1 KB holding, for each of the unit's 256
-// LDS rows lr (weight_row), the scale bytes of MX blocks 4s .. 4s+3 (127,
-// i.e. 2^0, past K).  A block takes CPB chunks of 32 LDS rows of one unit:
-// the chunk's rows are read into LDS (one contiguous range unless rows are
-// clamped), then written out step by step.
+// LDS rows lr, the scale bytes of MX blocks 4s .. 4s+3 of weight row
+// weight_row(lr) (127, i.e. 2^0, past K, and for LDS rows past the last
+// weight row, whose outputs are never stored).  A block takes CPB chunks of
+// 32 LDS rows of one unit: the chunk's rows are read into LDS, then written
+// out step by step.
+__device__ __forceinline__ int lds_row_index(bool gateup, int lr, int nt) {
+  return gateup ? nt * (kBN / 2) + (lr & (kBN / 2 - 1)) : nt * kBN + lr;   // before clamping
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void scale_stream_kernel(const uint8_t* __restrict__ ws, int R, int nout, int nb,
                                                            int NT, int nsteps, int cpb, uint32_t* __restrict__ out) {
@@ -654,25 +659,28 @@ __global__ __launch_bounds__(256) void scale_stream_kernel(const uint8_t* __rest
   const int e = unit / NT, nt = unit - e * NT;
   const int t = threadIdx.x;
   const int chunk_dw = 8 * nb;                // dwords of 32 rows
-  bool contiguous = true;
-  for (int c = 0; c < cpb; ++c) {
-    const int r0 = weight_row<GATEUP>(32 * (c0 + c), nt, nout);
-    contiguous = contiguous && weight_row<GATEUP>(32 * (c0 + c) + 31, nt, nout) == r0 + 31;
-  }
-  if (contiguous && cpb == 8 && chunk_dw <= 768) {
-    // each chunk is 32 consecutive rows: 32 * nb bytes at an offset that is a
-    // multiple of 32 from the 4-byte aligned scales; a chunk's base is
-    // wave-uniform and a thread loads dwords t, t + 256, t + 512 of it (an
-    // index past the chunk loads its last dword again, unused).  The loads are
-    // straight-line code, all issued before the first store to LDS (loads
-    // under branches get a full wait at each branch).
+  if (cpb == 8 && chunk_dw <= 768) {
+    // chunk c holds LDS rows 32c .. 32c+31, i.e. weight rows row0 .. row0+31
+    // of which the first nv are real (row index below nout); those are
+    // nv * nb contiguous bytes at an offset that is a multiple of 32 from the
+    // 4-byte aligned scales.  A thread loads dwords t, t + 256, t + 512 of
+    // it, an index past the real bytes taking the chunk's last dword that
+    // holds real bytes (inside the tensor: its size is a multiple of 4).
+    // The loads are straight-line code, all issued before the first store to
+    // LDS (loads under branches get a full wait at each branch).
     uint32_t v[8][3];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(
-          ws + ((int64_t)e * R + weight_row<GATEUP>(32 * (c0 + c), nt, nout)) * nb);
+      const int i0 = lds_row_index(GATEUP, 32 * c, nt);
+      const int half = GATEUP && c >= 4 ? nout : 0;   // first weight row of the chunk's half
+      // a chunk with no real rows reads its half's first row (32-aligned,
+      // unused: written as 127)
+      const int row0 = half + (i0 < nout ? i0 : 0);
+      const int nv = max(1, min(32, nout - i0));
+      const int last = (nv * nb - 1) >> 2;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(ws + ((int64_t)e * R + row0) * nb);
 #pragma unroll
-      for (int q = 0; q < 3; ++q) v[c][q] = src[min(t + 256 * q, chunk_dw - 1)];
+      for (int q = 0; q < 3; ++q) v[c][q] = src[min(t + 256 * q, last)];
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -681,7 +689,7 @@ __global__ __launch_bounds__(256) void scale_stream_kernel(const uint8_t* __rest
         if (t + 256 * q < chunk_dw) reinterpret_cast<uint32_t*>(rows)[c * chunk_dw + t + 256 * q] = v[c][q];
     }
   } else {
-    // chunks with clamped rows (the last n-tile of a tensor), or K > 3072
+    // K > 3072: one byte per thread and step, rows clamped as the GEMM does
     for (int i = t; i < 32 * cpb * nb; i += blockDim.x) {
       const int l = i / nb, b = i - l * nb;
       rows[i] = ws[((int64_t)e * R + weight_row<GATEUP>(32 * c0 + l, nt, nout)) * nb + b];
@@ -692,6 +700,7 @@ __global__ __launch_bounds__(256) void scale_stream_kernel(const uint8_t* __rest
   // consecutive words)
   const int l = t;
   if (l < 32 * cpb) {
+    const bool real = lds_row_index(GATEUP, 32 * c0 + l, nt) < nout;
     const uint8_t* src = rows + l * nb;
     uint32_t* dst = out + (int64_t)unit * nsteps * 256 + 32 * c0 + l;
     for (int st = 0; st < nsteps; ++st) {
@@ -699,7 +708,7 @@ __global__ __launch_bounds__(256) void scale_stream_kernel(const uint8_t* __rest
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int b = 4 * st + j;
-        word |= (uint32_t)(b < nb ? src[b] : 127u) << (8 * j);
+        word |= (uint32_t)(real && b < nb ? src[b] : 127u) << (8 * j);
       }
       dst[st * 256] = word;
     }

@@ -498,22 +498,22 @@ def _mx_act_check(mx, L, x, ids, w, what):
 def _expected_stream(scales, nout, gateup):
     """The restaged scale stream from its definition: for expert e, n-tile nt,
     K step s and LDS row lr of the unit, the scales of blocks 4s .. 4s+3 of
-    the weight row the unit holds in that LDS row (127 past K)."""
+    the weight row the unit holds in that LDS row (127 past K, and for LDS
+    rows past the last weight row)."""
     E, R, nb = scales.shape
     bn = 128 if gateup else 256
     NT, ns = -(-nout // bn), -(-nb // 4)
     lr = np.arange(256)
     out = np.full((E, NT, ns, 256, 4), 127, dtype=np.uint8)
     for nt in range(NT):
-        if gateup:
-            rows = np.where(lr < 128, 0, nout) + np.minimum(nt * 128 + (lr & 127), nout - 1)
-        else:
-            rows = np.minimum(nt * 256 + lr, nout - 1)
+        idx = nt * 128 + (lr & 127) if gateup else nt * 256 + lr
+        real = idx < nout
+        rows = (np.where(lr < 128, 0, nout) if gateup else 0) + np.minimum(idx, nout - 1)
         for s4 in range(ns):
             for j in range(4):
                 b = 4 * s4 + j
                 if b < nb:
-                    out[:, nt, s4, :, j] = scales[:, rows, b]
+                    out[:, nt, s4, real, j] = scales[:, rows[real], b]
     return out.reshape(-1)
 
 
