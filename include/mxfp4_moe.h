@@ -129,8 +129,9 @@ typedef struct {
                                MXFP4-activation mode: uint8 [T*k, H/32, 16]
                                E2M1 blocks of x in the same row order */
   uint64_t h;               /* BF16 mode: bf16 hi [T*k, I] then bf16 lo [T*k, I]
-                               with h = hi + lo; FP8 and MXFP4-activation modes:
-                               fp32 [T*k, I]; rows in sorted order */
+                               with h = hi + lo; FP8 mode: fp32 [T*k, I]; rows
+                               in sorted order.  MXFP4-activation mode: no
+                               bytes (h is quantised in the gate_up GEMM) */
   uint64_t h_codes;         /* FP8 mode: uint8 [T*k, I] E4M3 codes of h;
                                MXFP4-activation mode: uint8 [T*k, I/32, 16]
                                E2M1 blocks of h */

@@ -91,7 +91,7 @@ void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mod
   } else if (act_mode == MXFP4_ACT_MXFP4) {
     L->x_codes = o; o = up(o + (size_t)np * H / 2);
     L->x_scales = o; o = up(o + (size_t)mx::act_scale_bytes(np, (int)H));
-    L->h = o; o = up(o + (size_t)np * I * 4);
+    L->h = o;                      // h is quantised in the GEMM epilogue: no fp32 copy
     L->h_codes = o; o = up(o + (size_t)np * I / 2);
     L->h_scales = o; o = up(o + (size_t)mx::act_scale_bytes(np, (int)I));
   } else {
@@ -290,8 +290,6 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
                                   reinterpret_cast<const uint32_t*>(ws.status + mx::kStAmaxH),
                                   reinterpret_cast<float*>(ws.status + mx::kStScaleH), s),
             "quant h launch");
-  } else if (a4) {
-    MX_STEP(mx::launch_quant_h_mxfp4(sh, ws, s), "quant h launch");
   }
   if (restage) MX_STEP(mx::launch_scale_stream(sh, w, ws, false, s), "w2 scale stream launch");
   MX_STEP(mark(MXFP4_STAGE_QUANT_H), "event record");

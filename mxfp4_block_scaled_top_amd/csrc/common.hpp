@@ -75,6 +75,16 @@ __device__ __forceinline__ uint32_t e4m3_encode(float q) {
   return sign | (uint32_t)n;
 }
 
+// E2M1 magnitude code of q >= 0 (|v| / 2^X of the MX block rule): the count
+// of rounding thresholds passed.  A tie at a threshold goes to the code whose
+// mantissa bit is 0, so the boundary below an odd code is exclusive (q > t)
+// and below an even code inclusive; q past 6 saturates at code 7.
+__device__ __forceinline__ uint32_t e2m1_round_mag(float q) {
+  return (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) +
+         (uint32_t)(q >= 1.75f) + (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) +
+         (uint32_t)(q > 5.0f);
+}
+
 // silu(z) = z / (1 + exp(-z)); exp overflow gives -0 for very negative z.
 __device__ __forceinline__ float silu(float z) {
   return __fdividef(z, 1.0f + __expf(-z));

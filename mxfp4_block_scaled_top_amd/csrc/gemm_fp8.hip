@@ -104,7 +104,12 @@ struct PrefillArgs {
   const uint8_t* asc;      // E2M1 activations: E8M0 [nsteps, sorted rows, 4] (step-major)
   int64_t asc_step;        // bytes per step of asc (4 * sorted rows)
   int scale_word;          // status word holding the per-tensor activation scale (E4M3)
-  float* out;              // h [rows, I] (gate_up) or y [rows, H] (down), fp32
+  float* out;              // h [rows, I] (gate_up, E4M3 mode) or y [rows, H] (down), fp32
+  // gate_up with E2M1 activations: h quantised in the epilogue into E2M1
+  // blocks [rows, I/32, 16] and step-major E8M0 scales [ceil(I/128), rows, 4]
+  uint8_t* h_codes;
+  uint8_t* h_scales;
+  int64_t h_rows;          // rows of the step-major scale array (T*k)
 };
 
 // 8 E4M3 codes (two dwords) -> 8 bf16 (exact: every E4M3 value is a bf16).
@@ -586,7 +591,55 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
 
     // ---- epilogue of the unit: the lane holds rows 4g + jj of each 16-row
     // weight group and sorted row r of each 16-row token group
-    if (GATEUP) {
+    if (GATEUP && A4) {
+      // the wave's 32 h columns [ib, ib + 32) are MX block b of each token
+      // row: lane (r, g) holds columns 4g..4g+3 (half 0) and 16+4g..16+4g+3
+      // (half 1).  The block is quantised here (the rule of
+      // quant_x_mxfp4_sorted_kernel): amax over the row's four lanes, shared
+      // exponent, codes; no fp32 h is written.  Every lane takes part in the
+      // shuffles; only real rows store.
+      const int ib = nt * (kBN / 2) + 32 * wn;
+      if (ib < a.nout) {
+        const int b = ib / kBlockElems, nbh = a.nout / kBlockElems;
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg) {
+          const int row = rb + 64 * wm + 16 * tg + r;
+          float hv[8];
+          uint32_t am = 0;
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const float gate = acc[half][tg][jj] + bf16_of(bq[2 * half], jj);
+              const float up = acc[half + 2][tg][jj] + bf16_of(bq[2 * half + 1], jj);
+              hv[4 * half + jj] = silu_accurate(gate) * up;
+              am = max(am, __float_as_uint(hv[4 * half + jj]) & 0x7fffffffu);
+            }
+          am = max(am, (uint32_t)__shfl_xor((int)am, 16, 64));
+          am = max(am, (uint32_t)__shfl_xor((int)am, 32, 64));
+          const int x = min(max((int)(am >> 23) - 127 - 2, -125), 125);
+          const float inv = __uint_as_float((uint32_t)(127 - x) << 23);
+          uint32_t q[2] = {0u, 0u};     // nibbles of columns 4g.. (half 0) and 16+4g.. (half 1)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t bits = __float_as_uint(hv[i]);
+            const uint32_t code = e2m1_round_mag(__uint_as_float(bits & 0x7fffffffu) * inv) | ((bits >> 31) << 3);
+            q[i >> 2] |= code << (4 * (i & 3));
+          }
+          if (row < re) {
+            uint8_t* hb = a.h_codes + (int64_t)row * (a.nout / 2) + b * kBlockBytes;
+            *reinterpret_cast<uint16_t*>(hb + 2 * g) = (uint16_t)q[0];
+            *reinterpret_cast<uint16_t*>(hb + 8 + 2 * g) = (uint16_t)q[1];
+            if (g == 0) {
+              a.h_scales[((int64_t)(b >> 2) * a.h_rows + row) * 4 + (b & 3)] = (uint8_t)(x + 127);
+              if (b == nbh - 1)   // the pad bytes of the row's last step
+                for (int p = nbh; p < 4 * ((nbh + 3) / 4); ++p)
+                  a.h_scales[((int64_t)(p >> 2) * a.h_rows + row) * 4 + (p & 3)] = 127;
+            }
+          }
+        }
+      }
+    } else if (GATEUP) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int i0 = nt * (kBN / 2) + 32 * wn + 16 * half;
@@ -801,7 +854,10 @@ hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const 
   a.asc = ws.x_scales;
   a.asc_step = (int64_t)4 * sh.T * sh.k;
   a.scale_word = -1;
-  a.out = static_cast<float*>(ws.h);
+  a.out = nullptr;
+  a.h_codes = ws.h_codes;
+  a.h_scales = ws.h_scales;
+  a.h_rows = (int64_t)sh.T * sh.k;
   return launch_prefill<true, true>(a, ws, s);
 }
 

@@ -25,7 +25,7 @@ struct WsPtrs {
   int* chunk_ranks;
   int* tiles;
   uint8_t* x_codes;  // FP8: E4M3 codes; MXFP4 activations: E2M1 blocks
-  void* h;           // bf16 hi|lo (BF16 mode) or fp32 (FP8 / MXFP4-activation modes)
+  void* h;           // bf16 hi|lo (BF16 mode) or fp32 (FP8 mode)
   uint8_t* h_codes;
   float* y;
   uint8_t* x_scales;  // MXFP4 activations: E8M0 [ceil(H/128), T*k, 4] (step-major)
@@ -105,11 +105,10 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
 hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
                                int64_t ntile_bound, hipStream_t s);
 
-// MXFP4 activations: x in expert-sorted row order, and fp32 h (rows below
-// offsets[E]), each as E2M1 blocks + padded E8M0 scale rows.
+// MXFP4 activations: x in expert-sorted row order as E2M1 blocks + step-major
+// E8M0 scales (h is quantised by the gate_up GEMM's epilogue).
 hipError_t launch_quant_x_mxfp4_sorted(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
                                        hipStream_t s);
-hipError_t launch_quant_h_mxfp4(const MoeShape& sh, const WsPtrs& ws, hipStream_t s);
 
 // Restage one weight tensor's E8M0 scales (w13 when gateup, else w2) into
 // the order the prefill GEMM copies them.

@@ -18,15 +18,6 @@
 
 namespace mx {
 
-// Magnitude code of q in [0, 8): count of rounding thresholds passed.  A tie
-// at a threshold goes to the code whose mantissa bit is 0, so the boundary
-// below an odd code is exclusive (q > t) and below an even code inclusive.
-__device__ __forceinline__ uint32_t e2m1_round_mag(float q) {
-  return (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) +
-         (uint32_t)(q >= 1.75f) + (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) +
-         (uint32_t)(q > 5.0f);
-}
-
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ w, int64_t nblocks,
                                                           uint8_t* __restrict__ blocks,
                                                           uint8_t* __restrict__ scales) {
@@ -69,8 +60,8 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// MXFP4 activations (FP4 x FP4 MoE mode): the same block rule on x (bf16) and
-// on the SwiGLU output h (fp32).  Scales are stored step-major: block b of
+// MXFP4 activations (FP4 x FP4 MoE mode): the same block rule on x (bf16);
+// h is quantised in the gate_up GEMM's epilogue.  Scales are stored step-major: block b of
 // row r at ((b / 4) * rows + r) * 4 + b % 4, so one 128-element K step's
 // scales of consecutive rows are contiguous; blocks past K (up to the whole
 // step) hold 127 (2^0).
@@ -132,32 +123,6 @@ __global__ __launch_bounds__(256) void quant_x_mxfp4_sorted_kernel(
   }
 }
 
-// One thread per (sorted row r < offsets[E], scale slot c < nbp) of fp32 h.
-__global__ __launch_bounds__(256) void quant_h_mxfp4_kernel(const float* __restrict__ h, int64_t rows,
-                                                            int I, int nbp, const int* __restrict__ nvalid,
-                                                            uint8_t* __restrict__ hb,
-                                                            uint8_t* __restrict__ hs) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= rows * nbp) return;
-  const int64_t r = idx / nbp;
-  const int c = (int)(idx - r * nbp);
-  if (r >= *nvalid) return;
-  uint32_t sc = 127u;
-  if (c < I / kBlockElems) {
-    const float4* src = reinterpret_cast<const float4*>(h + r * I + c * kBlockElems);
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 q = src[i];
-      v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
-    }
-    uint4 packed;
-    sc = mx_encode32(v, packed);
-    *reinterpret_cast<uint4*>(hb + r * (I / 2) + c * kBlockBytes) = packed;
-  }
-  hs[((c >> 2) * rows + r) * 4 + (c & 3)] = (uint8_t)sc;
-}
-
 hipError_t launch_quant_x_mxfp4_sorted(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
                                        hipStream_t s) {
   const int nbp = 4 * ((sh.H + 127) / 128);
@@ -165,17 +130,6 @@ hipError_t launch_quant_x_mxfp4_sorted(const uint16_t* x, const MoeShape& sh, co
   if (n <= 0) return hipSuccess;
   quant_x_mxfp4_sorted_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, sh.T, sh.H, sh.k, nbp, ws.inv,
                                                                           ws.x_codes, ws.x_scales);
-  return hipGetLastError();
-}
-
-hipError_t launch_quant_h_mxfp4(const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
-  const int nbp = 4 * ((sh.I + 127) / 128);
-  const int64_t rows = (int64_t)sh.T * sh.k;
-  const int64_t n = rows * nbp;
-  if (n <= 0) return hipSuccess;
-  quant_h_mxfp4_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<const float*>(ws.h), rows, sh.I,
-                                                                   nbp, ws.offsets + sh.E, ws.h_codes,
-                                                                   ws.h_scales);
   return hipGetLastError();
 }
 

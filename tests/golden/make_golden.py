@@ -85,6 +85,17 @@ def mx_code_gap(h32):
     return gap.reshape(h32.shape)
 
 
+def mx_scale_ambiguous(h32):
+    """Per 32-element block of h32 [..., I]: True where the shared exponent of
+    an h within the stated error may differ from that of h32."""
+    lead, I = h32.shape[:-1], h32.shape[-1]
+    hb = np.asarray(h32, dtype=np.float64).reshape(lead + (I // 32, 32))
+    amax = np.abs(hb).max(axis=-1)
+    wa = H_REL_ERR * 2.1 * amax + H_ABS_ERR * np.ldexp(1.0, oracle.quant.block_exponent(amax))
+    return (oracle.quant.block_exponent(np.maximum(amax - wa, 0.0))
+            != oracle.quant.block_exponent(amax + wa))
+
+
 def output_slack(h32, ids, w, layer, tokens, gap_fn):
     """slack[ti, :] = sum_j |w[t, j]| |W2[e]| @ gap(h32[t, j]) for t = tokens[ti]."""
     k = ids.shape[1]

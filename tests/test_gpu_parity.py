@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from golden.make_golden import mx_code_gap, output_slack
+from golden.make_golden import mx_code_gap, mx_scale_ambiguous, output_slack
 from helpers import (assert_close, assert_close_rounded, assert_close_rounded_slack, assert_close_slack,
                      bf16_bits_to_f64, bf16_dev_to_f64, errors, no_constant_rows, to_dev)
 
@@ -408,24 +408,13 @@ def test_moe_full_size_workloads(mx, full_layer, name):
         assert np.array_equal(xs[:, :H // 32], rs[sp // k])
         assert np.array_equal(xb, rb[sp // k])
         del xb, rb
-        # h within the error the slack assumes, on the sampled pairs
-        h_t = ws[lay["h"]:lay["h"] + np_ * I * 4].view(torch.float32).view(np_, I)
-        rel, absu = float(gold["h_rel_err"]), float(gold["h_abs_err"])
-        rows = torch.from_numpy(inv[gold["h_pairs"]].astype(np.int64)).cuda()
-        h_gpu = h_t[rows].cpu().numpy().astype(np.float64)
-        h_ref = gold["h_ref"].astype(np.float64)
-        hb_ref = h_ref.reshape(len(h_ref), I // 32, 32)
-        bscale = np.ldexp(1.0, oracle.quant.block_exponent(np.abs(hb_ref).max(axis=-1)))[..., None]
-        bound = rel * np.abs(hb_ref) + absu * bscale
-        assert np.all(np.abs(h_gpu.reshape(hb_ref.shape) - hb_ref) <= bound)
-        # h codes on a sample of rows: the oracle quantiser of the kernel's own h
-        srows = torch.from_numpy(np.random.default_rng(1).choice(np_, 512, replace=False)).cuda()
-        h_rows = h_t[srows].cpu().numpy().astype(np.float64)
-        rhb, rhs = oracle.quantize_mxfp4(h_rows)
-        hb = ws[lay["h_codes"]:lay["h_codes"] + np_ * I // 2].view(np_, I // 32, 16)[srows]
-        hs = _step_major(ws, lay, "h_scales", np_, I)[srows.cpu().numpy()]
-        assert np.array_equal(hs[:, :I // 32], rhs)
-        assert np.array_equal(hb.cpu().numpy(), rhb)
+        # h codes of the sampled pairs against the oracle's h, where unique
+        rows = inv[gold["h_pairs"]].astype(np.int64)
+        hb = ws[lay["h_codes"]:lay["h_codes"] + np_ * I // 2].view(np_, I // 32, 16)
+        hb = hb[torch.from_numpy(rows).cuda()].cpu().numpy()
+        hs = _step_major(ws, lay, "h_scales", np_, I)[rows]
+        h32 = gold["h_ref"].astype(np.float64)          # the oracle's h, rounded to fp32
+        _mx_h_codes_check(hb, hs[:, :I // 32], h32, name)
 
 
 # ------------------------------------- MXFP4 activations (FP4 x FP4 MFMA) ----
@@ -439,16 +428,31 @@ def _step_major(ws, lay, key, rows, K):
     return a.transpose(1, 0, 2).reshape(rows, ns * 4)
 
 
+def _mx_h_codes_check(hb, hs, h32, what):
+    """The kernel's MXFP4 codes of h (blocks hb, scales hs) against the oracle
+    quantiser applied to the oracle's h32, for the same rows: equal wherever
+    no h within the stated h error rounds differently (the shared exponent
+    where the block's amax cannot cross a power of two, the dequantised value
+    of an element wherever its code is unique); the rest may take either
+    neighbour, and the output slack covers them."""
+    rb, rs = oracle.quantize_mxfp4(h32)
+    amb_scale = mx_scale_ambiguous(h32)
+    assert np.array_equal(hs[~amb_scale], rs[~amb_scale]), what + ": h scales"
+    unique = mx_code_gap(h32) == 0
+    got_v, ref_v = oracle.dequant(hb, hs), oracle.dequant(rb, rs)
+    assert np.array_equal(got_v[unique], ref_v[unique]), what + ": h codes"
+    assert unique.mean() > 0.99, what + ": too many ambiguous h codes"
+
+
 def _mx_act_check(mx, L, x, ids, w, what):
     """The FP4 x FP4 layer against the oracle, step by step.
 
-    The x codes are unique and compared bit for bit.  h is compared with the
-    oracle's h.  The h codes are the oracle quantiser applied to the kernel's
-    own fp32 h, bit for bit: where an h value lies within the contraction's
-    rounding of a code boundary (or a block's amax of a power of two) both
-    codes are correct, and the kernel's h decides.  The output is then
-    compared with the oracle's down projection and combine of those codes.
-    Returns (relative error of h, relative error against the float64 layer)."""
+    The x codes are unique and compared bit for bit.  The h codes (quantised
+    in the gate_up epilogue; no fp32 h is kept) are compared with the oracle
+    quantiser of the oracle's h wherever they are unique.  The output is
+    compared with the oracle's down projection and combine of the kernel's
+    own h codes, and end to end within the slack of the ambiguous codes.
+    Returns the relative error against the float64 layer."""
     E = L["w13_blocks"].shape[0]
     T, H = x.shape
     I = L["w2_blocks"].shape[2] * 32
@@ -464,15 +468,11 @@ def _mx_act_check(mx, L, x, ids, w, what):
     assert np.array_equal(xb, ref["x_blocks"][pairs // k])
     assert np.array_equal(xs[:, :H // 32], ref["x_scales"][pairs // k])
     assert np.all(xs[:, H // 32:] == 127)
-    h_gpu = _ws_view(ws, lay, "h", np.float32, np_ * I).reshape(np_, I)[:nrows].astype(np.float64)
-    h_rel = errors(h_gpu, ref["h"].reshape(np_, I)[pairs])[0] if nrows else 0.0
-    assert h_rel < 1e-4, "%s: h rel Frobenius %.3e" % (what, h_rel)
     hb = _ws_view(ws, lay, "h_codes", np.uint8, np_ * I // 2).reshape(np_, I // 32, 16)[:nrows]
     hs = _step_major(ws, lay, "h_scales", np_, I)[:nrows]
-    rb, rs = oracle.quantize_mxfp4(h_gpu)
-    assert np.array_equal(hs[:, :I // 32], rs)
     assert np.all(hs[:, I // 32:] == 127)
-    assert np.array_equal(hb, rb)
+    if nrows:
+        _mx_h_codes_check(hb, hs[:, :I // 32], ref["h32"].reshape(np_, I)[pairs], what)
     # y = W2 h' + b2 of the kernel's h codes and the weighted combine, float64
     hq = oracle.dequant(hb, hs[:, :I // 32])
     e_of = ids.reshape(-1).astype(np.int64)[pairs]
@@ -491,8 +491,8 @@ def _mx_act_check(mx, L, x, ids, w, what):
     slack = output_slack(ref["h32"], ids64, w, L, np.arange(T), mx_code_gap)
     assert_close_rounded_slack(got, ref["out"], slack, what + " end to end")
     end = errors(got, ref["out"])[0]
-    print("%s: h rel %.3e, end-to-end rel %.3e, slack max %.3g" % (what, h_rel, end, slack.max()))
-    return h_rel, end
+    print("%s: end-to-end rel %.3e, slack max %.3g" % (what, end, slack.max()))
+    return end
 
 
 def _expected_stream(scales, nout, gateup):
