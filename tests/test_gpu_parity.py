@@ -518,7 +518,8 @@ def _expected_stream(scales, nout, gateup):
 
 
 @pytest.mark.parametrize("act", [synth.ACT_FP8_E4M3, synth.ACT_MXFP4])
-@pytest.mark.parametrize("E,H,I", [(8, 288, 320), (4, 224, 96), (2, 544, 384), (2, 1056, 1024), (3, 2880, 2880)])
+@pytest.mark.parametrize("E,H,I", [(8, 288, 320), (4, 224, 96), (2, 544, 384), (2, 1056, 1024), (3, 2880, 2880),
+                                   (2, 3200, 3328)])
 def test_prefill_scale_streams(mx, E, H, I, act):
     L = synth.layer(seed=E + H + I, E=E, H=H, I=I)
     logits, x = synth.moe_inputs(5, 20, E=E, H=H)
@@ -552,6 +553,22 @@ def test_scale_streams_ready_reuses_the_workspace(mx, act):
     ws[lay["w13_scale_stream"]:lay["total_bytes"]] = 0
     assert not torch.equal(run(True), first)
     assert torch.equal(run(False), first)          # and a normal call restages them again
+
+
+@pytest.mark.parametrize("act", [synth.ACT_FP8_E4M3, synth.ACT_MXFP4])
+def test_prefill_long_k(mx, act):
+    # K = 3200 and 3328 (more than 3072: the scale restage's generic path),
+    # 25 and 26 K steps with ragged last steps
+    E, H, I, T, k = 2, 3200, 3328, 6, 2
+    L = synth.layer(seed=97, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(98, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    if act == synth.ACT_MXFP4:
+        _mx_act_check(mx, L, x, ids, w, "long K mxfp4-act")
+    else:
+        got = _run_moe(mx, _layer_dev(L), x, ids, w, act)
+        ref = oracle.moe_forward_routed(x, ids, w, **L, act_mode=act)
+        assert_close_rounded(got, ref["out"], "long K fp8")
 
 
 @pytest.mark.parametrize("E,H,I,T,k", SMALL)
