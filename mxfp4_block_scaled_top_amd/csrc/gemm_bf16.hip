@@ -357,6 +357,12 @@ __device__ __forceinline__ uint4 row_rotate4(uint4 v) {
                     (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctrl, 0xf, 0xf, true));
 }
 
+template <int Q>
+__device__ __forceinline__ float rot4_f32(float v) {
+  constexpr int ctrl = 0x120 + 16 - 4 * Q;   // DPP row_ror:(16 - 4Q)
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, true));
+}
+
 // NV: NVFP4 weights (16-element blocks with E4M3 scales: two scales per
 // 32-element chunk; the tensor's global scale is applied to the sums).
 template <int MODE, int HG, bool NV>
@@ -483,6 +489,10 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(b), acc, 0, 0, 0);
     if (MODE == kDown) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(bl), acc, 0, 0, 0);
   };
+  // The activations stay in the compact layout: lane (c, g) holds K chunk
+  // (c / 4) % 4 of column c % 4.  MFMA step Q multiplies weight chunk Q, so
+  // in accumulator Q only columns 4Q .. 4Q+3 hold valid sums (those of
+  // columns 0-3); the epilogue rotates them into place once per unit.
 
   // unit u = m-tile m, row tile nt (stepped without dividing)
   int64_t u = u_begin;
@@ -538,6 +548,8 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     }
     v4f acc0 = {0.f, 0.f, 0.f, 0.f};
     v4f acc1 = {0.f, 0.f, 0.f, 0.f};
+    v4f acc2 = {0.f, 0.f, 0.f, 0.f};
+    v4f acc3 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jj = 0; jj < HG; ++jj) {
       const uint4 w = wreg[jj];
@@ -556,17 +568,21 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
       const uint4 lo = MODE == kDown ? xl[jj] : xa[jj];
       if (NV) {
         step(acc0, fp4x8_times_bf16(w.x, f0), xa[jj], lo);
-        step(acc1, fp4x8_times_bf16(w.y, f0), row_rotate4<1>(xa[jj]), row_rotate4<1>(lo));
-        step(acc0, fp4x8_times_bf16(w.z, f1), row_rotate4<2>(xa[jj]), row_rotate4<2>(lo));
-        step(acc1, fp4x8_times_bf16(w.w, f1), row_rotate4<3>(xa[jj]), row_rotate4<3>(lo));
+        step(acc1, fp4x8_times_bf16(w.y, f0), xa[jj], lo);
+        step(acc2, fp4x8_times_bf16(w.z, f1), xa[jj], lo);
+        step(acc3, fp4x8_times_bf16(w.w, f1), xa[jj], lo);
       } else {
         step(acc0, fp4x8_to_bf16(w.x, f0), xa[jj], lo);
-        step(acc1, fp4x8_to_bf16(w.y, f0), row_rotate4<1>(xa[jj]), row_rotate4<1>(lo));
-        step(acc0, fp4x8_to_bf16(w.z, f1), row_rotate4<2>(xa[jj]), row_rotate4<2>(lo));
-        step(acc1, fp4x8_to_bf16(w.w, f1), row_rotate4<3>(xa[jj]), row_rotate4<3>(lo));
+        step(acc1, fp4x8_to_bf16(w.y, f0), xa[jj], lo);
+        step(acc2, fp4x8_to_bf16(w.z, f1), xa[jj], lo);
+        step(acc3, fp4x8_to_bf16(w.w, f1), xa[jj], lo);
       }
     }
-    v4f acc = acc0 + acc1;
+    // lane c of each 16-lane row takes chunk Q's sums from lane c + 4Q
+    v4f acc;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      acc[jj] = (acc0[jj] + rot4_f32<1>(acc1[jj])) + (rot4_f32<2>(acc2[jj]) + rot4_f32<3>(acc3[jj]));
     if (kh == 1) red[lane] = acc;
     // wave 1's partial sums are in LDS; the next unit's DMA stays in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
