@@ -682,7 +682,14 @@ def test_quantized_weights_feed_the_linear(mx):
                                            (8, 288, 320, 16, 4, synth.ACT_FP8_E4M3),
                                            (512, 64, 64, 1, 4, synth.ACT_BF16),
                                            (48, 96, 128, 9, 2, synth.ACT_BF16),
-                                           (200, 64, 96, 13, 3, synth.ACT_BF16)])
+                                           (200, 64, 96, 13, 3, synth.ACT_BF16),
+                                           # single-wave permutation: <= 128 pairs, <= 128 experts, k <= 16
+                                           (128, 256, 128, 32, 4, synth.ACT_BF16),
+                                           (128, 256, 128, 31, 4, synth.ACT_FP8_E4M3),
+                                           (64, 96, 128, 25, 5, synth.ACT_BF16),
+                                           (16, 64, 64, 8, 16, synth.ACT_BF16),
+                                           (3, 64, 64, 2, 3, synth.ACT_BF16),
+                                           (127, 64, 96, 42, 3, synth.ACT_BF16)])
 def test_moe_layer_equals_route_then_forward(mx, E, H, I, T, k, act):
     L = synth.layer(seed=E + H, E=E, H=H, I=I)
     logits, x = synth.moe_inputs(T + 3, T, E=E, H=H)
@@ -697,6 +704,32 @@ def test_moe_layer_equals_route_then_forward(mx, E, H, I, T, k, act):
     assert torch.equal(ids, ids_b) and torch.equal(w, w_b)
     assert torch.equal(out_a, out_b)
     rid, rw = oracle.route_topk(logits, k)
+    assert np.array_equal(ids_b.cpu().numpy(), rid)
+
+
+@pytest.mark.parametrize("T,E,k", [(32, 128, 4), (7, 128, 16), (25, 100, 5)])
+def test_moe_layer_routing_ties_and_signed_zero(mx, T, E, k):
+    """Tie-heavy logits (small integers, all-zero rows, -0 next to +0) routed by
+    the layer's fused route + permutation launch equal the stand-alone router
+    bitwise, and the oracle's choices."""
+    rng = np.random.default_rng(T + E)
+    logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    logits[0] = 0.0
+    logits[1, ::3] = -0.0
+    logits[2, :] = -np.inf
+    logits[2, 5] = 1.0
+    H = I = 64
+    L = synth.layer(seed=9, E=E, H=H, I=I)
+    Ld = _layer_dev(L)
+    x = synth.f32_to_bf16_bits(rng.normal(size=(T, H)).astype(np.float32))
+    lg = to_dev(logits, torch)
+    ids, w = mx.mxfp4_route_topk(lg, k)
+    _, ids_b, w_b = mx.mxfp4_moe_layer(to_dev(x, torch), lg, k, Ld["w13_blocks"], Ld["w13_scales"],
+                                       Ld["w13_bias"], Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"],
+                                       synth.ACT_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_b) and torch.equal(w, w_b)
+    rid, _ = oracle.route_topk(logits, k)
     assert np.array_equal(ids_b.cpu().numpy(), rid)
 
 
