@@ -5,9 +5,11 @@ A step is one pass of the hot path over one batch: router top-k, then the MoE
 layer (permutation, [FP8 quantisation of x], gate_up GEMM + SwiGLU, [FP8
 quantisation of h], down GEMM, weighted combine), all through the C ABI.
 Weights, logits and activations are resident in HBM before timing starts.
-Before every timed step a 1 GiB buffer is overwritten so the step reads its
-weights from HBM and not from the 256 MB last-level cache; each step is
-bracketed by events on the launch stream and the flush is outside them.
+Before every timed step a 1 GiB buffer is read through (a reduction) so the
+step reads its weights from HBM and not from the 256 MB last-level cache;
+each step is bracketed by events on the launch stream and the eviction is
+outside them.  (--flush write overwrites the buffer instead, which leaves
+dirty lines whose write-back then competes with the timed step.)
 
 The headline line is the 32-token decode batch (hidden 2880, 128 experts,
 top-4, bf16 activations).  The same run also measures the 4-token decode,
@@ -78,10 +80,21 @@ def source_digest(files):
 
 
 class Runner:
-    def __init__(self, torch, mx):
+    def __init__(self, torch, mx, flush_mode="read"):
         self.torch = torch
         self.mx = mx
-        self.flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.flush_mode = flush_mode
+        self.flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def evict(self, i):
+        """Push the layer out of the 256 MB last-level cache and the L2s.  "read"
+        streams the 1 GiB buffer through a reduction, leaving clean lines behind;
+        "write" overwrites it, which also leaves up to 256 MB of dirty lines that
+        are written back while the next step runs."""
+        if self.flush_mode == "write":
+            self.flush.fill_(float(i))
+        else:
+            self._sink = self.flush.amax()
 
     def dev(self, a):
         torch = self.torch
@@ -95,7 +108,7 @@ class Runner:
         torch, mx = self.torch, self.mx
         for _ in range(warmup):
             if flush:
-                self.flush.fill_(1.0)
+                self.evict(1)
             step(None)
         torch.cuda.synchronize()
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -107,7 +120,7 @@ class Runner:
         t0 = time.perf_counter()
         for i in range(steps):
             if flush:
-                self.flush.fill_(float(i))
+                self.evict(i)
             starts[i].record()
             step(evs[i] if evs else None)
             ends[i].record()
@@ -326,6 +339,8 @@ def main():
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--primary-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", choices=("read", "write"), default="read",
+                    help="how the 1 GiB cache eviction before each timed step touches its buffer")
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (3 times), the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
@@ -351,7 +366,7 @@ def main():
                           "launches": 3}))
         return
     mx.lib()
-    run = Runner(torch, mx)
+    run = Runner(torch, mx, args.flush)
     L = synth.layer()
     Ld = {k: run.dev(v) for k, v in L.items()}
     del L
@@ -408,7 +423,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": prim["tokens"], "experts": 128, "topk": 4,
                    "hidden": 2880, "intermediate": 2880, "weights": "mxfp4", "act": prim["act"],
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)", "cache_eviction": "%s 1 GiB before each step" % args.flush},
         "hbm_frac": prim["layer_hbm_frac"],
         "roofline": roof,
         "detail": prim,
