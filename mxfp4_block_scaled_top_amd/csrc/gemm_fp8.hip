@@ -110,6 +110,7 @@ struct PrefillArgs {
   uint8_t* h_codes;
   uint8_t* h_scales;
   int64_t h_rows;          // rows of the step-major scale array (T*k)
+  int sched_xcd;           // units in expert-major order, one contiguous share per XCD (see unit_tile)
 };
 
 // 8 E4M3 codes (two dwords) -> 8 bf16 (exact: every E4M3 value is a bf16).
@@ -143,6 +144,34 @@ __device__ __forceinline__ int3 tile_entry(const int* p) {
   v4i_t v;
   asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
   return make_int3(v.x, v.y, v.z);
+}
+
+// Word 3 of a tile-list entry (the expert's first entry and entry count).
+__device__ __forceinline__ int tile_word_at(const int* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0xc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  return v;
+}
+
+// Unit v of the schedule -> (row tile, n-tile).  Plain order: v = tile * NT
+// + nt.  Expert-major order (sched_xcd): the units of expert e, whose row
+// tiles are entries [f, f + c) of the list, are v in [NT f, NT (f + c)),
+// n-tile-major inside: v = NT f + nt c + i for tile f + i.  The grid hands
+// each XCD (blocks b with the same b mod 8, the hardware's round-robin
+// placement) one contiguous eighth of that order, round-robin over its
+// blocks, so the blocks of one XCD stream the same weight n-tile for
+// different row tiles of a hot expert and share it in that XCD's L2.
+__device__ __forceinline__ void unit_tile(const PrefillArgs& a, const int* tiles, int v, int& tile, int& nt) {
+  if (a.sched_xcd) {
+    const int w = tile_word_at(tiles + kTileInts * (v / a.NT));
+    const int f = w & 0xffff, c = w >> 16;
+    const int local = v - a.NT * f;
+    nt = local / c;
+    tile = f + (local - nt * c);
+  } else {
+    tile = v / a.NT;
+    nt = v - tile * a.NT;
+  }
 }
 
 // Weight row (within the expert) held in LDS row lr of n-tile nt, clamped
@@ -223,8 +252,8 @@ struct PrefillCopier {
   }
 
   __device__ __forceinline__ void setup(const PrefillArgs& a, int u) {
-    const int tile = u / a.NT;
-    const int nt = u - tile * a.NT;
+    int tile, nt;
+    unit_tile(a, tiles, u, tile, nt);
     const int3 te = tile_entry(tiles + kTileInts * tile);
 #pragma unroll
     for (int i = 0; i < C::kActDma; ++i) {
@@ -405,10 +434,20 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
   const int num_units = status[kStNumTiles] * a.NT;
   const float sx = A4 ? 1.0f : __uint_as_float((uint32_t)status[a.scale_word]);
-  const int G = gridDim.x;
-  const int u0 = blockIdx.x;
-  if (u0 >= num_units) return;
-  const int my_units = (num_units - 1 - u0) / G + 1;
+  // this block's units: u0, u0 + G, ... (my_units of them) in the schedule
+  int u0, G, my_units;
+  if (a.sched_xcd) {
+    const int x = blockIdx.x & 7, gx = gridDim.x >> 3;
+    const int s0 = (int)((int64_t)num_units * x / 8), s1 = (int)((int64_t)num_units * (x + 1) / 8);
+    u0 = s0 + (int)(blockIdx.x >> 3);
+    G = gx;
+    my_units = u0 < s1 ? (s1 - 1 - u0) / gx + 1 : 0;
+  } else {
+    u0 = blockIdx.x;
+    G = gridDim.x;
+    my_units = u0 < num_units ? (num_units - 1 - u0) / G + 1 : 0;
+  }
+  if (my_units == 0) return;
   const int total = my_units * a.nsteps;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -445,8 +484,8 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
   // pairs (gate_up: gate and up rows of groups 0 and 1; down: groups 0..3)
   uint2 bq[4];
   auto comp_setup = [&](int u) __attribute__((always_inline)) {
-    const int tile = u / a.NT;
-    nt = u - tile * a.NT;
+    int tile;
+    unit_tile(a, tiles, u, tile, nt);
     const int3 te = tile_entry(tiles + kTileInts * tile);
     e = te.x; rb = te.y; re = te.z;
     // through the scalar cache, 16 rows at a time (a group past nout is
@@ -789,12 +828,16 @@ hipError_t launch_scale_stream(const MoeShape& sh, const MoeWeights& w, const Ws
 }
 
 template <bool GATEUP, bool A4 = false>
-static hipError_t launch_prefill(const PrefillArgs& a, const WsPtrs& ws, hipStream_t s) {
+static hipError_t launch_prefill(const PrefillArgs& args, const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
   // one block per compute unit: the LDS ring takes most of a unit's LDS
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
+  PrefillArgs a = args;
+  // the expert-major XCD schedule needs the tile words (bounded list) and
+  // a grid of whole XCDs
+  a.sched_xcd = cus % 8 == 0 && max_tiles((int64_t)sh.T * sh.k, sh.E, kPrefillBM) <= kTileWordMaxBound;
   prefill_gemm_kernel<GATEUP, kPrefillBM, A4><<<cus, Ring<kPrefillBM, A4>::kThreads, 0, s>>>(a, ws.tiles,
                                                                                             ws.status);
   return hipGetLastError();
@@ -816,7 +859,7 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
   a.act_ld = sh.H;
   a.scale_word = kStScaleX;
   a.out = static_cast<float*>(ws.h);
-  return launch_prefill<true>(a, ws, s);
+  return launch_prefill<true>(a, sh, ws, s);
 }
 
 hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
@@ -835,7 +878,7 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
   a.act_ld = sh.I;
   a.scale_word = kStScaleH;
   a.out = ws.y;
-  return launch_prefill<false>(a, ws, s);
+  return launch_prefill<false>(a, sh, ws, s);
 }
 
 hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, hipStream_t s) {
@@ -858,7 +901,7 @@ hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const 
   a.h_codes = ws.h_codes;
   a.h_scales = ws.h_scales;
   a.h_rows = (int64_t)sh.T * sh.k;
-  return launch_prefill<true, true>(a, ws, s);
+  return launch_prefill<true, true>(a, sh, ws, s);
 }
 
 hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, hipStream_t s) {
@@ -878,7 +921,7 @@ hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const Ws
   a.asc_step = (int64_t)4 * sh.T * sh.k;
   a.scale_word = -1;
   a.out = ws.y;
-  return launch_prefill<false, true>(a, ws, s);
+  return launch_prefill<false, true>(a, sh, ws, s);
 }
 
 }  // namespace mx

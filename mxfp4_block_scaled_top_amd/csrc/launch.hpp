@@ -11,9 +11,16 @@ constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to h
 constexpr int kFusedRouteMaxTokens = 32;     // single-block route + permute up to here
 constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
 constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 and FP4 x FP4 paths
-// A row tile is 4 ints: expert, first sorted row, end row (exclusive), 0.
-// Entries past the number of tiles (up to max_tiles) hold expert -1.
+// A row tile is 4 ints: expert, first sorted row, end row (exclusive), and
+// a word locating the expert's entries (tile_word).  Entries past the number
+// of tiles (up to max_tiles) hold expert -1.
 constexpr int kTileInts = 4;
+// tile_word: (index of the expert's first entry) | (its entry count << 16),
+// or 0 when the list bound exceeds kTileWordMaxBound
+constexpr int kTileWordMaxBound = 32768;
+__host__ __device__ inline int tile_word(int first, int count, int bound) {
+  return bound <= kTileWordMaxBound ? (first | (count << 16)) : 0;
+}
 
 // Typed pointers into the caller's MoE workspace.
 struct WsPtrs {

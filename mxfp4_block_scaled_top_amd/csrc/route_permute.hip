@@ -148,7 +148,9 @@ __device__ int chunk_rank(int e, bool valid, int E, int id_bits, int* wcnt) {
 __device__ __forceinline__ bool id_ok(int e, int E) { return e >= 0 && e < E; }
 
 // Tile list: expert e with n_e sorted rows contributes ceil(n_e / BM) entries
-// (e, offsets[e] + i*BM, min(offsets[e] + (i+1)*BM, offsets[e] + n_e), 0);
+// (e, offsets[e] + i*BM, min(offsets[e] + (i+1)*BM, offsets[e] + n_e), w)
+// with w = (index of e's first entry) | (e's entry count << 16) while the
+// list bound is at most kTileWordMaxBound entries, else 0;
 // entries from the tile count up to `bound` get expert -1, so a GEMM block
 // learns everything about its tile from one 16-byte read.  Called by a whole
 // 1024-thread block with cnt and off valid in LDS (E <= 1024).
@@ -158,10 +160,11 @@ __device__ void write_tiles(const int* cnt, const int* off, int E, int BM, int b
   const int nt = (e < E) ? (cnt[e] + BM - 1) / BM : 0;
   int total;
   const int first = block_exclusive_scan(nt, scan_tmp, &total);
+  const int w = tile_word(first, nt, bound);
   for (int i = 0; i < nt; ++i) {
     const int b = off[e] + i * BM;
     const int end = off[e] + cnt[e];
-    *reinterpret_cast<int4*>(tiles + kTileInts * (first + i)) = make_int4(e, b, min(b + BM, end), 0);
+    *reinterpret_cast<int4*>(tiles + kTileInts * (first + i)) = make_int4(e, b, min(b + BM, end), w);
   }
   for (int t = total + (int)threadIdx.x; t < bound; t += (int)blockDim.x)
     *reinterpret_cast<int4*>(tiles + kTileInts * t) = make_int4(-1, 0, 0, 0);
@@ -415,13 +418,14 @@ __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
   const int tincl = wave_incl_scan(na + nb2);
   const int fa = tincl - na - nb2, fb = fa + na;
   const int ntiles = __shfl(tincl, 63, 64);
+  const int wa = tile_word(fa, na, bound), wb = tile_word(fb, nb2, bound);
   for (int i = 0; i < na; ++i) {
     const int b = offa + i * BM;
-    *reinterpret_cast<int4*>(tiles + kTileInts * (fa + i)) = make_int4(ea, b, min(b + BM, offa + ca), 0);
+    *reinterpret_cast<int4*>(tiles + kTileInts * (fa + i)) = make_int4(ea, b, min(b + BM, offa + ca), wa);
   }
   for (int i = 0; i < nb2; ++i) {
     const int b = offb + i * BM;
-    *reinterpret_cast<int4*>(tiles + kTileInts * (fb + i)) = make_int4(eb, b, min(b + BM, offb + cb), 0);
+    *reinterpret_cast<int4*>(tiles + kTileInts * (fb + i)) = make_int4(eb, b, min(b + BM, offb + cb), wb);
   }
   for (int t = ntiles + lane; t < bound; t += 64)
     *reinterpret_cast<int4*>(tiles + kTileInts * t) = make_int4(-1, 0, 0, 0);

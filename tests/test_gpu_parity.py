@@ -149,11 +149,16 @@ def test_permutation_bit_exact(mx, T, E, k, hot):
         bm = 4 if act == synth.ACT_BF16 else 128
         assert _status(ws, lay)[5] == int(np.sum((counts + bm - 1) // bm))
         assert _status(ws, lay)[0] == 0
-        # row-tile list: (expert, first row, end row, 0) per BM rows of each expert in
-        # expert order, then expert -1 up to the workspace's bound on the tile count
-        want = [(e, offsets[e] + b, min(offsets[e] + b + bm, offsets[e + 1]), 0)
-                for e in range(E) for b in range(0, int(counts[e]), bm)]
+        # row-tile list: (expert, first row, end row, w) per BM rows of each expert in
+        # expert order, w = (index of the expert's first entry) | (its entry count << 16),
+        # then expert -1 up to the workspace's bound on the tile count
+        ntile = (counts + bm - 1) // bm
+        first = np.concatenate([[0], np.cumsum(ntile)[:-1]])
         bound = np_ // bm + min(np_, E) + 1
+        assert bound <= 32768
+        want = [(e, offsets[e] + b, min(offsets[e] + b + bm, offsets[e + 1]),
+                 int(first[e]) | (int(ntile[e]) << 16))
+                for e in range(E) for b in range(0, int(counts[e]), bm)]
         want += [(-1, 0, 0, 0)] * (bound - len(want))
         got_tiles = _ws_view(ws, lay, "tiles", np.int32, 4 * bound).reshape(bound, 4)
         assert np.array_equal(got_tiles, np.array(want, dtype=np.int32))
