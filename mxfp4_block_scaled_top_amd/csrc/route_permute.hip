@@ -302,6 +302,13 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
   v = max(v, dpp_u32<0x128>(v));   // row_ror:8
   return v;
 }
+__device__ __forceinline__ uint32_t row16_min(uint32_t v) {
+  v = min(v, dpp_u32<0x121>(v));
+  v = min(v, dpp_u32<0x122>(v));
+  v = min(v, dpp_u32<0x124>(v));
+  v = min(v, dpp_u32<0x128>(v));
+  return v;
+}
 // lanes holding expert e among the lanes of mask `valid`, given the wave's
 // ballots of each id bit
 __device__ __forceinline__ uint64_t lanes_with(int e, const uint64_t* bits, uint64_t valid) {
@@ -334,34 +341,29 @@ __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
     const int t = t0 + 4 * wave + tw;
     const bool live = t < T;   // the whole 16-lane row agrees
     const float* row = logits + (size_t)(live ? t : 0) * E;
-    float v[8];
-    bool avail[8];
+    // keys of the lane's logits l16 + 16 i (0: taken or past E)
+    uint32_t key[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int idx = l16 + 16 * i;
-      avail[i] = live && idx < E;
-      v[i] = avail[i] ? row[idx] : 0.0f;
+      key[i] = live && idx < E ? order_key(row[idx]) : 0u;
     }
     int chosen[kSmallMaxK] = {};
     float val[kSmallMaxK] = {};
     for (int j = 0; j < k; ++j) {
-      uint32_t m = 0;
+      uint32_t m = key[0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, avail[i] ? order_key(v[i]) : 0u);
+      for (int i = 1; i < 8; ++i) m = max(m, key[i]);
       m = row16_max(m);
-      // lowest index holding the maximum: the first i whose ballot (this
-      // row's 16 bits) is not empty
-      int win = 0x7fffffff;
+      // lowest index holding the maximum: the lane's first i with that key,
+      // then the row minimum
+      uint32_t cand = 0xffffffffu;
 #pragma unroll
-      for (int i = 7; i >= 0; --i) {
-        const uint64_t b = __ballot(avail[i] && order_key(v[i]) == m);
-        const uint32_t r = (uint32_t)(b >> (16 * tw)) & 0xffffu;
-        if (r) win = 16 * i + __builtin_ctz(r);
-      }
+      for (int i = 7; i >= 0; --i) cand = key[i] == m ? (uint32_t)(l16 + 16 * i) : cand;
+      const uint32_t win = row16_min(cand);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (l16 + 16 * i == win) avail[i] = false;
-      chosen[j] = win;
+      for (int i = 0; i < 8; ++i) key[i] = (uint32_t)(l16 + 16 * i) == win ? 0u : key[i];
+      chosen[j] = (int)win;
       val[j] = key_value(m);
     }
     // softmax over the k chosen logits, the sum in 32-lane butterfly order
