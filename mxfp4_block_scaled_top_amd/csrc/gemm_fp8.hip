@@ -24,7 +24,8 @@
 //     tile (up to BM expert-sorted rows of one expert, from the tile list the
 //     permutation builds) times one n-tile of 256 weight rows (gate_up: 128
 //     gate rows and the matching 128 up rows).  Block b takes units b, b + G,
-//     b + 2G, ...; a unit is nsteps K steps of 128.  (Placing the n-tiles of
+//     b + 2G, ...; a unit is nsteps K steps of 128 (256 with MXFP4
+//     activations).  (Placing the n-tiles of
 //     one row tile on one XCD, to share its activations in that XCD's L2, made
 //     no measurable difference.)
 //   * Every K step's activations (BM x 128 B of E4M3 codes, rows in
@@ -59,31 +60,35 @@ namespace mx {
 
 constexpr int kBN = 256;               // weight rows per unit
 constexpr int kBK = 128;               // K per step (four MX blocks)
-constexpr int kWTile = kBN * kBK / 2;  // E2M1 bytes per step
-constexpr int kScTile = kBN * 4;       // the step's four scale bytes of each weight row
 
-// A4: MXFP4 activations (64 B of E2M1 codes per row per step, the geometry
-// of a weight row, plus one dword of four E8M0 scales per row); otherwise
-// E4M3 activations (128 B per row per step).
+// A4: MXFP4 activations, K steps of 256 (eight MX blocks): 128 B of E2M1
+// codes per activation and weight row, so every 1 KB copy covers 8 whole
+// 128-byte lines, plus two dwords of E8M0 scales per row.  Otherwise E4M3
+// activations, K steps of 128: 128 B per activation row, 64 B per weight
+// row, one dword of scales per weight row.
 template <int BM, bool A4 = false>
 struct Ring {
   static constexpr int kWaves = BM / 16;                // each 64 sorted rows x 64 weight rows
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kStages = A4 ? 5 : BM == 128 ? 4 : 6;
-  static constexpr int kActRow = A4 ? kBK / 2 : kBK;    // activation bytes per row per step
+  static constexpr int kK = A4 ? 2 * kBK : kBK;         // K per step
+  static constexpr int kSub = kK / kBK;                 // 128-element sub-steps per step (scale dwords per row)
+  static constexpr int kStages = A4 ? 3 : BM == 128 ? 4 : 6;
+  static constexpr int kActRow = A4 ? kK / 2 : kK;      // activation bytes per row per step
+  static constexpr int kWRow = kK / 2;                  // weight bytes per row per step
   static constexpr int kAct = BM * kActRow;             // activation bytes per slot
   static constexpr int kW = kAct;                       // offsets inside a slot
-  static constexpr int kSc = kAct + kWTile;
-  static constexpr int kASc = kSc + kScTile;            // A4: activation scales, 4 B per row
-  static constexpr int kSlot = kASc + (A4 ? BM * 4 : 0);
+  static constexpr int kSc = kAct + kBN * kWRow;
+  static constexpr int kASc = kSc + kBN * 4 * kSub;     // A4: activation scales, 4 B per row and sub-step
+  static constexpr int kSlot = kASc + (A4 ? BM * 4 * kSub : 0);
   static constexpr int kActDma = BM * kActRow / 1024 / kWaves;  // 1 KB activation DMAs per wave per step
-  static constexpr int kWDma = 16 / kWaves;             // 1 KB weight DMAs per wave per step
+  static constexpr int kWDma = kBN * kWRow / 1024 / kWaves;     // 1 KB weight DMAs per wave per step
   static constexpr int kScDma = 1;                      // the wave's 1/8 of the step's weight scales
   static constexpr int kAScDma = A4 ? 1 : 0;            // the wave's 1/8 of the step's activation scales
   static constexpr int kDma = kActDma + kWDma + kScDma + kAScDma;  // DMA instructions per wave per step
   static constexpr int kLds = kStages * kSlot;
   static_assert(kActDma * kWaves * 1024 == BM * kActRow, "copies split over the waves");
-  static_assert(kWaves == 8 && (!A4 || BM == 128), "each wave copies 128 B of weight and 64 B of activation scales");
+  static_assert(kWDma * kWaves * 1024 == kBN * kWRow, "copies split over the waves");
+  static_assert(kWaves == 8 && (!A4 || BM == 128), "each wave copies 1/8 of the step's scales");
   static_assert((kStages - 2) * kDma <= 63, "vector-memory count range");
   static_assert(kStages - 2 <= 4, "waits cover up to four steps ahead");
   static_assert(kLds <= 160 * 1024, "LDS");
@@ -98,7 +103,8 @@ struct PrefillArgs {
   int nb;                  // K / 32
   int K;
   int NT;                  // n-tiles
-  int nsteps;              // ceil(nb / 4)
+  int nsteps;              // K steps: ceil(nb / 4), MXFP4 activations ceil(nb / 8)
+  int nsteps_s;            // 128-element steps of the scale streams: ceil(nb / 4)
   const uint8_t* act;      // [sorted rows, K] E4M3 codes, or [sorted rows, K/32, 16] E2M1 blocks
   int act_ld;              // activation bytes per row (K, or K/2 for E2M1)
   const uint8_t* asc;      // E2M1 activations: E8M0 [nsteps, sorted rows, 4] (step-major)
@@ -243,10 +249,14 @@ struct PrefillCopier {
                                        int grid, int units) {
     tiles = t; smem = sm; wave = w; u0 = first; G = grid; my_units = units;
     this->lane = lane;
-    a_row = A4 ? lane >> 2 : lane >> 3;
-    a_chunk = A4 ? (lane & 3) ^ ((lane >> 3) & 3) : (lane & 7) ^ a_row;
-    w_row = lane >> 2;
-    w_blk = (lane & 3) ^ ((lane >> 3) & 3);
+    // a 1 KB copy fills 8 LDS rows of 128 B (E4M3 activations; A4 activations
+    // and weights) or 16 rows of 64 B (E4M3-mode weights); the lane's 16 B
+    // slot in its row is fixed, the block fetched into it is slot ^ (row % 8)
+    // (128 B rows) or slot ^ ((row / 2) % 4) (64 B rows)
+    a_row = lane >> 3;
+    a_chunk = (lane & 7) ^ a_row;
+    w_row = A4 ? lane >> 3 : lane >> 2;
+    w_blk = A4 ? (lane & 7) ^ (lane >> 3) : (lane & 3) ^ ((lane >> 3) & 3);
     k = 0; step = 0; slot = 0;
     setup(a, u0);
   }
@@ -257,19 +267,23 @@ struct PrefillCopier {
     const int3 te = tile_entry(tiles + kTileInts * tile);
 #pragma unroll
     for (int i = 0; i < C::kActDma; ++i) {
-      int row = te.y + (A4 ? 16 : 8) * (NW * i + wave) + a_row;
+      int row = te.y + 8 * (NW * i + wave) + a_row;
       row = row < te.z ? row : te.y;
       aptr[i] = a.act + (int64_t)row * a.act_ld;
     }
     // rows past the tile end read other rows' scales (never stored)
-    if (A4) ascp = a.asc + (int64_t)te.y * 4 + 64 * wave + 16 * (lane & 3);
+    // A4: wave w copies rows 32 (w % 4) .. +31 of sub-step w / 4
+    if (A4) ascp = a.asc + (int64_t)te.y * 4 + 128 * (wave & 3) + 16 * (lane & 7);
     const int64_t ebase = (int64_t)te.x * a.R;
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
-      const int wr = weight_row<GATEUP>(16 * (NW * i + wave) + w_row, nt, a.nout);
+      const int wr = weight_row<GATEUP>((A4 ? 8 : 16) * (NW * i + wave) + w_row, nt, a.nout);
       wptr[i] = a.wb + (ebase + wr) * a.nb * kBlockBytes;
     }
-    wsp = a.wsp + ((int64_t)te.x * a.NT + nt) * a.nsteps * 1024 + 128 * wave + 16 * (lane & 7);
+    // the unit's stream: 1 KB per 128-element sub-step; A4: wave w copies 256 B
+    // (lanes 0-15) of sub-step w / 4, else 128 B (lanes 0-7)
+    wsp = a.wsp + ((int64_t)te.x * a.NT + nt) * a.nsteps_s * 1024 +
+          (A4 ? 256 * (wave & 3) + 16 * (lane & 15) : 128 * wave + 16 * (lane & 7));
   }
 
   // copies of the next step into its slot, then advance
@@ -280,7 +294,7 @@ struct PrefillCopier {
 #pragma unroll
     for (int i = 0; i < C::kActDma; ++i) {
       if (A4) {
-        const int blk = 4 * step + a_chunk;        // past K: the row's first block
+        const int blk = 8 * step + a_chunk;        // past K: the row's first block
         __builtin_amdgcn_global_load_lds(aptr[i] + (!tail || blk < a.nb ? blk * kBlockBytes : 0),
                                          dst + 1024 * (NW * i + wave), 16, 0, 0);
       } else {
@@ -291,13 +305,21 @@ struct PrefillCopier {
     }
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
-      const int blk = 4 * step + w_blk;            // past K: the row's first block
+      const int blk = C::kSub * 4 * step + w_blk;  // past K: the row's first block
       __builtin_amdgcn_global_load_lds(wptr[i] + (!tail || blk < a.nb ? blk * kBlockBytes : 0),
                                        dst + C::kW + 1024 * (NW * i + wave), 16, 0, 0);
     }
-    if (lane < 8) __builtin_amdgcn_global_load_lds(wsp + step * 1024, dst + C::kSc + 128 * wave, 16, 0, 0);
-    if (A4 && lane < 4)
-      __builtin_amdgcn_global_load_lds(ascp + step * a.asc_step, dst + C::kASc + 64 * wave, 16, 0, 0);
+    if (A4) {
+      // sub-step wave / 4 of this step; past the last one (K tail) the last
+      // sub-step again (its values are masked)
+      int ss = 2 * step + (wave >> 2);
+      ss = ss < a.nsteps_s ? ss : a.nsteps_s - 1;
+      if (lane < 16) __builtin_amdgcn_global_load_lds(wsp + ss * 1024, dst + C::kSc + 256 * wave, 16, 0, 0);
+      if (lane < 8)
+        __builtin_amdgcn_global_load_lds(ascp + ss * a.asc_step, dst + C::kASc + 128 * wave, 16, 0, 0);
+    } else if (lane < 8) {
+      __builtin_amdgcn_global_load_lds(wsp + step * 1024, dst + C::kSc + 128 * wave, 16, 0, 0);
+    }
     slot = slot + 1 == C::kStages ? 0 : slot + 1;
     if (++step == a.nsteps) {
       step = 0;
@@ -383,24 +405,26 @@ __device__ __forceinline__ void lds_wait_rest(v4u_t& xb0, v4u_t& xb1, v4u_t& xb2
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xb0), "+v"(xb1), "+v"(xb2), "+v"(xb3));
 }
 
-// A4 step reads: 4 activation blocks (token groups at LDS rows +0, +16, +32,
-// +48), the 4 weight blocks and weight scales as in lds_step_reads, and the
-// 4 activation scale bytes, in one assembly block with its own wait.
-template <bool GATEUP>
-__device__ __forceinline__ void lds_step_reads_a4(uint32_t aa, uint32_t ww, uint32_t ss, uint32_t as,
+
+// A4, one half (four MX blocks) of a 256-element step: 4 activation reads
+// (token-row groups 16 rows = 2 KB apart), 4 weight reads (gate_up: weight
+// groups at LDS rows +0, +16, +128, +144; down: +0, +16, +32, +48; rows of
+// 128 B), 4 weight-scale bytes and 4 activation-scale bytes, waited for in
+// the same assembly block.
+__device__ __forceinline__ void lds_half_reads_a4(bool gateup, uint32_t aa, uint32_t ww, uint32_t ss, uint32_t as,
                                                   v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3,
                                                   v4u_t& wq0, v4u_t& wq1, v4u_t& wq2, v4u_t& wq3,
                                                   uint32_t& sb0, uint32_t& sb1, uint32_t& sb2, uint32_t& sb3,
                                                   uint32_t& ab0, uint32_t& ab1, uint32_t& ab2, uint32_t& ab3) {
-  if (GATEUP) {
+  if (gateup) {
     asm volatile("ds_read_u8 %8, %18\n\tds_read_u8 %9, %18 offset:64\n\t"
                  "ds_read_u8 %10, %18 offset:512\n\tds_read_u8 %11, %18 offset:576\n\t"
                  "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
                  "ds_read_u8 %14, %19 offset:128\n\tds_read_u8 %15, %19 offset:192\n\t"
-                 "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:1024\n\t"
-                 "ds_read_b128 %6, %17 offset:8192\n\tds_read_b128 %7, %17 offset:9216\n\t"
-                 "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:1024\n\t"
-                 "ds_read_b128 %2, %16 offset:2048\n\tds_read_b128 %3, %16 offset:3072\n\t"
+                 "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:2048\n\t"
+                 "ds_read_b128 %6, %17 offset:16384\n\tds_read_b128 %7, %17 offset:18432\n\t"
+                 "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:2048\n\t"
+                 "ds_read_b128 %2, %16 offset:4096\n\tds_read_b128 %3, %16 offset:6144\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(wq0), "=&v"(wq1), "=&v"(wq2),
                    "=&v"(wq3), "=&v"(sb0), "=&v"(sb1), "=&v"(sb2), "=&v"(sb3), "=&v"(ab0), "=&v"(ab1),
@@ -411,10 +435,10 @@ __device__ __forceinline__ void lds_step_reads_a4(uint32_t aa, uint32_t ww, uint
                  "ds_read_u8 %10, %18 offset:128\n\tds_read_u8 %11, %18 offset:192\n\t"
                  "ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
                  "ds_read_u8 %14, %19 offset:128\n\tds_read_u8 %15, %19 offset:192\n\t"
-                 "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:1024\n\t"
-                 "ds_read_b128 %6, %17 offset:2048\n\tds_read_b128 %7, %17 offset:3072\n\t"
-                 "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:1024\n\t"
-                 "ds_read_b128 %2, %16 offset:2048\n\tds_read_b128 %3, %16 offset:3072\n\t"
+                 "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:2048\n\t"
+                 "ds_read_b128 %6, %17 offset:4096\n\tds_read_b128 %7, %17 offset:6144\n\t"
+                 "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:2048\n\t"
+                 "ds_read_b128 %2, %16 offset:4096\n\tds_read_b128 %3, %16 offset:6144\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(wq0), "=&v"(wq1), "=&v"(wq2),
                    "=&v"(wq3), "=&v"(sb0), "=&v"(sb1), "=&v"(sb2), "=&v"(sb3), "=&v"(ab0), "=&v"(ab1),
@@ -472,10 +496,14 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
   const uint32_t a1 = lds0 + (64 * wm + r) * kBK + 16 * c1;
   const uint32_t w0 = lds0 + C::kW + lrow0 * 64 + 16 * wslot;
   const uint32_t s0 = lds0 + C::kSc + lrow0 * 4 + g;   // scale of MX block g of the step
-  // A4: activation block g of token row 64 wm + r sits in slot wslot (the
-  // rows' swizzle phase (row/2)%4 is that of r), its scale at byte g of the
-  // row's dword
-  const uint32_t ax0 = lds0 + (64 * wm + r) * 64 + 16 * wslot;
+  // A4 (rows of 128 B, eight 16-byte slots swizzled by row % 8 = r % 8):
+  // MX block 4h + g of a row sits in slot (4h + g) ^ (r % 8); the scales of
+  // half h sit in the step's second 128-element scale chunk (weights: 1 KB
+  // on, activations: 512 B on)
+  const uint32_t ax[2] = {lds0 + (64 * wm + r) * 128 + 16 * (g ^ (r & 7)),
+                          lds0 + (64 * wm + r) * 128 + 16 * ((4 + g) ^ (r & 7))};
+  const uint32_t wx[2] = {lds0 + C::kW + lrow0 * 128 + 16 * (g ^ (r & 7)),
+                          lds0 + C::kW + lrow0 * 128 + 16 * ((4 + g) ^ (r & 7))};
   const uint32_t as0 = lds0 + C::kASc + (64 * wm + r) * 4 + g;
 
   int cstep = 0, cslot = 0, ck = 0;
@@ -545,32 +573,36 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
     v4u_t xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3;
     uint32_t sb0, sb1, sb2, sb3;
     if constexpr (A4) {
-      uint32_t ab0, ab1, ab2, ab3;
-      lds_step_reads_a4<GATEUP>(ax0 + so, ww, ss, as0 + so, xa0, xa1, xa2, xa3, wq0, wq1, wq2, wq3, sb0, sb1,
-                                sb2, sb3, ab0, ab1, ab2, ab3);
-      const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
-      const v4u_t wq[4] = {wq0, wq1, wq2, wq3};
-      const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
-      const uint32_t ab[4] = {ab0, ab1, ab2, ab3};
-      // lane group g holds MX block g of the step in both operands; past K the
-      // weights are zero and both scales 2^0
-      const bool valid = 4 * cstep + g < a.nb;
-      v8i B[4];
-      int bsc[4];
+      // two halves of four MX blocks: the reads of half 1 overlap the MFMAs
+      // of half 0; lane group g holds MX block 4h + g of the step in both
+      // operands; past K the weights are zero and both scales 2^0
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
-        B[tg] = v8i{(int)xa[tg].x, (int)xa[tg].y, (int)xa[tg].z, (int)xa[tg].w, 0, 0, 0, 0};
-        bsc[tg] = valid ? (int)ab[tg] : 127;
-      }
+      for (int h = 0; h < 2; ++h) {
+        uint32_t ab0, ab1, ab2, ab3;
+        lds_half_reads_a4(GATEUP, ax[h] + so, wx[h] + so, ss + 1024 * h, as0 + so + 512 * h, xa0, xa1, xa2, xa3,
+                          wq0, wq1, wq2, wq3, sb0, sb1, sb2, sb3, ab0, ab1, ab2, ab3);
+        const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
+        const v4u_t wq[4] = {wq0, wq1, wq2, wq3};
+        const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
+        const uint32_t ab[4] = {ab0, ab1, ab2, ab3};
+        const bool valid = 8 * cstep + 4 * h + g < a.nb;
+        v8i B[4];
+        int bsc[4];
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
-        const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
-        const int asc = valid ? (int)sb[rg] : 127;
+        for (int tg = 0; tg < 4; ++tg) {
+          B[tg] = v8i{(int)xa[tg].x, (int)xa[tg].y, (int)xa[tg].z, (int)xa[tg].w, 0, 0, 0, 0};
+          bsc[tg] = valid ? (int)ab[tg] : 127;
+        }
 #pragma unroll
-        for (int tg = 0; tg < 4; ++tg)
-          acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 4, 0, asc, 0,
-                                                                         bsc[tg]);
+        for (int rg = 0; rg < 4; ++rg) {
+          const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
+          const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
+          const int asc = valid ? (int)sb[rg] : 127;
+#pragma unroll
+          for (int tg = 0; tg < 4; ++tg)
+            acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 4, 0, asc, 0,
+                                                                           bsc[tg]);
+        }
       }
     } else {
       if (GATEUP) {
@@ -855,6 +887,7 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
   a.K = sh.H;
   a.NT = (sh.I + kBN / 2 - 1) / (kBN / 2);
   a.nsteps = (a.nb + 3) / 4;
+  a.nsteps_s = a.nsteps;
   a.act = ws.x_codes;
   a.act_ld = sh.H;
   a.scale_word = kStScaleX;
@@ -874,6 +907,7 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
   a.K = sh.I;
   a.NT = (sh.H + kBN - 1) / kBN;
   a.nsteps = (a.nb + 3) / 4;
+  a.nsteps_s = a.nsteps;
   a.act = ws.h_codes;
   a.act_ld = sh.I;
   a.scale_word = kStScaleH;
@@ -891,7 +925,8 @@ hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const 
   a.nb = sh.H / kBlockElems;
   a.K = sh.H;
   a.NT = (sh.I + kBN / 2 - 1) / (kBN / 2);
-  a.nsteps = (a.nb + 3) / 4;
+  a.nsteps = (a.nb + 7) / 8;        // K steps of 256
+  a.nsteps_s = (a.nb + 3) / 4;
   a.act = ws.x_codes;
   a.act_ld = sh.H / 2;
   a.asc = ws.x_scales;
@@ -914,7 +949,8 @@ hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const Ws
   a.nb = sh.I / kBlockElems;
   a.K = sh.I;
   a.NT = (sh.H + kBN - 1) / kBN;
-  a.nsteps = (a.nb + 3) / 4;
+  a.nsteps = (a.nb + 7) / 8;        // K steps of 256
+  a.nsteps_s = (a.nb + 3) / 4;
   a.act = ws.h_codes;
   a.act_ld = sh.I / 2;
   a.asc = ws.h_scales;

@@ -576,7 +576,17 @@ def test_prefill_long_k(mx, act):
         assert_close_rounded(got, ref["out"], "long K fp8")
 
 
-@pytest.mark.parametrize("E,H,I,T,k", SMALL)
+# MXFP4 activations run K steps of 256 (eight MX blocks): H/32 and I/32 here
+# add the tails 5 and 6 modulo 8 and multi-step tails 3, 5, 6, 7 and 0
+SMALL_A4 = SMALL + [
+    (4, 416, 352, 19, 2),
+    (4, 448, 480, 23, 4),
+    (4, 512, 160, 7, 2),
+    (2, 192, 768, 5, 1),
+]
+
+
+@pytest.mark.parametrize("E,H,I,T,k", SMALL_A4)
 def test_mxfp4_act_small_layers(mx, E, H, I, T, k):
     L = synth.layer(seed=E * 13 + H, E=E, H=H, I=I)
     logits, x = synth.moe_inputs(T + 17, T, E=E, H=H)
