@@ -668,7 +668,10 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
       // (half 1).  The block is quantised here (the rule of
       // quant_x_mxfp4_sorted_kernel): amax over the row's four lanes, shared
       // exponent, codes; no fp32 h is written.  Every lane takes part in the
-      // shuffles; only real rows store.
+      // shuffles; only real rows store.  SwiGLU uses the hardware exp and
+      // reciprocal (a few 1e-7 relative, far inside the h error the codes
+      // are specified against), not the correctly rounded ones of the FP8
+      // path.
       const int ib = nt * (kBN / 2) + 32 * wn;
       if (ib < a.nout) {
         const int b = ib / kBlockElems, nbh = a.nout / kBlockElems;
@@ -683,7 +686,7 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
             for (int jj = 0; jj < 4; ++jj) {
               const float gate = acc[half][tg][jj] + bf16_of(bq[2 * half], jj);
               const float up = acc[half + 2][tg][jj] + bf16_of(bq[2 * half + 1], jj);
-              hv[4 * half + jj] = silu_accurate(gate) * up;
+              hv[4 * half + jj] = silu(gate) * up;
               am = max(am, __float_as_uint(hv[4 * half + jj]) & 0x7fffffffu);
             }
           am = max(am, (uint32_t)__shfl_xor((int)am, 16, 64));
