@@ -85,6 +85,18 @@ __device__ __forceinline__ uint32_t e2m1_round_mag(float q) {
          (uint32_t)(q > 5.0f);
 }
 
+// Eight fp32 values already scaled by 2^-X (|q| < 8) -> eight E2M1 nibbles,
+// value i in nibble i (low nibble first).  The hardware conversion rounds
+// exactly as e2m1_round_mag (nearest, ties to the even mantissa bit,
+// saturating at 6) and keeps the sign bit, -0 included: checked on every fp32
+// pattern below 8 in magnitude.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* q) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
+}
+
 // silu(z) = z / (1 + exp(-z)); exp overflow gives -0 for very negative z.
 __device__ __forceinline__ float silu(float z) {
   return __fdividef(z, 1.0f + __expf(-z));

@@ -42,17 +42,20 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
     // and subnormal blocks land below the clamp
     const int x = min(max((int)(amax >> 7) - 127 - 2, -125), 125);
     const float inv = __uint_as_float((uint32_t)(127 - x) << 23);   // 2^-X, a normal fp32
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+    // elements 2i (low half of v[i]) and 2i + 1 scaled by 2^-X (exact, below
+    // 8 in magnitude) -> byte i of the block, element 2i in the low nibble.
+    // The hardware conversion rounds exactly as e2m1_round_mag and keeps
+    // the sign bit (checked on every fp32 below 8 in magnitude).
+    uint32_t packed[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int d = 0; d < 4; ++d) {
+      float f[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t bits = (v[i] >> (16 * h)) & 0xffffu;
-        const float q = __uint_as_float((bits & 0x7fffu) << 16) * inv;   // exact
-        const uint32_t code = e2m1_round_mag(q) | ((bits >> 15) << 3);
-        const int e = 2 * i + h;                    // element index in the block
-        packed[e >> 3] |= code << (4 * (e & 7));    // element 2k low nibble, 2k+1 high
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(v[4 * d + i] << 16) * inv;
+        f[2 * i + 1] = __uint_as_float(v[4 * d + i] & 0xffff0000u) * inv;
       }
+      packed[d] = e2m1_pack8(f);
     }
     *reinterpret_cast<uint4*>(blocks + b * kBlockBytes) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     scales[b] = (uint8_t)(x + 127);
@@ -76,12 +79,15 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, uint4& out) {
   for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7fffffffu);
   const int x = min(max((int)(amax >> 23) - 127 - 2, -125), 125);
   const float inv = __uint_as_float((uint32_t)(127 - x) << 23);
-  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+  // elements 2j, 2j + 1 -> byte j, by the hardware conversion (rounding and
+  // sign as e2m1_round_mag, checked on every fp32 below 8 in magnitude)
+  uint32_t packed[4];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    const uint32_t bits = __float_as_uint(v[e]);
-    const float q = __uint_as_float(bits & 0x7fffffffu) * inv;
-    packed[e >> 3] |= (e2m1_round_mag(q) | ((bits >> 31) << 3)) << (4 * (e & 7));
+  for (int d = 0; d < 4; ++d) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = v[8 * d + i] * inv;
+    packed[d] = e2m1_pack8(f);
   }
   out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   return (uint32_t)(x + 127);
