@@ -835,12 +835,20 @@ __global__ __launch_bounds__(256) void scale_stream_kernel(const uint8_t* __rest
     const bool real = lds_row_index(GATEUP, 32 * c0 + l, nt) < nout;
     const uint8_t* src = rows + l * nb;
     uint32_t* dst = out + (int64_t)unit * nsteps * 256 + 32 * c0 + l;
-    for (int st = 0; st < nsteps; ++st) {
+    int st = 0;
+    if (!real) {
+      for (; st < nsteps; ++st) dst[st * 256] = 0x7f7f7f7fu;
+    } else if ((nb & 1) == 0) {
+      // even nb: a step's four bytes start 2-byte aligned, two halfword reads
+      const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+      for (; st < nb / 4; ++st) dst[st * 256] = (uint32_t)s16[2 * st] | ((uint32_t)s16[2 * st + 1] << 16);
+    }
+    for (; st < nsteps; ++st) {   // the tail step (past K: 127), or odd nb
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int b = 4 * st + j;
-        word |= (uint32_t)(real && b < nb ? src[b] : 127u) << (8 * j);
+        word |= (uint32_t)(b < nb ? src[b] : 127u) << (8 * j);
       }
       dst[st * 256] = word;
     }
