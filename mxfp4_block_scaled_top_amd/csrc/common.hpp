@@ -75,6 +75,15 @@ __device__ __forceinline__ uint32_t e4m3_encode(float q) {
   return sign | (uint32_t)n;
 }
 
+// Four E4M3 codes (q0 in the low byte) of fp32 values below 464 in
+// magnitude: the hardware conversion equals e4m3_encode on every such fp32
+// pattern, both signs (checked exhaustively).  The codec's quotients v / s
+// stay within 448 (1 + 2^-23) of zero.
+__device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
+}
+
 // E2M1 magnitude code of q >= 0 (|v| / 2^X of the MX block rule): the count
 // of rounding thresholds passed.  A tie at a threshold goes to the code whose
 // mantissa bit is 0, so the boundary below an odd code is exclusive (q > t)

@@ -82,8 +82,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const void* __restrict__ in
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      w[q] = e4m3_encode(v[4 * q] / s) | (e4m3_encode(v[4 * q + 1] / s) << 8) |
-             (e4m3_encode(v[4 * q + 2] / s) << 16) | (e4m3_encode(v[4 * q + 3] / s) << 24);
+      w[q] = e4m3_pack4(v[4 * q] / s, v[4 * q + 1] / s, v[4 * q + 2] / s, v[4 * q + 3] / s);
     }
     *reinterpret_cast<uint4*>(codes + i * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -110,8 +109,7 @@ __global__ __launch_bounds__(256) void encode_sorted_rows_kernel(
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      w[q] = e4m3_encode(v[4 * q] / s) | (e4m3_encode(v[4 * q + 1] / s) << 8) |
-             (e4m3_encode(v[4 * q + 2] / s) << 16) | (e4m3_encode(v[4 * q + 3] / s) << 24);
+      w[q] = e4m3_pack4(v[4 * q] / s, v[4 * q + 1] / s, v[4 * q + 2] / s, v[4 * q + 3] / s);
     }
     const uint4 o = make_uint4(w[0], w[1], w[2], w[3]);
     for (int j = 0; j < k; ++j) {
