@@ -49,8 +49,10 @@
 //   * BM/16 waves (two per SIMD at BM = 128), each 64 sorted rows x 64 weight
 //     rows (4 x 4 MFMA tiles of 16 x 16).
 //   * LDS layouts are XOR-swizzled at 16-byte granularity, chosen through
-//     each lane's DMA source address, so that the MFMA-layout reads of a
-//     group of 8 lanes hit distinct banks.
+//     each lane's DMA source address, so that the MFMA-layout reads hit
+//     distinct banks in each pass of a 16-byte read (lanes 0-7 with 16-23,
+//     8-15 with 24-31, ..., over 64 four-byte banks; the bank-conflict
+//     counter reads zero for every read here).
 //   * K tails: chunks past K are loaded from a valid address and the weight
 //     operand of MX blocks past K is forced to zero.
 #include "common.hpp"
@@ -490,9 +492,13 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
   const int lrow0 = (GATEUP ? 32 * wn : 64 * wn) + r;
   const int wslot = g ^ ((r >> 1) & 3);             // slot of MX block g in these rows
   // activation chunks: the bf16 path takes K [32g, 32g+32) = chunks 2g, 2g+1,
-  // the block-scaled path chunks g and 4+g; the row's swizzle is row%8 = r%8
-  const int c0 = (GATEUP ? 2 * g : g) ^ (r & 7);
-  const int c1 = (GATEUP ? 2 * g + 1 : 4 + g) ^ (r & 7);
+  // the block-scaled path chunks g and 4+g; the row's swizzle is row%8 = r%8.
+  // A 16-byte LDS read serves lanes 0-7 with 16-23 (and 8-15 with 24-31, ...)
+  // in one pass over 64 four-byte banks; for those pairs to hit distinct
+  // banks the bf16 path's odd lane groups read chunk 2g+1 first (their K
+  // order within the block is then 16..31, 0..15, for both operands).
+  const int c0 = (GATEUP ? 2 * g + (g & 1) : g) ^ (r & 7);
+  const int c1 = (GATEUP ? 2 * g + 1 - (g & 1) : 4 + g) ^ (r & 7);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const uint32_t a0 = lds0 + (64 * wm + r) * kBK + 16 * c0;
   const uint32_t a1 = lds0 + (64 * wm + r) * kBK + 16 * c1;
@@ -616,13 +622,19 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
                                sb0, sb1, sb2, sb3);
       }
       const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
-      const v4u_t wq[4] = {wq0, wq1, wq2, wq3};
+      v4u_t wq[4] = {wq0, wq1, wq2, wq3};
+      if (GATEUP && (g & 1)) {
+        // odd lane groups hold activation K 16..31 of the block in xa: take
+        // the weight dwords in the same order
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) wq[rg] = v4u_t{wq[rg].z, wq[rg].w, wq[rg].x, wq[rg].y};
+      }
       const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
       const bool valid = 4 * cstep + g < a.nb;        // this lane's MX block lies inside K
       if (GATEUP) {
         // lane group g holds K [32g, 32g+32) of the step (its own MX block);
-        // MFMA q takes elements 8q..8q+7 of it, in the same order for both
-        // operands; MFMAs 2-3 use the chunks read last
+        // MFMA q takes elements 8q..8q+7 of it (8(q^2).. for odd g), in the
+        // same order for both operands; MFMAs 2-3 use the chunks read last
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
