@@ -434,16 +434,16 @@ __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
   if (lane < kStWords) status[lane] = lane == kStNumTiles ? ntiles : 0;
 }
 
-// Multi-block path, phase 1: per-chunk ranks and per-chunk expert counts.
+// Multi-block path, phase 1: per-chunk ranks and per-chunk expert counts
+// (a pair whose id lies outside [0, E) gets rank -1 and is not counted).
 __global__ __launch_bounds__(1024) void permute_count_kernel(
-    const int* __restrict__ ids, int npairs, int E, int id_bits, int* __restrict__ status,
+    const int* __restrict__ ids, int npairs, int E, int id_bits,
     int* __restrict__ chunk_counts, int* __restrict__ chunk_ranks) {
   extern __shared__ int wcnt[];
   const int c = blockIdx.x;
   const int p = c * kChunk + threadIdx.x;
   const int e = p < npairs ? ids[p] : -1;
   const bool valid = p < npairs && id_ok(e, E);
-  if (p < npairs && !valid) atomicOr(&status[kStFlags], 1);
   const int r = chunk_rank(e, valid, E, id_bits, wcnt);
   if (p < npairs) chunk_ranks[p] = valid ? r : -1;
   for (int ee = threadIdx.x; ee < E; ee += kChunk) {
@@ -453,9 +453,11 @@ __global__ __launch_bounds__(1024) void permute_count_kernel(
   }
 }
 
-// Phase 2 (one block): per-expert totals, offsets, per-chunk bases, tiles.
+// Phase 2 (one block): per-expert totals, offsets, per-chunk bases, tiles,
+// and every status word of the call (the skipped-id flag from the count of
+// pairs that were kept; the words later steps accumulate into start at 0).
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
-    int nchunks, int E, int BM, int bound, int* __restrict__ status, int* __restrict__ offsets,
+    int npairs, int nchunks, int E, int BM, int bound, int* __restrict__ status, int* __restrict__ offsets,
     int* __restrict__ chunk_counts, int* __restrict__ tiles) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
@@ -478,6 +480,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
     for (int c = 0; c < nchunks; ++c) chunk_counts[(size_t)c * E + e] += ex;
   }
   if (e == 0) offsets[E] = total;
+  if (e < kStWords && e != kStNumTiles) status[e] = e == kStFlags ? (total != npairs ? 1 : 0) : 0;
   __syncthreads();
   write_tiles(cnt, off, E, BM, bound, scan_tmp, tiles, status);
 }
@@ -495,11 +498,6 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   const int pos = chunk_counts[(size_t)c * E + e] + r;
   sorted_pairs[pos] = p;
   inv[p] = pos;
-}
-
-// Clears the status words (multi-block path; the fused kernel does it itself).
-__global__ void clear_status_kernel(int* status) {
-  if (threadIdx.x < kStWords) status[threadIdx.x] = 0;
 }
 
 // ------------------------------------------------------------- launchers ----
@@ -554,10 +552,9 @@ hipError_t launch_permute(const int* ids, int npairs, int E, int BM, int tile_bo
     return hipGetLastError();
   }
   const int nchunks = (npairs + kChunk - 1) / kChunk;
-  clear_status_kernel<<<1, 64, 0, s>>>(ws.status);
   permute_count_kernel<<<nchunks, kChunk, (size_t)kChunkWaves * E * sizeof(int), s>>>(
-      ids, npairs, E, bits, ws.status, ws.chunk_counts, ws.chunk_ranks);
-  permute_scan_kernel<<<1, kChunk, 0, s>>>(nchunks, E, BM, tile_bound, ws.status, ws.offsets,
+      ids, npairs, E, bits, ws.chunk_counts, ws.chunk_ranks);
+  permute_scan_kernel<<<1, kChunk, 0, s>>>(npairs, nchunks, E, BM, tile_bound, ws.status, ws.offsets,
                                            ws.chunk_counts, ws.tiles);
   permute_scatter_kernel<<<nchunks, kChunk, 0, s>>>(ids, npairs, E, ws.chunk_counts,
                                                     ws.chunk_ranks, ws.sorted_pairs, ws.inv);

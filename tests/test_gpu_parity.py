@@ -164,6 +164,51 @@ def test_permutation_bit_exact(mx, T, E, k, hot):
         assert np.array_equal(got_tiles, np.array(want, dtype=np.int32))
 
 
+@pytest.mark.parametrize("act", [synth.ACT_BF16, synth.ACT_FP8_E4M3])
+def test_multiblock_permutation_bad_ids_and_status_reuse(mx, act):
+    # 4400 pairs: the multi-block permutation.  Ids outside [0, E) are skipped
+    # and flagged; a second call on the same workspace with clean ids and x
+    # halved (a smaller FP8 amax) must start from cleared status words.
+    E, H, I, T, k = 16, 64, 64, 1100, 4
+    L = synth.layer(seed=41, E=E, H=H, I=I)
+    Ld = _layer_dev(L)
+    logits, x = synth.moe_inputs(42, T, E=E, H=H, hot=2)
+    ids, w = oracle.route_topk(logits, k)
+    ids_bad = ids.copy()
+    ids_bad[0, 1] = -1
+    ids_bad[700, 3] = E + 2
+    ids_bad[1099, 0] = -7
+    ws = torch.zeros(mx.mxfp4_moe_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device="cuda")
+    lay = mx.mxfp4_moe_workspace_layout_query(T, H, I, E, k, act)
+
+    def call(xb, idb):
+        out = mx.mxfp4_moe_forward(to_dev(xb, torch), to_dev(idb.astype(np.int32), torch),
+                                   to_dev(w.astype(np.float32), torch), Ld["w13_blocks"], Ld["w13_scales"],
+                                   Ld["w13_bias"], Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"], act,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        return bf16_dev_to_f64(out)
+
+    got = call(x, ids_bad)
+    assert _status(ws, lay)[0] & 1
+    flat = ids_bad.reshape(-1).astype(np.int64)
+    keep = np.nonzero((flat >= 0) & (flat < E))[0]
+    _, offsets, sp, inv_kept = oracle.permute(flat[keep].reshape(-1, 1), E)
+    want_inv = np.full(T * k, -1, dtype=np.int64)
+    want_inv[keep] = inv_kept
+    assert np.array_equal(_ws_view(ws, lay, "expert_offsets", np.int32, E + 1), offsets)
+    assert np.array_equal(_ws_view(ws, lay, "sorted_pairs", np.int32, keep.size), keep[sp])
+    assert np.array_equal(_ws_view(ws, lay, "inv_pairs", np.int32, T * k), want_inv)
+    assert_close_rounded(got, oracle.moe_forward_routed(x, ids_bad, w, **L, act_mode=act)["out"], "bad ids")
+
+    # x / 2 exactly (bf16 exponent field minus one; no zeros or subnormals here)
+    assert np.all((x & 0x7f80) > 0x80)
+    x2 = (x - 0x80).astype(np.uint16)
+    got = call(x2, ids)
+    assert _status(ws, lay)[0] == 0
+    assert_close_rounded(got, oracle.moe_forward_routed(x2, ids, w, **L, act_mode=act)["out"], "reused workspace")
+
+
 # ------------------------------------------------------------ small layers ----
 
 SMALL = [  # E, H, I, T, k   (H/32 and I/32 give every K tail modulo 4)
