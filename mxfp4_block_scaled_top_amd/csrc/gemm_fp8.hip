@@ -573,8 +573,12 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
     else wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // refill the slot freed by the barrier
-    if (t + C::kStages - 1 < total) cp.issue(a);
+    // refill the slot freed by the barrier: A4 halfway through the step's
+    // MFMAs, so the matrix core works while this wave issues its copies
+    // (measured 1-2% faster there; the FP8 steps, with their two waits on
+    // LDS reads, were not faster that way)
+    const bool refill = t + C::kStages - 1 < total;
+    if (!A4 && refill) cp.issue(a);
     // step t's operands
     const uint32_t so = (uint32_t)(cslot * C::kSlot);
     const uint32_t aa0 = a0 + so, aa1 = a1 + so, ww = w0 + so, ss = s0 + so;
@@ -610,6 +614,11 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
           for (int tg = 0; tg < 4; ++tg)
             acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 4, 0, asc, 0,
                                                                            bsc[tg]);
+        }
+        if (h == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (refill) cp.issue(a);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
