@@ -350,7 +350,7 @@ def main():
                          "kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (requested %d)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (requested %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

@@ -150,7 +150,7 @@ typedef struct {
   uint64_t w2_scale_stream; /* the same for w2 */
 } mxfp4_moe_workspace_layout;
 
-/* Library ABI version (MXFP4_ABI_VERSION of the build). */
+/* Library ABI version (MXFP4_ABI_VERSION of the compiled library). */
 int mxfp4_abi_version(void);
 
 /* Static text for a status code. */
