@@ -292,6 +292,12 @@ struct PrefillCopier {
 
   // copies of the next step into its slot, then advance
   __device__ __forceinline__ void issue(const PrefillArgs& a) {
+    issue_act(a);
+    issue_w(a);
+    advance(a);
+  }
+  // the activation copies (and the scale copies) of the next step
+  __device__ __forceinline__ void issue_act(const PrefillArgs& a) {
     uint8_t* dst = smem + slot * C::kSlot;
     const bool tail = step == a.nsteps - 1;
     const int kb = step * kBK;
@@ -307,12 +313,6 @@ struct PrefillCopier {
                                          16, 0, 0);
       }
     }
-#pragma unroll
-    for (int i = 0; i < C::kWDma; ++i) {
-      const int blk = C::kSub * 4 * step + w_blk;  // past K: the row's first block
-      __builtin_amdgcn_global_load_lds(wptr[i] + (!tail || blk < a.nb ? blk * kBlockBytes : 0),
-                                       dst + C::kW + 1024 * (NW * i + wave), 16, 0, 0);
-    }
     if (A4) {
       // sub-step wave / 4 of this step; past the last one (K tail) the last
       // sub-step again (its values are masked)
@@ -324,6 +324,19 @@ struct PrefillCopier {
     } else if (lane < 8) {
       __builtin_amdgcn_global_load_lds(wsp + step * 1024, dst + C::kSc + 128 * wave, 16, 0, 0);
     }
+  }
+  // the weight copies of the next step
+  __device__ __forceinline__ void issue_w(const PrefillArgs& a) {
+    uint8_t* dst = smem + slot * C::kSlot;
+    const bool tail = step == a.nsteps - 1;
+#pragma unroll
+    for (int i = 0; i < C::kWDma; ++i) {
+      const int blk = C::kSub * 4 * step + w_blk;  // past K: the row's first block
+      __builtin_amdgcn_global_load_lds(wptr[i] + (!tail || blk < a.nb ? blk * kBlockBytes : 0),
+                                       dst + C::kW + 1024 * (NW * i + wave), 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void advance(const PrefillArgs& a) {
     slot = slot + 1 == C::kStages ? 0 : slot + 1;
     if (++step == a.nsteps) {
       step = 0;
@@ -573,12 +586,16 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
     else wait_vm<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // refill the slot freed by the barrier: A4 halfway through the step's
-    // MFMAs, so the matrix core works while this wave issues its copies
-    // (measured 1-2% faster there; the FP8 steps, with their two waits on
-    // LDS reads, were not faster that way)
+    // refill the slot freed by the barrier.  A4: the activation and scale
+    // copies here, the weight copies (16 rows, 8 lines per instruction)
+    // halfway through the step's MFMAs, so the matrix core works while this
+    // wave issues them (measured 4-5% faster than all copies here; weights
+    // first was 15% slower).  The FP8 steps were not faster with any split.
     const bool refill = t + C::kStages - 1 < total;
-    if (!A4 && refill) cp.issue(a);
+    if (refill) {
+      if (A4) cp.issue_act(a);
+      else cp.issue(a);
+    }
     // step t's operands
     const uint32_t so = (uint32_t)(cslot * C::kSlot);
     const uint32_t aa0 = a0 + so, aa1 = a1 + so, ww = w0 + so, ss = s0 + so;
@@ -617,7 +634,10 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
         }
         if (h == 0) {
           __builtin_amdgcn_sched_barrier(0);
-          if (refill) cp.issue(a);
+          if (refill) {
+            cp.issue_w(a);
+            cp.advance(a);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
