@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer GB/s & % HBM roofline (decode 4–32 tok); MXFP4 TFLOP/s (prefill)"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # dense MFMA, bf16
 FP8_PEAK_TFLOPS = 5000.0        # dense MFMA, FP8 (the FP8 x FP4 instruction's operand rate)
 MXFP4_PEAK_TFLOPS = 10100.0     # dense MFMA, FP4 / FP6
 PRIMARY = "moe_decode_t32"
@@ -51,14 +52,22 @@ def expert_bytes(H, I):
     return gate_up, down
 
 
-def moe_accounting(ids, T, H, I, act):
+def h_bytes_written(pairs, I, act):
+    """Bytes of h the gate_up kernel writes: bf16 hi + lo (bf16 activations) or
+    fp32 (FP8) = 4 B per element; with MXFP4 activations the epilogue writes
+    E2M1 codes and one E8M0 byte per 32 elements = 17/32 B per element."""
+    if act == 2:
+        return pairs * I * 17 // 32
+    return pairs * I * 4
+
+
+def moe_accounting(ids, T, H, I, act, E=128):
     """Algorithmic bytes and flops of one layer pass and of its gate_up kernel."""
     touched = len(np.unique(ids))
     pairs = ids.size
     gu, dn = expert_bytes(H, I)
-    E = 128
     layer_bytes = touched * (gu + dn) + T * H * 2 + T * E * 4 + T * H * 2
-    h_bytes = pairs * I * 4                     # bf16 hi+lo or fp32 h written
+    h_bytes = h_bytes_written(pairs, I, act)
     # bf16 x, E4M3 codes, or E2M1 codes + one scale byte per 32 read
     xin = T * H * 2 if act == 0 else T * H if act == 1 else T * H * 17 // 32
     gemm1_bytes = touched * gu + xin + h_bytes
@@ -66,6 +75,35 @@ def moe_accounting(ids, T, H, I, act):
     flops = 2.0 * pairs * (2 * I * H + H * I)
     return dict(touched=touched, pairs=pairs, layer_bytes=layer_bytes, gemm1_bytes=gemm1_bytes,
                 gemm1_flops=gemm1_flops, flops=flops)
+
+
+def issued_peak_tflops(act):
+    """Dense peak of the MFMA instructions a quantised layer issues: FP8 mode
+    runs gate_up (2/3 of the flops) on the bf16 MFMA with exactly expanded
+    operands and down (1/3) on the block-scaled FP8 x FP4 MFMA at the FP8 rate;
+    MXFP4 activations run both on the FP4 x FP4 form at the FP4 rate."""
+    if act == 2:
+        return MXFP4_PEAK_TFLOPS
+    if act == 1:
+        return 1.0 / ((2.0 / 3.0) / BF16_PEAK_TFLOPS + (1.0 / 3.0) / FP8_PEAK_TFLOPS)
+    return BF16_PEAK_TFLOPS
+
+
+def tflops_fractions(tflops, flops, nbytes, act, ceiling_gbps=None):
+    """The four readings of a prefill TFLOP/s figure: raw, against the nominal
+    MXFP4 peak, against the peak of the issued MFMA form, and against the
+    attainable roofline min(issued peak, AI x HBM) (nominal 8 TB/s, and the
+    measured read ceiling when given)."""
+    ai = flops / nbytes
+    peak = issued_peak_tflops(act)
+    out = dict(TFLOPs=tflops, frac_mxfp4_peak=tflops / MXFP4_PEAK_TFLOPS, issued_peak_TFLOPs=peak,
+               frac_issued_peak=tflops / peak, flop_per_byte=ai,
+               attainable_TFLOPs=min(peak, ai * HBM_PEAK_GBS / 1e3))
+    out["frac_attainable"] = tflops / out["attainable_TFLOPs"]
+    if ceiling_gbps:
+        out["attainable_measured_TFLOPs"] = min(peak, ai * ceiling_gbps / 1e3)
+        out["frac_attainable_measured"] = tflops / out["attainable_measured_TFLOPs"]
+    return out
 
 
 def source_digest(files):
@@ -165,7 +203,35 @@ def moe_setup(run, Ld, name, synth):
     return step, acct, wl
 
 
-def measure_moe(run, Ld, name, synth, steps, warmup):
+def measure_ceiling(run, nbytes=4 << 30, reps=10):
+    """Streaming-read ceiling of this device: a buffer of `nbytes` (4 GiB,
+    16 times the last-level cache) read once per launch with nontemporal
+    register loads and with nontemporal direct-to-LDS copies; mean GB/s of
+    `reps` launches after one warm-up each."""
+    torch, mx = run.torch, run.mx
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = dict(bytes=nbytes)
+    for mode, key in ((0, "register_loads_GBps"), (1, "lds_dma_GBps")):
+        n = mx.mxfp4_stream_read(buf, mode, sink)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            mx.mxfp4_stream_read(buf, mode, sink)
+        b.record()
+        torch.cuda.synchronize()
+        out[key] = n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+        out["bytes_read"] = n
+    out["ceiling_GBps"] = max(out["register_loads_GBps"], out["lds_dma_GBps"])
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_moe(run, Ld, name, synth, steps, warmup, ceiling_gbps=None):
     step, acct, wl = moe_setup(run, Ld, name, synth)
     ms, stages, wall = run.time_steps(step, steps, warmup, flush=True, stage_events=True)
     ms_plain, _, _ = run.time_steps(step, steps, warmup, flush=True, stage_events=False)
@@ -193,6 +259,15 @@ def measure_moe(run, Ld, name, synth, steps, warmup):
         gemm1_TFLOPs=acct["gemm1_flops"] / g1 / 1e9,
         algorithmic_bytes=acct["layer_bytes"], gemm1_bytes=acct["gemm1_bytes"],
         flops=acct["flops"], wall_s=wall)
+    if ceiling_gbps:
+        res["layer_frac_measured_ceiling"] = res["layer_GBps"] / ceiling_gbps
+        res["gemm1_frac_measured_ceiling"] = res["gemm1_GBps"] / ceiling_gbps
+    if act != 0:
+        res["layer_tflops"] = tflops_fractions(res["layer_TFLOPs"], acct["flops"], acct["layer_bytes"], act,
+                                               ceiling_gbps)
+        if prepared:
+            res["layer_tflops_prepared_scales"] = tflops_fractions(
+                acct["flops"] / prepared / 1e9, acct["flops"], acct["layer_bytes"], act, ceiling_gbps)
     return res
 
 
@@ -290,30 +365,47 @@ def measure_quantizer(run, synth, steps, warmup):
                 bytes=nbytes)
 
 
-def cpu_baseline(synth, budget_tokens=32, min_seconds=10.0, max_reps=4):
-    """The float64 oracle on the first `budget_tokens` tokens of the headline batch (all 32 by
-    default: about 80 experts), on host cores, repeated until at least `min_seconds` of CPU
-    work (at most `max_reps` passes); the rate is the mean over the passes."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(synth, budget_tokens=16, runs=3):
+    """The float64 oracle on the first `budget_tokens` tokens of the headline batch
+    (16 of 32 by default, about 50 experts), on host cores, `runs` timed passes;
+    the rate is the median over the passes."""
     import oracle
+    threads, blas = 1, "unknown"
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
         threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(sorted({"%s %s (%s)" % (i.get("internal_api", "?"), i.get("version", "?"),
+                                                 i.get("threading_layer", "?"))
+                                 for i in info if i.get("user_api") == "blas"})) or "none found"
     except Exception:
-        threads = 1
+        pass
     L = synth.layer()
     wl = synth.workload(PRIMARY)
     x, logits = wl["x"][:budget_tokens], wl["logits"][:budget_tokens]
-    reps, dt = 0, 0.0
-    while reps < max_reps and (reps == 0 or dt < min_seconds):
+    times = []
+    for _ in range(runs):
         t0 = time.perf_counter()
         res = oracle.moe_forward(x, logits, **L, k=synth.TOPK_GPT_OSS, act_mode=wl["act_mode"])
-        dt += time.perf_counter() - t0
-        reps += 1
+        times.append(time.perf_counter() - t0)
     acct = moe_accounting(res["ids"], budget_tokens, synth.H_GPT_OSS, synth.H_GPT_OSS, 0)
-    return dict(value=acct["layer_bytes"] * reps / dt / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample="first %d of the %d tokens of the decode batch (%d experts touched), "
-                       "float64 numpy, %d passes, %.1f s" % (budget_tokens, wl["T"], acct["touched"], reps, dt))
+    med = float(np.median(times))
+    return dict(value=acct["layer_bytes"] / med / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample="first %d of the %d tokens of the decode batch (%d experts touched), float64 numpy, "
+                       "median of %d passes (%s s)" % (budget_tokens, wl["T"], acct["touched"], runs,
+                                                       ", ".join("%.2f" % t for t in times)),
+                cpu_model=_cpu_model(), nproc=os.cpu_count(), blas=blas, seconds_median=med)
 
 
 def pmc_traffic(kernel):
@@ -348,6 +440,10 @@ def main():
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (3 times), the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="only measure the streaming-read ceiling (4 GiB read once per launch, register "
+                         "loads and direct-to-LDS copies) and print it")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (requested %d)" % args.gpus,
@@ -371,20 +467,29 @@ def main():
         return
     mx.lib()
     run = Runner(torch, mx, args.flush)
+    ceiling = None if args.no_ceiling else measure_ceiling(run)
+    if ceiling:
+        print("bench: read ceiling %.0f GB/s (register loads %.0f, LDS DMA %.0f)"
+              % (ceiling["ceiling_GBps"], ceiling["register_loads_GBps"], ceiling["lds_dma_GBps"]),
+              file=sys.stderr, flush=True)
+    if args.hbm_ceiling:
+        print(json.dumps({"hbm_ceiling": ceiling}), flush=True)
+        return
+    cg = ceiling["ceiling_GBps"] if ceiling else None
     L = synth.layer()
     Ld = {k: run.dev(v) for k, v in L.items()}
     del L
     print("bench: layer resident (%.2f GB)" % (sum(t.numel() * t.element_size() for t in Ld.values()) / 1e9),
           file=sys.stderr, flush=True)
 
-    prim = measure_moe(run, Ld, args.workload, synth, args.steps, args.warmup)
+    prim = measure_moe(run, Ld, args.workload, synth, args.steps, args.warmup, cg)
     print("bench: %s %.1f us/step" % (args.workload, prim["ms_per_step"] * 1e3), file=sys.stderr, flush=True)
     others = {}
     if not args.primary_only:
         for name in synth.MOE_WORKLOADS:
             if name == args.workload:
                 continue
-            others[name] = measure_moe(run, Ld, name, synth, max(args.steps // 2, 5), 2)
+            others[name] = measure_moe(run, Ld, name, synth, max(args.steps // 2, 5), 2, cg)
             print("bench: %s %.1f us/step" % (name, others[name]["ms_per_step"] * 1e3),
                   file=sys.stderr, flush=True)
         del Ld
@@ -412,6 +517,9 @@ def main():
                     frac=prim["gemm1_GBps"] / HBM_PEAK_GBS)
     roof["kernel"] = kname
     roof["traffic"] = pmc_traffic(kname)
+    if cg and roof["unit"] == "GB/s":
+        roof["measured_ceiling"] = cg
+        roof["frac_measured_ceiling"] = roof["achieved"] / cg
     line = {
         "metric": METRIC,
         "value": prim["layer_GBps"],
@@ -429,6 +537,7 @@ def main():
                    "hidden": 2880, "intermediate": 2880, "weights": "mxfp4", "act": prim["act"],
                    "parallelism": "none (1 GPU)", "cache_eviction": "%s 1 GiB before each step" % args.flush},
         "hbm_frac": prim["layer_hbm_frac"],
+        "hbm_ceiling": ceiling,
         "roofline": roof,
         "detail": prim,
         "workloads": others,

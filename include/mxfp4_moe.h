@@ -198,7 +198,7 @@ int mxfp4_moe_workspace_layout_query(int64_t T, int64_t H, int64_t I, int32_t E,
  * fp32 quotient v / s.  In MXFP4_ACT_MXFP4 mode a_t and h' are the
  * MXFP4-dequantised values, each 32-element block of a row of x (and of each
  * pair's fp32 h) quantised on its own: shared exponent X = floor(log2 amax)
- * - 2 clamped to [-125, 125], codes = the E2M1 value nearest to |v| / 2^X
+ * - 2 clamped to [-116, 125], codes = the E2M1 value nearest to |v| / 2^X
  * (ties to the even code, saturating at 6), sign kept (the rule of
  * mxfp4_quantize_weights).  W13 rows [0, I) are the gate rows, [I, 2I) the up
  * rows.
@@ -220,9 +220,23 @@ int mxfp4_moe_workspace_layout_query(int64_t T, int64_t H, int64_t I, int32_t E,
  *   workspace    >= mxfp4_moe_workspace_size() bytes, 256-byte aligned
  *   opts         NULL or per-call options (stage events)
  * Limits: H, I positive multiples of 32 (<= 65536); 1 <= E <= 512;
- * 1 <= k <= min(E, 16); 0 <= T <= 2^22 (T == 0 is a no-op).  In MXFP4_ACT_BF16 mode, E8M0 scale bytes must
- * lie in [2, 252] (the weight is formed exactly in bf16 before the MFMA); the
- * FP8 and MXFP4-activation modes accept every byte except 255.
+ * 1 <= k <= min(E, 16); 0 <= T <= 2^22 (T == 0 is a no-op).
+ * E8M0 scale bytes (the gpt-oss page's range is 2^-127 .. 2^127; 255 is not a
+ * scale in any mode):
+ *   - MXFP4_ACT_BF16 and MXFP4_ACT_FP8_E4M3: bytes in [11, 252] for w13
+ *     and w2.  These paths form each weight in bf16 with the hardware's
+ *     scaled FP4 conversion, which is exact for bytes 11..252 only (measured
+ *     on gfx950: for a byte s <= 10 it gives E2M1 * (2^s + 3) * 2^-127, and
+ *     253, 254 overflow bf16 at 6 * 2^126).  In FP8 mode the sums are
+ *     moreover taken over the E4M3 codes (up to 448) and the per-tensor
+ *     scales applied after them, so a row whose sum of |weight| * 448
+ *     exceeds the fp32 range overflows even where the scaled result would not
+ *     (with K = 2880 this needs weights of magnitude 2^104 or more).
+ *   - MXFP4_ACT_MXFP4: every byte except 255 (the block-scaled MFMA applies
+ *     both operands' E8M0 scales itself).
+ * Bytes outside these ranges are not rejected (that would need a pass over
+ * the scales on every call); the result is then undefined.  The same holds
+ * for NaN or infinite bf16 values in x or the biases.
  */
 int mxfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E,
                       int32_t k, const int32_t* topk_ids, const float* topk_weights,
@@ -281,7 +295,11 @@ int nvfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
  * activations, fp32 accumulation, one round-to-nearest-even to bf16.
  *   x         bf16 [M, K]          16-byte aligned
  *   w_blocks  uint8 [N, K/32, 16]  16-byte aligned
- *   w_scales  uint8 [N, K/32]      4-byte aligned; E8M0 bytes in [2, 252]
+ *   w_scales  uint8 [N, K/32]      4-byte aligned; E8M0 bytes in [11, 252]
+ *                                  (the weight is formed in bf16 with the
+ *                                  scaled FP4 conversion, exact for these
+ *                                  bytes only; others are not rejected and
+ *                                  give undefined results)
  *   bias      bf16 [N] or NULL, 8-byte aligned
  *   out       bf16 [M, N]          16-byte aligned, must not alias the inputs
  * Limits: K a positive multiple of 32, N a positive multiple of 16,
@@ -293,7 +311,11 @@ int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K,
 
 /*
  * Per-tensor FP8 E4M3 quantiser, exactly the codec the FP8 MoE mode applies to
- * x and h, exported for bit-exact tests:
+ * x and h, exported for bit-exact tests.  The pages run the MoE as FP8
+ * activations times FP4 weights (spark-vllm page, "What's Included") and list
+ * real activation scales as open work ("Numerical Accuracy"); this codec is
+ * the OCP E4M3 encoding with the per-tensor scale amax/448 the FP8 workloads
+ * specify:
  *   amax = max |v|; s = fp32(amax / 448) (1 if amax == 0);
  *   code = E4M3 round-to-nearest-even, saturating to +-448, of fp32(v / s).
  *   in        fp32 [n] (in_dtype 0) or bf16 [n] (in_dtype 1), 16-byte aligned
@@ -311,8 +333,12 @@ int mxfp4_quant_fp8_e4m3(const void* in, int32_t in_dtype, int64_t n, uint8_t* c
  * stored bf16; spark-vllm page: MXFP4 for qkv/o/lm_head).  The steps follow
  * the gpt-oss page's "Conversion Methodology" (per-block amax, scale, E2M1
  * rounding, packing) with 32-element blocks and the OCP MX scale rule:
- *   X = floor(log2(max |v| of the block)) - 2, clamped to [-125, 125];
- *   scale byte = X + 127 (so 2..252, what mxfp4_linear takes);
+ *   X = floor(log2(max |v| of the block)) - 2, clamped to [-116, 125] (the
+ *       lower clamp is this library's departure from the OCP rule, which
+ *       would go down to -127: it keeps every byte written inside what all
+ *       entry points apply exactly; it only affects blocks with max |v|
+ *       below 2^-114);
+ *   scale byte = X + 127 (so 11..252, what mxfp4_linear takes);
  *   code = E2M1 value nearest to |v| / 2^X, ties to the even mantissa,
  *          saturating at 6, with the sign bit of v;
  *   nibbles packed as mxfp4_linear reads them (element 2i low, 2i+1 high).
@@ -323,6 +349,25 @@ int mxfp4_quant_fp8_e4m3(const void* in, int32_t in_dtype, int64_t n, uint8_t* c
  */
 int mxfp4_quantize_weights(const uint16_t* w, int64_t N, int64_t K, uint8_t* blocks,
                            uint8_t* scales, void* stream);
+
+/*
+ * Measurement helper, not part of the layer: reads `bytes` of device memory
+ * once, so that a caller timing it gets the device's streaming-read rate, the
+ * ceiling against which the weight streams of the layer are judged (the
+ * forum page compares its decode rate with the "bandwidth ceiling" of its
+ * GPU the same way).
+ *   buf        device memory, 1024-byte aligned, at least `bytes` long
+ *   mode       0: 16-byte nontemporal loads into registers; 1: 16-byte
+ *              nontemporal direct-to-LDS copies, 1 KB per wave instruction
+ *              (the decode GEMV's access)
+ *   sink       uint32 [1] device word; written only in the (practically
+ *              impossible) case that the folded data equals a fixed value
+ *   bytes_read host output: bytes actually read (the grid reads whole 16 KB
+ *              rounds per block: `bytes` rounded down, 0 below 16 KB)
+ * Limits: bytes <= 2^40.
+ */
+int mxfp4_stream_read(const void* buf, uint64_t bytes, int32_t mode, uint32_t* sink,
+                      uint64_t* bytes_read, void* stream);
 
 /* Thin hipEvent helpers so callers can time stages without their own HIP
    bindings: create (timing enabled), destroy, and elapsed milliseconds between

@@ -94,13 +94,15 @@ def lib():
         L.mxfp4_quant_fp8_e4m3.argtypes = [_c_void_p, _i32, _i64, _c_void_p, _c_void_p, _c_void_p,
                                            _c_void_p]
         L.mxfp4_quantize_weights.argtypes = [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]
+        L.mxfp4_stream_read.argtypes = [_c_void_p, ctypes.c_uint64, _i32, _c_void_p,
+                                        ctypes.POINTER(ctypes.c_uint64), _c_void_p]
         L.mxfp4_event_create.argtypes = [ctypes.POINTER(_c_void_p)]
         L.mxfp4_event_destroy.argtypes = [_c_void_p]
         L.mxfp4_event_elapsed_ms.argtypes = [_c_void_p, _c_void_p, ctypes.POINTER(ctypes.c_float)]
         for name in ("mxfp4_route_topk", "mxfp4_moe_workspace_size", "mxfp4_moe_workspace_layout_query",
                      "mxfp4_moe_forward", "mxfp4_moe_layer", "nvfp4_moe_forward", "mxfp4_linear",
                      "mxfp4_quant_fp8_e4m3",
-                     "mxfp4_quantize_weights", "mxfp4_event_create",
+                     "mxfp4_quantize_weights", "mxfp4_stream_read", "mxfp4_event_create",
                      "mxfp4_event_destroy", "mxfp4_event_elapsed_ms"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -366,6 +368,19 @@ def mxfp4_quantize_weights(w, blocks=None, scales=None, stream=None):
     _check("mxfp4_quantize_weights", lib().mxfp4_quantize_weights(
         _ptr(w), N, K, _ptr(blocks), _ptr(scales), _stream(stream)))
     return blocks, scales
+
+
+def mxfp4_stream_read(buf, mode, sink=None, stream=None):
+    """Read the device buffer `buf` once (mode 0: register loads, 1: direct-to-LDS
+    copies); returns the bytes actually read.  For ceiling measurements."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    n = ctypes.c_uint64()
+    _check("mxfp4_stream_read", lib().mxfp4_stream_read(
+        _ptr(buf), buf.numel() * buf.element_size(), mode, _ptr(sink), ctypes.byref(n), _stream(stream)))
+    return n.value
 
 
 def mxfp4_event_create():

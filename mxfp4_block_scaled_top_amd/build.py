@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmxfp4moe.so")
 SOURCES = ["route_permute.hip", "quant_combine.hip", "quant_mxfp4.hip", "gemm_bf16.hip", "gemm_fp8.hip",
-           "abi.hip"]
+           "stream_probe.hip", "abi.hip"]
 ARCH = "gfx950"
 # No fast-math: the FP8 quantiser relies on correctly rounded fp32 division.
 # Packed fp32 VALU ops are switched off for the device code.

@@ -394,6 +394,24 @@ int mxfp4_quantize_weights(const uint16_t* w, int64_t N, int64_t K, uint8_t* blo
   return ok();
 }
 
+int mxfp4_stream_read(const void* buf, uint64_t bytes, int32_t mode, uint32_t* sink,
+                      uint64_t* bytes_read, void* stream) {
+  if (mode != 0 && mode != 1) return fail(MXFP4_E_MODE, "stream_read: unknown mode %d", mode);
+  if (!bytes_read) return fail(MXFP4_E_NULL, "stream_read: bytes_read is null");
+  if (bytes > (1ULL << 40)) return fail(MXFP4_E_SHAPE, "stream_read: %llu bytes out of range",
+                                        (unsigned long long)bytes);
+  if (bytes > 0 && (!buf || !sink)) return fail(MXFP4_E_NULL, "stream_read: null pointer");
+  if (!aligned(buf, 1024) || !aligned(sink, 4))
+    return fail(MXFP4_E_ALIGN, "stream_read: buf needs 1024-byte, sink 4-byte alignment");
+  int rc = check_device();
+  if (rc) return rc;
+  *bytes_read = (uint64_t)mx::stream_read_bytes((int64_t)bytes);
+  if (*bytes_read == 0) return ok();
+  hipError_t e = mx::launch_stream_read(buf, (int64_t)bytes, mode == 1, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream_read launch");
+  return ok();
+}
+
 int mxfp4_event_create(void** event) {
   if (!event) return fail(MXFP4_E_NULL, "event is null");
   hipEvent_t ev;

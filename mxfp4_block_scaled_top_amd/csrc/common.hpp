@@ -19,6 +19,12 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kBlockElems = 32;   // elements per MX block
+// Shared-exponent range of the library's MXFP4 quantisers (scale bytes
+// 11..252).  Below 11 the scaled FP4 -> bf16 conversion the bf16 and FP8
+// contractions use does not give E2M1 * 2^(s-127) (measured: it gives
+// E2M1 * (2^s + 3) * 2^-127 for s <= 10), so no quantiser writes such bytes.
+constexpr int kMxExpMin = -116;
+constexpr int kMxExpMax = 125;
 constexpr int kBlockBytes = 16;   // bytes per MX block of E2M1 nibbles
 
 // Indices of the int32 status words at the head of the MoE workspace.

@@ -734,7 +734,7 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
             }
           am = max(am, (uint32_t)__shfl_xor((int)am, 16, 64));
           am = max(am, (uint32_t)__shfl_xor((int)am, 32, 64));
-          const int x = min(max((int)(am >> 23) - 127 - 2, -125), 125);
+          const int x = min(max((int)(am >> 23) - 127 - 2, kMxExpMin), kMxExpMax);
           const float inv = __uint_as_float((uint32_t)(127 - x) << 23);
           // codes of h * 2^-X (|.| < 8): the hardware conversion rounds exactly
           // as e2m1_round_mag with the sign bit kept (checked on every fp32

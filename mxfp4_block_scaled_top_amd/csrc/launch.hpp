@@ -132,6 +132,12 @@ hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const Ws
 hipError_t launch_quant_mxfp4(const uint16_t* w, int64_t nblocks, uint8_t* blocks, uint8_t* scales,
                               hipStream_t s);
 
+// Streaming read of `bytes` (rounded down to whole 16 KB rounds of the
+// grid: stream_read_bytes gives the bytes actually read) for ceiling
+// measurements; dma selects direct-to-LDS copies over register loads.
+hipError_t launch_stream_read(const void* buf, int64_t bytes, bool dma, uint32_t* sink, hipStream_t s);
+int64_t stream_read_bytes(int64_t bytes);
+
 // out[t] = sum_j w[t,j] * y[inv[t*k+j]]  -> bf16
 hipError_t launch_combine(const MoeShape& sh, const float* topk_weights, const WsPtrs& ws,
                           uint16_t* out, hipStream_t s);

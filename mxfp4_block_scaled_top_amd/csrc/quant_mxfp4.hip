@@ -5,7 +5,7 @@
 // The steps are those of the gpt-oss page's "Conversion Methodology" (per
 // block: amax, scale, E2M1 rounding, packing), with the OCP MX scale rule for
 // E8M0: shared exponent X = floor(log2 amax) - 2 (2 = exponent of the largest
-// E2M1 magnitude, 6), clamped to [-125, 125] (scale bytes 2..252); codes are
+// E2M1 magnitude, 6), clamped to [kMxExpMin, kMxExpMax] = [-116, 125] (scale bytes 11..252); codes are
 // the nearest E2M1 magnitude of |v| / 2^X with ties to the even mantissa and
 // saturation at 6; the sign bit is the input's.
 //
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
     for (int i = 0; i < 16; ++i) amax = max(amax, max(v[i] & 0x7fffu, (v[i] >> 16) & 0x7fffu));
     // floor(log2 amax) is the bf16 exponent field - 127 for normal amax; zero
     // and subnormal blocks land below the clamp
-    const int x = min(max((int)(amax >> 7) - 127 - 2, -125), 125);
+    const int x = min(max((int)(amax >> 7) - 127 - 2, kMxExpMin), kMxExpMax);
     const float inv = __uint_as_float((uint32_t)(127 - x) << 23);   // 2^-X, a normal fp32
     // elements 2i (low half of v[i]) and 2i + 1 scaled by 2^-X (exact, below
     // 8 in magnitude) -> byte i of the block, element 2i in the low nibble.
@@ -77,7 +77,7 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, uint4& out) {
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7fffffffu);
-  const int x = min(max((int)(amax >> 23) - 127 - 2, -125), 125);
+  const int x = min(max((int)(amax >> 23) - 127 - 2, kMxExpMin), kMxExpMax);
   const float inv = __uint_as_float((uint32_t)(127 - x) << 23);
   // elements 2j, 2j + 1 -> byte j, by the hardware conversion (rounding and
   // sign as e2m1_round_mag, checked on every fp32 below 8 in magnitude)

@@ -6,12 +6,21 @@ elements rounded to E2M1 with that scale, packed codes and per-block scales.
 MXFP4 takes the same steps with 32-element blocks and power-of-two E8M0 scales
 (gpt-oss page, "GPT-OSS-120B Architecture" and the MXFP4/NVFP4 property
 table).  The pages leave the MXFP4 scale rule open; the reading taken here is
-the OCP Microscaling one:
+the OCP Microscaling one, with one departure of this library's own:
 
   * shared exponent X = floor(log2(amax)) - 2, where 2 is the exponent of the
     largest E2M1 magnitude (6 = 1.5 * 2^2), so every |v| / 2^X is below 8;
-  * X clamped to [-125, 125], i.e. scale bytes in [2, 252], the range the
-    library's bf16 kernels take (an all-zero block gets X = -125);
+  * X clamped to [-116, 125], i.e. scale bytes in [11, 252].  This clamp is
+    the library's choice, not the OCP rule: the page's E8M0 range is
+    2^-127 .. 2^127 and the OCP rule would give X down to -127 (bytes 0..10)
+    to blocks with amax below 2^-114.  The library clamps so that every scale
+    byte its quantisers write is one that all of its kernels apply exactly:
+    its bf16 and FP8 contractions form each weight in bf16 with the
+    hardware's scaled FP4 conversion, which is exact for bytes 11..252 only
+    (measured on gfx950).  Only blocks with amax < 2^-114 are affected: for
+    finite bf16 or fp32 input floor(log2(amax)) <= 127, so the upper clamp is
+    never reached.  An all-zero block gets X = -116.  Pinned by a hand-worked
+    block (tests/golden/mxfp4_small_block_case.txt);
   * element code = the E2M1 magnitude nearest to |v| / 2^X, ties to the code
     with an even mantissa bit, values above 6 saturating to 6; the sign bit
     is the input's sign (a negative value that rounds to zero gives -0).
@@ -21,7 +30,7 @@ import numpy as np
 
 from .mxfp4 import BLOCK, E2M1_TABLE, pack_nibbles
 
-X_MIN = -125
+X_MIN = -116
 X_MAX = 125
 
 

@@ -16,7 +16,7 @@ E_NULL, E_SHAPE, E_ALIGN, E_MODE, E_WORKSPACE, E_DEVICE = 1, 2, 3, 4, 5, 6
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mxfp4_[a-z0-9_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:mxfp4|nvfp4)_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -183,3 +183,12 @@ def test_nvfp4_moe_forward_rejects_bad_arguments_without_touching_memory(L):
     assert f(*a) == E_SHAPE
     a = list(args); a[2] = 2880 + 16                  # H % 32
     assert f(*a) == E_SHAPE
+
+
+def test_stream_read_validation(L):
+    n = ctypes.c_uint64(0)
+    assert L.mxfp4_stream_read(_fake(), 1 << 20, 2, _fake(), ctypes.byref(n), None) == E_MODE
+    assert L.mxfp4_stream_read(_fake(), 1 << 20, 0, _fake(), None, None) == E_NULL
+    assert L.mxfp4_stream_read(None, 1 << 20, 1, _fake(), ctypes.byref(n), None) == E_NULL
+    assert L.mxfp4_stream_read(ctypes.c_void_p(0x1010), 1 << 20, 0, _fake(), ctypes.byref(n), None) == E_ALIGN
+    assert L.mxfp4_stream_read(_fake(), 1 << 41, 0, _fake(), ctypes.byref(n), None) == E_SHAPE

@@ -55,3 +55,32 @@ def test_counter_traffic_is_reported_only_for_matching_sources(tmp_path, monkeyp
     assert bench.pmc_traffic("other") is None
     p.write_text(json.dumps(stale))
     assert bench.pmc_traffic("k") is None
+
+
+def test_gate_up_h_bytes_follow_the_activation_mode():
+    # h written by the gate_up kernel: bf16 hi + lo or fp32 = 4 B per element;
+    # MXFP4 activations: E2M1 codes (1/2 B) and one E8M0 byte per 32 elements
+    T, H, I = 2, 2880, 2880
+    ids = np.array([[0, 1, 2, 3], [4, 5, 6, 7]])
+    gu, _ = bench.expert_bytes(H, I)
+    for act, xin, hb in ((0, T * H * 2, 8 * I * 4), (1, T * H, 8 * I * 4),
+                         (2, T * H * 17 // 32, 8 * I * 17 // 32)):
+        acc = bench.moe_accounting(ids, T, H, I, act)
+        assert acc["gemm1_bytes"] == 8 * gu + xin + hb
+    assert bench.h_bytes_written(8, I, 2) == 8 * 2880 // 32 * 17 == 12240
+    # the logits term takes the layer's expert count
+    a128 = bench.moe_accounting(ids, T, H, I, 0)
+    a64 = bench.moe_accounting(ids, T, H, I, 0, E=64)
+    assert a128["layer_bytes"] - a64["layer_bytes"] == T * 64 * 4
+
+
+def test_tflops_fractions():
+    # FP8 mode: 2/3 of the flops on the bf16 MFMA (2.5 PF), 1/3 at the FP8 rate (5 PF)
+    assert abs(bench.issued_peak_tflops(1) - 3000.0) < 1e-9
+    assert bench.issued_peak_tflops(2) == bench.MXFP4_PEAK_TFLOPS
+    f = bench.tflops_fractions(1500.0, 2e12, 1e9, 2, ceiling_gbps=6000.0)
+    assert f["flop_per_byte"] == 2000.0
+    assert f["attainable_TFLOPs"] == min(10100.0, 2000.0 * 8000.0 / 1e3)
+    assert abs(f["frac_attainable"] - 1500.0 / 10100.0) < 1e-12
+    assert f["attainable_measured_TFLOPs"] == min(10100.0, 2000.0 * 6.0)
+    assert abs(f["frac_mxfp4_peak"] - 1500.0 / 10100.0) < 1e-12

@@ -104,14 +104,14 @@ def _bf_floor_log2(a):
 
 def _bf_mx_quant(values):
     """MXFP4 of one row (length a multiple of 32), block by block: shared
-    exponent floor(log2 amax) - 2 clamped to [-125, 125], each |v| / 2^X to the
+    exponent floor(log2 amax) - 2 clamped to [-116, 125], each |v| / 2^X to the
     nearest E2M1 magnitude (a tie to the even code, past 6 to 6), sign kept.
     Returns the dequantized Fractions."""
     out = []
     for b0 in range(0, len(values), 32):
         blk = values[b0:b0 + 32]
         amax = max(abs(v) for v in blk)
-        X = -125 if amax == 0 else min(max(_bf_floor_log2(amax) - 2, -125), 125)
+        X = -116 if amax == 0 else min(max(_bf_floor_log2(amax) - 2, -116), 125)
         sc = Fraction(2) ** X
         for v in blk:
             q = abs(v) / sc
@@ -129,7 +129,11 @@ def _silu(z):
     return z / (1.0 + math.exp(-z))
 
 
-def _bf_moe(x_bits, logits, L, k, act_mode):
+def _bf_moe(x_bits, logits, L, k, act_mode, routes=None):
+    """Exact-rational MoE layer.  `routes`, if given, is the routing itself:
+    routes[t] = [(expert id, weight), ...] for the k slots of token t; ids
+    outside [0, E) name no expert, so their slot is left out altogether (no h,
+    no part in the FP8 h scale, nothing added to the output)."""
     T, H = x_bits.shape
     E = L["w13_blocks"].shape[0]
     I = L["w2_blocks"].shape[2] * 32
@@ -139,14 +143,17 @@ def _bf_moe(x_bits, logits, L, k, act_mode):
         x = [flat[t * H:(t + 1) * H] for t in range(T)]
     elif act_mode == ACT_MXFP4:
         x = [_bf_mx_quant(row) for row in x]
-    routes = []
-    for t in range(T):
-        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
-        z = [math.exp(float(logits[t, e]) - float(logits[t, order[0]])) for e in order]
-        routes.append([(e, zi / sum(z)) for e, zi in zip(order, z)])
+    if routes is None:
+        routes = []
+        for t in range(T):
+            order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+            z = [math.exp(float(logits[t, e]) - float(logits[t, order[0]])) for e in order]
+            routes.append([(e, zi / sum(z)) for e, zi in zip(order, z)])
     hs = {}
     for t in range(T):
         for j, (e, _) in enumerate(routes[t]):
+            if not 0 <= e < E:
+                continue
             g = []
             for n in range(2 * I):
                 acc = sum(_bf_weight(L["w13_blocks"][e], L["w13_scales"][e], n, kk) * x[t][kk]
@@ -164,6 +171,8 @@ def _bf_moe(x_bits, logits, L, k, act_mode):
     out = np.zeros((T, H))
     for t in range(T):
         for j, (e, w) in enumerate(routes[t]):
+            if not 0 <= e < E:
+                continue
             for n in range(H):
                 acc = sum(_bf_weight(L["w2_blocks"][e], L["w2_scales"][e], n, kk) * hs[t, j][kk]
                           for kk in range(I))
@@ -235,6 +244,33 @@ def test_moe_forward_matches_exact_brute_force(act_mode):
     bf = _bf_moe(x, logits, L, 2, act_mode)
     scale = np.sqrt(np.mean(bf ** 2))
     assert np.max(np.abs(res["out"] - bf)) <= 1e-12 * scale * 64
+
+
+@pytest.mark.parametrize("act_mode", [ACT_BF16, ACT_FP8_E4M3, ACT_MXFP4])
+def test_moe_forward_skips_out_of_range_ids_brute_force(act_mode):
+    # ids -1, E and E+3 name no expert: the brute force leaves those slots out
+    # (no h, no part in the FP8 h scale, nothing added to the output).  An id of
+    # -1 read as the last expert (numpy's negative index) would add that
+    # expert's output and, in FP8 mode, its h to the scale.
+    L, logits, x = _tiny(T=4)
+    E = L["w13_blocks"].shape[0]
+    ids = np.array([[0, -1], [E, 2], [3, 1], [E + 3, -1]], dtype=np.int32)
+    w = np.array([[0.75, 0.25], [0.5, 0.5], [0.625, 0.375], [0.9, 0.1]])
+    res = oracle.moe_forward_routed(x, ids, w, **L, act_mode=act_mode)
+    routes = [[(int(e), float(wi)) for e, wi in zip(ids[t], w[t])] for t in range(4)]
+    bf = _bf_moe(x, logits, L, 2, act_mode, routes=routes)
+    scale = np.sqrt(np.mean(bf ** 2))
+    assert np.max(np.abs(res["out"] - bf)) <= 1e-12 * scale * 64
+    assert np.all(res["out"][3] == 0.0)             # both slots of token 3 skipped
+    # the skipped slots carry no h, and the FP8 h scale is the one of the valid
+    # pairs alone (against the same layer with the bad slots given expert E-1)
+    assert np.all(res["h"][ids < 0] == 0.0) and np.all(res["h"][ids >= E] == 0.0)
+    if act_mode == ACT_FP8_E4M3:
+        valid = (ids >= 0) & (ids < E)
+        amax = np.max(np.abs(res["h32"][valid]))
+        assert res["h_scale"] == oracle.fp8.f32_scale(amax)
+        alt = oracle.moe_forward_routed(x, np.where(valid, ids, E - 1), w, **L, act_mode=act_mode)
+        assert not np.array_equal(alt["out"], res["out"])
 
 
 def test_mxfp4_activation_mode_passes_representable_x_unchanged():

@@ -16,6 +16,27 @@ import oracle
 from oracle import quant
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mxfp4_quant_cases.txt")
+SMALL_BLOCK = os.path.join(os.path.dirname(__file__), "golden", "mxfp4_small_block_case.txt")
+
+
+def small_block_case():
+    """The hand-worked block of tests/golden/mxfp4_small_block_case.txt:
+    (values float64 [32], codes uint8 [32], scale byte)."""
+    vals, codes, sbyte = [], [], None
+    with open(SMALL_BLOCK) as f:
+        for line in f:
+            if line.startswith("# scale_byte"):
+                sbyte = int(line.split()[2])
+            line = line.split("#")[0].strip()
+            if line:
+                m, e, c = (int(t) for t in line.split())
+                vals.append(np.ldexp(float(m), e))
+                codes.append(c)
+    v = np.zeros(32)
+    c = np.zeros(32, dtype=np.uint8)
+    v[:len(vals)] = vals
+    c[:len(codes)] = codes
+    return v, c, sbyte
 
 
 def _cases():
@@ -45,9 +66,24 @@ def test_scale_rule_closed_form():
     assert np.all((r >= 4) & (r < 8))
     # exact powers of two and the clamps
     assert quant.block_exponent(np.array([1.0, 4.0, 6.0, 7.99, 8.0]))[:].tolist() == [-2, 0, 0, 0, 1]
-    assert quant.block_exponent(np.array([0.0]))[0] == -125
-    assert quant.block_exponent(np.array([2.0 ** -130]))[0] == -125
+    assert quant.block_exponent(np.array([0.0]))[0] == -116
+    assert quant.block_exponent(np.array([2.0 ** -130]))[0] == -116
+    assert quant.block_exponent(np.array([2.0 ** -114]))[0] == -116
+    assert quant.block_exponent(np.array([2.0 ** -115]))[0] == -116
     assert quant.block_exponent(np.array([3.3e38]))[0] == 125
+
+
+def test_block_below_the_clamp_hand_worked():
+    # amax = 2^-115 < 2^-114: the library's clamp (X >= -116) departs from the
+    # unclamped OCP exponent (-117) here; codes and scale byte worked by hand
+    v, want, sbyte = small_block_case()
+    assert sbyte == 11
+    b, s = oracle.quantize_mxfp4(v[None, :])
+    assert s.tolist() == [[sbyte]]
+    assert np.array_equal(oracle.unpack_nibbles(b)[0], want)
+    # every value is a bf16 value (the quantiser's input type)
+    assert np.array_equal(oracle.bf16_bits_to_f64(
+        (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)), v)
 
 
 def test_round_trip_of_representable_blocks():
@@ -61,7 +97,7 @@ def test_round_trip_of_representable_blocks():
     cb = codes.reshape(N, nb, 32)
     cb[np.arange(N)[:, None], np.arange(nb)[None, :], where] = big
     codes = cb.reshape(N, K)
-    scales = rng.integers(2, 253, (N, nb)).astype(np.uint8)
+    scales = rng.integers(11, 253, (N, nb)).astype(np.uint8)
     blocks = oracle.pack_nibbles(codes)
     w = oracle.dequant(blocks, scales)
     b2, s2 = oracle.quantize_mxfp4(w)
@@ -89,7 +125,7 @@ def test_zero_block_and_signs():
     w = np.zeros((2, 64))
     w[1, 32:] = -1e-40            # tiny negatives round to -0
     b, s = oracle.quantize_mxfp4(w)
-    assert s.tolist() == [[2, 2], [2, 2]]
+    assert s.tolist() == [[11, 11], [11, 11]]
     codes = oracle.unpack_nibbles(b)
     assert np.all(codes[0] == 0) and np.all(codes[1, :32] == 0) and np.all(codes[1, 32:] == 8)
 
