@@ -261,6 +261,38 @@ int mxfp4_moe_layer(const uint16_t* x, const float* logits, int64_t T, int64_t H
                     int32_t act_mode, uint16_t* out, void* workspace, size_t workspace_bytes,
                     const mxfp4_moe_opts* opts, void* stream);
 
+/* Bytes of the fixed device scratch mxfp4_moe_layer_noalloc works in. */
+#define MXFP4_NOALLOC_SCRATCH_BYTES (32ull << 20)
+
+/*
+ * mxfp4_moe_layer for callers that cannot allocate device memory, or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results (bitwise), limits and
+ * errors as mxfp4_moe_layer, without workspace / workspace_bytes: the
+ * intermediates live in a fixed scratch array of the library, of
+ * MXFP4_NOALLOC_SCRATCH_BYTES (32 MiB), one per device, held from the first
+ * call on a device until the process ends.  The call allocates nothing.
+ *   - Sizes whose workspace (mxfp4_moe_workspace_size) exceeds the scratch
+ *     are rejected with MXFP4_E_WORKSPACE before anything is enqueued: the
+ *     gpt-oss shape (hidden 2880, 128 experts, top-4) fits up to 363 tokens
+ *     with bf16 activations (decode);
+ *     the FP8 and MXFP4-activation modes need their restaged weight scales
+ *     in the workspace (about 100 MB at that shape) and do not fit it.
+ *   - All calls on one device share its scratch, which keeps the last
+ *     call's contents: calls that overlap on one device (other streams,
+ *     other threads) race and must be ordered by the caller.  Nothing in it
+ *     needs to start at zero (every call writes what it reads).
+ *   - opts->flags MXFP4_OPT_SCALE_STREAMS_READY is ignored (another call may
+ *     have overwritten the restaged scales): the scales are restaged on
+ *     every call.
+ */
+int mxfp4_moe_layer_noalloc(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t I,
+                            int32_t E, int32_t k, int32_t* topk_ids, float* topk_weights,
+                            const uint8_t* w13_blocks, const uint8_t* w13_scales,
+                            const uint16_t* w13_bias, const uint8_t* w2_blocks,
+                            const uint8_t* w2_scales, const uint16_t* w2_bias, int32_t act_mode,
+                            uint16_t* out, const mxfp4_moe_opts* opts, void* stream);
+
 /*
  * The MoE layer of mxfp4_moe_forward with NVFP4 expert weights (gpt-oss page,
  * "The MXFP4 -> NVFP4 Conversion": the same E2M1 element code, 16-element

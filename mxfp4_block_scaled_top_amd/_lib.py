@@ -85,6 +85,10 @@ def lib():
             _c_void_p, _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
             _i32, _c_void_p, _c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeOpts), _c_void_p]
+        L.mxfp4_moe_layer_noalloc.argtypes = [
+            _c_void_p, _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
+            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+            _i32, _c_void_p, ctypes.POINTER(MoeOpts), _c_void_p]
         L.nvfp4_moe_forward.argtypes = [
             _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
             _c_void_p, _c_void_p, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, ctypes.c_float,
@@ -100,7 +104,8 @@ def lib():
         L.mxfp4_event_destroy.argtypes = [_c_void_p]
         L.mxfp4_event_elapsed_ms.argtypes = [_c_void_p, _c_void_p, ctypes.POINTER(ctypes.c_float)]
         for name in ("mxfp4_route_topk", "mxfp4_moe_workspace_size", "mxfp4_moe_workspace_layout_query",
-                     "mxfp4_moe_forward", "mxfp4_moe_layer", "nvfp4_moe_forward", "mxfp4_linear",
+                     "mxfp4_moe_forward", "mxfp4_moe_layer", "mxfp4_moe_layer_noalloc", "nvfp4_moe_forward",
+                     "mxfp4_linear",
                      "mxfp4_quant_fp8_e4m3",
                      "mxfp4_quantize_weights", "mxfp4_stream_read", "mxfp4_event_create",
                      "mxfp4_event_destroy", "mxfp4_event_elapsed_ms"):
@@ -262,10 +267,10 @@ def nvfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_glo
     return out
 
 
-def mxfp4_moe_layer(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias,
-                    act_mode, out=None, topk_ids=None, topk_weights=None, workspace=None, events=None,
-                    stream=None, scale_streams_ready=False):
-    """Router + MoE layer in one call; returns (out, topk_ids, topk_weights)."""
+def _layer_args(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias, out, topk_ids,
+                topk_weights):
+    """Shape and dtype checks of the router + layer entry points; outputs
+    created when not given.  Returns (T, H, I, E, out, topk_ids, topk_weights)."""
     _need(x, "x", torch.bfloat16, 2)
     _need(logits, "logits", torch.float32, 2)
     T, H = x.shape
@@ -295,6 +300,16 @@ def mxfp4_moe_layer(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, 2)
+    return T, H, I, E, out, topk_ids, topk_weights
+
+
+def mxfp4_moe_layer(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias,
+                    act_mode, out=None, topk_ids=None, topk_weights=None, workspace=None, events=None,
+                    stream=None, scale_streams_ready=False):
+    """Router + MoE layer in one call; returns (out, topk_ids, topk_weights)."""
+    T, H, I, E, out, topk_ids, topk_weights = _layer_args(
+        x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias, out, topk_ids,
+        topk_weights)
     if workspace is None:
         workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, act_mode), 1),
                                 dtype=torch.uint8, device=x.device)
@@ -306,6 +321,24 @@ def mxfp4_moe_layer(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w
         _ptr(w2_blocks), _ptr(w2_scales), _ptr(w2_bias), act_mode, _ptr(out),
         _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts is not None else None,
         _stream(stream)))
+    return out, topk_ids, topk_weights
+
+
+def mxfp4_moe_layer_noalloc(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias,
+                            act_mode, out, topk_ids, topk_weights, events=None, stream=None):
+    """Router + MoE layer in the library's fixed device scratch (no workspace);
+    the caller passes every output.  Returns (out, topk_ids, topk_weights)."""
+    if out is None or topk_ids is None or topk_weights is None:
+        raise ValueError("mxfp4_moe_layer_noalloc takes caller-owned outputs")
+    T, H, I, E, out, topk_ids, topk_weights = _layer_args(
+        x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias, out, topk_ids,
+        topk_weights)
+    opts = _opts(events, False)
+    _check("mxfp4_moe_layer_noalloc", lib().mxfp4_moe_layer_noalloc(
+        _ptr(x), _ptr(logits), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
+        _ptr(w13_blocks), _ptr(w13_scales), _ptr(w13_bias),
+        _ptr(w2_blocks), _ptr(w2_scales), _ptr(w2_bias), act_mode, _ptr(out),
+        ctypes.byref(opts) if opts is not None else None, _stream(stream)))
     return out, topk_ids, topk_weights
 
 

@@ -134,6 +134,37 @@ int hip_fail(hipError_t e, const char* what) {
 
 }  // namespace
 
+// Fixed device scratch of mxfp4_moe_layer_noalloc: every device the library
+// runs on holds one copy for the life of the process, shared by all calls on
+// that device.  Host code never uses this name as an address: the device
+// address of each device's copy comes from hipGetSymbolAddress (see
+// scratch_ptr) and only that pointer is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[MXFP4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void*> g_scratch[64];
+
+// Device address of the current device's scratch, looked up on the first call
+// on that device (with that device current) and kept per device.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MXFP4_E_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MXFP4_E_DEVICE, "device index %d out of range", dev);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MXFP4_E_HIP, "hipGetSymbolAddress(scratch) gave no address");
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MXFP4_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int mxfp4_abi_version(void) { return MXFP4_ABI_VERSION; }
@@ -328,6 +359,40 @@ int mxfp4_moe_layer(const uint16_t* x, const float* logits, int64_t T, int64_t H
   return moe_run(x, logits, T, H, I, E, k, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bias,
                  w2_blocks, w2_scales, w2_bias, act_mode, out, workspace, workspace_bytes, opts,
                  stream, "moe_layer");
+}
+
+int mxfp4_moe_layer_noalloc(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_t I,
+                            int32_t E, int32_t k, int32_t* topk_ids, float* topk_weights,
+                            const uint8_t* w13_blocks, const uint8_t* w13_scales,
+                            const uint16_t* w13_bias, const uint8_t* w2_blocks,
+                            const uint8_t* w2_scales, const uint16_t* w2_bias, int32_t act_mode,
+                            uint16_t* out, const mxfp4_moe_opts* opts, void* stream) {
+  if (T > 0 && !logits) return fail(MXFP4_E_NULL, "moe_layer_noalloc: logits is null");
+  int rc = moe_shape_check(T, H, I, E, k, act_mode);
+  if (rc) return rc;
+  mxfp4_moe_workspace_layout L;
+  plan(T, H, I, E, k, act_mode, &L);
+  if (L.total_bytes > MXFP4_NOALLOC_SCRATCH_BYTES)
+    return fail(MXFP4_E_WORKSPACE,
+                "moe_layer_noalloc: these sizes need %llu bytes of scratch; the fixed scratch holds %llu "
+                "(use mxfp4_moe_layer with a workspace)",
+                (unsigned long long)L.total_bytes, (unsigned long long)MXFP4_NOALLOC_SCRATCH_BYTES);
+  if (T == 0) return ok();
+  rc = check_device();
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = scratch_ptr(&ws);
+  if (rc) return rc;
+  // restaged scale streams in the shared scratch may belong to another call:
+  // always restage
+  mxfp4_moe_opts o;
+  if (opts) {
+    o = *opts;
+    o.flags &= ~(uint32_t)MXFP4_OPT_SCALE_STREAMS_READY;
+  }
+  return moe_run(x, logits, T, H, I, E, k, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bias,
+                 w2_blocks, w2_scales, w2_bias, act_mode, out, ws, MXFP4_NOALLOC_SCRATCH_BYTES,
+                 opts ? &o : nullptr, stream, "moe_layer_noalloc");
 }
 
 int nvfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,

@@ -192,3 +192,17 @@ def test_stream_read_validation(L):
     assert L.mxfp4_stream_read(None, 1 << 20, 1, _fake(), ctypes.byref(n), None) == E_NULL
     assert L.mxfp4_stream_read(ctypes.c_void_p(0x1010), 1 << 20, 0, _fake(), ctypes.byref(n), None) == E_ALIGN
     assert L.mxfp4_stream_read(_fake(), 1 << 41, 0, _fake(), ctypes.byref(n), None) == E_SHAPE
+
+
+def test_moe_layer_noalloc_rejects_bad_arguments_without_touching_memory(L):
+    f = L.mxfp4_moe_layer_noalloc
+    args = lambda T, H, I, E, k, act, logits=_fake(2): (  # noqa: E731
+        _fake(), logits, T, H, I, E, k, _fake(3), _fake(4), _fake(5), _fake(6), None, _fake(7), _fake(8), None,
+        act, _fake(9), None, None)
+    # 400 tokens x top-4 at 2880 x 2880 need more than the 32 MiB scratch
+    assert f(*args(400, 2880, 2880, 4, 4, 0)) == E_WORKSPACE
+    assert f(*args(2048, 2880, 2880, 128, 4, 1)) == E_WORKSPACE
+    assert f(*args(32, 2880, 2880, 128, 4, 7)) == E_MODE
+    assert f(*args(32, 2880, 2880, 128, 4, 0, logits=None)) == E_NULL
+    assert f(*args(32, 33, 2880, 128, 4, 0)) == E_SHAPE
+    assert f(*args(0, 2880, 2880, 128, 4, 0)) == 0          # T == 0: no-op
