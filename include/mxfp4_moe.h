@@ -74,7 +74,11 @@ enum {
 /* Stage boundaries at which mxfp4_moe_forward can record caller events. */
 enum {
   MXFP4_STAGE_BEGIN = 0,      /* before the first kernel */
-  MXFP4_STAGE_PERMUTE = 1,    /* after the token-by-expert permutation */
+  MXFP4_STAGE_PERMUTE = 1,    /* after the token-by-expert permutation (in
+                                 mxfp4_moe_layer with bf16 activations and at
+                                 most 8 tokens the gate_up kernel routes the
+                                 batch itself: this stage is then empty and
+                                 GEMM1 includes the routing) */
   MXFP4_STAGE_QUANT_X = 2,    /* after quantisation of x and the restaging of the
                                  w13 scales (FP8, MXFP4 activations) */
   MXFP4_STAGE_GEMM1 = 3,      /* after gate_up GEMM + SwiGLU */

@@ -291,9 +291,15 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   } while (0)
 
   MX_STEP(mark(MXFP4_STAGE_BEGIN), "event record");
+  // decode batches with bf16 activations: the gate_up kernel routes the batch
+  // itself (no route + permutation launch; the permute stage is then empty)
+  const bool route_in_gateup = logits && act_mode == MXFP4_ACT_BF16 && !nv_globals &&
+                               mx::gateup_routes_batch(sh, false);
   // one launch for route + permute while the block routes the whole batch in
   // one round (a half wave per token)
-  if (logits && T <= mx::kFusedRouteMaxTokens && npairs <= mx::kFusedPermuteMaxPairs) {
+  if (route_in_gateup) {
+    // (routed in the gate_up launch below)
+  } else if (logits && T <= mx::kFusedRouteMaxTokens && npairs <= mx::kFusedPermuteMaxPairs) {
     MX_STEP(mx::launch_route_permute(logits, (int)T, E, k, topk_ids, topk_weights, bm, (int)bound, ws, s),
             "route+permute launch");
   } else {
@@ -314,6 +320,9 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   MX_STEP(mark(MXFP4_STAGE_QUANT_X), "event record");
   if (fp8) MX_STEP(mx::launch_moe_gateup_fp8(sh, w, ws, bound, s), "gate_up launch");
   else if (a4) MX_STEP(mx::launch_moe_gateup_fp4(sh, w, ws, s), "gate_up launch");
+  else if (route_in_gateup)
+    MX_STEP(mx::launch_moe_gateup_bf16_routed(x, logits, topk_ids, topk_weights, sh, w, ws, bound, s),
+            "gate_up launch");
   else MX_STEP(mx::launch_moe_gateup_bf16(x, sh, w, ws, bound, s), "gate_up launch");
   MX_STEP(mark(MXFP4_STAGE_GEMM1), "event record");
   if (fp8) {

@@ -15,7 +15,7 @@
 //     routed tokens) the K range of a row tile is split across KSPLIT waves
 //     of the block and the partial sums are added in LDS in a fixed order;
 //   * the E2M1 nibbles are expanded in registers with the scaled FP4->bf16
-//     convert (the E8M0 block scale folded in; exact for scale bytes 2..252)
+//     convert (the E8M0 block scale folded in; exact for scale bytes 11..252)
 //     and fed to v_mfma_f32_16x16x32_bf16 with the routed tokens as the 16
 //     columns; a K-group is four MFMAs, each taking 8 elements of the lane's
 //     own block, so the K order inside an MFMA is permuted identically for
@@ -28,6 +28,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "route_small.hpp"
 
 namespace mx {
 
@@ -54,7 +55,25 @@ struct GemvArgs {
   uint16_t* out_lo;         // gate_up: h lo
   float* y;                 // down
   float gscale;             // NVFP4: the weight tensor's global scale (MXFP4: 1)
+  // gate_up that routes the batch itself (decode batches): router logits
+  // [T, E] and the outputs block 0 writes (top-k ids and weights, and the
+  // permutation for the down and combine kernels)
+  const float* logits;
+  int T, E, bound;
+  int* ids_out;
+  float* w_out;
+  int* g_status;
+  int* g_offsets;
+  int* g_sorted;
+  int* g_inv;
+  int* g_tiles;
 };
+
+// LDS of a routing gate_up block beyond the GEMV's: ids, expert offsets,
+// sorted pairs (128 each), status words, then the row-tile list.
+constexpr int kRouteLdsInts = 3 * kSmallMaxPairs + kStWords;
+static_assert(kSmallMaxExperts <= kSmallMaxPairs, "expert offsets share the pair-sized slot");
+inline size_t route_lds_bytes(int bound) { return (size_t)(kRouteLdsInts + kTileInts * bound) * 4; }
 
 // One K-group's operands for one lane.
 template <int MODE>
@@ -365,26 +384,81 @@ __device__ __forceinline__ float rot4_f32(float v) {
 
 // NV: NVFP4 weights (16-element blocks with E4M3 scales: two scales per
 // 32-element chunk; the tensor's global scale is applied to the sums).
-template <int MODE, int HG, bool NV>
+// RT (gate_up of decode batches only): every block first routes the whole
+// batch itself (T <= 8 tokens, T * k <= 128 pairs, E <= 128) with the router
+// and permutation of the stand-alone route + permutation kernel, into its
+// LDS; block 0 also writes the router outputs and the permutation to global
+// memory for the down and combine kernels.  This replaces a single-block
+// launch (about 8 us plus a launch gap) by a prologue of about 5 us.
+template <int MODE, int HG, bool NV, bool RT = false>
 __global__ __launch_bounds__(128) void gemv_persist_kernel(
     GemvArgs a, PersistPlan P, const int* __restrict__ tiles, const int* __restrict__ sorted_pairs,
     const int* __restrict__ status) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   constexpr bool kPair = MODE == kGateUp;
+  static_assert(!RT || (MODE == kGateUp && !NV), "only the MXFP4 gate_up routes");
   const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
+  using RL = RunLayout<NV>;
+
+  int64_t mtiles;
+  if constexpr (RT) {
+    int* rl = reinterpret_cast<int*>(smem + RL::kLds);
+    int* ids_l = rl;
+    int* eoff_l = rl + kSmallMaxPairs;
+    int* sorted_l = rl + 2 * kSmallMaxPairs;
+    int* st_l = rl + 3 * kSmallMaxPairs;
+    int* tiles_l = rl + kRouteLdsInts;
+    // 16 lanes per token, 8 tokens per round; every round's logits are
+    // loaded first, so the rounds wait for memory once
+    constexpr int kRounds = kGateUpRouteMaxTokens / 8;
+    const int l16 = lane & 15, tw = lane >> 4;
+    uint32_t keys[kRounds][8];
+#pragma unroll
+    for (int rd = 0; rd < kRounds; ++rd) {
+      const int t = 8 * rd + 4 * kh + tw;
+      const bool live = t < a.T;
+      route16_keys(a.logits + (size_t)(live ? t : 0) * a.E, live, a.E, l16, keys[rd]);
+    }
+#pragma unroll
+    for (int rd = 0; rd < kRounds; ++rd) {
+      if (8 * rd >= a.T) break;
+      const int t = 8 * rd + 4 * kh + tw;
+      int id;
+      float w;
+      route16_pick(keys[rd], a.topk, l16, id, w);
+      if (t < a.T && l16 < a.topk) {
+        ids_l[t * a.topk + l16] = id;
+        if (blockIdx.x == 0) {
+          a.ids_out[t * a.topk + l16] = id;
+          a.w_out[t * a.topk + l16] = w;
+        }
+      }
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const PermDst dl{nullptr, sorted_l, nullptr, tiles_l, st_l};
+      const PermDst dg = blockIdx.x == 0 ? PermDst{a.g_offsets, a.g_sorted, a.g_inv, a.g_tiles, a.g_status}
+                                          : PermDst{nullptr, nullptr, nullptr, nullptr, nullptr};
+      permute_wave(ids_l, a.T * a.topk, a.E, kCols, a.bound, eoff_l, dl, dg);
+    }
+    __syncthreads();
+    tiles = tiles_l;
+    sorted_pairs = sorted_l;
+    mtiles = st_l[kStNumTiles];
+  } else {
+    mtiles = MODE == kDense ? (a.M + kCols - 1) / kCols : status[kStNumTiles];
+  }
 
   // this block's units
-  const int64_t mtiles = MODE == kDense ? (a.M + kCols - 1) / kCols : status[kStNumTiles];
   const int64_t U = mtiles * P.row_tiles;
   const int64_t u_begin = U * blockIdx.x / gridDim.x;
   const int64_t u_end = U * (blockIdx.x + 1) / gridDim.x;
   if (u_begin >= u_end) return;   // the same for both waves: no barrier is skipped by one
 
   const int64_t rb = (int64_t)a.nb * kBlockBytes;
-  using RL = RunLayout<NV>;
   constexpr int kRunBytes = RL::kRunBytes;
   v4f* red = reinterpret_cast<v4f*>(smem + RL::kBufBytes);
   const int nsr = NV ? 2 * a.nb : a.nb;               // scale bytes per weight row
@@ -642,43 +716,46 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
 }
 
 // Blocks of the persistent kernel: as many as are resident at once on the
-// device (compute units x resident blocks per unit, queried per kernel).
-template <int MODE, int HG, bool NV>
+// device (compute units x resident blocks per unit, queried per kernel and
+// LDS size).
+template <int MODE, int HG, bool NV, bool RT = false>
 static hipError_t launch_persist_hg(const GemvArgs& a, const PersistPlan& P, const int* tiles,
-                                    const int* sorted_pairs, const int* status, hipStream_t s) {
-  constexpr int kPersistLds = RunLayout<NV>::kLds;
-  // (device + 1) << 32 | blocks, cached per kernel; threads may race to fill
-  // it, but every writer stores the same value
+                                    const int* sorted_pairs, const int* status, hipStream_t s,
+                                    size_t extra_lds = 0) {
+  const size_t lds = RunLayout<NV>::kLds + extra_lds;
+  // (device + 1) << 48 | lds << 24 | blocks, cached per kernel; threads may
+  // race to fill it, but every writer stores the same value for its key
   static std::atomic<uint64_t> cache{0};
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  const uint64_t key = (uint64_t)(dev + 1) << 32;
+  const uint64_t key = ((uint64_t)(dev + 1) << 48) | ((uint64_t)lds << 24);
   uint64_t c = cache.load(std::memory_order_relaxed);
-  if ((c >> 32) != (key >> 32)) {
+  if ((c & ~0xffffffull) != key) {
     int cus = 0, per_cu = 0;
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_persist_kernel<MODE, HG, NV>, 128,
-                                                       kPersistLds);
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_persist_kernel<MODE, HG, NV, RT>, 128,
+                                                       lds);
     if (err != hipSuccess) return err;
     c = key | (uint64_t)(cus * (per_cu > 0 ? per_cu : 1));
     cache.store(c, std::memory_order_relaxed);
   }
-  const unsigned blocks = (unsigned)(c & 0xffffffffu);
-  gemv_persist_kernel<MODE, HG, NV><<<blocks, 128, kPersistLds, s>>>(a, P, tiles, sorted_pairs, status);
+  const unsigned blocks = (unsigned)(c & 0xffffffu);
+  gemv_persist_kernel<MODE, HG, NV, RT><<<blocks, 128, lds, s>>>(a, P, tiles, sorted_pairs, status);
   return hipGetLastError();
 }
 
-template <int MODE, bool NV = false>
+template <int MODE, bool NV = false, bool RT = false>
 static hipError_t launch_persist(const GemvArgs& a, const PersistPlan& P, const int* tiles,
-                                 const int* sorted_pairs, const int* status, hipStream_t s) {
+                                 const int* sorted_pairs, const int* status, hipStream_t s,
+                                 size_t extra_lds = 0) {
   switch (persist_hg(a.nb)) {
-    case 1: return launch_persist_hg<MODE, 1, NV>(a, P, tiles, sorted_pairs, status, s);
-    case 2: return launch_persist_hg<MODE, 2, NV>(a, P, tiles, sorted_pairs, status, s);
-    case 3: return launch_persist_hg<MODE, 3, NV>(a, P, tiles, sorted_pairs, status, s);
-    case 6: return launch_persist_hg<MODE, 6, NV>(a, P, tiles, sorted_pairs, status, s);
-    case 12: return launch_persist_hg<MODE, 12, NV>(a, P, tiles, sorted_pairs, status, s);
+    case 1: return launch_persist_hg<MODE, 1, NV, RT>(a, P, tiles, sorted_pairs, status, s, extra_lds);
+    case 2: return launch_persist_hg<MODE, 2, NV, RT>(a, P, tiles, sorted_pairs, status, s, extra_lds);
+    case 3: return launch_persist_hg<MODE, 3, NV, RT>(a, P, tiles, sorted_pairs, status, s, extra_lds);
+    case 6: return launch_persist_hg<MODE, 6, NV, RT>(a, P, tiles, sorted_pairs, status, s, extra_lds);
+    case 12: return launch_persist_hg<MODE, 12, NV, RT>(a, P, tiles, sorted_pairs, status, s, extra_lds);
     default: return hipErrorInvalidValue;
   }
 }
@@ -738,6 +815,47 @@ hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const M
     return launch_persist<kGateUp>(a, persist_plan(kGateUp, sh.I), ws.tiles, ws.sorted_pairs,
                                    ws.status, s);
   return launch_gemv<kGateUp>(a, sh.I, ntile_bound, pick_ksplit(busy), s);
+}
+
+bool gateup_routes_batch(const MoeShape& sh, bool nvfp4) {
+  const int64_t pairs = (int64_t)sh.T * sh.k;
+  const size_t xbytes = (size_t)sh.T * sh.H * 2;
+  return !nvfp4 && sh.T >= 1 && sh.T <= kGateUpRouteMaxTokens && pairs <= kSmallMaxPairs &&
+         sh.E <= kSmallMaxExperts && sh.k <= kSmallMaxK && xbytes < (1u << 31) &&
+         persist_fits(sh.H / kBlockElems, (uint32_t)xbytes);
+}
+
+hipError_t launch_moe_gateup_bf16_routed(const uint16_t* x, const float* logits, int* ids, float* wts,
+                                         const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
+                                         int64_t ntile_bound, hipStream_t s) {
+  if (!gateup_routes_batch(sh, w.nvfp4)) return hipErrorInvalidValue;
+  GemvArgs a{};
+  a.wb = w.w13_blocks;
+  a.ws = w.w13_scales;
+  a.bias = w.w13_bias;
+  a.rows_per_expert = 2 * (int64_t)sh.I;
+  a.nout = sh.I;
+  a.nb = sh.H / kBlockElems;
+  a.act = x;
+  a.act_bytes = (uint32_t)((size_t)sh.T * sh.H * 2);
+  a.topk = sh.k;
+  uint16_t* h = static_cast<uint16_t*>(ws.h);
+  a.out_hi = h;
+  a.out_lo = h + (size_t)sh.T * sh.k * sh.I;
+  a.gscale = 1.0f;
+  a.logits = logits;
+  a.T = sh.T;
+  a.E = sh.E;
+  a.bound = (int)ntile_bound;
+  a.ids_out = ids;
+  a.w_out = wts;
+  a.g_status = ws.status;
+  a.g_offsets = ws.offsets;
+  a.g_sorted = ws.sorted_pairs;
+  a.g_inv = ws.inv;
+  a.g_tiles = ws.tiles;
+  return launch_persist<kGateUp, false, true>(a, persist_plan(kGateUp, sh.I), nullptr, nullptr, nullptr, s,
+                                              route_lds_bytes((int)ntile_bound));
 }
 
 hipError_t launch_moe_down_bf16(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,

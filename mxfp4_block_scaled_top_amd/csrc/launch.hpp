@@ -102,6 +102,18 @@ hipError_t launch_moe_gateup_bf16(const uint16_t* x, const MoeShape& sh, const M
                                   const WsPtrs& ws, int64_t ntile_bound, hipStream_t s);
 hipError_t launch_moe_down_bf16(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
                                 int64_t ntile_bound, hipStream_t s);
+// Decode batches: the gate_up kernel routes the batch itself (top-k of
+// `logits`, writing ids / wts and the permutation into the workspace), in
+// place of the route + permutation launch.  Applies when
+// gateup_routes_batch() holds.
+// One routing round of 8 tokens (16 lanes each) per block; measured, each
+// further round costs the gate_up kernel about 3 us, more than the route +
+// permutation launch it replaces (about 8 us plus a launch gap) at 32 tokens.
+constexpr int kGateUpRouteMaxTokens = 8;
+bool gateup_routes_batch(const MoeShape& sh, bool nvfp4);
+hipError_t launch_moe_gateup_bf16_routed(const uint16_t* x, const float* logits, int* ids, float* wts,
+                                         const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
+                                         int64_t ntile_bound, hipStream_t s);
 hipError_t launch_linear_bf16(const uint16_t* x, int M, int N, int K, const uint8_t* wb,
                               const uint8_t* ws, const uint16_t* bias, uint16_t* out,
                               hipStream_t s);

@@ -8,6 +8,7 @@
 // the fp32 softmax of the k chosen logits.
 #include "common.hpp"
 #include "launch.hpp"
+#include "route_small.hpp"
 
 namespace mx {
 
@@ -275,57 +276,7 @@ __global__ __launch_bounds__(1024) void route_permute_kernel(
 // lower index on ties, -0 equal to +0) and the same softmax arithmetic
 // (exp of the difference to the largest chosen logit, the k terms summed in
 // the order of a 32-lane butterfly, then one division).
-constexpr int kSmallMaxPairs = 128;
-constexpr int kSmallMaxExperts = 128;
-constexpr int kSmallMaxK = 16;
 constexpr int kSmallThreads = 512;
-
-// Order-preserving map of a non-NaN float to uint32 (larger float, larger
-// key; -0 and +0 map to the same key); 0 is below every mapped value.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b << 1) == 0) b = 0;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, true);
-}
-// maximum over the 16 lanes of a DPP row, in every lane of the row
-__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
-  v = max(v, dpp_u32<0x121>(v));   // row_ror:1
-  v = max(v, dpp_u32<0x122>(v));   // row_ror:2
-  v = max(v, dpp_u32<0x124>(v));   // row_ror:4
-  v = max(v, dpp_u32<0x128>(v));   // row_ror:8
-  return v;
-}
-__device__ __forceinline__ uint32_t row16_min(uint32_t v) {
-  v = min(v, dpp_u32<0x121>(v));
-  v = min(v, dpp_u32<0x122>(v));
-  v = min(v, dpp_u32<0x124>(v));
-  v = min(v, dpp_u32<0x128>(v));
-  return v;
-}
-// lanes holding expert e among the lanes of mask `valid`, given the wave's
-// ballots of each id bit
-__device__ __forceinline__ uint64_t lanes_with(int e, const uint64_t* bits, uint64_t valid) {
-  uint64_t m = valid;
-#pragma unroll
-  for (int b = 0; b < 7; ++b) m &= ((e >> b) & 1) ? bits[b] : ~bits[b];
-  return m;
-}
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
 
 __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int BM, int bound,
@@ -340,98 +291,20 @@ __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
   for (int t0 = 0; t0 < T; t0 += 4 * (kSmallThreads / 64)) {
     const int t = t0 + 4 * wave + tw;
     const bool live = t < T;   // the whole 16-lane row agrees
-    const float* row = logits + (size_t)(live ? t : 0) * E;
-    // keys of the lane's logits l16 + 16 i (0: taken or past E)
-    uint32_t key[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = l16 + 16 * i;
-      key[i] = live && idx < E ? order_key(row[idx]) : 0u;
-    }
-    int chosen[kSmallMaxK] = {};
-    float val[kSmallMaxK] = {};
-    for (int j = 0; j < k; ++j) {
-      uint32_t m = key[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) m = max(m, key[i]);
-      m = row16_max(m);
-      // lowest index holding the maximum: the lane's first i with that key,
-      // then the row minimum
-      uint32_t cand = 0xffffffffu;
-#pragma unroll
-      for (int i = 7; i >= 0; --i) cand = key[i] == m ? (uint32_t)(l16 + 16 * i) : cand;
-      const uint32_t win = row16_min(cand);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) key[i] = (uint32_t)(l16 + 16 * i) == win ? 0u : key[i];
-      chosen[j] = (int)win;
-      val[j] = key_value(m);
-    }
-    // softmax over the k chosen logits, the sum in 32-lane butterfly order
-    float z[kSmallMaxK];
-#pragma unroll
-    for (int j = 0; j < kSmallMaxK; ++j) z[j] = j < k ? expf(val[j] - val[0]) : 0.0f;
-    float b8[8], c4[4];
-#pragma unroll
-    for (int l = 0; l < 8; ++l) b8[l] = z[l] + z[l + 8];
-#pragma unroll
-    for (int l = 0; l < 4; ++l) c4[l] = b8[l] + b8[l + 4];
-    const float ssum = (c4[0] + c4[2]) + (c4[1] + c4[3]);
+    int id;
+    float w;
+    route16_token(logits + (size_t)(live ? t : 0) * E, live, E, k, l16, id, w);
     if (live && l16 < k) {
-      int id = 0;
-      float zz = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kSmallMaxK; ++j)
-        if (j == l16) { id = chosen[j]; zz = z[j]; }
       ids[t * k + l16] = id;
       ids_out[(size_t)t * k + l16] = id;
-      w_out[(size_t)t * k + l16] = zz / ssum;
+      w_out[(size_t)t * k + l16] = w;
     }
   }
   __syncthreads();
   if (wave != 0) return;
-  // ---- permutation, one wave: pairs lane and lane + 64, experts 2 lane and 2 lane + 1
-  const int p0 = lane, p1 = lane + 64;
-  const bool v0 = p0 < npairs, v1 = p1 < npairs;
-  const int e0 = v0 ? ids[p0] : 0, e1 = v1 ? ids[p1] : 0;
-  uint64_t B0[7], B1[7];
-#pragma unroll
-  for (int b = 0; b < 7; ++b) {
-    B0[b] = __ballot(v0 && ((e0 >> b) & 1));
-    B1[b] = __ballot(v1 && ((e1 >> b) & 1));
-  }
-  const uint64_t V0 = __ballot(v0), V1 = __ballot(v1);
-  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  const int r0 = __popcll(lanes_with(e0, B0, V0) & below);
-  const int r1 = __popcll(lanes_with(e1, B0, V0)) + __popcll(lanes_with(e1, B1, V1) & below);
-  const int ea = 2 * lane, eb = 2 * lane + 1;
-  const int ca = ea < E ? __popcll(lanes_with(ea, B0, V0)) + __popcll(lanes_with(ea, B1, V1)) : 0;
-  const int cb = eb < E ? __popcll(lanes_with(eb, B0, V0)) + __popcll(lanes_with(eb, B1, V1)) : 0;
-  const int pincl = wave_incl_scan(ca + cb);
-  const int offa = pincl - ca - cb, offb = offa + ca;
-  if (ea < E) { offsets[ea] = offa; eoff[ea] = offa; }
-  if (eb < E) { offsets[eb] = offb; eoff[eb] = offb; }
-  if (lane == 63) offsets[E] = pincl;
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes done
-  __builtin_amdgcn_wave_barrier();
-  if (v0) { const int pos = eoff[e0] + r0; sorted_pairs[pos] = p0; inv[p0] = pos; }
-  if (v1) { const int pos = eoff[e1] + r1; sorted_pairs[pos] = p1; inv[p1] = pos; }
-  // row tiles: expert e contributes ceil(n_e / BM) entries, in expert order
-  const int na = (ca + BM - 1) / BM, nb2 = (cb + BM - 1) / BM;
-  const int tincl = wave_incl_scan(na + nb2);
-  const int fa = tincl - na - nb2, fb = fa + na;
-  const int ntiles = __shfl(tincl, 63, 64);
-  const int wa = tile_word(fa, na, bound), wb = tile_word(fb, nb2, bound);
-  for (int i = 0; i < na; ++i) {
-    const int b = offa + i * BM;
-    *reinterpret_cast<int4*>(tiles + kTileInts * (fa + i)) = make_int4(ea, b, min(b + BM, offa + ca), wa);
-  }
-  for (int i = 0; i < nb2; ++i) {
-    const int b = offb + i * BM;
-    *reinterpret_cast<int4*>(tiles + kTileInts * (fb + i)) = make_int4(eb, b, min(b + BM, offb + cb), wb);
-  }
-  for (int t = ntiles + lane; t < bound; t += 64)
-    *reinterpret_cast<int4*>(tiles + kTileInts * t) = make_int4(-1, 0, 0, 0);
-  if (lane < kStWords) status[lane] = lane == kStNumTiles ? ntiles : 0;
+  const PermDst d0{offsets, sorted_pairs, inv, tiles, status};
+  const PermDst none{nullptr, nullptr, nullptr, nullptr, nullptr};
+  permute_wave(ids, npairs, E, BM, bound, eoff, d0, none);
 }
 
 // Multi-block path, phase 1: per-chunk ranks and per-chunk expert counts

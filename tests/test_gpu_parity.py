@@ -816,7 +816,15 @@ def test_quantized_weights_feed_the_linear(mx):
                                            (64, 96, 128, 25, 5, synth.ACT_BF16),
                                            (16, 64, 64, 8, 16, synth.ACT_BF16),
                                            (3, 64, 64, 2, 3, synth.ACT_BF16),
-                                           (127, 64, 96, 42, 3, synth.ACT_BF16)])
+                                           (127, 64, 96, 42, 3, synth.ACT_BF16),
+                                           # decode batches: gate_up routes the batch itself
+                                           # (T <= 8, T * k <= 128, E <= 128, H >= 160)
+                                           (128, 288, 320, 8, 4, synth.ACT_BF16),
+                                           (128, 288, 320, 9, 4, synth.ACT_BF16),
+                                           (100, 256, 128, 5, 5, synth.ACT_BF16),
+                                           (64, 256, 128, 7, 16, synth.ACT_BF16),
+                                           (128, 320, 256, 1, 1, synth.ACT_BF16),
+                                           (9, 2880, 2880, 3, 4, synth.ACT_BF16)])
 def test_moe_layer_equals_route_then_forward(mx, E, H, I, T, k, act):
     L = synth.layer(seed=E + H, E=E, H=H, I=I)
     logits, x = synth.moe_inputs(T + 3, T, E=E, H=H)
@@ -834,10 +842,12 @@ def test_moe_layer_equals_route_then_forward(mx, E, H, I, T, k, act):
     assert np.array_equal(ids_b.cpu().numpy(), rid)
 
 
-@pytest.mark.parametrize("T,E,k", [(32, 128, 4), (7, 128, 16), (25, 100, 5)])
-def test_moe_layer_routing_ties_and_signed_zero(mx, T, E, k):
+@pytest.mark.parametrize("H", [64, 256])
+@pytest.mark.parametrize("T,E,k", [(32, 128, 4), (7, 128, 16), (25, 100, 5), (8, 128, 4), (3, 100, 5)])
+def test_moe_layer_routing_ties_and_signed_zero(mx, T, E, k, H):
     """Tie-heavy logits (small integers, all-zero rows, -0 next to +0) routed by
-    the layer's fused route + permutation launch equal the stand-alone router
+    the layer (H = 64: the fused route + permutation launch; H = 256: the
+    gate_up kernel routing the batch itself) equal the stand-alone router
     bitwise, and the oracle's choices."""
     rng = np.random.default_rng(T + E)
     logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
@@ -845,7 +855,7 @@ def test_moe_layer_routing_ties_and_signed_zero(mx, T, E, k):
     logits[1, ::3] = -0.0
     logits[2, :] = -np.inf
     logits[2, 5] = 1.0
-    H = I = 64
+    I = H
     L = synth.layer(seed=9, E=E, H=H, I=I)
     Ld = _layer_dev(L)
     x = synth.f32_to_bf16_bits(rng.normal(size=(T, H)).astype(np.float32))
