@@ -444,6 +444,9 @@ def main():
                     help="only measure the streaming-read ceiling (4 GiB read once per launch, register "
                          "loads and direct-to-LDS copies) and print it")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling measurement")
+    ap.add_argument("--dense-only", action="store_true",
+                    help="only measure the dense projections (qkv_proj, o_proj, lm_head at 1 and 4 tokens) "
+                         "and print them")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (requested %d)" % args.gpus,
@@ -476,6 +479,9 @@ def main():
         print(json.dumps({"hbm_ceiling": ceiling}), flush=True)
         return
     cg = ceiling["ceiling_GBps"] if ceiling else None
+    if args.dense_only:
+        print(json.dumps({"dense": measure_dense(run, synth, args.steps, args.warmup)}), flush=True)
+        return
     L = synth.layer()
     Ld = {k: run.dev(v) for k, v in L.items()}
     del L

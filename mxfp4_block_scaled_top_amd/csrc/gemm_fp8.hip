@@ -529,6 +529,14 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
 
   int cstep = 0, cslot = 0, ck = 0;
   int e = 0, rb = 0, re = 0, nt = 0;
+  // 16-row groups of this wave's 64 sorted rows that hold rows of the tile:
+  // in the FP8 kernels the MFMAs (and activation expansions) of groups
+  // wholly past the tile's end are skipped (their outputs are never stored).
+  // A tile of an expert with ~64 rows fills only wm = 0's half of the 128
+  // rows (same-box A/B: 2048-token FP8 call 781 -> 720 us).  The FP4 x FP4
+  // kernels, bound by their copies, gained nothing from it and keep every
+  // MFMA.
+  int ntg = 4;
   // bias of the lane's four output rows of each epilogue group, as bf16
   // pairs (gate_up: gate and up rows of groups 0 and 1; down: groups 0..3)
   uint2 bq[4];
@@ -537,6 +545,10 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
     unit_tile(a, tiles, u, tile, nt);
     const int3 te = tile_entry(tiles + kTileInts * tile);
     e = te.x; rb = te.y; re = te.z;
+    {
+      const int v = re - rb - 64 * wm;
+      ntg = v <= 0 ? 0 : v >= 64 ? 4 : (v + 15) >> 4;
+    }
     // through the scalar cache, 16 rows at a time (a group past nout is
     // never stored and not loaded)
     const uint16_t* bias_e = a.bias + (size_t)e * a.R;
@@ -664,23 +676,49 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
         // lane group g holds K [32g, 32g+32) of the step (its own MX block);
         // MFMA q takes elements 8q..8q+7 of it (8(q^2).. for odd g), in the
         // same order for both operands; MFMAs 2-3 use the chunks read last
+        if (ntg == 4) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
-          const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
-          v8bf B[4];
+          for (int q = 0; q < 4; ++q) {
+            if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
+            const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
+            v8bf B[4];
 #pragma unroll
-          for (int tg = 0; tg < 4; ++tg) {
-            const v4u_t c = q < 2 ? xa[tg] : xb[tg];
-            B[tg] = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
+            for (int tg = 0; tg < 4; ++tg) {
+              const v4u_t c = q < 2 ? xa[tg] : xb[tg];
+              B[tg] = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
+            }
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
+              const v8bf A = fp4x8_to_bf16(wq[rg][q], f);
+#pragma unroll
+              for (int tg = 0; tg < 4; ++tg)
+                acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[tg], acc[rg][tg], 0, 0, 0);
+            }
           }
+        } else {
+          // part of the wave's rows lie past the tile: only the groups that
+          // hold rows of it (none: no expansion either)
 #pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
-            const v8bf A = fp4x8_to_bf16(wq[rg][q], f);
+          for (int q = 0; q < 4; ++q) {
+            if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
+            if (ntg == 0) continue;
+            const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
+            v8bf A[4];
 #pragma unroll
-            for (int tg = 0; tg < 4; ++tg)
-              acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[tg], acc[rg][tg], 0, 0, 0);
+            for (int rg = 0; rg < 4; ++rg) {
+              const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
+              A[rg] = fp4x8_to_bf16(wq[rg][q], f);
+            }
+#pragma unroll
+            for (int tg = 0; tg < 3; ++tg) {
+              if (tg >= ntg) break;
+              const v4u_t c = q < 2 ? xa[tg] : xb[tg];
+              const v8bf B = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
+#pragma unroll
+              for (int rg = 0; rg < 4; ++rg)
+                acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rg], B, acc[rg][tg], 0, 0, 0);
+            }
           }
         }
       } else {
@@ -689,14 +727,31 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg)
           B[tg] = __builtin_bit_cast(v8i, __builtin_shufflevector(xa[tg], xb[tg], 0, 1, 2, 3, 4, 5, 6, 7));
+        if (ntg == 4) {
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
-          const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
+          for (int rg = 0; rg < 4; ++rg) {
+            const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
+            const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
 #pragma unroll
-          for (int tg = 0; tg < 4; ++tg)
-            acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 0, 0,
-                                                                           (int)sb[rg], 0, 127);
+            for (int tg = 0; tg < 4; ++tg)
+              acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 0, 0,
+                                                                             (int)sb[rg], 0, 127);
+          }
+        } else {
+          v8i A[4];
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
+            A[rg] = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int tg = 0; tg < 3; ++tg) {
+            if (tg >= ntg) break;
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg)
+              acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rg], B[tg], acc[rg][tg], 4, 0, 0,
+                                                                             (int)sb[rg], 0, 127);
+          }
         }
       }
     }
