@@ -447,6 +447,8 @@ def main():
     ap.add_argument("--dense-only", action="store_true",
                     help="only measure the dense projections (qkv_proj, o_proj, lm_head at 1 and 4 tokens) "
                          "and print them")
+    ap.add_argument("--nvfp4-only", action="store_true",
+                    help="only measure the NVFP4 decode layers (4 and 32 tokens) and print them")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (requested %d)" % args.gpus,
@@ -481,6 +483,9 @@ def main():
     cg = ceiling["ceiling_GBps"] if ceiling else None
     if args.dense_only:
         print(json.dumps({"dense": measure_dense(run, synth, args.steps, args.warmup)}), flush=True)
+        return
+    if args.nvfp4_only:
+        print(json.dumps({"nvfp4": measure_nvfp4(run, synth, args.steps, args.warmup)}), flush=True)
         return
     L = synth.layer()
     Ld = {k: run.dev(v) for k, v in L.items()}

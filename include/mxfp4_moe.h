@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 2
+#define MXFP4_ABI_VERSION 3
 
 /* Status codes.  0 is success; every failure leaves outputs untouched. */
 enum {
@@ -326,24 +326,46 @@ int nvfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
                       size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream);
 
 /*
- * Dense MXFP4 projection out = x W^T + b (spark-vllm page, MXFP4 qkv/o/lm_head;
- * gptoss-spark page: qkv_proj, o_proj and the 201k-row lm_head in MXFP4), bf16
- * activations, fp32 accumulation, one round-to-nearest-even to bf16.
+ * Dense MXFP4 projection out = x W^T + b (spark-vllm page, MXFP4 qkv/o/lm_head,
+ * and "Performance Optimizations": FP8 activations on the block-scaled MMA for
+ * the dense layers; gptoss-spark page: qkv_proj, o_proj and the 201k-row
+ * lm_head in MXFP4), fp32 accumulation, one round-to-nearest-even to bf16.
  *   x         bf16 [M, K]          16-byte aligned
  *   w_blocks  uint8 [N, K/32, 16]  16-byte aligned
  *   w_scales  uint8 [N, K/32]      4-byte aligned; E8M0 bytes in [11, 252]
- *                                  (the weight is formed in bf16 with the
- *                                  scaled FP4 conversion, exact for these
- *                                  bytes only; others are not rejected and
- *                                  give undefined results)
+ *                                  (with bf16 and E4M3 activations the
+ *                                  weight is formed with the scaled FP4
+ *                                  conversion, exact for these bytes only;
+ *                                  others are not rejected and give
+ *                                  undefined results; MXFP4 activations
+ *                                  take every byte except 255)
  *   bias      bf16 [N] or NULL, 8-byte aligned
+ *   act_mode  MXFP4_ACT_BF16: out = bf16(x W^T + b) with x used as given
+ *               (a weight stream for decode-sized M; any M is correct);
+ *             MXFP4_ACT_FP8_E4M3: x is quantised with the codec of
+ *               mxfp4_quant_fp8_e4m3 (one scale s over all of x) and
+ *               out = bf16(s (codes W^T) + b) on the FP8 x FP4 block-scaled
+ *               MFMA, whose internal sums carry about 2.4e-5 of the sum of
+ *               |products| per 128 elements (prefill-sized M);
+ *             MXFP4_ACT_MXFP4: each 32-element block of each row of x is
+ *               quantised to MXFP4 with the weight quantiser's rule
+ *               (mxfp4_quantize_weights) and out = bf16(xq W^T + b) on the
+ *               FP4 x FP4 block-scaled MFMA;
+ *             anything else: MXFP4_E_MODE
  *   out       bf16 [M, N]          16-byte aligned, must not alias the inputs
+ *   workspace device memory of mxfp4_linear_workspace_size() bytes, 256-byte
+ *             aligned, caller-owned (contents undefined after the call); may
+ *             be NULL when that size is 0 (MXFP4_ACT_BF16); too small:
+ *             MXFP4_E_WORKSPACE
  * Limits: K a positive multiple of 32, N a positive multiple of 16,
- * 0 <= M <= 2^20 (M == 0 is a no-op).
+ * 0 <= M <= 2^20 (M == 0 is a no-op); with quantised activations also
+ * K <= 65536 and (M/128 + 1)(N/256 + 1) < 2^30 (MXFP4_E_SHAPE otherwise).
  */
+int mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t act_mode, size_t* bytes);
 int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                  const uint8_t* w_blocks, const uint8_t* w_scales, const uint16_t* bias,
-                 uint16_t* out, void* stream);
+                 int32_t act_mode, uint16_t* out, void* workspace, size_t workspace_bytes,
+                 void* stream);
 
 /*
  * Per-tensor FP8 E4M3 quantiser, exactly the codec the FP8 MoE mode applies to

@@ -9,6 +9,7 @@ mxfp4_block_scaled_top_amd.build``.
 from ._lib import (ACT_BF16, ACT_FP8_E4M3, ACT_MXFP4, LIB_PATH, NUM_STAGES, STAGES,  # noqa: F401
                    Mxfp4Error, lib, mxfp4_abi_version, mxfp4_event_create,
                    mxfp4_event_destroy, mxfp4_event_elapsed_ms, mxfp4_linear,
+                   mxfp4_linear_workspace_size,
                    mxfp4_moe_forward, mxfp4_moe_layer, mxfp4_moe_layer_noalloc,
                    mxfp4_moe_workspace_layout_query,
                    mxfp4_moe_workspace_size, mxfp4_quant_fp8_e4m3, mxfp4_quantize_weights,

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmxfp4moe.so")
 ACT_BF16 = 0
 ACT_FP8_E4M3 = 1
 ACT_MXFP4 = 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 NUM_STAGES = 7
 STAGES = ("begin", "permute", "quant_x", "gemm1", "quant_h", "gemm2", "combine")
 
@@ -93,8 +93,9 @@ def lib():
             _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
             _c_void_p, _c_void_p, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, ctypes.c_float,
             _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeOpts), _c_void_p]
+        L.mxfp4_linear_workspace_size.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(ctypes.c_size_t)]
         L.mxfp4_linear.argtypes = [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
-                                   _c_void_p, _c_void_p]
+                                   _i32, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
         L.mxfp4_quant_fp8_e4m3.argtypes = [_c_void_p, _i32, _i64, _c_void_p, _c_void_p, _c_void_p,
                                            _c_void_p]
         L.mxfp4_quantize_weights.argtypes = [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]
@@ -105,7 +106,7 @@ def lib():
         L.mxfp4_event_elapsed_ms.argtypes = [_c_void_p, _c_void_p, ctypes.POINTER(ctypes.c_float)]
         for name in ("mxfp4_route_topk", "mxfp4_moe_workspace_size", "mxfp4_moe_workspace_layout_query",
                      "mxfp4_moe_forward", "mxfp4_moe_layer", "mxfp4_moe_layer_noalloc", "nvfp4_moe_forward",
-                     "mxfp4_linear",
+                     "mxfp4_linear_workspace_size", "mxfp4_linear",
                      "mxfp4_quant_fp8_e4m3",
                      "mxfp4_quantize_weights", "mxfp4_stream_read", "mxfp4_event_create",
                      "mxfp4_event_destroy", "mxfp4_event_elapsed_ms"):
@@ -342,8 +343,17 @@ def mxfp4_moe_layer_noalloc(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_b
     return out, topk_ids, topk_weights
 
 
-def mxfp4_linear(x, w_blocks, w_scales, bias=None, out=None, stream=None):
-    """Dense MXFP4 projection out = x W^T + b, bf16 [M, N]."""
+def mxfp4_linear_workspace_size(M, N, K, act_mode=ACT_BF16):
+    n = ctypes.c_size_t()
+    _check("mxfp4_linear_workspace_size", lib().mxfp4_linear_workspace_size(M, N, K, act_mode, ctypes.byref(n)))
+    return n.value
+
+
+def mxfp4_linear(x, w_blocks, w_scales, bias=None, out=None, stream=None, act_mode=ACT_BF16, workspace=None):
+    """Dense MXFP4 projection out = x W^T + b, bf16 [M, N].  With act_mode
+    ACT_FP8_E4M3 or ACT_MXFP4 x is quantised first; `workspace` is a uint8
+    device tensor of at least mxfp4_linear_workspace_size() bytes (allocated
+    here if None)."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_blocks, "w_blocks", torch.uint8, 3)
     _need(w_scales, "w_scales", torch.uint8, 2)
@@ -358,8 +368,14 @@ def mxfp4_linear(x, w_blocks, w_scales, bias=None, out=None, stream=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, 2)
+    need = mxfp4_linear_workspace_size(M, N, K, act_mode)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
     _check("mxfp4_linear", lib().mxfp4_linear(
-        _ptr(x), M, N, K, _ptr(w_blocks), _ptr(w_scales), _ptr(bias), _ptr(out), _stream(stream)))
+        _ptr(x), M, N, K, _ptr(w_blocks), _ptr(w_scales), _ptr(bias), act_mode, _ptr(out),
+        _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream)))
     return out
 
 

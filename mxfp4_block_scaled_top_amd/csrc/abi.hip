@@ -107,6 +107,43 @@ void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mod
   L->total_bytes = o;
 }
 
+// Workspace of the quantised-activation dense projection (one expert, M
+// rows in order): status words, tile list, identity row map (MXFP4), the
+// activation codes (and MXFP4 scales, step-major), the restaged weight
+// scales.  BF16 activations need none.
+struct LinearLayout {
+  size_t status, tiles, inv, codes, scales, w_stream, total;
+};
+
+int linear_shape_check(int64_t M, int64_t N, int64_t K, int32_t act_mode) {
+  if (act_mode != MXFP4_ACT_BF16 && act_mode != MXFP4_ACT_FP8_E4M3 && act_mode != MXFP4_ACT_MXFP4)
+    return fail(MXFP4_E_MODE, "unknown act_mode %d", act_mode);
+  if (M < 0 || M > (1 << 20)) return fail(MXFP4_E_SHAPE, "M=%lld outside [0, 2^20]", (long long)M);
+  if (N <= 0 || N % 16 || N > (1LL << 26)) return fail(MXFP4_E_SHAPE, "N=%lld must be a positive multiple of 16", (long long)N);
+  if (K <= 0 || K % 32 || K > (1 << 20)) return fail(MXFP4_E_SHAPE, "K=%lld must be a positive multiple of 32", (long long)K);
+  if (act_mode != MXFP4_ACT_BF16) {
+    if (K > (1 << 16)) return fail(MXFP4_E_SHAPE, "K=%lld above 65536 with quantised activations", (long long)K);
+    // (row tiles) x (256-row n-tiles) work units in an int
+    if ((M / mx::kPrefillBM + 1) * (N / 256 + 1) >= (1LL << 30))
+      return fail(MXFP4_E_SHAPE, "M=%lld x N=%lld too large with quantised activations", (long long)M, (long long)N);
+  }
+  return MXFP4_OK;
+}
+
+void linear_plan(int64_t M, int64_t N, int64_t K, int32_t act_mode, LinearLayout* L) {
+  memset(L, 0, sizeof(*L));
+  if (act_mode == MXFP4_ACT_BF16) return;
+  const bool a4 = act_mode == MXFP4_ACT_MXFP4;
+  size_t o = 0;
+  L->status = o; o = up(o + mx::kStWords * 4);
+  L->tiles = o; o = up(o + (size_t)mx::max_tiles(M, 1, mx::kPrefillBM) * mx::kTileInts * 4);
+  L->inv = o; if (a4) o = up(o + (size_t)M * 4);
+  L->codes = o; o = up(o + (size_t)M * (a4 ? K / 2 : K));
+  L->scales = o; if (a4) o = up(o + (size_t)mx::act_scale_bytes(M, (int)K));
+  L->w_stream = o; o = up(o + (size_t)mx::scale_stream_bytes(1, mx::down_ntiles((int)N), (int)K));
+  L->total = o;
+}
+
 mx::WsPtrs ws_ptrs(void* base, const mxfp4_moe_workspace_layout& L) {
   uint8_t* b = static_cast<uint8_t*>(base);
   mx::WsPtrs w;
@@ -417,21 +454,81 @@ int nvfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
                  "nvfp4_moe_forward", g);
 }
 
+int mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t act_mode, size_t* bytes) {
+  if (!bytes) return fail(MXFP4_E_NULL, "bytes is null");
+  int rc = linear_shape_check(M, N, K, act_mode);
+  if (rc) return rc;
+  LinearLayout L;
+  linear_plan(M, N, K, act_mode, &L);
+  *bytes = L.total;
+  return ok();
+}
+
 int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_blocks,
-                 const uint8_t* w_scales, const uint16_t* bias, uint16_t* out, void* stream) {
-  if (M < 0 || M > (1 << 20)) return fail(MXFP4_E_SHAPE, "M=%lld outside [0, 2^20]", (long long)M);
-  if (N <= 0 || N % 16 || N > (1LL << 26)) return fail(MXFP4_E_SHAPE, "N=%lld must be a positive multiple of 16", (long long)N);
-  if (K <= 0 || K % 32 || K > (1 << 20)) return fail(MXFP4_E_SHAPE, "K=%lld must be a positive multiple of 32", (long long)K);
+                 const uint8_t* w_scales, const uint16_t* bias, int32_t act_mode, uint16_t* out,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = linear_shape_check(M, N, K, act_mode);
+  if (rc) return rc;
   if (M == 0) return ok();
   if (!x || !w_blocks || !w_scales || !out) return fail(MXFP4_E_NULL, "linear: null pointer");
   if (!aligned(x, 16) || !aligned(w_blocks, 16) || !aligned(out, 16) || !aligned(w_scales, 4) ||
       (bias && !aligned(bias, 8)))
     return fail(MXFP4_E_ALIGN, "linear: x, w_blocks and out need 16-byte, bias 8-byte, w_scales 4-byte alignment");
-  int rc = check_device();
+  LinearLayout L;
+  linear_plan(M, N, K, act_mode, &L);
+  if (L.total) {
+    if (!workspace) return fail(MXFP4_E_WORKSPACE, "linear: workspace is null");
+    if (!aligned(workspace, 256)) return fail(MXFP4_E_ALIGN, "linear: workspace must be 256-byte aligned");
+    if (workspace_bytes < L.total)
+      return fail(MXFP4_E_WORKSPACE, "linear: workspace %zu bytes < required %llu", workspace_bytes,
+                  (unsigned long long)L.total);
+  }
+  rc = check_device();
   if (rc) return rc;
-  hipError_t e = mx::launch_linear_bf16(x, (int)M, (int)N, (int)K, w_blocks, w_scales, bias, out,
-                                        static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (act_mode == MXFP4_ACT_BF16) {
+    e = mx::launch_linear_bf16(x, (int)M, (int)N, (int)K, w_blocks, w_scales, bias, out, s);
+    if (e != hipSuccess) return hip_fail(e, "linear launch");
+    return ok();
+  }
+  // quantised activations: the MoE down GEMM with one expert whose rows are
+  // the M activation rows in order, written straight to bf16
+  const bool a4 = act_mode == MXFP4_ACT_MXFP4;
+  uint8_t* b = static_cast<uint8_t*>(workspace);
+  mx::WsPtrs ws{};
+  ws.status = reinterpret_cast<int*>(b + L.status);
+  ws.tiles = reinterpret_cast<int*>(b + L.tiles);
+  ws.inv = a4 ? reinterpret_cast<int*>(b + L.inv) : nullptr;
+  ws.x_codes = ws.h_codes = b + L.codes;
+  ws.x_scales = ws.h_scales = a4 ? b + L.scales : nullptr;
+  ws.w2_stream = b + L.w_stream;
+  const mx::MoeShape sh{(int)M, (int)N, (int)K, 1, 1};
+  mx::MoeWeights w{};
+  w.w2_blocks = w_blocks;
+  w.w2_scales = w_scales;
+  w.w2_bias = bias;
+  const int64_t bound = mx::max_tiles(M, 1, mx::kPrefillBM);
+#define MX_STEP(call, what)                      \
+  do {                                           \
+    e = (call);                                  \
+    if (e != hipSuccess) return hip_fail(e, what); \
+  } while (0)
+  MX_STEP(mx::launch_dense_tiles((int)M, mx::kPrefillBM, (int)bound, ws.status, ws.tiles, ws.inv, s),
+          "linear tiles launch");
+  if (a4) {
+    // per-row 32-element blocks of x (the rows' K is the quantiser's H)
+    const mx::MoeShape shq{(int)M, (int)K, (int)N, 1, 1};
+    MX_STEP(mx::launch_quant_x_mxfp4_sorted(x, shq, ws, s), "linear quant x launch");
+  } else {
+    MX_STEP(mx::launch_quant_fp8(x, true, M * K, ws.h_codes, reinterpret_cast<uint32_t*>(ws.status + mx::kStAmaxH),
+                                 reinterpret_cast<float*>(ws.status + mx::kStScaleH), s),
+            "linear quant x launch");
+  }
+  MX_STEP(mx::launch_scale_stream(sh, w, ws, false, s), "linear scale stream launch");
+  if (a4) MX_STEP(mx::launch_moe_down_fp4(sh, w, ws, s, out), "linear GEMM launch");
+  else MX_STEP(mx::launch_moe_down_fp8(sh, w, ws, bound, s, out), "linear GEMM launch");
+#undef MX_STEP
   return ok();
 }
 

@@ -113,6 +113,7 @@ struct PrefillArgs {
   int64_t asc_step;        // bytes per step of asc (4 * sorted rows)
   int scale_word;          // status word holding the per-tensor activation scale (E4M3)
   float* out;              // h [rows, I] (gate_up, E4M3 mode) or y [rows, H] (down), fp32
+  uint16_t* out_bf16;      // down: y rounded once to bf16 [rows, H] in place of out, or null
   // gate_up with E2M1 activations: h quantised in the epilogue into E2M1
   // blocks [rows, I/32, 16] and step-major E8M0 scales [ceil(I/128), rows, 4]
   uint8_t* h_codes;
@@ -846,8 +847,14 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
           float v[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) v[jj] = acc[rg][tg][jj] * sx + bf16_of(bq[rg], jj);
-          *reinterpret_cast<float4*>(a.out + (size_t)row * a.nout + n0 + 4 * g) =
-              make_float4(v[0], v[1], v[2], v[3]);
+          if (a.out_bf16) {
+            *reinterpret_cast<uint2*>(a.out_bf16 + (size_t)row * a.nout + n0 + 4 * g) =
+                make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                           f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+          } else {
+            *reinterpret_cast<float4*>(a.out + (size_t)row * a.nout + n0 + 4 * g) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
         }
       }
     }
@@ -1007,7 +1014,7 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
 }
 
 hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
-                               int64_t /*ntile_bound*/, hipStream_t s) {
+                               int64_t /*ntile_bound*/, hipStream_t s, uint16_t* out_bf16) {
   PrefillArgs a{};
   a.wb = w.w2_blocks;
   a.wsp = ws.w2_stream;
@@ -1023,6 +1030,7 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
   a.act_ld = sh.I;
   a.scale_word = kStScaleH;
   a.out = ws.y;
+  a.out_bf16 = out_bf16;
   return launch_prefill<false>(a, sh, ws, s);
 }
 
@@ -1050,7 +1058,8 @@ hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const 
   return launch_prefill<true, true>(a, sh, ws, s);
 }
 
-hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, hipStream_t s) {
+hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, hipStream_t s,
+                               uint16_t* out_bf16) {
   PrefillArgs a{};
   a.wb = w.w2_blocks;
   a.wsp = ws.w2_stream;
@@ -1068,6 +1077,7 @@ hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const Ws
   a.asc_step = (int64_t)4 * sh.T * sh.k;
   a.scale_word = -1;
   a.out = ws.y;
+  a.out_bf16 = out_bf16;
   return launch_prefill<false, true>(a, sh, ws, s);
 }
 

@@ -121,8 +121,10 @@ hipError_t launch_linear_bf16(const uint16_t* x, int M, int N, int K, const uint
 // FP8 x FP4 block-scaled MFMA path.
 hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
                                  int64_t ntile_bound, hipStream_t s);
+// With out_bf16, down writes y rounded once to bf16 there instead of fp32 y
+// (the dense projection: one expert, rows in order, routing weight 1).
 hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
-                               int64_t ntile_bound, hipStream_t s);
+                               int64_t ntile_bound, hipStream_t s, uint16_t* out_bf16 = nullptr);
 
 // MXFP4 activations: x in expert-sorted row order as E2M1 blocks + step-major
 // E8M0 scales (h is quantised by the gate_up GEMM's epilogue).
@@ -138,7 +140,12 @@ hipError_t launch_scale_stream(const MoeShape& sh, const MoeWeights& w, const Ws
 hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
                                  hipStream_t s);
 hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,
-                               hipStream_t s);
+                               hipStream_t s, uint16_t* out_bf16 = nullptr);
+
+// Dense rows as one expert (the prefill-sized dense projection): zeroes the
+// status words and writes the tile list of M rows in BM-row tiles (bound
+// entries) and, when inv is not null, the identity row map inv[m] = m.
+hipError_t launch_dense_tiles(int M, int BM, int bound, int* status, int* tiles, int* inv, hipStream_t s);
 
 // bf16 [nblocks * 32] -> MXFP4 blocks [nblocks, 16] + E8M0 scales [nblocks]
 hipError_t launch_quant_mxfp4(const uint16_t* w, int64_t nblocks, uint8_t* blocks, uint8_t* scales,

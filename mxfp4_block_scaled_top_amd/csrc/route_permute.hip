@@ -415,6 +415,30 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* i
   return hipGetLastError();
 }
 
+// ------------------------------------------------- dense rows, one expert ----
+// The prefill-sized dense projection runs the down GEMM with one expert whose
+// rows are the M activation rows in order: tiles of BM rows, the tile count
+// and zeroed status words, and (MXFP4 activations) the identity row map.
+__global__ __launch_bounds__(256) void dense_tiles_kernel(int M, int BM, int bound, int* __restrict__ status,
+                                                          int* __restrict__ tiles, int* __restrict__ inv) {
+  const int ntiles = (M + BM - 1) / BM;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x < kStWords) status[threadIdx.x] = threadIdx.x == kStNumTiles ? ntiles : 0;
+  if (i < bound) {
+    const int t = (int)i;
+    *reinterpret_cast<int4*>(tiles + kTileInts * i) =
+        t < ntiles ? make_int4(0, t * BM, min(t * BM + BM, M), tile_word(0, ntiles, bound)) : make_int4(-1, 0, 0, 0);
+  }
+  if (inv && i < M) inv[i] = (int)i;
+}
+
+hipError_t launch_dense_tiles(int M, int BM, int bound, int* status, int* tiles, int* inv, hipStream_t s) {
+  const int64_t n = M > bound ? M : bound;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  dense_tiles_kernel<<<grid > 0 ? grid : 1, 256, 0, s>>>(M, BM, bound, status, tiles, inv);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const int* ids, int npairs, int E, int BM, int tile_bound,
                           const WsPtrs& ws, hipStream_t s) {
   const int bits = id_bits_for(E);

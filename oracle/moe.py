@@ -214,6 +214,44 @@ def linear(x_bits, w_blocks, w_scales, bias_bits=None):
     return x @ W.T + _bias(bias_bits, (W.shape[0],))
 
 
+def linear_act(x_bits, w_blocks, w_scales, bias_bits=None, act_mode=ACT_BF16):
+    """Dense MXFP4 projection with the activation formats of the MoE layer,
+    float64.  Returns a dict with out [M, N] and the activation codes.
+
+    Reading (listed in the design doc): at prefill sizes the dense layers take the
+    activations the MoE contraction takes -- the spark-vllm page runs the
+    MoE layers as FP8 activations times FP4 weights ("What's Included") and
+    asks for the dense layers on the same block-scaled MMA ("Performance
+    Optimizations"); the FP4 x FP4 form is the one it lists as future work.
+      ACT_BF16      out = x W^T + b (linear()).
+      ACT_FP8_E4M3  x quantised with one scale over the whole of x
+                    (quant_per_tensor): out = s (codes W^T) + b.
+      ACT_MXFP4     each 32-element block of each row of x quantised with the
+                    weight rule (quantize_mxfp4): out = dequant(xq) W^T + b.
+    """
+    x = bf16_bits_to_f64(x_bits)
+    W = dequant(w_blocks, w_scales)
+    if W.shape[1] != x.shape[1]:
+        raise ValueError("K mismatch")
+    b = _bias(bias_bits, (W.shape[0],))
+    res = {}
+    if act_mode == ACT_BF16:
+        a = x
+    elif act_mode == ACT_FP8_E4M3:
+        xc, sx, _ = quant_per_tensor(x)
+        a = e4m3_decode(xc) * sx
+        res.update(x_codes=xc, x_scale=sx)
+    elif act_mode == ACT_MXFP4:
+        xb, xs = quantize_mxfp4(x)
+        a = dequant(xb, xs)
+        res.update(x_blocks=xb, x_scales=xs)
+    else:
+        raise ValueError("unknown act_mode")
+    res["a"] = a
+    res["out"] = a @ W.T + b
+    return res
+
+
 def linear_rows(x_bits, w_blocks, w_scales, bias_bits, rows):
     """linear() for a subset of output columns (rows of W), float64 [M, len(rows)]."""
     rows = np.asarray(rows)

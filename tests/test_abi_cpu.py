@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 2
+    assert L.mxfp4_abi_version() == 3
     assert L.mxfp4_status_string(0) == b"ok"
     assert L.mxfp4_status_string(E_WORKSPACE) == b"workspace too small"
     assert L.mxfp4_status_string(99) == b"unknown status"
@@ -140,13 +140,25 @@ def test_moe_forward_rejects_bad_arguments_without_touching_memory(L):
                              None, None) == E_MODE
 
 
+def _lin(L, x, M, N, K, bias=None, mode=0, ws=None, ws_bytes=0):
+    return L.mxfp4_linear(x, M, N, K, _fake(), _fake(), bias, mode, _fake(), ws, ws_bytes, None)
+
+
 def test_linear_and_quant_and_route_validation(L):
-    assert L.mxfp4_linear(_fake(), 1, 100, 2880, _fake(), _fake(), None, _fake(), None) == E_SHAPE
-    assert L.mxfp4_linear(_fake(), 1, 128, 2881, _fake(), _fake(), None, _fake(), None) == E_SHAPE
-    assert L.mxfp4_linear(None, 1, 128, 2880, _fake(), _fake(), None, _fake(), None) == E_NULL
-    assert L.mxfp4_linear(_fake(), 0, 128, 2880, _fake(), _fake(), None, _fake(), None) == 0
-    assert L.mxfp4_linear(_fake(), 1, 128, 2880, _fake(), _fake(), ctypes.c_void_p(0x1002), _fake(),
-                          None) == E_ALIGN
+    assert _lin(L, _fake(), 1, 100, 2880) == E_SHAPE
+    assert _lin(L, _fake(), 1, 128, 2881) == E_SHAPE
+    assert _lin(L, None, 1, 128, 2880) == E_NULL
+    assert _lin(L, _fake(), 0, 128, 2880) == 0
+    assert _lin(L, _fake(), 1, 128, 2880, bias=ctypes.c_void_p(0x1002)) == E_ALIGN
+    assert _lin(L, _fake(), 1, 128, 2880, mode=7) == E_MODE
+    # quantised activations need the workspace the size query gives
+    for mode in (1, 2):
+        assert _lin(L, _fake(), 4, 128, 2880, mode=mode) == E_WORKSPACE
+        assert _lin(L, _fake(), 4, 128, 2880, mode=mode, ws=_fake(), ws_bytes=1024) == E_WORKSPACE
+        assert _lin(L, _fake(), 4, 128, 2880, mode=mode, ws=ctypes.c_void_p(0x1010),
+                    ws_bytes=1 << 40) == E_ALIGN
+        assert _lin(L, _fake(), 4, 128, 1 << 17, mode=mode) == E_SHAPE
+    assert _lin(L, _fake(), 4, 128, 1 << 17, mode=9) == E_MODE
     assert L.mxfp4_quant_fp8_e4m3(_fake(), 5, 10, _fake(), _fake(), _fake(), None) == E_MODE
     assert L.mxfp4_quant_fp8_e4m3(_fake(), 0, 10, _fake(), None, _fake(), None) == E_NULL
     assert L.mxfp4_route_topk(_fake(), 4, 128, 0, _fake(), _fake(), None) == E_SHAPE
@@ -206,3 +218,22 @@ def test_moe_layer_noalloc_rejects_bad_arguments_without_touching_memory(L):
     assert f(*args(32, 2880, 2880, 128, 4, 0, logits=None)) == E_NULL
     assert f(*args(32, 33, 2880, 128, 4, 0)) == E_SHAPE
     assert f(*args(0, 2880, 2880, 128, 4, 0)) == 0          # T == 0: no-op
+
+
+def test_linear_workspace_size(L):
+    n = ctypes.c_size_t()
+    assert L.mxfp4_linear_workspace_size(4, 5120, 2880, 0, ctypes.byref(n)) == 0 and n.value == 0
+    assert L.mxfp4_linear_workspace_size(4, 5120, 2880, 3, ctypes.byref(n)) == E_MODE
+    assert L.mxfp4_linear_workspace_size(4, 5120, 2880, 1, None) == E_NULL
+    sizes = {}
+    for mode in (1, 2):
+        for M in (1, 2048):
+            assert L.mxfp4_linear_workspace_size(M, 5120, 2880, mode, ctypes.byref(n)) == 0
+            sizes[mode, M] = n.value
+    # codes (1 byte, MXFP4 half a byte, per element of x) plus the restaged
+    # weight scales (1 KB per 256-row n-tile and 128-element K step)
+    stream = 20 * 23 * 1024
+    assert sizes[1, 2048] >= 2048 * 2880 + stream
+    assert sizes[2, 2048] >= 2048 * 1440 + stream + 23 * 2048 * 4
+    assert sizes[1, 2048] - sizes[1, 1] >= 2047 * 2880
+    assert sizes[2, 2048] < sizes[1, 2048]

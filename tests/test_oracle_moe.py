@@ -348,6 +348,100 @@ def test_linear_matches_exact_brute_force():
                           got[:, rows])
 
 
+@pytest.mark.parametrize("act_mode", [ACT_FP8_E4M3, ACT_MXFP4])
+def test_linear_act_matches_exact_brute_force(act_mode):
+    """The quantised-activation dense projection against the brute force:
+    per-tensor FP8 over all of x, or MXFP4 per 32-element block of each row,
+    then the exact contraction and the bias."""
+    N, K, M = 16, 96, 3
+    D = synth.dense(43, N, K)
+    x = synth.dense_x(44, M, K)
+    res = oracle.moe.linear_act(x, D["w_blocks"], D["w_scales"], D["bias"], act_mode)
+    vals = [_bf_bf16(v) for v in x.reshape(-1)]
+    if act_mode == ACT_FP8_E4M3:
+        q = _bf_quant(vals)                    # one scale over the whole of x
+        a = [q[m * K:(m + 1) * K] for m in range(M)]
+    else:
+        a = [_bf_mx_quant(vals[m * K:(m + 1) * K]) for m in range(M)]
+    for m in range(M):
+        for kk in range(K):
+            assert res["a"][m, kk] == float(a[m][kk])
+        for n in range(N):
+            acc = sum(_bf_weight(D["w_blocks"], D["w_scales"], n, kk) * a[m][kk] for kk in range(K))
+            want = float(acc + _bf_bf16(D["bias"][n]))
+            assert abs(res["out"][m, n] - want) <= 1e-13 * max(1.0, abs(want))
+
+
+def test_linear_act_fp8_scale_spans_all_rows():
+    """FP8 activations take one scale over the whole of x: a large element in
+    row 0 changes the codes of the other rows; MXFP4 blocks do not see it."""
+    N, K, M = 16, 64, 3
+    D = synth.dense(45, N, K)
+    x = synth.dense_x(46, M, K)
+    big = x.copy()
+    big[0, 5] = np.uint16(0x4700)                # bf16 32768.0
+    f0 = oracle.moe.linear_act(x, D["w_blocks"], D["w_scales"], None, ACT_FP8_E4M3)
+    f1 = oracle.moe.linear_act(big, D["w_blocks"], D["w_scales"], None, ACT_FP8_E4M3)
+    assert f1["x_scale"] == np.float32(32768.0 / 448)
+    assert not np.array_equal(f0["x_codes"][1:], f1["x_codes"][1:])
+    m0 = oracle.moe.linear_act(x, D["w_blocks"], D["w_scales"], None, ACT_MXFP4)
+    m1 = oracle.moe.linear_act(big, D["w_blocks"], D["w_scales"], None, ACT_MXFP4)
+    assert np.array_equal(m0["out"][1:], m1["out"][1:])
+    assert np.array_equal(m0["x_blocks"][0, 1:], m1["x_blocks"][0, 1:])
+
+
+def test_linear_act_reduces_to_linear_on_representable_x():
+    """Activations the quantisers represent exactly leave the projection as
+    the plain definition: bf16 values k * 2^j with |k| <= 6 on a per-tensor
+    maximum of 448 * 2^-3 (FP8), and E2M1 values times 2^X with a block
+    maximum of 6 * 2^X (MXFP4)."""
+    N, K, M = 32, 128, 4
+    D = synth.dense(47, N, K)
+    rng = np.random.default_rng(48)
+
+    def bf16(v):
+        return (np.asarray(v, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+    e4 = np.array([0, 0.25, 0.5, 1, 1.5, 2, 3, 4, 6, 56, 448], dtype=np.float64) / 8
+    xf = rng.choice(e4, size=(M, K)) * rng.choice([-1, 1], size=(M, K))
+    xf[0, 0] = 448 / 8
+    x = bf16(xf)
+    ref = oracle.linear(x, D["w_blocks"], D["w_scales"], D["bias"])
+    got = oracle.moe.linear_act(x, D["w_blocks"], D["w_scales"], D["bias"], ACT_FP8_E4M3)
+    assert got["x_scale"] == np.float32(1 / 8)
+    assert np.array_equal(got["out"], ref)
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
+    xm = rng.choice(mags, size=(M, K)) * rng.choice([-1, 1], size=(M, K))
+    X = rng.integers(-20, 20, size=(M, K // 32))
+    xm = xm.reshape(M, K // 32, 32)
+    xm[:, :, 7] = 6.0
+    xm = (xm * np.exp2(X)[:, :, None]).reshape(M, K)
+    x = bf16(xm)
+    ref = oracle.linear(x, D["w_blocks"], D["w_scales"], D["bias"])
+    got = oracle.moe.linear_act(x, D["w_blocks"], D["w_scales"], D["bias"], ACT_MXFP4)
+    assert np.array_equal(got["x_scales"], (X + 127).astype(np.uint8))
+    assert np.array_equal(got["out"], ref)
+
+
+def test_linear_act_power_of_two_scaling_of_x():
+    """Scaling x by 2^j (in range) keeps every FP8 code and MXFP4 code, moves
+    the scales by j, and scales the bias-free output by exactly 2^j."""
+    N, K, M = 16, 64, 3
+    D = synth.dense(49, N, K)
+    x = synth.dense_x(50, M, K)
+    x2 = (x.astype(np.uint32) + (3 << 7)).astype(np.uint16)   # bf16 exponent + 3 (no zeros in x)
+    assert np.all((x & 0x7f80) != 0)
+    for mode in (ACT_FP8_E4M3, ACT_MXFP4):
+        r1 = oracle.moe.linear_act(x, D["w_blocks"], D["w_scales"], None, mode)
+        r2 = oracle.moe.linear_act(x2, D["w_blocks"], D["w_scales"], None, mode)
+        assert np.array_equal(r2["out"], 8 * r1["out"])
+        if mode == ACT_FP8_E4M3:
+            assert np.array_equal(r1["x_codes"], r2["x_codes"]) and r2["x_scale"] == 8 * r1["x_scale"]
+        else:
+            assert np.array_equal(r1["x_blocks"], r2["x_blocks"])
+            assert np.array_equal(r2["x_scales"].astype(int), r1["x_scales"].astype(int) + 3)
+
+
 def test_one_bf16_rounding_fits_the_tolerance_but_two_do_not():
     """Error budget behind the 'one rounding at the end' design: rounding a
     Gaussian output to bf16 once costs about 1.7e-3 relative Frobenius error,
