@@ -345,6 +345,46 @@ def measure_dense(run, synth, steps, warmup):
     return out
 
 
+def dense_prefill_peak_tflops(act):
+    """Dense peak of the block-scaled MFMA form a quantised dense projection
+    issues: E4M3 x E2M1 at the FP8 rate, E2M1 x E2M1 at the FP4 rate."""
+    return MXFP4_PEAK_TFLOPS if act == 2 else FP8_PEAK_TFLOPS
+
+
+def measure_dense_prefill(run, synth, steps, warmup, tokens=2048):
+    """The dense projections at a prefill's token count with quantised
+    activations (x quantised inside the call): time per call, TFLOP/s and its
+    fraction of the issued form's peak and of min(peak, AI x 8 TB/s)."""
+    mx = run.mx
+    out = {}
+    for name, (N, K) in synth.DENSE_SHAPES.items():
+        D = synth.dense(synth.DENSE_SEEDS[name], N, K)
+        wb, wsc, b = run.dev(D["w_blocks"]), run.dev(D["w_scales"]), run.dev(D["bias"])
+        x = run.dev(synth.dense_x(synth.DENSE_X_SEED + 100, tokens, K))
+        y = run.torch.empty((tokens, N), dtype=run.torch.bfloat16, device="cuda")
+        for act in (1, 2):
+            ws = run.torch.empty(max(mx.mxfp4_linear_workspace_size(tokens, N, K, act), 1),
+                                 dtype=run.torch.uint8, device="cuda")
+
+            def step(_ev, x=x, y=y, wb=wb, wsc=wsc, b=b, act=act, ws=ws):
+                mx.mxfp4_linear(x, wb, wsc, b, out=y, act_mode=act, workspace=ws)
+
+            ms, _, _ = run.time_steps(step, steps, warmup, flush=True)
+            mean = float(np.mean(ms))
+            flops = 2.0 * tokens * N * K
+            nbytes = N * (K // 32) * 17 + 2 * N + tokens * K * 2 + tokens * N * 2
+            tf = flops / mean / 1e9
+            peak = dense_prefill_peak_tflops(act)
+            attain = min(peak, flops / nbytes * HBM_PEAK_GBS / 1e3)
+            out["%s_%s_m%d" % (name, ACT_NAMES[act], tokens)] = dict(
+                N=N, K=K, M=tokens, act=ACT_NAMES[act], ms=mean, TFLOPs=tf, issued_peak_TFLOPs=peak,
+                frac_issued_peak=tf / peak, flop_per_byte=flops / nbytes, attainable_TFLOPs=attain,
+                frac_attainable=tf / attain)
+            del ws
+        del wb, wsc, b, x, y
+    return out
+
+
 def measure_quantizer(run, synth, steps, warmup):
     """BF16 -> MXFP4 quantisation of the lm_head weight (201,088 x 2880): a stream
     of N*K*2 bytes in and N*K*17/32 bytes out."""
@@ -482,7 +522,9 @@ def main():
         return
     cg = ceiling["ceiling_GBps"] if ceiling else None
     if args.dense_only:
-        print(json.dumps({"dense": measure_dense(run, synth, args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"dense": measure_dense(run, synth, args.steps, args.warmup),
+                          "dense_prefill": measure_dense_prefill(run, synth, max(args.steps // 2, 5), 2)}),
+              flush=True)
         return
     if args.nvfp4_only:
         print(json.dumps({"nvfp4": measure_nvfp4(run, synth, args.steps, args.warmup)}), flush=True)
@@ -512,6 +554,8 @@ def main():
         torch.cuda.empty_cache()
         others["dense"] = measure_dense(run, synth, max(args.steps // 2, 5), 2)
         print("bench: dense set done", file=sys.stderr, flush=True)
+        others["dense_prefill"] = measure_dense_prefill(run, synth, max(args.steps // 3, 5), 2)
+        print("bench: prefill dense set done", file=sys.stderr, flush=True)
         others["quantize_lm_head"] = measure_quantizer(run, synth, max(args.steps // 3, 5), 2)
         print("bench: quantiser %.1f us" % (others["quantize_lm_head"]["ms"] * 1e3), file=sys.stderr, flush=True)
 

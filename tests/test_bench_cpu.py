@@ -84,3 +84,9 @@ def test_tflops_fractions():
     assert abs(f["frac_attainable"] - 1500.0 / 10100.0) < 1e-12
     assert f["attainable_measured_TFLOPs"] == min(10100.0, 2000.0 * 6.0)
     assert abs(f["frac_mxfp4_peak"] - 1500.0 / 10100.0) < 1e-12
+
+
+def test_dense_prefill_peaks_follow_the_issued_form():
+    # E4M3 x E2M1 at the FP8 rate, E2M1 x E2M1 at the FP4 rate
+    assert bench.dense_prefill_peak_tflops(1) == bench.FP8_PEAK_TFLOPS == 5000.0
+    assert bench.dense_prefill_peak_tflops(2) == bench.MXFP4_PEAK_TFLOPS == 10100.0
