@@ -231,11 +231,34 @@ def measure_ceiling(run, nbytes=4 << 30, reps=10):
     return out
 
 
+def graph_replay_times(run, step, steps, warmup):
+    """Per-replay times (ms) of `step` captured in a HIP graph."""
+    torch = run.torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(None)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(None)
+    torch.cuda.synchronize()
+    ms, _, _ = run.time_steps(lambda _ev: g.replay(), steps, warmup, flush=True)
+    del g
+    return ms
+
+
 def measure_moe(run, Ld, name, synth, steps, warmup, ceiling_gbps=None):
     step, acct, wl = moe_setup(run, Ld, name, synth)
     ms, stages, wall = run.time_steps(step, steps, warmup, flush=True, stage_events=True)
     ms_plain, _, _ = run.time_steps(step, steps, warmup, flush=True, stage_events=False)
     warm, _, _ = run.time_steps(step, max(steps // 2, 3), 1, flush=False)
+    graph_ms = None
+    if wl["act_mode"] == 0:
+        # the same call captured once in a HIP graph and replayed (the
+        # launches of a serving loop); the cache eviction stays outside
+        graph_ms = float(np.mean(graph_replay_times(run, step, steps, warmup)))
     prepared = None
     if wl["act_mode"] != 0:
         # the weight scales restaged once (a load-time step for fixed weights):
@@ -253,6 +276,7 @@ def measure_moe(run, Ld, name, synth, steps, warmup, ceiling_gbps=None):
         layer_TFLOPs=acct["flops"] / mean / 1e9,
         layer_hbm_frac=acct["layer_bytes"] / mean / 1e6 / HBM_PEAK_GBS,
         warm_ms_per_step=float(np.mean(warm)),
+        graph_ms_per_step=graph_ms,
         prepared_scales_ms_per_step=prepared,
         stage_ms=stages, gemm1_ms=g1,
         gemm1_GBps=acct["gemm1_bytes"] / g1 / 1e6,
