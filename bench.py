@@ -304,8 +304,10 @@ def nvfp4_expert_bytes(H, I):
 
 
 def measure_nvfp4(run, synth, steps, warmup):
-    """The decode batches with NVFP4 expert weights: router top-k and the NVFP4
-    MoE layer, bf16 activations."""
+    """The MoE batches with NVFP4 expert weights: router top-k and the NVFP4
+    MoE layer; the decode batches with bf16 activations, the prefill batches
+    with E4M3 activations (both GEMMs on the bf16 MFMA with exactly expanded
+    operands; also timed with the restaged scale streams kept)."""
     torch, mx = run.torch, run.mx
     L = synth.nvfp4_layer()
     Nd = {k: (run.dev(v) if isinstance(v, np.ndarray) else v) for k, v in L.items()}
@@ -313,35 +315,43 @@ def measure_nvfp4(run, synth, steps, warmup):
     H = I = synth.H_GPT_OSS
     E, k = synth.E_GPT_OSS, synth.TOPK_GPT_OSS
     res = {}
-    for name in ("moe_decode_t4", "moe_decode_t32"):
+    for name in ("moe_decode_t4", "moe_decode_t32", "moe_prefill_t2048_fp8", "moe_prefill_t8192_fp8_skewed"):
         wl = synth.workload(name)
         T = wl["T"]
+        act = wl["act_mode"]
         logits, x = run.dev(wl["logits"]), run.dev(wl["x"])
         ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
         w = torch.empty((T, k), dtype=torch.float32, device="cuda")
         out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(mx.mxfp4_moe_workspace_size(T, H, I, E, k, synth.ACT_BF16), dtype=torch.uint8,
-                         device="cuda")
+        ws = torch.empty(mx.nvfp4_moe_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device="cuda")
 
-        def step(events, logits=logits, x=x, ids=ids, w=w, out=out, ws=ws):
+        def step(events, ready=False, logits=logits, x=x, ids=ids, w=w, out=out, ws=ws, act=act):
             mx.mxfp4_route_topk(logits, k, topk_ids=ids, topk_weights=w)
             mx.nvfp4_moe_forward(x, ids, w, Nd["w13_blocks"], Nd["w13_scales"], Nd["w13_global"],
                                  Nd["w13_bias"], Nd["w2_blocks"], Nd["w2_scales"], Nd["w2_global"],
-                                 Nd["w2_bias"], out=out, workspace=ws, events=events)
+                                 Nd["w2_bias"], out=out, workspace=ws, events=events, act_mode=act,
+                                 scale_streams_ready=ready)
 
         step(None)
         torch.cuda.synchronize()
         touched = len(np.unique(ids.cpu().numpy()))
         gu, dn = nvfp4_expert_bytes(H, I)
         layer_bytes = touched * (gu + dn) + T * H * 2 + T * E * 4 + T * H * 2
-        gemm1_bytes = touched * gu + T * H * 2 + ids.numel() * I * 4
+        gemm1_bytes = touched * gu + T * H * (1 if act else 2) + ids.numel() * I * 4
         ms, stages, _ = run.time_steps(step, steps, warmup, flush=True, stage_events=True)
         ms_plain, _, _ = run.time_steps(step, steps, warmup, flush=True)
         mean = float(np.mean(ms_plain))
-        res[name.replace("moe_", "moe_nvfp4_")] = dict(
-            tokens=T, touched_experts=touched, ms_per_step=mean, layer_GBps=layer_bytes / mean / 1e6,
-            layer_hbm_frac=layer_bytes / mean / 1e6 / HBM_PEAK_GBS, stage_ms=stages,
-            gemm1_GBps=gemm1_bytes / stages["gemm1"] / 1e6, algorithmic_bytes=layer_bytes)
+        flops = 2.0 * ids.numel() * (2 * I * H + H * I)
+        r = dict(tokens=T, act=ACT_NAMES[act], touched_experts=touched, ms_per_step=mean,
+                 layer_GBps=layer_bytes / mean / 1e6, layer_hbm_frac=layer_bytes / mean / 1e6 / HBM_PEAK_GBS,
+                 layer_TFLOPs=flops / mean / 1e9, stage_ms=stages,
+                 gemm1_GBps=gemm1_bytes / stages["gemm1"] / 1e6, algorithmic_bytes=layer_bytes)
+        if act:
+            ms_prep, _, _ = run.time_steps(lambda ev: step(ev, True), steps, warmup, flush=True)
+            r["prepared_scales_ms_per_step"] = float(np.mean(ms_prep))
+            # both GEMMs issue the bf16 MFMA
+            r["frac_issued_peak"] = r["layer_TFLOPs"] / BF16_PEAK_TFLOPS
+        res[name.replace("moe_", "moe_nvfp4_")] = r
     del Nd
     return res
 
@@ -572,9 +582,11 @@ def main():
         del Ld
         torch.cuda.empty_cache()
         others.update(measure_nvfp4(run, synth, max(args.steps // 2, 5), 2))
-        print("bench: nvfp4 decode %.1f / %.1f us (4 / 32 tokens)"
+        print("bench: nvfp4 decode %.1f / %.1f us (4 / 32 tokens), prefill %.1f / %.1f us (2048 / 8192 tokens)"
               % (others["moe_nvfp4_decode_t4"]["ms_per_step"] * 1e3,
-                 others["moe_nvfp4_decode_t32"]["ms_per_step"] * 1e3), file=sys.stderr, flush=True)
+                 others["moe_nvfp4_decode_t32"]["ms_per_step"] * 1e3,
+                 others["moe_nvfp4_prefill_t2048_fp8"]["ms_per_step"] * 1e3,
+                 others["moe_nvfp4_prefill_t8192_fp8_skewed"]["ms_per_step"] * 1e3), file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         others["dense"] = measure_dense(run, synth, max(args.steps // 2, 5), 2)
         print("bench: dense set done", file=sys.stderr, flush=True)

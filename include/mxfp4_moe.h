@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 3
+#define MXFP4_ABI_VERSION 4
 
 /* Status codes.  0 is success; every failure leaves outputs untouched. */
 enum {
@@ -300,8 +300,9 @@ int mxfp4_moe_layer_noalloc(const uint16_t* x, const float* logits, int64_t T, i
 /*
  * The MoE layer of mxfp4_moe_forward with NVFP4 expert weights (gpt-oss page,
  * "The MXFP4 -> NVFP4 Conversion": the same E2M1 element code, 16-element
- * blocks, one E4M3 scale per block, one global scale per tensor), bf16
- * activations only.  A weight is E2M1(code) * E4M3(block scale) * global.
+ * blocks, one E4M3 scale per block, one global scale per tensor; spark-vllm
+ * page, "New Features": NVFP4 with group size 16).  A weight is
+ * E2M1(code) * E4M3(block scale) * global.
  *   w13_blocks   uint8 [E, 2I, H/16, 8]      16-byte aligned; element 2i of a
  *                                            block in the low nibble of byte i
  *   w13_scales   uint8 [E, 2I, H/16]         4-byte aligned; finite OCP E4M3
@@ -310,20 +311,29 @@ int mxfp4_moe_layer_noalloc(const uint16_t* x, const float* logits, int64_t T, i
  *   w2_blocks    uint8 [E, H, I/16, 8]       16-byte aligned
  *   w2_scales    uint8 [E, H, I/16]          4-byte aligned
  *   w2_global    fp32 global scale of w2 (finite)
- * Every other argument is that of mxfp4_moe_forward with act_mode
- * MXFP4_ACT_BF16 (workspace: mxfp4_moe_workspace_size(..., MXFP4_ACT_BF16)).
- * Each weight is formed exactly in bf16 (E2M1 x E4M3 has at most 6
- * significant bits) and the global scale multiplies the fp32 sums before the
- * bias.  Limits as mxfp4_moe_forward, and 160 <= H, I <= 3072 (five to 96
- * 32-element chunks per weight row, the span of the persistent decode
- * kernel) and T*k*max(H, I)*2 < 2^31; outside them MXFP4_E_SHAPE.
+ *   act_mode     MXFP4_ACT_BF16 (decode: the persistent weight stream) or
+ *                MXFP4_ACT_FP8_E4M3 (prefill: x and h quantised exactly as
+ *                in mxfp4_moe_forward, both GEMMs on the bf16 MFMA with the
+ *                E4M3 codes and the weights expanded exactly to bf16: an
+ *                E4M3 block scale cannot ride on the block-scaled MFMA,
+ *                whose scales are E8M0); MXFP4_ACT_MXFP4: MXFP4_E_MODE
+ *   workspace    nvfp4_moe_workspace_size() bytes (its restaged scale
+ *                streams take 8 bytes per weight row and 128-element step)
+ * Every other argument is that of mxfp4_moe_forward.  Each weight is formed
+ * exactly in bf16 (E2M1 x E4M3 has at most 6 significant bits) and the global
+ * scale multiplies the fp32 sums (with the activation scale) before the bias.
+ * Limits as mxfp4_moe_forward; with bf16 activations also 160 <= H, I <= 3072
+ * (five to 96 32-element chunks per weight row, the span of the persistent
+ * decode kernel) and T*k*max(H, I)*2 < 2^31; outside them MXFP4_E_SHAPE.
  */
+int nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mode,
+                             size_t* bytes);
 int nvfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
                       const int32_t* topk_ids, const float* topk_weights,
                       const uint8_t* w13_blocks, const uint8_t* w13_scales, float w13_global,
                       const uint16_t* w13_bias, const uint8_t* w2_blocks, const uint8_t* w2_scales,
-                      float w2_global, const uint16_t* w2_bias, uint16_t* out, void* workspace,
-                      size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream);
+                      float w2_global, const uint16_t* w2_bias, int32_t act_mode, uint16_t* out,
+                      void* workspace, size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream);
 
 /*
  * Dense MXFP4 projection out = x W^T + b (spark-vllm page, MXFP4 qkv/o/lm_head,

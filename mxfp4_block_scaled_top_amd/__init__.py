@@ -13,4 +13,5 @@ from ._lib import (ACT_BF16, ACT_FP8_E4M3, ACT_MXFP4, LIB_PATH, NUM_STAGES, STAG
                    mxfp4_moe_forward, mxfp4_moe_layer, mxfp4_moe_layer_noalloc,
                    mxfp4_moe_workspace_layout_query,
                    mxfp4_moe_workspace_size, mxfp4_quant_fp8_e4m3, mxfp4_quantize_weights,
-                   mxfp4_route_topk, mxfp4_stream_read, nvfp4_moe_forward)
+                   mxfp4_route_topk, mxfp4_stream_read, nvfp4_moe_forward,
+                   nvfp4_moe_workspace_size)

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmxfp4moe.so")
 ACT_BF16 = 0
 ACT_FP8_E4M3 = 1
 ACT_MXFP4 = 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 NUM_STAGES = 7
 STAGES = ("begin", "permute", "quant_x", "gemm1", "quant_h", "gemm2", "combine")
 
@@ -92,7 +92,9 @@ def lib():
         L.nvfp4_moe_forward.argtypes = [
             _c_void_p, _i64, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p,
             _c_void_p, _c_void_p, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, ctypes.c_float,
-            _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeOpts), _c_void_p]
+            _c_void_p, _i32, _c_void_p, _c_void_p, ctypes.c_size_t, ctypes.POINTER(MoeOpts), _c_void_p]
+        L.nvfp4_moe_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32,
+                                               ctypes.POINTER(ctypes.c_size_t)]
         L.mxfp4_linear_workspace_size.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(ctypes.c_size_t)]
         L.mxfp4_linear.argtypes = [_c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                    _i32, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
@@ -106,6 +108,7 @@ def lib():
         L.mxfp4_event_elapsed_ms.argtypes = [_c_void_p, _c_void_p, ctypes.POINTER(ctypes.c_float)]
         for name in ("mxfp4_route_topk", "mxfp4_moe_workspace_size", "mxfp4_moe_workspace_layout_query",
                      "mxfp4_moe_forward", "mxfp4_moe_layer", "mxfp4_moe_layer_noalloc", "nvfp4_moe_forward",
+                     "nvfp4_moe_workspace_size",
                      "mxfp4_linear_workspace_size", "mxfp4_linear",
                      "mxfp4_quant_fp8_e4m3",
                      "mxfp4_quantize_weights", "mxfp4_stream_read", "mxfp4_event_create",
@@ -224,12 +227,19 @@ def mxfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bia
     return out
 
 
+def nvfp4_moe_workspace_size(T, H, I, E, k, act_mode=ACT_BF16):
+    n = ctypes.c_size_t()
+    _check("nvfp4_moe_workspace_size",
+           lib().nvfp4_moe_workspace_size(T, H, I, E, k, act_mode, ctypes.byref(n)))
+    return n.value
+
+
 def nvfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_global, w13_bias,
                       w2_blocks, w2_scales, w2_global, w2_bias, out=None, workspace=None, events=None,
-                      stream=None):
+                      stream=None, act_mode=ACT_BF16, scale_streams_ready=False):
     """MoE layer with NVFP4 expert weights (blocks [E, N, K/16, 8], E4M3 scales
-    [E, N, K/16], one fp32 global scale per tensor), bf16 activations; returns
-    out (bf16 [T, H])."""
+    [E, N, K/16], one fp32 global scale per tensor), bf16 or (act_mode
+    ACT_FP8_E4M3) per-tensor E4M3 activations; returns out (bf16 [T, H])."""
     _need(x, "x", torch.bfloat16, 2)
     _need(topk_ids, "topk_ids", torch.int32, 2)
     _need(topk_weights, "topk_weights", torch.float32, 2)
@@ -255,14 +265,14 @@ def nvfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_glo
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, 2)
     if workspace is None:
-        workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, ACT_BF16), 1),
+        workspace = torch.empty(max(nvfp4_moe_workspace_size(T, H, I, E, k, act_mode), 1),
                                 dtype=torch.uint8, device=x.device)
     _need(workspace, "workspace", torch.uint8, 1)
-    opts = _opts(events, False)
+    opts = _opts(events, scale_streams_ready)
     _check("nvfp4_moe_forward", lib().nvfp4_moe_forward(
         _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
         _ptr(w13_blocks), _ptr(w13_scales), float(w13_global), _ptr(w13_bias),
-        _ptr(w2_blocks), _ptr(w2_scales), float(w2_global), _ptr(w2_bias), _ptr(out),
+        _ptr(w2_blocks), _ptr(w2_scales), float(w2_global), _ptr(w2_bias), act_mode, _ptr(out),
         _ptr(workspace), workspace.numel(), ctypes.byref(opts) if opts is not None else None,
         _stream(stream)))
     return out

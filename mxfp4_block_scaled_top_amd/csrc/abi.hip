@@ -70,8 +70,10 @@ int moe_shape_check(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32
   return MXFP4_OK;
 }
 
+// nv: NVFP4 weights, whose restaged scale streams take 8 bytes per row and
+// 128-element step instead of 4.
 void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mode,
-          mxfp4_moe_workspace_layout* L) {
+          mxfp4_moe_workspace_layout* L, bool nv = false) {
   const int64_t np = T * k;
   const int64_t nchunks = (np + 1023) / 1024;
   const int bm = act_mode == MXFP4_ACT_BF16 ? mx::kDecodeBM : mx::kPrefillBM;
@@ -101,8 +103,9 @@ void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mod
   }
   L->y = o; o = up(o + (size_t)np * H * 4);
   if (act_mode != MXFP4_ACT_BF16) {
-    L->w13_scale_stream = o; o = up(o + (size_t)mx::scale_stream_bytes(E, mx::gateup_ntiles((int)I), (int)H));
-    L->w2_scale_stream = o; o = up(o + (size_t)mx::scale_stream_bytes(E, mx::down_ntiles((int)H), (int)I));
+    const size_t f = nv ? 2 : 1;
+    L->w13_scale_stream = o; o = up(o + f * (size_t)mx::scale_stream_bytes(E, mx::gateup_ntiles((int)I), (int)H));
+    L->w2_scale_stream = o; o = up(o + f * (size_t)mx::scale_stream_bytes(E, mx::down_ntiles((int)H), (int)I));
   }
   L->total_bytes = o;
 }
@@ -272,14 +275,16 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   int rc = moe_shape_check(T, H, I, E, k, act_mode);
   if (rc) return rc;
   if (nv_globals) {
-    if (act_mode != MXFP4_ACT_BF16)
-      return fail(MXFP4_E_MODE, "%s: NVFP4 weights take bf16 activations only", fn);
-    if (H < 160 || I < 160 || H > 3072 || I > 3072)
-      return fail(MXFP4_E_SHAPE, "%s: NVFP4 weights need 160 <= H, I <= 3072", fn);
+    if (act_mode == MXFP4_ACT_MXFP4)
+      return fail(MXFP4_E_MODE, "%s: NVFP4 weights take bf16 or E4M3 activations", fn);
     if (!std::isfinite(nv_globals[0]) || !std::isfinite(nv_globals[1]))
       return fail(MXFP4_E_SHAPE, "%s: global scales must be finite", fn);
-    if ((int64_t)T * k * (I > H ? I : H) * 2 >= (1LL << 31))
-      return fail(MXFP4_E_SHAPE, "%s: NVFP4 path needs T*k*max(H, I)*2 < 2^31", fn);
+    if (act_mode == MXFP4_ACT_BF16) {
+      if (H < 160 || I < 160 || H > 3072 || I > 3072)
+        return fail(MXFP4_E_SHAPE, "%s: NVFP4 weights with bf16 activations need 160 <= H, I <= 3072", fn);
+      if ((int64_t)T * k * (I > H ? I : H) * 2 >= (1LL << 31))
+        return fail(MXFP4_E_SHAPE, "%s: NVFP4 weights with bf16 activations need T*k*max(H, I)*2 < 2^31", fn);
+    }
   }
   if (T == 0) return ok();
   if (!x || !topk_ids || !topk_weights || !w13_blocks || !w13_scales || !w2_blocks ||
@@ -291,7 +296,7 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
       (w13_bias && !aligned(w13_bias, 8)) || (w2_bias && !aligned(w2_bias, 8)))
     return fail(MXFP4_E_ALIGN, "%s: x/out/blocks need 16-byte, biases 8-byte, logits/ids/weights/scales 4-byte alignment", fn);
   mxfp4_moe_workspace_layout L;
-  plan(T, H, I, E, k, act_mode, &L);
+  plan(T, H, I, E, k, act_mode, &L, nv_globals != nullptr);
   if (!workspace) return fail(MXFP4_E_WORKSPACE, "workspace is null");
   if (!aligned(workspace, 256)) return fail(MXFP4_E_ALIGN, "workspace must be 256-byte aligned");
   if (workspace_bytes < L.total_bytes)
@@ -445,13 +450,26 @@ int nvfp4_moe_forward(const uint16_t* x, int64_t T, int64_t H, int64_t I, int32_
                       const int32_t* topk_ids, const float* topk_weights,
                       const uint8_t* w13_blocks, const uint8_t* w13_scales, float w13_global,
                       const uint16_t* w13_bias, const uint8_t* w2_blocks, const uint8_t* w2_scales,
-                      float w2_global, const uint16_t* w2_bias, uint16_t* out, void* workspace,
-                      size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream) {
+                      float w2_global, const uint16_t* w2_bias, int32_t act_mode, uint16_t* out,
+                      void* workspace, size_t workspace_bytes, const mxfp4_moe_opts* opts, void* stream) {
   const float g[2] = {w13_global, w2_global};
   return moe_run(x, nullptr, T, H, I, E, k, const_cast<int32_t*>(topk_ids),
                  const_cast<float*>(topk_weights), w13_blocks, w13_scales, w13_bias, w2_blocks,
-                 w2_scales, w2_bias, MXFP4_ACT_BF16, out, workspace, workspace_bytes, opts, stream,
+                 w2_scales, w2_bias, act_mode, out, workspace, workspace_bytes, opts, stream,
                  "nvfp4_moe_forward", g);
+}
+
+int nvfp4_moe_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mode,
+                             size_t* bytes) {
+  if (!bytes) return fail(MXFP4_E_NULL, "bytes is null");
+  int rc = moe_shape_check(T, H, I, E, k, act_mode);
+  if (rc) return rc;
+  if (act_mode == MXFP4_ACT_MXFP4)
+    return fail(MXFP4_E_MODE, "nvfp4_moe_workspace_size: NVFP4 weights take bf16 or E4M3 activations");
+  mxfp4_moe_workspace_layout L;
+  plan(T, H, I, E, k, act_mode, &L, true);
+  *bytes = L.total_bytes;
+  return ok();
 }
 
 int mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t act_mode, size_t* bytes) {

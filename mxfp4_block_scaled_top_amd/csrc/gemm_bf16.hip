@@ -310,25 +310,6 @@ constexpr int kMaxHG = 12;             // K-groups per wave: K <= 3072 on this p
 constexpr int kRunDma = 12;            // 1 KB weight DMA instructions per run (8 x 1536 B max)
 // 256 B scale DMA instructions per run: MXFP4 8 x 96 B max, NVFP4 (two
 // scales per 32 elements) 8 x 192 B max
-// Eight E2M1 nibbles (one dword) times a full fp32 factor, as bf16.  The
-// scaled FP4 conversions apply only the exponent field of their scale
-// operand, so an E4M3 block scale (four significant bits) cannot ride on
-// them: the nibbles are converted at unit scale, multiplied in fp32 and
-// rounded to bf16.  Every step is exact: an E2M1 value times an E4M3 value
-// has at most six significant bits and stays inside bf16's normal range.
-__device__ __forceinline__ v8bf fp4x8_times_bf16(uint32_t w, float f) {
-  const v2f p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  const v2f p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  const v2f p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  const v2f p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-  v8bf r;
-  r[0] = (__bf16)(p0[0] * f); r[1] = (__bf16)(p0[1] * f);
-  r[2] = (__bf16)(p1[0] * f); r[3] = (__bf16)(p1[1] * f);
-  r[4] = (__bf16)(p2[0] * f); r[5] = (__bf16)(p2[1] * f);
-  r[6] = (__bf16)(p3[0] * f); r[7] = (__bf16)(p3[1] * f);
-  return r;
-}
-
 template <bool NV> struct RunLayout {
   static constexpr int kScDma = NV ? 6 : 3;
   // (a run's region also covers reads of blocks up to 95 of its last row:

@@ -68,7 +68,10 @@ constexpr int kBK = 128;               // K per step (four MX blocks)
 // 128-byte lines, plus two dwords of E8M0 scales per row.  Otherwise E4M3
 // activations, K steps of 128: 128 B per activation row, 64 B per weight
 // row, one dword of scales per weight row.
-template <int BM, bool A4 = false>
+// NV: NVFP4 weights (E4M3 activations only): the same 64 B of E2M1 codes per
+// weight row and step, two E4M3 scales per 32 elements (8 bytes per row and
+// step instead of 4).
+template <int BM, bool A4 = false, bool NV = false>
 struct Ring {
   static constexpr int kWaves = BM / 16;                // each 64 sorted rows x 64 weight rows
   static constexpr int kThreads = 64 * kWaves;
@@ -80,7 +83,8 @@ struct Ring {
   static constexpr int kAct = BM * kActRow;             // activation bytes per slot
   static constexpr int kW = kAct;                       // offsets inside a slot
   static constexpr int kSc = kAct + kBN * kWRow;
-  static constexpr int kASc = kSc + kBN * 4 * kSub;     // A4: activation scales, 4 B per row and sub-step
+  static constexpr int kScRow = NV ? 8 : 4;             // weight-scale bytes per row and 128-element step
+  static constexpr int kASc = kSc + kBN * kScRow * kSub; // A4: activation scales, 4 B per row and sub-step
   static constexpr int kSlot = kASc + (A4 ? BM * 4 * kSub : 0);
   static constexpr int kActDma = BM * kActRow / 1024 / kWaves;  // 1 KB activation DMAs per wave per step
   static constexpr int kWDma = kBN * kWRow / 1024 / kWaves;     // 1 KB weight DMAs per wave per step
@@ -91,6 +95,7 @@ struct Ring {
   static_assert(kActDma * kWaves * 1024 == BM * kActRow, "copies split over the waves");
   static_assert(kWDma * kWaves * 1024 == kBN * kWRow, "copies split over the waves");
   static_assert(kWaves == 8 && (!A4 || BM == 128), "each wave copies 1/8 of the step's scales");
+  static_assert(!(A4 && NV), "NVFP4 weights take E4M3 activations");
   static_assert((kStages - 2) * kDma <= 63, "vector-memory count range");
   static_assert(kStages - 2 <= 4, "waits cover up to four steps ahead");
   static_assert(kLds <= 160 * 1024, "LDS");
@@ -114,6 +119,7 @@ struct PrefillArgs {
   int scale_word;          // status word holding the per-tensor activation scale (E4M3)
   float* out;              // h [rows, I] (gate_up, E4M3 mode) or y [rows, H] (down), fp32
   uint16_t* out_bf16;      // down: y rounded once to bf16 [rows, H] in place of out, or null
+  float gscale;            // NVFP4 weights: the tensor's global scale (applied to the sums)
   // gate_up with E2M1 activations: h quantised in the epilogue into E2M1
   // blocks [rows, I/32, 16] and step-major E8M0 scales [ceil(I/128), rows, 4]
   uint8_t* h_codes;
@@ -236,9 +242,9 @@ __device__ __forceinline__ float bf16_of(uint2 q, int jj) {
 // (lane%4) ^ ((row/2)%4)).  The activation scales are stored step-major, so a
 // step's scales of the tile's 128 rows are 512 contiguous bytes; wave w
 // copies rows 16w .. 16w+15 with lanes 0-3.
-template <bool GATEUP, int BM, bool A4 = false>
+template <bool GATEUP, int BM, bool A4 = false, bool NV = false>
 struct PrefillCopier {
-  using C = Ring<BM, A4>;
+  using C = Ring<BM, A4, NV>;
   static constexpr int NW = C::kWaves;
   const int* tiles;
   uint8_t* smem;
@@ -287,8 +293,8 @@ struct PrefillCopier {
     }
     // the unit's stream: 1 KB per 128-element sub-step; A4: wave w copies 256 B
     // (lanes 0-15) of sub-step w / 4, else 128 B (lanes 0-7)
-    wsp = a.wsp + ((int64_t)te.x * a.NT + nt) * a.nsteps_s * 1024 +
-          (A4 ? 256 * (wave & 3) + 16 * (lane & 15) : 128 * wave + 16 * (lane & 7));
+    wsp = a.wsp + ((int64_t)te.x * a.NT + nt) * a.nsteps_s * (kBN * C::kScRow) +
+          (A4 ? 256 * (wave & 3) + 16 * (lane & 15) : NV ? 256 * wave + 16 * (lane & 15) : 128 * wave + 16 * (lane & 7));
   }
 
   // copies of the next step into its slot, then advance
@@ -322,8 +328,10 @@ struct PrefillCopier {
       if (lane < 16) __builtin_amdgcn_global_load_lds(wsp + ss * 1024, dst + C::kSc + 256 * wave, 16, 0, 0);
       if (lane < 8)
         __builtin_amdgcn_global_load_lds(ascp + ss * a.asc_step, dst + C::kASc + 128 * wave, 16, 0, 0);
-    } else if (lane < 8) {
-      __builtin_amdgcn_global_load_lds(wsp + step * 1024, dst + C::kSc + 128 * wave, 16, 0, 0);
+    } else if (lane < 2 * C::kScRow) {
+      // (NVFP4: 256 B per wave, the 8 scale bytes of rows 32w .. 32w+31)
+      __builtin_amdgcn_global_load_lds(wsp + step * (kBN * C::kScRow), dst + C::kSc + 32 * C::kScRow * wave, 16,
+                                       0, 0);
     }
   }
   // the weight copies of the next step
@@ -359,13 +367,33 @@ struct PrefillCopier {
 #define MX_RD_OUTS                                                                   \
   "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(xb0), "=&v"(xb1), "=&v"(xb2), "=&v"(xb3), \
       "=&v"(wq0), "=&v"(wq1), "=&v"(wq2), "=&v"(wq3), "=&v"(sb0), "=&v"(sb1), "=&v"(sb2), "=&v"(sb3)
-template <bool GATEUP>
+// NV (NVFP4 weights): 2 scale bytes per row (the step's 16-element blocks 2g
+// and 2g+1), rows 8 B apart.
+template <bool GATEUP, bool NV = false>
 __device__ __forceinline__ void lds_step_reads(uint32_t aa0, uint32_t aa1, uint32_t ww, uint32_t ss,
                                                v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3,
                                                v4u_t& xb0, v4u_t& xb1, v4u_t& xb2, v4u_t& xb3,
                                                v4u_t& wq0, v4u_t& wq1, v4u_t& wq2, v4u_t& wq3,
                                                uint32_t& sb0, uint32_t& sb1, uint32_t& sb2, uint32_t& sb3) {
-  if (GATEUP) {
+  if (NV && GATEUP) {
+    asm volatile(MX_RD_ACT
+                 "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
+                 "ds_read_b128 %10, %18 offset:8192\n\tds_read_b128 %11, %18 offset:9216\n\t"
+                 "ds_read_u16 %12, %19\n\tds_read_u16 %13, %19 offset:128\n\t"
+                 "ds_read_u16 %14, %19 offset:1024\n\tds_read_u16 %15, %19 offset:1152\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_RD_OUTS
+                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
+  } else if (NV) {
+    asm volatile(MX_RD_ACT
+                 "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
+                 "ds_read_b128 %10, %18 offset:2048\n\tds_read_b128 %11, %18 offset:3072\n\t"
+                 "ds_read_u16 %12, %19\n\tds_read_u16 %13, %19 offset:128\n\t"
+                 "ds_read_u16 %14, %19 offset:256\n\tds_read_u16 %15, %19 offset:384\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_RD_OUTS
+                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
+  } else if (GATEUP) {
     asm volatile(MX_RD_ACT
                  "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
                  "ds_read_b128 %10, %18 offset:8192\n\tds_read_b128 %11, %18 offset:9216\n\t"
@@ -468,14 +496,20 @@ __device__ __forceinline__ void lds_half_reads_a4(bool gateup, uint32_t aa, uint
 // A4: E2M1 activations with E8M0 block scales; both operands of the
 // block-scaled MFMA are FP4 and carry their own scales, and the epilogue has
 // no per-tensor factor.
-template <bool GATEUP, int BM, bool A4 = false>
-__global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(PrefillArgs a,
-                                                                              const int* __restrict__ tiles,
-                                                                              int* status) {
-  using C = Ring<BM, A4>;
+// NV: NVFP4 weights with E4M3 activations; both GEMMs then expand their
+// operands exactly to bf16 (an E4M3 block scale cannot ride on the
+// block-scaled MFMA, whose scales are E8M0) and the global scale joins the
+// per-tensor activation scale in the epilogue.
+template <bool GATEUP, int BM, bool A4 = false, bool NV = false>
+__global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_kernel(PrefillArgs a,
+                                                                                  const int* __restrict__ tiles,
+                                                                                  int* status) {
+  using C = Ring<BM, A4, NV>;
+  constexpr bool EXP = GATEUP || NV;   // operands expanded to bf16, v_mfma_f32_16x16x32_bf16
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
   const int num_units = status[kStNumTiles] * a.NT;
-  const float sx = A4 ? 1.0f : __uint_as_float((uint32_t)status[a.scale_word]);
+  float sx = A4 ? 1.0f : __uint_as_float((uint32_t)status[a.scale_word]);
+  if constexpr (NV) sx *= a.gscale;
   // this block's units: u0, u0 + G, ... (my_units of them) in the schedule
   int u0, G, my_units;
   if (a.sched_xcd) {
@@ -494,7 +528,7 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
-  PrefillCopier<GATEUP, BM, A4> cp;
+  PrefillCopier<GATEUP, BM, A4, NV> cp;
   cp.init(a, tiles, smem, wave, lane, u0, G, my_units);
 
   // ---------------- compute: 64 sorted rows x 64 weight rows ----------------
@@ -511,13 +545,14 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
   // in one pass over 64 four-byte banks; for those pairs to hit distinct
   // banks the bf16 path's odd lane groups read chunk 2g+1 first (their K
   // order within the block is then 16..31, 0..15, for both operands).
-  const int c0 = (GATEUP ? 2 * g + (g & 1) : g) ^ (r & 7);
-  const int c1 = (GATEUP ? 2 * g + 1 - (g & 1) : 4 + g) ^ (r & 7);
+  const int c0 = (EXP ? 2 * g + (g & 1) : g) ^ (r & 7);
+  const int c1 = (EXP ? 2 * g + 1 - (g & 1) : 4 + g) ^ (r & 7);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const uint32_t a0 = lds0 + (64 * wm + r) * kBK + 16 * c0;
   const uint32_t a1 = lds0 + (64 * wm + r) * kBK + 16 * c1;
   const uint32_t w0 = lds0 + C::kW + lrow0 * 64 + 16 * wslot;
-  const uint32_t s0 = lds0 + C::kSc + lrow0 * 4 + g;   // scale of MX block g of the step
+  // scale of MX block g of the step (NVFP4: of its 16-element blocks 2g, 2g+1)
+  const uint32_t s0 = lds0 + C::kSc + lrow0 * C::kScRow + (NV ? 2 * g : g);
   // A4 (rows of 128 B, eight 16-byte slots swizzled by row % 8 = r % 8):
   // MX block 4h + g of a row sits in slot (4h + g) ^ (r % 8); the scales of
   // half h sit in the step's second 128-element scale chunk (weights: 1 KB
@@ -655,17 +690,17 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
         }
       }
     } else {
-      if (GATEUP) {
+      if (GATEUP && !NV) {
         lds_step_issue_gateup(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3, sb0,
                               sb1, sb2, sb3);
         lds_wait_first(xa0, xa1, xa2, xa3, wq0, wq1, wq2, wq3, sb0, sb1, sb2, sb3);
       } else {
-        lds_step_reads<GATEUP>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3,
-                               sb0, sb1, sb2, sb3);
+        lds_step_reads<GATEUP, NV>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3,
+                                   sb0, sb1, sb2, sb3);
       }
       const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
       v4u_t wq[4] = {wq0, wq1, wq2, wq3};
-      if (GATEUP && (g & 1)) {
+      if (EXP && (g & 1)) {
         // odd lane groups hold activation K 16..31 of the block in xa: take
         // the weight dwords in the same order
 #pragma unroll
@@ -673,7 +708,21 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
       }
       const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
       const bool valid = 4 * cstep + g < a.nb;        // this lane's MX block lies inside K
-      if (GATEUP) {
+      // weights of chunk q (elements 8q..8q+7 of the lane's block, 8(q^2).. for
+      // odd g) of weight group rg, exactly as bf16: MXFP4 through the scaled
+      // conversion with the block's E8M0 scale; NVFP4 times the E4M3 scale of
+      // the chunk's 16-element block (the low byte of sb holds block 2g)
+      auto expand_w = [&](int rg, int q) __attribute__((always_inline)) {
+        if constexpr (NV) {
+          const uint32_t sub = (uint32_t)((q >> 1) ^ (g & 1));
+          const float f = valid ? e4m3_to_f32((sb[rg] >> (8 * sub)) & 0xffu) : 0.0f;
+          return fp4x8_times_bf16(wq[rg][q], f);
+        } else {
+          const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
+          return fp4x8_to_bf16(wq[rg][q], f);
+        }
+      };
+      if (EXP) {
         // lane group g holds K [32g, 32g+32) of the step (its own MX block);
         // MFMA q takes elements 8q..8q+7 of it (8(q^2).. for odd g), in the
         // same order for both operands; MFMAs 2-3 use the chunks read last
@@ -690,8 +739,7 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
             }
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-              const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
-              const v8bf A = fp4x8_to_bf16(wq[rg][q], f);
+              const v8bf A = expand_w(rg, q);
 #pragma unroll
               for (int tg = 0; tg < 4; ++tg)
                 acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[tg], acc[rg][tg], 0, 0, 0);
@@ -707,10 +755,7 @@ __global__ __launch_bounds__((Ring<BM, A4>::kThreads)) void prefill_gemm_kernel(
             const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
             v8bf A[4];
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-              const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
-              A[rg] = fp4x8_to_bf16(wq[rg][q], f);
-            }
+            for (int rg = 0; rg < 4; ++rg) A[rg] = expand_w(rg, q);
 #pragma unroll
             for (int tg = 0; tg < 3; ++tg) {
               if (tg >= ntg) break;
@@ -957,8 +1002,152 @@ __global__ __launch_bounds__(256) void scale_stream_kernel(const uint8_t* __rest
   }
 }
 
+// NVFP4 weights: per (expert, n-tile, 128-element K step) 2 KB holding the 8
+// E4M3 scale bytes (16-element blocks 8 step .. 8 step + 7) of each of the
+// unit's 256 LDS rows in row order; blocks past K are 0.  One thread per
+// (unit, LDS row) walks the row's scale bytes in order (dword loads when the
+// row's K/16 bytes keep them aligned, else 16-bit ones) and writes each step's
+// 8 bytes, the 256 threads of a block writing 2 KB contiguously per step.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void scale_stream_nv_kernel(const uint8_t* __restrict__ ws, int R, int nout,
+                                                              int nb16, int NT, int nsteps, int64_t n,
+                                                              uint2* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int lr = (int)(i & (kBN - 1));
+  const int64_t unit = i >> 8;                // e * NT + nt
+  const int e = (int)(unit / NT), nt = (int)(unit - (int64_t)e * NT);
+  const uint8_t* src = ws + ((int64_t)e * R + weight_row<GATEUP>(lr, nt, nout)) * nb16;
+  uint2* dst = out + unit * nsteps * kBN + lr;
+  const bool dw = (nb16 & 3) == 0;            // rows start 4-byte aligned
+  for (int step = 0; step < nsteps; ++step) {
+    const int b0 = 8 * step;
+    uint32_t lo, hi;
+    if (b0 + 8 <= nb16) {
+      if (dw) {
+        lo = *reinterpret_cast<const uint32_t*>(src + b0);
+        hi = *reinterpret_cast<const uint32_t*>(src + b0 + 4);
+      } else {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(src + b0);
+        lo = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        hi = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+      }
+    } else {                                  // the step past K: its real blocks, then 0
+      lo = hi = 0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint32_t v = b0 + b < nb16 ? src[b0 + b] : 0u;
+        if (b < 4) lo |= v << (8 * b);
+        else hi |= v << (8 * (b - 4));
+      }
+    }
+    dst[(int64_t)step * kBN] = make_uint2(lo, hi);
+  }
+}
+
+// The same stream, one block per (expert, n-tile) with the unit's rows staged
+// in LDS (K <= 3072: 256 rows x K/16 bytes <= 48 KB): the rows of a half
+// (gate_up: 128 gate rows, 128 up rows; down: 256 rows) are contiguous in
+// the tensor, so they are loaded with consecutive 16-bit or 32-bit loads;
+// LDS rows past the matrix are zero (never stored).  Then every step's 2 KB
+// is written by the block's 256 threads, one LDS row each.
+constexpr int kNvStageMaxNb16 = 192;   // 48 KB of LDS: K <= 3072
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void scale_stream_nv_lds_kernel(const uint8_t* __restrict__ ws, int R, int nout,
+                                                                  int nb16, int NT, int nsteps,
+                                                                  uint2* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t rows[];   // 256 x nb16 bytes
+  const int unit = blockIdx.x, e = unit / NT, nt = unit - e * NT;
+  const int t = threadIdx.x;
+  constexpr int kHalves = GATEUP ? 2 : 1, kHalfRows = kBN / kHalves;
+#pragma unroll
+  for (int h = 0; h < kHalves; ++h) {
+    const int first = nt * kHalfRows;                                  // first row of the half's block
+    const int nv = max(0, min(kHalfRows, nout - first));               // rows inside the matrix
+    const uint8_t* src = ws + ((int64_t)e * R + (h ? nout : 0) + first) * nb16;
+    uint8_t* dst = rows + h * kHalfRows * nb16;
+    const int bytes = nv * nb16, all = kHalfRows * nb16;
+    // batches of 12 loads per thread issued before their LDS stores
+    constexpr int kB = 12;
+    if ((bytes & 3) == 0) {     // whole dwords (the block start is 4-byte aligned: nb16 is even)
+      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+      uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+      const int nd = all / 4;
+      for (int d0 = t; d0 < nd; d0 += 256 * kB) {
+        uint32_t v[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+          const int d = d0 + 256 * j;
+          v[j] = d < nd && 4 * d < bytes ? s32[d] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j)
+          if (d0 + 256 * j < nd) d32[d0 + 256 * j] = v[j];
+      }
+    } else {
+      const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+      uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+      const int nd = all / 2;
+      for (int d0 = t; d0 < nd; d0 += 256 * kB) {
+        uint16_t v[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+          const int d = d0 + 256 * j;
+          v[j] = d < nd && 2 * d < bytes ? s16[d] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j)
+          if (d0 + 256 * j < nd) d16[d0 + 256 * j] = v[j];
+      }
+    }
+  }
+  __syncthreads();
+  const uint8_t* row = rows + t * nb16;
+  uint2* dst = out + (int64_t)unit * nsteps * kBN + t;
+  for (int step = 0; step < nsteps; ++step) {
+    const int b0 = 8 * step;
+    uint32_t lo = 0, hi = 0;
+    if (b0 + 8 <= nb16 && (nb16 & 3) == 0) {
+      lo = *reinterpret_cast<const uint32_t*>(row + b0);
+      hi = *reinterpret_cast<const uint32_t*>(row + b0 + 4);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint32_t v = b0 + b < nb16 ? row[b0 + b] : 0u;
+        if (b < 4) lo |= v << (8 * b);
+        else hi |= v << (8 * (b - 4));
+      }
+    }
+    dst[(int64_t)step * kBN] = make_uint2(lo, hi);
+  }
+}
+
 hipError_t launch_scale_stream(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, bool gateup,
                                hipStream_t s) {
+  if (w.nvfp4) {
+    const int R = gateup ? 2 * sh.I : sh.H, nout = gateup ? sh.I : sh.H;
+    const int K = gateup ? sh.H : sh.I;
+    const int NT = gateup ? (sh.I + kBN / 2 - 1) / (kBN / 2) : (sh.H + kBN - 1) / kBN;
+    const int nsteps = (K / kBlockElems + 3) / 4;
+    uint2* out = reinterpret_cast<uint2*>(gateup ? ws.w13_stream : ws.w2_stream);
+    const int nb16 = K / 16;
+    if (sh.E * NT <= 0) return hipSuccess;
+    if (nb16 <= kNvStageMaxNb16) {
+      const size_t lds = (size_t)kBN * nb16;
+      if (gateup)
+        scale_stream_nv_lds_kernel<true><<<sh.E * NT, 256, lds, s>>>(w.w13_scales, R, nout, nb16, NT, nsteps, out);
+      else
+        scale_stream_nv_lds_kernel<false><<<sh.E * NT, 256, lds, s>>>(w.w2_scales, R, nout, nb16, NT, nsteps, out);
+      return hipGetLastError();
+    }
+    const int64_t n = (int64_t)sh.E * NT * kBN;   // one thread per (unit, LDS row)
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (gateup)
+      scale_stream_nv_kernel<true><<<grid, 256, 0, s>>>(w.w13_scales, R, nout, K / 16, NT, nsteps, n, out);
+    else
+      scale_stream_nv_kernel<false><<<grid, 256, 0, s>>>(w.w2_scales, R, nout, K / 16, NT, nsteps, n, out);
+    return hipGetLastError();
+  }
   const int R = gateup ? 2 * sh.I : sh.H, nout = gateup ? sh.I : sh.H;
   const int K = gateup ? sh.H : sh.I, nb = K / kBlockElems;
   const int NT = gateup ? (sh.I + kBN / 2 - 1) / (kBN / 2) : (sh.H + kBN - 1) / kBN;
@@ -977,7 +1166,7 @@ hipError_t launch_scale_stream(const MoeShape& sh, const MoeWeights& w, const Ws
   return hipGetLastError();
 }
 
-template <bool GATEUP, bool A4 = false>
+template <bool GATEUP, bool A4 = false, bool NV = false>
 static hipError_t launch_prefill(const PrefillArgs& args, const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
   // one block per compute unit: the LDS ring takes most of a unit's LDS
   int dev = 0, cus = 0;
@@ -988,8 +1177,8 @@ static hipError_t launch_prefill(const PrefillArgs& args, const MoeShape& sh, co
   // the expert-major XCD schedule needs the tile words (bounded list) and
   // a grid of whole XCDs
   a.sched_xcd = cus % 8 == 0 && max_tiles((int64_t)sh.T * sh.k, sh.E, kPrefillBM) <= kTileWordMaxBound;
-  prefill_gemm_kernel<GATEUP, kPrefillBM, A4><<<cus, Ring<kPrefillBM, A4>::kThreads, 0, s>>>(a, ws.tiles,
-                                                                                            ws.status);
+  prefill_gemm_kernel<GATEUP, kPrefillBM, A4, NV><<<cus, Ring<kPrefillBM, A4, NV>::kThreads, 0, s>>>(
+      a, ws.tiles, ws.status);
   return hipGetLastError();
 }
 
@@ -1010,6 +1199,10 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
   a.act_ld = sh.H;
   a.scale_word = kStScaleX;
   a.out = static_cast<float*>(ws.h);
+  if (w.nvfp4) {
+    a.gscale = w.w13_global;
+    return launch_prefill<true, false, true>(a, sh, ws, s);
+  }
   return launch_prefill<true>(a, sh, ws, s);
 }
 
@@ -1031,6 +1224,10 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
   a.scale_word = kStScaleH;
   a.out = ws.y;
   a.out_bf16 = out_bf16;
+  if (w.nvfp4) {
+    a.gscale = w.w2_global;
+    return launch_prefill<false, false, true>(a, sh, ws, s);
+  }
   return launch_prefill<false>(a, sh, ws, s);
 }
 

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 3
+    assert L.mxfp4_abi_version() == 4
     assert L.mxfp4_status_string(0) == b"ok"
     assert L.mxfp4_status_string(E_WORKSPACE) == b"workspace too small"
     assert L.mxfp4_status_string(99) == b"unknown status"
@@ -184,17 +184,37 @@ def test_nvfp4_moe_forward_rejects_bad_arguments_without_touching_memory(L):
     f = L.nvfp4_moe_forward
     fake = _fake
     args = [fake(1), 4, 2880, 2880, 128, 4, fake(2), fake(3), fake(4), fake(5), ctypes.c_float(1.0), None,
-            fake(6), fake(7), ctypes.c_float(1.0), None, fake(8), fake(9), ctypes.c_size_t(1 << 30), None, None]
+            fake(6), fake(7), ctypes.c_float(1.0), None, 0, fake(8), fake(9), ctypes.c_size_t(1 << 30), None,
+            None]
     a = list(args); a[8] = None                       # null w13_blocks
     assert f(*a) == E_NULL
-    a = list(args); a[2] = 4096; a[3] = 4096          # beyond the NVFP4 limit
+    a = list(args); a[2] = 4096; a[3] = 4096          # beyond the bf16-activation NVFP4 limit
     assert f(*a) == E_SHAPE
-    a = list(args); a[2] = 128                        # below the NVFP4 limit
+    a = list(args); a[2] = 128                        # below the bf16-activation NVFP4 limit
     assert f(*a) == E_SHAPE
     a = list(args); a[10] = ctypes.c_float(float("nan"))
     assert f(*a) == E_SHAPE
     a = list(args); a[2] = 2880 + 16                  # H % 32
     assert f(*a) == E_SHAPE
+    a = list(args); a[16] = 2                         # MXFP4 activations: not with NVFP4 weights
+    assert f(*a) == E_MODE
+    a = list(args); a[16] = 5
+    assert f(*a) == E_MODE
+    # E4M3 activations lift the decode kernel's 3072 limit; a small workspace is then the error
+    a = list(args); a[16] = 1; a[2] = 4096; a[3] = 4096; a[19] = ctypes.c_size_t(1024)
+    assert f(*a) == E_WORKSPACE
+
+
+def test_nvfp4_workspace_size_doubles_the_scale_streams(L):
+    n_mx, n_nv, n_bf = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.mxfp4_moe_workspace_size(2048, 2880, 2880, 128, 4, 1, ctypes.byref(n_mx)) == 0
+    assert L.nvfp4_moe_workspace_size(2048, 2880, 2880, 128, 4, 1, ctypes.byref(n_nv)) == 0
+    streams = 128 * (23 + 12) * 23 * 1024      # w13 (23 n-tiles) + w2 (12), 23 K steps, 1 KB each
+    assert n_nv.value - n_mx.value >= streams
+    assert L.nvfp4_moe_workspace_size(32, 2880, 2880, 128, 4, 0, ctypes.byref(n_bf)) == 0
+    assert L.mxfp4_moe_workspace_size(32, 2880, 2880, 128, 4, 0, ctypes.byref(n_mx)) == 0
+    assert n_bf.value == n_mx.value
+    assert L.nvfp4_moe_workspace_size(32, 2880, 2880, 128, 4, 2, ctypes.byref(n_bf)) == E_MODE
 
 
 def test_stream_read_validation(L):
