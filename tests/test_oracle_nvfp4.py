@@ -7,6 +7,7 @@ MXFP4 decode and to the page's property table.
 """
 
 import numpy as np
+import pytest
 
 import oracle
 from oracle import nvfp4
@@ -65,7 +66,8 @@ def test_element_scale_and_global_placement():
     assert np.array_equal(w, want)
 
 
-def test_moe_forward_with_nvfp4_equals_mxfp4_for_the_same_values():
+@pytest.mark.parametrize("act_mode", [oracle.ACT_BF16, oracle.ACT_FP8_E4M3])
+def test_moe_forward_with_nvfp4_equals_mxfp4_for_the_same_values(act_mode):
     rng = np.random.default_rng(3)
     E, H, I, T, k = 4, 64, 96, 7, 2
     w13 = rng.integers(0, 256, (E, 2 * I, H // 32, 16)).astype(np.uint8)
@@ -77,14 +79,21 @@ def test_moe_forward_with_nvfp4_equals_mxfp4_for_the_same_values():
     x = (rng.standard_normal((T, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     ids = rng.integers(0, E, (T, k)).astype(np.int32)
     wts = rng.random((T, k))
-    ref = oracle.moe_forward_routed(x, ids, wts, w13, s13, b13, w2, s2, b2)
+    ref = oracle.moe_forward_routed(x, ids, wts, w13, s13, b13, w2, s2, b2, act_mode=act_mode)
     n13, m13 = _mx_as_nv(w13, s13)
     n2, m2 = _mx_as_nv(w2, s2)
-    got = oracle.moe_forward_routed(x, ids, wts, n13, m13, b13, n2, m2, b2,
+    got = oracle.moe_forward_routed(x, ids, wts, n13, m13, b13, n2, m2, b2, act_mode=act_mode,
                                     weight_format=("nvfp4", 1.0, 1.0))
     assert np.array_equal(got["out"], ref["out"])
     # a power-of-two global scale of w2 scales y minus its bias exactly
-    got2 = oracle.moe_forward_routed(x, ids, wts, n13, m13, b13, n2, m2, b2,
+    got2 = oracle.moe_forward_routed(x, ids, wts, n13, m13, b13, n2, m2, b2, act_mode=act_mode,
                                      weight_format=("nvfp4", 1.0, 4.0))
     bias = oracle.bf16_bits_to_f64(b2)[ids]
     assert np.array_equal(got2["y"] - bias, 4.0 * (ref["y"] - bias))
+    # a power-of-two global scale of w13 is the MXFP4 layer with every w13
+    # scale byte raised by its exponent (the weights are the same values)
+    got3 = oracle.moe_forward_routed(x, ids, wts, n13, m13, b13, n2, m2, b2, act_mode=act_mode,
+                                     weight_format=("nvfp4", 8.0, 1.0))
+    ref3 = oracle.moe_forward_routed(x, ids, wts, w13, s13 + 3, b13, w2, s2, b2, act_mode=act_mode)
+    assert np.array_equal(got3["out"], ref3["out"])
+    assert not np.array_equal(got3["out"], ref["out"])
