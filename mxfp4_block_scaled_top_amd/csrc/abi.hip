@@ -65,6 +65,7 @@ int moe_shape_check(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32
   if (E < 1 || E > 512) return fail(MXFP4_E_SHAPE, "E=%d outside [1, 512]", E);
   if (k < 1 || k > 16 || k > E) return fail(MXFP4_E_SHAPE, "k=%d outside [1, min(E, 16)]", k);
   const int64_t npairs = T * k;
+  // (64-row tiles are taken only below 64 E pairs: far inside the limit)
   const int bm = act_mode == MXFP4_ACT_BF16 ? mx::kDecodeBM : mx::kPrefillBM;
   if (mx::max_tiles(npairs, E, bm) > 65535) return fail(MXFP4_E_SHAPE, "T*k=%lld gives too many row tiles", (long long)npairs);
   return MXFP4_OK;
@@ -76,7 +77,12 @@ void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mod
           mxfp4_moe_workspace_layout* L, bool nv = false) {
   const int64_t np = T * k;
   const int64_t nchunks = (np + 1023) / 1024;
-  const int bm = act_mode == MXFP4_ACT_BF16 ? mx::kDecodeBM : mx::kPrefillBM;
+  // E4M3 activations: room for the 64-row tiles of NVFP4 weights with
+  // either weight format, so that both share the layout up to the scale
+  // streams
+  const int bm = act_mode == MXFP4_ACT_BF16       ? mx::kDecodeBM
+                 : act_mode == MXFP4_ACT_FP8_E4M3 ? mx::prefill_bm(np, E, true)
+                                                  : mx::kPrefillBM;
   size_t o = 0;
   memset(L, 0, sizeof(*L));
   L->status = o; o = up(o + mx::kStWords * 4);
@@ -316,8 +322,8 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   }
   const bool fp8 = act_mode == MXFP4_ACT_FP8_E4M3;
   const bool a4 = act_mode == MXFP4_ACT_MXFP4;
-  const int bm = act_mode == MXFP4_ACT_BF16 ? mx::kDecodeBM : mx::kPrefillBM;
   const int64_t npairs = T * k;
+  const int bm = act_mode == MXFP4_ACT_BF16 ? mx::kDecodeBM : mx::prefill_bm(npairs, E, nv_globals != nullptr);
   const int64_t bound = mx::max_tiles(npairs, E, bm);
 
   auto mark = [&](int stage) -> hipError_t {
@@ -526,13 +532,14 @@ int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8
   w.w2_blocks = w_blocks;
   w.w2_scales = w_scales;
   w.w2_bias = bias;
-  const int64_t bound = mx::max_tiles(M, 1, mx::kPrefillBM);
+  const int bm = mx::kPrefillBM;
+  const int64_t bound = mx::max_tiles(M, 1, bm);
 #define MX_STEP(call, what)                      \
   do {                                           \
     e = (call);                                  \
     if (e != hipSuccess) return hip_fail(e, what); \
   } while (0)
-  MX_STEP(mx::launch_dense_tiles((int)M, mx::kPrefillBM, (int)bound, ws.status, ws.tiles, ws.inv, s),
+  MX_STEP(mx::launch_dense_tiles((int)M, bm, (int)bound, ws.status, ws.tiles, ws.inv, s),
           "linear tiles launch");
   if (a4) {
     // per-row 32-element blocks of x (the rows' K is the quantiser's H)

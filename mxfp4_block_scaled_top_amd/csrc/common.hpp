@@ -54,12 +54,11 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(s << 23);
 }
 
-// OCP E4M3 code -> fp32 (exact; the NaN codes S.1111.111 are not expected
-// here and decode as +-480).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-  return (c & 0x80u) ? -mag : mag;
+// Two OCP E4M3 codes (the low two bytes of c) -> fp32, by the gfx950
+// conversion at unit scale: exact for every finite code (subnormals m * 2^-9
+// included); the NaN codes S.1111.111 are not expected here.
+__device__ __forceinline__ v2f e4m3x2_to_f32(uint32_t c) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
 }
 
 // OCP E4M3 code of an fp32 value q: round to nearest, ties to even mantissa,

@@ -614,8 +614,9 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
       if (NV) {
         // E4M3 block scales, applied whole (mantissa included) below
         const uint32_t sw = (spk[jj / 2] >> (16 * (jj % 2))) & 0xffffu;
-        f0 = in_k ? e4m3_to_f32(sw & 0xffu) : 0.0f;
-        f1 = in_k ? e4m3_to_f32(sw >> 8) : 0.0f;
+        const v2f fs = e4m3x2_to_f32(sw);
+        f0 = in_k ? fs[0] : 0.0f;
+        f1 = in_k ? fs[1] : 0.0f;
       } else {
         const uint32_t sc = (spk[jj / 4] >> (8 * (jj % 4))) & 0xffu;
         f0 = f1 = e8m0_to_f32(in_k ? sc : 0u);

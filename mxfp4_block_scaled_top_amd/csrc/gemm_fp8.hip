@@ -71,9 +71,11 @@ constexpr int kBK = 128;               // K per step (four MX blocks)
 // NV: NVFP4 weights (E4M3 activations only): the same 64 B of E2M1 codes per
 // weight row and step, two E4M3 scales per 32 elements (8 bytes per row and
 // step instead of 4).
+// BM = 64 (narrow tiles, E4M3 activations): eight waves each take all 64
+// sorted rows and 32 of the 256 weight rows; six slots of 25 KB.
 template <int BM, bool A4 = false, bool NV = false>
 struct Ring {
-  static constexpr int kWaves = BM / 16;                // each 64 sorted rows x 64 weight rows
+  static constexpr int kWaves = 8;                      // 64 sorted rows x (BM 128: 64, BM 64: 32) weight rows
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kK = A4 ? 2 * kBK : kBK;         // K per step
   static constexpr int kSub = kK / kBK;                 // 128-element sub-steps per step (scale dwords per row)
@@ -94,7 +96,7 @@ struct Ring {
   static constexpr int kLds = kStages * kSlot;
   static_assert(kActDma * kWaves * 1024 == BM * kActRow, "copies split over the waves");
   static_assert(kWDma * kWaves * 1024 == kBN * kWRow, "copies split over the waves");
-  static_assert(kWaves == 8 && (!A4 || BM == 128), "each wave copies 1/8 of the step's scales");
+  static_assert((BM == 128 || BM == 64) && (!A4 || BM == 128), "tile heights");
   static_assert(!(A4 && NV), "NVFP4 weights take E4M3 activations");
   static_assert((kStages - 2) * kDma <= 63, "vector-memory count range");
   static_assert(kStages - 2 <= 4, "waits cover up to four steps ahead");
@@ -416,6 +418,55 @@ __device__ __forceinline__ void lds_step_reads(uint32_t aa0, uint32_t aa1, uint3
 #undef MX_RD_ACT
 #undef MX_RD_OUTS
 
+// Narrow tiles (BM = 64): the 8 activation reads and, per wave, two weight
+// groups (gate_up: its 16 gate rows and their 16 up rows, LDS rows +0 and
+// +128; down: rows +0 and +16) with their scales (NV: 2 bytes per row).
+#define MX_RD_ACT_N                                                                  \
+  "ds_read_b128 %0, %12\n\tds_read_b128 %4, %13\n\t"                               \
+  "ds_read_b128 %1, %12 offset:2048\n\tds_read_b128 %5, %13 offset:2048\n\t"       \
+  "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %6, %13 offset:4096\n\t"       \
+  "ds_read_b128 %3, %12 offset:6144\n\tds_read_b128 %7, %13 offset:6144\n\t"
+#define MX_RD_OUTS_N                                                                 \
+  "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(xb0), "=&v"(xb1), "=&v"(xb2), "=&v"(xb3), \
+      "=&v"(wq0), "=&v"(wq1), "=&v"(sb0), "=&v"(sb1)
+template <bool GATEUP, bool NV>
+__device__ __forceinline__ void lds_step_reads_narrow(uint32_t aa0, uint32_t aa1, uint32_t ww, uint32_t ss,
+                                                      v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3,
+                                                      v4u_t& xb0, v4u_t& xb1, v4u_t& xb2, v4u_t& xb3,
+                                                      v4u_t& wq0, v4u_t& wq1, uint32_t& sb0, uint32_t& sb1) {
+  if (GATEUP && NV) {
+    asm volatile(MX_RD_ACT_N
+                 "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:8192\n\t"
+                 "ds_read_u16 %10, %15\n\tds_read_u16 %11, %15 offset:1024\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_RD_OUTS_N
+                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
+  } else if (GATEUP) {
+    asm volatile(MX_RD_ACT_N
+                 "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:8192\n\t"
+                 "ds_read_u8 %10, %15\n\tds_read_u8 %11, %15 offset:512\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_RD_OUTS_N
+                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
+  } else if (NV) {
+    asm volatile(MX_RD_ACT_N
+                 "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:1024\n\t"
+                 "ds_read_u16 %10, %15\n\tds_read_u16 %11, %15 offset:128\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_RD_OUTS_N
+                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
+  } else {
+    asm volatile(MX_RD_ACT_N
+                 "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:1024\n\t"
+                 "ds_read_u8 %10, %15\n\tds_read_u8 %11, %15 offset:64\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : MX_RD_OUTS_N
+                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
+  }
+}
+#undef MX_RD_ACT_N
+#undef MX_RD_OUTS_N
+
 // gate_up variant in two phases: the 16 reads are issued in the order the
 // MFMAs consume them (scales, weights, then the activation chunks of MFMAs
 // 0-1, then those of MFMAs 2-3), and the caller waits for the first twelve
@@ -532,12 +583,16 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
   cp.init(a, tiles, smem, wave, lane, u0, G, my_units);
 
   // ---------------- compute: 64 sorted rows x 64 weight rows ----------------
-  const int wm = wave >> 2, wn = wave & 3;
+  // (narrow tiles: 64 sorted rows x 32 weight rows, every wave all 64 rows)
+  constexpr bool NARROW = BM == 64;
+  constexpr int kRG = NARROW ? 2 : 4;               // 16-row weight groups per wave
+  static_assert(!NARROW || !A4, "narrow tiles take E4M3 activations");
+  const int wm = NARROW ? 0 : wave >> 2, wn = NARROW ? wave : wave & 3;
   const int r = lane & 15, g = lane >> 4;
   // LDS weight row of this lane in the wave's first 16-row group; the others
   // follow at fixed offsets (gate_up: groups 0, 1 gate rows, 2, 3 the
-  // matching up rows)
-  const int lrow0 = (GATEUP ? 32 * wn : 64 * wn) + r;
+  // matching up rows; narrow gate_up: group 0 gate rows, 1 the up rows)
+  const int lrow0 = (GATEUP ? (NARROW ? 16 : 32) * wn : (NARROW ? 32 : 64) * wn) + r;
   const int wslot = g ^ ((r >> 1) & 3);             // slot of MX block g in these rows
   // activation chunks: the bf16 path takes K [32g, 32g+32) = chunks 2g, 2g+1,
   // the block-scaled path chunks g and 4+g; the row's swizzle is row%8 = r%8.
@@ -589,14 +644,15 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
     // never stored and not loaded)
     const uint16_t* bias_e = a.bias + (size_t)e * a.R;
 #pragma unroll
-    for (int jp = 0; jp < 4; jp += 2) {
+    for (int jp = 0; jp < kRG; jp += 2) {
       // groups jp and jp + 1 (16 rows each); a group past nout reads group jp's
       // rows again and is zeroed (never stored)
       int n0[2], off[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = jp + h;
-        n0[h] = GATEUP ? nt * (kBN / 2) + 32 * wn + 16 * (j >> 1) : nt * kBN + 64 * wn + 16 * j;
+        n0[h] = GATEUP ? nt * (kBN / 2) + (NARROW ? 16 : 32) * wn + 16 * (j >> 1)
+                       : nt * kBN + (NARROW ? 32 : 64) * wn + 16 * j;
         off[h] = (GATEUP && (j & 1) ? a.nout : 0) + n0[h];
       }
       if (a.bias && n0[0] < a.nout) {
@@ -614,9 +670,9 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
   const int pro = total < C::kStages - 1 ? total : C::kStages - 1;
   for (int p = 0; p < pro; ++p) cp.issue(a);
 
-  v4f acc[4][4];
+  v4f acc[kRG][4];
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg)
+  for (int rg = 0; rg < kRG; ++rg)
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = {0.f, 0.f, 0.f, 0.f};
   float amax = 0.0f;     // gate_up: max |h| of the lane's outputs
@@ -671,7 +727,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
           bsc[tg] = valid ? (int)ab[tg] : 127;
         }
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
+        for (int rg = 0; rg < kRG; ++rg) {
           const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
           const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
           const int asc = valid ? (int)sb[rg] : 127;
@@ -690,7 +746,12 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
         }
       }
     } else {
-      if (GATEUP && !NV) {
+      if (NARROW) {
+        lds_step_reads_narrow<GATEUP, NV>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, sb0,
+                                          sb1);
+        wq2 = wq3 = v4u_t{0u, 0u, 0u, 0u};   // (groups 2, 3 do not exist)
+        sb2 = sb3 = 0u;
+      } else if (GATEUP && !NV) {
         lds_step_issue_gateup(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3, sb0,
                               sb1, sb2, sb3);
         lds_wait_first(xa0, xa1, xa2, xa3, wq0, wq1, wq2, wq3, sb0, sb1, sb2, sb3);
@@ -704,7 +765,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
         // odd lane groups hold activation K 16..31 of the block in xa: take
         // the weight dwords in the same order
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) wq[rg] = v4u_t{wq[rg].z, wq[rg].w, wq[rg].x, wq[rg].y};
+        for (int rg = 0; rg < kRG; ++rg) wq[rg] = v4u_t{wq[rg].z, wq[rg].w, wq[rg].x, wq[rg].y};
       }
       const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
       const bool valid = 4 * cstep + g < a.nb;        // this lane's MX block lies inside K
@@ -715,7 +776,8 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
       auto expand_w = [&](int rg, int q) __attribute__((always_inline)) {
         if constexpr (NV) {
           const uint32_t sub = (uint32_t)((q >> 1) ^ (g & 1));
-          const float f = valid ? e4m3_to_f32((sb[rg] >> (8 * sub)) & 0xffu) : 0.0f;
+          const v2f fs = e4m3x2_to_f32(sb[rg]);
+          const float f = valid ? (sub ? fs[1] : fs[0]) : 0.0f;
           return fp4x8_times_bf16(wq[rg][q], f);
         } else {
           const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
@@ -738,7 +800,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
               B[tg] = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
             }
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
+            for (int rg = 0; rg < kRG; ++rg) {
               const v8bf A = expand_w(rg, q);
 #pragma unroll
               for (int tg = 0; tg < 4; ++tg)
@@ -755,14 +817,14 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
             const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
             v8bf A[4];
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) A[rg] = expand_w(rg, q);
+            for (int rg = 0; rg < kRG; ++rg) A[rg] = expand_w(rg, q);
 #pragma unroll
             for (int tg = 0; tg < 3; ++tg) {
               if (tg >= ntg) break;
               const v4u_t c = q < 2 ? xa[tg] : xb[tg];
               const v8bf B = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
 #pragma unroll
-              for (int rg = 0; rg < 4; ++rg)
+              for (int rg = 0; rg < kRG; ++rg)
                 acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rg], B, acc[rg][tg], 0, 0, 0);
             }
           }
@@ -775,7 +837,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
           B[tg] = __builtin_bit_cast(v8i, __builtin_shufflevector(xa[tg], xb[tg], 0, 1, 2, 3, 4, 5, 6, 7));
         if (ntg == 4) {
 #pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
+          for (int rg = 0; rg < kRG; ++rg) {
             const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
             const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
 #pragma unroll
@@ -786,7 +848,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
         } else {
           v8i A[4];
 #pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
+          for (int rg = 0; rg < kRG; ++rg) {
             const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
             A[rg] = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
           }
@@ -794,7 +856,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
           for (int tg = 0; tg < 3; ++tg) {
             if (tg >= ntg) break;
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg)
+            for (int rg = 0; rg < kRG; ++rg)
               acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rg], B[tg], acc[rg][tg], 4, 0, 0,
                                                                              (int)sb[rg], 0, 127);
           }
@@ -806,7 +868,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
 
     // ---- epilogue of the unit: the lane holds rows 4g + jj of each 16-row
     // weight group and sorted row r of each 16-row token group
-    if (GATEUP && A4) {
+    if constexpr (GATEUP && A4) {
       // the wave's 32 h columns [ib, ib + 32) are MX block b of each token
       // row: lane (r, g) holds columns 4g..4g+3 (half 0) and 16+4g..16+4g+3
       // (half 1).  The block is quantised here (the rule of
@@ -859,10 +921,13 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
           }
         }
       }
-    } else if (GATEUP) {
+    } else if constexpr (GATEUP) {
+      // wide: halves 0, 1 take gate groups 0, 1 and up groups 2, 3; narrow:
+      // one half, gate group 0 and up group 1
+      constexpr int kHalves = NARROW ? 1 : 2;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int i0 = nt * (kBN / 2) + 32 * wn + 16 * half;
+      for (int half = 0; half < kHalves; ++half) {
+        const int i0 = nt * (kBN / 2) + (NARROW ? 16 : 32) * wn + 16 * half;
         if (i0 >= a.nout) continue;
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
@@ -872,7 +937,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const float gate = acc[half][tg][jj] * sx + bf16_of(bq[2 * half], jj);
-            const float up = acc[half + 2][tg][jj] * sx + bf16_of(bq[2 * half + 1], jj);
+            const float up = acc[half + kHalves][tg][jj] * sx + bf16_of(bq[2 * half + 1], jj);
             hv[jj] = silu_rcp(gate) * up;
             amax = fmaxf(amax, fabsf(hv[jj]));
           }
@@ -882,8 +947,8 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
       }
     } else {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int n0 = nt * kBN + 64 * wn + 16 * rg;
+      for (int rg = 0; rg < kRG; ++rg) {
+        const int n0 = nt * kBN + (NARROW ? 32 : 64) * wn + 16 * rg;
         if (n0 >= a.nout) continue;
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
@@ -904,7 +969,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
       }
     }
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg)
+    for (int rg = 0; rg < kRG; ++rg)
 #pragma unroll
       for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = {0.f, 0.f, 0.f, 0.f};
     cstep = 0;
@@ -1166,8 +1231,8 @@ hipError_t launch_scale_stream(const MoeShape& sh, const MoeWeights& w, const Ws
   return hipGetLastError();
 }
 
-template <bool GATEUP, bool A4 = false, bool NV = false>
-static hipError_t launch_prefill(const PrefillArgs& args, const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
+template <bool GATEUP, int BM, bool NV, bool A4 = false>
+static hipError_t launch_prefill_bm(const PrefillArgs& args, const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
   // one block per compute unit: the LDS ring takes most of a unit's LDS
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1176,10 +1241,19 @@ static hipError_t launch_prefill(const PrefillArgs& args, const MoeShape& sh, co
   PrefillArgs a = args;
   // the expert-major XCD schedule needs the tile words (bounded list) and
   // a grid of whole XCDs
-  a.sched_xcd = cus % 8 == 0 && max_tiles((int64_t)sh.T * sh.k, sh.E, kPrefillBM) <= kTileWordMaxBound;
-  prefill_gemm_kernel<GATEUP, kPrefillBM, A4, NV><<<cus, Ring<kPrefillBM, A4, NV>::kThreads, 0, s>>>(
-      a, ws.tiles, ws.status);
+  a.sched_xcd = cus % 8 == 0 && max_tiles((int64_t)sh.T * sh.k, sh.E, BM) <= kTileWordMaxBound;
+  prefill_gemm_kernel<GATEUP, BM, A4, NV><<<cus, Ring<BM, A4, NV>::kThreads, 0, s>>>(a, ws.tiles, ws.status);
   return hipGetLastError();
+}
+
+// The tile height follows prefill_bm, the rule the tile list was built with.
+template <bool GATEUP, bool A4 = false, bool NV = false>
+static hipError_t launch_prefill(const PrefillArgs& args, const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
+  if constexpr (NV) {
+    if (prefill_bm((int64_t)sh.T * sh.k, sh.E, true) == kPrefillNarrowBM)
+      return launch_prefill_bm<GATEUP, kPrefillNarrowBM, NV>(args, sh, ws, s);
+  }
+  return launch_prefill_bm<GATEUP, kPrefillBM, NV, A4>(args, sh, ws, s);
 }
 
 hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws,

@@ -11,6 +11,16 @@ constexpr int kFusedPermuteMaxPairs = 4096;  // single-block permutation up to h
 constexpr int kFusedRouteMaxTokens = 32;     // single-block route + permute up to here
 constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
 constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 and FP4 x FP4 paths
+constexpr int kPrefillNarrowBM = 64;         // NVFP4 weights when experts average <= 64 rows
+// Row-tile height of the prefill GEMMs for npairs routed rows over E experts:
+// with NVFP4 weights (E4M3 activations) 64-row tiles, all eight waves on the
+// tile's rows, when the experts average at most 64 rows; else 128.  (The
+// NVFP4 weight expansion is the heaviest vector work of these kernels and
+// gains from two waves per SIMD; with MXFP4 weights the narrow tiles were
+// slower: 2048-token FP8 layer 720 -> 810 us, same-box A/B.)
+inline int prefill_bm(int64_t npairs, int64_t E, bool nv) {
+  return nv && npairs <= (int64_t)kPrefillNarrowBM * E ? kPrefillNarrowBM : kPrefillBM;
+}
 // A row tile is 4 ints: expert, first sorted row, end row (exclusive), and
 // a word locating the expert's entries (tile_word).  Entries past the number
 // of tiles (up to max_tiles) hold expert -1.

@@ -19,7 +19,7 @@ import oracle
 import synth
 from helpers import assert_close_rounded, bf16_dev_to_f64, errors, no_constant_rows, to_dev
 from parity import down_combine, fp32, fp8_code_mismatch, gate_up_terms, h_tolerance
-from test_gpu_parity import _f32, _layer_dev, _mx_as_nv, _nv_dev, _run_moe, _status, _ws_view
+from test_gpu_parity import _f32, _layer_dev, _mx_as_nv, _nv_dev, _run_moe, _run_nv, _status, _ws_view
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -124,7 +124,9 @@ def _check(mx, L, x, ids, w, what, tokens=None, ready=False):
 
 
 # every K tail modulo 4 (H/32, I/32), one expert, k = 1, a token count past
-# one 128-row tile per expert; no lower limit on H, I with E4M3 activations
+# one 128-row tile per expert; no lower limit on H, I with E4M3 activations.
+# Experts averaging at most 64 rows take 64-row tiles (all but the 300- and
+# 150-token cases; at 120 tokens some experts span two tiles).
 NV_FP8_SMALL = [  # E, H, I, T, k
     (8, 288, 320, 1, 4),
     (8, 288, 320, 37, 4),
@@ -132,6 +134,7 @@ NV_FP8_SMALL = [  # E, H, I, T, k
     (4, 224, 64, 70, 2),
     (1, 64, 96, 9, 1),
     (2, 3200, 1024, 150, 2),
+    (8, 288, 320, 120, 4),
 ]
 
 
@@ -173,3 +176,33 @@ def test_nvfp4_fp8_prefill_full_size_sampled(mx, T):
     ids, w = oracle.route_topk(logits, synth.TOPK_GPT_OSS)
     toks = np.sort(np.random.default_rng(T + 1).choice(T, 16, replace=False))
     _check(mx, L, x, ids, w, "nvfp4 fp8 T%d" % T, tokens=toks)
+
+
+def _every_scale_code(L, seed):
+    """L with its block scales drawn from every finite E4M3 code (both signs,
+    zero and the subnormals m * 2^-9 included), each code at least once per
+    tensor; the kernels decode the scales with the hardware conversion."""
+    rng = np.random.default_rng(seed)
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    out = dict(L)
+    for key in ("w13_scales", "w2_scales"):
+        sc = rng.choice(codes, size=L[key].shape).astype(np.uint8)
+        sc.reshape(-1)[:codes.size] = rng.permutation(codes)
+        out[key] = sc
+    return out
+
+
+def test_nvfp4_every_finite_scale_code(mx):
+    """Both NVFP4 paths (bf16 activations: the decode GEMV; E4M3 activations:
+    the prefill GEMMs) with every finite E4M3 block-scale code."""
+    E, H, I, T, k = 8, 288, 320, 37, 4
+    L = _every_scale_code(synth.nvfp4_layer(seed=401, E=E, H=H, I=I), 402)
+    logits, x = synth.moe_inputs(403, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    got = bf16_dev_to_f64(_run_nv(mx, _nv_dev(L), x, ids, w))
+    no_constant_rows(got)
+    ref = oracle.moe_forward_routed(x, ids, w, L["w13_blocks"], L["w13_scales"], L["w13_bias"],
+                                    L["w2_blocks"], L["w2_scales"], L["w2_bias"],
+                                    weight_format=("nvfp4", L["w13_global"], L["w2_global"]))
+    assert_close_rounded(got, ref["out"], "nvfp4 bf16, every scale code")
+    _check(mx, L, x, ids, w, "nvfp4 fp8, every scale code")

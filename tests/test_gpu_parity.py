@@ -230,6 +230,7 @@ SMALL = [  # E, H, I, T, k   (H/32 and I/32 give every K tail modulo 4)
     (16, 96, 128, 300, 4),
     (4, 224, 64, 70, 2),
     (1, 64, 96, 9, 1),
+    (8, 288, 320, 120, 4),
 ]
 
 
