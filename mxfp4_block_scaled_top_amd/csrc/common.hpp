@@ -10,6 +10,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mx {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -17,6 +19,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kBlockElems = 32;   // elements per MX block
 // Shared-exponent range of the library's MXFP4 quantisers (scale bytes
@@ -146,6 +150,47 @@ __device__ __forceinline__ v8bf fp4x8_times_bf16(uint32_t w, float f) {
   r[4] = (__bf16)(p2[0] * f); r[5] = (__bf16)(p2[1] * f);
   r[6] = (__bf16)(p3[0] * f); r[7] = (__bf16)(p3[1] * f);
   return r;
+}
+
+// An E4M3 block scale f (as fp32) split for the f16 expansion: the power of
+// two 2^e the scaled FP4 conversion applies (|f| with its mantissa cleared)
+// and the f16 pair (M, M), M = f / 2^e with f's sign (1 <= |M| < 2, three
+// mantissa bits: exact in f16); f = 0 gives M = 0.
+struct NvScale {
+  float pow2;
+  uint32_t m2;
+};
+__device__ __forceinline__ NvScale nv_scale(float f) {
+  const uint32_t u = __float_as_uint(f);
+  NvScale s;
+  s.pow2 = __uint_as_float(u & 0x7f800000u);
+  const uint32_t m = (u & 0x7fffffffu) ? (((u >> 16) & 0x8000u) | 0x3c00u | ((u >> 13) & 0x3ffu)) : 0u;
+  s.m2 = m | (m << 16);
+  return s;
+}
+
+// Eight E2M1 nibbles times an E4M3 block scale, as f16, exactly: the scaled
+// conversion applies 2^e (E2M1 x 2^e lies in [2^-10, 1536] for the finite
+// E4M3 scales) and v_pk_mul_f16 the mantissa M (a product of at most six
+// significant bits, below 2^12).  Two instructions per pair of weights,
+// against four for the bf16 form.
+__device__ __forceinline__ v8h fp4x8_times_f16(uint32_t w, const NvScale& s) {
+  const v2h m = __builtin_bit_cast(v2h, s.m2);
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 0) * m;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 1) * m;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 2) * m;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.pow2, 3) * m;
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ v4f mfma16x16x32(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma16x16x32(const v8h& a, const v8h& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ v8bf as_v8bf(uint4 v) {

@@ -317,7 +317,8 @@ template <bool NV> struct RunLayout {
   // 7 * 192 + 192 <= 1536)
   static constexpr int kRunBytes = kRunDma * 1024 + kScDma * 256;   // LDS per run
   static constexpr int kBufBytes = 2 * kRunBytes;                  // LDS per unit buffer
-  static constexpr int kLds = kBufBytes + 64 * 16;                 // buffer + partial sums
+  // buffer, partial sums; NVFP4: the two waves' per-column activation maxima
+  static constexpr int kLds = kBufBytes + 64 * 16 + (NV ? 2 * kCols * 4 : 0);
 };
 static_assert(kCols == kDecodeBM, "a decode row tile is one m-tile");
 
@@ -364,7 +365,13 @@ __device__ __forceinline__ float rot4_f32(float v) {
 }
 
 // NV: NVFP4 weights (16-element blocks with E4M3 scales: two scales per
-// 32-element chunk; the tensor's global scale is applied to the sums).
+// 32-element chunk; the tensor's global scale is applied to the sums).  The
+// NVFP4 kernels multiply f16 operands: the weights expand exactly to f16
+// (fp4x8_times_f16, half the instructions of the bf16 form), and each m-tile
+// column's bf16 activations are scaled by a power of two 2^-k that puts the
+// column's max |x| in [2^14, 2^15) and converted to f16, exactly for every
+// value of at least max|x| * 2^-32 (smaller ones round to f16 subnormals:
+// at most max|x| * 2^-40 each); the sums are multiplied by 2^k.
 // RT (gate_up of decode batches only): every block first routes the whole
 // batch itself (T <= 8 tokens, T * k <= 128 pairs, E <= 128) with the router
 // and permutation of the stand-alone route + permutation kernel, into its
@@ -495,7 +502,10 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
                                         (int)a.act_bytes, 0x00020000);
   uint4 xa[HG];
   uint4 xl[MODE == kDown ? HG : 1];
+  bool x_new = true;   // NVFP4: xa (xl) hold a new m-tile's bf16 values
+  int xk = 0;          // NVFP4: the lane's column exponent k
   auto load_x = [&](int rbeg, int rend) {
+    x_new = true;
     const int ncols = rend - rbeg;
     int arow = rbeg + min(xt, ncols - 1);
     if (MODE == kGateUp) {   // token of the lane's column
@@ -544,6 +554,43 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(b), acc, 0, 0, 0);
     if (MODE == kDown) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, as_v8bf(bl), acc, 0, 0, 0);
   };
+  auto step_h = [&](v4f& acc, const v8h& A, const uint4& b, const uint4& bl) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(v8h, b), acc, 0, 0, 0);
+    if (MODE == kDown)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(v8h, bl), acc, 0, 0, 0);
+  };
+  // NVFP4: max |x| over the lane's chunks (bf16 magnitude bits), then over
+  // the wave's 16 lanes of the same column (lane % 4)
+  uint32_t* xmax_l = reinterpret_cast<uint32_t*>(smem + RL::kBufBytes + 64 * 16);
+  auto column_max = [&]() {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int jj = 0; jj < HG; ++jj) {
+      const uint32_t d[4] = {xa[jj].x, xa[jj].y, xa[jj].z, xa[jj].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = max(mx, max(d[i] & 0x7fffu, (d[i] >> 16) & 0x7fffu));
+    }
+#pragma unroll
+    for (int sh = 4; sh < 64; sh <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, sh, 64));
+    return mx;
+  };
+  // NVFP4: the m-tile's activations (both waves' maxima in LDS) as f16 times
+  // 2^-k, in place
+  auto to_f16 = [&]() {
+    const uint32_t mx = max(xmax_l[xt], xmax_l[kCols + xt]);
+    const int ex = (int)(mx >> 7);                 // bf16 exponent field (finite x)
+    xk = ex == 0 ? 0 : ex - 141;                   // max|x| * 2^-k in [2^14, 2^15)
+    auto cvt = [&](uint32_t d) {
+      const v2h p = {(_Float16)ldexpf(__uint_as_float(d << 16), -xk),
+                     (_Float16)ldexpf(__uint_as_float(d & 0xffff0000u), -xk)};
+      return __builtin_bit_cast(uint32_t, p);
+    };
+#pragma unroll
+    for (int jj = 0; jj < HG; ++jj) {
+      xa[jj] = make_uint4(cvt(xa[jj].x), cvt(xa[jj].y), cvt(xa[jj].z), cvt(xa[jj].w));
+      if (MODE == kDown) xl[jj] = make_uint4(cvt(xl[jj].x), cvt(xl[jj].y), cvt(xl[jj].z), cvt(xl[jj].w));
+    }
+  };
   // The activations stay in the compact layout: lane (c, g) holds K chunk
   // (c / 4) % 4 of column c % 4.  MFMA step Q multiplies weight chunk Q, so
   // in accumulator Q only columns 4Q .. 4Q+3 hold valid sums (those of
@@ -561,7 +608,20 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
   load_bias(e, n0);
   for (;;) {
     __builtin_amdgcn_s_waitcnt(0);            // this wave's run of unit u, activations, bias
+    if constexpr (NV) {
+      if (x_new) {
+        const uint32_t mx = column_max();
+        if (lane < kCols) xmax_l[kh * kCols + lane] = mx;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+    }
     asm volatile("s_barrier" ::: "memory");   // both runs of unit u have landed
+    if constexpr (NV) {
+      if (x_new) {
+        to_f16();
+        x_new = false;
+      }
+    }
     // blocks past K (up to 8 HG - 1 < 96) read bytes inside the run's region
     // (finite FP4 codes or stale scales); their scale is forced to 0 below
     // scale bytes of groups jj: MXFP4 one per group, packed four per
@@ -622,11 +682,12 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
         f0 = f1 = e8m0_to_f32(in_k ? sc : 0u);
       }
       const uint4 lo = MODE == kDown ? xl[jj] : xa[jj];
-      if (NV) {
-        step(acc0, fp4x8_times_bf16(w.x, f0), xa[jj], lo);
-        step(acc1, fp4x8_times_bf16(w.y, f0), xa[jj], lo);
-        step(acc2, fp4x8_times_bf16(w.z, f1), xa[jj], lo);
-        step(acc3, fp4x8_times_bf16(w.w, f1), xa[jj], lo);
+      if constexpr (NV) {
+        const NvScale s0 = nv_scale(f0), s1 = nv_scale(f1);
+        step_h(acc0, fp4x8_times_f16(w.x, s0), xa[jj], lo);
+        step_h(acc1, fp4x8_times_f16(w.y, s0), xa[jj], lo);
+        step_h(acc2, fp4x8_times_f16(w.z, s1), xa[jj], lo);
+        step_h(acc3, fp4x8_times_f16(w.w, s1), xa[jj], lo);
       } else {
         step(acc0, fp4x8_to_bf16(w.x, f0), xa[jj], lo);
         step(acc1, fp4x8_to_bf16(w.y, f0), xa[jj], lo);
@@ -644,7 +705,10 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kh == 0) {
       acc += red[lane];
-      if (NV) acc *= a.gscale;
+      if constexpr (NV) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[jj] = ldexpf(acc[jj], xk) * a.gscale;
+      }
       // lane (column r, group g) holds rows 4g + jj of column r
       const int row = rbeg + r;
       const bool col_ok = r < rend - rbeg;

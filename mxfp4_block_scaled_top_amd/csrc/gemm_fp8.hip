@@ -142,6 +142,18 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// 8 E4M3 codes (two dwords) -> 8 f16 (exact: every E4M3 value is an f16).
+__device__ __forceinline__ v8h fp8x8_to_f16(uint32_t lo, uint32_t hi) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
 // silu with the hardware exp and reciprocal: a few 1e-7 relative error (at
 // most about 3e-6 for |z| <= 50; beyond, silu is z or negligible), inside the
 // h error both quantised modes are specified against.
@@ -770,19 +782,26 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
       const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
       const bool valid = 4 * cstep + g < a.nb;        // this lane's MX block lies inside K
       // weights of chunk q (elements 8q..8q+7 of the lane's block, 8(q^2).. for
-      // odd g) of weight group rg, exactly as bf16: MXFP4 through the scaled
-      // conversion with the block's E8M0 scale; NVFP4 times the E4M3 scale of
-      // the chunk's 16-element block (the low byte of sb holds block 2g)
+      // odd g) of weight group rg, exactly: MXFP4 as bf16 through the scaled
+      // conversion with the block's E8M0 scale; NVFP4 as f16, times the E4M3
+      // scale of the chunk's 16-element block (the low byte of sb holds block
+      // 2g).  The NVFP4 kernels run the f16 MFMA on f16 operands (E4M3 codes
+      // are f16 values too), the MXFP4 gate_up the bf16 one.
       auto expand_w = [&](int rg, int q) __attribute__((always_inline)) {
         if constexpr (NV) {
           const uint32_t sub = (uint32_t)((q >> 1) ^ (g & 1));
           const v2f fs = e4m3x2_to_f32(sb[rg]);
           const float f = valid ? (sub ? fs[1] : fs[0]) : 0.0f;
-          return fp4x8_times_bf16(wq[rg][q], f);
+          return fp4x8_times_f16(wq[rg][q], nv_scale(f));
         } else {
           const float f = valid ? e8m0_to_f32(sb[rg]) : 0.0f;
           return fp4x8_to_bf16(wq[rg][q], f);
         }
+      };
+      using XT = std::conditional_t<NV, v8h, v8bf>;
+      auto expand_x = [&](uint32_t lo, uint32_t hi) __attribute__((always_inline)) {
+        if constexpr (NV) return fp8x8_to_f16(lo, hi);
+        else return fp8x8_to_bf16(lo, hi);
       };
       if (EXP) {
         // lane group g holds K [32g, 32g+32) of the step (its own MX block);
@@ -793,18 +812,17 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
           for (int q = 0; q < 4; ++q) {
             if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
             const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
-            v8bf B[4];
+            XT B[4];
 #pragma unroll
             for (int tg = 0; tg < 4; ++tg) {
               const v4u_t c = q < 2 ? xa[tg] : xb[tg];
-              B[tg] = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
+              B[tg] = (q & 1) ? expand_x(c.z, c.w) : expand_x(c.x, c.y);
             }
 #pragma unroll
             for (int rg = 0; rg < kRG; ++rg) {
-              const v8bf A = expand_w(rg, q);
+              const XT A = expand_w(rg, q);
 #pragma unroll
-              for (int tg = 0; tg < 4; ++tg)
-                acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[tg], acc[rg][tg], 0, 0, 0);
+              for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = mfma16x16x32(A, B[tg], acc[rg][tg]);
             }
           }
         } else {
@@ -815,17 +833,16 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
             if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
             if (ntg == 0) continue;
             const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
-            v8bf A[4];
+            XT A[4];
 #pragma unroll
             for (int rg = 0; rg < kRG; ++rg) A[rg] = expand_w(rg, q);
 #pragma unroll
             for (int tg = 0; tg < 3; ++tg) {
               if (tg >= ntg) break;
               const v4u_t c = q < 2 ? xa[tg] : xb[tg];
-              const v8bf B = (q & 1) ? fp8x8_to_bf16(c.z, c.w) : fp8x8_to_bf16(c.x, c.y);
+              const XT B = (q & 1) ? expand_x(c.z, c.w) : expand_x(c.x, c.y);
 #pragma unroll
-              for (int rg = 0; rg < kRG; ++rg)
-                acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[rg], B, acc[rg][tg], 0, 0, 0);
+              for (int rg = 0; rg < kRG; ++rg) acc[rg][tg] = mfma16x16x32(A[rg], B, acc[rg][tg]);
             }
           }
         }
