@@ -955,6 +955,27 @@ def test_nvfp4_small_layers(mx, E, H, I, T, k):
     assert_close_rounded(got, ref["out"], "nvfp4 E%d H%d I%d T%d" % (E, H, I, T))
 
 
+def test_nvfp4_decode_wide_activation_range(mx):
+    """The NVFP4 decode kernels multiply f16 operands: each m-tile column of
+    bf16 activations is scaled by its own power of two into f16.  Tokens
+    2^50 apart in magnitude (beyond f16's range on both sides, several in one
+    m-tile) and a token with outliers 2^12 above its other values must meet
+    the layer bar against the oracle."""
+    E, H, I, T, k = 4, 288, 320, 8, 4
+    L = synth.nvfp4_layer(seed=412, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(411, T, E=E, H=H)
+    xf = oracle.bf16_bits_to_f64(x) * 2.0 ** np.array([20, -30, 0, 12, -12, 5, 0, -20])[:, None]
+    xf[2, ::37] *= 2.0 ** 12
+    x = synth.f32_to_bf16_bits(xf.astype(np.float32))
+    ids, w = oracle.route_topk(logits, k)
+    got = bf16_dev_to_f64(_run_nv(mx, _nv_dev(L), x, ids, w))
+    ref = oracle.moe_forward_routed(x, ids, w, L["w13_blocks"], L["w13_scales"], L["w13_bias"],
+                                    L["w2_blocks"], L["w2_scales"], L["w2_bias"],
+                                    weight_format=("nvfp4", L["w13_global"], L["w2_global"]))
+    for t in range(T):   # per token: their magnitudes differ by up to 2^100
+        assert_close_rounded(got[t:t + 1], ref["out"][t:t + 1], "nvfp4 wide range, token %d" % t)
+
+
 @pytest.mark.parametrize("T", [4, 32])
 def test_nvfp4_decode_full_size_sampled(mx, T):
     # gpt-oss-120b MoE shape with NVFP4 weights; the oracle on 4 sampled tokens
