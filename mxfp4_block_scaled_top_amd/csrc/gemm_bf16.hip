@@ -607,6 +607,19 @@ __global__ __launch_bounds__(128) void gemv_persist_kernel(
   load_x(rbeg, rend);
   load_bias(e, n0);
   for (;;) {
+    // Blocks sharing a compute unit do not progress alike (its waves are
+    // issued oldest first: with equal shares a CU's first-dispatched block
+    // ended, on average, 18 us before its last at 32 tokens).  A wave's issue
+    // priority follows the share of its block's units still ahead of it:
+    // blocks that are behind get the higher priority and catch up.
+    {
+      const int64_t left = u_end - u;
+      const int64_t n = u_end - u_begin;
+      if (4 * left > 3 * n) __builtin_amdgcn_s_setprio(3);
+      else if (2 * left > n) __builtin_amdgcn_s_setprio(2);
+      else if (4 * left > n) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     __builtin_amdgcn_s_waitcnt(0);            // this wave's run of unit u, activations, bias
     if constexpr (NV) {
       if (x_new) {
