@@ -71,32 +71,35 @@ constexpr int kBK = 128;               // K per step (four MX blocks)
 // NV: NVFP4 weights (E4M3 activations only): the same 64 B of E2M1 codes per
 // weight row and step, two E4M3 scales per 32 elements (8 bytes per row and
 // step instead of 4).
-// BM = 64 (narrow tiles, E4M3 activations): eight waves each take all 64
-// sorted rows and 32 of the 256 weight rows; six slots of 25 KB.
-template <int BM, bool A4 = false, bool NV = false>
+// WN (wide-N units, BM = 64, E4M3 activations): a unit is 64 sorted rows x
+// two n-tiles (512 weight rows); waves 0-3 take the first n-tile, 4-7 the
+// second, each 64 rows x 64 weight rows as in the 128-row tiles; three
+// slots of 42 KB (NVFP4: 44 KB).
+template <int BM, bool A4 = false, bool NV = false, bool WN = false>
 struct Ring {
-  static constexpr int kWaves = 8;                      // 64 sorted rows x (BM 128: 64, BM 64: 32) weight rows
+  static constexpr int kWaves = 8;                      // each 64 sorted rows x 64 weight rows
   static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBNu = WN ? 2 * kBN : kBN;       // weight rows per unit
   static constexpr int kK = A4 ? 2 * kBK : kBK;         // K per step
   static constexpr int kSub = kK / kBK;                 // 128-element sub-steps per step (scale dwords per row)
-  static constexpr int kStages = A4 ? 3 : BM == 128 ? 4 : 6;
+  static constexpr int kStages = A4 || WN ? 3 : 4;
   static constexpr int kActRow = A4 ? kK / 2 : kK;      // activation bytes per row per step
   static constexpr int kWRow = kK / 2;                  // weight bytes per row per step
   static constexpr int kAct = BM * kActRow;             // activation bytes per slot
   static constexpr int kW = kAct;                       // offsets inside a slot
-  static constexpr int kSc = kAct + kBN * kWRow;
+  static constexpr int kSc = kAct + kBNu * kWRow;
   static constexpr int kScRow = NV ? 8 : 4;             // weight-scale bytes per row and 128-element step
-  static constexpr int kASc = kSc + kBN * kScRow * kSub; // A4: activation scales, 4 B per row and sub-step
+  static constexpr int kASc = kSc + kBNu * kScRow * kSub; // A4: activation scales, 4 B per row and sub-step
   static constexpr int kSlot = kASc + (A4 ? BM * 4 * kSub : 0);
   static constexpr int kActDma = BM * kActRow / 1024 / kWaves;  // 1 KB activation DMAs per wave per step
-  static constexpr int kWDma = kBN * kWRow / 1024 / kWaves;     // 1 KB weight DMAs per wave per step
+  static constexpr int kWDma = kBNu * kWRow / 1024 / kWaves;    // 1 KB weight DMAs per wave per step
   static constexpr int kScDma = 1;                      // the wave's 1/8 of the step's weight scales
   static constexpr int kAScDma = A4 ? 1 : 0;            // the wave's 1/8 of the step's activation scales
   static constexpr int kDma = kActDma + kWDma + kScDma + kAScDma;  // DMA instructions per wave per step
   static constexpr int kLds = kStages * kSlot;
   static_assert(kActDma * kWaves * 1024 == BM * kActRow, "copies split over the waves");
-  static_assert(kWDma * kWaves * 1024 == kBN * kWRow, "copies split over the waves");
-  static_assert((BM == 128 || BM == 64) && (!A4 || BM == 128), "tile heights");
+  static_assert(kWDma * kWaves * 1024 == kBNu * kWRow, "copies split over the waves");
+  static_assert(WN ? BM == 64 && !A4 : BM == 128, "tile heights: 128 rows, wide-N units 64");
   static_assert(!(A4 && NV), "NVFP4 weights take E4M3 activations");
   static_assert((kStages - 2) * kDma <= 63, "vector-memory count range");
   static_assert(kStages - 2 <= 4, "waits cover up to four steps ahead");
@@ -111,7 +114,8 @@ struct PrefillArgs {
   int nout;                // I (gate_up) or H (down)
   int nb;                  // K / 32
   int K;
-  int NT;                  // n-tiles
+  int NT;                  // n-tile units per row tile (wide-N: pairs of n-tiles)
+  int NTs;                 // n-tiles of the restaged scale stream
   int nsteps;              // K steps: ceil(nb / 4), MXFP4 activations ceil(nb / 8)
   int nsteps_s;            // 128-element steps of the scale streams: ceil(nb / 4)
   const uint8_t* act;      // [sorted rows, K] E4M3 codes, or [sorted rows, K/32, 16] E2M1 blocks
@@ -256,9 +260,9 @@ __device__ __forceinline__ float bf16_of(uint2 q, int jj) {
 // (lane%4) ^ ((row/2)%4)).  The activation scales are stored step-major, so a
 // step's scales of the tile's 128 rows are 512 contiguous bytes; wave w
 // copies rows 16w .. 16w+15 with lanes 0-3.
-template <bool GATEUP, int BM, bool A4 = false, bool NV = false>
+template <bool GATEUP, int BM, bool A4 = false, bool NV = false, bool WN = false>
 struct PrefillCopier {
-  using C = Ring<BM, A4, NV>;
+  using C = Ring<BM, A4, NV, WN>;
   static constexpr int NW = C::kWaves;
   const int* tiles;
   uint8_t* smem;
@@ -302,13 +306,25 @@ struct PrefillCopier {
     const int64_t ebase = (int64_t)te.x * a.R;
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
-      const int wr = weight_row<GATEUP>((A4 ? 8 : 16) * (NW * i + wave) + w_row, nt, a.nout);
+      const int lr = (A4 ? 8 : 16) * (NW * i + wave) + w_row;
+      // wide-N: LDS rows 256 h .. 256 h + 255 hold n-tile 2 nt + h
+      const int wr = WN ? weight_row<GATEUP>(lr & (kBN - 1), 2 * nt + (lr >> 8), a.nout)
+                        : weight_row<GATEUP>(lr, nt, a.nout);
       wptr[i] = a.wb + (ebase + wr) * a.nb * kBlockBytes;
     }
     // the unit's stream: 1 KB per 128-element sub-step; A4: wave w copies 256 B
-    // (lanes 0-15) of sub-step w / 4, else 128 B (lanes 0-7)
-    wsp = a.wsp + ((int64_t)te.x * a.NT + nt) * a.nsteps_s * (kBN * C::kScRow) +
-          (A4 ? 256 * (wave & 3) + 16 * (lane & 15) : NV ? 256 * wave + 16 * (lane & 15) : 128 * wave + 16 * (lane & 7));
+    // (lanes 0-15) of sub-step w / 4, else 128 B (lanes 0-7).  Wide-N: waves
+    // 0-3 copy the first n-tile's 1 KB (NVFP4 2 KB), 4-7 the second's (an odd
+    // last n-tile re-reads the stream's last one: its outputs are never
+    // stored), 256 B (512 B) each
+    if (WN) {
+      const int ntr = min(2 * nt + (wave >> 2), a.NTs - 1);
+      wsp = a.wsp + ((int64_t)te.x * a.NTs + ntr) * a.nsteps_s * (kBN * C::kScRow) +
+            (kBN * C::kScRow / 4) * (wave & 3) + 16 * lane;
+    } else {
+      wsp = a.wsp + ((int64_t)te.x * a.NTs + nt) * a.nsteps_s * (kBN * C::kScRow) +
+            (A4 ? 256 * (wave & 3) + 16 * (lane & 15) : NV ? 256 * wave + 16 * (lane & 15) : 128 * wave + 16 * (lane & 7));
+    }
   }
 
   // copies of the next step into its slot, then advance
@@ -342,10 +358,11 @@ struct PrefillCopier {
       if (lane < 16) __builtin_amdgcn_global_load_lds(wsp + ss * 1024, dst + C::kSc + 256 * wave, 16, 0, 0);
       if (lane < 8)
         __builtin_amdgcn_global_load_lds(ascp + ss * a.asc_step, dst + C::kASc + 128 * wave, 16, 0, 0);
-    } else if (lane < 2 * C::kScRow) {
-      // (NVFP4: 256 B per wave, the 8 scale bytes of rows 32w .. 32w+31)
-      __builtin_amdgcn_global_load_lds(wsp + step * (kBN * C::kScRow), dst + C::kSc + 32 * C::kScRow * wave, 16,
-                                       0, 0);
+    } else if (lane < C::kBNu * C::kScRow / C::kWaves / 16) {
+      // the scale bytes of rows (kBNu / 8) w .. (kBNu / 8)(w + 1) - 1 (NVFP4:
+      // 8 per row)
+      __builtin_amdgcn_global_load_lds(wsp + step * (kBN * C::kScRow),
+                                       dst + C::kSc + (C::kBNu / C::kWaves) * C::kScRow * wave, 16, 0, 0);
     }
   }
   // the weight copies of the next step
@@ -430,54 +447,6 @@ __device__ __forceinline__ void lds_step_reads(uint32_t aa0, uint32_t aa1, uint3
 #undef MX_RD_ACT
 #undef MX_RD_OUTS
 
-// Narrow tiles (BM = 64): the 8 activation reads and, per wave, two weight
-// groups (gate_up: its 16 gate rows and their 16 up rows, LDS rows +0 and
-// +128; down: rows +0 and +16) with their scales (NV: 2 bytes per row).
-#define MX_RD_ACT_N                                                                  \
-  "ds_read_b128 %0, %12\n\tds_read_b128 %4, %13\n\t"                               \
-  "ds_read_b128 %1, %12 offset:2048\n\tds_read_b128 %5, %13 offset:2048\n\t"       \
-  "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %6, %13 offset:4096\n\t"       \
-  "ds_read_b128 %3, %12 offset:6144\n\tds_read_b128 %7, %13 offset:6144\n\t"
-#define MX_RD_OUTS_N                                                                 \
-  "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(xb0), "=&v"(xb1), "=&v"(xb2), "=&v"(xb3), \
-      "=&v"(wq0), "=&v"(wq1), "=&v"(sb0), "=&v"(sb1)
-template <bool GATEUP, bool NV>
-__device__ __forceinline__ void lds_step_reads_narrow(uint32_t aa0, uint32_t aa1, uint32_t ww, uint32_t ss,
-                                                      v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3,
-                                                      v4u_t& xb0, v4u_t& xb1, v4u_t& xb2, v4u_t& xb3,
-                                                      v4u_t& wq0, v4u_t& wq1, uint32_t& sb0, uint32_t& sb1) {
-  if (GATEUP && NV) {
-    asm volatile(MX_RD_ACT_N
-                 "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:8192\n\t"
-                 "ds_read_u16 %10, %15\n\tds_read_u16 %11, %15 offset:1024\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : MX_RD_OUTS_N
-                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
-  } else if (GATEUP) {
-    asm volatile(MX_RD_ACT_N
-                 "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:8192\n\t"
-                 "ds_read_u8 %10, %15\n\tds_read_u8 %11, %15 offset:512\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : MX_RD_OUTS_N
-                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
-  } else if (NV) {
-    asm volatile(MX_RD_ACT_N
-                 "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:1024\n\t"
-                 "ds_read_u16 %10, %15\n\tds_read_u16 %11, %15 offset:128\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : MX_RD_OUTS_N
-                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
-  } else {
-    asm volatile(MX_RD_ACT_N
-                 "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:1024\n\t"
-                 "ds_read_u8 %10, %15\n\tds_read_u8 %11, %15 offset:64\n\t"
-                 "s_waitcnt lgkmcnt(0)"
-                 : MX_RD_OUTS_N
-                 : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
-  }
-}
-#undef MX_RD_ACT_N
-#undef MX_RD_OUTS_N
 
 // gate_up variant in two phases: the 16 reads are issued in the order the
 // MFMAs consume them (scales, weights, then the activation chunks of MFMAs
@@ -563,11 +532,11 @@ __device__ __forceinline__ void lds_half_reads_a4(bool gateup, uint32_t aa, uint
 // operands exactly to bf16 (an E4M3 block scale cannot ride on the
 // block-scaled MFMA, whose scales are E8M0) and the global scale joins the
 // per-tensor activation scale in the epilogue.
-template <bool GATEUP, int BM, bool A4 = false, bool NV = false>
-__global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_kernel(PrefillArgs a,
+template <bool GATEUP, int BM, bool A4 = false, bool NV = false, bool WN = false>
+__global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm_kernel(PrefillArgs a,
                                                                                   const int* __restrict__ tiles,
                                                                                   int* status) {
-  using C = Ring<BM, A4, NV>;
+  using C = Ring<BM, A4, NV, WN>;
   constexpr bool EXP = GATEUP || NV;   // operands expanded to bf16, v_mfma_f32_16x16x32_bf16
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
   const int num_units = status[kStNumTiles] * a.NT;
@@ -591,20 +560,21 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
-  PrefillCopier<GATEUP, BM, A4, NV> cp;
+  PrefillCopier<GATEUP, BM, A4, NV, WN> cp;
   cp.init(a, tiles, smem, wave, lane, u0, G, my_units);
 
   // ---------------- compute: 64 sorted rows x 64 weight rows ----------------
-  // (narrow tiles: 64 sorted rows x 32 weight rows, every wave all 64 rows)
-  constexpr bool NARROW = BM == 64;
-  constexpr int kRG = NARROW ? 2 : 4;               // 16-row weight groups per wave
-  static_assert(!NARROW || !A4, "narrow tiles take E4M3 activations");
-  const int wm = NARROW ? 0 : wave >> 2, wn = NARROW ? wave : wave & 3;
+  constexpr int kRG = 4;                            // 16-row weight groups per wave
+  // wave (wm, wn): 128-row tiles, sorted rows 64 wm .. 64 wm + 63; wide-N
+  // units, the unit's n-tile wm; weight rows 64 wn .. 64 wn + 63 of it
+  const int wm = wave >> 2, wn = wave & 3;
   const int r = lane & 15, g = lane >> 4;
   // LDS weight row of this lane in the wave's first 16-row group; the others
   // follow at fixed offsets (gate_up: groups 0, 1 gate rows, 2, 3 the
-  // matching up rows; narrow gate_up: group 0 gate rows, 1 the up rows)
-  const int lrow0 = (GATEUP ? (NARROW ? 16 : 32) * wn : (NARROW ? 32 : 64) * wn) + r;
+  // matching up rows)
+  const int lrow0 = (WN ? kBN * wm : 0) + (GATEUP ? 32 : 64) * wn + r;
+  // first sorted row of the wave's 64 (wide-N: every wave takes rows 0-63)
+  const int arow = WN ? 0 : 64 * wm;
   const int wslot = g ^ ((r >> 1) & 3);             // slot of MX block g in these rows
   // activation chunks: the bf16 path takes K [32g, 32g+32) = chunks 2g, 2g+1,
   // the block-scaled path chunks g and 4+g; the row's swizzle is row%8 = r%8.
@@ -615,8 +585,8 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
   const int c0 = (EXP ? 2 * g + (g & 1) : g) ^ (r & 7);
   const int c1 = (EXP ? 2 * g + 1 - (g & 1) : 4 + g) ^ (r & 7);
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const uint32_t a0 = lds0 + (64 * wm + r) * kBK + 16 * c0;
-  const uint32_t a1 = lds0 + (64 * wm + r) * kBK + 16 * c1;
+  const uint32_t a0 = lds0 + (arow + r) * kBK + 16 * c0;
+  const uint32_t a1 = lds0 + (arow + r) * kBK + 16 * c1;
   const uint32_t w0 = lds0 + C::kW + lrow0 * 64 + 16 * wslot;
   // scale of MX block g of the step (NVFP4: of its 16-element blocks 2g, 2g+1)
   const uint32_t s0 = lds0 + C::kSc + lrow0 * C::kScRow + (NV ? 2 * g : g);
@@ -632,6 +602,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
 
   int cstep = 0, cslot = 0, ck = 0;
   int e = 0, rb = 0, re = 0, nt = 0;
+  int ntr = 0;   // the wave's n-tile (wide-N units: 2 nt + wm)
   // 16-row groups of this wave's 64 sorted rows that hold rows of the tile:
   // in the FP8 kernels the MFMAs (and activation expansions) of groups
   // wholly past the tile's end are skipped (their outputs are never stored).
@@ -646,10 +617,11 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
   auto comp_setup = [&](int u) __attribute__((always_inline)) {
     int tile;
     unit_tile(a, tiles, u, tile, nt);
+    ntr = WN ? 2 * nt + wm : nt;
     const int3 te = tile_entry(tiles + kTileInts * tile);
     e = te.x; rb = te.y; re = te.z;
     {
-      const int v = re - rb - 64 * wm;
+      const int v = re - rb - arow;
       ntg = v <= 0 ? 0 : v >= 64 ? 4 : (v + 15) >> 4;
     }
     // through the scalar cache, 16 rows at a time (a group past nout is
@@ -663,8 +635,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = jp + h;
-        n0[h] = GATEUP ? nt * (kBN / 2) + (NARROW ? 16 : 32) * wn + 16 * (j >> 1)
-                       : nt * kBN + (NARROW ? 32 : 64) * wn + 16 * j;
+        n0[h] = GATEUP ? ntr * (kBN / 2) + 32 * wn + 16 * (j >> 1) : ntr * kBN + 64 * wn + 16 * j;
         off[h] = (GATEUP && (j & 1) ? a.nout : 0) + n0[h];
       }
       if (a.bias && n0[0] < a.nout) {
@@ -758,12 +729,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
         }
       }
     } else {
-      if (NARROW) {
-        lds_step_reads_narrow<GATEUP, NV>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, sb0,
-                                          sb1);
-        wq2 = wq3 = v4u_t{0u, 0u, 0u, 0u};   // (groups 2, 3 do not exist)
-        sb2 = sb3 = 0u;
-      } else if (GATEUP && !NV) {
+      if (GATEUP && !NV) {
         lds_step_issue_gateup(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3, sb0,
                               sb1, sb2, sb3);
         lds_wait_first(xa0, xa1, xa2, xa3, wq0, wq1, wq2, wq3, sb0, sb1, sb2, sb3);
@@ -900,7 +866,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
         const int b = ib / kBlockElems, nbh = a.nout / kBlockElems;
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-          const int row = rb + 64 * wm + 16 * tg + r;
+          const int row = rb + arow + 16 * tg + r;
           float hv[8];
           uint32_t am = 0;
 #pragma unroll
@@ -939,22 +905,20 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
         }
       }
     } else if constexpr (GATEUP) {
-      // wide: halves 0, 1 take gate groups 0, 1 and up groups 2, 3; narrow:
-      // one half, gate group 0 and up group 1
-      constexpr int kHalves = NARROW ? 1 : 2;
+      // halves 0, 1 take gate groups 0, 1 and up groups 2, 3
 #pragma unroll
-      for (int half = 0; half < kHalves; ++half) {
-        const int i0 = nt * (kBN / 2) + (NARROW ? 16 : 32) * wn + 16 * half;
+      for (int half = 0; half < 2; ++half) {
+        const int i0 = ntr * (kBN / 2) + 32 * wn + 16 * half;
         if (i0 >= a.nout) continue;
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-          const int row = rb + 64 * wm + 16 * tg + r;
+          const int row = rb + arow + 16 * tg + r;
           if (row >= re) continue;
           float hv[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const float gate = acc[half][tg][jj] * sx + bf16_of(bq[2 * half], jj);
-            const float up = acc[half + kHalves][tg][jj] * sx + bf16_of(bq[2 * half + 1], jj);
+            const float up = acc[half + 2][tg][jj] * sx + bf16_of(bq[2 * half + 1], jj);
             hv[jj] = silu_rcp(gate) * up;
             amax = fmaxf(amax, fabsf(hv[jj]));
           }
@@ -965,11 +929,11 @@ __global__ __launch_bounds__((Ring<BM, A4, NV>::kThreads)) void prefill_gemm_ker
     } else {
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) {
-        const int n0 = nt * kBN + (NARROW ? 32 : 64) * wn + 16 * rg;
+        const int n0 = ntr * kBN + 64 * wn + 16 * rg;
         if (n0 >= a.nout) continue;
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-          const int row = rb + 64 * wm + 16 * tg + r;
+          const int row = rb + arow + 16 * tg + r;
           if (row >= re) continue;
           float v[4];
 #pragma unroll
@@ -1248,7 +1212,7 @@ hipError_t launch_scale_stream(const MoeShape& sh, const MoeWeights& w, const Ws
   return hipGetLastError();
 }
 
-template <bool GATEUP, int BM, bool NV, bool A4 = false>
+template <bool GATEUP, int BM, bool NV, bool A4 = false, bool WN = false>
 static hipError_t launch_prefill_bm(const PrefillArgs& args, const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
   // one block per compute unit: the LDS ring takes most of a unit's LDS
   int dev = 0, cus = 0;
@@ -1256,10 +1220,11 @@ static hipError_t launch_prefill_bm(const PrefillArgs& args, const MoeShape& sh,
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   PrefillArgs a = args;
+  if (WN) a.NT = (args.NT + 1) / 2;   // units of two n-tiles
   // the expert-major XCD schedule needs the tile words (bounded list) and
   // a grid of whole XCDs
   a.sched_xcd = cus % 8 == 0 && max_tiles((int64_t)sh.T * sh.k, sh.E, BM) <= kTileWordMaxBound;
-  prefill_gemm_kernel<GATEUP, BM, A4, NV><<<cus, Ring<BM, A4, NV>::kThreads, 0, s>>>(a, ws.tiles, ws.status);
+  prefill_gemm_kernel<GATEUP, BM, A4, NV, WN><<<cus, Ring<BM, A4, NV, WN>::kThreads, 0, s>>>(a, ws.tiles, ws.status);
   return hipGetLastError();
 }
 
@@ -1268,7 +1233,7 @@ template <bool GATEUP, bool A4 = false, bool NV = false>
 static hipError_t launch_prefill(const PrefillArgs& args, const MoeShape& sh, const WsPtrs& ws, hipStream_t s) {
   if constexpr (NV) {
     if (prefill_bm((int64_t)sh.T * sh.k, sh.E, true) == kPrefillNarrowBM)
-      return launch_prefill_bm<GATEUP, kPrefillNarrowBM, NV>(args, sh, ws, s);
+      return launch_prefill_bm<GATEUP, kPrefillNarrowBM, NV, false, true>(args, sh, ws, s);
   }
   return launch_prefill_bm<GATEUP, kPrefillBM, NV, A4>(args, sh, ws, s);
 }
@@ -1283,7 +1248,7 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
   a.nout = sh.I;
   a.nb = sh.H / kBlockElems;
   a.K = sh.H;
-  a.NT = (sh.I + kBN / 2 - 1) / (kBN / 2);
+  a.NT = a.NTs = (sh.I + kBN / 2 - 1) / (kBN / 2);
   a.nsteps = (a.nb + 3) / 4;
   a.nsteps_s = a.nsteps;
   a.act = ws.x_codes;
@@ -1307,7 +1272,7 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
   a.nout = sh.H;
   a.nb = sh.I / kBlockElems;
   a.K = sh.I;
-  a.NT = (sh.H + kBN - 1) / kBN;
+  a.NT = a.NTs = (sh.H + kBN - 1) / kBN;
   a.nsteps = (a.nb + 3) / 4;
   a.nsteps_s = a.nsteps;
   a.act = ws.h_codes;
@@ -1331,7 +1296,7 @@ hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const 
   a.nout = sh.I;
   a.nb = sh.H / kBlockElems;
   a.K = sh.H;
-  a.NT = (sh.I + kBN / 2 - 1) / (kBN / 2);
+  a.NT = a.NTs = (sh.I + kBN / 2 - 1) / (kBN / 2);
   a.nsteps = (a.nb + 7) / 8;        // K steps of 256
   a.nsteps_s = (a.nb + 3) / 4;
   a.act = ws.x_codes;
@@ -1356,7 +1321,7 @@ hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const Ws
   a.nout = sh.H;
   a.nb = sh.I / kBlockElems;
   a.K = sh.I;
-  a.NT = (sh.H + kBN - 1) / kBN;
+  a.NT = a.NTs = (sh.H + kBN - 1) / kBN;
   a.nsteps = (a.nb + 7) / 8;        // K steps of 256
   a.nsteps_s = (a.nb + 3) / 4;
   a.act = ws.h_codes;

@@ -13,11 +13,11 @@ constexpr int kDecodeBM = 4;                 // sorted rows per tile, bf16 path
 constexpr int kPrefillBM = 128;              // sorted rows per tile, FP8 and FP4 x FP4 paths
 constexpr int kPrefillNarrowBM = 64;         // NVFP4 weights when experts average <= 64 rows
 // Row-tile height of the prefill GEMMs for npairs routed rows over E experts:
-// with NVFP4 weights (E4M3 activations) 64-row tiles, all eight waves on the
-// tile's rows, when the experts average at most 64 rows; else 128.  (The
-// NVFP4 weight expansion is the heaviest vector work of these kernels and
-// gains from two waves per SIMD; with MXFP4 weights the narrow tiles were
-// slower: 2048-token FP8 layer 720 -> 810 us, same-box A/B.)
+// with NVFP4 weights (E4M3 activations), while the experts average at most
+// 64 rows, units of 64 rows x two n-tiles (all eight waves busy: in 128-row
+// tiles the lower half's waves would hold no rows), else 128-row tiles.
+// With MXFP4 weights the 64-row units were no faster for gate_up and slower
+// for down (2048-token FP8 layer 720 -> 761 us, same-box A/B).
 inline int prefill_bm(int64_t npairs, int64_t E, bool nv) {
   return nv && npairs <= (int64_t)kPrefillNarrowBM * E ? kPrefillNarrowBM : kPrefillBM;
 }
