@@ -597,8 +597,8 @@ def main():
 
     fp8 = prim["act"] != "bf16"
     fp4 = prim["act"] == "mxfp4"
-    kname = ("prefill_gemm_kernel<true, 128, true>" if fp4 else "prefill_gemm_kernel<true, 128, false>"
-             if fp8 else "gemv_persist_kernel<0, 12, false, false>")
+    kname = ("prefill_gemm_kernel<true, 128, true, false, false>" if fp4 else
+             "prefill_gemm_kernel<true, 128, false, false, false>" if fp8 else "gemv_persist_kernel<0, 12, false, false>")
     if fp8 and prim["tokens"] >= 4096:
         peak = MXFP4_PEAK_TFLOPS if fp4 else FP8_PEAK_TFLOPS
         roof = dict(bound="mfma", achieved=prim["gemm1_TFLOPs"], peak=peak, unit="TFLOP/s",
