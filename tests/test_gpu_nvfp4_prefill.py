@@ -167,6 +167,17 @@ def test_nvfp4_fp8_gate_up_equals_mxfp4_for_power_of_two_scales(mx, E, H, I, T, 
     assert np.array_equal(_status(ws_mx, lay)[:5], _status(ws_nv, lay)[:5])
 
 
+def test_nvfp4_fp8_wide_n_units_multi_unit(mx):
+    """gpt-oss widths with the experts averaging 50 rows: the wide-N units
+    (64 rows x two n-tiles), about 750 gate_up units over the 256 blocks, so
+    the copier steps into further units; every token checked."""
+    E, H, I, T, k = 48, 2880, 2880, 600, 4
+    L = synth.nvfp4_layer(seed=421, E=E, H=H, I=I)
+    logits, x = synth.moe_inputs(422, T, E=E, H=H)
+    ids, w = oracle.route_topk(logits, k)
+    _check(mx, L, x, ids, w, "nvfp4 fp8 wide-N E%d T%d" % (E, T))
+
+
 @pytest.mark.parametrize("T", [2048])
 def test_nvfp4_fp8_prefill_full_size_sampled(mx, T):
     """The gpt-oss-120b MoE shape with NVFP4 weights at a 2048-token prefill;
