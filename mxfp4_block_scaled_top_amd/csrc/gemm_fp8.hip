@@ -448,40 +448,6 @@ __device__ __forceinline__ void lds_step_reads(uint32_t aa0, uint32_t aa1, uint3
 #undef MX_RD_OUTS
 
 
-// gate_up variant in two phases: the 16 reads are issued in the order the
-// MFMAs consume them (scales, weights, then the activation chunks of MFMAs
-// 0-1, then those of MFMAs 2-3), and the caller waits for the first twelve
-// (lds_wait_first) before it starts and for the rest (lds_wait_rest) halfway.
-// The destination registers of pending reads are only named by these
-// assembly blocks until their wait.
-__device__ __forceinline__ void lds_step_issue_gateup(uint32_t aa0, uint32_t aa1, uint32_t ww, uint32_t ss,
-                                                      v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3,
-                                                      v4u_t& xb0, v4u_t& xb1, v4u_t& xb2, v4u_t& xb3,
-                                                      v4u_t& wq0, v4u_t& wq1, v4u_t& wq2, v4u_t& wq3,
-                                                      uint32_t& sb0, uint32_t& sb1, uint32_t& sb2, uint32_t& sb3) {
-  asm volatile("ds_read_u8 %12, %19\n\tds_read_u8 %13, %19 offset:64\n\t"
-               "ds_read_u8 %14, %19 offset:512\n\tds_read_u8 %15, %19 offset:576\n\t"
-               "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:1024\n\t"
-               "ds_read_b128 %10, %18 offset:8192\n\tds_read_b128 %11, %18 offset:9216\n\t"
-               "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:2048\n\t"
-               "ds_read_b128 %2, %16 offset:4096\n\tds_read_b128 %3, %16 offset:6144\n\t"
-               "ds_read_b128 %4, %17\n\tds_read_b128 %5, %17 offset:2048\n\t"
-               "ds_read_b128 %6, %17 offset:4096\n\tds_read_b128 %7, %17 offset:6144"
-               : "=&v"(xa0), "=&v"(xa1), "=&v"(xa2), "=&v"(xa3), "=&v"(xb0), "=&v"(xb1), "=&v"(xb2),
-                 "=&v"(xb3), "=&v"(wq0), "=&v"(wq1), "=&v"(wq2), "=&v"(wq3), "=&v"(sb0), "=&v"(sb1),
-                 "=&v"(sb2), "=&v"(sb3)
-               : "v"(aa0), "v"(aa1), "v"(ww), "v"(ss));
-}
-__device__ __forceinline__ void lds_wait_first(v4u_t& xa0, v4u_t& xa1, v4u_t& xa2, v4u_t& xa3, v4u_t& wq0,
-                                               v4u_t& wq1, v4u_t& wq2, v4u_t& wq3, uint32_t& sb0,
-                                               uint32_t& sb1, uint32_t& sb2, uint32_t& sb3) {
-  asm volatile("s_waitcnt lgkmcnt(4)"
-               : "+v"(xa0), "+v"(xa1), "+v"(xa2), "+v"(xa3), "+v"(wq0), "+v"(wq1), "+v"(wq2), "+v"(wq3),
-                 "+v"(sb0), "+v"(sb1), "+v"(sb2), "+v"(sb3));
-}
-__device__ __forceinline__ void lds_wait_rest(v4u_t& xb0, v4u_t& xb1, v4u_t& xb2, v4u_t& xb3) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xb0), "+v"(xb1), "+v"(xb2), "+v"(xb3));
-}
 
 
 // A4, one half (four MX blocks) of a 256-element step: 4 activation reads
@@ -729,14 +695,11 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
         }
       }
     } else {
-      if (GATEUP && !NV) {
-        lds_step_issue_gateup(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3, sb0,
-                              sb1, sb2, sb3);
-        lds_wait_first(xa0, xa1, xa2, xa3, wq0, wq1, wq2, wq3, sb0, sb1, sb2, sb3);
-      } else {
-        lds_step_reads<GATEUP, NV>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3,
-                                   sb0, sb1, sb2, sb3);
-      }
+      // all 16 reads and their wait in one assembly block: no register of a
+      // read in flight is ever visible to compiler-generated code (variants
+      // that waited for the reads in two or four phases were no faster)
+      lds_step_reads<GATEUP, NV>(aa0, aa1, ww, ss, xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3, wq0, wq1, wq2, wq3, sb0,
+                                 sb1, sb2, sb3);
       const v4u_t xa[4] = {xa0, xa1, xa2, xa3};
       v4u_t wq[4] = {wq0, wq1, wq2, wq3};
       if (EXP && (g & 1)) {
@@ -772,11 +735,10 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
       if (EXP) {
         // lane group g holds K [32g, 32g+32) of the step (its own MX block);
         // MFMA q takes elements 8q..8q+7 of it (8(q^2).. for odd g), in the
-        // same order for both operands; MFMAs 2-3 use the chunks read last
+        // same order for both operands; MFMAs 2-3 take the second chunks
         if (ntg == 4) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
             const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
             XT B[4];
 #pragma unroll
@@ -796,7 +758,6 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
           // hold rows of it (none: no expansion either)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if (q == 2) lds_wait_rest(xb0, xb1, xb2, xb3);
             if (ntg == 0) continue;
             const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
             XT A[4];
@@ -814,35 +775,20 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
         }
       } else {
         const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
-        v8i B[4];
+        v8i A[4];
 #pragma unroll
-        for (int tg = 0; tg < 4; ++tg)
-          B[tg] = __builtin_bit_cast(v8i, __builtin_shufflevector(xa[tg], xb[tg], 0, 1, 2, 3, 4, 5, 6, 7));
-        if (ntg == 4) {
+        for (int rg = 0; rg < kRG; ++rg) {
+          const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
+          A[rg] = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
+        }
 #pragma unroll
-          for (int rg = 0; rg < kRG; ++rg) {
-            const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
-            const v8i A = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
+        for (int tg = 0; tg < 4; ++tg) {
+          if (tg >= ntg) break;   // rows past the tile (never stored)
+          const v8i B = __builtin_bit_cast(v8i, __builtin_shufflevector(xa[tg], xb[tg], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int tg = 0; tg < 4; ++tg)
-              acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 0, 0,
-                                                                             (int)sb[rg], 0, 127);
-          }
-        } else {
-          v8i A[4];
-#pragma unroll
-          for (int rg = 0; rg < kRG; ++rg) {
-            const v4u_t wz = valid ? wq[rg] : v4u_t{0u, 0u, 0u, 0u};
-            A[rg] = v8i{(int)wz.x, (int)wz.y, (int)wz.z, (int)wz.w, 0, 0, 0, 0};
-          }
-#pragma unroll
-          for (int tg = 0; tg < 3; ++tg) {
-            if (tg >= ntg) break;
-#pragma unroll
-            for (int rg = 0; rg < kRG; ++rg)
-              acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rg], B[tg], acc[rg][tg], 4, 0, 0,
-                                                                             (int)sb[rg], 0, 127);
-          }
+          for (int rg = 0; rg < kRG; ++rg)
+            acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rg], B, acc[rg][tg], 4, 0, 0,
+                                                                           (int)sb[rg], 0, 127);
         }
       }
     }
