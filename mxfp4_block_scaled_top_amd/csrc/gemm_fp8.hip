@@ -626,7 +626,15 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
     for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = {0.f, 0.f, 0.f, 0.f};
   float amax = 0.0f;     // gate_up: max |h| of the lane's outputs
 
-  for (int t = 0; t < total; ++t) {
+  // one K step; NTG: the wave's 16-row groups that hold rows of the tile,
+  // fixed per unit (-1: taken from ntg at run time).  The expanding kernels
+  // run a separate step loop for each value, so that the step holds no
+  // branch on it: the compiler then keeps the accumulators in place (a
+  // merge of full and partial paths inside the step cost 24-72 register
+  // copies per step)
+  auto step = [&](const int t, auto ntg_c) __attribute__((always_inline)) {
+    constexpr int NTG = decltype(ntg_c)::value;
+    const int nrg = NTG < 0 ? ntg : NTG;
     // this wave's copies of step t have landed (steps issued beyond t:
     // min(STAGES - 2, total - 1 - t)); after the barrier everybody's have,
     // and everybody is done reading step t-1's slot
@@ -694,7 +702,9 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-    } else {
+    } else if (nrg > 0) {
+      // (a wave whose rows all lie past the tile neither reads nor computes:
+      // at ~64 rows per expert that is half the waves of a 128-row tile)
       // all 16 reads and their wait in one assembly block: no register of a
       // read in flight is ever visible to compiler-generated code (variants
       // that waited for the reads in two or four phases were no faster)
@@ -736,7 +746,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
         // lane group g holds K [32g, 32g+32) of the step (its own MX block);
         // MFMA q takes elements 8q..8q+7 of it (8(q^2).. for odd g), in the
         // same order for both operands; MFMAs 2-3 take the second chunks
-        if (ntg == 4) {
+        if (nrg == 4) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
@@ -758,14 +768,13 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
           // hold rows of it (none: no expansion either)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            if (ntg == 0) continue;
             const v4u_t xb[4] = {xb0, xb1, xb2, xb3};
             XT A[4];
 #pragma unroll
             for (int rg = 0; rg < kRG; ++rg) A[rg] = expand_w(rg, q);
 #pragma unroll
             for (int tg = 0; tg < 3; ++tg) {
-              if (tg >= ntg) break;
+              if (tg >= nrg) break;
               const v4u_t c = q < 2 ? xa[tg] : xb[tg];
               const XT B = (q & 1) ? expand_x(c.z, c.w) : expand_x(c.x, c.y);
 #pragma unroll
@@ -783,7 +792,7 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
         }
 #pragma unroll
         for (int tg = 0; tg < 4; ++tg) {
-          if (tg >= ntg) break;   // rows past the tile (never stored)
+          if (tg >= nrg) break;   // rows past the tile (never stored)
           const v8i B = __builtin_bit_cast(v8i, __builtin_shufflevector(xa[tg], xb[tg], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int rg = 0; rg < kRG; ++rg)
@@ -793,7 +802,23 @@ __global__ __launch_bounds__((Ring<BM, A4, NV, WN>::kThreads)) void prefill_gemm
       }
     }
     cslot = cslot + 1 == C::kStages ? 0 : cslot + 1;
-    if (++cstep < a.nsteps) continue;
+    ++cstep;
+  };
+
+  for (int t = 0; t < total;) {
+    // the unit's steps
+    const int t_end = t + a.nsteps;
+    if constexpr (EXP && !A4) {
+      switch (ntg) {
+        case 0: for (; t < t_end; ++t) step(t, std::integral_constant<int, 0>{}); break;
+        case 1: for (; t < t_end; ++t) step(t, std::integral_constant<int, 1>{}); break;
+        case 2: for (; t < t_end; ++t) step(t, std::integral_constant<int, 2>{}); break;
+        case 3: for (; t < t_end; ++t) step(t, std::integral_constant<int, 3>{}); break;
+        default: for (; t < t_end; ++t) step(t, std::integral_constant<int, 4>{}); break;
+      }
+    } else {
+      for (; t < t_end; ++t) step(t, std::integral_constant<int, -1>{});
+    }
 
     // ---- epilogue of the unit: the lane holds rows 4g + jj of each 16-row
     // weight group and sorted row r of each 16-row token group
