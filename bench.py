@@ -597,7 +597,11 @@ def main():
 
     fp8 = prim["act"] != "bf16"
     fp4 = prim["act"] == "mxfp4"
+    # the FP8 gate_up runs with copy waves while the experts average at most 64
+    # rows (tokens * top-k <= 64 * experts)
+    cw = fp8 and not fp4 and prim["tokens"] * 4 <= 64 * 128
     kname = ("prefill_gemm_kernel<true, 128, true, false, false>" if fp4 else
+             "prefill_gemm_cw_kernel" if cw else
              "prefill_gemm_kernel<true, 128, false, false, false>" if fp8 else "gemv_persist_kernel<0, 12, false, false>")
     if fp8 and prim["tokens"] >= 4096:
         peak = MXFP4_PEAK_TFLOPS if fp4 else FP8_PEAK_TFLOPS

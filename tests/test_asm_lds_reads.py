@@ -43,7 +43,7 @@ def lds_read_hazards(asm):
     """(kernel, line) pairs where an instruction names a register of an LDS
     read still in flight; also the number of kernels and ds_reads seen."""
     bad, kernels, reads = [], 0, 0
-    for name in re.findall(r"^(_ZN2mx19prefill_gemm_kernel\S+):", asm, re.M):
+    for name in re.findall(r"^(_ZN2mx\d+prefill_gemm\w*kernel\S*):", asm, re.M):
         kernels += 1
         body = asm[asm.index(name + ":"):asm.index(".Lfunc_end", asm.index(name + ":"))]
         pending = []
@@ -79,7 +79,7 @@ def test_prefill_lds_reads_are_waited_before_use(tmp_path):
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     bad, kernels, reads = lds_read_hazards(out.read_text())
-    assert kernels >= 8 and reads > 100
+    assert kernels >= 9 and reads > 100
     assert not bad, "registers of LDS reads in flight used: %s" % bad[:5]
 
 
