@@ -189,13 +189,18 @@ def moe_setup(run, Ld, name, synth):
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(mx.mxfp4_moe_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device="cuda")
+    codes = None
+    if act != 0:
+        # the E2M1 codes restaged once for the prefill GEMMs (a load-time step)
+        codes = (mx.mxfp4_moe_prepare_code_stream(Ld["w13_blocks"], H, I, 0),
+                 mx.mxfp4_moe_prepare_code_stream(Ld["w2_blocks"], H, I, 1))
 
-    def step(events, ready=False):
+    def step(events, ready=False, prepared_codes=False):
         # router + layer in one library call (its "permute" stage covers routing too)
         mx.mxfp4_moe_layer(x, logits, k, Ld["w13_blocks"], Ld["w13_scales"], Ld["w13_bias"],
                            Ld["w2_blocks"], Ld["w2_scales"], Ld["w2_bias"], act, out=out,
                            topk_ids=ids, topk_weights=w, workspace=ws, events=events,
-                           scale_streams_ready=ready)
+                           scale_streams_ready=ready, code_streams=codes if prepared_codes else None)
 
     step(None)
     torch.cuda.synchronize()
@@ -259,12 +264,17 @@ def measure_moe(run, Ld, name, synth, steps, warmup, ceiling_gbps=None):
         # the same call captured once in a HIP graph and replayed (the
         # launches of a serving loop); the cache eviction stays outside
         graph_ms = float(np.mean(graph_replay_times(run, step, steps, warmup)))
-    prepared = None
+    prepared = prepared_all = prepared_stages = None
     if wl["act_mode"] != 0:
         # the weight scales restaged once (a load-time step for fixed weights):
         # every timed call passes MXFP4_OPT_SCALE_STREAMS_READY
         ms_prep, _, _ = run.time_steps(lambda ev: step(ev, True), steps, warmup, flush=True)
         prepared = float(np.mean(ms_prep))
+        # ... and the E2M1 codes too (restaged code streams)
+        _, prepared_stages, _ = run.time_steps(lambda ev: step(ev, True, True), steps, warmup, flush=True,
+                                               stage_events=True)
+        ms_all, _, _ = run.time_steps(lambda ev: step(ev, True, True), steps, warmup, flush=True)
+        prepared_all = float(np.mean(ms_all))
     mean = float(np.mean(ms_plain))
     g1 = stages["gemm1"]
     act = wl["act_mode"]
@@ -278,6 +288,7 @@ def measure_moe(run, Ld, name, synth, steps, warmup, ceiling_gbps=None):
         warm_ms_per_step=float(np.mean(warm)),
         graph_ms_per_step=graph_ms,
         prepared_scales_ms_per_step=prepared,
+        prepared_ms_per_step=prepared_all, prepared_stage_ms=prepared_stages,
         stage_ms=stages, gemm1_ms=g1,
         gemm1_GBps=acct["gemm1_bytes"] / g1 / 1e6,
         gemm1_TFLOPs=acct["gemm1_flops"] / g1 / 1e9,
@@ -292,6 +303,9 @@ def measure_moe(run, Ld, name, synth, steps, warmup, ceiling_gbps=None):
         if prepared:
             res["layer_tflops_prepared_scales"] = tflops_fractions(
                 acct["flops"] / prepared / 1e9, acct["flops"], acct["layer_bytes"], act, ceiling_gbps)
+        if prepared_all:
+            res["layer_tflops_prepared"] = tflops_fractions(
+                acct["flops"] / prepared_all / 1e9, acct["flops"], acct["layer_bytes"], act, ceiling_gbps)
     return res
 
 
@@ -315,6 +329,7 @@ def measure_nvfp4(run, synth, steps, warmup):
     H = I = synth.H_GPT_OSS
     E, k = synth.E_GPT_OSS, synth.TOPK_GPT_OSS
     res = {}
+    nv_codes = None
     for name in ("moe_decode_t4", "moe_decode_t32", "moe_prefill_t2048_fp8", "moe_prefill_t8192_fp8_skewed"):
         wl = synth.workload(name)
         T = wl["T"]
@@ -325,12 +340,12 @@ def measure_nvfp4(run, synth, steps, warmup):
         out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(mx.nvfp4_moe_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device="cuda")
 
-        def step(events, ready=False, logits=logits, x=x, ids=ids, w=w, out=out, ws=ws, act=act):
+        def step(events, ready=False, codes=None, logits=logits, x=x, ids=ids, w=w, out=out, ws=ws, act=act):
             mx.mxfp4_route_topk(logits, k, topk_ids=ids, topk_weights=w)
             mx.nvfp4_moe_forward(x, ids, w, Nd["w13_blocks"], Nd["w13_scales"], Nd["w13_global"],
                                  Nd["w13_bias"], Nd["w2_blocks"], Nd["w2_scales"], Nd["w2_global"],
                                  Nd["w2_bias"], out=out, workspace=ws, events=events, act_mode=act,
-                                 scale_streams_ready=ready)
+                                 scale_streams_ready=ready, code_streams=codes)
 
         step(None)
         torch.cuda.synchronize()
@@ -349,6 +364,11 @@ def measure_nvfp4(run, synth, steps, warmup):
         if act:
             ms_prep, _, _ = run.time_steps(lambda ev: step(ev, True), steps, warmup, flush=True)
             r["prepared_scales_ms_per_step"] = float(np.mean(ms_prep))
+            if nv_codes is None:
+                nv_codes = (mx.mxfp4_moe_prepare_code_stream(Nd["w13_blocks"], H, I, 0),
+                            mx.mxfp4_moe_prepare_code_stream(Nd["w2_blocks"], H, I, 1))
+            ms_all, _, _ = run.time_steps(lambda ev: step(ev, True, nv_codes), steps, warmup, flush=True)
+            r["prepared_ms_per_step"] = float(np.mean(ms_all))
             # both GEMMs issue the bf16 MFMA
             r["frac_issued_peak"] = r["layer_TFLOPs"] / BF16_PEAK_TFLOPS
         res[name.replace("moe_", "moe_nvfp4_")] = r
@@ -569,16 +589,21 @@ def main():
     print("bench: layer resident (%.2f GB)" % (sum(t.numel() * t.element_size() for t in Ld.values()) / 1e9),
           file=sys.stderr, flush=True)
 
+    def moe_line(name, r):
+        extra = ""
+        if r.get("prepared_ms_per_step"):
+            extra = " (restaged scales and codes: %.1f us)" % (r["prepared_ms_per_step"] * 1e3)
+        return "bench: %s %.1f us/step%s" % (name, r["ms_per_step"] * 1e3, extra)
+
     prim = measure_moe(run, Ld, args.workload, synth, args.steps, args.warmup, cg)
-    print("bench: %s %.1f us/step" % (args.workload, prim["ms_per_step"] * 1e3), file=sys.stderr, flush=True)
+    print(moe_line(args.workload, prim), file=sys.stderr, flush=True)
     others = {}
     if not args.primary_only:
         for name in synth.MOE_WORKLOADS:
             if name == args.workload:
                 continue
             others[name] = measure_moe(run, Ld, name, synth, max(args.steps // 2, 5), 2, cg)
-            print("bench: %s %.1f us/step" % (name, others[name]["ms_per_step"] * 1e3),
-                  file=sys.stderr, flush=True)
+            print(moe_line(name, others[name]), file=sys.stderr, flush=True)
         del Ld
         torch.cuda.empty_cache()
         others.update(measure_nvfp4(run, synth, max(args.steps // 2, 5), 2))

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MXFP4_ABI_VERSION 4
+#define MXFP4_ABI_VERSION 5
 
 /* Status codes.  0 is success; every failure leaves outputs untouched. */
 enum {
@@ -107,6 +107,15 @@ typedef struct {
      boundary i (0 <= i < MXFP4_NUM_STAGES).  Used for per-kernel timing. */
   void* events[MXFP4_NUM_STAGES];
   uint32_t flags;             /* MXFP4_OPT_* bits; 0 for none */
+  /* FP8 and MXFP4-activation modes: NULL, or the E2M1 codes of w13_blocks /
+     w2_blocks restaged by mxfp4_moe_prepare_code_stream for exactly these
+     weights and shapes (16-byte aligned); the prefill GEMMs then copy the
+     codes from there (contiguous 16 KB per tile and step) instead of the
+     blocks.  The results are bitwise those without them.  Ignored in BF16
+     mode.  A stale or foreign stream gives undefined results (every access
+     stays inside the stream's mxfp4_moe_code_stream_size bytes). */
+  const void* w13_codes;
+  const void* w2_codes;
 } mxfp4_moe_opts;
 
 /* Byte offsets of the intermediate results inside the MoE workspace, for
@@ -153,6 +162,31 @@ typedef struct {
                                copies them (internal layout); 0 in BF16 mode */
   uint64_t w2_scale_stream; /* the same for w2 */
 } mxfp4_moe_workspace_layout;
+
+/*
+ * Load-time restaging of an expert weight tensor's E2M1 codes for the prefill
+ * GEMMs (E4M3 and MXFP4 activations).  Not a step of the method: a layout of
+ * this library, for callers whose weights stay fixed.  The GEMMs read each
+ * weight tile 64 bytes per row and 128-element step (rows 1440 bytes apart at
+ * the gpt-oss shape), which the memory system serves at about two thirds of
+ * the rate of contiguous reads; restaged, a tile's step is one contiguous
+ * 16 KB chunk.  For expert e, row tile nt (gate_up: 128 gate rows and the
+ * matching 128 up rows; down: 256 rows) and step s, the chunk holds for each
+ * of the tile's 256 rows 64 bytes: four 16-byte blocks of 32 codes, blocks
+ * 4s..4s+3 of the row in an order of this library, zeros past K.
+ *   which   0: w13 (E x 2I rows of H codes, gate rows [0, I) then up rows),
+ *           1: w2 (E x H rows of I codes)
+ *   blocks  the codes as mxfp4_moe_forward takes them ([E, R, K/32, 16]) or as
+ *           nvfp4_moe_forward takes them ([E, R, K/16, 8]): the same K/2
+ *           bytes per row; 16-byte aligned
+ *   out     mxfp4_moe_code_stream_size() bytes, 16-byte aligned, caller-owned
+ * Limits: H, I positive multiples of 32 (<= 65536); 1 <= E <= 512.  The size:
+ * E * ceil(rows / 256) * ceil(K / 128) * 16 KB (gate_up counts ceil(I / 128)
+ * tiles), about 4.5% above the blocks at the gpt-oss shape.
+ */
+int mxfp4_moe_code_stream_size(int64_t H, int64_t I, int32_t E, int32_t which, size_t* bytes);
+int mxfp4_moe_prepare_code_stream(const uint8_t* blocks, int64_t H, int64_t I, int32_t E, int32_t which,
+                                  void* out, size_t out_bytes, void* stream);
 
 /* Library ABI version (MXFP4_ABI_VERSION of the compiled library). */
 int mxfp4_abi_version(void);

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmxfp4moe.so")
 ACT_BF16 = 0
 ACT_FP8_E4M3 = 1
 ACT_MXFP4 = 2
-ABI_VERSION = 4
+ABI_VERSION = 5
 NUM_STAGES = 7
 STAGES = ("begin", "permute", "quant_x", "gemm1", "quant_h", "gemm2", "combine")
 
@@ -36,16 +36,24 @@ OPT_SCALE_STREAMS_READY = 1
 
 
 class MoeOpts(ctypes.Structure):
-    _fields_ = [("events", _c_void_p * NUM_STAGES), ("flags", ctypes.c_uint32)]
+    _fields_ = [("events", _c_void_p * NUM_STAGES), ("flags", ctypes.c_uint32),
+                ("w13_codes", _c_void_p), ("w2_codes", _c_void_p)]
 
 
-def _opts(events, scale_streams_ready):
-    if events is None and not scale_streams_ready:
+def _opts(events, scale_streams_ready, code_streams=None):
+    if events is None and not scale_streams_ready and code_streams is None:
         return None
     opts = MoeOpts()
     for i, ev in enumerate(events or ()):
         opts.events[i] = ev
     opts.flags = OPT_SCALE_STREAMS_READY if scale_streams_ready else 0
+    if code_streams is not None:
+        w13c, w2c = code_streams
+        for t, name in ((w13c, "w13 code stream"), (w2c, "w2 code stream")):
+            if t is not None:
+                _need(t, name, torch.uint8, 1)
+        opts.w13_codes = None if w13c is None else w13c.data_ptr()
+        opts.w2_codes = None if w2c is None else w2c.data_ptr()
     return opts
 
 
@@ -103,6 +111,9 @@ def lib():
         L.mxfp4_quantize_weights.argtypes = [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]
         L.mxfp4_stream_read.argtypes = [_c_void_p, ctypes.c_uint64, _i32, _c_void_p,
                                         ctypes.POINTER(ctypes.c_uint64), _c_void_p]
+        L.mxfp4_moe_code_stream_size.argtypes = [_i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.mxfp4_moe_prepare_code_stream.argtypes = [_c_void_p, _i64, _i64, _i32, _i32, _c_void_p,
+                                                    ctypes.c_size_t, _c_void_p]
         L.mxfp4_event_create.argtypes = [ctypes.POINTER(_c_void_p)]
         L.mxfp4_event_destroy.argtypes = [_c_void_p]
         L.mxfp4_event_elapsed_ms.argtypes = [_c_void_p, _c_void_p, ctypes.POINTER(ctypes.c_float)]
@@ -111,7 +122,8 @@ def lib():
                      "nvfp4_moe_workspace_size",
                      "mxfp4_linear_workspace_size", "mxfp4_linear",
                      "mxfp4_quant_fp8_e4m3",
-                     "mxfp4_quantize_weights", "mxfp4_stream_read", "mxfp4_event_create",
+                     "mxfp4_quantize_weights", "mxfp4_stream_read", "mxfp4_moe_code_stream_size",
+                     "mxfp4_moe_prepare_code_stream", "mxfp4_event_create",
                      "mxfp4_event_destroy", "mxfp4_event_elapsed_ms"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -183,12 +195,14 @@ def mxfp4_moe_workspace_layout_query(T, H, I, E, k, act_mode):
 
 def mxfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bias,
                       w2_blocks, w2_scales, w2_bias, act_mode, out=None, workspace=None,
-                      events=None, stream=None, scale_streams_ready=False):
+                      events=None, stream=None, scale_streams_ready=False, code_streams=None):
     """One MoE layer; returns out (bf16 [T, H]).  `workspace` is a uint8 device
     tensor of at least mxfp4_moe_workspace_size() bytes (allocated here if None);
     `events` is an optional list of NUM_STAGES event handles (or None entries);
     `scale_streams_ready` sets MXFP4_OPT_SCALE_STREAMS_READY (the workspace
-    already holds these weights' restaged scales from an earlier call)."""
+    already holds these weights' restaged scales from an earlier call);
+    `code_streams` is None or (w13, w2) code streams from
+    mxfp4_moe_prepare_code_stream (either may be None)."""
     _need(x, "x", torch.bfloat16, 2)
     _need(topk_ids, "topk_ids", torch.int32, 2)
     _need(topk_weights, "topk_weights", torch.float32, 2)
@@ -217,7 +231,7 @@ def mxfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_bia
         workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, act_mode), 1),
                                 dtype=torch.uint8, device=x.device)
     _need(workspace, "workspace", torch.uint8, 1)
-    opts = _opts(events, scale_streams_ready)
+    opts = _opts(events, scale_streams_ready, code_streams)
     _check("mxfp4_moe_forward", lib().mxfp4_moe_forward(
         _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
         _ptr(w13_blocks), _ptr(w13_scales), _ptr(w13_bias),
@@ -236,7 +250,7 @@ def nvfp4_moe_workspace_size(T, H, I, E, k, act_mode=ACT_BF16):
 
 def nvfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_global, w13_bias,
                       w2_blocks, w2_scales, w2_global, w2_bias, out=None, workspace=None, events=None,
-                      stream=None, act_mode=ACT_BF16, scale_streams_ready=False):
+                      stream=None, act_mode=ACT_BF16, scale_streams_ready=False, code_streams=None):
     """MoE layer with NVFP4 expert weights (blocks [E, N, K/16, 8], E4M3 scales
     [E, N, K/16], one fp32 global scale per tensor), bf16 or (act_mode
     ACT_FP8_E4M3) per-tensor E4M3 activations; returns out (bf16 [T, H])."""
@@ -268,7 +282,7 @@ def nvfp4_moe_forward(x, topk_ids, topk_weights, w13_blocks, w13_scales, w13_glo
         workspace = torch.empty(max(nvfp4_moe_workspace_size(T, H, I, E, k, act_mode), 1),
                                 dtype=torch.uint8, device=x.device)
     _need(workspace, "workspace", torch.uint8, 1)
-    opts = _opts(events, scale_streams_ready)
+    opts = _opts(events, scale_streams_ready, code_streams)
     _check("nvfp4_moe_forward", lib().nvfp4_moe_forward(
         _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
         _ptr(w13_blocks), _ptr(w13_scales), float(w13_global), _ptr(w13_bias),
@@ -316,7 +330,7 @@ def _layer_args(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_sc
 
 def mxfp4_moe_layer(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias,
                     act_mode, out=None, topk_ids=None, topk_weights=None, workspace=None, events=None,
-                    stream=None, scale_streams_ready=False):
+                    stream=None, scale_streams_ready=False, code_streams=None):
     """Router + MoE layer in one call; returns (out, topk_ids, topk_weights)."""
     T, H, I, E, out, topk_ids, topk_weights = _layer_args(
         x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w2_scales, w2_bias, out, topk_ids,
@@ -325,7 +339,7 @@ def mxfp4_moe_layer(x, logits, k, w13_blocks, w13_scales, w13_bias, w2_blocks, w
         workspace = torch.empty(max(mxfp4_moe_workspace_size(T, H, I, E, k, act_mode), 1),
                                 dtype=torch.uint8, device=x.device)
     _need(workspace, "workspace", torch.uint8, 1)
-    opts = _opts(events, scale_streams_ready)
+    opts = _opts(events, scale_streams_ready, code_streams)
     _check("mxfp4_moe_layer", lib().mxfp4_moe_layer(
         _ptr(x), _ptr(logits), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
         _ptr(w13_blocks), _ptr(w13_scales), _ptr(w13_bias),
@@ -457,3 +471,25 @@ def mxfp4_event_elapsed_ms(start, end):
     _check("mxfp4_event_elapsed_ms",
            lib().mxfp4_event_elapsed_ms(ctypes.c_void_p(start), ctypes.c_void_p(end), ctypes.byref(ms)))
     return ms.value
+
+
+def mxfp4_moe_code_stream_size(H, I, E, which):
+    """Bytes of the restaged code stream of w13 (which=0) or w2 (which=1)."""
+    n = ctypes.c_size_t(0)
+    _check("mxfp4_moe_code_stream_size", lib().mxfp4_moe_code_stream_size(H, I, E, which, ctypes.byref(n)))
+    return n.value
+
+
+def mxfp4_moe_prepare_code_stream(blocks, H, I, which, out=None, stream=None):
+    """The E2M1 codes of w13 (which=0, blocks [E, 2I, ...]) or w2 (which=1,
+    blocks [E, H, ...]) restaged for the prefill GEMMs; a uint8 device tensor."""
+    _need(blocks, "blocks", torch.uint8)
+    E = blocks.shape[0]
+    n = mxfp4_moe_code_stream_size(H, I, E, which)
+    if out is None:
+        out = torch.empty(max(n, 1), dtype=torch.uint8, device=blocks.device)
+    _need(out, "out", torch.uint8, 1)
+    _check("mxfp4_moe_prepare_code_stream", lib().mxfp4_moe_prepare_code_stream(
+        _ptr(blocks), H, I, E, which, _ptr(out), out.numel(), _stream(stream)))
+    return out
+

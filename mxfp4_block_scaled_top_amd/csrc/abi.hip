@@ -301,6 +301,8 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
       !aligned(w13_scales, 4) || !aligned(w2_scales, 4) || (logits && !aligned(logits, 4)) ||
       (w13_bias && !aligned(w13_bias, 8)) || (w2_bias && !aligned(w2_bias, 8)))
     return fail(MXFP4_E_ALIGN, "%s: x/out/blocks need 16-byte, biases 8-byte, logits/ids/weights/scales 4-byte alignment", fn);
+  if (opts && (!aligned(opts->w13_codes, 16) || !aligned(opts->w2_codes, 16)))
+    return fail(MXFP4_E_ALIGN, "%s: restaged code streams need 16-byte alignment", fn);
   mxfp4_moe_workspace_layout L;
   plan(T, H, I, E, k, act_mode, &L, nv_globals != nullptr);
   if (!workspace) return fail(MXFP4_E_WORKSPACE, "workspace is null");
@@ -322,6 +324,10 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   }
   const bool fp8 = act_mode == MXFP4_ACT_FP8_E4M3;
   const bool a4 = act_mode == MXFP4_ACT_MXFP4;
+  if ((fp8 || a4) && opts) {
+    w.w13_codes = static_cast<const uint8_t*>(opts->w13_codes);
+    w.w2_codes = static_cast<const uint8_t*>(opts->w2_codes);
+  }
   const int64_t npairs = T * k;
   const int bm = act_mode == MXFP4_ACT_BF16 ? mx::kDecodeBM : mx::prefill_bm(npairs, E, nv_globals != nullptr);
   const int64_t bound = mx::max_tiles(npairs, E, bm);
@@ -587,6 +593,54 @@ int mxfp4_quantize_weights(const uint16_t* w, int64_t N, int64_t K, uint8_t* blo
   if (rc) return rc;
   const hipError_t e = mx::launch_quant_mxfp4(w, N * (K / 32), blocks, scales, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quantize_weights launch");
+  return ok();
+}
+
+namespace {
+// rows, K and row tiles of one expert tensor (which: 0 w13, 1 w2)
+void code_stream_shape(int64_t H, int64_t I, int32_t which, int& R, int& nout, int& K, int& tiles) {
+  const bool gu = which == 0;
+  R = (int)(gu ? 2 * I : H);
+  nout = (int)(gu ? I : H);
+  K = (int)(gu ? H : I);
+  tiles = gu ? (nout + 127) / 128 : (nout + 255) / 256;
+}
+int code_stream_check(int64_t H, int64_t I, int32_t E, int32_t which, const char* fn) {
+  if (which != 0 && which != 1) return fail(MXFP4_E_MODE, "%s: which must be 0 (w13) or 1 (w2)", fn);
+  if (H <= 0 || I <= 0 || H % 32 || I % 32 || H > 65536 || I > 65536)
+    return fail(MXFP4_E_SHAPE, "%s: H, I must be positive multiples of 32 up to 65536", fn);
+  if (E < 1 || E > 512) return fail(MXFP4_E_SHAPE, "%s: E=%d out of [1, 512]", fn, E);
+  return MXFP4_OK;
+}
+}  // namespace
+
+int mxfp4_moe_code_stream_size(int64_t H, int64_t I, int32_t E, int32_t which, size_t* bytes) {
+  int rc = code_stream_check(H, I, E, which, "code_stream_size");
+  if (rc) return rc;
+  if (!bytes) return fail(MXFP4_E_NULL, "code_stream_size: bytes is null");
+  int R, nout, K, tiles;
+  code_stream_shape(H, I, which, R, nout, K, tiles);
+  *bytes = (size_t)mx::code_stream_bytes(E, tiles, K);
+  return ok();
+}
+
+int mxfp4_moe_prepare_code_stream(const uint8_t* blocks, int64_t H, int64_t I, int32_t E, int32_t which,
+                                  void* out, size_t out_bytes, void* stream) {
+  int rc = code_stream_check(H, I, E, which, "prepare_code_stream");
+  if (rc) return rc;
+  if (!blocks || !out) return fail(MXFP4_E_NULL, "prepare_code_stream: null pointer");
+  if (!aligned(blocks, 16) || !aligned(out, 16))
+    return fail(MXFP4_E_ALIGN, "prepare_code_stream: blocks and out need 16-byte alignment");
+  int R, nout, K, tiles;
+  code_stream_shape(H, I, which, R, nout, K, tiles);
+  const int64_t need = mx::code_stream_bytes(E, tiles, K);
+  if ((int64_t)out_bytes < need)
+    return fail(MXFP4_E_WORKSPACE, "prepare_code_stream: out %zu bytes < required %lld", out_bytes, (long long)need);
+  rc = check_device();
+  if (rc) return rc;
+  const hipError_t e = mx::launch_code_stream(blocks, E, R, nout, K, which == 0, static_cast<uint8_t*>(out),
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prepare_code_stream launch");
   return ok();
 }
 

@@ -62,6 +62,7 @@ namespace mx {
 
 constexpr int kBN = 256;               // weight rows per unit
 constexpr int kBK = 128;               // K per step (four MX blocks)
+constexpr int kCodeChunk = kBN * kBK / 2;  // restaged codes per (n-tile, step): 16 KB
 
 // A4: MXFP4 activations, K steps of 256 (eight MX blocks): 128 B of E2M1
 // codes per activation and weight row, so every 1 KB copy covers 8 whole
@@ -108,6 +109,7 @@ struct Ring {
 
 struct PrefillArgs {
   const uint8_t* wb;       // [E, R, nb, 16]
+  const uint8_t* wcs;      // the codes restaged by launch_code_stream, or null (copies then read wb)
   const uint8_t* wsp;      // the weight scales restaged by launch_scale_stream
   const uint16_t* bias;    // [E, R] or null
   int R;                   // rows per expert: 2I (gate_up) or H (down)
@@ -269,7 +271,8 @@ struct PrefillCopier {
   int wave, u0, G, my_units;
   int lane, a_chunk, a_row, w_row, w_blk;
   const uint8_t* aptr[C::kActDma];
-  const uint8_t* wptr[C::kWDma];
+  const uint8_t* wptr[C::kWDma];   // codes of weight copy i: the row (wb), or step 0's 16 bytes (wcs)
+  int wback;            // restaged A4 codes: bytes back to the lane's K-tail substitute
   const uint8_t* wsp;   // this lane's 16 bytes of the unit's first step in the scale stream
   const uint8_t* ascp;  // A4: this lane's 16 bytes of the tile's scales at step 0
   int k, step, slot;    // next copy: local unit, step, ring slot
@@ -307,10 +310,29 @@ struct PrefillCopier {
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
       const int lr = (A4 ? 8 : 16) * (NW * i + wave) + w_row;
-      // wide-N: LDS rows 256 h .. 256 h + 255 hold n-tile 2 nt + h
-      const int wr = WN ? weight_row<GATEUP>(lr & (kBN - 1), 2 * nt + (lr >> 8), a.nout)
-                        : weight_row<GATEUP>(lr, nt, a.nout);
-      wptr[i] = a.wb + (ebase + wr) * a.nb * kBlockBytes;
+      if (a.wcs) {
+        // restaged codes: 16 KB per (n-tile, 128-element step) in LDS order
+        // (E4M3 activations: copy c takes bytes 1 KB c of the chunk).  A4
+        // rows of 128 B take their two 64-byte halves from the chunks of
+        // steps 2s and 2s + 1: slot j of row lr holds block 8s + jx, jx =
+        // j ^ (lr % 8), which chunk 2s + jx / 4 keeps at slot (jx % 4) ^
+        // ((lr / 2) % 4) of the row
+        const int h = WN ? lr >> 8 : 0;
+        const int ntr = WN ? min(2 * nt + h, a.NTs - 1) : nt;
+        const uint8_t* chunk0 = a.wcs + ((int64_t)te.x * a.NTs + ntr) * a.nsteps_s * kCodeChunk;
+        if (A4) {
+          const int jx = w_blk, hi = jx >> 2;
+          wptr[i] = chunk0 + hi * kCodeChunk + lr * 64 + 16 * ((jx & 3) ^ ((lr >> 1) & 3));
+          wback = hi * kCodeChunk;
+        } else {
+          wptr[i] = chunk0 + 1024 * ((NW * i + wave) & 15) + 16 * lane;
+        }
+      } else {
+        // wide-N: LDS rows 256 h .. 256 h + 255 hold n-tile 2 nt + h
+        const int wr = WN ? weight_row<GATEUP>(lr & (kBN - 1), 2 * nt + (lr >> 8), a.nout)
+                          : weight_row<GATEUP>(lr, nt, a.nout);
+        wptr[i] = a.wb + (ebase + wr) * a.nb * kBlockBytes;
+      }
     }
     // the unit's stream: 1 KB per 128-element sub-step; A4: wave w copies 256 B
     // (lanes 0-15) of sub-step w / 4, else 128 B (lanes 0-7).  Wide-N: waves
@@ -369,11 +391,18 @@ struct PrefillCopier {
   __device__ __forceinline__ void issue_w(const PrefillArgs& a) {
     uint8_t* dst = smem + slot * C::kSlot;
     const bool tail = step == a.nsteps - 1;
+    const int blk = C::kSub * 4 * step + w_blk;    // past K: the row's first block
+    if (a.wcs) {
+      // restaged: the step's chunk (zeros past K); A4 past K: chunk 2s
+      const int64_t off = (int64_t)step * C::kSub * kCodeChunk - (A4 && tail && blk >= a.nb ? wback : 0);
 #pragma unroll
-    for (int i = 0; i < C::kWDma; ++i) {
-      const int blk = C::kSub * 4 * step + w_blk;  // past K: the row's first block
-      __builtin_amdgcn_global_load_lds(wptr[i] + (!tail || blk < a.nb ? blk * kBlockBytes : 0),
-                                       dst + C::kW + 1024 * (NW * i + wave), 16, 0, 0);
+      for (int i = 0; i < C::kWDma; ++i)
+        __builtin_amdgcn_global_load_lds(wptr[i] + off, dst + C::kW + 1024 * (NW * i + wave), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kWDma; ++i)
+        __builtin_amdgcn_global_load_lds(wptr[i] + (!tail || blk < a.nb ? blk * kBlockBytes : 0),
+                                         dst + C::kW + 1024 * (NW * i + wave), 16, 0, 0);
     }
   }
   __device__ __forceinline__ void advance(const PrefillArgs& a) {
@@ -967,6 +996,42 @@ __global__ __launch_bounds__((Ring<kPrefillBM>::kThreads)) void prefill_gemm_cw_
   prefill_gemm_body<true, kPrefillBM, false, false, false, true>(a, tiles, status);
 }
 
+// The E2M1 codes of one weight tensor in the order the E4M3-activation copies
+// take them (launch_code_stream): for expert e, n-tile nt and 128-element
+// step s, 16 KB holding, for LDS row lr = 0..255, 64 bytes whose 16-byte slot
+// j is block 4s + (j ^ ((lr / 2) % 4)) of weight row weight_row(lr), zeros
+// past K.  One thread per 16 bytes, stores contiguous.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void code_stream_kernel(const uint8_t* __restrict__ wb, int R, int nout, int nb,
+                                                          int NT, int nsteps, int64_t n16, uint8_t* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n16) return;
+  const int within = (int)(q & 1023);                  // 16-byte piece of the chunk
+  const int64_t c = q >> 10;                           // chunk (e, nt, s)
+  const int st = (int)(c % nsteps);
+  const int64_t u = c / nsteps;
+  const int nt = (int)(u % NT), e = (int)(u / NT);
+  const int lr = within >> 2, j = within & 3;
+  const int b = 4 * st + (j ^ ((lr >> 1) & 3));
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (b < nb)
+    v = *reinterpret_cast<const uint4*>(wb + (((int64_t)e * R + weight_row<GATEUP>(lr, nt, nout)) * nb + b) *
+                                                 kBlockBytes);
+  reinterpret_cast<uint4*>(out)[q] = v;
+}
+
+hipError_t launch_code_stream(const uint8_t* wb, int E, int R, int nout, int K, bool gateup, uint8_t* out,
+                              hipStream_t s) {
+  const int nb = K / kBlockElems, nsteps = (nb + 3) / 4;
+  const int NT = gateup ? (nout + kBN / 2 - 1) / (kBN / 2) : (nout + kBN - 1) / kBN;
+  const int64_t n16 = (int64_t)E * NT * nsteps * (kCodeChunk / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = (n16 + 255) / 256;
+  if (gateup) code_stream_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(wb, R, nout, nb, NT, nsteps, n16, out);
+  else code_stream_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(wb, R, nout, nb, NT, nsteps, n16, out);
+  return hipGetLastError();
+}
+
 // The weight scales of every unit in the order the copies take them: for
 // expert e, n-tile nt and K step s, 1 KB holding, for each of the unit's 256
 // LDS rows lr, the scale bytes of MX blocks 4s .. 4s+3 of weight row
@@ -1254,6 +1319,7 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
                                  int64_t /*ntile_bound*/, hipStream_t s) {
   PrefillArgs a{};
   a.wb = w.w13_blocks;
+  a.wcs = w.w13_codes;
   a.wsp = ws.w13_stream;
   a.bias = w.w13_bias;
   a.R = 2 * sh.I;
@@ -1278,6 +1344,7 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
                                int64_t /*ntile_bound*/, hipStream_t s, uint16_t* out_bf16) {
   PrefillArgs a{};
   a.wb = w.w2_blocks;
+  a.wcs = w.w2_codes;
   a.wsp = ws.w2_stream;
   a.bias = w.w2_bias;
   a.R = sh.H;
@@ -1302,6 +1369,7 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
 hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const WsPtrs& ws, hipStream_t s) {
   PrefillArgs a{};
   a.wb = w.w13_blocks;
+  a.wcs = w.w13_codes;
   a.wsp = ws.w13_stream;
   a.bias = w.w13_bias;
   a.R = 2 * sh.I;
@@ -1327,6 +1395,7 @@ hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const Ws
                                uint16_t* out_bf16) {
   PrefillArgs a{};
   a.wb = w.w2_blocks;
+  a.wcs = w.w2_codes;
   a.wsp = ws.w2_stream;
   a.bias = w.w2_bias;
   a.R = sh.H;

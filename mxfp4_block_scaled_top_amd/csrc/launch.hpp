@@ -56,6 +56,13 @@ struct WsPtrs {
 // 512 bytes so that a step's read of a partial last row tile stays inside.
 inline int64_t act_scale_bytes(int64_t rows, int K) { return (int64_t)((K + 127) / 128) * rows * 4 + 512; }
 
+// Bytes of a restaged weight-code stream: 16 KB per (expert, n-tile, K step).
+inline int64_t code_stream_bytes(int E, int nout_tiles, int K) { return (int64_t)E * nout_tiles * ((K + 127) / 128) * 16384; }
+// The E2M1 codes of one expert tensor [E, R, K/2 bytes] restaged for the
+// prefill GEMMs' copies (gateup: R = 2 nout rows, gate then up; else R = nout).
+hipError_t launch_code_stream(const uint8_t* wb, int E, int R, int nout, int K, bool gateup, uint8_t* out,
+                              hipStream_t s);
+
 // Bytes of a restaged weight-scale stream: 1 KB per (expert, n-tile, K step).
 inline int64_t scale_stream_bytes(int E, int nout_tiles, int K) { return (int64_t)E * nout_tiles * ((K + 127) / 128) * 1024; }
 inline int gateup_ntiles(int I) { return (I + 127) / 128; }
@@ -83,6 +90,10 @@ struct MoeWeights {
   bool nvfp4 = false;
   float w13_global = 1.0f;
   float w2_global = 1.0f;
+  // E4M3 and MXFP4 activations: the codes restaged by launch_code_stream
+  // (null: the prefill copies read the blocks above)
+  const uint8_t* w13_codes = nullptr;
+  const uint8_t* w2_codes = nullptr;
 };
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* ids, float* w,

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mxfp4_abi_version() == 4
+    assert L.mxfp4_abi_version() == 5
     assert L.mxfp4_status_string(0) == b"ok"
     assert L.mxfp4_status_string(E_WORKSPACE) == b"workspace too small"
     assert L.mxfp4_status_string(99) == b"unknown status"
