@@ -177,7 +177,7 @@ class Runner:
         return ms, stages, wall
 
 
-def moe_setup(run, Ld, name, synth):
+def moe_setup(run, Ld, name, synth, prepare=True):
     torch, mx = run.torch, run.mx
     wl = synth.workload(name)
     T, H = wl["x"].shape
@@ -190,7 +190,7 @@ def moe_setup(run, Ld, name, synth):
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(mx.mxfp4_moe_workspace_size(T, H, I, E, k, act), dtype=torch.uint8, device="cuda")
     codes = None
-    if act != 0:
+    if act != 0 and prepare:
         # the E2M1 codes restaged once for the prefill GEMMs (a load-time step)
         codes = (mx.mxfp4_moe_prepare_code_stream(Ld["w13_blocks"], H, I, 0),
                  mx.mxfp4_moe_prepare_code_stream(Ld["w2_blocks"], H, I, 1))
@@ -254,8 +254,8 @@ def graph_replay_times(run, step, steps, warmup):
     return ms
 
 
-def measure_moe(run, Ld, name, synth, steps, warmup, ceiling_gbps=None):
-    step, acct, wl = moe_setup(run, Ld, name, synth)
+def measure_moe(run, Ld, name, synth, steps, warmup, ceiling_gbps=None, prepared_runs=True):
+    step, acct, wl = moe_setup(run, Ld, name, synth, prepared_runs)
     ms, stages, wall = run.time_steps(step, steps, warmup, flush=True, stage_events=True)
     ms_plain, _, _ = run.time_steps(step, steps, warmup, flush=True, stage_events=False)
     warm, _, _ = run.time_steps(step, max(steps // 2, 3), 1, flush=False)
@@ -265,7 +265,7 @@ def measure_moe(run, Ld, name, synth, steps, warmup, ceiling_gbps=None):
         # launches of a serving loop); the cache eviction stays outside
         graph_ms = float(np.mean(graph_replay_times(run, step, steps, warmup)))
     prepared = prepared_all = prepared_stages = None
-    if wl["act_mode"] != 0:
+    if wl["act_mode"] != 0 and prepared_runs:
         # the weight scales restaged once (a load-time step for fixed weights):
         # every timed call passes MXFP4_OPT_SCALE_STREAMS_READY
         ms_prep, _, _ = run.time_steps(lambda ev: step(ev, True), steps, warmup, flush=True)
@@ -317,7 +317,7 @@ def nvfp4_expert_bytes(H, I):
     return gate_up, down
 
 
-def measure_nvfp4(run, synth, steps, warmup):
+def measure_nvfp4(run, synth, steps, warmup, prepared_runs=True):
     """The MoE batches with NVFP4 expert weights: router top-k and the NVFP4
     MoE layer; the decode batches with bf16 activations, the prefill batches
     with E4M3 activations (both GEMMs on the bf16 MFMA with exactly expanded
@@ -361,7 +361,7 @@ def measure_nvfp4(run, synth, steps, warmup):
                  layer_GBps=layer_bytes / mean / 1e6, layer_hbm_frac=layer_bytes / mean / 1e6 / HBM_PEAK_GBS,
                  layer_TFLOPs=flops / mean / 1e9, stage_ms=stages,
                  gemm1_GBps=gemm1_bytes / stages["gemm1"] / 1e6, algorithmic_bytes=layer_bytes)
-        if act:
+        if act and prepared_runs:
             ms_prep, _, _ = run.time_steps(lambda ev: step(ev, True), steps, warmup, flush=True)
             r["prepared_scales_ms_per_step"] = float(np.mean(ms_prep))
             if nv_codes is None:
@@ -369,6 +369,7 @@ def measure_nvfp4(run, synth, steps, warmup):
                             mx.mxfp4_moe_prepare_code_stream(Nd["w2_blocks"], H, I, 1))
             ms_all, _, _ = run.time_steps(lambda ev: step(ev, True, nv_codes), steps, warmup, flush=True)
             r["prepared_ms_per_step"] = float(np.mean(ms_all))
+        if act:
             # both GEMMs issue the bf16 MFMA
             r["frac_issued_peak"] = r["layer_TFLOPs"] / BF16_PEAK_TFLOPS
         res[name.replace("moe_", "moe_nvfp4_")] = r
@@ -538,6 +539,9 @@ def main():
                     help="only measure the streaming-read ceiling (4 GiB read once per launch, register "
                          "loads and direct-to-LDS copies) and print it")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling measurement")
+    ap.add_argument("--no-prepared", action="store_true",
+                    help="skip the prefill timings with restaged scales and codes (kernel traces of the "
+                         "default path alone)")
     ap.add_argument("--dense-only", action="store_true",
                     help="only measure the dense projections (qkv_proj, o_proj, lm_head at 1 and 4 tokens) "
                          "and print them")
@@ -581,7 +585,8 @@ def main():
               flush=True)
         return
     if args.nvfp4_only:
-        print(json.dumps({"nvfp4": measure_nvfp4(run, synth, args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"nvfp4": measure_nvfp4(run, synth, args.steps, args.warmup, not args.no_prepared)}),
+              flush=True)
         return
     L = synth.layer()
     Ld = {k: run.dev(v) for k, v in L.items()}
@@ -595,18 +600,18 @@ def main():
             extra = " (restaged scales and codes: %.1f us)" % (r["prepared_ms_per_step"] * 1e3)
         return "bench: %s %.1f us/step%s" % (name, r["ms_per_step"] * 1e3, extra)
 
-    prim = measure_moe(run, Ld, args.workload, synth, args.steps, args.warmup, cg)
+    prim = measure_moe(run, Ld, args.workload, synth, args.steps, args.warmup, cg, not args.no_prepared)
     print(moe_line(args.workload, prim), file=sys.stderr, flush=True)
     others = {}
     if not args.primary_only:
         for name in synth.MOE_WORKLOADS:
             if name == args.workload:
                 continue
-            others[name] = measure_moe(run, Ld, name, synth, max(args.steps // 2, 5), 2, cg)
+            others[name] = measure_moe(run, Ld, name, synth, max(args.steps // 2, 5), 2, cg, not args.no_prepared)
             print(moe_line(name, others[name]), file=sys.stderr, flush=True)
         del Ld
         torch.cuda.empty_cache()
-        others.update(measure_nvfp4(run, synth, max(args.steps // 2, 5), 2))
+        others.update(measure_nvfp4(run, synth, max(args.steps // 2, 5), 2, not args.no_prepared))
         print("bench: nvfp4 decode %.1f / %.1f us (4 / 32 tokens), prefill %.1f / %.1f us (2048 / 8192 tokens)"
               % (others["moe_nvfp4_decode_t4"]["ms_per_step"] * 1e3,
                  others["moe_nvfp4_decode_t32"]["ms_per_step"] * 1e3,
