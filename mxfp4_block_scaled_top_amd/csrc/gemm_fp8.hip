@@ -688,7 +688,10 @@ __device__ __forceinline__ void prefill_gemm_body(PrefillArgs a, const int* __re
   // branch on it: the compiler then keeps the accumulators in place (a
   // merge of full and partial paths inside the step cost 24-72 register
   // copies per step)
-  auto step = [&](const int t, auto ntg_c) __attribute__((always_inline)) {
+  // TAIL: the unit's last K step, the only one whose blocks can lie past K
+  // (the other steps take no masking of weights and scales)
+  auto step = [&](const int t, auto ntg_c, auto tail_c) __attribute__((always_inline)) {
+    constexpr bool TAIL = decltype(tail_c)::value;
     constexpr int NTG = decltype(ntg_c)::value;
     const int nrg = NTG < 0 ? ntg : NTG;
     // this wave's copies of step t have landed (steps issued beyond t:
@@ -738,7 +741,7 @@ __device__ __forceinline__ void prefill_gemm_body(PrefillArgs a, const int* __re
         const v4u_t wq[4] = {wq0, wq1, wq2, wq3};
         const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
         const uint32_t ab[4] = {ab0, ab1, ab2, ab3};
-        const bool valid = 8 * cstep + 4 * h + g < a.nb;
+        const bool valid = !TAIL || 8 * cstep + 4 * h + g < a.nb;
         v8i B[4];
         int bsc[4];
 #pragma unroll
@@ -782,7 +785,7 @@ __device__ __forceinline__ void prefill_gemm_body(PrefillArgs a, const int* __re
         for (int rg = 0; rg < kRG; ++rg) wq[rg] = v4u_t{wq[rg].z, wq[rg].w, wq[rg].x, wq[rg].y};
       }
       const uint32_t sb[4] = {sb0, sb1, sb2, sb3};
-      const bool valid = 4 * cstep + g < a.nb;        // this lane's MX block lies inside K
+      const bool valid = !TAIL || 4 * cstep + g < a.nb;   // this lane's MX block lies inside K
       // weights of chunk q (elements 8q..8q+7 of the lane's block, 8(q^2).. for
       // odd g) of weight group rg, exactly: MXFP4 as bf16 through the scaled
       // conversion with the block's E8M0 scale; NVFP4 as f16, times the E4M3
@@ -873,14 +876,17 @@ __device__ __forceinline__ void prefill_gemm_body(PrefillArgs a, const int* __re
     const int t_end = t + a.nsteps;
     if constexpr (EXP && !A4) {
       switch (ntg) {
-        case 0: for (; t < t_end; ++t) step(t, std::integral_constant<int, 0>{}); break;
-        case 1: for (; t < t_end; ++t) step(t, std::integral_constant<int, 1>{}); break;
-        case 2: for (; t < t_end; ++t) step(t, std::integral_constant<int, 2>{}); break;
-        case 3: for (; t < t_end; ++t) step(t, std::integral_constant<int, 3>{}); break;
-        default: for (; t < t_end; ++t) step(t, std::integral_constant<int, 4>{}); break;
+        case 0: for (; t < t_end; ++t) step(t, std::integral_constant<int, 0>{}, std::true_type{}); break;
+        case 1: for (; t < t_end; ++t) step(t, std::integral_constant<int, 1>{}, std::true_type{}); break;
+        case 2: for (; t < t_end; ++t) step(t, std::integral_constant<int, 2>{}, std::true_type{}); break;
+        case 3: for (; t < t_end; ++t) step(t, std::integral_constant<int, 3>{}, std::true_type{}); break;
+        default: for (; t < t_end; ++t) step(t, std::integral_constant<int, 4>{}, std::true_type{}); break;
       }
     } else {
-      for (; t < t_end; ++t) step(t, std::integral_constant<int, -1>{});
+      // the steps before the last without the K-tail masking
+      for (; t < t_end - 1; ++t) step(t, std::integral_constant<int, -1>{}, std::false_type{});
+      step(t, std::integral_constant<int, -1>{}, std::true_type{});
+      ++t;
     }
 
     // ---- epilogue of the unit: the lane holds rows 4g + jj of each 16-row
