@@ -95,8 +95,11 @@ struct Ring {
   static constexpr int kSlot = kASc + (A4 ? BM * 4 * kSub : 0);
   static constexpr int kActDma = BM * kActRow / 1024 / kWaves;  // 1 KB activation DMAs per wave per step
   static constexpr int kWDma = kBNu * kWRow / 1024 / kWaves;    // 1 KB weight DMAs per wave per step
-  static constexpr int kScDma = 1;                      // the wave's 1/8 of the step's weight scales
-  static constexpr int kAScDma = A4 ? 1 : 0;            // the wave's 1/8 of the step's activation scales
+  // the step's weight scales: E4M3 activations, the wave's 1/8; A4 (two
+  // 128-element sub-steps), whole 1 KB copies by waves 0 and 1, and both
+  // sub-steps' activation scales (512 B each) by wave 2
+  static constexpr int kScDma = 1;                      // at most, per wave and step
+  static constexpr int kAScDma = 0;
   static constexpr int kDma = kActDma + kWDma + kScDma + kAScDma;  // DMA instructions per wave per step
   static constexpr int kLds = kStages * kSlot;
   static_assert(kActDma * kWaves * 1024 == BM * kActRow, "copies split over the waves");
@@ -319,8 +322,8 @@ struct PrefillCopier {
       aptr[i] = a.act + (int64_t)row * a.act_ld;
     }
     // rows past the tile end read other rows' scales (never stored)
-    // A4: wave w copies rows 32 (w % 4) .. +31 of sub-step w / 4
-    if (A4) ascp = a.asc + (int64_t)te.y * 4 + 128 * (wave & 3) + 16 * (lane & 7);
+    // A4: wave 2 copies the tile's 128 rows of both sub-steps
+    if (A4) ascp = a.asc + (int64_t)te.y * 4 + 16 * (lane & 31);
     const int64_t ebase = (int64_t)te.x * a.R;
 #pragma unroll
     for (int i = 0; i < C::kWDma; ++i) {
@@ -360,7 +363,7 @@ struct PrefillCopier {
             (kBN * C::kScRow / 4) * (wave & 3) + 16 * lane;
     } else {
       wsp = a.wsp + ((int64_t)te.x * a.NTs + nt) * a.nsteps_s * (kBN * C::kScRow) +
-            (A4 ? 256 * (wave & 3) + 16 * (lane & 15) : NV ? 256 * wave + 16 * (lane & 15) : 128 * wave + 16 * (lane & 7));
+            (A4 ? 16 * lane : NV ? 256 * wave + 16 * (lane & 15) : 128 * wave + 16 * (lane & 7));
     }
   }
 
@@ -390,11 +393,11 @@ struct PrefillCopier {
     if (A4) {
       // sub-step wave / 4 of this step; past the last one (K tail) the last
       // sub-step again (its values are masked)
-      int ss = 2 * step + (wave >> 2);
-      ss = ss < a.nsteps_s ? ss : a.nsteps_s - 1;
-      if (lane < 16) __builtin_amdgcn_global_load_lds(wsp + ss * 1024, dst + C::kSc + 256 * wave, 16, 0, 0);
-      if (lane < 8)
-        __builtin_amdgcn_global_load_lds(ascp + ss * a.asc_step, dst + C::kASc + 128 * wave, 16, 0, 0);
+      const int ss0 = min(2 * step, a.nsteps_s - 1), ss1 = min(2 * step + 1, a.nsteps_s - 1);
+      if (wave < 2)
+        __builtin_amdgcn_global_load_lds(wsp + (wave ? ss1 : ss0) * 1024, dst + C::kSc + 1024 * wave, 16, 0, 0);
+      else if (wave == 2)
+        __builtin_amdgcn_global_load_lds(ascp + (lane < 32 ? ss0 : ss1) * a.asc_step, dst + C::kASc, 16, 0, 0);
     } else if (lane < C::kBNu * C::kScRow / C::kWaves / 16) {
       // the scale bytes of rows (kBNu / 8) w .. (kBNu / 8)(w + 1) - 1 (NVFP4:
       // 8 per row)
@@ -705,7 +708,15 @@ __device__ __forceinline__ void prefill_gemm_body(PrefillArgs a, const int* __re
     constexpr int kD = CW ? 2 * C::kDma : C::kDma;
     int ahead = total - 1 - t;
     ahead = ahead < C::kStages - 2 ? ahead : C::kStages - 2;
-    if (!copies) {
+    if (A4) {
+      constexpr int kA = C::kActDma + C::kWDma;   // + one scale copy in waves 0-2
+      static_assert(!A4 || C::kStages == 3, "one step ahead");
+      if (wave < 3) {
+        if (ahead >= 1) wait_vm<kA + 1>(); else wait_vm<0>();
+      } else {
+        if (ahead >= 1) wait_vm<kA>(); else wait_vm<0>();
+      }
+    } else if (!copies) {
     } else if (ahead >= 4) wait_vm<4 * kD>();
     else if (ahead == 3) wait_vm<3 * kD>();
     else if (ahead == 2) wait_vm<2 * kD>();
