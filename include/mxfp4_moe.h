@@ -140,14 +140,19 @@ typedef struct {
                                row order: row r holds token sorted_pairs[r] / k
                                (rows past expert_offsets[E] unused);
                                MXFP4-activation mode: uint8 [T*k, H/32, 16]
-                               E2M1 blocks of x in the same row order */
+                               E2M1 blocks of x in the same row order.  Rows
+                               are padded to whole 128-byte lines: row r starts
+                               at r * ceil(H / 128) * 128 bytes (FP8) or
+                               r * ceil(H / 256) * 128 (E2M1); pad bytes are
+                               unspecified */
   uint64_t h;               /* BF16 mode: bf16 hi [T*k, I] then bf16 lo [T*k, I]
                                with h = hi + lo; FP8 mode: fp32 [T*k, I]; rows
                                in sorted order.  MXFP4-activation mode: no
                                bytes (h is quantised in the gate_up GEMM) */
   uint64_t h_codes;         /* FP8 mode: uint8 [T*k, I] E4M3 codes of h;
                                MXFP4-activation mode: uint8 [T*k, I/32, 16]
-                               E2M1 blocks of h */
+                               E2M1 blocks of h; rows padded as in x_codes
+                               (with I for H) */
   uint64_t y;               /* fp32 [T*k, H] per-pair expert outputs, sorted rows */
   uint64_t x_scales;        /* MXFP4-activation mode: uint8 [ceil(H/128), T*k, 4]
                                E8M0 scales of the x blocks, step-major: block b

@@ -12,6 +12,7 @@
 #include "../../include/mxfp4_moe.h"
 #include "common.hpp"
 #include "launch.hpp"
+#include "code_rows.hpp"
 
 namespace {
 
@@ -93,14 +94,14 @@ void plan(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, int32_t act_mod
   L->chunk_ranks = o; o = up(o + (size_t)np * 4);
   L->tiles = o; o = up(o + (size_t)mx::max_tiles(np, E, bm) * mx::kTileInts * 4);
   if (act_mode == MXFP4_ACT_FP8_E4M3) {
-    L->x_codes = o; o = up(o + (size_t)np * H);
+    L->x_codes = o; o = up(o + (size_t)np * mx::code_row_bytes(H, false));
     L->h = o; o = up(o + (size_t)np * I * 4);
-    L->h_codes = o; o = up(o + (size_t)np * I);
+    L->h_codes = o; o = up(o + (size_t)np * mx::code_row_bytes(I, false));
   } else if (act_mode == MXFP4_ACT_MXFP4) {
-    L->x_codes = o; o = up(o + (size_t)np * H / 2);
+    L->x_codes = o; o = up(o + (size_t)np * mx::code_row_bytes(H, true));
     L->x_scales = o; o = up(o + (size_t)mx::act_scale_bytes(np, (int)H));
     L->h = o;                      // h is quantised in the GEMM epilogue: no fp32 copy
-    L->h_codes = o; o = up(o + (size_t)np * I / 2);
+    L->h_codes = o; o = up(o + (size_t)np * mx::code_row_bytes(I, true));
     L->h_scales = o; o = up(o + (size_t)mx::act_scale_bytes(np, (int)I));
   } else {
     L->x_codes = o;
@@ -147,7 +148,7 @@ void linear_plan(int64_t M, int64_t N, int64_t K, int32_t act_mode, LinearLayout
   L->status = o; o = up(o + mx::kStWords * 4);
   L->tiles = o; o = up(o + (size_t)mx::max_tiles(M, 1, mx::kPrefillBM) * mx::kTileInts * 4);
   L->inv = o; if (a4) o = up(o + (size_t)M * 4);
-  L->codes = o; o = up(o + (size_t)M * (a4 ? K / 2 : K));
+  L->codes = o; o = up(o + (size_t)M * mx::code_row_bytes(K, a4));
   L->scales = o; if (a4) o = up(o + (size_t)mx::act_scale_bytes(M, (int)K));
   L->w_stream = o; o = up(o + (size_t)mx::scale_stream_bytes(1, mx::down_ntiles((int)N), (int)K));
   L->total = o;
@@ -380,9 +381,9 @@ int moe_run(const uint16_t* x, const float* logits, int64_t T, int64_t H, int64_
   else MX_STEP(mx::launch_moe_gateup_bf16(x, sh, w, ws, bound, s), "gate_up launch");
   MX_STEP(mark(MXFP4_STAGE_GEMM1), "event record");
   if (fp8) {
-    MX_STEP(mx::launch_encode_fp8(ws.h, false, npairs * I, ws.h_codes,
-                                  reinterpret_cast<const uint32_t*>(ws.status + mx::kStAmaxH),
-                                  reinterpret_cast<float*>(ws.status + mx::kStScaleH), s),
+    MX_STEP(mx::launch_encode_fp8_rows(ws.h, false, npairs, I, mx::code_row_bytes(I, false), ws.h_codes,
+                                       reinterpret_cast<const uint32_t*>(ws.status + mx::kStAmaxH),
+                                       reinterpret_cast<float*>(ws.status + mx::kStScaleH), s),
             "quant h launch");
   }
   if (restage) MX_STEP(mx::launch_scale_stream(sh, w, ws, false, s), "w2 scale stream launch");
@@ -552,8 +553,9 @@ int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8
     const mx::MoeShape shq{(int)M, (int)K, (int)N, 1, 1};
     MX_STEP(mx::launch_quant_x_mxfp4_sorted(x, shq, ws, s), "linear quant x launch");
   } else {
-    MX_STEP(mx::launch_quant_fp8(x, true, M * K, ws.h_codes, reinterpret_cast<uint32_t*>(ws.status + mx::kStAmaxH),
-                                 reinterpret_cast<float*>(ws.status + mx::kStScaleH), s),
+    MX_STEP(mx::launch_quant_fp8_rows(x, true, M, K, mx::code_row_bytes(K, false), ws.h_codes,
+                                      reinterpret_cast<uint32_t*>(ws.status + mx::kStAmaxH),
+                                      reinterpret_cast<float*>(ws.status + mx::kStScaleH), s),
             "linear quant x launch");
   }
   MX_STEP(mx::launch_scale_stream(sh, w, ws, false, s), "linear scale stream launch");

@@ -57,6 +57,7 @@
 //     operand of MX blocks past K is forced to zero.
 #include "common.hpp"
 #include "launch.hpp"
+#include "code_rows.hpp"
 
 namespace mx {
 
@@ -125,7 +126,7 @@ struct PrefillArgs {
   int nsteps;              // K steps: ceil(nb / 4), MXFP4 activations ceil(nb / 8)
   int nsteps_s;            // 128-element steps of the scale streams: ceil(nb / 4)
   const uint8_t* act;      // [sorted rows, K] E4M3 codes, or [sorted rows, K/32, 16] E2M1 blocks
-  int act_ld;              // activation bytes per row (K, or K/2 for E2M1)
+  int act_ld;              // activation row stride in bytes (code_row_bytes: K or K/2, whole 128-B lines)
   const uint8_t* asc;      // E2M1 activations: E8M0 [nsteps, sorted rows, 4] (step-major)
   int64_t asc_step;        // bytes per step of asc (4 * sorted rows)
   int scale_word;          // status word holding the per-tensor activation scale (E4M3)
@@ -947,7 +948,7 @@ __device__ __forceinline__ void prefill_gemm_body(PrefillArgs a, const int* __re
           // nibbles of columns 4g.. (half 0) and 16+4g.. (half 1)
           const uint32_t q[2] = {w & 0xffffu, w >> 16};
           if (row < re) {
-            uint8_t* hb = a.h_codes + (int64_t)row * (a.nout / 2) + b * kBlockBytes;
+            uint8_t* hb = a.h_codes + (int64_t)row * code_row_bytes(a.nout, true) + b * kBlockBytes;
             *reinterpret_cast<uint16_t*>(hb + 2 * g) = (uint16_t)q[0];
             *reinterpret_cast<uint16_t*>(hb + 8 + 2 * g) = (uint16_t)q[1];
             if (g == 0) {
@@ -1366,7 +1367,7 @@ hipError_t launch_moe_gateup_fp8(const MoeShape& sh, const MoeWeights& w, const 
   a.nsteps = (a.nb + 3) / 4;
   a.nsteps_s = a.nsteps;
   a.act = ws.x_codes;
-  a.act_ld = sh.H;
+  a.act_ld = (int)code_row_bytes(sh.H, false);
   a.scale_word = kStScaleX;
   a.out = static_cast<float*>(ws.h);
   if (w.nvfp4) {
@@ -1391,7 +1392,7 @@ hipError_t launch_moe_down_fp8(const MoeShape& sh, const MoeWeights& w, const Ws
   a.nsteps = (a.nb + 3) / 4;
   a.nsteps_s = a.nsteps;
   a.act = ws.h_codes;
-  a.act_ld = sh.I;
+  a.act_ld = (int)code_row_bytes(sh.I, false);
   a.scale_word = kStScaleH;
   a.out = ws.y;
   a.out_bf16 = out_bf16;
@@ -1416,7 +1417,7 @@ hipError_t launch_moe_gateup_fp4(const MoeShape& sh, const MoeWeights& w, const 
   a.nsteps = (a.nb + 7) / 8;        // K steps of 256
   a.nsteps_s = (a.nb + 3) / 4;
   a.act = ws.x_codes;
-  a.act_ld = sh.H / 2;
+  a.act_ld = (int)code_row_bytes(sh.H, true);
   a.asc = ws.x_scales;
   a.asc_step = (int64_t)4 * sh.T * sh.k;
   a.scale_word = -1;
@@ -1442,7 +1443,7 @@ hipError_t launch_moe_down_fp4(const MoeShape& sh, const MoeWeights& w, const Ws
   a.nsteps = (a.nb + 7) / 8;        // K steps of 256
   a.nsteps_s = (a.nb + 3) / 4;
   a.act = ws.h_codes;
-  a.act_ld = sh.I / 2;
+  a.act_ld = (int)code_row_bytes(sh.I, true);
   a.asc = ws.h_scales;
   a.asc_step = (int64_t)4 * sh.T * sh.k;
   a.scale_word = -1;

@@ -9,6 +9,7 @@
 // so that `/` on float stays correctly rounded.
 #include "common.hpp"
 #include "launch.hpp"
+#include "code_rows.hpp"
 
 namespace mx {
 
@@ -66,11 +67,13 @@ __device__ __forceinline__ float scale_from_amax(uint32_t bits) {
   return amax > 0.0f ? amax / 448.0f : 1.0f;      // correctly rounded divide
 }
 
+// Codes of n values; with row_len < ld (row_len a multiple of 16, n a
+// multiple of row_len) value e goes to byte (e / row_len) * ld + e % row_len.
 template <bool BF16>
 __global__ __launch_bounds__(256) void encode_kernel(const void* __restrict__ in, int64_t n,
                                                      uint8_t* __restrict__ codes,
                                                      const uint32_t* __restrict__ amax_bits,
-                                                     float* __restrict__ scale_out) {
+                                                     float* __restrict__ scale_out, int64_t row_len, int64_t ld) {
   const float s = scale_from_amax(*amax_bits);
   if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
   const int64_t n16 = n / 16;
@@ -84,7 +87,9 @@ __global__ __launch_bounds__(256) void encode_kernel(const void* __restrict__ in
     for (int q = 0; q < 4; ++q) {
       w[q] = e4m3_pack4(v[4 * q] / s, v[4 * q + 1] / s, v[4 * q + 2] / s, v[4 * q + 3] / s);
     }
-    *reinterpret_cast<uint4*>(codes + i * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    const int64_t e0 = i * 16;
+    const int64_t o = ld == row_len ? e0 : (e0 / row_len) * ld + e0 % row_len;
+    *reinterpret_cast<uint4*>(codes + o) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   if (blockIdx.x == 0)
     for (int64_t i = n16 * 16 + threadIdx.x; i < n; i += blockDim.x)
@@ -97,8 +102,8 @@ __global__ __launch_bounds__(256) void encode_kernel(const void* __restrict__ in
 // to the token's k sorted rows (pairs whose expert id was skipped have no
 // row, inv < 0).
 __global__ __launch_bounds__(256) void encode_sorted_rows_kernel(
-    const uint16_t* __restrict__ x, int H, int k, const int* __restrict__ inv,
-    uint8_t* __restrict__ codes, const uint32_t* __restrict__ amax_bits, float* __restrict__ scale_out) {
+    const uint16_t* __restrict__ x, int H, int k, const int* __restrict__ inv, uint8_t* __restrict__ codes,
+    int64_t ld, const uint32_t* __restrict__ amax_bits, float* __restrict__ scale_out) {
   const float s = scale_from_amax(*amax_bits);
   if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
   const int64_t t = blockIdx.x;
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(256) void encode_sorted_rows_kernel(
     const uint4 o = make_uint4(w[0], w[1], w[2], w[3]);
     for (int j = 0; j < k; ++j) {
       const int r = inv[t * k + j];
-      if (r >= 0) *reinterpret_cast<uint4*>(codes + (int64_t)r * H + c) = o;
+      if (r >= 0) *reinterpret_cast<uint4*>(codes + (int64_t)r * ld + c) = o;
     }
   }
 }
@@ -149,16 +154,34 @@ hipError_t launch_amax(const void* in, bool in_bf16, int64_t n, uint32_t* amax_b
 hipError_t launch_encode_fp8(const void* in, bool in_bf16, int64_t n, uint8_t* codes,
                              const uint32_t* amax_bits, float* scale_out, hipStream_t s) {
   const int grid = grid_for(n / 16);
-  if (in_bf16) encode_kernel<true><<<grid, 256, 0, s>>>(in, n, codes, amax_bits, scale_out);
-  else encode_kernel<false><<<grid, 256, 0, s>>>(in, n, codes, amax_bits, scale_out);
+  if (in_bf16) encode_kernel<true><<<grid, 256, 0, s>>>(in, n, codes, amax_bits, scale_out, n, n);
+  else encode_kernel<false><<<grid, 256, 0, s>>>(in, n, codes, amax_bits, scale_out, n, n);
   return hipGetLastError();
+}
+
+hipError_t launch_encode_fp8_rows(const void* in, bool in_bf16, int64_t rows, int64_t row_len, int64_t ld,
+                                  uint8_t* codes, const uint32_t* amax_bits, float* scale_out, hipStream_t s) {
+  if (row_len % 16 != 0 || ld < row_len) return hipErrorInvalidValue;
+  const int64_t n = rows * row_len;
+  const int grid = grid_for(n / 16);
+  if (in_bf16) encode_kernel<true><<<grid, 256, 0, s>>>(in, n, codes, amax_bits, scale_out, row_len, ld);
+  else encode_kernel<false><<<grid, 256, 0, s>>>(in, n, codes, amax_bits, scale_out, row_len, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8_rows(const void* in, bool in_bf16, int64_t rows, int64_t row_len, int64_t ld,
+                                 uint8_t* codes, uint32_t* amax_bits, float* scale_out, hipStream_t s) {
+  hipError_t e = launch_amax(in, in_bf16, rows * row_len, amax_bits, s);
+  if (e != hipSuccess) return e;
+  return launch_encode_fp8_rows(in, in_bf16, rows, row_len, ld, codes, amax_bits, scale_out, s);
 }
 
 hipError_t launch_encode_sorted_rows(const uint16_t* x, const MoeShape& sh, const WsPtrs& ws,
                                     hipStream_t s) {
   if (sh.T <= 0) return hipSuccess;
   encode_sorted_rows_kernel<<<sh.T, 256, 0, s>>>(
-      x, sh.H, sh.k, ws.inv, ws.x_codes, reinterpret_cast<const uint32_t*>(ws.status + kStAmaxX),
+      x, sh.H, sh.k, ws.inv, ws.x_codes, code_row_bytes(sh.H, false),
+      reinterpret_cast<const uint32_t*>(ws.status + kStAmaxX),
       reinterpret_cast<float*>(ws.status + kStScaleX));
   return hipGetLastError();
 }

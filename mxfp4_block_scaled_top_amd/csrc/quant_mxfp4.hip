@@ -15,6 +15,7 @@
 // arithmetic, so the codes are bit-exact.
 #include "common.hpp"
 #include "launch.hpp"
+#include "code_rows.hpp"
 
 namespace mx {
 
@@ -98,7 +99,7 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, uint4& out) {
 // the token's pairs occupy (inv[t*k + j] >= 0).
 __global__ __launch_bounds__(256) void quant_x_mxfp4_sorted_kernel(
     const uint16_t* __restrict__ x, int T, int H, int k, int nbp, const int* __restrict__ inv,
-    uint8_t* __restrict__ xb, uint8_t* __restrict__ xs) {
+    uint8_t* __restrict__ xb, int64_t ld, uint8_t* __restrict__ xs) {
   const int64_t rows = (int64_t)T * k;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)T * nbp) return;
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void quant_x_mxfp4_sorted_kernel(
   for (int j = 0; j < k; ++j) {
     const int r = inv[(int64_t)t * k + j];
     if (r < 0) continue;
-    if (real) *reinterpret_cast<uint4*>(xb + (int64_t)r * (H / 2) + c * kBlockBytes) = packed;
+    if (real) *reinterpret_cast<uint4*>(xb + (int64_t)r * ld + c * kBlockBytes) = packed;
     xs[((c >> 2) * rows + r) * 4 + (c & 3)] = (uint8_t)sc;
   }
 }
@@ -134,8 +135,8 @@ hipError_t launch_quant_x_mxfp4_sorted(const uint16_t* x, const MoeShape& sh, co
   const int nbp = 4 * ((sh.H + 127) / 128);
   const int64_t n = (int64_t)sh.T * nbp;
   if (n <= 0) return hipSuccess;
-  quant_x_mxfp4_sorted_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, sh.T, sh.H, sh.k, nbp, ws.inv,
-                                                                          ws.x_codes, ws.x_scales);
+  quant_x_mxfp4_sorted_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+      x, sh.T, sh.H, sh.k, nbp, ws.inv, ws.x_codes, code_row_bytes(sh.H, true), ws.x_scales);
   return hipGetLastError();
 }
 

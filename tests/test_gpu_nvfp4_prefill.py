@@ -19,7 +19,7 @@ import oracle
 import synth
 from helpers import assert_close_rounded, bf16_dev_to_f64, errors, no_constant_rows, to_dev
 from parity import down_combine, fp32, fp8_code_mismatch, gate_up_terms, h_tolerance
-from test_gpu_parity import _f32, _layer_dev, _mx_as_nv, _nv_dev, _run_moe, _run_nv, _status, _ws_view
+from test_gpu_parity import _code_rows, _f32, _layer_dev, _mx_as_nv, _nv_dev, _run_moe, _run_nv, _status, _ws_view
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -83,12 +83,12 @@ def _check(mx, L, x, ids, w, what, tokens=None, ready=False):
     # x codes (sorted rows) and the scale over the whole batch
     xc_all, xs_all, _ = oracle.quant_per_tensor(oracle.bf16_bits_to_f64(x))
     assert _f32(st[3]) == xs_all
-    xc = _ws_view(ws, lay, "x_codes", np.uint8, np_ * H).reshape(np_, H)
+    xc = _code_rows(ws, lay, "x_codes", np_, H)
     rows = inv.reshape(T, k)[tokens].reshape(-1)
     assert np.array_equal(xc[rows], np.repeat(xc_all[tokens], k, axis=0))
     # the GPU's h codes are the codec on its own fp32 h, amax over all pairs
     h_gpu = _ws_view(ws, lay, "h", np.float32, np_ * I).reshape(np_, I).astype(np.float64)
-    hc_gpu = _ws_view(ws, lay, "h_codes", np.uint8, np_ * I).reshape(np_, I)
+    hc_gpu = _code_rows(ws, lay, "h_codes", np_, I)
     s_h = _f32(st[4])
     rc, rs, ra = oracle.quant_per_tensor(h_gpu)
     assert _f32(st[2]) == ra and s_h == rs
@@ -162,8 +162,9 @@ def test_nvfp4_fp8_gate_up_equals_mxfp4_for_power_of_two_scales(mx, E, H, I, T, 
                       w2_blocks=n2, w2_scales=m2, w2_global=1.0, w2_bias=L["w2_bias"]))
     _, ws_nv, _ = _run(mx, Nd, x, ids, w)
     np_ = T * k
-    for key, dt, n in (("x_codes", np.uint8, np_ * H), ("h", np.float32, np_ * I), ("h_codes", np.uint8, np_ * I)):
-        assert np.array_equal(_ws_view(ws_mx, lay, key, dt, n), _ws_view(ws_nv, lay, key, dt, n)), key
+    for key, n in (("x_codes", H), ("h_codes", I)):
+        assert np.array_equal(_code_rows(ws_mx, lay, key, np_, n), _code_rows(ws_nv, lay, key, np_, n)), key
+    assert np.array_equal(_ws_view(ws_mx, lay, "h", np.float32, np_ * I), _ws_view(ws_nv, lay, "h", np.float32, np_ * I))
     assert np.array_equal(_status(ws_mx, lay)[:5], _status(ws_nv, lay)[:5])
 
 

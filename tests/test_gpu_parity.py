@@ -70,6 +70,17 @@ def _ws_view(ws, lay, key, dtype, count):
     return ws[lay[key]:lay[key] + nbytes].cpu().numpy().view(dtype)
 
 
+def _code_rows_dev(ws, lay, key, rows, row_bytes):
+    """Rows of an activation code buffer (x_codes, h_codes) as a device view:
+    row_bytes bytes per row at a stride of whole 128-byte lines."""
+    ld = -(-row_bytes // 128) * 128
+    return ws[lay[key]:lay[key] + rows * ld].view(rows, ld)[:, :row_bytes]
+
+
+def _code_rows(ws, lay, key, rows, row_bytes):
+    return _code_rows_dev(ws, lay, key, rows, row_bytes).cpu().numpy()
+
+
 def _status(ws, lay):
     return _ws_view(ws, lay, "status", np.int32, 16)
 
@@ -250,11 +261,11 @@ def test_moe_small_layers(mx, E, H, I, T, k, act):
         # x codes are stored in expert-sorted row order: row r is token sp[r] // k
         sp = _ws_view(ws, lay, "sorted_pairs", np.int32, np_)
         nrows = int(_ws_view(ws, lay, "expert_offsets", np.int32, E + 1)[E])
-        xc = _ws_view(ws, lay, "x_codes", np.uint8, np_ * H).reshape(np_, H)[:nrows]
+        xc = _code_rows(ws, lay, "x_codes", np_, H)[:nrows]
         assert np.array_equal(xc, ref["x_codes"][sp[:nrows] // k])
         assert _f32(st[3]) == ref["x_scale"]
         h_gpu = _ws_view(ws, lay, "h", np.float32, np_ * I).reshape(np_, I)
-        hc_gpu = _ws_view(ws, lay, "h_codes", np.uint8, np_ * I).reshape(np_, I)
+        hc_gpu = _code_rows(ws, lay, "h_codes", np_, I)
         # the GPU's codes of h are the oracle codec applied to the GPU's own fp32 h
         rc, rs, ra = oracle.quant_per_tensor(h_gpu.astype(np.float64))
         assert _f32(st[2]) == ra and _f32(st[4]) == rs
@@ -476,7 +487,7 @@ def test_moe_full_size_workloads(mx, full_layer, name):
     if act == synth.ACT_FP8_E4M3:
         xc_ref, sx, _ = oracle.quant_per_tensor(oracle.bf16_bits_to_f64(wl["x"]))
         assert _f32(st[3]) == sx == float(gold["x_scale"])
-        xc = _ws_view(ws, lay, "x_codes", np.uint8, np_ * H).reshape(np_, H)
+        xc = _code_rows(ws, lay, "x_codes", np_, H)
         assert np.array_equal(xc, xc_ref[sp // k])          # every pair routed
         h_t = ws[lay["h"]:lay["h"] + np_ * I * 4].view(torch.float32).view(np_, I)
         # the kernel's fp32 h within the error bound, on every pair of the sampled tokens
@@ -495,7 +506,7 @@ def test_moe_full_size_workloads(mx, full_layer, name):
         h_rows = h_t[torch.from_numpy(srows).cuda()].cpu().numpy().astype(np.float64)
         sh = _f32(st[4])
         rc = oracle.e4m3_encode((h_rows / sh).astype(np.float32).astype(np.float64))
-        hc_all = ws[lay["h_codes"]:lay["h_codes"] + np_ * I].view(np_, I)
+        hc_all = _code_rows_dev(ws, lay, "h_codes", np_, I)
         assert np.array_equal(hc_all[torch.from_numpy(srows).cuda()].cpu().numpy(), rc)
         # codes of every pair of the sampled tokens against the oracle's codes
         c_gpu = hc_all[rows].cpu().numpy()
@@ -503,14 +514,14 @@ def test_moe_full_size_workloads(mx, full_layer, name):
         hq = oracle.e4m3_decode(c_gpu) * sh
     else:
         # x codes of every sorted row (every pair is routed)
-        xb = _ws_view(ws, lay, "x_codes", np.uint8, np_ * H // 2).reshape(np_, H // 32, 16)
+        xb = _code_rows(ws, lay, "x_codes", np_, H // 2).reshape(np_, H // 32, 16)
         xs = _step_major(ws, lay, "x_scales", np_, H)
         rb, rs = oracle.quantize_mxfp4(oracle.bf16_bits_to_f64(wl["x"]))
         assert np.array_equal(xs[:, :H // 32], rs[sp // k])
         assert np.array_equal(xb, rb[sp // k])
         del xb, rb
         # h codes of every pair of the sampled tokens against the oracle's
-        hb = ws[lay["h_codes"]:lay["h_codes"] + np_ * I // 2].view(np_, I // 32, 16)
+        hb = _code_rows_dev(ws, lay, "h_codes", np_, I // 2).reshape(np_, I // 32, 16)
         hb = hb[rows].cpu().numpy()
         hs = _step_major(ws, lay, "h_scales", np_, I)[rows_np][:, :I // 32]
         delta, ndiff = mx_code_mismatch(hb, hs, h_ref, tol)
@@ -540,11 +551,11 @@ def test_moe_multi_unit_layers(mx, act):
         h_gpu = _ws_view(ws, lay, "h", np.float32, np_ * I).reshape(np_, I)[inv].astype(np.float64)
         assert np.all(np.abs(h_gpu - h_ref) <= tol)
         sh = _f32(_status(ws, lay)[4])
-        c_gpu = _ws_view(ws, lay, "h_codes", np.uint8, np_ * I).reshape(np_, I)[inv]
+        c_gpu = _code_rows(ws, lay, "h_codes", np_, I)[inv]
         delta, ndiff = fp8_code_mismatch(c_gpu, sh, h_ref, tol, ref["h_scale"])
         hq = oracle.e4m3_decode(c_gpu) * sh
     else:
-        hb = _ws_view(ws, lay, "h_codes", np.uint8, np_ * I // 2).reshape(np_, I // 32, 16)[inv]
+        hb = _code_rows(ws, lay, "h_codes", np_, I // 2).reshape(np_, I // 32, 16)[inv]
         hs = _step_major(ws, lay, "h_scales", np_, I)[inv][:, :I // 32]
         delta, ndiff = mx_code_mismatch(hb, hs, h_ref, tol)
         hq = oracle.dequant(hb, hs)
@@ -583,12 +594,12 @@ def _mx_act_check(mx, L, x, ids, w, what):
     sp = _ws_view(ws, lay, "sorted_pairs", np.int32, np_)
     nrows = int(_ws_view(ws, lay, "expert_offsets", np.int32, E + 1)[E])
     pairs = sp[:nrows].astype(np.int64)
-    xb = _ws_view(ws, lay, "x_codes", np.uint8, np_ * H // 2).reshape(np_, H // 32, 16)[:nrows]
+    xb = _code_rows(ws, lay, "x_codes", np_, H // 2).reshape(np_, H // 32, 16)[:nrows]
     xs = _step_major(ws, lay, "x_scales", np_, H)[:nrows]
     assert np.array_equal(xb, ref["x_blocks"][pairs // k])
     assert np.array_equal(xs[:, :H // 32], ref["x_scales"][pairs // k])
     assert np.all(xs[:, H // 32:] == 127)
-    hb = _ws_view(ws, lay, "h_codes", np.uint8, np_ * I // 2).reshape(np_, I // 32, 16)[:nrows]
+    hb = _code_rows(ws, lay, "h_codes", np_, I // 2).reshape(np_, I // 32, 16)[:nrows]
     hs = _step_major(ws, lay, "h_scales", np_, I)[:nrows]
     assert np.all(hs[:, I // 32:] == 127)
     hs = hs[:, :I // 32]
