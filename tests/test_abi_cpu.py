@@ -78,8 +78,10 @@ def test_layout_offsets_are_ordered_and_aligned(L):
             lay.chunk_ranks, lay.tiles, lay.x_codes, lay.h, lay.h_codes, lay.y]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs) and lay.total_bytes > lay.y
-    assert lay.y - lay.h >= 8192 * 4 * 2880 * 5          # fp32 h + u8 codes
-    assert lay.h - lay.x_codes >= 8192 * 4 * 2880        # x codes per routed pair (sorted rows)
+    # code rows are padded to whole 128-byte lines: 2880 E4M3 codes -> 2944 bytes
+    assert lay.y - lay.h >= 8192 * 4 * (2880 * 4 + 2944)  # fp32 h + u8 codes
+    assert lay.y - lay.h_codes >= 8192 * 4 * 2944
+    assert lay.h - lay.x_codes >= 8192 * 4 * 2944        # x codes per routed pair (sorted rows)
     assert lay.x_scales == 0 and lay.h_scales == 0
     # restaged scale streams: 1 KB per (expert, n-tile, K step)
     assert lay.y < lay.w13_scale_stream < lay.w2_scale_stream < lay.total_bytes
@@ -96,10 +98,10 @@ def test_layout_of_mxfp4_activations(L):
     offs = [lay.x_codes, lay.x_scales, lay.h, lay.h_codes, lay.h_scales, lay.y, lay.w13_scale_stream,
             lay.w2_scale_stream]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
-    assert lay.x_scales - lay.x_codes >= np_ * H // 2    # E2M1 blocks per sorted row
+    assert lay.x_scales - lay.x_codes >= np_ * 1536      # E2M1 blocks per sorted row, 1440 -> 1536 B
     assert lay.h - lay.x_scales >= 23 * np_ * 4 + 512    # 23 steps x 4 scales per row, + read slack
     assert lay.h_codes == lay.h                          # h is quantised in the GEMM: no fp32 copy
-    assert lay.h_scales - lay.h_codes >= np_ * I // 2
+    assert lay.h_scales - lay.h_codes >= np_ * 1536
     assert lay.y - lay.h_scales >= 23 * np_ * 4 + 512
     assert lay.w13_scale_stream - lay.y >= np_ * H * 4
     assert lay.total_bytes - lay.w2_scale_stream >= 128 * 12 * 23 * 1024
