@@ -224,11 +224,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint4*>(out + (size_t)t * H + n0) = o;
 }
 
+// The same sums for a fixed k: the k row indices, then all 2k y loads, are
+// issued before the first FMA (a skipped pair loads row 0 and is not
+// added), so a lane waits for memory twice instead of twice per slot.
+template <int K>
+__global__ __launch_bounds__(256) void combine_k_kernel(const float* __restrict__ y,
+                                                        const int* __restrict__ inv,
+                                                        const float* __restrict__ w, int T, int H,
+                                                        uint16_t* __restrict__ out) {
+  const int per_row = H / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * per_row) return;
+  const int t = (int)(idx / per_row);
+  const int n0 = (int)(idx % per_row) * 8;
+  int r[K];
+  float wt[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    r[j] = inv[(size_t)t * K + j];
+    wt[j] = w[(size_t)t * K + j];
+  }
+  float4 a[K], b[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const float4* p = reinterpret_cast<const float4*>(y + (size_t)(r[j] < 0 ? 0 : r[j]) * H + n0);
+    a[j] = p[0];
+    b[j] = p[1];
+  }
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (r[j] < 0) continue;
+    acc[0] = fmaf(wt[j], a[j].x, acc[0]); acc[1] = fmaf(wt[j], a[j].y, acc[1]);
+    acc[2] = fmaf(wt[j], a[j].z, acc[2]); acc[3] = fmaf(wt[j], a[j].w, acc[3]);
+    acc[4] = fmaf(wt[j], b[j].x, acc[4]); acc[5] = fmaf(wt[j], b[j].y, acc[5]);
+    acc[6] = fmaf(wt[j], b[j].z, acc[6]); acc[7] = fmaf(wt[j], b[j].w, acc[7]);
+  }
+  uint4 o;
+  o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+  o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+  o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
+  o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * H + n0) = o;
+}
+
 hipError_t launch_combine(const MoeShape& sh, const float* topk_weights, const WsPtrs& ws,
                           uint16_t* out, hipStream_t s) {
   const int64_t threads = (int64_t)sh.T * (sh.H / 8);
   const int grid = (int)((threads + 255) / 256);
-  combine_kernel<<<grid, 256, 0, s>>>(ws.y, ws.inv, topk_weights, sh.T, sh.H, sh.k, out);
+  if (sh.k == 4) combine_k_kernel<4><<<grid, 256, 0, s>>>(ws.y, ws.inv, topk_weights, sh.T, sh.H, out);
+  else combine_kernel<<<grid, 256, 0, s>>>(ws.y, ws.inv, topk_weights, sh.T, sh.H, sh.k, out);
   return hipGetLastError();
 }
 
