@@ -336,12 +336,21 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   __shared__ int off[1024];
   __shared__ int scan_tmp[kChunkWaves + 1];
   const int e = threadIdx.x;
+  // chunks in batches of 8, each batch's loads issued before its stores
+  // (the stores go to the same array, so a load cannot pass the previous
+  // chunk's store: one memory round trip per batch instead of per chunk)
+  constexpr int kB = 8;
   int running = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_counts[(size_t)c * E + e];
-      chunk_counts[(size_t)c * E + e] = running;
-      running += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kB) {
+      int v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (c0 + u < nchunks) chunk_counts[(size_t)(c0 + u) * E + e] = running;
+        running += v[u];
+      }
     }
     cnt[e] = running;
   }
@@ -350,7 +359,14 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   if (e < E) {
     off[e] = ex;
     offsets[e] = ex;
-    for (int c = 0; c < nchunks; ++c) chunk_counts[(size_t)c * E + e] += ex;
+    for (int c0 = 0; c0 < nchunks; c0 += kB) {
+      int v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(size_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (c0 + u < nchunks) chunk_counts[(size_t)(c0 + u) * E + e] = v[u] + ex;
+    }
   }
   if (e == 0) offsets[E] = total;
   if (e < kStWords && e != kStNumTiles) status[e] = e == kStFlags ? (total != npairs ? 1 : 0) : 0;
